@@ -1,0 +1,155 @@
+"""Seeded synthetic workloads for the fused input projection.
+
+This module holds shapes, seeds and the random-number recipe only: none of the
+projection's arithmetic. Both the GPU path's tests/benchmark and the float64
+oracle take their inputs from here, so they see the same stored values.
+
+Recipe: NumPy ``default_rng(seed)`` draws x, then W, then the bias in float64
+from standard normals; W is scaled to variance 1/C and the bias to variance
+0.02; each tensor is then rounded once to the storage dtype (bf16 by
+round-to-nearest-even through fp32). The float64 copies returned alongside are
+exact images of the stored values.
+
+Shapes stand in for the workloads on the pages: the Walrus processor block
+(Walrus PR "Make fused_ff_qkv contiguous": a 32x32x1 latent grid, 6 steps,
+batch 4, folded into 24 slabs), a BERT-base linear + GELU and its QKV
+projection (xformers PR "Fused linear: small FW cleanup and much better
+perfs", follow-up comments), a 32-head decoder QKV with rotate-half RoPE
+(NVIDIA/Fuser issue "Improve performance on RoPE (and code around it)"), and
+the SD-2.1 attention projection at 4096 tokens, 5 heads, batch 2
+(memory-efficient-attention issue "Improve performance via batched-matmul and
+fused multiplies"). No dataset or trained weight is involved.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str              # "bf16" or "f32": storage type of x, W, bias and outputs
+    layout: str             # "channels_first" ([b,c,spatial...]) or "tokens_last" ([b,s,c])
+    x_shape: tuple
+    ff_dim: int
+    ff_act: str             # "gelu" or "none"
+    n_heads: int
+    head_dim: int
+    has_bias: bool
+    rope: bool
+    seed: int
+    rope_base: float = 10000.0
+    pos_offset: int = 0
+    w_layout: str = "cf"    # "cf": W [C,F]; "fc": W [F,C]
+    description: str = field(default="", compare=False)
+
+    @property
+    def C(self) -> int:
+        return self.x_shape[1] if self.layout == "channels_first" else self.x_shape[2]
+
+    @property
+    def nb(self) -> int:
+        return self.x_shape[0]
+
+    @property
+    def S(self) -> int:
+        if self.layout == "channels_first":
+            return int(np.prod(self.x_shape[2:]))
+        return self.x_shape[1]
+
+    @property
+    def M(self) -> int:
+        return self.nb * self.S
+
+    @property
+    def F(self) -> int:
+        return self.ff_dim + 3 * self.n_heads * self.head_dim
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic flops of the contraction: 2*M*C*F."""
+        return 2.0 * self.M * self.C * self.F
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    @property
+    def alg_bytes(self) -> float:
+        """Algorithmic HBM bytes: x once, W once, bias, RoPE table (fp32 cos+sin,
+        [positions, head_dim/2]) and every output once."""
+        e = self.elem_bytes
+        b = self.M * self.C * e + self.C * self.F * e + self.M * self.F * e
+        if self.has_bias:
+            b += self.F * e
+        if self.rope and self.n_heads > 0:
+            b += 2 * 4 * (self.S + self.pos_offset) * (self.head_dim // 2)
+        return float(b)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny_f32", "f32", "channels_first", (1, 32, 8, 8, 1), 128, "gelu", 4, 8, True, True, 1,
+                 description="tiny fp32: x [1,32,8,8,1], W [32,224], FF 128 GELU, Q/K/V 4x8, RoPE"),
+        Workload("walrus_bf16", "bf16", "channels_first", (24, 768, 32, 32, 1), 3072, "gelu", 12, 64, True, True, 2,
+                 description="Walrus-like bf16: x [24,768,32,32,1] (4 x 6 steps), W [768,5376], FF 3072 GELU, "
+                             "Q/K/V 12x64, RoPE"),
+        Workload("bert_ff_bf16", "bf16", "tokens_last", (32, 512, 768), 3072, "gelu", 0, 0, True, False, 3,
+                 description="BERT-base FF bf16: x [32,512,768], W [768,3072], GELU"),
+        Workload("bert_qkv_bf16", "bf16", "tokens_last", (32, 512, 768), 0, "none", 12, 64, True, False, 31,
+                 description="BERT-base QKV bf16: x [32,512,768], W [768,2304], 3 x [384,512,64]"),
+        Workload("decoder_qkv_rope_bf16", "bf16", "tokens_last", (2, 4096, 4096), 0, "none", 32, 128, False, True, 4,
+                 description="decoder QKV+RoPE bf16: x [2,4096,4096], W [4096,12288], 3 x [64,4096,128]"),
+        Workload("smallk_qkv_bf16", "bf16", "channels_first", (2, 320, 64, 64), 0, "none", 5, 64, False, False, 5,
+                 description="small-K bf16: x [2,320,64,64] channels-first, W [320,960], 3 x [10,4096,64]"),
+    ]
+}
+
+
+def round_to(a64: np.ndarray, dtype: str) -> torch.Tensor:
+    """Round a float64 array once to the storage dtype (RNE); returns a CPU tensor."""
+    t = torch.from_numpy(np.ascontiguousarray(a64, dtype=np.float32)) if dtype == "f32" else \
+        torch.from_numpy(np.ascontiguousarray(a64, dtype=np.float32)).to(torch.bfloat16)
+    return t
+
+
+def as_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 image of a bf16/fp32 CPU tensor."""
+    return t.to(torch.float64).numpy()
+
+
+@dataclass
+class Inputs:
+    x: torch.Tensor          # storage dtype, CPU, contiguous in the workload's layout
+    w: torch.Tensor          # [C,F] or [F,C]
+    bias: torch.Tensor | None
+    x64: np.ndarray
+    w64: np.ndarray
+    bias64: np.ndarray | None
+
+
+def make_inputs(wl: Workload, seed: int | None = None) -> Inputs:
+    """Draw x ~ N(0,1), W ~ N(0,1/C), bias ~ N(0,0.02) (second argument = variance)."""
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    C, F = wl.C, wl.F
+    x = rng.standard_normal(wl.x_shape)
+    w = rng.standard_normal((C, F)) * math.sqrt(1.0 / C)
+    if wl.w_layout == "fc":
+        w = np.ascontiguousarray(w.T)
+    b = rng.standard_normal(F) * math.sqrt(0.02) if wl.has_bias else None
+    xt, wt = round_to(x, wl.dtype), round_to(w, wl.dtype)
+    bt = round_to(b, wl.dtype) if b is not None else None
+    return Inputs(xt, wt, bt, as_f64(xt), as_f64(wt), None if bt is None else as_f64(bt))
+
+
+def with_shape(wl: Workload, name: str, **kw) -> Workload:
+    """A variant of a workload (smaller or ragged shapes for tests)."""
+    d = dict(wl.__dict__)
+    d.update(kw)
+    d["name"] = name
+    return Workload(**d)

@@ -1,0 +1,166 @@
+"""Float64 CPU oracle of the fused input projection.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the GPU library never does. It shares
+no code with the GPU path. The arithmetic lives in ``fused_proj_oracle.c``
+(plain loops, float64); this module only builds that file with gcc, marshals
+NumPy arrays into it and reorders its token-major q/k/v rows into the
+head-major ``[batch*heads, tokens, head_dim]`` buffers described in the
+memory-efficient-attention issue "Improve performance via batched-matmul and
+fused multiplies" (first comment), using a plain array transpose.
+
+Parity pins: see ``tests/test_oracle_pins.py``. The RoPE angle convention
+``phi = p * base**(-2i/head_dim)`` is the one point the pages leave open (their
+tables are random); it is pinned to hand-derived closed forms, not to the pages.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fused_proj_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_fused_proj.so")
+_lib = None
+
+GCC_FLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared", "-std=c99"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fused multiply-add contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        d = ctypes.POINTER(ctypes.c_double)
+        i64 = ctypes.c_int64
+        p64 = ctypes.POINTER(ctypes.c_int64)
+        lib.oracle_fused_proj.restype = ctypes.c_int
+        lib.oracle_fused_proj.argtypes = [
+            d, i64, i64, i64, i64, i64, ctypes.c_int, p64, p64,
+            d, i64, ctypes.c_int, d,
+            i64, ctypes.c_int, i64, i64,
+            ctypes.c_int, ctypes.c_double, i64,
+            p64, i64, d, d, d, d, ctypes.c_int,
+        ]
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+@dataclass
+class OracleResult:
+    """Outputs in float64. Full runs: ff [nb, S, FF], q/k/v [nb*H, S, hd].
+    Token-subset runs: ff [ntok, FF], q/k/v [ntok, H, hd] (token-major)."""
+    ff: np.ndarray | None
+    q: np.ndarray | None
+    k: np.ndarray | None
+    v: np.ndarray | None
+
+
+def _dptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def fused_proj(x: np.ndarray, layout: str, w: np.ndarray, w_layout: str, bias: np.ndarray | None,
+               ff_dim: int, ff_act: str, n_heads: int, head_dim: int, rope: bool,
+               rope_base: float = 10000.0, pos_offset: int = 0, tokens: np.ndarray | None = None,
+               nthreads: int = 0) -> OracleResult:
+    """Float64 fused projection.
+
+    x: float64 array, ``layout`` "channels_first" ([b,c,h,w,d] or [b,c,s...]:
+       dim 0 batch, dim 1 channel, the rest spatial, flattened row-major) or
+       "tokens_last" ([b,s,c]). Any strides (element strides are passed as-is).
+    w: float64 [C,F] (w_layout "cf") or [F,C] (w_layout "fc").
+    tokens: None for every token (full layouts returned) or an int64 array of
+       global token indices bi*S + s (token-major rows returned).
+    """
+    lib = _load()
+    x = np.asarray(x)
+    if x.dtype != np.float64:
+        raise TypeError("oracle takes float64 inputs")
+    item = x.itemsize
+    if layout == "channels_first":
+        nb, C = x.shape[0], x.shape[1]
+        sp = x.shape[2:]
+        sp_stride = [st // item for st in x.strides[2:]]
+        sb, sc = x.strides[0] // item, x.strides[1] // item
+    elif layout == "tokens_last":
+        nb, C = x.shape[0], x.shape[2]
+        sp = (x.shape[1],)
+        sp_stride = [x.strides[1] // item]
+        sb, sc = x.strides[0] // item, x.strides[2] // item
+    else:
+        raise ValueError(layout)
+    if not 1 <= len(sp) <= 3:
+        raise ValueError("1 to 3 spatial dims")
+    S = int(np.prod(sp))
+    # base pointer of the view: strides may be arbitrary but non-negative
+    if any(s < 0 for s in x.strides):
+        raise ValueError("negative strides not supported by the oracle wrapper")
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    if w_layout == "cf":
+        assert w.shape[0] == C
+        F = w.shape[1]
+        w_fc = 0
+    elif w_layout == "fc":
+        assert w.shape[1] == C
+        F = w.shape[0]
+        w_fc = 1
+    else:
+        raise ValueError(w_layout)
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float64)
+        assert bias.shape == (F,)
+    full = tokens is None
+    if full:
+        tokens = np.arange(nb * S, dtype=np.int64)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+    ntok = tokens.shape[0]
+    qw = n_heads * head_dim
+    ff_rows = np.empty((ntok, ff_dim)) if ff_dim > 0 else None
+    q_rows = np.empty((ntok, qw)) if qw > 0 else None
+    k_rows = np.empty((ntok, qw)) if qw > 0 else None
+    v_rows = np.empty((ntok, qw)) if qw > 0 else None
+    spz = (ctypes.c_int64 * len(sp))(*sp)
+    sps = (ctypes.c_int64 * len(sp))(*sp_stride)
+    act = {"none": 0, "gelu": 1}[ff_act]
+    rc = lib.oracle_fused_proj(
+        x.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), nb, C, S, sb, sc, len(sp), spz, sps,
+        _dptr(w), F, w_fc, _dptr(bias),
+        ff_dim, act, n_heads, head_dim, int(bool(rope)), float(rope_base), int(pos_offset),
+        tokens.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ntok,
+        _dptr(ff_rows), _dptr(q_rows), _dptr(k_rows), _dptr(v_rows), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    if not full:
+        rs = (lambda a: None if a is None else a.reshape(ntok, n_heads, head_dim))
+        return OracleResult(ff_rows, rs(q_rows), rs(k_rows), rs(v_rows))
+
+    def head_major(a):
+        if a is None:
+            return None
+        # [b, S, H, hd] -> [b, H, S, hd] -> [b*H, S, hd]
+        return a.reshape(nb, S, n_heads, head_dim).transpose(0, 2, 1, 3).reshape(nb * n_heads, S, head_dim)
+
+    ff = None if ff_rows is None else ff_rows.reshape(nb, S, ff_dim)
+    return OracleResult(ff, head_major(q_rows), head_major(k_rows), head_major(v_rows))

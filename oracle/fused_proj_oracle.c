@@ -1,0 +1,215 @@
+/*
+ * Fused input projection: float64 CPU oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the plain, slow, obviously correct
+ * definition of what the fused projection computes. Only the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg may load it. It shares no
+ * code, header, table or constant with the GPU library, and it never reads
+ * anything the GPU library produced.
+ *
+ * What it computes, and where each step is stated:
+ *
+ *  1. Token gather. Walrus PR "Make fused_ff_qkv contiguous" (first comment):
+ *     the block takes a channels-first activation x[b,c,h,w,d], views it as
+ *     channels-last [b,h,w,d,c] and projects every (b,h,w,d) position, i.e.
+ *     one row per token, contracted over c. The same op on a token-major
+ *     [b,s,c] activation is the plain linear layer. Tokens are numbered
+ *     t = bi*S + s with s the row-major flattening of the spatial indices.
+ *
+ *  2. Contraction, bias and activation. xformers PR "Fused linear: small FW
+ *     cleanup and much better perfs" (description and follow-up comments):
+ *     the op is y = act(x W^T + b); for the attention projection it is the
+ *     same op with no activation, written into three buffers.
+ *     y[t,f] = sum_c x[t,c] * W[c,f] + b[f], summed in increasing c.
+ *
+ *  3. Split. Walrus PR (second comment): the fused output is split into
+ *     ff, q, k, v. Reading: contiguous column slices in that order, each of
+ *     the q/k/v slices holding n_heads heads of head_dim columns, head-major.
+ *
+ *  4. Activation on the ff slice: exact-erf GELU, 0.5*y*(1+erf(y/sqrt 2)).
+ *     (The pages name no GELU form; erf is the reading taken.)
+ *
+ *  5. Head-major buffers. memory-efficient-attention issue "Improve
+ *     performance via batched-matmul and fused multiplies" (first comment):
+ *     q/k/v live as [batch*num_heads, tokens, channels_per_head]. This file
+ *     writes token-major rows [t, h, j]; the Python side reorders them into
+ *     [bi*H + h, s, j] with a plain array transpose.
+ *
+ *  6. RoPE on q and k. NVIDIA/Fuser issue "Improve performance on RoPE (and
+ *     code around it)", rope_one_entry in the thunder example: split the head
+ *     into halves x1, x2; the rotated vector is (-x2, x1); the output is
+ *     x*cos + rotated*sin. Pairs are (i, i + head_dim/2). The page fills the
+ *     cos/sin tables with random numbers, so the angle is the textbook
+ *     phi = p * base^(-2i/head_dim) (a convention, not fixed by the pages),
+ *     with p = s + pos_offset, the token's position inside its slab.
+ *
+ * No step is blocked, fused or reordered beyond that statement.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL (-1)
+
+/* x element for token (bi, s), channel c.
+ * The spatial index s is unflattened row-major over sp_size[0..nsp). */
+static double x_at(const double *x, int64_t bi, int64_t s, int64_t c, int64_t sb, int64_t sc,
+                   int nsp, const int64_t *sp_size, const int64_t *sp_stride)
+{
+    int64_t off = bi * sb + c * sc;
+    int64_t rem = s;
+    for (int d = nsp - 1; d >= 0; --d) {
+        int64_t idx = rem % sp_size[d];
+        rem /= sp_size[d];
+        off += idx * sp_stride[d];
+    }
+    return x[off];
+}
+
+static double w_at(const double *w, int64_t c, int64_t f, int64_t C, int64_t F, int w_fc)
+{
+    /* w_fc == 0: W stored [C, F] (row c holds all outputs of channel c).
+     * w_fc == 1: W stored [F, C] (nn.Linear weight, y = x W^T). */
+    return w_fc ? w[f * C + c] : w[c * F + f];
+}
+
+static double gelu_erf(double y)
+{
+    return 0.5 * y * (1.0 + erf(y / sqrt(2.0)));
+}
+
+/* Rotate-half RoPE of one head vector v[0..hd) at position p, in place. */
+static void rope_rotate_half(double *v, int64_t hd, double p, double base)
+{
+    int64_t half = hd / 2;
+    for (int64_t i = 0; i < half; ++i) {
+        double theta = pow(base, -2.0 * (double)i / (double)hd);
+        double phi = p * theta;
+        double cs = cos(phi), sn = sin(phi);
+        double x1 = v[i], x2 = v[i + half];
+        v[i] = x1 * cs - x2 * sn;        /* x1*cos + (-x2)*sin */
+        v[i + half] = x2 * cs + x1 * sn; /* x2*cos + ( x1)*sin */
+    }
+}
+
+/*
+ * Computes the fused projection for the tokens listed in tokens[0..ntok).
+ *
+ *   x        float64 activation; element (bi, c, s) at
+ *            bi*sb + c*sc + sum_d idx_d(s)*sp_stride[d]
+ *   nb, C, S slabs, channels, tokens per slab (S = prod sp_size)
+ *   w        float64 weight, [C,F] (w_fc=0) or [F,C] (w_fc=1)
+ *   bias     float64 [F] or NULL
+ *   ff_dim   width of the ff slice; F = ff_dim + 3*n_heads*head_dim
+ *   ff_gelu  1: exact-erf GELU on the ff slice, 0: identity
+ *   rope     1: rotate-half RoPE on q and k (head_dim must be even)
+ *   tokens   global token indices t = bi*S + s, each in [0, nb*S)
+ *   outputs  token-major rows: ff_rows [ntok, ff_dim],
+ *            q_rows/k_rows/v_rows [ntok, n_heads*head_dim]; any may be NULL
+ *            when its slice is empty.
+ *   nthreads OpenMP threads (<= 0: runtime default)
+ * Returns 0, or -1 on an invalid argument (nothing is written then).
+ */
+int oracle_fused_proj(const double *x, int64_t nb, int64_t C, int64_t S, int64_t sb, int64_t sc,
+                      int nsp, const int64_t *sp_size, const int64_t *sp_stride,
+                      const double *w, int64_t F, int w_fc, const double *bias,
+                      int64_t ff_dim, int ff_gelu, int64_t n_heads, int64_t head_dim,
+                      int rope, double rope_base, int64_t pos_offset,
+                      const int64_t *tokens, int64_t ntok,
+                      double *ff_rows, double *q_rows, double *k_rows, double *v_rows,
+                      int nthreads)
+{
+    if (!x || !w || !tokens || nb <= 0 || C <= 0 || S <= 0 || nsp < 1 || nsp > 3 || ntok < 0)
+        return ORACLE_EINVAL;
+    int64_t prod = 1;
+    for (int d = 0; d < nsp; ++d) {
+        if (sp_size[d] <= 0) return ORACLE_EINVAL;
+        prod *= sp_size[d];
+    }
+    if (prod != S) return ORACLE_EINVAL;
+    if (ff_dim < 0 || n_heads < 0 || head_dim < 0) return ORACLE_EINVAL;
+    const int64_t qw = n_heads * head_dim;
+    if (F != ff_dim + 3 * qw || F <= 0) return ORACLE_EINVAL;
+    if (rope && (head_dim % 2 != 0)) return ORACLE_EINVAL;
+    if (ff_dim > 0 && !ff_rows) return ORACLE_EINVAL;
+    if (qw > 0 && (!q_rows || !k_rows || !v_rows)) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < ntok; ++i)
+        if (tokens[i] < 0 || tokens[i] >= nb * S) return ORACLE_EINVAL;
+
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+
+    int status = ORACLE_OK;
+#pragma omp parallel
+    {
+        double *y = (double *)malloc((size_t)F * sizeof(double));
+        double *xr = (double *)malloc((size_t)C * sizeof(double));
+        if (!y || !xr) {
+#pragma omp atomic write
+            status = ORACLE_EINVAL;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t i = 0; i < ntok; ++i) {
+            if (!y || !xr) continue;
+            const int64_t t = tokens[i];
+            const int64_t bi = t / S, s = t % S;
+            /* 1. gather the token's row */
+            for (int64_t c = 0; c < C; ++c)
+                xr[c] = x_at(x, bi, s, c, sb, sc, nsp, sp_size, sp_stride);
+            /* 2. contraction, sequential in c for every output column */
+            for (int64_t f = 0; f < F; ++f) y[f] = 0.0;
+            if (!w_fc) {
+                for (int64_t c = 0; c < C; ++c) {
+                    const double xc = xr[c];
+                    const double *wr = w + c * F;
+                    for (int64_t f = 0; f < F; ++f) y[f] += xc * wr[f];
+                }
+            } else {
+                for (int64_t f = 0; f < F; ++f) {
+                    double acc = 0.0;
+                    for (int64_t c = 0; c < C; ++c) acc += xr[c] * w_at(w, c, f, C, F, 1);
+                    y[f] = acc;
+                }
+            }
+            /* bias */
+            if (bias)
+                for (int64_t f = 0; f < F; ++f) y[f] += bias[f];
+            /* 3+4. ff slice with activation */
+            for (int64_t f = 0; f < ff_dim; ++f)
+                ff_rows[i * ff_dim + f] = ff_gelu ? gelu_erf(y[f]) : y[f];
+            /* 3+6. q, k, v slices; RoPE on q and k per head */
+            if (qw > 0) {
+                double *dst[3] = {q_rows + i * qw, k_rows + i * qw, v_rows + i * qw};
+                for (int which = 0; which < 3; ++which) {
+                    const double *src = y + ff_dim + which * qw;
+                    for (int64_t e = 0; e < qw; ++e) dst[which][e] = src[e];
+                    if (rope && which < 2)
+                        for (int64_t h = 0; h < n_heads; ++h)
+                            rope_rotate_half(dst[which] + h * head_dim, head_dim,
+                                             (double)(s + pos_offset), rope_base);
+                }
+            }
+        }
+        free(y);
+        free(xr);
+    }
+    return status;
+}
+
+/* Threads the OpenMP runtime would use by default (for reporting). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

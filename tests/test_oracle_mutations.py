@@ -1,0 +1,54 @@
+"""Each plausible mistake planted in a scratch copy of the oracle must fail a pin.
+
+The mistakes are planted in the oracle's C source on the CPU (never on a GPU);
+the pins in test_oracle_pins.py are then run against the mutated copy in a
+subprocess. A mutation that every pin lets through would mean the pins do not
+cover that part of the definition.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (description, original text, planted mistake)
+MUTATIONS = [
+    ("RoPE first-half sign", "v[i] = x1 * cs - x2 * sn;", "v[i] = x1 * cs + x2 * sn;"),
+    ("RoPE second-half sign", "v[i + half] = x2 * cs + x1 * sn;", "v[i + half] = x2 * cs - x1 * sn;"),
+    ("RoPE frequency exponent", "pow(base, -2.0 * (double)i / (double)hd)", "pow(base, -(double)i / (double)hd)"),
+    ("RoPE interleaved pairs", "double x1 = v[i], x2 = v[i + half];", "double x1 = v[2 * i], x2 = v[2 * i + 1];"),
+    ("RoPE global token position", "(double)(s + pos_offset)", "(double)(t + pos_offset)"),
+    ("RoPE ignores pos_offset", "(double)(s + pos_offset)", "(double)(s)"),
+    ("RoPE applied to v", "if (rope && which < 2)", "if (rope && which < 3)"),
+    ("dropped last channel", "for (int64_t c = 0; c < C; ++c) {\n                    const double xc",
+     "for (int64_t c = 0; c < C - 1; ++c) {\n                    const double xc"),
+    ("[F,C] weight read as [C,F]", "return w_fc ? w[f * C + c] : w[c * F + f];",
+     "return w_fc ? w[c * F + f] : w[c * F + f];"),
+    ("q and k slices swapped", "const double *src = y + ff_dim + which * qw;",
+     "const double *src = y + ff_dim + (which == 0 ? 1 : which == 1 ? 0 : 2) * qw;"),
+    ("tanh GELU", "return 0.5 * y * (1.0 + erf(y / sqrt(2.0)));",
+     "return 0.5 * y * (1.0 + tanh(0.7978845608028654 * (y + 0.044715 * y * y * y)));"),
+    ("spatial dims unflattened in reverse", "int64_t idx = rem % sp_size[d];", "int64_t idx = rem % sp_size[nsp - 1 - d];"),
+    ("bias skipped on the ff slice", "for (int64_t f = 0; f < F; ++f) y[f] += bias[f];",
+     "for (int64_t f = 0; f < F; ++f) y[f] += (f < ff_dim ? 0.0 : bias[f]);"),
+]
+
+
+@pytest.mark.parametrize("desc,orig,bad", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_fails_a_pin(tmp_path, desc, orig, bad):
+    src = open(os.path.join(ROOT, "oracle", "fused_proj_oracle.c")).read()
+    assert src.count(orig) >= 1, f"mutation site not found: {desc}"
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
+                    ignore=shutil.ignore_patterns("*.so", "*.tmp", "__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "tests"), tmp_path / "tests",
+                    ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutations.py"))
+    (tmp_path / "oracle" / "fused_proj_oracle.c").write_text(src.replace(orig, bad, 1))
+    env = dict(os.environ, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle_pins.py", "-q", "-x",
+                        "-p", "no:cacheprovider"], cwd=tmp_path, env=env, capture_output=True, text=True,
+                       timeout=600)
+    assert r.returncode != 0, f"no pin caught the planted mistake: {desc}\n{r.stdout[-2000:]}"
+    assert "failed" in r.stdout, r.stdout[-2000:]

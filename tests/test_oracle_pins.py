@@ -1,0 +1,304 @@
+"""Pins of the float64 oracle to facts outside itself (CPU only).
+
+Each test names the plausible mistake it would catch. Sources: Walrus PR "Make
+fused_ff_qkv contiguous" (gather + single GEMM), xformers PR "Fused linear:
+small FW cleanup and much better perfs" (y = act(xW^T + b), three-buffer QKV),
+NVIDIA/Fuser issue "Improve performance on RoPE (and code around it)"
+(rotate-half RoPE), memory-efficient-attention issue "Improve performance via
+batched-matmul and fused multiplies" ([batch*heads, tokens, head_dim]).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng_inputs(seed, x_shape, C, F, bias=True):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal(x_shape)
+    w = r.standard_normal((C, F)) / math.sqrt(C)
+    b = r.standard_normal(F) * math.sqrt(0.02) if bias else None
+    return x, w, b
+
+
+def gathered_rows(x, layout):
+    """[M, C] token rows by the pages' rearrange 'b c h w d -> b h w d c' (numpy transpose)."""
+    if layout == "channels_first":
+        nd = x.ndim
+        perm = (0,) + tuple(range(2, nd)) + (1,)
+        return x.transpose(perm).reshape(-1, x.shape[1])
+    return x.reshape(-1, x.shape[2])
+
+
+def scale(xr, w, b):
+    s = np.linalg.norm(xr, axis=1)[:, None] * np.linalg.norm(w, axis=0)[None, :]
+    if b is not None:
+        s = s + np.abs(b)[None, :]
+    return s
+
+
+# --------------------------------------------------------------------------- contraction + gather
+
+@pytest.mark.parametrize("w_layout", ["cf", "fc"])
+@pytest.mark.parametrize("layout,x_shape", [("channels_first", (2, 12, 3, 5, 2)),
+                                             ("tokens_last", (3, 7, 12))])
+def test_per_token_gemv_equals_batched_gemm(layout, x_shape, w_layout):
+    """Per-token GEMV loop (oracle) == one batched GEMM (numpy @) on the gathered
+    matrix. Catches a dropped c term, a transposed W, a wrong gather stride."""
+    C = x_shape[1] if layout == "channels_first" else x_shape[2]
+    FF, H, hd = 8, 2, 4
+    F = FF + 3 * H * hd
+    x, w, b = rng_inputs(11, x_shape, C, F)
+    wa = w if w_layout == "cf" else np.ascontiguousarray(w.T)
+    res = oracle.fused_proj(x, layout, wa, w_layout, b, FF, "none", H, hd, rope=False)
+    X = gathered_rows(x, layout)
+    Y = X @ w + b
+    s = scale(X, w, b)
+    nb = x.shape[0]
+    S = X.shape[0] // nb
+    ff = res.ff.reshape(-1, FF)
+    assert np.all(np.abs(ff - Y[:, :FF]) <= 1e-12 * s[:, :FF])
+    # q/k/v: explicit index definition dst[bi*H + h, s, j] = y[bi*S + s, off + h*hd + j]
+    for which, dst in enumerate([res.q, res.k, res.v]):
+        off = FF + which * H * hd
+        for bi in range(nb):
+            for h in range(H):
+                for si in range(S):
+                    t = bi * S + si
+                    cols = slice(off + h * hd, off + (h + 1) * hd)
+                    assert np.all(np.abs(dst[bi * H + h, si] - Y[t, cols]) <= 1e-12 * s[t, cols])
+
+
+def test_one_hot_weight_returns_gathered_rows_exactly():
+    """W = [I | 0]: the ff slice is the gathered row itself, bit for bit.
+    Catches any error in the channels-first index order (h, w, d, c)."""
+    x = np.random.default_rng(3).standard_normal((2, 6, 3, 4, 5))
+    C = 6
+    FF, H, hd = C, 1, 2
+    w = np.zeros((C, FF + 3 * H * hd))
+    w[:, :C] = np.eye(C)
+    res = oracle.fused_proj(x, "channels_first", w, "cf", None, FF, "none", H, hd, rope=False)
+    expect = np.ascontiguousarray(x.transpose(0, 2, 3, 4, 1)).reshape(2, 60, C)
+    assert np.array_equal(res.ff, expect)
+    assert np.all(res.q == 0) and np.all(res.k == 0) and np.all(res.v == 0)
+
+
+def test_layout_invariance_channels_first_vs_contiguous_copy():
+    """Only contiguity changes between a channels-first tensor and its channels-last
+    copy, so the result must be bitwise identical (the page's whole point)."""
+    x, w, b = rng_inputs(5, (3, 16, 4, 4, 2), 16, 8 + 3 * 2 * 8)
+    cl = np.ascontiguousarray(x.transpose(0, 2, 3, 4, 1)).reshape(3, 32, 16)
+    args = dict(w=w, w_layout="cf", bias=b, ff_dim=8, ff_act="gelu", n_heads=2, head_dim=8, rope=True)
+    r1 = oracle.fused_proj(x, "channels_first", **args)
+    r2 = oracle.fused_proj(cl, "tokens_last", **args)
+    for a, c in zip([r1.ff, r1.q, r1.k, r1.v], [r2.ff, r2.q, r2.k, r2.v]):
+        assert np.array_equal(a, c)
+
+
+def test_strided_view_equals_contiguous_copy():
+    """x as a channel slice of a larger tensor (non-unit batch stride) and a view with
+    a transposed spatial order give the same result as contiguous copies."""
+    big = np.random.default_rng(9).standard_normal((2, 20, 4, 6, 1))
+    x = big[:, 3:15]                               # channel slice, strided batch
+    C, FF, H, hd = 12, 4, 2, 4
+    w = np.random.default_rng(10).standard_normal((C, FF + 3 * H * hd))
+    args = dict(w=w, w_layout="cf", bias=None, ff_dim=FF, ff_act="none", n_heads=H, head_dim=hd, rope=True)
+    r1 = oracle.fused_proj(x, "channels_first", **args)
+    r2 = oracle.fused_proj(np.ascontiguousarray(x), "channels_first", **args)
+    assert np.array_equal(r1.ff, r2.ff) and np.array_equal(r1.q, r2.q)
+
+
+def test_token_subset_matches_full_run():
+    x, w, b = rng_inputs(21, (2, 10, 3, 3, 1), 10, 6 + 3 * 3 * 4)
+    args = dict(w=w, w_layout="cf", bias=b, ff_dim=6, ff_act="gelu", n_heads=3, head_dim=4, rope=True)
+    full = oracle.fused_proj(x, "channels_first", **args)
+    toks = np.array([0, 5, 9, 17, 8])
+    sub = oracle.fused_proj(x, "channels_first", tokens=toks, **args)
+    S = 9
+    for i, t in enumerate(toks):
+        bi, si = divmod(int(t), S)
+        assert np.array_equal(sub.ff[i], full.ff[bi, si])
+        for h in range(3):
+            assert np.array_equal(sub.q[i, h], full.q[bi * 3 + h, si])
+            assert np.array_equal(sub.k[i, h], full.k[bi * 3 + h, si])
+            assert np.array_equal(sub.v[i, h], full.v[bi * 3 + h, si])
+
+
+# --------------------------------------------------------------------------- split + head-major layout
+
+def test_head_major_matches_pages_transpose_flatten():
+    """[batch, tokens, heads, depth] -> transpose(1,2).flatten(end_dim=1) is the page's
+    conversion to [batch*heads, tokens, depth]; computed here with torch (not the
+    numpy reshape the oracle wrapper uses). Also pins q, k, v column order and
+    that neither GELU nor RoPE touches v."""
+    b_, S, C, H, hd, FF = 3, 5, 8, 2, 4, 4
+    x, w, b = rng_inputs(31, (b_, S, C), C, FF + 3 * H * hd)
+    res = oracle.fused_proj(x, "tokens_last", w, "cf", b, FF, "gelu", H, hd, rope=False)
+    Y = torch.from_numpy(x.reshape(-1, C) @ w + b).reshape(b_, S, -1)
+    for which, dst in enumerate([res.q, res.k, res.v]):
+        sl = Y[..., FF + which * H * hd: FF + (which + 1) * H * hd].reshape(b_, S, H, hd)
+        ref = sl.transpose(1, 2).flatten(end_dim=1).numpy()
+        assert ref.shape == dst.shape
+        assert np.allclose(dst, ref, rtol=0, atol=1e-12)
+
+
+def test_fused_equals_separate_slice_projections():
+    """The fused op equals separate projections with the W and b column slices,
+    bitwise in float64 (no interaction between slices)."""
+    x, w, b = rng_inputs(41, (2, 9, 16), 16, 8 + 3 * 2 * 4)
+    FF, H, hd = 8, 2, 4
+    fused = oracle.fused_proj(x, "tokens_last", w, "cf", b, FF, "gelu", H, hd, rope=True)
+    ff_only = oracle.fused_proj(x, "tokens_last", w[:, :FF], "cf", b[:FF], FF, "gelu", 0, 0, rope=True)
+    qkv_only = oracle.fused_proj(x, "tokens_last", w[:, FF:], "cf", b[FF:], 0, "none", H, hd, rope=True)
+    assert np.array_equal(fused.ff, ff_only.ff)
+    assert np.array_equal(fused.q, qkv_only.q)
+    assert np.array_equal(fused.k, qkv_only.k)
+    assert np.array_equal(fused.v, qkv_only.v)
+
+
+# --------------------------------------------------------------------------- bias and GELU
+
+def test_zero_weight_gives_activated_bias():
+    """W = 0: ff = gelu(b), v = b, q/k = RoPE(b) at position 0 = b. Catches a missing
+    bias, or a bias added after the activation."""
+    C, FF, H, hd = 4, 6, 2, 4
+    x = np.random.default_rng(1).standard_normal((1, 1, C))
+    w = np.zeros((C, FF + 3 * H * hd))
+    b = np.linspace(-2.0, 2.0, FF + 3 * H * hd)
+    res = oracle.fused_proj(x, "tokens_last", w, "cf", b, FF, "gelu", H, hd, rope=True)
+    from scipy.special import ndtr
+    assert np.allclose(res.ff[0, 0], b[:FF] * ndtr(b[:FF]), rtol=0, atol=1e-15)
+    assert np.array_equal(res.v[:, 0].reshape(-1), b[FF + 2 * H * hd:])
+    assert np.array_equal(res.q[:, 0].reshape(-1), b[FF:FF + H * hd])  # position 0
+
+
+def _gelu_via_oracle(vals):
+    """Run the oracle with W = I on the FF slice so that ff = gelu(x)."""
+    n = len(vals)
+    x = np.asarray(vals, dtype=np.float64).reshape(1, 1, n)
+    w = np.eye(n)
+    return oracle.fused_proj(x, "tokens_last", w, "cf", None, n, "gelu", 0, 0, rope=False).ff.reshape(-1)
+
+
+def test_gelu_golden_values():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "gelu_erf_values.txt")) if l.strip() and l[0] != "#"]
+    ys = [float(r[0]) for r in rows]
+    ref = [float(r[1]) for r in rows]
+    got = _gelu_via_oracle(ys)
+    assert np.allclose(got, ref, rtol=2e-15, atol=1e-300)
+
+
+def test_gelu_identities_and_torch_exact_gelu():
+    """gelu(y) - gelu(-y) = y; agreement with torch's exact GELU in float64.
+    Catches the tanh approximation (off by up to ~5e-4)."""
+    y = np.linspace(-6, 6, 97)
+    g = _gelu_via_oracle(y)
+    gm = _gelu_via_oracle(-y)
+    assert np.allclose(g - gm, y, rtol=0, atol=4e-15)
+    t = torch.nn.functional.gelu(torch.from_numpy(y), approximate="none").numpy()
+    assert np.allclose(g, t, rtol=0, atol=1e-15)
+    tanh = torch.nn.functional.gelu(torch.from_numpy(y), approximate="tanh").numpy()
+    assert np.max(np.abs(g - tanh)) > 1e-4
+
+
+# --------------------------------------------------------------------------- RoPE
+
+def _rope_via_oracle(vec, p, base, which="q"):
+    """Rotate one head vector at position p: W = I on the q (or k) slice, one token
+    row placed at slab position p (tokens_last [1, p+1, hd], the last row used)."""
+    hd = len(vec)
+    S = p + 1
+    x = np.zeros((1, S, hd))
+    x[0, p] = vec
+    w = np.zeros((hd, 3 * hd))
+    col = 0 if which == "q" else hd
+    w[:, col:col + hd] = np.eye(hd)
+    res = oracle.fused_proj(x, "tokens_last", w, "cf", None, 0, "none", 1, hd, rope=True, rope_base=base)
+    return (res.q if which == "q" else res.k)[0, p]
+
+
+def _golden_rope_cases():
+    out = []
+    for line in open(os.path.join(GOLDEN, "rope_rotate_half_cases.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        lhs, rhs = line.split(":")
+        hd, base, p, idx = lhs.split()
+        terms = []
+        for t in rhs.split():
+            o, e = t.split("=")
+            fn, ang = e[:-1].split("(")
+            terms.append((int(o), fn, float(ang)))
+        out.append((int(hd), float(base), int(p), int(idx), terms))
+    return out
+
+
+@pytest.mark.parametrize("case", _golden_rope_cases())
+@pytest.mark.parametrize("which", ["q", "k"])
+def test_rope_golden_unit_vectors(case, which):
+    """A unit vector maps to one column of the rotate-half rotation, worked out by hand.
+    Catches sign errors, interleaved (2i, 2i+1) pairing and a wrong frequency exponent."""
+    hd, base, p, idx, terms = case
+    v = np.zeros(hd)
+    v[idx] = 1.0
+    got = _rope_via_oracle(v, p, base, which)
+    expect = np.zeros(hd)
+    fns = {"cos": math.cos, "sin": math.sin, "-sin": lambda a: -math.sin(a)}
+    for o, fn, ang in terms:
+        expect[o] = fns[fn](ang)
+    assert np.allclose(got, expect, rtol=0, atol=2e-12)
+
+
+def test_rope_position_zero_identity_and_norm_preservation():
+    """Position 0 leaves q/k unchanged exactly; each (i, i+hd/2) pair keeps its norm."""
+    hd, H, C, S = 16, 3, 24, 40
+    x, w, b = rng_inputs(51, (2, S, C), C, 3 * H * hd)
+    r_on = oracle.fused_proj(x, "tokens_last", w, "cf", b, 0, "none", H, hd, rope=True)
+    r_off = oracle.fused_proj(x, "tokens_last", w, "cf", b, 0, "none", H, hd, rope=False)
+    # position 0 of EVERY slab (positions restart per slab)
+    assert np.array_equal(r_on.q[:, 0], r_off.q[:, 0])
+    assert np.array_equal(r_on.k[:, 0], r_off.k[:, 0])
+    assert np.array_equal(r_on.v, r_off.v)
+    half = hd // 2
+    for a_on, a_off in [(r_on.q, r_off.q), (r_on.k, r_off.k)]:
+        n_on = a_on[..., :half] ** 2 + a_on[..., half:] ** 2
+        n_off = a_off[..., :half] ** 2 + a_off[..., half:] ** 2
+        assert np.allclose(n_on, n_off, rtol=1e-13, atol=0)
+        assert not np.allclose(a_on[:, 1:], a_off[:, 1:])
+
+
+def test_rope_relative_position_and_pos_offset():
+    """<R_p q, R_p' k> depends only on p - p' (rotations compose); pos_offset shifts
+    the position of every token by the same amount."""
+    hd, C, S = 8, 8, 12
+    row = np.random.default_rng(61).standard_normal(C)
+    x = np.tile(row, (1, S, 1))                    # identical token rows
+    w = np.random.default_rng(62).standard_normal((C, 3 * hd))
+    r = oracle.fused_proj(x, "tokens_last", w, "cf", None, 0, "none", 1, hd, rope=True)
+    q, k = r.q[0], r.k[0]
+    g = q @ k.T
+    for d in range(-3, 4):
+        vals = [g[i, i + d] for i in range(max(0, -d), min(S, S - d))]
+        assert np.allclose(vals, vals[0], rtol=1e-12, atol=1e-12)
+    r5 = oracle.fused_proj(x, "tokens_last", w, "cf", None, 0, "none", 1, hd, rope=True, pos_offset=5)
+    assert np.allclose(r5.q[0, :S - 5], q[5:], rtol=0, atol=1e-13)
+    assert np.allclose(r5.k[0, :S - 5], k[5:], rtol=0, atol=1e-13)
+
+
+def test_oracle_rejects_bad_arguments():
+    x = np.zeros((1, 4, 6))
+    w = np.zeros((6, 10))
+    with pytest.raises(ValueError):   # F != ff + 3*H*hd
+        oracle.fused_proj(x, "tokens_last", w, "cf", None, 3, "none", 1, 2, rope=False)
+    w2 = np.zeros((6, 1 + 9))
+    with pytest.raises(ValueError):   # odd head_dim with RoPE
+        oracle.fused_proj(x, "tokens_last", w2, "cf", None, 1, "none", 1, 3, rope=True)
+    with pytest.raises(ValueError):   # token out of range
+        oracle.fused_proj(x, "tokens_last", w, "cf", None, 4, "none", 1, 2, rope=False, tokens=np.array([4]))
