@@ -1,0 +1,320 @@
+// C ABI of the fused input projection: descriptor checks, plan and RoPE table,
+// argument checks and the launch. The arithmetic all runs in the HIP kernels.
+#include "../../include/fused_proj.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "fused_proj_kernels.h"
+
+namespace {
+
+thread_local hipError_t g_last_hip = hipSuccess;
+thread_local char g_msg[256];
+
+constexpr int64_t kMaxOffset = int64_t(1) << 62;
+constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
+
+// a*b, or -1 when it would leave [0, kMaxOffset)
+int64_t mul_cap(int64_t a, int64_t b) {
+    if (a < 0 || b < 0) return -1;
+    if (a == 0 || b == 0) return 0;
+    if (a > kMaxOffset / b) return -1;
+    return a * b;
+}
+int64_t add_cap(int64_t a, int64_t b) {
+    if (a < 0 || b < 0 || a > kMaxOffset - b) return -1;
+    return a + b;
+}
+
+struct Derived {
+    int64_t S = 0, M = 0, F = 0, qw = 0, V = 8;
+    int64_t sb = 0, ss = 0, sc = 0;  // canonical strides: slab, token, channel
+    int64_t x_span = 0;              // 1 + largest element offset of x (0 when empty)
+};
+
+// Full descriptor check; fills the canonical strides on success.
+int check_desc(const fused_proj_desc* d, Derived* out) {
+    if (!d) return FUSED_PROJ_EINVAL;
+    if (d->dtype != FUSED_PROJ_BF16 && d->dtype != FUSED_PROJ_F32) return FUSED_PROJ_EINVAL;
+    if (d->x_layout != FUSED_PROJ_X_CHANNELS_FIRST && d->x_layout != FUSED_PROJ_X_TOKENS_LAST) return FUSED_PROJ_EINVAL;
+    if (d->w_layout != FUSED_PROJ_W_CF && d->w_layout != FUSED_PROJ_W_FC) return FUSED_PROJ_EINVAL;
+    if (d->ff_act != FUSED_PROJ_ACT_NONE && d->ff_act != FUSED_PROJ_ACT_GELU_ERF) return FUSED_PROJ_EINVAL;
+    if (d->batch < 0 || d->channels < 0 || d->ff_dim < 0 || d->n_heads < 0 || d->head_dim < 0) return FUSED_PROJ_EINVAL;
+    if ((d->n_heads > 0) != (d->head_dim > 0)) return FUSED_PROJ_EINVAL;
+    if (d->x_layout == FUSED_PROJ_X_TOKENS_LAST ? d->n_spatial != 1 : (d->n_spatial < 1 || d->n_spatial > 3))
+        return FUSED_PROJ_EINVAL;
+    if (d->x_stride_batch < 0 || d->x_stride_channel < 0) return FUSED_PROJ_EINVAL;
+    for (int i = 0; i < d->n_spatial; ++i)
+        if (d->spatial[i] < 0 || d->x_stride_spatial[i] < 0) return FUSED_PROJ_EINVAL;
+    if (d->pos_offset < 0) return FUSED_PROJ_EINVAL;
+    if (d->rope) {
+        if (d->head_dim % 2 != 0) return FUSED_PROJ_EINVAL;
+        if (!(d->rope_base > 0.0) || !std::isfinite(d->rope_base)) return FUSED_PROJ_EINVAL;
+    }
+    Derived r;
+    r.V = d->dtype == FUSED_PROJ_BF16 ? 8 : 4;
+    r.qw = mul_cap(d->n_heads, d->head_dim);
+    if (r.qw < 0 || r.qw > kMaxIndex) return FUSED_PROJ_EUNSUPPORTED;
+    r.F = add_cap(d->ff_dim, mul_cap(3, r.qw));
+    if (r.F == 0) return FUSED_PROJ_EINVAL;
+    if (r.F < 0 || r.F > kMaxIndex || d->channels > kMaxIndex) return FUSED_PROJ_EUNSUPPORTED;
+    int64_t S = 1;
+    for (int i = 0; i < d->n_spatial; ++i) {
+        S = mul_cap(S, d->spatial[i]);
+        if (S < 0) return FUSED_PROJ_EUNSUPPORTED;
+    }
+    r.S = S;
+    r.M = mul_cap(d->batch, S);
+    if (r.M < 0 || r.M > kMaxIndex || S > kMaxIndex) return FUSED_PROJ_EUNSUPPORTED;
+
+    // Supported shapes.
+    const int64_t V = r.V;
+    if (d->channels % V || d->ff_dim % V || d->head_dim % V) return FUSED_PROJ_EUNSUPPORTED;
+    if (d->rope && r.qw > 0) {
+        const int64_t hd = d->head_dim;
+        if ((hd / 2) % V) return FUSED_PROJ_EUNSUPPORTED;
+        if (128 % hd) return FUSED_PROJ_EUNSUPPORTED;         // a 128-column tile holds whole heads
+        if (d->ff_dim % hd) return FUSED_PROJ_EUNSUPPORTED;   // heads start on head boundaries
+        if (add_cap(S, d->pos_offset) < 0 || S + d->pos_offset > kMaxIndex) return FUSED_PROJ_EUNSUPPORTED;
+    }
+    // Canonical strides.
+    r.sb = d->x_stride_batch;
+    r.sc = d->x_stride_channel;
+    if (d->x_layout == FUSED_PROJ_X_TOKENS_LAST) {
+        r.ss = d->x_stride_spatial[0];
+        if (d->channels > 1 && r.sc != 1) return FUSED_PROJ_EUNSUPPORTED;
+        r.sc = 1;
+        if ((S > 1 && r.ss % V) || (d->batch > 1 && r.sb % V)) return FUSED_PROJ_EUNSUPPORTED;
+    } else {
+        // spatial dims must flatten into one unit-stride token index
+        int64_t expect = 1;
+        for (int i = d->n_spatial - 1; i >= 0; --i) {
+            if (d->spatial[i] > 1 && d->x_stride_spatial[i] != expect) return FUSED_PROJ_EUNSUPPORTED;
+            expect = mul_cap(expect, d->spatial[i]);
+            if (expect < 0) return FUSED_PROJ_EUNSUPPORTED;
+        }
+        r.ss = 1;
+        if (S % V || (d->channels > 1 && r.sc % V) || (d->batch > 1 && r.sb % V)) return FUSED_PROJ_EUNSUPPORTED;
+    }
+    // Offsets must stay below 2^62.
+    if (r.M > 0 && d->channels > 0) {
+        int64_t span = add_cap(mul_cap(d->batch - 1, r.sb), mul_cap(S - 1, r.ss));
+        span = add_cap(span, mul_cap(d->channels - 1, r.sc));
+        span = add_cap(span, 1);
+        if (span < 0) return FUSED_PROJ_EUNSUPPORTED;
+        r.x_span = span;
+    }
+    if (mul_cap(d->channels, r.F) < 0 || mul_cap(r.M, r.F) < 0) return FUSED_PROJ_EUNSUPPORTED;
+    // one workgroup per 128 x 128 output tile; the grid must fit a 31-bit count
+    if (mul_cap((r.M + 127) / 128, (r.F + 127) / 128) > kMaxIndex) return FUSED_PROJ_EUNSUPPORTED;
+    if (out) *out = r;
+    return FUSED_PROJ_OK;
+}
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+}  // namespace
+
+struct fused_proj_plan {
+    fused_proj_desc d;
+    Derived r;
+    fp::DType dt;
+    bool x_tl, w_fc;
+    fp::TilePlan tile;
+    fp::KernelArgs base;
+    float* d_cos = nullptr;
+    float* d_sin = nullptr;
+    int device = 0;
+    bool debug_sync = false;
+};
+
+extern "C" {
+
+int fused_proj_validate(const fused_proj_desc* desc) { return check_desc(desc, nullptr); }
+
+int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
+    if (!out) return FUSED_PROJ_EINVAL;
+    *out = nullptr;
+    Derived r;
+    int rc = check_desc(desc, &r);
+    if (rc) return rc;
+    fused_proj_plan* h = new (std::nothrow) fused_proj_plan();
+    if (!h) return FUSED_PROJ_EHIP;
+    h->d = *desc;
+    h->r = r;
+    h->dt = desc->dtype == FUSED_PROJ_BF16 ? fp::DType::BF16 : fp::DType::F32;
+    h->x_tl = desc->x_layout == FUSED_PROJ_X_TOKENS_LAST;
+    h->w_fc = desc->w_layout == FUSED_PROJ_W_FC;
+    h->tile = fp::TilePlan{128, 128, h->dt == fp::DType::BF16 ? 64 : 32, 8};
+    const char* dbg = std::getenv("FUSED_PROJ_DEBUG_SYNC");
+    h->debug_sync = dbg && dbg[0] == '1';
+    hipError_t e = hipGetDevice(&h->device);
+    if (e != hipSuccess) {
+        g_last_hip = e;
+        delete h;
+        return FUSED_PROJ_EHIP;
+    }
+
+    fp::KernelArgs& a = h->base;
+    std::memset(&a, 0, sizeof(a));
+    a.x_sb = r.sb;
+    a.x_ss = r.ss;
+    a.x_sc = r.sc;
+    a.M = r.M;
+    a.S = (int32_t)r.S;
+    a.K = (int32_t)desc->channels;
+    a.N = (int32_t)r.F;
+    a.ff_dim = (int32_t)desc->ff_dim;
+    a.n_heads = (int32_t)desc->n_heads;
+    a.head_dim = (int32_t)desc->head_dim;
+    a.qw = (int32_t)r.qw;
+    a.act = desc->ff_act == FUSED_PROJ_ACT_GELU_ERF ? 1 : 0;
+    a.rope = (desc->rope && r.qw > 0) ? 1 : 0;
+    a.tiles_m = (int32_t)((r.M + h->tile.bm - 1) / h->tile.bm);
+    a.tiles_n = (int32_t)((r.F + h->tile.bn - 1) / h->tile.bn);
+    a.group_m = h->tile.group_m;
+
+    if (a.rope && r.S > 0) {
+        // cos/sin of (s + pos_offset) * base^(-2i/hd), computed in float64, stored fp32
+        const int64_t half = desc->head_dim / 2;
+        const size_t n = (size_t)r.S * (size_t)half;
+        std::vector<float> hc(n), hs(n);
+        std::vector<double> theta((size_t)half);
+        for (int64_t i = 0; i < half; ++i)
+            theta[(size_t)i] = std::pow(desc->rope_base, -2.0 * (double)i / (double)desc->head_dim);
+        for (int64_t s = 0; s < r.S; ++s) {
+            const double p = (double)(s + desc->pos_offset);
+            for (int64_t i = 0; i < half; ++i) {
+                const double phi = p * theta[(size_t)i];
+                hc[(size_t)(s * half + i)] = (float)std::cos(phi);
+                hs[(size_t)(s * half + i)] = (float)std::sin(phi);
+            }
+        }
+        e = hipMalloc((void**)&h->d_cos, n * sizeof(float));
+        if (e == hipSuccess) e = hipMalloc((void**)&h->d_sin, n * sizeof(float));
+        if (e == hipSuccess) e = hipMemcpy(h->d_cos, hc.data(), n * sizeof(float), hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemcpy(h->d_sin, hs.data(), n * sizeof(float), hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            g_last_hip = e;
+            fused_proj_destroy(h);
+            return FUSED_PROJ_EHIP;
+        }
+    }
+    a.rope_cos = h->d_cos;
+    a.rope_sin = h->d_sin;
+    *out = h;
+    return FUSED_PROJ_OK;
+}
+
+int fused_proj_run(fused_proj_t h, const void* x, const void* w, const void* bias, void* ff, void* q, void* k,
+                   void* v, void* stream) {
+    if (!h) return FUSED_PROJ_EINVAL;
+    const Derived& r = h->r;
+    if (r.M == 0) return FUSED_PROJ_OK;  // no tokens: nothing to do
+    const bool need_xw = h->d.channels > 0;
+    if (need_xw && (!x || !w)) return FUSED_PROJ_EINVAL;
+    if (h->d.has_bias && !bias) return FUSED_PROJ_EINVAL;
+    if (h->d.ff_dim > 0 && !ff) return FUSED_PROJ_EINVAL;
+    if (r.qw > 0 && (!q || !k || !v)) return FUSED_PROJ_EINVAL;
+    const void* ptrs[] = {need_xw ? x : nullptr, need_xw ? w : nullptr, h->d.has_bias ? bias : nullptr,
+                          h->d.ff_dim > 0 ? ff : nullptr, r.qw > 0 ? q : nullptr, r.qw > 0 ? k : nullptr,
+                          r.qw > 0 ? v : nullptr};
+    for (const void* p : ptrs)
+        if (p && (reinterpret_cast<uintptr_t>(p) & 15u)) return FUSED_PROJ_EALIGN;
+
+    // Outputs may overlap neither each other nor an input.
+    const uintptr_t es = h->dt == fp::DType::BF16 ? 2 : 4;
+    std::vector<Range> ins, outs;
+    if (need_xw) {
+        ins.push_back({(uintptr_t)x, (uintptr_t)x + (uintptr_t)r.x_span * es});
+        ins.push_back({(uintptr_t)w, (uintptr_t)w + (uintptr_t)(h->d.channels * r.F) * es});
+    }
+    if (h->d.has_bias) ins.push_back({(uintptr_t)bias, (uintptr_t)bias + (uintptr_t)r.F * es});
+    if (h->d.ff_dim > 0) outs.push_back({(uintptr_t)ff, (uintptr_t)ff + (uintptr_t)(r.M * h->d.ff_dim) * es});
+    if (r.qw > 0)
+        for (void* p : {q, k, v}) outs.push_back({(uintptr_t)p, (uintptr_t)p + (uintptr_t)(r.M * r.qw) * es});
+    for (size_t i = 0; i < outs.size(); ++i) {
+        for (size_t j = i + 1; j < outs.size(); ++j)
+            if (overlap(outs[i], outs[j])) return FUSED_PROJ_EALIAS;
+        for (const Range& in : ins)
+            if (overlap(outs[i], in)) return FUSED_PROJ_EALIAS;
+    }
+
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip = e;
+        return FUSED_PROJ_EHIP;
+    }
+    if (dev != h->device) return FUSED_PROJ_EINVAL;
+
+    fp::KernelArgs a = h->base;
+    a.x = x;
+    a.w = w;
+    a.bias = h->d.has_bias ? bias : nullptr;
+    a.ff = ff;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    e = fp::launch_fused_proj(h->dt, h->x_tl, h->w_fc, h->tile, a, s);
+    if (e == hipSuccess && h->debug_sync) {
+        e = hipStreamSynchronize(s);
+        if (e == hipSuccess) e = hipGetLastError();
+    }
+    if (e != hipSuccess) {
+        g_last_hip = e;
+        return FUSED_PROJ_EHIP;
+    }
+    return FUSED_PROJ_OK;
+}
+
+int fused_proj_destroy(fused_proj_t h) {
+    if (!h) return FUSED_PROJ_OK;
+    hipError_t e1 = h->d_cos ? hipFree(h->d_cos) : hipSuccess;
+    hipError_t e2 = h->d_sin ? hipFree(h->d_sin) : hipSuccess;
+    delete h;
+    if (e1 != hipSuccess || e2 != hipSuccess) {
+        g_last_hip = e1 != hipSuccess ? e1 : e2;
+        return FUSED_PROJ_EHIP;
+    }
+    return FUSED_PROJ_OK;
+}
+
+const char* fused_proj_strerror(int code) {
+    switch (code) {
+        case FUSED_PROJ_OK: return "success";
+        case FUSED_PROJ_EINVAL: return "invalid argument";
+        case FUSED_PROJ_EUNSUPPORTED: return "unsupported shape, layout or stride";
+        case FUSED_PROJ_EALIGN: return "device pointer not 16-byte aligned";
+        case FUSED_PROJ_EALIAS: return "output overlaps another output or an input";
+        case FUSED_PROJ_EHIP:
+            std::snprintf(g_msg, sizeof(g_msg), "HIP error: %s", hipGetErrorString(g_last_hip));
+            return g_msg;
+        default: return "unknown status code";
+    }
+}
+
+int fused_proj_describe(fused_proj_t h, char* buf, size_t len) {
+    if (!h || !buf || len == 0) return FUSED_PROJ_EINVAL;
+    std::snprintf(buf, len,
+                  "kernel=fused_proj_tile_kernel dtype=%s x=%s w=%s tile=%dx%dx%d group_m=%d grid=%d "
+                  "M=%lld K=%lld N=%lld",
+                  h->dt == fp::DType::BF16 ? "bf16" : "f32", h->x_tl ? "tokens_last" : "channels_first",
+                  h->w_fc ? "FC" : "CF", h->tile.bm, h->tile.bn, h->tile.bk, h->tile.group_m,
+                  h->base.tiles_m * h->base.tiles_n, (long long)h->r.M, (long long)h->d.channels,
+                  (long long)h->r.F);
+    return FUSED_PROJ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal interface between the C-ABI layer and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp {
+
+// Everything a launch needs, passed by value as the kernel argument.
+struct KernelArgs {
+    const void* x;       // activation (storage type)
+    const void* w;       // weight [C,F] or [F,C]
+    const void* bias;    // [F] or nullptr
+    void* ff;            // [b, S, ff_dim]
+    void* q;             // [b*H, S, hd]
+    void* k;
+    void* v;
+    const float* rope_cos;  // [S, hd/2] fp32, row s holds angle (s + pos_offset) * theta_i
+    const float* rope_sin;
+    int64_t x_sb;        // element stride between slabs
+    int64_t x_ss;        // element stride between consecutive tokens of a slab
+    int64_t x_sc;        // element stride between channels
+    int64_t M;           // tokens = b * S
+    int32_t S;           // tokens per slab
+    int32_t K;           // channels (contraction length)
+    int32_t N;           // fused columns F
+    int32_t ff_dim;
+    int32_t n_heads;
+    int32_t head_dim;
+    int32_t qw;          // n_heads * head_dim
+    int32_t act;         // 0 none, 1 exact-erf GELU on the ff slice
+    int32_t rope;        // 1: RoPE on q and k
+    int32_t tiles_m;
+    int32_t tiles_n;
+    int32_t group_m;     // tile rows per raster group
+};
+
+// Tile plan chosen on the host.
+struct TilePlan {
+    int bm, bn, bk;
+    int group_m;         // tiles along M that share a column sweep (L2 reuse)
+};
+
+// Kernel variants: storage type x activation layout x weight layout.
+enum class DType { BF16 = 0, F32 = 1 };
+
+// Launches one fused projection. Returns hipSuccess or the launch error.
+hipError_t launch_fused_proj(DType dt, bool x_tokens_last, bool w_fc, const TilePlan& plan,
+                             const KernelArgs& args, hipStream_t stream);
+
+// Whether a tile plan is compiled for this combination.
+bool plan_supported(DType dt, const TilePlan& plan);
+
+}  // namespace fp

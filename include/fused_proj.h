@@ -1,0 +1,166 @@
+/*
+ * fused_proj.h — C ABI of the MI355X (gfx950) fused input projection.
+ *
+ * The operation (one call = one kernel launch):
+ *
+ *   For every token t = bi*S + s of a batch of activations, gather its row
+ *   x[t, 0..C) straight from a channels-first [b, c, spatial...] or a
+ *   token-major [b, s, c] tensor (no rearranged copy), and compute
+ *
+ *     y[t, f] = sum_c x[t, c] * W[c, f] + bias[f],        f in [0, F)
+ *
+ *   as one [tokens, C] x [C, F] product. The columns split, in this order,
+ *   into an ff slice [0, ff_dim), then q, k and v slices of n_heads*head_dim
+ *   columns each (head h, element j at slice column h*head_dim + j):
+ *
+ *     ff[bi, s, f]            = act(y[t, f])                    act: none | exact-erf GELU
+ *     q[bi*H + h, s, j]       = RoPE_p(y[t, Q0 + h*hd + .])[j]  p = s + pos_offset
+ *     k[bi*H + h, s, j]       = RoPE_p(y[t, K0 + h*hd + .])[j]
+ *     v[bi*H + h, s, j]       = y[t, V0 + h*hd + j]
+ *
+ *   RoPE is rotate-half: for i < hd/2, with phi = p * base^(-2i/hd),
+ *     out[i]        = y[i] cos(phi) - y[i + hd/2] sin(phi)
+ *     out[i + hd/2] = y[i + hd/2] cos(phi) + y[i] sin(phi).
+ *   Accumulation, bias, GELU and RoPE run in fp32; each output is rounded once
+ *   to the storage type (round to nearest even).
+ *
+ * Where each part is defined:
+ *   - gather + single GEMM instead of one GEMV per token: Walrus PR
+ *     "Make fused_ff_qkv contiguous", first comment (the rearrange from
+ *     channels-first to channels-last and the [tokens, fused_dims] product);
+ *   - y = act(x W^T + b), and the attention projection as the same op with no
+ *     activation written into three buffers: xformers PR "Fused linear: small
+ *     FW cleanup and much better perfs", description and follow-up comments;
+ *   - the ff, q, k, v split of the fused output: Walrus PR, second comment;
+ *   - head-major [batch*heads, tokens, head_dim] buffers: memory-efficient-
+ *     attention issue "Improve performance via batched-matmul and fused
+ *     multiplies", first comment;
+ *   - rotate-half RoPE: NVIDIA/Fuser issue "Improve performance on RoPE (and
+ *     code around it)", rope_one_entry in the thunder example. The angle
+ *     convention base^(-2i/hd) is the textbook one (the page's tables are
+ *     random numbers).
+ *
+ * Threading: a handle may be used from several host threads and streams at
+ * once; fused_proj_run only reads it. Create and destroy are not concurrent
+ * with runs on the same handle.
+ */
+#ifndef FUSED_PROJ_H
+#define FUSED_PROJ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (every call returns one; 0 is success). */
+#define FUSED_PROJ_OK 0
+#define FUSED_PROJ_EINVAL (-1)       /* malformed descriptor or argument (NULL, negative size, F mismatch) */
+#define FUSED_PROJ_EUNSUPPORTED (-2) /* well formed, but outside what the kernels handle (see validate) */
+#define FUSED_PROJ_EALIGN (-3)       /* a device pointer is not 16-byte aligned */
+#define FUSED_PROJ_EALIAS (-4)       /* an output overlaps another output or an input */
+#define FUSED_PROJ_EHIP (-5)         /* a HIP runtime call failed (allocation, copy, launch) */
+
+/* Storage type of x, W, bias and every output. Accumulation is always fp32. */
+#define FUSED_PROJ_BF16 0
+#define FUSED_PROJ_F32 1
+
+/* Activation layout. */
+#define FUSED_PROJ_X_CHANNELS_FIRST 0 /* [b, c, spatial...]: tokens are the row-major flattening of the
+                                         1-3 spatial dims; channel c of token s is x_stride_channel apart */
+#define FUSED_PROJ_X_TOKENS_LAST 1    /* [b, s, c]: one spatial dim (s); channels contiguous */
+
+/* Weight layout (both dense, row-major). */
+#define FUSED_PROJ_W_CF 0 /* W[C, F]: W[c*F + f] */
+#define FUSED_PROJ_W_FC 1 /* W[F, C] (torch nn.Linear weight, y = x W^T): W[f*C + c] */
+
+/* Activation on the ff slice. */
+#define FUSED_PROJ_ACT_NONE 0
+#define FUSED_PROJ_ACT_GELU_ERF 1 /* 0.5 y (1 + erf(y / sqrt 2)) */
+
+typedef struct fused_proj_desc {
+    int32_t dtype;             /* FUSED_PROJ_BF16 | FUSED_PROJ_F32 */
+    int32_t x_layout;          /* FUSED_PROJ_X_* */
+    int64_t batch;             /* b >= 1 (slabs; time steps may be folded in) */
+    int64_t channels;          /* C >= 1, the contraction length */
+    int32_t n_spatial;         /* 1..3 for channels-first, exactly 1 for tokens-last */
+    int64_t spatial[3];        /* sizes of the spatial dims; S = their product */
+    int64_t x_stride_batch;    /* element strides of x, all >= 0 */
+    int64_t x_stride_channel;
+    int64_t x_stride_spatial[3];
+    int32_t w_layout;          /* FUSED_PROJ_W_* */
+    int32_t has_bias;          /* 1: bias[F] (storage type) is added to every column */
+    int64_t ff_dim;            /* width of the ff slice, >= 0 */
+    int32_t ff_act;            /* FUSED_PROJ_ACT_* */
+    int64_t n_heads;           /* H >= 0; q, k, v each hold H*head_dim columns */
+    int64_t head_dim;          /* hd >= 0 */
+    int32_t rope;              /* 1: rotate-half RoPE on q and k */
+    double rope_base;          /* > 0; 10000 is customary */
+    int64_t pos_offset;        /* >= 0; position of token s is s + pos_offset */
+} fused_proj_desc;
+
+typedef struct fused_proj_plan *fused_proj_t;
+
+/*
+ * Checks a descriptor on the host; touches no GPU and allocates nothing.
+ * Returns FUSED_PROJ_OK, FUSED_PROJ_EINVAL (malformed: a size < 0, F = ff_dim +
+ * 3*H*hd == 0, n_spatial out of range, unknown enum, odd hd with RoPE, base <= 0)
+ * or FUSED_PROJ_EUNSUPPORTED. Supported, with V = 8 for bf16 and 4 for fp32:
+ *   C, ff_dim and head_dim multiples of V; with RoPE, head_dim/2 a multiple of V,
+ *   head_dim <= 256 and ff_dim a multiple of head_dim;
+ *   channels-first: spatial strides that flatten into one unit-stride token
+ *   index (stride of the last spatial dim 1, each outer stride the product of the
+ *   inner sizes), S, x_stride_channel and x_stride_batch multiples of V;
+ *   tokens-last: x_stride_channel 1, token and batch strides multiples of V;
+ *   every element offset of x, W and the outputs below 2^62.
+ */
+int fused_proj_validate(const fused_proj_desc *desc);
+
+/*
+ * Validates, picks the kernel and tile plan, and (with RoPE) builds the cos/sin
+ * table for positions pos_offset .. pos_offset+S-1 in float64, rounds it to fp32
+ * and uploads it to the current HIP device (synchronous; this is the only call
+ * that allocates or synchronises). On success *out owns that table.
+ * Errors: as validate, FUSED_PROJ_EINVAL for out == NULL, FUSED_PROJ_EHIP.
+ */
+int fused_proj_create(const fused_proj_desc *desc, fused_proj_t *out);
+
+/*
+ * Enqueues the projection on `stream` (a hipStream_t; NULL = the legacy default
+ * stream of the current device) and returns without waiting. Allocates nothing
+ * and never synchronises, so it may be captured into a HIP graph.
+ *
+ *   x     device, storage type, laid out as the descriptor says
+ *   w     device, [C,F] or [F,C] dense
+ *   bias  device [F] when has_bias, else ignored (may be NULL)
+ *   ff    device [b, S, ff_dim] dense token-major; required when ff_dim > 0
+ *   q,k,v device [b*H, S, hd] dense head-major; required when H*hd > 0
+ * The caller owns every buffer and keeps them alive until the work completes.
+ * Every pointer must be 16-byte aligned (FUSED_PROJ_EALIGN); outputs may not
+ * overlap each other or any input (FUSED_PROJ_EALIAS); a NULL required pointer
+ * is FUSED_PROJ_EINVAL. A failed launch returns FUSED_PROJ_EHIP; faults inside
+ * the kernel surface at the caller's next synchronisation, as for any launch.
+ * With FUSED_PROJ_DEBUG_SYNC=1 in the environment the call synchronises the
+ * stream and reports kernel errors as FUSED_PROJ_EHIP (debugging only).
+ */
+int fused_proj_run(fused_proj_t plan, const void *x, const void *w, const void *bias, void *ff, void *q,
+                   void *k, void *v, void *stream);
+
+/* Frees the plan and its table. NULL is accepted. Not concurrent with runs in flight
+ * on the plan: synchronise their streams first. */
+int fused_proj_destroy(fused_proj_t plan);
+
+/* Human-readable text for a status code (static storage). For FUSED_PROJ_EHIP the
+ * text of the last HIP error seen by this library on the calling thread follows. */
+const char *fused_proj_strerror(int code);
+
+/* Writes a one-line description of the chosen kernel and tiling into buf
+ * (NUL-terminated, truncated to len). Returns FUSED_PROJ_OK or FUSED_PROJ_EINVAL. */
+int fused_proj_describe(fused_proj_t plan, char *buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FUSED_PROJ_H */

@@ -1,0 +1,123 @@
+"""Per-element parity bar between the GPU outputs and the float64 oracle.
+
+TEST INFRASTRUCTURE ONLY (used by the tests, the smoke check and the
+benchmark's CPU-baseline leg).
+
+The bar: |gpu - oracle| <= rel * scale, element by element, with
+scale = ||x_t|| * ||w_col|| + |b_col|, rel = 4e-3 for bf16 storage and 1e-5
+for fp32. For q/k elements after RoPE the output is itself a projection with
+the effective column w_eff = cos(phi) W[:, j] -/+ sin(phi) W[:, j'] (and the
+same mix of biases), since RoPE is linear; its norm is used. For GELU outputs
+the pre-activation scale is used (GELU is 1.13-Lipschitz).
+
+A second, tighter diagnostic bar is also reported for bf16: the output's own
+rounding (2^-8 relative) plus 1e-4 * scale of accumulation error.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+REL = {"bf16": 4e-3, "f32": 1e-5}
+
+
+def token_rows(x64: np.ndarray, layout: str, tokens: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Rows x[t, :] (float64) and in-slab positions s for the given global tokens."""
+    if layout == "channels_first":
+        nb, C = x64.shape[0], x64.shape[1]
+        S = int(np.prod(x64.shape[2:]))
+        xf = x64.reshape(nb, C, S)
+        bi, s = np.divmod(tokens, S)
+        rows = xf[bi, :, s]
+    else:
+        nb, S, C = x64.shape
+        bi, s = np.divmod(tokens, S)
+        rows = x64[bi, s, :]
+    return np.ascontiguousarray(rows), s
+
+
+@dataclass
+class Scales:
+    ff: np.ndarray | None   # [n, FF]
+    q: np.ndarray | None    # [n, H, hd]
+    k: np.ndarray | None
+    v: np.ndarray | None
+
+
+def scales(rows: np.ndarray, positions: np.ndarray, w_cf: np.ndarray, bias: np.ndarray | None, ff_dim: int,
+           n_heads: int, head_dim: int, rope: bool, rope_base: float = 10000.0, pos_offset: int = 0) -> Scales:
+    """Per-element scale for tokens with gathered rows [n, C]; w_cf is W as [C, F]."""
+    n = rows.shape[0]
+    F = w_cf.shape[1]
+    xn = np.linalg.norm(rows, axis=1)                         # [n]
+    wn = np.linalg.norm(w_cf, axis=0)                         # [F]
+    b = np.zeros(F) if bias is None else np.asarray(bias, dtype=np.float64)
+    plain = xn[:, None] * wn[None, :] + np.abs(b)[None, :]    # [n, F]
+    ff = plain[:, :ff_dim] if ff_dim > 0 else None
+    qw = n_heads * head_dim
+    if qw == 0:
+        return Scales(ff, None, None, None)
+    out = []
+    for which in range(3):
+        off = ff_dim + which * qw
+        s_plain = plain[:, off:off + qw].reshape(n, n_heads, head_dim)
+        if not (rope and which < 2):
+            out.append(s_plain)
+            continue
+        half = head_dim // 2
+        Wh = w_cf[:, off:off + qw].reshape(-1, n_heads, head_dim)
+        bh = b[off:off + qw].reshape(n_heads, head_dim)
+        w1, w2 = Wh[:, :, :half], Wh[:, :, half:]             # [C, H, half]
+        n1, n2 = (w1 ** 2).sum(0), (w2 ** 2).sum(0)            # [H, half]
+        d12 = (w1 * w2).sum(0)
+        theta = rope_base ** (-2.0 * np.arange(half) / head_dim)
+        phi = (positions.astype(np.float64) + pos_offset)[:, None] * theta[None, :]   # [n, half]
+        c, s = np.cos(phi)[:, None, :], np.sin(phi)[:, None, :]                     # [n, 1, half]
+        # first half: c w1 - s w2 ; second half: c w2 + s w1
+        e1 = np.sqrt(np.maximum(c * c * n1 + s * s * n2 - 2 * c * s * d12, 0.0))
+        e2 = np.sqrt(np.maximum(c * c * n2 + s * s * n1 + 2 * c * s * d12, 0.0))
+        b1 = np.abs(c * bh[None, :, :half] - s * bh[None, :, half:])
+        b2 = np.abs(c * bh[None, :, half:] + s * bh[None, :, :half])
+        sc = np.concatenate([xn[:, None, None] * e1 + b1, xn[:, None, None] * e2 + b2], axis=2)
+        out.append(sc)
+    return Scales(ff, out[0], out[1], out[2])
+
+
+@dataclass
+class Verdict:
+    ok: bool
+    max_ratio: float        # max |err| / (rel * scale); <= 1 passes the bar
+    max_tight_ratio: float  # diagnostic bar (bf16 only; equals max_ratio for fp32)
+    max_abs_err: float
+    n: int
+
+    def __str__(self):
+        return (f"ok={self.ok} max_err/tol={self.max_ratio:.3g} tight={self.max_tight_ratio:.3g} "
+                f"max_abs_err={self.max_abs_err:.3g} n={self.n}")
+
+
+def compare(got: list, ref: list, scl: list, dtype: str) -> Verdict:
+    """got/ref/scl: matching lists of arrays (None entries skipped)."""
+    rel = REL[dtype]
+    mr, mt, ma, n = 0.0, 0.0, 0.0, 0
+    finite = True
+    for g, r, s in zip(got, ref, scl):
+        if r is None:
+            continue
+        g = np.asarray(g, dtype=np.float64)
+        err = np.abs(g - r)
+        finite &= bool(np.all(np.isfinite(g)))
+        ratio = err / (rel * s + 1e-300)
+        mr = max(mr, float(np.max(ratio)) if ratio.size else 0.0)
+        if dtype == "bf16":
+            tight = err / (2.0 ** -8 * np.abs(r) + 1e-4 * s + 1e-300)
+        else:
+            tight = ratio
+        mt = max(mt, float(np.max(tight)) if tight.size else 0.0)
+        ma = max(ma, float(np.max(err)) if err.size else 0.0)
+        n += g.size
+    if not finite:
+        mr = mt = math.inf
+    return Verdict(finite and mr <= 1.0, mr, mt, ma, n)

@@ -1,0 +1,131 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and the host-only descriptor check returns the documented codes."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import ff_input_projection_amd as fpa
+from ff_input_projection_amd import Desc, make_desc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fused_proj.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fused_proj_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fpa.load_library()
+    decl = declared_functions()
+    assert set(decl) == set(fpa.EXPORTED_SYMBOLS), decl
+    for name in decl:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fpa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (fused_proj_\w+)", out))
+    assert set(decl) <= exported
+
+
+def test_header_compiles_as_plain_c():
+    src = '#include "fused_proj.h"\nint main(void){ fused_proj_desc d; (void)d; return 0; }\n'
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        "-x", "c", "-", "-fsyntax-only"], input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_desc_struct_layout_matches_c():
+    src = ('#include <stdio.h>\n#include <stddef.h>\n#include "fused_proj.h"\n'
+           'int main(void){printf("%zu %zu %zu %zu\\n", sizeof(fused_proj_desc), '
+           'offsetof(fused_proj_desc, rope_base), offsetof(fused_proj_desc, x_stride_spatial), '
+           'offsetof(fused_proj_desc, pos_offset)); return 0;}\n')
+    exe = os.path.join("/tmp", f"fp_desc_layout_{os.getpid()}")
+    r = subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), "-x", "c", "-", "-o", exe],
+                       input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    vals = list(map(int, subprocess.run([exe], capture_output=True, text=True).stdout.split()))
+    os.remove(exe)
+    assert vals == [ctypes.sizeof(Desc), Desc.rope_base.offset, Desc.x_stride_spatial.offset,
+                    Desc.pos_offset.offset]
+
+
+def walrus_desc(**kw):
+    import torch
+    shape = (24, 768, 32, 32, 1)
+    strides = (768 * 1024, 1024, 32, 1, 1)
+    base = dict(w_layout="cf", has_bias=True, ff_dim=3072, ff_act="gelu", n_heads=12, head_dim=64, rope=True)
+    base.update(kw)
+    return make_desc(shape, strides, "channels_first", torch.bfloat16, **base)
+
+
+def test_validate_accepts_all_benchmark_workloads():
+    import torch
+    from ff_input_projection_amd.workloads import WORKLOADS
+    for wl in WORKLOADS.values():
+        t = torch.empty(wl.x_shape, dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, device="meta")
+        d = make_desc(t.shape, t.stride(), wl.layout, t.dtype, w_layout=wl.w_layout, has_bias=wl.has_bias,
+                      ff_dim=wl.ff_dim, ff_act=wl.ff_act, n_heads=wl.n_heads, head_dim=wl.head_dim, rope=wl.rope)
+        assert fpa.validate(d) == fpa.OK, wl.name
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda d: setattr(d, "dtype", 7), fpa.EINVAL),
+    (lambda d: setattr(d, "x_layout", 5), fpa.EINVAL),
+    (lambda d: setattr(d, "w_layout", 2), fpa.EINVAL),
+    (lambda d: setattr(d, "ff_act", 9), fpa.EINVAL),
+    (lambda d: setattr(d, "batch", -1), fpa.EINVAL),
+    (lambda d: setattr(d, "n_spatial", 4), fpa.EINVAL),
+    (lambda d: setattr(d, "head_dim", 0), fpa.EINVAL),             # heads without width
+    (lambda d: (setattr(d, "ff_dim", 0), setattr(d, "n_heads", 0), setattr(d, "head_dim", 0)), fpa.EINVAL),
+    (lambda d: setattr(d, "rope_base", 0.0), fpa.EINVAL),
+    (lambda d: setattr(d, "pos_offset", -3), fpa.EINVAL),
+    (lambda d: setattr(d, "x_stride_channel", -1024), fpa.EINVAL),
+    (lambda d: setattr(d, "channels", 764), fpa.EUNSUPPORTED),      # C not a multiple of 8 (bf16)
+    (lambda d: setattr(d, "ff_dim", 3076), fpa.EUNSUPPORTED),       # ff not a multiple of 8
+    (lambda d: setattr(d, "ff_dim", 3104), fpa.EUNSUPPORTED),       # ff not a multiple of hd (RoPE)
+    (lambda d: setattr(d, "head_dim", 24), fpa.EUNSUPPORTED),       # hd/2 not a multiple of 8
+    (lambda d: setattr(d, "head_dim", 96), fpa.EUNSUPPORTED),       # a 128-wide tile cannot hold whole heads
+    (lambda d: d.x_stride_spatial.__setitem__(0, 33), fpa.EUNSUPPORTED),  # spatial dims do not flatten
+    (lambda d: setattr(d, "x_stride_channel", 1020), fpa.EUNSUPPORTED),   # misaligned channel stride
+    (lambda d: setattr(d, "batch", 1 << 22), fpa.EUNSUPPORTED),     # more than 2^31 tokens
+])
+def test_validate_error_codes(mutate, code):
+    d = walrus_desc()
+    assert fpa.validate(d) == fpa.OK
+    mutate(d)
+    assert fpa.validate(d) == code
+
+
+def test_validate_accepts_edge_shapes():
+    import torch
+    # odd head_dim is fine without RoPE only if it is a multiple of 8; hd=24 without RoPE is supported
+    d = walrus_desc(rope=False, head_dim=24, ff_dim=3072)
+    assert fpa.validate(d) == fpa.OK
+    # empty batch: a valid no-op
+    d = walrus_desc()
+    d.batch = 0
+    assert fpa.validate(d) == fpa.OK
+    # fp32 allows 4-wide vectors: hd 8 with RoPE
+    d = make_desc((1, 32, 8, 8, 1), (2048, 64, 8, 1, 1), "channels_first", torch.float32, has_bias=True,
+                  ff_dim=128, ff_act="gelu", n_heads=4, head_dim=8, rope=True)
+    assert fpa.validate(d) == fpa.OK
+    # token-major with a row stride larger than C (a channel slice of a wider tensor)
+    d = make_desc((2, 100, 64), (100 * 96, 96, 1), "tokens_last", torch.bfloat16, ff_dim=64)
+    assert fpa.validate(d) == fpa.OK
+
+
+def test_null_handles_and_strerror():
+    lib = fpa.load_library()
+    assert lib.fused_proj_validate(None) == fpa.EINVAL
+    assert lib.fused_proj_destroy(None) == fpa.OK
+    assert lib.fused_proj_run(None, None, None, None, None, None, None, None, None) == fpa.EINVAL
+    assert lib.fused_proj_create(ctypes.byref(walrus_desc()), None) == fpa.EINVAL
+    buf = ctypes.create_string_buffer(16)
+    assert lib.fused_proj_describe(None, buf, 16) == fpa.EINVAL
+    for code in (0, -1, -2, -3, -4):
+        assert len(fpa.strerror(code)) > 3
+    assert "unknown" in fpa.strerror(42)

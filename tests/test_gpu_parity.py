@@ -1,0 +1,204 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle, per element.
+
+Bar (stated for the fused projection): |gpu - oracle| <= 4e-3 * (||x_t|| ||w_col|| + |b|)
+for bf16 and 1e-5 * the same scale for fp32, with the RoPE-effective column for q/k
+(see oracle/compare.py). Full-size workloads are checked on sampled tokens (ends,
+slab and tile boundaries, random); small shapes that span several tiles with
+ragged tails are checked on every token.
+"""
+import numpy as np
+import pytest
+import torch
+
+from ff_input_projection_amd import FusedProjError, EALIAS, EALIGN, EINVAL
+from ff_input_projection_amd.workloads import WORKLOADS, make_inputs, with_shape
+
+from helpers import all_tokens, plan_for, run_gpu, sample_tokens, verdict
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _check(wl, inp, outs, tokens, label):
+    v = verdict(wl, inp, outs, tokens)
+    print(f"[parity] {label}: {v}", flush=True)
+    assert v.ok, f"{label}: {v}"
+    assert v.max_tight_ratio <= 1.0, f"{label} (tight bar): {v}"
+    return v
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_full_size_sampled(name):
+    wl = WORKLOADS[name]
+    print(f"[case] full-size {name}", flush=True)
+    inp = make_inputs(wl)
+    proj, outs = run_gpu(wl, inp, DEV)
+    print(f"[plan] {proj.describe()}", flush=True)
+    tokens = all_tokens(wl) if wl.M <= 4096 else sample_tokens(wl, 384, seed=1)
+    _check(wl, inp, outs, tokens, name)
+    # every output element was written (outputs come from torch.empty; catch NaN/garbage)
+    for t in outs:
+        if t is not None:
+            assert torch.isfinite(t).all().item()
+
+
+SMALL = [
+    # channels-first, RoPE, GELU, ragged M (120 tokens), K tail (72), 3 column tiles with a ragged last one
+    with_shape(WORKLOADS["walrus_bf16"], "cf_rope_ragged", x_shape=(3, 72, 5, 8, 1), ff_dim=64, n_heads=3,
+               head_dim=32, seed=101),
+    # token-major, [F,C] weight, RoPE hd 16, ragged everything
+    with_shape(WORKLOADS["bert_qkv_bf16"], "tl_fc_rope", x_shape=(2, 77, 80), ff_dim=48, ff_act="gelu",
+               n_heads=2, head_dim=16, rope=True, w_layout="fc", seed=102),
+    # channels-first, [F,C] weight, no bias, hd 128, pos_offset
+    with_shape(WORKLOADS["walrus_bf16"], "cf_fc_hd128_offset", x_shape=(2, 136, 6, 20), ff_dim=128,
+               n_heads=2, head_dim=128, has_bias=False, w_layout="fc", pos_offset=7, seed=103),
+    # token-major, [C,F] weight, ff only, K = 8 (one chunk), 9 tokens
+    with_shape(WORKLOADS["bert_ff_bf16"], "tl_tiny_k", x_shape=(1, 9, 8), ff_dim=24, seed=104),
+    # several M tiles, hd 64 without RoPE, 3 heads (192 columns per slice)
+    with_shape(WORKLOADS["smallk_qkv_bf16"], "cf_smallk_multitile", x_shape=(2, 64, 16, 24), n_heads=3,
+               seed=105),
+    # fp32, token-major, [F,C], RoPE hd 8, GELU
+    with_shape(WORKLOADS["tiny_f32"], "f32_tl_fc", layout="tokens_last", x_shape=(3, 50, 36), ff_dim=16,
+               n_heads=3, head_dim=8, w_layout="fc", seed=106),
+    # fp32, channels-first, several tiles
+    with_shape(WORKLOADS["tiny_f32"], "f32_cf_multitile", x_shape=(2, 68, 10, 16, 1), ff_dim=136,
+               n_heads=5, head_dim=8, seed=107),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_small_ragged_all_tokens(wl):
+    print(f"[case] small {wl.name} x={wl.x_shape}", flush=True)
+    inp = make_inputs(wl)
+    _, outs = run_gpu(wl, inp, DEV)
+    _check(wl, inp, outs, all_tokens(wl), wl.name)
+
+
+def test_strided_views_channel_slice_and_row_stride():
+    """x as a view: a channel slice of a wider channels-first tensor, and a token-major
+    view whose row stride exceeds C. No copy is made; results match the oracle."""
+    wl = with_shape(WORKLOADS["walrus_bf16"], "cf_view", x_shape=(2, 48, 8, 16, 1), ff_dim=64, n_heads=2,
+                    head_dim=32, seed=201)
+    inp = make_inputs(wl)
+    big = torch.zeros((2, 64, 8, 16, 1), dtype=torch.bfloat16)
+    big[:, 8:56] = inp.x
+    xv = big.to(DEV)[:, 8:56]
+    assert not xv.is_contiguous()
+    _, outs = run_gpu(wl, inp, DEV, x_dev=xv)
+    _check(wl, inp, outs, all_tokens(wl), "channel-slice view")
+
+    wl2 = with_shape(WORKLOADS["bert_qkv_bf16"], "tl_view", x_shape=(3, 40, 64), n_heads=2, head_dim=32,
+                     seed=202)
+    inp2 = make_inputs(wl2)
+    wide = torch.zeros((3, 40, 96), dtype=torch.bfloat16)
+    wide[:, :, :64] = inp2.x
+    xv2 = wide.to(DEV)[:, :, :64]
+    _, outs2 = run_gpu(wl2, inp2, DEV, x_dev=xv2)
+    _check(wl2, inp2, outs2, all_tokens(wl2), "row-stride view")
+
+
+def test_layout_invariance_on_gpu():
+    """Channels-first input and its channels-last copy give the same outputs."""
+    wl = with_shape(WORKLOADS["walrus_bf16"], "inv", x_shape=(2, 64, 8, 16, 1), ff_dim=64, n_heads=2,
+                    head_dim=32, seed=301)
+    inp = make_inputs(wl)
+    _, o1 = run_gpu(wl, inp, DEV)
+    xl = inp.x.permute(0, 2, 3, 4, 1).reshape(2, 128, 64).contiguous()
+    wl2 = with_shape(wl, "inv_tl", layout="tokens_last", x_shape=(2, 128, 64))
+    _, o2 = run_gpu(wl2, inp, DEV, x_dev=xl.to(DEV))
+    for a, b in zip(o1, o2):
+        if a is not None:
+            assert torch.equal(a, b)
+
+
+def test_determinism_bitwise():
+    wl = WORKLOADS["bert_qkv_bf16"]
+    inp = make_inputs(wl)
+    x, w, b = inp.x.to(DEV), inp.w.to(DEV), inp.bias.to(DEV)
+    proj = plan_for(wl, x)
+    o1 = [t.clone() for t in proj(x, w, b) if t is not None]
+    o2 = [t for t in proj(x, w, b) if t is not None]
+    torch.cuda.synchronize()
+    for a, c in zip(o1, o2):
+        assert torch.equal(a, c)
+
+
+def test_canary_guard_bands_untouched():
+    """Outputs live inside larger NaN-filled buffers: every output element is written,
+    nothing outside is."""
+    wl = SMALL[0]
+    inp = make_inputs(wl)
+    x, w, b = inp.x.to(DEV), inp.w.to(DEV), inp.bias.to(DEV)
+    proj = plan_for(wl, x)
+    ffs, qkvs = proj.out_shapes()
+    guard = 4096
+    bufs, outs = [], []
+    for s in (ffs, qkvs, qkvs, qkvs):
+        n = int(np.prod(s))
+        buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.bfloat16, device=DEV)
+        bufs.append(buf)
+        outs.append(buf[guard:guard + n].view(s))
+    proj(x, w, b, out=outs)
+    torch.cuda.synchronize()
+    for buf, o in zip(bufs, outs):
+        assert torch.isfinite(o).all().item()
+        assert torch.isnan(buf[:guard]).all().item() and torch.isnan(buf[-guard:]).all().item()
+
+
+def test_empty_batch_is_a_noop():
+    wl = with_shape(WORKLOADS["walrus_bf16"], "empty", x_shape=(0, 64, 8, 8, 1), ff_dim=64, n_heads=2,
+                    head_dim=32)
+    x = torch.empty(wl.x_shape, dtype=torch.bfloat16, device=DEV)
+    w = torch.empty((64, wl.F), dtype=torch.bfloat16, device=DEV)
+    b = torch.empty((wl.F,), dtype=torch.bfloat16, device=DEV)
+    proj = plan_for(wl, x)
+    ff, q, k, v = proj(x, w, b)
+    torch.cuda.synchronize()
+    assert ff.numel() == 0 and q.numel() == 0
+
+
+def test_run_error_paths():
+    wl = SMALL[0]
+    inp = make_inputs(wl)
+    x, w, b = inp.x.to(DEV), inp.w.to(DEV), inp.bias.to(DEV)
+    proj = plan_for(wl, x)
+    ff, q, k, v = proj.alloc_outputs(DEV)
+    st = torch.cuda.current_stream().cuda_stream
+    p = lambda t: t.data_ptr()
+    assert proj.run_ptrs(p(x), p(w), p(b), p(ff), p(q), p(k), p(v), st) == 0
+    assert proj.run_ptrs(p(x), p(w), p(b), p(ff), p(q), p(k), None, st) == EINVAL
+    assert proj.run_ptrs(p(x), p(w), None, p(ff), p(q), p(k), p(v), st) == EINVAL    # bias required
+    assert proj.run_ptrs(p(x), p(w), p(b), p(ff) + 2, p(q), p(k), p(v), st) == EALIGN
+    assert proj.run_ptrs(p(x), p(w), p(b), p(ff), p(q), p(q), p(v), st) == EALIAS    # q == k
+    assert proj.run_ptrs(p(x), p(w), p(b), p(x), p(q), p(k), p(v), st) == EALIAS     # ff over x
+    torch.cuda.synchronize()
+    with pytest.raises(FusedProjError):
+        proj(x, w, b, out=(ff, q, q, v))
+
+
+def test_hip_graph_capture_replays_match_eager():
+    """fused_proj_run allocates and synchronises nothing, so it can be captured;
+    every replay must equal the eager result."""
+    wl = SMALL[1]
+    inp = make_inputs(wl)
+    x, w, b = inp.x.to(DEV), inp.w.to(DEV), inp.bias.to(DEV)
+    proj = plan_for(wl, x)
+    eager = [t.clone() for t in proj(x, w, b) if t is not None]
+    outs = proj.alloc_outputs(DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            proj(x, w, b, out=outs)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for t in outs:
+            if t is not None:
+                t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, c in zip(eager, [t for t in outs if t is not None]):
+            assert torch.equal(a, c), f"replay {rep}"
