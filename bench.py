@@ -65,7 +65,20 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true", help="replay the timed steps from one HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 times), to scale HBM counters")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -139,7 +152,7 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms * 1e3:.2f} us/step (events), wall {wall * 1e3 / args.steps:.2f} us/step",
+    print(f"[bench] timed {args.steps} steps: {ms * 1e3:.2f} us/step (events), wall {wall * 1e6 / args.steps:.2f} us/step",
           file=sys.stderr, flush=True)
 
     tflops = wl.flops / (ms * 1e-3) / 1e12
@@ -186,10 +199,12 @@ def main() -> int:
                                   nthreads=cores)
             return r, time.perf_counter() - t
 
-        probe = np.sort(rng.choice(wl.M, size=min(wl.M, 4 * cores), replace=False)).astype(np.int64)
+        # calibrate on a probe large enough to amortise thread start-up, then size the sample
+        probe = np.sort(rng.choice(wl.M, size=min(wl.M, max(64 * cores, 1)), replace=False)).astype(np.int64)
         _, tp = run_oracle(probe)
         n = int(min(wl.M, max(len(probe), args.cpu_seconds / max(tp / len(probe), 1e-9))))
-        tokens = np.sort(rng.choice(wl.M, size=n, replace=False)).astype(np.int64)
+        tokens = np.arange(wl.M, dtype=np.int64) if n >= wl.M else \
+            np.sort(rng.choice(wl.M, size=n, replace=False)).astype(np.int64)
         ref, secs = run_oracle(tokens)
         cpu_tflops = per_tok_flops * n / secs / 1e12
         result["cpu_baseline"] = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": cores,

@@ -132,8 +132,11 @@ struct fused_proj_plan {
     bool x_tl, w_fc;
     fp::TilePlan tile;
     fp::KernelArgs base;
+    bool fast = false;  // fast bf16 kernel (else the general kernel)
+    int dg = 0;         // its RoPE partner distance in 8-column groups
     float* d_cos = nullptr;
     float* d_sin = nullptr;
+    void* d_zeros = nullptr;
     int device = 0;
     bool debug_sync = false;
 };
@@ -155,7 +158,17 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     h->dt = desc->dtype == FUSED_PROJ_BF16 ? fp::DType::BF16 : fp::DType::F32;
     h->x_tl = desc->x_layout == FUSED_PROJ_X_TOKENS_LAST;
     h->w_fc = desc->w_layout == FUSED_PROJ_W_FC;
-    h->tile = fp::TilePlan{128, 128, h->dt == fp::DType::BF16 ? 64 : 32, 8};
+    // Kernel choice: the fast bf16 kernel unless the RoPE head size needs the general one.
+    // FUSED_PROJ_KERNEL=general forces the general kernel (used by the tests to cover both).
+    const char* force = std::getenv("FUSED_PROJ_KERNEL");
+    const bool want_general = force && std::strcmp(force, "general") == 0;
+    const int dg = fp::fast_rope_groups((int)desc->head_dim, desc->rope && r.qw > 0);
+    // the fast kernel addresses x and W with 32-bit byte offsets from a per-step base
+    const bool fits32 = r.x_span * 2 < (int64_t(1) << 32) && desc->channels * r.F * 2 < (int64_t(1) << 32);
+    h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && !want_general;
+    h->dg = dg < 0 ? 0 : dg;
+    h->tile = h->fast ? fp::TilePlan{128, 256, 32, 8}
+                      : fp::TilePlan{128, 128, h->dt == fp::DType::BF16 ? 64 : 32, 8};
     const char* dbg = std::getenv("FUSED_PROJ_DEBUG_SYNC");
     h->debug_sync = dbg && dbg[0] == '1';
     hipError_t e = hipGetDevice(&h->device);
@@ -212,6 +225,16 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     }
     a.rope_cos = h->d_cos;
     a.rope_sin = h->d_sin;
+    // a zero block: operand chunks outside the problem are read from here
+    e = hipMalloc(&h->d_zeros, 256);
+    if (e == hipSuccess) e = hipMemset(h->d_zeros, 0, 256);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        g_last_hip = e;
+        fused_proj_destroy(h);
+        return FUSED_PROJ_EHIP;
+    }
+    a.zeros = h->d_zeros;
     *out = h;
     return FUSED_PROJ_OK;
 }
@@ -267,7 +290,8 @@ int fused_proj_run(fused_proj_t h, const void* x, const void* w, const void* bia
     a.k = k;
     a.v = v;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    e = fp::launch_fused_proj(h->dt, h->x_tl, h->w_fc, h->tile, a, s);
+    e = h->fast ? fp::launch_fused_proj_fast(h->x_tl, h->w_fc, h->dg, h->tile, a, s)
+                : fp::launch_fused_proj(h->dt, h->x_tl, h->w_fc, h->tile, a, s);
     if (e == hipSuccess && h->debug_sync) {
         e = hipStreamSynchronize(s);
         if (e == hipSuccess) e = hipGetLastError();
@@ -283,6 +307,8 @@ int fused_proj_destroy(fused_proj_t h) {
     if (!h) return FUSED_PROJ_OK;
     hipError_t e1 = h->d_cos ? hipFree(h->d_cos) : hipSuccess;
     hipError_t e2 = h->d_sin ? hipFree(h->d_sin) : hipSuccess;
+    hipError_t e3 = h->d_zeros ? hipFree(h->d_zeros) : hipSuccess;
+    if (e2 == hipSuccess) e2 = e3;
     delete h;
     if (e1 != hipSuccess || e2 != hipSuccess) {
         g_last_hip = e1 != hipSuccess ? e1 : e2;
@@ -308,8 +334,9 @@ const char* fused_proj_strerror(int code) {
 int fused_proj_describe(fused_proj_t h, char* buf, size_t len) {
     if (!h || !buf || len == 0) return FUSED_PROJ_EINVAL;
     std::snprintf(buf, len,
-                  "kernel=fused_proj_tile_kernel dtype=%s x=%s w=%s tile=%dx%dx%d group_m=%d grid=%d "
+                  "kernel=%s dtype=%s x=%s w=%s tile=%dx%dx%d group_m=%d grid=%d "
                   "M=%lld K=%lld N=%lld",
+                  h->fast ? "fused_proj_fast_kernel" : "fused_proj_tile_kernel",
                   h->dt == fp::DType::BF16 ? "bf16" : "f32", h->x_tl ? "tokens_last" : "channels_first",
                   h->w_fc ? "FC" : "CF", h->tile.bm, h->tile.bn, h->tile.bk, h->tile.group_m,
                   h->base.tiles_m * h->base.tiles_n, (long long)h->r.M, (long long)h->d.channels,

@@ -32,6 +32,7 @@ struct KernelArgs {
     int32_t tiles_m;
     int32_t tiles_n;
     int32_t group_m;     // tile rows per raster group
+    const void* zeros;   // >= 16 zero bytes: source of operand chunks outside the problem
 };
 
 // Tile plan chosen on the host.
@@ -49,5 +50,12 @@ hipError_t launch_fused_proj(DType dt, bool x_tokens_last, bool w_fc, const Tile
 
 // Whether a tile plan is compiled for this combination.
 bool plan_supported(DType dt, const TilePlan& plan);
+
+// Fast bf16 kernel (F-major MFMA orientation, register epilogue, tile 128 tokens x 256
+// columns). fast_rope_groups returns the RoPE partner distance in 8-column groups it
+// needs (0 without RoPE) or -1 when the head size is not supported by it.
+int fast_rope_groups(int head_dim, bool rope);
+hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, const TilePlan& plan,
+                                  const KernelArgs& args, hipStream_t stream);
 
 }  // namespace fp

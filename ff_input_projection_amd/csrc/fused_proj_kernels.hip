@@ -18,7 +18,8 @@
 //     ds_read_b64_tr_b16 (two per operand), so no rearranged copy of x is ever
 //     made, in memory or in LDS.
 // Both LDS layouts XOR-swizzle 16-byte chunks to spread MFMA-operand reads
-// over the banks.
+// over the banks. This kernel serves fp32 and the bf16 shapes the fast kernel
+// does not take (RoPE head sizes other than 32, 64 or 128).
 //
 // Epilogue. The fp32 accumulators (+ bias) are restaged through LDS so that
 // each thread owns 16 consecutive bytes of one output row: RoPE needs the
@@ -31,6 +32,7 @@
 // with its own L2; the linear block id is remapped so that every XCD walks a
 // contiguous range of tiles, in groups of group_m tile rows that sweep the
 // columns together, so an XCD's L2 holds the x and W panels its CUs share.
+#include "device_common.h"
 #include "fused_proj_kernels.h"
 
 namespace fp {
@@ -184,9 +186,8 @@ __device__ __forceinline__ float fetch_f32(const float* tile, int rb, int kk, in
 }
 
 // ---------------------------------------------------------------- epilogue helpers
-__device__ __forceinline__ float gelu_erf(float y) {
-    return 0.5f * y * (1.0f + erff(y * 0.70710678118654752440f));
-}
+using dev::gelu_erf;
+using dev::tile_coords;
 
 template <typename T> __device__ __forceinline__ void store16(T* dst, const float* y);
 template <> __device__ __forceinline__ void store16<__bf16>(__bf16* dst, const float* y) {
@@ -201,22 +202,6 @@ template <> __device__ __forceinline__ void store16<float>(float* dst, const flo
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v) { return (float)v; }
-
-// Tile of linear block id: XCD-contiguous ranges, then grouped raster.
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int group_m, int& tm,
-                                            int& tn) {
-    const int total = tiles_m * tiles_n;
-    const int xcd = bid & 7, idx = bid >> 3;
-    const int q = total >> 3, r = total & 7;
-    const int lin = xcd * q + (xcd < r ? xcd : r) + idx;
-    const int per_group = group_m * tiles_n;
-    const int grp = lin / per_group;
-    const int first_m = grp * group_m;
-    const int gsz = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
-    const int in = lin - grp * per_group;
-    tm = first_m + in % gsz;
-    tn = in / gsz;
-}
 
 // ---------------------------------------------------------------- the kernel
 template <typename T, bool A_KM, bool B_KM, int BM, int BN, int BK>

@@ -29,9 +29,9 @@ def _check(wl, inp, outs, tokens, label):
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
-def test_workload_full_size_sampled(name):
+def test_workload_full_size_sampled(name, kernel_choice):
     wl = WORKLOADS[name]
-    print(f"[case] full-size {name}", flush=True)
+    print(f"[case] full-size {name} kernel={kernel_choice}", flush=True)
     inp = make_inputs(wl)
     proj, outs = run_gpu(wl, inp, DEV)
     print(f"[plan] {proj.describe()}", flush=True)
@@ -58,6 +58,12 @@ SMALL = [
     # several M tiles, hd 64 without RoPE, 3 heads (192 columns per slice)
     with_shape(WORKLOADS["smallk_qkv_bf16"], "cf_smallk_multitile", x_shape=(2, 64, 16, 24), n_heads=3,
                seed=105),
+    # K = 40 (one full 32-wide K step and a ragged one), channels-first, RoPE hd 64, ragged F tile
+    with_shape(WORKLOADS["walrus_bf16"], "cf_ktail_hd64", x_shape=(2, 40, 4, 24, 1), ff_dim=64, n_heads=3,
+               head_dim=64, seed=108),
+    # token-major [F,C] weight, RoPE hd 32, two M tiles + tail, bias, no GELU
+    with_shape(WORKLOADS["bert_qkv_bf16"], "tl_fc_hd32", x_shape=(3, 100, 96), ff_dim=32, n_heads=4,
+               head_dim=32, rope=True, w_layout="fc", seed=109),
     # fp32, token-major, [F,C], RoPE hd 8, GELU
     with_shape(WORKLOADS["tiny_f32"], "f32_tl_fc", layout="tokens_last", x_shape=(3, 50, 36), ff_dim=16,
                n_heads=3, head_dim=8, w_layout="fc", seed=106),
@@ -67,15 +73,26 @@ SMALL = [
 ]
 
 
+@pytest.fixture(params=["auto", "general"])
+def kernel_choice(request, monkeypatch):
+    """Run a case through the default kernel choice and through the general kernel."""
+    if request.param == "general":
+        monkeypatch.setenv("FUSED_PROJ_KERNEL", "general")
+    else:
+        monkeypatch.delenv("FUSED_PROJ_KERNEL", raising=False)
+    return request.param
+
+
 @pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
-def test_small_ragged_all_tokens(wl):
-    print(f"[case] small {wl.name} x={wl.x_shape}", flush=True)
+def test_small_ragged_all_tokens(wl, kernel_choice):
+    print(f"[case] small {wl.name} x={wl.x_shape} kernel={kernel_choice}", flush=True)
     inp = make_inputs(wl)
-    _, outs = run_gpu(wl, inp, DEV)
+    proj, outs = run_gpu(wl, inp, DEV)
+    print(f"[plan] {proj.describe()}", flush=True)
     _check(wl, inp, outs, all_tokens(wl), wl.name)
 
 
-def test_strided_views_channel_slice_and_row_stride():
+def test_strided_views_channel_slice_and_row_stride(kernel_choice):
     """x as a view: a channel slice of a wider channels-first tensor, and a token-major
     view whose row stride exceeds C. No copy is made; results match the oracle."""
     wl = with_shape(WORKLOADS["walrus_bf16"], "cf_view", x_shape=(2, 48, 8, 16, 1), ff_dim=64, n_heads=2,
@@ -98,7 +115,7 @@ def test_strided_views_channel_slice_and_row_stride():
     _check(wl2, inp2, outs2, all_tokens(wl2), "row-stride view")
 
 
-def test_layout_invariance_on_gpu():
+def test_layout_invariance_on_gpu(kernel_choice):
     """Channels-first input and its channels-last copy give the same outputs."""
     wl = with_shape(WORKLOADS["walrus_bf16"], "inv", x_shape=(2, 64, 8, 16, 1), ff_dim=64, n_heads=2,
                     head_dim=32, seed=301)
