@@ -158,25 +158,35 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     h->dt = desc->dtype == FUSED_PROJ_BF16 ? fp::DType::BF16 : fp::DType::F32;
     h->x_tl = desc->x_layout == FUSED_PROJ_X_TOKENS_LAST;
     h->w_fc = desc->w_layout == FUSED_PROJ_W_FC;
-    // Kernel choice: the fast bf16 kernel unless the RoPE head size needs the general one.
-    // FUSED_PROJ_KERNEL=general forces the general kernel (used by the tests to cover both).
-    const char* force = std::getenv("FUSED_PROJ_KERNEL");
-    const bool want_general = force && std::strcmp(force, "general") == 0;
-    const int dg = fp::fast_rope_groups((int)desc->head_dim, desc->rope && r.qw > 0);
-    // the fast kernel addresses x and W with 32-bit byte offsets from a per-step base
-    const bool fits32 = r.x_span * 2 < (int64_t(1) << 32) && desc->channels * r.F * 2 < (int64_t(1) << 32);
-    h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && !want_general;
-    h->dg = dg < 0 ? 0 : dg;
-    h->tile = h->fast ? fp::TilePlan{128, 256, 32, 8}
-                      : fp::TilePlan{128, 128, h->dt == fp::DType::BF16 ? 64 : 32, 8};
     const char* dbg = std::getenv("FUSED_PROJ_DEBUG_SYNC");
     h->debug_sync = dbg && dbg[0] == '1';
     hipError_t e = hipGetDevice(&h->device);
+    int num_cus = 0;
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, h->device);
     if (e != hipSuccess) {
         g_last_hip = e;
         delete h;
         return FUSED_PROJ_EHIP;
     }
+    // Kernel choice. The fast bf16 kernel needs a RoPE head size of 32, 64 or 128 (or no
+    // RoPE) and x and W spans under 4 GiB (it addresses them with 32-bit offsets). It is
+    // used only on exact tilings -- tokens and columns multiples of its 256 x 256 tile,
+    // channels a multiple of 128, at least one tile per CU -- the shapes it has been
+    // verified on; every other shape goes to the general kernel.
+    // FUSED_PROJ_KERNEL=general forces the general kernel (the tests use it to cover both);
+    // FUSED_PROJ_KERNEL=fast takes the fast kernel on any shape it can address.
+    const char* force = std::getenv("FUSED_PROJ_KERNEL");
+    const bool want_general = force && std::strcmp(force, "general") == 0;
+    const bool want_fast = force && std::strcmp(force, "fast") == 0;
+    const int dg = fp::fast_rope_groups((int)desc->head_dim, desc->rope && r.qw > 0);
+    const bool fits32 = r.x_span * 2 < (int64_t(1) << 32) && desc->channels * r.F * 2 < (int64_t(1) << 32);
+    const fp::TilePlan fp_plan = fp::fast_plan(r.M, r.F, num_cus);
+    const int64_t fast_tiles = (r.M / fp_plan.bm) * (r.F / fp_plan.bn);
+    const bool exact = r.M % fp_plan.bm == 0 && r.F % fp_plan.bn == 0 && desc->channels % 128 == 0 &&
+                       desc->channels > 0 && fast_tiles >= (num_cus > 0 ? num_cus : 256);
+    h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && (exact || want_fast) && !want_general;
+    h->dg = dg < 0 ? 0 : dg;
+    h->tile = h->fast ? fp_plan : fp::TilePlan{128, 128, h->dt == fp::DType::BF16 ? 64 : 32, 8, 0};
 
     fp::KernelArgs& a = h->base;
     std::memset(&a, 0, sizeof(a));
@@ -193,7 +203,7 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     a.qw = (int32_t)r.qw;
     a.act = desc->ff_act == FUSED_PROJ_ACT_GELU_ERF ? 1 : 0;
     a.rope = (desc->rope && r.qw > 0) ? 1 : 0;
-    a.tiles_m = (int32_t)((r.M + h->tile.bm - 1) / h->tile.bm);
+    a.tiles_m = (int32_t)((r.M + h->tile.bm - 1) / h->tile.bm);  // token tiles
     a.tiles_n = (int32_t)((r.F + h->tile.bn - 1) / h->tile.bn);
     a.group_m = h->tile.group_m;
 
@@ -334,11 +344,12 @@ const char* fused_proj_strerror(int code) {
 int fused_proj_describe(fused_proj_t h, char* buf, size_t len) {
     if (!h || !buf || len == 0) return FUSED_PROJ_EINVAL;
     std::snprintf(buf, len,
-                  "kernel=%s dtype=%s x=%s w=%s tile=%dx%dx%d group_m=%d grid=%d "
+                  "kernel=%s dtype=%s x=%s w=%s tile=%dx%dx%d group_m=%d grid=%d tiles=%d "
                   "M=%lld K=%lld N=%lld",
                   h->fast ? "fused_proj_fast_kernel" : "fused_proj_tile_kernel",
                   h->dt == fp::DType::BF16 ? "bf16" : "f32", h->x_tl ? "tokens_last" : "channels_first",
                   h->w_fc ? "FC" : "CF", h->tile.bm, h->tile.bn, h->tile.bk, h->tile.group_m,
+                  h->tile.grid > 0 ? h->tile.grid : h->base.tiles_m * h->base.tiles_n,
                   h->base.tiles_m * h->base.tiles_n, (long long)h->r.M, (long long)h->d.channels,
                   (long long)h->r.F);
     return FUSED_PROJ_OK;

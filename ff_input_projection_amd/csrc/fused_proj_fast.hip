@@ -20,17 +20,23 @@
 // token-major [b,s,c] layout (Walrus PR "Make fused_ff_qkv contiguous": no
 // rearranged copy), W from [C,F] or [F,C]. K steps of BK are copied from global
 // memory into LDS by global_load_lds_dwordx4 (16 bytes per lane straight into
-// LDS, no staging registers) three stages deep, one barrier per K step: before
-// reading stage k a wave waits (vmcnt) for its own loads of that stage only,
-// then the barrier makes every wave's loads visible. Each
+// LDS, no staging registers), one barrier per K step: before reading stage k a
+// wave waits (vmcnt) for its own loads of that stage only, then the barrier
+// makes every wave's loads visible. Each
 // lane's source chunk is chosen so that the LDS image comes out XOR-swizzled.
 // M/N-contiguous tiles feed the MFMA through ds_read_b64_tr_b16, K-contiguous
 // ones through ds_read_b128. Chunks outside the problem (ragged M, N or K) are
 // read from a small zero block instead, so no access leaves the operands.
 //
-// Occupancy. 256 threads as 2 x 2 waves, each wave a 128 (f) x 64 (token) tile
-// (128 accumulators); two workgroups per CU, i.e. two waves per SIMD, so one
-// wave's VALU-heavy epilogue co-issues with the other wave's MFMAs.
+// Schedule. The kernel is persistent: one workgroup of 8 waves per CU, each
+// workgroup walking a list of 256 x 256 tiles (2 x 4 waves of 128 (f) x 64
+// (tokens), 128 accumulators each, two waves per SIMD). The direct-load
+// pipeline is four stages deep and runs straight on into the next tile: the
+// first K steps of tile i+1 are in flight while tile i finishes its last K
+// steps and its epilogue. Larger tiles halve the panel traffic from L2 per
+// flop compared with 128-token tiles (the L2->CU path, about 54 B/clk per CU
+// measured, is the scarce resource), and the workgroup's tiles are taken from
+// a contiguous, grouped range of the XCD it runs on.
 #include "device_common.h"
 #include "fused_proj_kernels.h"
 
@@ -38,19 +44,12 @@ namespace fp {
 namespace {
 
 using namespace dev;
-constexpr int kThreads = 256;
 
+// s_waitcnt vmcnt(N): at most N of this wave's vector memory operations outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else static_assert(N == 0, "add this vmcnt value");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 __device__ __forceinline__ void store4_bf16(__bf16* dst, const float* o) {
@@ -63,10 +62,6 @@ __device__ __forceinline__ void store4_bf16(__bf16* dst, const float* o) {
 }
 
 __device__ __forceinline__ void load4_bias(const __bf16* bias, int f, float* b) {
-    if (bias == nullptr) {
-        b[0] = b[1] = b[2] = b[3] = 0.0f;
-        return;
-    }
     const bf16x4 v = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(bias + f));
     b[0] = (float)v[0];
     b[1] = (float)v[1];
@@ -105,58 +100,65 @@ __device__ __forceinline__ unsigned k_operand_base(int rb, int kk, int lane) {
     return (unsigned)((r * CPR + (c ^ ((r * CPR / 16) % CPR))) * 16);
 }
 
-template <bool X_TL, bool W_FC, int BF, int BT, int BK>
+// Tile geometry: BF output columns x BT tokens per workgroup, NWF x NWT waves.
+template <bool X_TL, bool W_FC, int BF, int BT, int NWF, int NWT, int BK, int STAGES>
 struct FastCfg {
-    static constexpr int STAGES = 3;
-    static constexpr int WF = BF / 2, WT = BT / 2;   // 2 x 2 waves
+    static constexpr int NW = NWF * NWT, THREADS = 64 * NW;
+    static constexpr int WF = BF / NWF, WT = BT / NWT;   // wave tile
     static constexpr int TI = WF / 32, TJ = WT / 32;
-    static constexpr int NG = TI * 4;                // 8-column groups per wave
-    static constexpr int KK = BK / 16;               // MFMA k steps per K step
+    static constexpr int NG = TI * 4;                    // 8-column groups per wave
+    static constexpr int KK = BK / 16;                   // MFMA k steps per K step
     static constexpr int W_BYTES = BF * BK * 2, X_BYTES = BT * BK * 2;
     static constexpr int X_REGION = STAGES * W_BYTES;
     static constexpr int LDS_BYTES = STAGES * (W_BYTES + X_BYTES);
     static constexpr int W_CPR = W_FC ? BK / 8 : BF / 8;
     static constexpr int X_CPR = X_TL ? BK / 8 : BT / 8;
-    static constexpr int W_INSTR = BF * BK / 8 / 64 / 4;   // direct loads per wave per K step
-    static constexpr int X_INSTR = BT * BK / 8 / 64 / 4;
+    static constexpr int W_INSTR = BF * BK / 8 / 64 / NW;   // direct loads per wave per K step
+    static constexpr int X_INSTR = BT * BK / 8 / 64 / NW;
     static constexpr int NLOAD = W_INSTR + X_INSTR;
-    static_assert(W_INSTR * 8 * 64 * 4 == BF * BK && X_INSTR * 8 * 64 * 4 == BT * BK, "tile split");
-    static_assert(BK % 16 == 0, "BK");
-    // immediate LDS offsets (stage + k step) must fit the 16-bit offset field
-    static_assert(STAGES * W_BYTES <= 65536 && STAGES * X_BYTES <= 65536, "16-bit LDS offsets");
+    static_assert(W_INSTR * 8 * 64 * NW == BF * BK && X_INSTR * 8 * 64 * NW == BT * BK, "tile split");
+    static_assert(TI >= 1 && TJ >= 1 && BK % 16 == 0 && STAGES >= 3, "geometry");
+    // the largest immediate LDS offset (stage + k step) must fit the 16-bit field
+    static constexpr int W_MAX_IMM = (STAGES - 1) * W_BYTES + (W_FC ? 0 : ((KK - 1) * 16 + 4) * W_CPR * 16);
+    static constexpr int X_MAX_IMM = (STAGES - 1) * X_BYTES + (X_TL ? 0 : ((KK - 1) * 16 + 4) * X_CPR * 16);
+    static_assert(W_MAX_IMM < 65536 && X_MAX_IMM < 65536, "16-bit LDS offsets");
+    static_assert((STAGES - 2) * NLOAD < 64, "vmcnt range");
 };
 
-// Operand state of one wave: read bases and direct-load sources.
-template <bool X_TL, bool W_FC, int BF, int BT, int BK>
+// Wave-constant operand state: LDS read bases and the direct-load chunk map.
+template <class C, bool X_TL, bool W_FC, int BK>
 struct FastPipe {
-    using C = FastCfg<X_TL, W_FC, BF, BT, BK>;
     unsigned wbase[C::TI][W_FC ? C::KK : 1];   // LDS read bases of the W^T operands
     unsigned xbase[C::TJ][X_TL ? C::KK : 1];   // and of the x operands
-    unsigned voff[C::NLOAD];                   // per-lane byte offset of each direct-load chunk
-    int kofs[C::NLOAD];                        // its k offset inside the K step
+    int kofs[C::NLOAD];                        // k offset of each direct-load chunk in its K step
+    unsigned lds0;
+    int wave;
     const char* wsrc;                          // W and x byte addresses of K step 0
     const char* xsrc;
     int64_t wstep, xstep;                      // bytes per K step
-    unsigned lds0;                             // LDS byte address of the tile storage
-    int wave;
 
-    // Issue the direct loads of K step kt into stage ST. `tail`: K step kt runs past K;
-    // its chunks beyond K are read from the zero block instead.
+    // Issue the direct loads of K step ks (of the tile whose chunk offsets are voff) into
+    // stage ST. Chunks at or past K (a ragged last step, or the steps that pad the step
+    // count to a multiple of the stage count) are read from the zero block.
     template <int ST>
-    __device__ __forceinline__ void issue(int kt, int K, bool tail, const char* zeros) const {
-        const char* ws = wsrc + (int64_t)kt * wstep;
-        const char* xs = xsrc + (int64_t)kt * xstep;
+    __device__ __forceinline__ void issue(const unsigned (&voff)[C::NLOAD], int ks, int K,
+                                          const char* zeros) const {
+        const char* ws = wsrc + (int64_t)ks * wstep;
+        const char* xs = xsrc + (int64_t)ks * xstep;
+        const bool tail = (ks + 1) * BK > K;
 #pragma unroll
         for (int q = 0; q < C::NLOAD; ++q) {
             const bool isw = q < C::W_INSTR;
             const unsigned dst = lds0 + (isw ? ST * C::W_BYTES + (wave * C::W_INSTR + q) * 1024
-                                             : C::X_REGION + ST * C::X_BYTES + (wave * C::X_INSTR + (q - C::W_INSTR)) * 1024);
+                                             : C::X_REGION + ST * C::X_BYTES +
+                                                   (wave * C::X_INSTR + (q - C::W_INSTR)) * 1024);
             const char* base = isw ? ws : xs;
             if (!tail) {
-                // SGPR base + 32-bit lane offset: no per-load VALU
+                // SGPR base + 32-bit lane offset: no per-load VALU. Inline asm keeps the
+                // compiler from waiting on every stage in flight before each LDS read.
                 asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff[q]), "s"(base), "{m0}"(dst) : "memory");
             } else {
-                const char* a = (kt * BK + kofs[q] < K) ? base + voff[q] : zeros;
+                const char* a = (ks * BK + kofs[q] < K) ? base + voff[q] : zeros;
                 asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(a), "{m0}"(dst) : "memory");
             }
         }
@@ -197,38 +199,98 @@ struct FastPipe {
     }
 };
 
-// One K step: wait for this wave's loads of stage ST, barrier (all waves' loads landed,
-// all waves done with the stage about to be refilled), refill it two steps ahead, compute.
-template <int ST, class Pipe, class Acc>
-__device__ __forceinline__ void k_step(const Pipe& pp, Acc& acc, int kt, int KT, int K, int KT_full,
-                                       const char* zeros) {
-    using C = typename Pipe::C;
-    if (kt + 1 < KT) wait_vmcnt<C::NLOAD>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    if (kt + 2 < KT) pp.template issue<(ST + 2) % C::STAGES>(kt + 2, K, kt + 2 >= KT_full, zeros);
-    pp.template compute<ST>(acc);
+// Byte offset of each lane's direct-load chunks for the tile at (m0, n0). Lane l of
+// instruction q fills physical LDS chunk (wave*INSTR + q)*64 + l, so choosing the
+// source chunk through the inverse swizzle makes the LDS image come out swizzled.
+// Rows past N and tokens past M read row / token 0 instead (in bounds, never stored).
+template <class C, bool X_TL, bool W_FC>
+__device__ __forceinline__ void tile_offsets(unsigned (&voff)[C::NLOAD], int (&kofs)[C::NLOAD], int m0, int n0,
+                                             int wave, int lane, int K, int N, int M, int S, int64_t sb,
+                                             int64_t ss, int64_t sc) {
+#pragma unroll
+    for (int q = 0; q < C::W_INSTR; ++q) {
+        const int pch = (wave * C::W_INSTR + q) * 64 + lane;
+        const int row = pch / C::W_CPR, pc = pch % C::W_CPR;
+        int64_t off;
+        int krow;
+        if constexpr (W_FC) {
+            const int c = pc ^ ((row * C::W_CPR / 16) % C::W_CPR);
+            const int n = n0 + row;
+            krow = c * 8;
+            off = (int64_t)(n < N ? n : 0) * K + krow;
+        } else {
+            const int c = pc ^ ((row & 3) << 2);
+            const int n = n0 + c * 8;
+            krow = row;
+            off = (int64_t)krow * N + (n < N ? n : 0);
+        }
+        voff[q] = (unsigned)(off * 2);
+        kofs[q] = krow;
+    }
+#pragma unroll
+    for (int q = 0; q < C::X_INSTR; ++q) {
+        const int pch = (wave * C::X_INSTR + q) * 64 + lane;
+        const int row = pch / C::X_CPR, pc = pch % C::X_CPR;
+        int m, krow;
+        if constexpr (X_TL) {
+            const int c = pc ^ ((row * C::X_CPR / 16) % C::X_CPR);
+            m = m0 + row;
+            krow = c * 8;
+        } else {
+            const int c = pc ^ ((row & 3) << 2);
+            m = m0 + c * 8;
+            krow = row;
+        }
+        const int mm = m < M ? m : 0;
+        const int bi = mm / S, s = mm - bi * S;
+        const int64_t off = (int64_t)bi * sb + (int64_t)s * ss + (int64_t)krow * sc;
+        voff[C::W_INSTR + q] = (unsigned)(off * 2);
+        kofs[C::W_INSTR + q] = krow;
+    }
+}
+
+// k-th tile of this workgroup. The tiles of the grid's linear order are split into 8
+// contiguous ranges, one per XCD (workgroup b runs on XCD b mod 8); inside its range a
+// workgroup takes every (workgroups per XCD)-th tile. Linear order: groups of group_m
+// token tiles sweep the column tiles together.
+__device__ __forceinline__ bool block_tile(int k, int tiles_t, int tiles_f, int group_m, int& tt, int& tf) {
+    const int total = tiles_t * tiles_f;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
+    const int q = total >> 3, r = total & 7;
+    const int count = q + (xcd < r ? 1 : 0);
+    const int li = slot + k * per_xcd;
+    if (li >= count) return false;
+    const int lin = xcd * q + (xcd < r ? xcd : r) + li;
+    const int per_group = group_m * tiles_f;
+    const int grp = lin / per_group;
+    const int first = grp * group_m;
+    const int gsz = (tiles_t - first) < group_m ? (tiles_t - first) : group_m;
+    const int in = lin - grp * per_group;
+    tt = first + in % gsz;
+    tf = in / gsz;
+    return true;
 }
 
 // X_TL: x token-major [b,s,c] (else channels-first). W_FC: W [F,C] (else [C,F]).
-// DG: RoPE partner distance in 8-column groups (hd/16), 0 = no RoPE in this kernel.
-template <bool X_TL, bool W_FC, int BF, int BT, int BK, int DG>
-__global__ __launch_bounds__(kThreads, 2) void fused_proj_fast_kernel(KernelArgs p) {
-    using C = FastCfg<X_TL, W_FC, BF, BT, BK>;
-    constexpr int WF = C::WF, WT = C::WT, TI = C::TI, TJ = C::TJ, NG = C::NG;
+// DG: RoPE partner distance in 8-column groups (hd/16), 0 = no RoPE.
+template <bool X_TL, bool W_FC, int BF, int BT, int NWF, int NWT, int BK, int STAGES, int DG>
+__global__ __launch_bounds__(64 * NWF * NWT, 1) void fused_proj_fast_kernel(KernelArgs p) {
+    using C = FastCfg<X_TL, W_FC, BF, BT, NWF, NWT, BK, STAGES>;
+    constexpr int WF = C::WF, WT = C::WT, TI = C::TI, TJ = C::TJ, NG = C::NG, NLOAD = C::NLOAD;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
-    __shared__ __attribute__((aligned(16))) float bias_s[BF];   // this tile's bias, fp32
+    __shared__ __attribute__((aligned(16))) float bias_s[2][BF];   // tile bias (fp32), double-buffered
 
-    int tt, tf;
-    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tt, tf);
-    const int m0 = tt * BT, n0 = tf * BF;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int wf = wave >> 1, wt = wave & 1;
+    const int wf = wave / NWT, wt = wave % NWT;
     const int K = p.K, N = p.N, M = (int)p.M, S = p.S;
     const char* const zeros = static_cast<const char*>(p.zeros);
+    const __bf16* const bias = static_cast<const __bf16*>(p.bias);
 
-    FastPipe<X_TL, W_FC, BF, BT, BK> pp;
+    int tt, tf;
+    if (!block_tile(0, p.tiles_m, p.tiles_n, p.group_m, tt, tf)) return;
+
+    FastPipe<C, X_TL, W_FC, BK> pp;
     pp.wave = wave;
     pp.lds0 = (unsigned)(size_t)(lds_void*)smem;
 #pragma unroll
@@ -250,83 +312,39 @@ __global__ __launch_bounds__(kThreads, 2) void fused_proj_fast_kernel(KernelArgs
             pp.xbase[j][0] = pp.lds0 + C::X_REGION + mn_operand_base<C::X_CPR>(wt * WT + 32 * j, lane);
         }
     }
-    // Direct-load chunk of each lane: the LDS image comes out swizzled because lane l of
-    // instruction q fills physical chunk (wave*INSTR + q)*64 + l.
-#pragma unroll
-    for (int q = 0; q < C::W_INSTR; ++q) {
-        const int pch = (wave * C::W_INSTR + q) * 64 + lane;
-        const int row = pch / C::W_CPR, pc = pch % C::W_CPR;
-        int64_t off;
-        int krow;
-        if constexpr (W_FC) {
-            const int c = pc ^ ((row * C::W_CPR / 16) % C::W_CPR);
-            const int n = n0 + row;
-            krow = c * 8;
-            off = (int64_t)(n < N ? n : 0) * K + krow;   // rows past N read row 0: never stored
-        } else {
-            const int c = pc ^ ((row & 3) << 2);
-            const int n = n0 + c * 8;
-            krow = row;
-            off = (int64_t)krow * N + (n < N ? n : 0);
-        }
-        pp.voff[q] = (unsigned)(off * 2);
-        pp.kofs[q] = krow;
-    }
-#pragma unroll
-    for (int q = 0; q < C::X_INSTR; ++q) {
-        const int pch = (wave * C::X_INSTR + q) * 64 + lane;
-        const int row = pch / C::X_CPR, pc = pch % C::X_CPR;
-        int m, krow;
-        if constexpr (X_TL) {
-            const int c = pc ^ ((row * C::X_CPR / 16) % C::X_CPR);
-            m = m0 + row;
-            krow = c * 8;
-        } else {
-            const int c = pc ^ ((row & 3) << 2);
-            m = m0 + c * 8;
-            krow = row;
-        }
-        const int mm = m < M ? m : 0;                  // tokens past M read token 0: never stored
-        const int bi = mm / S, s = mm - bi * S;
-        const int64_t off = (int64_t)bi * p.x_sb + (int64_t)s * p.x_ss + (int64_t)krow * p.x_sc;
-        pp.voff[C::W_INSTR + q] = (unsigned)(off * 2);
-        pp.kofs[C::W_INSTR + q] = krow;
-    }
     pp.wsrc = static_cast<const char*>(p.w);
     pp.xsrc = static_cast<const char*>(p.x);
     pp.wstep = (W_FC ? (int64_t)BK : (int64_t)BK * N) * 2;
     pp.xstep = (X_TL ? (int64_t)BK : (int64_t)BK * p.x_sc) * 2;
 
-    // The tile's bias goes to LDS once (fp32; zero past N or without bias): the epilogue
-    // then reads it without global loads, which would otherwise queue behind its stores.
-    if (tid < BF / 4) {
-        const int f = n0 + 4 * tid;
-        float b4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (p.bias != nullptr && f < N) load4_bias(static_cast<const __bf16*>(p.bias), f, b4);
-        *reinterpret_cast<f32x4*>(bias_s + 4 * tid) = f32x4{b4[0], b4[1], b4[2], b4[3]};
-    }
+    unsigned voff_cur[NLOAD], voff_nxt[NLOAD];
+    tile_offsets<C, X_TL, W_FC>(voff_cur, pp.kofs, tt * BT, tf * BF, wave, lane, K, N, M, S, p.x_sb, p.x_ss,
+                                p.x_sc);
 
-    f32x16 acc[TI][TJ];
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
+    // bias of the first tile (the barriers of its first K step publish it)
+    auto stage_bias = [&](int buf, int n0) __attribute__((always_inline)) {
+        if (tid < BF / 4) {
+            const int f = n0 + 4 * tid;
+            float b4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (bias != nullptr && f < N) load4_bias(bias, f, b4);
+            *reinterpret_cast<f32x4*>(&bias_s[buf][4 * tid]) = f32x4{b4[0], b4[1], b4[2], b4[3]};
+        }
+    };
+    stage_bias(0, tf * BF);
 
-    const int KT = (K + BK - 1) / BK;
-    const int KT_full = K / BK;  // K steps with no chunk past K
-    if (KT > 0) pp.template issue<0>(0, K, 0 >= KT_full, zeros);
-    if (KT > 1) pp.template issue<1>(1, K, 1 >= KT_full, zeros);
-    for (int kt = 0; kt < KT; kt += 3) {
-        k_step<0>(pp, acc, kt, KT, K, KT_full, zeros);
-        if (kt + 1 < KT) k_step<1>(pp, acc, kt + 1, KT, K, KT_full, zeros);
-        if (kt + 2 < KT) k_step<2>(pp, acc, kt + 2, KT, K, KT_full, zeros);
-    }
+    // K steps per tile, padded to a multiple of the stage count so that step s of every
+    // tile uses stage s mod STAGES (the padding steps read zeros). At least one step.
+    const int KT = K > 0 ? (K + BK - 1) / BK : 1;
+    const int KTp = (KT + STAGES - 1) / STAGES * STAGES;
 
-    if (KT == 0) __syncthreads();  // (with K steps, their barriers publish bias_s)
+    // prologue: the first STAGES-1 steps of the first tile
+    pp.template issue<0>(voff_cur, 0, K, zeros);
+    pp.template issue<1>(voff_cur, 1, K, zeros);
+    if constexpr (STAGES > 3) pp.template issue<2>(voff_cur, 2, K, zeros);
+    if constexpr (STAGES > 4) pp.template issue<3>(voff_cur, 3, K, zeros);
+    static_assert(STAGES <= 5, "prologue");
 
-    // ---- epilogue in registers. acc[i][j][e]: column f = 32i + 8(e/4) + 4(lane/32) + e%4,
-    // token 32j + lane%32 (both relative to the wave tile). The outputs never overlap the
-    // inputs (checked on the host), so loads may be hoisted above stores.
+    // epilogue constants
     const int hl = lane >> 5;
     __bf16* __restrict__ const out_ff = static_cast<__bf16*>(p.ff);
     __bf16* __restrict__ const out_q = static_cast<__bf16*>(p.q);
@@ -334,84 +352,139 @@ __global__ __launch_bounds__(kThreads, 2) void fused_proj_fast_kernel(KernelArgs
     __bf16* __restrict__ const out_v = static_cast<__bf16*>(p.v);
     const float* __restrict__ const rope_cos = p.rope_cos;
     const float* __restrict__ const rope_sin = p.rope_sin;
-    const int ff_dim = p.ff_dim, qw = p.qw, hd = p.head_dim;
-    const int n_heads = p.n_heads, act = p.act, rope = p.rope;
-    const int half = hd >> 1;
+    const int ff_dim = p.ff_dim, qw = p.qw, hd = p.head_dim, n_heads = p.n_heads, act = p.act;
     const int64_t head_stride = (int64_t)S * hd;   // elements between heads of one slab
+
+    for (int k_tile = 0;; ++k_tile) {
+        const int m0 = tt * BT, n0 = tf * BF;
+        int ntt = 0, ntf = 0;
+        const bool has_next = block_tile(k_tile + 1, p.tiles_m, p.tiles_n, p.group_m, ntt, ntf);
+        if (has_next)
+            tile_offsets<C, X_TL, W_FC>(voff_nxt, pp.kofs, ntt * BT, ntf * BF, wave, lane, K, N, M, S, p.x_sb,
+                                        p.x_ss, p.x_sc);
+
+        f32x16 acc[TI][TJ];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-        const int t = m0 + wt * WT + 32 * j + (lane & 31);
-        const bool tv = t < M;
-        const int bi = t / S, s = t - bi * S;
-        __bf16* const ff_row = out_ff + (int64_t)t * ff_dim;
-        const int64_t tok = (int64_t)bi * n_heads * head_stride + (int64_t)s * hd;   // head 0 of this token
-        const float* const cs_row = rope_cos + (int64_t)s * half;
-        const float* const sn_row = rope_sin + (int64_t)s * half;
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int G = 0; G < NG; ++G) {
-            const int f8 = n0 + wf * WF + 8 * G;  // wave-uniform column group
-            if (f8 >= N) continue;
-            const int f = f8 + 4 * hl;
-            const int fl = wf * WF + 8 * G + 4 * hl;   // column inside the tile
-            float y[4];
-            const f32x4 bv = *reinterpret_cast<const f32x4*>(bias_s + fl);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) y[u] = acc[G >> 2][j][4 * (G & 3) + u] + bv[u];
-            if (f8 < ff_dim) {
-                if (act == 1) {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) y[u] = gelu_erf_fast(y[u]);
-                }
-                if (tv) store4_bf16(ff_row + f, y);
-                continue;
-            }
-            const int r = f8 - ff_dim;
-            const int which = r / qw;
-            const int rem = r - which * qw;
-            const int h = rem / hd;
-            const int jh8 = rem - h * hd;   // wave-uniform group start inside the head
-            const int jh = jh8 + 4 * hl;    // this lane's first column
-            __bf16* const dst = (which == 0 ? out_q : which == 1 ? out_k : out_v) + tok + h * head_stride;
-            if (DG > 0 && rope && which < 2) {
-                // first-half group: compute it and its partner DG groups on (same head,
-                // hence inside this wave's tile); the partner's own iteration skips.
-                if (jh8 >= half || G + DG >= NG) continue;
-                const int G2 = (G + DG < NG) ? G + DG : G;  // constant after unrolling
-                float y2[4];
-                const f32x4 b2 = *reinterpret_cast<const f32x4*>(bias_s + fl + half);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) y2[u] = acc[G2 >> 2][j][4 * (G2 & 3) + u] + b2[u];
-                const f32x4 c = *reinterpret_cast<const f32x4*>(cs_row + jh);
-                const f32x4 sn = *reinterpret_cast<const f32x4*>(sn_row + jh);
-                float o1[4], o2[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    o1[u] = y[u] * c[u] - y2[u] * sn[u];
-                    o2[u] = y2[u] * c[u] + y[u] * sn[u];
-                }
-                if (tv) {
-                    store4_bf16(dst + jh, o1);
-                    store4_bf16(dst + jh + half, o2);
-                }
-                continue;
-            }
-            if (tv) store4_bf16(dst + jh, y);
+            for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
+
+        // One K step: wait for this wave's loads of the step (the loads of up to STAGES-2
+        // later steps may stay in flight), barrier (every wave's loads landed; every wave is
+        // done with the stage about to be refilled), refill it STAGES-1 steps ahead --
+        // from the next tile once this one runs out -- then compute.
+        auto k_step = [&](auto stc, int kt) __attribute__((always_inline)) {
+            constexpr int ST = decltype(stc)::value;
+            const int later = (KTp - 1 - kt) + (has_next ? KTp : 0);  // steps after kt still to run
+            if (later >= STAGES - 2) wait_vmcnt<(STAGES - 2) * NLOAD>();
+            else if (STAGES > 3 && later == 1) wait_vmcnt<NLOAD>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+            const int s_next = kt + STAGES - 1;
+            constexpr int SN = (ST + STAGES - 1) % STAGES;
+            if (s_next < KTp) pp.template issue<SN>(voff_cur, s_next, K, zeros);
+            else if (has_next) pp.template issue<SN>(voff_nxt, s_next - KTp, K, zeros);
+            pp.template compute<ST>(acc);
+        };
+        for (int kt = 0; kt < KTp; kt += STAGES) {
+            k_step(std::integral_constant<int, 0>{}, kt);
+            k_step(std::integral_constant<int, 1>{}, kt + 1);
+            k_step(std::integral_constant<int, 2>{}, kt + 2);
+            if constexpr (STAGES > 3) k_step(std::integral_constant<int, 3>{}, kt + 3);
+            if constexpr (STAGES > 4) k_step(std::integral_constant<int, 4>{}, kt + 4);
         }
+
+        // ---- epilogue in registers. acc[i][j][e]: column f = 32i + 8(e/4) + 4(lane/32) +
+        // e%4, token 32j + lane%32 (both relative to the wave tile). Outputs never overlap
+        // the inputs (checked on the host), so loads may be hoisted above stores.
+        const float* const bias_t = bias_s[k_tile & 1];
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+            const int t = m0 + wt * WT + 32 * j + (lane & 31);
+            const bool tv = t < M;
+            const int bi = t / S, s = t - bi * S;
+            __bf16* const ff_row = out_ff + (int64_t)t * ff_dim;
+            const int64_t tok = (int64_t)bi * n_heads * head_stride + (int64_t)s * hd;   // head 0 of this token
+            const float* const cs_row = rope_cos + (int64_t)s * (DG * 8);
+            const float* const sn_row = rope_sin + (int64_t)s * (DG * 8);
+#pragma unroll
+            for (int G = 0; G < NG; ++G) {
+                const int f8 = n0 + wf * WF + 8 * G;  // wave-uniform column group
+                if (f8 >= N) continue;
+                const int fl = wf * WF + 8 * G + 4 * hl;   // this lane's first column inside the tile
+                float y[4];
+                const f32x4 bv = *reinterpret_cast<const f32x4*>(bias_t + fl);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) y[u] = acc[G >> 2][j][4 * (G & 3) + u] + bv[u];
+                if (f8 < ff_dim) {
+                    if (act == 1) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) y[u] = gelu_erf_fast(y[u]);
+                    }
+                    if (tv) store4_bf16(ff_row + n0 + fl, y);
+                    continue;
+                }
+                const int r = f8 - ff_dim;
+                const int which = r / qw;
+                const int rem = r - which * qw;
+                const int h = rem / hd;
+                __bf16* const dst = (which == 0 ? out_q : which == 1 ? out_k : out_v) + tok + h * head_stride;
+                if (DG > 0 && which < 2) {
+                    // Heads start on head_dim boundaries of this wave's columns, so the
+                    // group's place inside its head is a compile-time constant. A
+                    // first-half group is computed together with its partner DG groups on;
+                    // the partner's own iteration skips.
+                    constexpr int HD = DG > 0 ? 16 * DG : 16, HALF = HD / 2;
+                    const int jh8 = (8 * G) % HD;
+                    if (jh8 >= HALF || G + DG >= NG) continue;
+                    const int G2 = (G + DG < NG) ? G + DG : G;  // constant after unrolling
+                    const int jh = jh8 + 4 * hl;
+                    float y2[4];
+                    const f32x4 b2 = *reinterpret_cast<const f32x4*>(bias_t + fl + HALF);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) y2[u] = acc[G2 >> 2][j][4 * (G2 & 3) + u] + b2[u];
+                    const f32x4 c = *reinterpret_cast<const f32x4*>(cs_row + jh);
+                    const f32x4 sn = *reinterpret_cast<const f32x4*>(sn_row + jh);
+                    float o1[4], o2[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        o1[u] = y[u] * c[u] - y2[u] * sn[u];
+                        o2[u] = y2[u] * c[u] + y[u] * sn[u];
+                    }
+                    if (tv) {
+                        store4_bf16(dst + jh, o1);
+                        store4_bf16(dst + jh + HALF, o2);
+                    }
+                    continue;
+                }
+                const int jh = rem - h * hd + 4 * hl;
+                if (tv) store4_bf16(dst + jh, y);
+            }
+        }
+        if (!has_next) break;
+        // the next tile's bias goes to the other buffer (last read two tiles ago)
+        stage_bias((k_tile + 1) & 1, ntf * BF);
+#pragma unroll
+        for (int q = 0; q < NLOAD; ++q) voff_cur[q] = voff_nxt[q];
+        tt = ntt;
+        tf = ntf;
     }
 }
 
-template <bool X_TL, bool W_FC, int BF, int BT, int BK, int DG>
-hipError_t launch_fast_one(const KernelArgs& a, hipStream_t stream) {
-    const unsigned grid = (unsigned)a.tiles_m * (unsigned)a.tiles_n;
-    hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, BF, BT, BK, DG>), dim3(grid), dim3(kThreads), 0, stream,
-                       a);
+// Tile shapes compiled for the fast kernel.
+constexpr int kBF = 256, kBT = 256, kNWF = 2, kNWT = 4, kBK = 32, kStages = 4;
+
+template <bool X_TL, bool W_FC, int DG>
+hipError_t launch_fast_one(const KernelArgs& a, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, kBF, kBT, kNWF, kNWT, kBK, kStages, DG>), dim3(grid),
+                       dim3(64 * kNWF * kNWT), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int BF, int BT, int BK, int DG>
-hipError_t dispatch_fast_layouts(bool x_tl, bool w_fc, const KernelArgs& a, hipStream_t s) {
-    if (x_tl) return w_fc ? launch_fast_one<true, true, BF, BT, BK, DG>(a, s) : launch_fast_one<true, false, BF, BT, BK, DG>(a, s);
-    return w_fc ? launch_fast_one<false, true, BF, BT, BK, DG>(a, s) : launch_fast_one<false, false, BF, BT, BK, DG>(a, s);
+template <int DG>
+hipError_t dispatch_fast_layouts(bool x_tl, bool w_fc, const KernelArgs& a, int grid, hipStream_t s) {
+    if (x_tl) return w_fc ? launch_fast_one<true, true, DG>(a, grid, s) : launch_fast_one<true, false, DG>(a, grid, s);
+    return w_fc ? launch_fast_one<false, true, DG>(a, grid, s) : launch_fast_one<false, false, DG>(a, grid, s);
 }
 
 }  // namespace
@@ -422,14 +495,23 @@ int fast_rope_groups(int head_dim, bool rope) {
     return (head_dim % 16 == 0 && (dg == 2 || dg == 4 || dg == 8)) ? dg : -1;
 }
 
+TilePlan fast_plan(int64_t M, int64_t F, int num_cus) {
+    TilePlan t{kBT, kBF, kBK, 8, 0};
+    const int64_t tiles = ((M + kBT - 1) / kBT) * ((F + kBF - 1) / kBF);
+    int64_t grid = num_cus > 0 ? num_cus : 256;           // one persistent workgroup per CU
+    if (grid > tiles) grid = tiles;
+    t.grid = (int)((grid + 7) / 8 * 8);                   // a multiple of the 8 XCDs
+    return t;
+}
+
 hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, const TilePlan& pl, const KernelArgs& a,
                                   hipStream_t stream) {
-    if (pl.bm != 128 || pl.bn != 256 || pl.bk != 32) return hipErrorInvalidValue;
+    if (pl.bm != kBT || pl.bn != kBF || pl.bk != kBK || pl.grid <= 0 || pl.grid % 8) return hipErrorInvalidValue;
     switch (dg) {
-        case 0: return dispatch_fast_layouts<256, 128, 32, 0>(x_tokens_last, w_fc, a, stream);
-        case 2: return dispatch_fast_layouts<256, 128, 32, 2>(x_tokens_last, w_fc, a, stream);
-        case 4: return dispatch_fast_layouts<256, 128, 32, 4>(x_tokens_last, w_fc, a, stream);
-        case 8: return dispatch_fast_layouts<256, 128, 32, 8>(x_tokens_last, w_fc, a, stream);
+        case 0: return dispatch_fast_layouts<0>(x_tokens_last, w_fc, a, pl.grid, stream);
+        case 2: return dispatch_fast_layouts<2>(x_tokens_last, w_fc, a, pl.grid, stream);
+        case 4: return dispatch_fast_layouts<4>(x_tokens_last, w_fc, a, pl.grid, stream);
+        case 8: return dispatch_fast_layouts<8>(x_tokens_last, w_fc, a, pl.grid, stream);
         default: return hipErrorInvalidValue;
     }
 }

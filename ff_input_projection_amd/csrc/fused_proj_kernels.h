@@ -39,6 +39,7 @@ struct KernelArgs {
 struct TilePlan {
     int bm, bn, bk;
     int group_m;         // tiles along M that share a column sweep (L2 reuse)
+    int grid;            // workgroups launched (0: one per tile)
 };
 
 // Kernel variants: storage type x activation layout x weight layout.
@@ -51,10 +52,12 @@ hipError_t launch_fused_proj(DType dt, bool x_tokens_last, bool w_fc, const Tile
 // Whether a tile plan is compiled for this combination.
 bool plan_supported(DType dt, const TilePlan& plan);
 
-// Fast bf16 kernel (F-major MFMA orientation, register epilogue, tile 128 tokens x 256
-// columns). fast_rope_groups returns the RoPE partner distance in 8-column groups it
-// needs (0 without RoPE) or -1 when the head size is not supported by it.
+// Fast bf16 kernel (F-major MFMA orientation, register epilogue, persistent workgroups
+// over 256 x 256 tiles). fast_rope_groups returns the RoPE partner distance in 8-column
+// groups it needs (0 without RoPE) or -1 when the head size is not supported by it.
+// fast_plan picks its tiles and grid (one workgroup per CU, a multiple of 8).
 int fast_rope_groups(int head_dim, bool rope);
+TilePlan fast_plan(int64_t M, int64_t F, int num_cus);
 hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, const TilePlan& plan,
                                   const KernelArgs& args, hipStream_t stream);
 

@@ -92,6 +92,19 @@ def test_small_ragged_all_tokens(wl, kernel_choice):
     _check(wl, inp, outs, all_tokens(wl), wl.name)
 
 
+@pytest.mark.skip(reason="the persistent fast kernel faulted the GPU on the small-K workload "
+                         "(x [2,320,64,64], W [320,960]: padded K steps, a ragged column tile, fewer "
+                         "tiles than CUs) with no cause found yet; it is switched off for every shape "
+                         "that is not an exact tiling, and this case stays off the GPU until the cause "
+                         "is shown")
+def test_fast_kernel_on_padded_or_ragged_tiling(monkeypatch):
+    monkeypatch.setenv("FUSED_PROJ_KERNEL", "fast")
+    wl = WORKLOADS["smallk_qkv_bf16"]
+    inp = make_inputs(wl)
+    _, outs = run_gpu(wl, inp, DEV)
+    _check(wl, inp, outs, sample_tokens(wl, 384, seed=1), wl.name)
+
+
 def test_strided_views_channel_slice_and_row_stride(kernel_choice):
     """x as a view: a channel slice of a wider channels-first tensor, and a token-major
     view whose row stride exceeds C. No copy is made; results match the oracle."""
