@@ -137,6 +137,7 @@ struct fused_proj_plan {
     float* d_cos = nullptr;
     float* d_sin = nullptr;
     void* d_zeros = nullptr;
+    unsigned* d_desc = nullptr;  // fast kernel: column descriptors
     int device = 0;
     bool debug_sync = false;
 };
@@ -170,8 +171,8 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     }
     // Kernel choice. The fast bf16 kernel needs a RoPE head size of 32, 64 or 128 (or no
     // RoPE) and x and W spans under 4 GiB (it addresses them with 32-bit offsets). It is
-    // used only on exact tilings -- tokens and columns multiples of its 256 x 256 tile,
-    // channels a multiple of 128, at least one tile per CU -- the shapes it has been
+    // used only on exact tilings -- tokens and columns multiples of its tile, channels a
+    // multiple of its K-step group, at least one tile per CU -- the shapes it has been
     // verified on; every other shape goes to the general kernel.
     // FUSED_PROJ_KERNEL=general forces the general kernel (the tests use it to cover both);
     // FUSED_PROJ_KERNEL=fast takes the fast kernel on any shape it can address.
@@ -182,9 +183,10 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     const bool fits32 = r.x_span * 2 < (int64_t(1) << 32) && desc->channels * r.F * 2 < (int64_t(1) << 32);
     const fp::TilePlan fp_plan = fp::fast_plan(r.M, r.F, num_cus);
     const int64_t fast_tiles = (r.M / fp_plan.bm) * (r.F / fp_plan.bn);
-    const bool exact = r.M % fp_plan.bm == 0 && r.F % fp_plan.bn == 0 && desc->channels % 128 == 0 &&
+    const bool exact = r.M % fp_plan.bm == 0 && r.F % fp_plan.bn == 0 && desc->channels % fp::fast_k_multiple() == 0 &&
                        desc->channels > 0 && fast_tiles >= (num_cus > 0 ? num_cus : 256);
-    h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && (exact || want_fast) && !want_general;
+    const bool addressable = fp::fast_addressable(r.M, r.S, desc->ff_dim, r.qw);
+    h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && addressable && (exact || want_fast) && !want_general;
     h->dg = dg < 0 ? 0 : dg;
     h->tile = h->fast ? fp_plan : fp::TilePlan{128, 128, h->dt == fp::DType::BF16 ? 64 : 32, 8, 0};
 
@@ -245,6 +247,19 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
         return FUSED_PROJ_EHIP;
     }
     a.zeros = h->d_zeros;
+    if (h->fast) {
+        const int64_t n = fp::fast_col_desc_entries(r.F);
+        std::vector<unsigned> hd((size_t)n);
+        fp::fast_col_desc(r.S, desc->ff_dim, desc->n_heads, desc->head_dim, r.F, hd.data(), n);
+        e = hipMalloc((void**)&h->d_desc, (size_t)n * sizeof(unsigned));
+        if (e == hipSuccess) e = hipMemcpy(h->d_desc, hd.data(), (size_t)n * sizeof(unsigned), hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            g_last_hip = e;
+            fused_proj_destroy(h);
+            return FUSED_PROJ_EHIP;
+        }
+    }
+    a.col_desc = h->d_desc;
     *out = h;
     return FUSED_PROJ_OK;
 }
@@ -318,7 +333,9 @@ int fused_proj_destroy(fused_proj_t h) {
     hipError_t e1 = h->d_cos ? hipFree(h->d_cos) : hipSuccess;
     hipError_t e2 = h->d_sin ? hipFree(h->d_sin) : hipSuccess;
     hipError_t e3 = h->d_zeros ? hipFree(h->d_zeros) : hipSuccess;
+    hipError_t e4 = h->d_desc ? hipFree(h->d_desc) : hipSuccess;
     if (e2 == hipSuccess) e2 = e3;
+    if (e2 == hipSuccess) e2 = e4;
     delete h;
     if (e1 != hipSuccess || e2 != hipSuccess) {
         g_last_hip = e1 != hipSuccess ? e1 : e2;

@@ -28,15 +28,21 @@
 // ones through ds_read_b128. Chunks outside the problem (ragged M, N or K) are
 // read from a small zero block instead, so no access leaves the operands.
 //
-// Schedule. The kernel is persistent: one workgroup of 8 waves per CU, each
-// workgroup walking a list of 256 x 256 tiles (2 x 4 waves of 128 (f) x 64
-// (tokens), 128 accumulators each, two waves per SIMD). The direct-load
-// pipeline is four stages deep and runs straight on into the next tile: the
-// first K steps of tile i+1 are in flight while tile i finishes its last K
-// steps and its epilogue. Larger tiles halve the panel traffic from L2 per
-// flop compared with 128-token tiles (the L2->CU path, about 54 B/clk per CU
-// measured, is the scarce resource), and the workgroup's tiles are taken from
-// a contiguous, grouped range of the XCD it runs on.
+// Schedule. The kernel is persistent, one workgroup of 8 waves per CU. Waves
+// w and w+4 share a SIMD (measured), so the waves form two groups of four, one
+// wave per SIMD each. Each group walks its own list of 256 (f) x 128 (token)
+// tiles (2 x 2 waves of 128 x 64, 128 accumulators per lane) through its own
+// LDS pipeline, six K steps of 16 deep. The two groups run the same cadence --
+// every wave passes one workgroup barrier per slot -- and a tile takes KT
+// slots of K steps followed by 32 epilogue slots (one 8-column x 32-token
+// group each), but group 1 runs half a tile behind group 0. So while one
+// group's waves spend their slots on the VALU work of an epilogue, the
+// other group's waves keep the matrix cores busy on the same SIMDs: the
+// epilogue overlaps the MFMAs instead of following them. The direct-load
+// pipeline runs straight on into a group's next tile, and the operands of the
+// next K step are read from LDS while the MFMAs of the current one run. The
+// workgroup's tiles come from a contiguous, grouped range of the XCD it runs on,
+// and the two groups take alternate tiles of it.
 #include "device_common.h"
 #include "fused_proj_kernels.h"
 
@@ -45,6 +51,15 @@ namespace {
 
 using namespace dev;
 
+// Wait states that every inline-asm memory instruction below starts with. The compiler
+// inserts the wait states its own instructions need, but it cannot see inside inline
+// asm: right before one it may restore a spilled SGPR with v_readlane (a VALU write of
+// an SGPR) or set M0 with an SALU move. On gfx9-family chips a VMEM instruction that
+// reads an SGPR written by VALU needs 5 wait states first (the compiler itself puts
+// s_nop 4 there for its own loads), and an LDS-DMA load needs 1 after an SALU write of
+// M0. Without them the load can use a stale base address.
+#define HAZARD_NOPS "s_nop 4\n\t"
+
 // s_waitcnt vmcnt(N): at most N of this wave's vector memory operations outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -52,7 +67,7 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-__device__ __forceinline__ void store4_bf16(__bf16* dst, const float* o) {
+__device__ __forceinline__ void store4_bf16(char* dst, const float* o) {
     bf16x4 v;
     v[0] = (__bf16)o[0];
     v[1] = (__bf16)o[1];
@@ -61,12 +76,20 @@ __device__ __forceinline__ void store4_bf16(__bf16* dst, const float* o) {
     *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, v);
 }
 
-__device__ __forceinline__ void load4_bias(const __bf16* bias, int f, float* b) {
-    const bf16x4 v = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(bias + f));
-    b[0] = (float)v[0];
-    b[1] = (float)v[1];
-    b[2] = (float)v[2];
-    b[3] = (float)v[3];
+// Four bf16 bias values from LDS, as fp32.
+__device__ __forceinline__ f32x4 bias4(const __bf16* p) {
+    const bf16x4 v = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(p));
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+// Four consecutive dwords of read-only memory at a wave-uniform address, through the
+// scalar unit. A vector load here would make the compiler wait (vmcnt) for every older
+// vector memory operation, including the direct-to-LDS loads of the next tile in flight;
+// the scalar load has its own counter, waited for right away.
+__device__ __forceinline__ u32x4 scalar_load4(const unsigned* p) {
+    u32x4 v;
+    asm volatile(HAZARD_NOPS "s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+    return v;
 }
 
 // LDS reads at integer byte addresses: base + compile-time constant folds into the
@@ -126,7 +149,7 @@ struct FastCfg {
 };
 
 // Wave-constant operand state: LDS read bases and the direct-load chunk map.
-template <class C, bool X_TL, bool W_FC, int BK>
+template <class C, bool X_TL, bool W_FC, int BK, bool TAILK>
 struct FastPipe {
     unsigned wbase[C::TI][W_FC ? C::KK : 1];   // LDS read bases of the W^T operands
     unsigned xbase[C::TJ][X_TL ? C::KK : 1];   // and of the x operands
@@ -139,13 +162,14 @@ struct FastPipe {
 
     // Issue the direct loads of K step ks (of the tile whose chunk offsets are voff) into
     // stage ST. Chunks at or past K (a ragged last step, or the steps that pad the step
-    // count to a multiple of the stage count) are read from the zero block.
+    // count to a multiple of the stage count) are read from the zero block; without
+    // TAILK every step is whole.
     template <int ST>
     __device__ __forceinline__ void issue(const unsigned (&voff)[C::NLOAD], int ks, int K,
                                           const char* zeros) const {
         const char* ws = wsrc + (int64_t)ks * wstep;
         const char* xs = xsrc + (int64_t)ks * xstep;
-        const bool tail = (ks + 1) * BK > K;
+        const bool tail = TAILK && (ks + 1) * BK > K;
 #pragma unroll
         for (int q = 0; q < C::NLOAD; ++q) {
             const bool isw = q < C::W_INSTR;
@@ -156,46 +180,52 @@ struct FastPipe {
             if (!tail) {
                 // SGPR base + 32-bit lane offset: no per-load VALU. Inline asm keeps the
                 // compiler from waiting on every stage in flight before each LDS read.
-                asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff[q]), "s"(base), "{m0}"(dst) : "memory");
+                asm volatile(HAZARD_NOPS "global_load_lds_dwordx4 %0, %1" ::"v"(voff[q]), "s"(base), "{m0}"(dst)
+                             : "memory");
             } else {
                 const char* a = (ks * BK + kofs[q] < K) ? base + voff[q] : zeros;
-                asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(a), "{m0}"(dst) : "memory");
+                asm volatile(HAZARD_NOPS "global_load_lds_dwordx4 %0, off" ::"v"(a), "{m0}"(dst) : "memory");
             }
         }
     }
 
-    // All MFMA k steps of stage ST.
-    template <int ST>
-    __device__ __forceinline__ void compute(f32x16 (&acc)[C::TI][C::TJ]) const {
-        bf16x8 a[C::KK][C::TI], b[C::KK][C::TJ];
+    // MFMA operands of one 16-deep k step: TI W^T row blocks and TJ token blocks.
+    struct Ops {
+        bf16x8 a[C::TI];
+        bf16x8 b[C::TJ];
+    };
+
+    // LDS reads of k step KK of stage ST.
+    template <int ST, int KK>
+    __device__ __forceinline__ Ops read() const {
+        Ops o;
 #pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk) {
-#pragma unroll
-            for (int i = 0; i < C::TI; ++i) {
-                if constexpr (W_FC) {
-                    a[kk][i] = __builtin_bit_cast(bf16x8, lds_b128(wbase[i][kk] + ST * C::W_BYTES));
-                } else {
-                    const unsigned o = wbase[i][0] + ST * C::W_BYTES + kk * 16 * C::W_CPR * 16;
-                    a[kk][i] = join_tr(lds_tr16(o), lds_tr16(o + 4 * C::W_CPR * 16));
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < C::TJ; ++j) {
-                if constexpr (X_TL) {
-                    b[kk][j] = __builtin_bit_cast(bf16x8, lds_b128(xbase[j][kk] + ST * C::X_BYTES));
-                } else {
-                    const unsigned o = xbase[j][0] + ST * C::X_BYTES + kk * 16 * C::X_CPR * 16;
-                    b[kk][j] = join_tr(lds_tr16(o), lds_tr16(o + 4 * C::X_CPR * 16));
-                }
+        for (int i = 0; i < C::TI; ++i) {
+            if constexpr (W_FC) {
+                o.a[i] = __builtin_bit_cast(bf16x8, lds_b128(wbase[i][KK] + ST * C::W_BYTES));
+            } else {
+                const unsigned a = wbase[i][0] + ST * C::W_BYTES + KK * 16 * C::W_CPR * 16;
+                o.a[i] = join_tr(lds_tr16(a), lds_tr16(a + 4 * C::W_CPR * 16));
             }
         }
 #pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk)
+        for (int j = 0; j < C::TJ; ++j) {
+            if constexpr (X_TL) {
+                o.b[j] = __builtin_bit_cast(bf16x8, lds_b128(xbase[j][KK] + ST * C::X_BYTES));
+            } else {
+                const unsigned a = xbase[j][0] + ST * C::X_BYTES + KK * 16 * C::X_CPR * 16;
+                o.b[j] = join_tr(lds_tr16(a), lds_tr16(a + 4 * C::X_CPR * 16));
+            }
+        }
+        return o;
+    }
+
+    static __device__ __forceinline__ void mma(f32x16 (&acc)[C::TI][C::TJ], const Ops& o) {
 #pragma unroll
-            for (int i = 0; i < C::TI; ++i)
+        for (int i = 0; i < C::TI; ++i)
 #pragma unroll
-                for (int j = 0; j < C::TJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][i], b[kk][j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < C::TJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
     }
 };
 
@@ -271,213 +301,299 @@ __device__ __forceinline__ bool block_tile(int k, int tiles_t, int tiles_f, int 
     return true;
 }
 
+// Tile shapes compiled for the fast kernel: per group, BF output columns x BT tokens,
+// NWF x NWT waves, K steps of BK through STAGES LDS stages.
+constexpr int kBF = 256, kBT = 128, kNWF = 2, kNWT = 2, kBK = 16, kStages = 6;
+
+// Number of tiles block_tile hands this workgroup.
+__device__ __forceinline__ int block_tile_count(int tiles_t, int tiles_f) {
+    const int total = tiles_t * tiles_f;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
+    const int count = (total >> 3) + (xcd < (total & 7) ? 1 : 0);
+    return slot < count ? (count - slot + per_xcd - 1) / per_xcd : 0;
+}
+
 // X_TL: x token-major [b,s,c] (else channels-first). W_FC: W [F,C] (else [C,F]).
-// DG: RoPE partner distance in 8-column groups (hd/16), 0 = no RoPE.
-template <bool X_TL, bool W_FC, int BF, int BT, int NWF, int NWT, int BK, int STAGES, int DG>
-__global__ __launch_bounds__(64 * NWF * NWT, 1) void fused_proj_fast_kernel(KernelArgs p) {
-    using C = FastCfg<X_TL, W_FC, BF, BT, NWF, NWT, BK, STAGES>;
+// DG: RoPE partner distance in 8-column groups (hd/16), 0 = no RoPE. TAILK: K is not a
+// multiple of STAGES * BK (some K steps are partial or padding).
+template <bool X_TL, bool W_FC, int DG, bool TAILK>
+__global__ __launch_bounds__(512, 1) void fused_proj_fast_kernel(KernelArgs p) {
+    constexpr int BF = kBF, BT = kBT, BK = kBK, STAGES = kStages;
+    using C = FastCfg<X_TL, W_FC, BF, BT, kNWF, kNWT, BK, STAGES>;   // one group's tile
+    using Pipe = FastPipe<C, X_TL, W_FC, BK, TAILK>;
+    using Ops = typename Pipe::Ops;
     constexpr int WF = C::WF, WT = C::WT, TI = C::TI, TJ = C::TJ, NG = C::NG, NLOAD = C::NLOAD;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
-    __shared__ __attribute__((aligned(16))) float bias_s[2][BF];   // tile bias (fp32), double-buffered
+    constexpr int EPI = TJ * NG;   // epilogue slots per tile: one per (token block, column group)
+    static_assert(C::NW == 4 && C::KK == 1, "four waves per group, one MFMA k step per K step");
+    static_assert(STAGES == 6, "the wait counts below are written for six stages");
+    static_assert(NG == 16, "one 16-entry column descriptor load per wave");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2][C::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) __bf16 bias_s[2][2][BF];   // [group][buffer]: tile bias
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int wf = wave / NWT, wt = wave % NWT;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wid >> 2, wave = wid & 3;   // group, wave within the group
+    const int wf = wave / kNWT, wt = wave % kNWT;
     const int K = p.K, N = p.N, M = (int)p.M, S = p.S;
     const char* const zeros = static_cast<const char*>(p.zeros);
     const __bf16* const bias = static_cast<const __bf16*>(p.bias);
 
-    int tt, tf;
-    if (!block_tile(0, p.tiles_m, p.tiles_n, p.group_m, tt, tf)) return;
+    // K steps per tile, padded to a multiple of the stage count so that step s of every
+    // tile uses stage s mod STAGES (the padding steps read zeros). At least one group.
+    const int KT = K > 0 ? (K + BK - 1) / BK : 1;
+    const int KTp = (KT + STAGES - 1) / STAGES * STAGES;
+    // Slots: a group's tile takes P; group 1 starts half a tile later; both groups pass
+    // the same number of barriers (idle slots pad the shorter one).
+    const int n_wg = block_tile_count(p.tiles_m, p.tiles_n);
+    const int P = KTp + EPI;
+    const int n0_tiles = (n_wg + 1) / 2, n1_tiles = n_wg / 2;   // group g takes the workgroup's tiles 2i + g
+    const int end0 = n0_tiles > 0 ? 1 + n0_tiles * P : 0;
+    const int end1 = n1_tiles > 0 ? P / 2 + 1 + n1_tiles * P : 0;
+    const int total_slots = end0 > end1 ? end0 : end1;
+    const int n_mine = grp ? n1_tiles : n0_tiles, my_off = grp ? P / 2 : 0;
 
-    FastPipe<C, X_TL, W_FC, BK> pp;
+    Pipe pp;
     pp.wave = wave;
-    pp.lds0 = (unsigned)(size_t)(lds_void*)smem;
+    pp.lds0 = (unsigned)(size_t)(lds_void*)smem[grp];
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
-        if constexpr (W_FC) {
-#pragma unroll
-            for (int kk = 0; kk < C::KK; ++kk) pp.wbase[i][kk] = pp.lds0 + k_operand_base<C::W_CPR>(wf * WF + 32 * i, kk, lane);
-        } else {
-            pp.wbase[i][0] = pp.lds0 + mn_operand_base<C::W_CPR>(wf * WF + 32 * i, lane);
-        }
+        if constexpr (W_FC) pp.wbase[i][0] = pp.lds0 + k_operand_base<C::W_CPR>(wf * WF + 32 * i, 0, lane);
+        else pp.wbase[i][0] = pp.lds0 + mn_operand_base<C::W_CPR>(wf * WF + 32 * i, lane);
     }
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-        if constexpr (X_TL) {
-#pragma unroll
-            for (int kk = 0; kk < C::KK; ++kk)
-                pp.xbase[j][kk] = pp.lds0 + C::X_REGION + k_operand_base<C::X_CPR>(wt * WT + 32 * j, kk, lane);
-        } else {
-            pp.xbase[j][0] = pp.lds0 + C::X_REGION + mn_operand_base<C::X_CPR>(wt * WT + 32 * j, lane);
-        }
+        if constexpr (X_TL) pp.xbase[j][0] = pp.lds0 + C::X_REGION + k_operand_base<C::X_CPR>(wt * WT + 32 * j, 0, lane);
+        else pp.xbase[j][0] = pp.lds0 + C::X_REGION + mn_operand_base<C::X_CPR>(wt * WT + 32 * j, lane);
     }
     pp.wsrc = static_cast<const char*>(p.w);
     pp.xsrc = static_cast<const char*>(p.x);
     pp.wstep = (W_FC ? (int64_t)BK : (int64_t)BK * N) * 2;
     pp.xstep = (X_TL ? (int64_t)BK : (int64_t)BK * p.x_sc) * 2;
 
-    unsigned voff_cur[NLOAD], voff_nxt[NLOAD];
-    tile_offsets<C, X_TL, W_FC>(voff_cur, pp.kofs, tt * BT, tf * BF, wave, lane, K, N, M, S, p.x_sb, p.x_ss,
-                                p.x_sc);
-
-    // bias of the first tile (the barriers of its first K step publish it)
-    auto stage_bias = [&](int buf, int n0) __attribute__((always_inline)) {
-        if (tid < BF / 4) {
-            const int f = n0 + 4 * tid;
-            float b4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (bias != nullptr && f < N) load4_bias(bias, f, b4);
-            *reinterpret_cast<f32x4*>(&bias_s[buf][4 * tid]) = f32x4{b4[0], b4[1], b4[2], b4[3]};
+    // The bias slice of a tile, copied into bias_s[grp][buf] by the group's first wave's
+    // first 32 lanes with the same direct-to-LDS loads as the operands (from the zero
+    // block where there is no bias). It is issued with the tile's first K steps, so the
+    // waits and barriers of those steps also cover it.
+    const unsigned bias_lds = (unsigned)(size_t)(lds_void*)&bias_s[grp][0][0];
+    auto issue_bias = [&](int buf, int n0) __attribute__((always_inline)) {
+        if (wave == 0 && lane < BF / 8) {
+            const int f = n0 + 8 * lane;
+            const char* src = (bias != nullptr && f < N) ? reinterpret_cast<const char*>(bias + f) : zeros;
+            const unsigned dst = bias_lds + (unsigned)buf * (BF * 2);
+            asm volatile(HAZARD_NOPS "global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
         }
     };
-    stage_bias(0, tf * BF);
-
-    // K steps per tile, padded to a multiple of the stage count so that step s of every
-    // tile uses stage s mod STAGES (the padding steps read zeros). At least one step.
-    const int KT = K > 0 ? (K + BK - 1) / BK : 1;
-    const int KTp = (KT + STAGES - 1) / STAGES * STAGES;
-
-    // prologue: the first STAGES-1 steps of the first tile
-    pp.template issue<0>(voff_cur, 0, K, zeros);
-    pp.template issue<1>(voff_cur, 1, K, zeros);
-    if constexpr (STAGES > 3) pp.template issue<2>(voff_cur, 2, K, zeros);
-    if constexpr (STAGES > 4) pp.template issue<3>(voff_cur, 3, K, zeros);
-    static_assert(STAGES <= 5, "prologue");
 
     // epilogue constants
     const int hl = lane >> 5;
-    __bf16* __restrict__ const out_ff = static_cast<__bf16*>(p.ff);
-    __bf16* __restrict__ const out_q = static_cast<__bf16*>(p.q);
-    __bf16* __restrict__ const out_k = static_cast<__bf16*>(p.k);
-    __bf16* __restrict__ const out_v = static_cast<__bf16*>(p.v);
+    char* const out_ff = static_cast<char*>(p.ff);
     const float* __restrict__ const rope_cos = p.rope_cos;
     const float* __restrict__ const rope_sin = p.rope_sin;
-    const int ff_dim = p.ff_dim, qw = p.qw, hd = p.head_dim, n_heads = p.n_heads, act = p.act;
-    const int64_t head_stride = (int64_t)S * hd;   // elements between heads of one slab
+    const int ff_dim = p.ff_dim, hd = p.head_dim, act = p.act;
+    const int64_t slab_elems = (int64_t)S * p.qw;   // q/k/v elements of one slab (all heads)
 
-    for (int k_tile = 0;; ++k_tile) {
+    int tt = 0, tf = 0;
+    unsigned voff_cur[NLOAD], voff_nxt[NLOAD];
+    Ops cur;
+    if (n_mine > 0) {
+        // The group's first tile: its first STAGES-1 K steps and its bias go in flight
+        // at once, whatever the group's start slot.
+        block_tile(grp, p.tiles_m, p.tiles_n, p.group_m, tt, tf);
+        tile_offsets<C, X_TL, W_FC>(voff_cur, pp.kofs, tt * BT, tf * BF, wave, lane, K, N, M, S, p.x_sb, p.x_ss,
+                                    p.x_sc);
+        pp.template issue<0>(voff_cur, 0, K, zeros);
+        issue_bias(0, tf * BF);
+        pp.template issue<1>(voff_cur, 1, K, zeros);
+        pp.template issue<2>(voff_cur, 2, K, zeros);
+        pp.template issue<3>(voff_cur, 3, K, zeros);
+        pp.template issue<4>(voff_cur, 4, K, zeros);
+    }
+    for (int s = 0; s < my_off; ++s) __syncthreads();   // idle slots before the group starts
+    if (n_mine > 0) {
+        // one slot: step 0 landed (steps 1-4 may still be in flight); read its operands
+        wait_vmcnt<4 * NLOAD>();
+        __syncthreads();
+        cur = pp.template read<0, 0>();
+    }
+
+    for (int i = 0; i < n_mine; ++i) {
         const int m0 = tt * BT, n0 = tf * BF;
         int ntt = 0, ntf = 0;
-        const bool has_next = block_tile(k_tile + 1, p.tiles_m, p.tiles_n, p.group_m, ntt, ntf);
-        if (has_next)
+        const bool has_next = i + 1 < n_mine;
+        if (has_next) {
+            block_tile(2 * (i + 1) + grp, p.tiles_m, p.tiles_n, p.group_m, ntt, ntf);
             tile_offsets<C, X_TL, W_FC>(voff_nxt, pp.kofs, ntt * BT, ntf * BF, wave, lane, K, N, M, S, p.x_sb,
                                         p.x_ss, p.x_sc);
+        } else {
+            // past the group's last tile the loads repeat this tile's first steps (in
+            // bounds, never read), which keeps the K loop free of branches
+            ntf = tf;
+#pragma unroll
+            for (int q = 0; q < NLOAD; ++q) voff_nxt[q] = voff_cur[q];
+        }
 
         f32x16 acc[TI][TJ];
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
+        for (int a = 0; a < TI; ++a)
 #pragma unroll
-            for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
+            for (int j = 0; j < TJ; ++j) acc[a][j] = f32x16{};
 
-        // One K step: wait for this wave's loads of the step (the loads of up to STAGES-2
-        // later steps may stay in flight), barrier (every wave's loads landed; every wave is
-        // done with the stage about to be refilled), refill it STAGES-1 steps ahead --
-        // from the next tile once this one runs out -- then compute.
-        auto k_step = [&](auto stc, int kt) __attribute__((always_inline)) {
+        // One K step (one slot), whose operands are already in registers: wait for this
+        // wave's loads of the next step (those of the three after it may stay in flight),
+        // barrier (every wave of the group has its loads of the next step landed and has
+        // consumed the stage of the previous step), refill that stage with the step
+        // STAGES-1 ahead -- the next tile's first steps once this one runs out -- and read
+        // the next step's operands while this step's MFMAs run.
+        auto k_step = [&](auto stc, const unsigned (&vo)[NLOAD], int s_load) __attribute__((always_inline)) {
             constexpr int ST = decltype(stc)::value;
-            const int later = (KTp - 1 - kt) + (has_next ? KTp : 0);  // steps after kt still to run
-            if (later >= STAGES - 2) wait_vmcnt<(STAGES - 2) * NLOAD>();
-            else if (STAGES > 3 && later == 1) wait_vmcnt<NLOAD>();
-            else wait_vmcnt<0>();
+            constexpr int SN = (ST + 1) % STAGES, SL = (ST + STAGES - 1) % STAGES;
+            wait_vmcnt<3 * NLOAD>();
             __syncthreads();
-            const int s_next = kt + STAGES - 1;
-            constexpr int SN = (ST + STAGES - 1) % STAGES;
-            if (s_next < KTp) pp.template issue<SN>(voff_cur, s_next, K, zeros);
-            else if (has_next) pp.template issue<SN>(voff_nxt, s_next - KTp, K, zeros);
-            pp.template compute<ST>(acc);
+            pp.template issue<SL>(vo, s_load, K, zeros);
+            const Ops nxt = pp.template read<SN, 0>();
+            Pipe::mma(acc, cur);
+            cur = nxt;
         };
-        for (int kt = 0; kt < KTp; kt += STAGES) {
-            k_step(std::integral_constant<int, 0>{}, kt);
-            k_step(std::integral_constant<int, 1>{}, kt + 1);
-            k_step(std::integral_constant<int, 2>{}, kt + 2);
-            if constexpr (STAGES > 3) k_step(std::integral_constant<int, 3>{}, kt + 3);
-            if constexpr (STAGES > 4) k_step(std::integral_constant<int, 4>{}, kt + 4);
+        for (int kt = 0; kt < KTp - STAGES; kt += STAGES) {
+            k_step(std::integral_constant<int, 0>{}, voff_cur, kt + 5);
+            k_step(std::integral_constant<int, 1>{}, voff_cur, kt + 6);
+            k_step(std::integral_constant<int, 2>{}, voff_cur, kt + 7);
+            k_step(std::integral_constant<int, 3>{}, voff_cur, kt + 8);
+            k_step(std::integral_constant<int, 4>{}, voff_cur, kt + 9);
+            k_step(std::integral_constant<int, 5>{}, voff_cur, kt + 10);
         }
+        // the last group of steps: its loads start the next tile (bias with its step 0);
+        // the last step reads nothing ahead (the next tile's first operands are read at
+        // the end of the epilogue, so that they do not occupy registers during it)
+        k_step(std::integral_constant<int, 0>{}, voff_cur, KTp - 1);
+        k_step(std::integral_constant<int, 1>{}, voff_nxt, 0);
+        issue_bias((i + 1) & 1, ntf * BF);
+        k_step(std::integral_constant<int, 2>{}, voff_nxt, 1);
+        k_step(std::integral_constant<int, 3>{}, voff_nxt, 2);
+        k_step(std::integral_constant<int, 4>{}, voff_nxt, 3);
+        wait_vmcnt<3 * NLOAD>();
+        __syncthreads();
+        pp.template issue<STAGES - 2>(voff_nxt, 4, K, zeros);
+        Pipe::mma(acc, cur);
 
-        // ---- epilogue in registers. acc[i][j][e]: column f = 32i + 8(e/4) + 4(lane/32) +
-        // e%4, token 32j + lane%32 (both relative to the wave tile). Outputs never overlap
-        // the inputs (checked on the host), so loads may be hoisted above stores.
-        const float* const bias_t = bias_s[k_tile & 1];
+        // ---- epilogue in registers, one slot per (token block j, column group G).
+        // acc[a][j][e]: column f = 32a + 8(e/4) + 4(lane/32) + e%4, token 32j + lane%32
+        // (both relative to the wave tile). Outputs never overlap the inputs (checked
+        // on the host), so loads may be hoisted above stores.
+        //
+        // Per-lane byte offsets (32-bit: the host keeps every output under 4 GiB) of this
+        // lane's token: its ff row, its q/k/v row of head 0, its cos/sin row.
+        unsigned ff_off[TJ], hv_off[TJ], rp_off[TJ];
+        bool tv[TJ];
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
             const int t = m0 + wt * WT + 32 * j + (lane & 31);
-            const bool tv = t < M;
-            const int bi = t / S, s = t - bi * S;
-            __bf16* const ff_row = out_ff + (int64_t)t * ff_dim;
-            const int64_t tok = (int64_t)bi * n_heads * head_stride + (int64_t)s * hd;   // head 0 of this token
-            const float* const cs_row = rope_cos + (int64_t)s * (DG * 8);
-            const float* const sn_row = rope_sin + (int64_t)s * (DG * 8);
+            tv[j] = t < M;
+            const int tc = tv[j] ? t : 0;
+            const int bi = tc / S, s = tc - bi * S;
+            ff_off[j] = (unsigned)((tc * ff_dim + 4 * hl) * 2);
+            hv_off[j] = (unsigned)(((int64_t)bi * slab_elems + (int64_t)s * hd + 4 * hl) * 2);
+            rp_off[j] = (unsigned)((s * (DG * 8) + 4 * hl) * 4);
+        }
+        // The wave's 16 column groups: kind (0 ff, 1 q, 2 k, 3 v) in bits 30-31 and the
+        // element offset of the group's first column in the low bits (ff: column; q/k/v:
+        // head * S * hd + place in head), read four at a time by the scalar unit.
+        const int fw = n0 + wf * WF;
+        const unsigned* const desc_w = p.col_desc + (fw >> 3);
+        const __bf16* const bias_t = bias_s[grp][i & 1] + wf * WF + 4 * hl;
+        // whether the wave's columns meet the q or k slice (then RoPE applies)
+        const bool wave_rope = DG > 0 && fw < ff_dim + 2 * p.qw && fw + WF > ff_dim;
+        constexpr int HD = DG > 0 ? 16 * DG : 16, HALF = HD / 2, NR = HALF / 8, NRB = NR > 4 ? 4 : NR;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+            // cos/sin of this lane's token at its 4 columns of each first-half group of a
+            // head; every head of the wave uses the same ones. Loaded before this token
+            // block's stores, so that the wait for them does not wait for those stores --
+            // all at once for head sizes up to 64, in two halves for 128 (registers).
+            f32x4 rc[NRB], rsn[NRB];
+            auto load_rope = [&](int r0) __attribute__((always_inline)) {
+#pragma unroll
+                for (int r = 0; r < NRB; ++r) {
+                    rc[r] = f32x4{};
+                    rsn[r] = f32x4{};
+                }
+                if (wave_rope) {
+#pragma unroll
+                    for (int r = 0; r < NRB; ++r) {
+                        const char* const c = reinterpret_cast<const char*>(rope_cos + 8 * (r0 + r)) + rp_off[j];
+                        const char* const sn = reinterpret_cast<const char*>(rope_sin + 8 * (r0 + r)) + rp_off[j];
+                        rc[r] = *reinterpret_cast<const f32x4*>(c);
+                        rsn[r] = *reinterpret_cast<const f32x4*>(sn);
+                    }
+                }
+            };
+            load_rope(0);
+            u32x4 desc4;
 #pragma unroll
             for (int G = 0; G < NG; ++G) {
-                const int f8 = n0 + wf * WF + 8 * G;  // wave-uniform column group
-                if (f8 >= N) continue;
-                const int fl = wf * WF + 8 * G + 4 * hl;   // this lane's first column inside the tile
+                __syncthreads();   // the slot of (j, G)
+                if (G % 4 == 0) desc4 = scalar_load4(desc_w + G);
+                if (fw + 8 * G >= N) continue;   // ragged last column tile
+                const unsigned d = desc4[G % 4];
+                const unsigned kind = d >> 30, off = d & 0x3fffffffu;
+                const f32x4 bv = bias4(bias_t + 8 * G);
                 float y[4];
-                const f32x4 bv = *reinterpret_cast<const f32x4*>(bias_t + fl);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) y[u] = acc[G >> 2][j][4 * (G & 3) + u] + bv[u];
-                if (f8 < ff_dim) {
+                if (kind == 0) {
                     if (act == 1) {
 #pragma unroll
                         for (int u = 0; u < 4; ++u) y[u] = gelu_erf_fast(y[u]);
                     }
-                    if (tv) store4_bf16(ff_row + n0 + fl, y);
+                    if (tv[j]) store4_bf16(out_ff + (size_t)off * 2 + ff_off[j], y);
                     continue;
                 }
-                const int r = f8 - ff_dim;
-                const int which = r / qw;
-                const int rem = r - which * qw;
-                const int h = rem / hd;
-                __bf16* const dst = (which == 0 ? out_q : which == 1 ? out_k : out_v) + tok + h * head_stride;
-                if (DG > 0 && which < 2) {
-                    // Heads start on head_dim boundaries of this wave's columns, so the
-                    // group's place inside its head is a compile-time constant. A
-                    // first-half group is computed together with its partner DG groups on;
-                    // the partner's own iteration skips.
-                    constexpr int HD = DG > 0 ? 16 * DG : 16, HALF = HD / 2;
+                char* const base = static_cast<char*>(kind == 1 ? p.q : kind == 2 ? p.k : p.v) + (size_t)off * 2;
+                if (DG > 0 && kind != 3) {
+                    // Heads start on head_dim boundaries of the wave's columns, so the
+                    // group's place in its head is a compile-time constant. A first-half
+                    // group is rotated together with its partner DG groups on, whose own
+                    // slot does nothing.
                     const int jh8 = (8 * G) % HD;
                     if (jh8 >= HALF || G + DG >= NG) continue;
-                    const int G2 = (G + DG < NG) ? G + DG : G;  // constant after unrolling
-                    const int jh = jh8 + 4 * hl;
-                    float y2[4];
-                    const f32x4 b2 = *reinterpret_cast<const f32x4*>(bias_t + fl + HALF);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) y2[u] = acc[G2 >> 2][j][4 * (G2 & 3) + u] + b2[u];
-                    const f32x4 c = *reinterpret_cast<const f32x4*>(cs_row + jh);
-                    const f32x4 sn = *reinterpret_cast<const f32x4*>(sn_row + jh);
+                    const int G2 = (G + DG < NG) ? G + DG : G;   // constant after unrolling
+                    if (NR > NRB && jh8 == 8 * NRB) load_rope(NRB);   // second half (head size 128)
+                    const f32x4 b2 = bias4(bias_t + 8 * G2);
+                    const f32x4 c = rc[(jh8 / 8) % NRB], sn = rsn[(jh8 / 8) % NRB];
                     float o1[4], o2[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        o1[u] = y[u] * c[u] - y2[u] * sn[u];
-                        o2[u] = y2[u] * c[u] + y[u] * sn[u];
+                        const float y2 = acc[G2 >> 2][j][4 * (G2 & 3) + u] + b2[u];
+                        o1[u] = y[u] * c[u] - y2 * sn[u];
+                        o2[u] = y2 * c[u] + y[u] * sn[u];
                     }
-                    if (tv) {
-                        store4_bf16(dst + jh, o1);
-                        store4_bf16(dst + jh + HALF, o2);
+                    if (tv[j]) {
+                        store4_bf16(base + hv_off[j], o1);
+                        store4_bf16(base + hv_off[j] + HALF * 2, o2);
                     }
                     continue;
                 }
-                const int jh = rem - h * hd + 4 * hl;
-                if (tv) store4_bf16(dst + jh, y);
+                if (tv[j]) store4_bf16(base + hv_off[j], y);
             }
         }
-        if (!has_next) break;
-        // the next tile's bias goes to the other buffer (last read two tiles ago)
-        stage_bias((k_tile + 1) & 1, ntf * BF);
+        if (has_next) cur = pp.template read<0, 0>();   // the next tile's step 0 landed before the last K step's barrier
 #pragma unroll
         for (int q = 0; q < NLOAD; ++q) voff_cur[q] = voff_nxt[q];
         tt = ntt;
         tf = ntf;
     }
+    // idle slots until the other group is done; then the trailing loads into LDS
+    const int mine_end = n_mine > 0 ? my_off + 1 + n_mine * P : my_off;
+    for (int s = mine_end; s < total_slots; ++s) __syncthreads();
+    wait_vmcnt<0>();
 }
-
-// Tile shapes compiled for the fast kernel.
-constexpr int kBF = 256, kBT = 256, kNWF = 2, kNWT = 4, kBK = 32, kStages = 4;
 
 template <bool X_TL, bool W_FC, int DG>
 hipError_t launch_fast_one(const KernelArgs& a, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, kBF, kBT, kNWF, kNWT, kBK, kStages, DG>), dim3(grid),
-                       dim3(64 * kNWF * kNWT), 0, stream, a);
+    if (a.K > 0 && a.K % (kBK * kStages) == 0)
+        hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, false>), dim3(grid), dim3(512), 0, stream, a);
+    else
+        hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, true>), dim3(grid), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -502,6 +618,34 @@ TilePlan fast_plan(int64_t M, int64_t F, int num_cus) {
     if (grid > tiles) grid = tiles;
     t.grid = (int)((grid + 7) / 8 * 8);                   // a multiple of the 8 XCDs
     return t;
+}
+
+bool fast_addressable(int64_t M, int64_t S, int64_t ff_dim, int64_t qw) {
+    const int64_t lim32 = int64_t(1) << 32, lim30 = int64_t(1) << 30;
+    return M * ff_dim * 2 < lim32 && M * qw * 2 < lim32 && ff_dim < lim30 && S * qw < lim30;
+}
+
+int fast_k_multiple() { return kBK * kStages; }
+
+int64_t fast_col_desc_entries(int64_t F) { return (F + kBF - 1) / kBF * (kBF / 8); }
+
+void fast_col_desc(int64_t S, int64_t ff_dim, int64_t n_heads, int64_t head_dim, int64_t F, unsigned* out,
+                   int64_t entries) {
+    const int64_t qw = n_heads * head_dim;
+    for (int64_t g = 0; g < entries; ++g) {
+        const int64_t f = 8 * g;
+        unsigned d = 0;
+        if (f < F) {
+            if (f < ff_dim) {
+                d = (unsigned)f;
+            } else {
+                const int64_t r = f - ff_dim, which = r / qw, rem = r - which * qw;
+                const int64_t h = rem / head_dim, jh = rem - h * head_dim;
+                d = ((unsigned)(which + 1) << 30) | (unsigned)(h * S * head_dim + jh);
+            }
+        }
+        out[g] = d;
+    }
 }
 
 hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, const TilePlan& pl, const KernelArgs& a,

@@ -33,6 +33,10 @@ struct KernelArgs {
     int32_t tiles_n;
     int32_t group_m;     // tile rows per raster group
     const void* zeros;   // >= 16 zero bytes: source of operand chunks outside the problem
+    // Fast kernel only: one entry per 8 output columns, covering every column tile in
+    // full. Bits 30-31: 0 ff, 1 q, 2 k, 3 v; bits 0-29: element offset of the group's
+    // first column (ff: its column; q/k/v: head * S * head_dim + place in the head).
+    const unsigned* col_desc;
 };
 
 // Tile plan chosen on the host.
@@ -53,11 +57,20 @@ hipError_t launch_fused_proj(DType dt, bool x_tokens_last, bool w_fc, const Tile
 bool plan_supported(DType dt, const TilePlan& plan);
 
 // Fast bf16 kernel (F-major MFMA orientation, register epilogue, persistent workgroups
-// over 256 x 256 tiles). fast_rope_groups returns the RoPE partner distance in 8-column
+// of two wave groups over 256 x 128 tiles). fast_rope_groups returns the RoPE partner distance in 8-column
 // groups it needs (0 without RoPE) or -1 when the head size is not supported by it.
 // fast_plan picks its tiles and grid (one workgroup per CU, a multiple of 8).
 int fast_rope_groups(int head_dim, bool rope);
 TilePlan fast_plan(int64_t M, int64_t F, int num_cus);
+// Whether the fast kernel can address this problem with its 32-bit per-lane output
+// offsets and 30-bit column offsets.
+bool fast_addressable(int64_t M, int64_t S, int64_t ff_dim, int64_t qw);
+// Column descriptor table of the fast kernel (entries for ceil(F / 256) full column tiles).
+void fast_col_desc(int64_t S, int64_t ff_dim, int64_t n_heads, int64_t head_dim, int64_t F, unsigned* out,
+                   int64_t entries);
+int64_t fast_col_desc_entries(int64_t F);
+// Channel counts that are a multiple of this take no partial or padding K steps.
+int fast_k_multiple();
 hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, const TilePlan& plan,
                                   const KernelArgs& args, hipStream_t stream);
 
