@@ -82,13 +82,22 @@ __device__ __forceinline__ f32x4 bias4(const __bf16* p) {
     return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 
-// Four consecutive dwords of read-only memory at a wave-uniform address, through the
+// Sixteen consecutive dwords of read-only memory at a wave-uniform address, through the
 // scalar unit. A vector load here would make the compiler wait (vmcnt) for every older
 // vector memory operation, including the direct-to-LDS loads of the next tile in flight;
 // the scalar load has its own counter, waited for right away.
-__device__ __forceinline__ u32x4 scalar_load4(const unsigned* p) {
-    u32x4 v;
-    asm volatile(HAZARD_NOPS "s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+// The address is passed through readfirstlane so that it is in SGPRs even where the
+// compiler cannot prove it uniform (it is uniform by construction). readfirstlane returns
+// int: each half goes through uint32_t before widening, else the low half would be
+// sign-extended into the high one.
+__device__ __forceinline__ u32x16 scalar_load16(const unsigned* p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint64_t ua = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32)) << 32) |
+                        (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((unsigned)a);
+    u32x16 v;
+    asm volatile(HAZARD_NOPS "s_load_dwordx16 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                 : "=s"(v)
+                 : "s"(reinterpret_cast<const unsigned*>(ua)));
     return v;
 }
 
@@ -188,6 +197,9 @@ struct FastPipe {
             }
         }
     }
+
+    // LDS read instructions per k step (a transposing operand takes two).
+    static constexpr int kReads = (W_FC ? 1 : 2) * C::TI + (X_TL ? 1 : 2) * C::TJ;
 
     // MFMA operands of one 16-deep k step: TI W^T row blocks and TJ token blocks.
     struct Ops {
@@ -317,7 +329,8 @@ __device__ __forceinline__ int block_tile_count(int tiles_t, int tiles_f) {
 // DG: RoPE partner distance in 8-column groups (hd/16), 0 = no RoPE. TAILK: K is not a
 // multiple of STAGES * BK (some K steps are partial or padding).
 template <bool X_TL, bool W_FC, int DG, bool TAILK>
-__global__ __launch_bounds__(512, 1) void fused_proj_fast_kernel(KernelArgs p) {
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_proj_fast_kernel(
+    KernelArgs p) {
     constexpr int BF = kBF, BT = kBT, BK = kBK, STAGES = kStages;
     using C = FastCfg<X_TL, W_FC, BF, BT, kNWF, kNWT, BK, STAGES>;   // one group's tile
     using Pipe = FastPipe<C, X_TL, W_FC, BK, TAILK>;
@@ -432,11 +445,21 @@ __global__ __launch_bounds__(512, 1) void fused_proj_fast_kernel(KernelArgs p) {
             for (int q = 0; q < NLOAD; ++q) voff_nxt[q] = voff_cur[q];
         }
 
+        // The accumulators start from the bias (in LDS since the last barrier): acc[a][j][e]
+        // holds column 32a + 8(e/4) + 4(lane/32) + e%4 of the wave tile.
+        const __bf16* const bias_t = bias_s[grp][i & 1] + wf * WF + 4 * hl;
         f32x16 acc[TI][TJ];
 #pragma unroll
-        for (int a = 0; a < TI; ++a)
+        for (int a = 0; a < TI; ++a) {
 #pragma unroll
-            for (int j = 0; j < TJ; ++j) acc[a][j] = f32x16{};
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 b = bias4(bias_t + 32 * a + 8 * q);
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[a][j][4 * q + u] = b[u];
+            }
+        }
 
         // One K step (one slot), whose operands are already in registers: wait for this
         // wave's loads of the next step (those of the three after it may stay in flight),
@@ -444,15 +467,23 @@ __global__ __launch_bounds__(512, 1) void fused_proj_fast_kernel(KernelArgs p) {
         // consumed the stage of the previous step), refill that stage with the step
         // STAGES-1 ahead -- the next tile's first steps once this one runs out -- and read
         // the next step's operands while this step's MFMAs run.
+        // The scheduling fences keep every instruction inside its slot: without them the
+        // compiler hoists the next step's MFMAs above the barrier, recycles the operand
+        // registers and then waits for the LDS reads right after issuing them.
         auto k_step = [&](auto stc, const unsigned (&vo)[NLOAD], int s_load) __attribute__((always_inline)) {
             constexpr int ST = decltype(stc)::value;
             constexpr int SN = (ST + 1) % STAGES, SL = (ST + STAGES - 1) % STAGES;
+            __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<3 * NLOAD>();
             __syncthreads();
             pp.template issue<SL>(vo, s_load, K, zeros);
             const Ops nxt = pp.template read<SN, 0>();
             Pipe::mma(acc, cur);
             cur = nxt;
+            // all LDS reads first, into registers of their own, then the MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, Pipe::kReads, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ, 0);
+            __builtin_amdgcn_sched_barrier(0);
         };
         for (int kt = 0; kt < KTp - STAGES; kt += STAGES) {
             k_step(std::integral_constant<int, 0>{}, voff_cur, kt + 5);
@@ -471,15 +502,17 @@ __global__ __launch_bounds__(512, 1) void fused_proj_fast_kernel(KernelArgs p) {
         k_step(std::integral_constant<int, 2>{}, voff_nxt, 1);
         k_step(std::integral_constant<int, 3>{}, voff_nxt, 2);
         k_step(std::integral_constant<int, 4>{}, voff_nxt, 3);
+        __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<3 * NLOAD>();
         __syncthreads();
         pp.template issue<STAGES - 2>(voff_nxt, 4, K, zeros);
         Pipe::mma(acc, cur);
+        __builtin_amdgcn_sched_barrier(0);
 
         // ---- epilogue in registers, one slot per (token block j, column group G).
-        // acc[a][j][e]: column f = 32a + 8(e/4) + 4(lane/32) + e%4, token 32j + lane%32
-        // (both relative to the wave tile). Outputs never overlap the inputs (checked
-        // on the host), so loads may be hoisted above stores.
+        // acc[a][j][e] (bias included): column f = 32a + 8(e/4) + 4(lane/32) + e%4, token
+        // 32j + lane%32 (both relative to the wave tile). Outputs never overlap the inputs
+        // (checked on the host), so loads may be hoisted above stores.
         //
         // Per-lane byte offsets (32-bit: the host keeps every output under 4 GiB) of this
         // lane's token: its ff row, its q/k/v row of head 0, its cos/sin row.
@@ -499,8 +532,7 @@ __global__ __launch_bounds__(512, 1) void fused_proj_fast_kernel(KernelArgs p) {
         // element offset of the group's first column in the low bits (ff: column; q/k/v:
         // head * S * hd + place in head), read four at a time by the scalar unit.
         const int fw = n0 + wf * WF;
-        const unsigned* const desc_w = p.col_desc + (fw >> 3);
-        const __bf16* const bias_t = bias_s[grp][i & 1] + wf * WF + 4 * hl;
+        const u32x16 desc = scalar_load16(p.col_desc + (fw >> 3));
         // whether the wave's columns meet the q or k slice (then RoPE applies)
         const bool wave_rope = DG > 0 && fw < ff_dim + 2 * p.qw && fw + WF > ff_dim;
         constexpr int HD = DG > 0 ? 16 * DG : 16, HALF = HD / 2, NR = HALF / 8, NRB = NR > 4 ? 4 : NR;
@@ -528,18 +560,16 @@ __global__ __launch_bounds__(512, 1) void fused_proj_fast_kernel(KernelArgs p) {
                 }
             };
             load_rope(0);
-            u32x4 desc4;
 #pragma unroll
             for (int G = 0; G < NG; ++G) {
+                __builtin_amdgcn_sched_barrier(0);
                 __syncthreads();   // the slot of (j, G)
-                if (G % 4 == 0) desc4 = scalar_load4(desc_w + G);
                 if (fw + 8 * G >= N) continue;   // ragged last column tile
-                const unsigned d = desc4[G % 4];
+                const unsigned d = desc[G];
                 const unsigned kind = d >> 30, off = d & 0x3fffffffu;
-                const f32x4 bv = bias4(bias_t + 8 * G);
                 float y[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) y[u] = acc[G >> 2][j][4 * (G & 3) + u] + bv[u];
+                for (int u = 0; u < 4; ++u) y[u] = acc[G >> 2][j][4 * (G & 3) + u];
                 if (kind == 0) {
                     if (act == 1) {
 #pragma unroll
@@ -558,12 +588,11 @@ __global__ __launch_bounds__(512, 1) void fused_proj_fast_kernel(KernelArgs p) {
                     if (jh8 >= HALF || G + DG >= NG) continue;
                     const int G2 = (G + DG < NG) ? G + DG : G;   // constant after unrolling
                     if (NR > NRB && jh8 == 8 * NRB) load_rope(NRB);   // second half (head size 128)
-                    const f32x4 b2 = bias4(bias_t + 8 * G2);
                     const f32x4 c = rc[(jh8 / 8) % NRB], sn = rsn[(jh8 / 8) % NRB];
                     float o1[4], o2[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        const float y2 = acc[G2 >> 2][j][4 * (G2 & 3) + u] + b2[u];
+                        const float y2 = acc[G2 >> 2][j][4 * (G2 & 3) + u];
                         o1[u] = y[u] * c[u] - y2 * sn[u];
                         o2[u] = y2 * c[u] + y[u] * sn[u];
                     }
