@@ -315,7 +315,7 @@ __device__ __forceinline__ bool block_tile(int k, int tiles_t, int tiles_f, int 
 
 // Tile shapes compiled for the fast kernel: per group, BF output columns x BT tokens,
 // NWF x NWT waves, K steps of BK through STAGES LDS stages.
-constexpr int kBF = 256, kBT = 128, kNWF = 2, kNWT = 2, kBK = 16, kStages = 6;
+constexpr int kBF = 256, kBT = 128, kNWF = 2, kNWT = 2, kBK = 32, kStages = 3;
 
 // Number of tiles block_tile hands this workgroup.
 __device__ __forceinline__ int block_tile_count(int tiles_t, int tiles_f) {
@@ -337,8 +337,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     using Ops = typename Pipe::Ops;
     constexpr int WF = C::WF, WT = C::WT, TI = C::TI, TJ = C::TJ, NG = C::NG, NLOAD = C::NLOAD;
     constexpr int EPI = TJ * NG;   // epilogue slots per tile: one per (token block, column group)
-    static_assert(C::NW == 4 && C::KK == 1, "four waves per group, one MFMA k step per K step");
-    static_assert(STAGES == 6, "the wait counts below are written for six stages");
+    static_assert(C::NW == 4 && C::KK == 2, "four waves per group, two MFMA k steps per K step");
+    static_assert(STAGES == 3, "the wait counts below are written for three stages");
     static_assert(NG == 16, "one 16-entry column descriptor load per wave");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[2][C::LDS_BYTES];
     __shared__ __attribute__((aligned(16))) __bf16 bias_s[2][2][BF];   // [group][buffer]: tile bias
@@ -360,23 +360,35 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int n_wg = block_tile_count(p.tiles_m, p.tiles_n);
     const int P = KTp + EPI;
     const int n0_tiles = (n_wg + 1) / 2, n1_tiles = n_wg / 2;   // group g takes the workgroup's tiles 2i + g
-    const int end0 = n0_tiles > 0 ? 1 + n0_tiles * P : 0;
-    const int end1 = n1_tiles > 0 ? P / 2 + 1 + n1_tiles * P : 0;
+    const int end0 = n0_tiles * P;
+    const int end1 = n1_tiles > 0 ? P / 2 + n1_tiles * P : 0;
     const int total_slots = end0 > end1 ? end0 : end1;
     const int n_mine = grp ? n1_tiles : n0_tiles, my_off = grp ? P / 2 : 0;
 
     Pipe pp;
     pp.wave = wave;
     pp.lds0 = (unsigned)(size_t)(lds_void*)smem[grp];
+    // LDS read bases: K-major operands need one per MFMA k step (the swizzle depends on
+    // the chunk), M/N-major ones a single one (the k step goes into the immediate offset).
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
-        if constexpr (W_FC) pp.wbase[i][0] = pp.lds0 + k_operand_base<C::W_CPR>(wf * WF + 32 * i, 0, lane);
-        else pp.wbase[i][0] = pp.lds0 + mn_operand_base<C::W_CPR>(wf * WF + 32 * i, lane);
+        if constexpr (W_FC) {
+#pragma unroll
+            for (int kk = 0; kk < C::KK; ++kk)
+                pp.wbase[i][kk] = pp.lds0 + k_operand_base<C::W_CPR>(wf * WF + 32 * i, kk, lane);
+        } else {
+            pp.wbase[i][0] = pp.lds0 + mn_operand_base<C::W_CPR>(wf * WF + 32 * i, lane);
+        }
     }
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-        if constexpr (X_TL) pp.xbase[j][0] = pp.lds0 + C::X_REGION + k_operand_base<C::X_CPR>(wt * WT + 32 * j, 0, lane);
-        else pp.xbase[j][0] = pp.lds0 + C::X_REGION + mn_operand_base<C::X_CPR>(wt * WT + 32 * j, lane);
+        if constexpr (X_TL) {
+#pragma unroll
+            for (int kk = 0; kk < C::KK; ++kk)
+                pp.xbase[j][kk] = pp.lds0 + C::X_REGION + k_operand_base<C::X_CPR>(wt * WT + 32 * j, kk, lane);
+        } else {
+            pp.xbase[j][0] = pp.lds0 + C::X_REGION + mn_operand_base<C::X_CPR>(wt * WT + 32 * j, lane);
+        }
     }
     pp.wsrc = static_cast<const char*>(p.w);
     pp.xsrc = static_cast<const char*>(p.x);
@@ -407,7 +419,6 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
     int tt = 0, tf = 0;
     unsigned voff_cur[NLOAD], voff_nxt[NLOAD];
-    Ops cur;
     if (n_mine > 0) {
         // The group's first tile: its first STAGES-1 K steps and its bias go in flight
         // at once, whatever the group's start slot.
@@ -417,17 +428,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         pp.template issue<0>(voff_cur, 0, K, zeros);
         issue_bias(0, tf * BF);
         pp.template issue<1>(voff_cur, 1, K, zeros);
-        pp.template issue<2>(voff_cur, 2, K, zeros);
-        pp.template issue<3>(voff_cur, 3, K, zeros);
-        pp.template issue<4>(voff_cur, 4, K, zeros);
     }
     for (int s = 0; s < my_off; ++s) __syncthreads();   // idle slots before the group starts
-    if (n_mine > 0) {
-        // one slot: step 0 landed (steps 1-4 may still be in flight); read its operands
-        wait_vmcnt<4 * NLOAD>();
-        __syncthreads();
-        cur = pp.template read<0, 0>();
-    }
 
     for (int i = 0; i < n_mine; ++i) {
         const int m0 = tt * BT, n0 = tf * BF;
@@ -445,69 +447,81 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             for (int q = 0; q < NLOAD; ++q) voff_nxt[q] = voff_cur[q];
         }
 
-        // The accumulators start from the bias (in LDS since the last barrier): acc[a][j][e]
-        // holds column 32a + 8(e/4) + 4(lane/32) + e%4 of the wave tile.
-        const __bf16* const bias_t = bias_s[grp][i & 1] + wf * WF + 4 * hl;
+        // One K step kt (one slot): wait for this wave's loads of step kt (those of kt+1 may
+        // stay in flight), barrier (every wave of the group has its loads of kt landed and
+        // has consumed the stage of kt-1), refill that stage with step kt+2 -- the next
+        // tile's first steps once this one runs out -- then read stage kt and run its
+        // MFMAs. The first step of a tile first sets the accumulators to the bias (in LDS
+        // once that step's wait and barrier are passed: it was loaded right after the
+        // tile's step 0). The LDS latency at the start of a step is covered by the other
+        // group's epilogue work on the same SIMD. The scheduling fences keep every
+        // instruction inside its slot (the compiler would otherwise move MFMAs across the
+        // barriers and recycle operand registers).
         f32x16 acc[TI][TJ];
-#pragma unroll
-        for (int a = 0; a < TI; ++a) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 b = bias4(bias_t + 32 * a + 8 * q);
-#pragma unroll
-                for (int j = 0; j < TJ; ++j)
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) acc[a][j][4 * q + u] = b[u];
-            }
-        }
-
-        // One K step (one slot), whose operands are already in registers: wait for this
-        // wave's loads of the next step (those of the three after it may stay in flight),
-        // barrier (every wave of the group has its loads of the next step landed and has
-        // consumed the stage of the previous step), refill that stage with the step
-        // STAGES-1 ahead -- the next tile's first steps once this one runs out -- and read
-        // the next step's operands while this step's MFMAs run.
-        // The scheduling fences keep every instruction inside its slot: without them the
-        // compiler hoists the next step's MFMAs above the barrier, recycles the operand
-        // registers and then waits for the LDS reads right after issuing them.
-        auto k_step = [&](auto stc, const unsigned (&vo)[NLOAD], int s_load) __attribute__((always_inline)) {
-            constexpr int ST = decltype(stc)::value;
-            constexpr int SN = (ST + 1) % STAGES, SL = (ST + STAGES - 1) % STAGES;
+        const __bf16* const bias_t = bias_s[grp][i & 1] + wf * WF + 4 * hl;
+        auto k_step = [&](auto stc, auto firstc, const unsigned (&vo)[NLOAD], int s_load)
+                          __attribute__((always_inline)) {
+            constexpr int ST = decltype(stc)::value, SL = (ST + 2) % STAGES;
+            constexpr bool FIRST = decltype(firstc)::value;
             __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<3 * NLOAD>();
+            wait_vmcnt<NLOAD>();
             __syncthreads();
             pp.template issue<SL>(vo, s_load, K, zeros);
-            const Ops nxt = pp.template read<SN, 0>();
-            Pipe::mma(acc, cur);
-            cur = nxt;
-            // all LDS reads first, into registers of their own, then the MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, Pipe::kReads, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ, 0);
+            if constexpr (FIRST) {
+                // acc[a][j][e] holds column 32a + 8(e/4) + 4(lane/32) + e%4 of the wave tile
+#pragma unroll
+                for (int a = 0; a < TI; ++a) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 b = bias4(bias_t + 32 * a + 8 * q);
+#pragma unroll
+                        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) acc[a][j][4 * q + u] = b[u];
+                    }
+                }
+            }
+            const Ops o0 = pp.template read<ST, 0>();
+            const Ops o1 = pp.template read<ST, 1>();
+            Pipe::mma(acc, o0);
+            Pipe::mma(acc, o1);
+            if constexpr (!FIRST) {
+                // all LDS reads first, then the MFMAs (the second half's reads land while
+                // the first half's MFMAs run)
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * Pipe::kReads, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * TI * TJ, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
         };
-        for (int kt = 0; kt < KTp - STAGES; kt += STAGES) {
-            k_step(std::integral_constant<int, 0>{}, voff_cur, kt + 5);
-            k_step(std::integral_constant<int, 1>{}, voff_cur, kt + 6);
-            k_step(std::integral_constant<int, 2>{}, voff_cur, kt + 7);
-            k_step(std::integral_constant<int, 3>{}, voff_cur, kt + 8);
-            k_step(std::integral_constant<int, 4>{}, voff_cur, kt + 9);
-            k_step(std::integral_constant<int, 5>{}, voff_cur, kt + 10);
+        using F0 = std::false_type;
+        using F1 = std::true_type;
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        using S2 = std::integral_constant<int, 2>;
+        // Loads issued by step kt are for step kt+2: this tile's while kt+2 < KTp, then the
+        // next tile's steps 0 and 1 (with its bias after step 0). Past the group's last
+        // tile they repeat this tile's first steps (in bounds, never read), which keeps
+        // the loop free of branches; they are waited for before the workgroup ends.
+        if (KTp == STAGES) {
+            // a single group of steps: step 0 loads step 2, steps 1 and 2 the next tile's 0, 1
+            k_step(S0{}, F1{}, voff_cur, 2);
+            k_step(S1{}, F0{}, voff_nxt, 0);
+            issue_bias((i + 1) & 1, ntf * BF);
+            k_step(S2{}, F0{}, voff_nxt, 1);
+        } else {
+            k_step(S0{}, F1{}, voff_cur, 2);
+            k_step(S1{}, F0{}, voff_cur, 3);
+            k_step(S2{}, F0{}, voff_cur, 4);
+            for (int kt = STAGES; kt < KTp - STAGES; kt += STAGES) {
+                k_step(S0{}, F0{}, voff_cur, kt + 2);
+                k_step(S1{}, F0{}, voff_cur, kt + 3);
+                k_step(S2{}, F0{}, voff_cur, kt + 4);
+            }
+            k_step(S0{}, F0{}, voff_cur, KTp - 1);
+            k_step(S1{}, F0{}, voff_nxt, 0);
+            issue_bias((i + 1) & 1, ntf * BF);
+            k_step(S2{}, F0{}, voff_nxt, 1);
         }
-        // the last group of steps: its loads start the next tile (bias with its step 0);
-        // the last step reads nothing ahead (the next tile's first operands are read at
-        // the end of the epilogue, so that they do not occupy registers during it)
-        k_step(std::integral_constant<int, 0>{}, voff_cur, KTp - 1);
-        k_step(std::integral_constant<int, 1>{}, voff_nxt, 0);
-        issue_bias((i + 1) & 1, ntf * BF);
-        k_step(std::integral_constant<int, 2>{}, voff_nxt, 1);
-        k_step(std::integral_constant<int, 3>{}, voff_nxt, 2);
-        k_step(std::integral_constant<int, 4>{}, voff_nxt, 3);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<3 * NLOAD>();
-        __syncthreads();
-        pp.template issue<STAGES - 2>(voff_nxt, 4, K, zeros);
-        Pipe::mma(acc, cur);
-        __builtin_amdgcn_sched_barrier(0);
 
         // ---- epilogue in registers, one slot per (token block j, column group G).
         // acc[a][j][e] (bias included): column f = 32a + 8(e/4) + 4(lane/32) + e%4, token
@@ -605,14 +619,13 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 if (tv[j]) store4_bf16(base + hv_off[j], y);
             }
         }
-        if (has_next) cur = pp.template read<0, 0>();   // the next tile's step 0 landed before the last K step's barrier
 #pragma unroll
         for (int q = 0; q < NLOAD; ++q) voff_cur[q] = voff_nxt[q];
         tt = ntt;
         tf = ntf;
     }
     // idle slots until the other group is done; then the trailing loads into LDS
-    const int mine_end = n_mine > 0 ? my_off + 1 + n_mine * P : my_off;
+    const int mine_end = my_off + n_mine * P;
     for (int s = mine_end; s < total_slots; ++s) __syncthreads();
     wait_vmcnt<0>();
 }
