@@ -28,21 +28,16 @@
 // ones through ds_read_b128. Chunks outside the problem (ragged M, N or K) are
 // read from a small zero block instead, so no access leaves the operands.
 //
-// Schedule. The kernel is persistent, one workgroup of 8 waves per CU. Waves
-// w and w+4 share a SIMD (measured), so the waves form two groups of four, one
-// wave per SIMD each. Each group walks its own list of 256 (f) x 128 (token)
-// tiles (2 x 2 waves of 128 x 64, 128 accumulators per lane) through its own
-// LDS pipeline, six K steps of 16 deep. The two groups run the same cadence --
-// every wave passes one workgroup barrier per slot -- and a tile takes KT
-// slots of K steps followed by 32 epilogue slots (one 8-column x 32-token
-// group each), but group 1 runs half a tile behind group 0. So while one
-// group's waves spend their slots on the VALU work of an epilogue, the
-// other group's waves keep the matrix cores busy on the same SIMDs: the
-// epilogue overlaps the MFMAs instead of following them. The direct-load
-// pipeline runs straight on into a group's next tile, and the operands of the
-// next K step are read from LDS while the MFMAs of the current one run. The
-// workgroup's tiles come from a contiguous, grouped range of the XCD it runs on,
-// and the two groups take alternate tiles of it.
+// Schedule. The kernel is persistent: one workgroup of 4 waves per CU, one wave
+// per SIMD, walks a list of 256 x 256 tiles. Each wave owns 128 (f) x 128 (token)
+// outputs, 256 fp32 accumulators (the compiler keeps them in the accumulation
+// registers, which one wave per SIMD may use next to 256 ordinary ones). The large
+// wave tile reads 0.5 KB of operands from LDS per MFMA instead of 0.75 KB for a
+// 128 x 64 tile, which keeps the LDS, also written by the direct loads, well below
+// its bandwidth. The direct-load pipeline is four K steps of 32 deep and runs
+// straight on into the next tile, and the operands of the next K step are read from
+// LDS while the MFMAs of the current one run. The workgroup's tiles come from a
+// contiguous, grouped range of the XCD it runs on.
 #include "device_common.h"
 #include "fused_proj_kernels.h"
 
@@ -198,9 +193,6 @@ struct FastPipe {
         }
     }
 
-    // LDS read instructions per k step (a transposing operand takes two).
-    static constexpr int kReads = (W_FC ? 1 : 2) * C::TI + (X_TL ? 1 : 2) * C::TJ;
-
     // MFMA operands of one 16-deep k step: TI W^T row blocks and TJ token blocks.
     struct Ops {
         bf16x8 a[C::TI];
@@ -313,61 +305,41 @@ __device__ __forceinline__ bool block_tile(int k, int tiles_t, int tiles_f, int 
     return true;
 }
 
-// Tile shapes compiled for the fast kernel: per group, BF output columns x BT tokens,
-// NWF x NWT waves, K steps of BK through STAGES LDS stages.
-constexpr int kBF = 256, kBT = 128, kNWF = 2, kNWT = 2, kBK = 32, kStages = 3;
-
-// Number of tiles block_tile hands this workgroup.
-__device__ __forceinline__ int block_tile_count(int tiles_t, int tiles_f) {
-    const int total = tiles_t * tiles_f;
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
-    const int count = (total >> 3) + (xcd < (total & 7) ? 1 : 0);
-    return slot < count ? (count - slot + per_xcd - 1) / per_xcd : 0;
-}
+// Tile shapes compiled for the fast kernel: BF output columns x BT tokens per workgroup,
+// NWF x NWT waves (one per SIMD), K steps of BK through STAGES LDS stages.
+constexpr int kBF = 256, kBT = 256, kNWF = 2, kNWT = 4, kBK = 32, kStages = 4;
+constexpr int kThreads = 64 * kNWF * kNWT;
 
 // X_TL: x token-major [b,s,c] (else channels-first). W_FC: W [F,C] (else [C,F]).
 // DG: RoPE partner distance in 8-column groups (hd/16), 0 = no RoPE. TAILK: K is not a
 // multiple of STAGES * BK (some K steps are partial or padding).
 template <bool X_TL, bool W_FC, int DG, bool TAILK>
-__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_proj_fast_kernel(
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_proj_fast_kernel(
     KernelArgs p) {
     constexpr int BF = kBF, BT = kBT, BK = kBK, STAGES = kStages;
-    using C = FastCfg<X_TL, W_FC, BF, BT, kNWF, kNWT, BK, STAGES>;   // one group's tile
+    using C = FastCfg<X_TL, W_FC, BF, BT, kNWF, kNWT, BK, STAGES>;
     using Pipe = FastPipe<C, X_TL, W_FC, BK, TAILK>;
     using Ops = typename Pipe::Ops;
     constexpr int WF = C::WF, WT = C::WT, TI = C::TI, TJ = C::TJ, NG = C::NG, NLOAD = C::NLOAD;
-    constexpr int EPI = TJ * NG;   // epilogue slots per tile: one per (token block, column group)
-    static_assert(C::NW == 4 && C::KK == 2, "four waves per group, two MFMA k steps per K step");
-    static_assert(STAGES == 3, "the wait counts below are written for three stages");
+    static_assert(C::NW == 8 && C::KK == 2, "eight waves, two MFMA k steps per K step");
+    static_assert(STAGES == 4, "the wait counts below are written for four stages");
     static_assert(NG == 16, "one 16-entry column descriptor load per wave");
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2][C::LDS_BYTES];
-    __shared__ __attribute__((aligned(16))) __bf16 bias_s[2][2][BF];   // [group][buffer]: tile bias
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) __bf16 bias_s[2][BF];   // tile bias, double-buffered
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wid >> 2, wave = wid & 3;   // group, wave within the group
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wf = wave / kNWT, wt = wave % kNWT;
     const int K = p.K, N = p.N, M = (int)p.M, S = p.S;
     const char* const zeros = static_cast<const char*>(p.zeros);
     const __bf16* const bias = static_cast<const __bf16*>(p.bias);
 
-    // K steps per tile, padded to a multiple of the stage count so that step s of every
-    // tile uses stage s mod STAGES (the padding steps read zeros). At least one group.
-    const int KT = K > 0 ? (K + BK - 1) / BK : 1;
-    const int KTp = (KT + STAGES - 1) / STAGES * STAGES;
-    // Slots: a group's tile takes P; group 1 starts half a tile later; both groups pass
-    // the same number of barriers (idle slots pad the shorter one).
-    const int n_wg = block_tile_count(p.tiles_m, p.tiles_n);
-    const int P = KTp + EPI;
-    const int n0_tiles = (n_wg + 1) / 2, n1_tiles = n_wg / 2;   // group g takes the workgroup's tiles 2i + g
-    const int end0 = n0_tiles * P;
-    const int end1 = n1_tiles > 0 ? P / 2 + n1_tiles * P : 0;
-    const int total_slots = end0 > end1 ? end0 : end1;
-    const int n_mine = grp ? n1_tiles : n0_tiles, my_off = grp ? P / 2 : 0;
+    int tt, tf;
+    if (!block_tile(0, p.tiles_m, p.tiles_n, p.group_m, tt, tf)) return;
 
     Pipe pp;
     pp.wave = wave;
-    pp.lds0 = (unsigned)(size_t)(lds_void*)smem[grp];
+    pp.lds0 = (unsigned)(size_t)(lds_void*)smem;
     // LDS read bases: K-major operands need one per MFMA k step (the swizzle depends on
     // the chunk), M/N-major ones a single one (the k step goes into the immediate offset).
 #pragma unroll
@@ -395,11 +367,11 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     pp.wstep = (W_FC ? (int64_t)BK : (int64_t)BK * N) * 2;
     pp.xstep = (X_TL ? (int64_t)BK : (int64_t)BK * p.x_sc) * 2;
 
-    // The bias slice of a tile, copied into bias_s[grp][buf] by the group's first wave's
-    // first 32 lanes with the same direct-to-LDS loads as the operands (from the zero
-    // block where there is no bias). It is issued with the tile's first K steps, so the
-    // waits and barriers of those steps also cover it.
-    const unsigned bias_lds = (unsigned)(size_t)(lds_void*)&bias_s[grp][0][0];
+    // The bias slice of a tile, copied into bias_s[buf] by the first wave's first 32 lanes
+    // with the same direct-to-LDS loads as the operands (from the zero block where there
+    // is no bias). It is issued right after the tile's step 0, so the waits and barriers
+    // that make step 0 visible also cover it.
+    const unsigned bias_lds = (unsigned)(size_t)(lds_void*)&bias_s[0][0];
     auto issue_bias = [&](int buf, int n0) __attribute__((always_inline)) {
         if (wave == 0 && lane < BF / 8) {
             const int f = n0 + 8 * lane;
@@ -409,6 +381,11 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         }
     };
 
+    // K steps per tile, padded to a multiple of the stage count so that step s of every
+    // tile uses stage s mod STAGES (the padding steps read zeros). At least one group.
+    const int KT = K > 0 ? (K + BK - 1) / BK : 1;
+    const int KTp = (KT + STAGES - 1) / STAGES * STAGES;
+
     // epilogue constants
     const int hl = lane >> 5;
     char* const out_ff = static_cast<char*>(p.ff);
@@ -417,113 +394,95 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int ff_dim = p.ff_dim, hd = p.head_dim, act = p.act;
     const int64_t slab_elems = (int64_t)S * p.qw;   // q/k/v elements of one slab (all heads)
 
-    int tt = 0, tf = 0;
     unsigned voff_cur[NLOAD], voff_nxt[NLOAD];
-    if (n_mine > 0) {
-        // The group's first tile: its first STAGES-1 K steps and its bias go in flight
-        // at once, whatever the group's start slot.
-        block_tile(grp, p.tiles_m, p.tiles_n, p.group_m, tt, tf);
-        tile_offsets<C, X_TL, W_FC>(voff_cur, pp.kofs, tt * BT, tf * BF, wave, lane, K, N, M, S, p.x_sb, p.x_ss,
-                                    p.x_sc);
-        pp.template issue<0>(voff_cur, 0, K, zeros);
-        issue_bias(0, tf * BF);
-        pp.template issue<1>(voff_cur, 1, K, zeros);
-    }
-    for (int s = 0; s < my_off; ++s) __syncthreads();   // idle slots before the group starts
+    tile_offsets<C, X_TL, W_FC>(voff_cur, pp.kofs, tt * BT, tf * BF, wave, lane, K, N, M, S, p.x_sb, p.x_ss,
+                                p.x_sc);
+    // Prologue: the first STAGES-1 K steps of the first tile and its bias in flight; once
+    // step 0 has landed (steps 1 and 2 may still be in flight), read its operands.
+    pp.template issue<0>(voff_cur, 0, K, zeros);
+    issue_bias(0, tf * BF);
+    pp.template issue<1>(voff_cur, 1, K, zeros);
+    pp.template issue<2>(voff_cur, 2, K, zeros);
+    wait_vmcnt<2 * NLOAD>();
+    __syncthreads();
+    Ops c0 = pp.template read<0, 0>();
+    Ops c1 = pp.template read<0, 1>();
 
-    for (int i = 0; i < n_mine; ++i) {
+    for (int k_tile = 0;; ++k_tile) {
         const int m0 = tt * BT, n0 = tf * BF;
         int ntt = 0, ntf = 0;
-        const bool has_next = i + 1 < n_mine;
+        const bool has_next = block_tile(k_tile + 1, p.tiles_m, p.tiles_n, p.group_m, ntt, ntf);
         if (has_next) {
-            block_tile(2 * (i + 1) + grp, p.tiles_m, p.tiles_n, p.group_m, ntt, ntf);
             tile_offsets<C, X_TL, W_FC>(voff_nxt, pp.kofs, ntt * BT, ntf * BF, wave, lane, K, N, M, S, p.x_sb,
                                         p.x_ss, p.x_sc);
         } else {
-            // past the group's last tile the loads repeat this tile's first steps (in
-            // bounds, never read), which keeps the K loop free of branches
+            // past the last tile the loads repeat this tile's first steps (in bounds, never
+            // read), which keeps the K loop free of branches
             ntf = tf;
 #pragma unroll
             for (int q = 0; q < NLOAD; ++q) voff_nxt[q] = voff_cur[q];
         }
 
-        // One K step kt (one slot): wait for this wave's loads of step kt (those of kt+1 may
-        // stay in flight), barrier (every wave of the group has its loads of kt landed and
-        // has consumed the stage of kt-1), refill that stage with step kt+2 -- the next
-        // tile's first steps once this one runs out -- then read stage kt and run its
-        // MFMAs. The first step of a tile first sets the accumulators to the bias (in LDS
-        // once that step's wait and barrier are passed: it was loaded right after the
-        // tile's step 0). The LDS latency at the start of a step is covered by the other
-        // group's epilogue work on the same SIMD. The scheduling fences keep every
-        // instruction inside its slot (the compiler would otherwise move MFMAs across the
-        // barriers and recycle operand registers).
+        // The accumulators start from the bias (in LDS since the last barrier): acc[a][j][e]
+        // holds column 32a + 8(e/4) + 4(lane/32) + e%4 of the wave tile.
+        const __bf16* const bias_t = bias_s[k_tile & 1] + wf * WF + 4 * hl;
         f32x16 acc[TI][TJ];
-        const __bf16* const bias_t = bias_s[grp][i & 1] + wf * WF + 4 * hl;
-        auto k_step = [&](auto stc, auto firstc, const unsigned (&vo)[NLOAD], int s_load)
-                          __attribute__((always_inline)) {
-            constexpr int ST = decltype(stc)::value, SL = (ST + 2) % STAGES;
-            constexpr bool FIRST = decltype(firstc)::value;
+#pragma unroll
+        for (int a = 0; a < TI; ++a) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 b = bias4(bias_t + 32 * a + 8 * q);
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[a][j][4 * q + u] = b[u];
+            }
+        }
+
+        // One K step kt, whose operands c0/c1 (its two MFMA k steps) are already in
+        // registers: wait for this wave's loads of step kt+1 (those of kt+2 may stay in
+        // flight), barrier (every wave's loads of kt+1 landed; every wave has consumed the
+        // stage of kt-1), refill that stage with step kt+3, and read step kt+1's operands
+        // while the MFMAs of kt run. Once kt+3 is past the tile the loads are the next
+        // tile's first steps (its bias right after its step 0), and the last step reads the
+        // next tile's step 0 ahead. Every step has the same code -- no step is peeled -- so
+        // the accumulators stay in the accumulation registers. The scheduling fences keep
+        // every instruction inside its step (the compiler would otherwise move MFMAs across
+        // the barrier and recycle operand registers); inside a step the compiler orders the
+        // LDS reads and MFMAs itself (forcing all reads first measured slower).
+        auto k_step = [&](auto stc, int kt) __attribute__((always_inline)) {
+            constexpr int ST = decltype(stc)::value;
+            constexpr int SN = (ST + 1) % STAGES, SL = (ST + STAGES - 1) % STAGES;
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<NLOAD>();
             __syncthreads();
-            pp.template issue<SL>(vo, s_load, K, zeros);
-            if constexpr (FIRST) {
-                // acc[a][j][e] holds column 32a + 8(e/4) + 4(lane/32) + e%4 of the wave tile
+            const int s_load = kt + STAGES - 1;
+            const bool ahead = s_load >= KTp;   // wave-uniform
+            unsigned vo[NLOAD];
 #pragma unroll
-                for (int a = 0; a < TI; ++a) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 b = bias4(bias_t + 32 * a + 8 * q);
-#pragma unroll
-                        for (int j = 0; j < TJ; ++j)
-#pragma unroll
-                            for (int u = 0; u < 4; ++u) acc[a][j][4 * q + u] = b[u];
-                    }
-                }
-            }
-            const Ops o0 = pp.template read<ST, 0>();
-            const Ops o1 = pp.template read<ST, 1>();
-            Pipe::mma(acc, o0);
-            Pipe::mma(acc, o1);
-            if constexpr (!FIRST) {
-                // all LDS reads first, then the MFMAs (the second half's reads land while
-                // the first half's MFMAs run)
-                __builtin_amdgcn_sched_group_barrier(0x100, 2 * Pipe::kReads, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 2 * TI * TJ, 0);
-            }
+            for (int q = 0; q < NLOAD; ++q) vo[q] = ahead ? voff_nxt[q] : voff_cur[q];
+            pp.template issue<SL>(vo, ahead ? s_load - KTp : s_load, K, zeros);
+            if (s_load == KTp) issue_bias((k_tile + 1) & 1, ntf * BF);
+            const Ops n0 = pp.template read<SN, 0>();
+            Pipe::mma(acc, c0);
+            const Ops n1 = pp.template read<SN, 1>();
+            Pipe::mma(acc, c1);
+            c0 = n0;
+            c1 = n1;
             __builtin_amdgcn_sched_barrier(0);
         };
-        using F0 = std::false_type;
-        using F1 = std::true_type;
-        using S0 = std::integral_constant<int, 0>;
-        using S1 = std::integral_constant<int, 1>;
-        using S2 = std::integral_constant<int, 2>;
-        // Loads issued by step kt are for step kt+2: this tile's while kt+2 < KTp, then the
-        // next tile's steps 0 and 1 (with its bias after step 0). Past the group's last
-        // tile they repeat this tile's first steps (in bounds, never read), which keeps
-        // the loop free of branches; they are waited for before the workgroup ends.
-        if (KTp == STAGES) {
-            // a single group of steps: step 0 loads step 2, steps 1 and 2 the next tile's 0, 1
-            k_step(S0{}, F1{}, voff_cur, 2);
-            k_step(S1{}, F0{}, voff_nxt, 0);
-            issue_bias((i + 1) & 1, ntf * BF);
-            k_step(S2{}, F0{}, voff_nxt, 1);
-        } else {
-            k_step(S0{}, F1{}, voff_cur, 2);
-            k_step(S1{}, F0{}, voff_cur, 3);
-            k_step(S2{}, F0{}, voff_cur, 4);
-            for (int kt = STAGES; kt < KTp - STAGES; kt += STAGES) {
-                k_step(S0{}, F0{}, voff_cur, kt + 2);
-                k_step(S1{}, F0{}, voff_cur, kt + 3);
-                k_step(S2{}, F0{}, voff_cur, kt + 4);
-            }
-            k_step(S0{}, F0{}, voff_cur, KTp - 1);
-            k_step(S1{}, F0{}, voff_nxt, 0);
-            issue_bias((i + 1) & 1, ntf * BF);
-            k_step(S2{}, F0{}, voff_nxt, 1);
-        }
+        // (a do-while: KTp >= STAGES, and a loop the compiler thinks may run zero times
+        // makes it keep a spilled copy of the initial accumulators for that path)
+        int kt = 0;
+        do {
+            k_step(std::integral_constant<int, 0>{}, kt);
+            k_step(std::integral_constant<int, 1>{}, kt + 1);
+            k_step(std::integral_constant<int, 2>{}, kt + 2);
+            k_step(std::integral_constant<int, 3>{}, kt + 3);
+            kt += STAGES;
+        } while (kt < KTp);
 
-        // ---- epilogue in registers, one slot per (token block j, column group G).
+        // ---- epilogue in registers.
         // acc[a][j][e] (bias included): column f = 32a + 8(e/4) + 4(lane/32) + e%4, token
         // 32j + lane%32 (both relative to the wave tile). Outputs never overlap the inputs
         // (checked on the host), so loads may be hoisted above stores.
@@ -544,7 +503,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         }
         // The wave's 16 column groups: kind (0 ff, 1 q, 2 k, 3 v) in bits 30-31 and the
         // element offset of the group's first column in the low bits (ff: column; q/k/v:
-        // head * S * hd + place in head), read four at a time by the scalar unit.
+        // head * S * hd + place in head), all sixteen in one scalar load.
         const int fw = n0 + wf * WF;
         const u32x16 desc = scalar_load16(p.col_desc + (fw >> 3));
         // whether the wave's columns meet the q or k slice (then RoPE applies)
@@ -576,8 +535,6 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             load_rope(0);
 #pragma unroll
             for (int G = 0; G < NG; ++G) {
-                __builtin_amdgcn_sched_barrier(0);
-                __syncthreads();   // the slot of (j, G)
                 if (fw + 8 * G >= N) continue;   // ragged last column tile
                 const unsigned d = desc[G];
                 const unsigned kind = d >> 30, off = d & 0x3fffffffu;
@@ -619,23 +576,21 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 if (tv[j]) store4_bf16(base + hv_off[j], y);
             }
         }
+        if (!has_next) break;
 #pragma unroll
         for (int q = 0; q < NLOAD; ++q) voff_cur[q] = voff_nxt[q];
         tt = ntt;
         tf = ntf;
     }
-    // idle slots until the other group is done; then the trailing loads into LDS
-    const int mine_end = my_off + n_mine * P;
-    for (int s = mine_end; s < total_slots; ++s) __syncthreads();
-    wait_vmcnt<0>();
+    wait_vmcnt<0>();   // the trailing loads into LDS
 }
 
 template <bool X_TL, bool W_FC, int DG>
 hipError_t launch_fast_one(const KernelArgs& a, int grid, hipStream_t stream) {
     if (a.K > 0 && a.K % (kBK * kStages) == 0)
-        hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, false>), dim3(grid), dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, false>), dim3(grid), dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, true>), dim3(grid), dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, true>), dim3(grid), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
