@@ -170,10 +170,10 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
         return FUSED_PROJ_EHIP;
     }
     // Kernel choice. The fast bf16 kernel needs a RoPE head size of 32, 64 or 128 (or no
-    // RoPE) and x and W spans under 4 GiB (it addresses them with 32-bit offsets). It is
-    // used only on exact tilings -- tokens and columns multiples of its tile, channels a
-    // multiple of its K-step group, at least one tile per CU -- the shapes it has been
-    // verified on; every other shape goes to the general kernel.
+    // RoPE) and x and W spans under 4 GiB (it addresses them with 32-bit offsets). With
+    // its large tiles it is used only on exact tilings; with its small tiles (chosen when
+    // the large ones cannot fill the CUs) on whole token tiles. Every other shape goes to
+    // the general kernel.
     // FUSED_PROJ_KERNEL=general forces the general kernel (the tests use it to cover both);
     // FUSED_PROJ_KERNEL=fast takes the fast kernel on any shape it can address.
     const char* force = std::getenv("FUSED_PROJ_KERNEL");
@@ -182,9 +182,12 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     const int dg = fp::fast_rope_groups((int)desc->head_dim, desc->rope && r.qw > 0);
     const bool fits32 = r.x_span * 2 < (int64_t(1) << 32) && desc->channels * r.F * 2 < (int64_t(1) << 32);
     const fp::TilePlan fp_plan = fp::fast_plan(r.M, r.F, num_cus);
-    const int64_t fast_tiles = (r.M / fp_plan.bm) * (r.F / fp_plan.bn);
-    const bool exact = r.M % fp_plan.bm == 0 && r.F % fp_plan.bn == 0 && desc->channels % fp::fast_k_multiple() == 0 &&
-                       desc->channels > 0 && fast_tiles >= (num_cus > 0 ? num_cus : 256);
+    const bool large = fp_plan.bn == 256;
+    // large tiles: exact tilings only; small tiles (too few large tiles to fill the CUs):
+    // whole token tiles, any column count (ragged last column tile) and any K (partial and
+    // padding K steps read zeros)
+    const bool exact = desc->channels > 0 && r.M % fp_plan.bm == 0 &&
+                       (!large || (r.F % fp_plan.bn == 0 && desc->channels % fp::fast_k_multiple() == 0));
     const bool addressable = fp::fast_addressable(r.M, r.S, desc->ff_dim, r.qw);
     h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && addressable && (exact || want_fast) && !want_general;
     h->dg = dg < 0 ? 0 : dg;

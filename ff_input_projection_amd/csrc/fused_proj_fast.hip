@@ -305,23 +305,27 @@ __device__ __forceinline__ bool block_tile(int k, int tiles_t, int tiles_f, int 
     return true;
 }
 
-// Tile shapes compiled for the fast kernel: BF output columns x BT tokens per workgroup,
-// NWF x NWT waves (one per SIMD), K steps of BK through STAGES LDS stages.
-constexpr int kBF = 256, kBT = 256, kNWF = 2, kNWT = 4, kBK = 32, kStages = 4;
-constexpr int kThreads = 64 * kNWF * kNWT;
+// Tile shapes compiled for the fast kernel, BF output columns x BT tokens per workgroup
+// with NWF x NWT waves; K steps of BK through STAGES LDS stages for both.
+//  - large: 256 x 256 by 2 x 4 waves of 128 x 64, one workgroup per CU (128 KB of LDS);
+//  - small: 128 x 128 by 1 x 4 waves of 128 x 32, two workgroups per CU (64 KB each), for
+//    problems with fewer large tiles than CUs (short K, few tokens): four times the tiles.
+struct LargeTile { static constexpr int BF = 256, BT = 256, NWF = 2, NWT = 4; };
+struct SmallTile { static constexpr int BF = 128, BT = 128, NWF = 1, NWT = 4; };
+constexpr int kBK = 32, kStages = 4;
 
 // X_TL: x token-major [b,s,c] (else channels-first). W_FC: W [F,C] (else [C,F]).
 // DG: RoPE partner distance in 8-column groups (hd/16), 0 = no RoPE. TAILK: K is not a
 // multiple of STAGES * BK (some K steps are partial or padding).
-template <bool X_TL, bool W_FC, int DG, bool TAILK>
-__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_proj_fast_kernel(
-    KernelArgs p) {
-    constexpr int BF = kBF, BT = kBT, BK = kBK, STAGES = kStages;
-    using C = FastCfg<X_TL, W_FC, BF, BT, kNWF, kNWT, BK, STAGES>;
+template <bool X_TL, bool W_FC, int DG, bool TAILK, class T>
+__global__ __launch_bounds__(64 * T::NWF * T::NWT, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+fused_proj_fast_kernel(KernelArgs p) {
+    constexpr int BF = T::BF, BT = T::BT, BK = kBK, STAGES = kStages, kNWT = T::NWT;
+    using C = FastCfg<X_TL, W_FC, BF, BT, T::NWF, kNWT, BK, STAGES>;
     using Pipe = FastPipe<C, X_TL, W_FC, BK, TAILK>;
     using Ops = typename Pipe::Ops;
     constexpr int WF = C::WF, WT = C::WT, TI = C::TI, TJ = C::TJ, NG = C::NG, NLOAD = C::NLOAD;
-    static_assert(C::NW == 8 && C::KK == 2, "eight waves, two MFMA k steps per K step");
+    static_assert(C::KK == 2, "two MFMA k steps per K step");
     static_assert(STAGES == 4, "the wait counts below are written for four stages");
     static_assert(NG == 16, "one 16-entry column descriptor load per wave");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
@@ -585,19 +589,32 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     wait_vmcnt<0>();   // the trailing loads into LDS
 }
 
-template <bool X_TL, bool W_FC, int DG>
+template <bool X_TL, bool W_FC, int DG, class T>
 hipError_t launch_fast_one(const KernelArgs& a, int grid, hipStream_t stream) {
+    const dim3 block(64 * T::NWF * T::NWT);
     if (a.K > 0 && a.K % (kBK * kStages) == 0)
-        hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, false, T>), dim3(grid), block, 0, stream, a);
     else
-        hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, true, T>), dim3(grid), block, 0, stream, a);
     return hipGetLastError();
 }
 
-template <int DG>
+template <int DG, class T>
 hipError_t dispatch_fast_layouts(bool x_tl, bool w_fc, const KernelArgs& a, int grid, hipStream_t s) {
-    if (x_tl) return w_fc ? launch_fast_one<true, true, DG>(a, grid, s) : launch_fast_one<true, false, DG>(a, grid, s);
-    return w_fc ? launch_fast_one<false, true, DG>(a, grid, s) : launch_fast_one<false, false, DG>(a, grid, s);
+    if (x_tl)
+        return w_fc ? launch_fast_one<true, true, DG, T>(a, grid, s) : launch_fast_one<true, false, DG, T>(a, grid, s);
+    return w_fc ? launch_fast_one<false, true, DG, T>(a, grid, s) : launch_fast_one<false, false, DG, T>(a, grid, s);
+}
+
+template <class T>
+hipError_t dispatch_fast_rope(int dg, bool x_tl, bool w_fc, const KernelArgs& a, int grid, hipStream_t s) {
+    switch (dg) {
+        case 0: return dispatch_fast_layouts<0, T>(x_tl, w_fc, a, grid, s);
+        case 2: return dispatch_fast_layouts<2, T>(x_tl, w_fc, a, grid, s);
+        case 4: return dispatch_fast_layouts<4, T>(x_tl, w_fc, a, grid, s);
+        case 8: return dispatch_fast_layouts<8, T>(x_tl, w_fc, a, grid, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -609,11 +626,19 @@ int fast_rope_groups(int head_dim, bool rope) {
 }
 
 TilePlan fast_plan(int64_t M, int64_t F, int num_cus) {
-    TilePlan t{kBT, kBF, kBK, 8, 0};
-    const int64_t tiles = ((M + kBT - 1) / kBT) * ((F + kBF - 1) / kBF);
-    int64_t grid = num_cus > 0 ? num_cus : 256;           // one persistent workgroup per CU
-    if (grid > tiles) grid = tiles;
-    t.grid = (int)((grid + 7) / 8 * 8);                   // a multiple of the 8 XCDs
+    const int cus = num_cus > 0 ? num_cus : 256;
+    const int64_t large = ((M + LargeTile::BT - 1) / LargeTile::BT) * ((F + LargeTile::BF - 1) / LargeTile::BF);
+    if (large >= cus) {
+        // persistent: one workgroup per CU walks the large tiles
+        TilePlan t{LargeTile::BT, LargeTile::BF, kBK, 8, 0};
+        t.grid = cus;
+        t.grid = (t.grid + 7) / 8 * 8;   // a multiple of the 8 XCDs
+        return t;
+    }
+    // too few large tiles to fill the CUs: small tiles, one per workgroup
+    TilePlan t{SmallTile::BT, SmallTile::BF, kBK, 8, 0};
+    const int64_t small = ((M + SmallTile::BT - 1) / SmallTile::BT) * ((F + SmallTile::BF - 1) / SmallTile::BF);
+    t.grid = (int)((small + 7) / 8 * 8);
     return t;
 }
 
@@ -624,7 +649,8 @@ bool fast_addressable(int64_t M, int64_t S, int64_t ff_dim, int64_t qw) {
 
 int fast_k_multiple() { return kBK * kStages; }
 
-int64_t fast_col_desc_entries(int64_t F) { return (F + kBF - 1) / kBF * (kBF / 8); }
+// Entries for whole large column tiles, which also covers whole small ones.
+int64_t fast_col_desc_entries(int64_t F) { return (F + LargeTile::BF - 1) / LargeTile::BF * (LargeTile::BF / 8); }
 
 void fast_col_desc(int64_t S, int64_t ff_dim, int64_t n_heads, int64_t head_dim, int64_t F, unsigned* out,
                    int64_t entries) {
@@ -647,14 +673,12 @@ void fast_col_desc(int64_t S, int64_t ff_dim, int64_t n_heads, int64_t head_dim,
 
 hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, const TilePlan& pl, const KernelArgs& a,
                                   hipStream_t stream) {
-    if (pl.bm != kBT || pl.bn != kBF || pl.bk != kBK || pl.grid <= 0 || pl.grid % 8) return hipErrorInvalidValue;
-    switch (dg) {
-        case 0: return dispatch_fast_layouts<0>(x_tokens_last, w_fc, a, pl.grid, stream);
-        case 2: return dispatch_fast_layouts<2>(x_tokens_last, w_fc, a, pl.grid, stream);
-        case 4: return dispatch_fast_layouts<4>(x_tokens_last, w_fc, a, pl.grid, stream);
-        case 8: return dispatch_fast_layouts<8>(x_tokens_last, w_fc, a, pl.grid, stream);
-        default: return hipErrorInvalidValue;
-    }
+    if (pl.bk != kBK || pl.grid <= 0 || pl.grid % 8) return hipErrorInvalidValue;
+    if (pl.bm == LargeTile::BT && pl.bn == LargeTile::BF)
+        return dispatch_fast_rope<LargeTile>(dg, x_tokens_last, w_fc, a, pl.grid, stream);
+    if (pl.bm == SmallTile::BT && pl.bn == SmallTile::BF)
+        return dispatch_fast_rope<SmallTile>(dg, x_tokens_last, w_fc, a, pl.grid, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace fp

@@ -64,6 +64,11 @@ SMALL = [
     # token-major [F,C] weight, RoPE hd 32, two M tiles + tail, bias, no GELU
     with_shape(WORKLOADS["bert_qkv_bf16"], "tl_fc_hd32", x_shape=(3, 100, 96), ff_dim=32, n_heads=4,
                head_dim=32, rope=True, w_layout="fc", seed=109),
+    # the fast kernel's small tiles: 256 tokens (two whole 128-token tiles), K = 72 (two
+    # whole K steps, a ragged one and a padding one), F = 448 (a ragged last 128-column
+    # tile), RoPE hd 64, GELU
+    with_shape(WORKLOADS["walrus_bf16"], "cf_small_tiles_rope", x_shape=(2, 72, 8, 16, 1), ff_dim=64,
+               n_heads=2, head_dim=64, seed=110),
     # fp32, token-major, [F,C], RoPE hd 8, GELU
     with_shape(WORKLOADS["tiny_f32"], "f32_tl_fc", layout="tokens_last", x_shape=(3, 50, 36), ff_dim=16,
                n_heads=3, head_dim=8, w_layout="fc", seed=106),
@@ -92,12 +97,11 @@ def test_small_ragged_all_tokens(wl, kernel_choice):
     _check(wl, inp, outs, all_tokens(wl), wl.name)
 
 
-@pytest.mark.skip(reason="the persistent fast kernel faulted the GPU on the small-K workload "
-                         "(x [2,320,64,64], W [320,960]: padded K steps, a ragged column tile, fewer "
-                         "tiles than CUs) with no cause found yet; it is switched off for every shape "
-                         "that is not an exact tiling, and this case stays off the GPU until the cause "
-                         "is shown")
 def test_fast_kernel_on_padded_or_ragged_tiling(monkeypatch):
+    """The small-K workload (padded K steps, a ragged column tile, fewer large tiles than
+    CUs) forced onto the fast kernel, which takes its small tiles there. This shape once
+    faulted the GPU: the cause, missing wait states before the inline-asm loads, is fixed
+    and pinned on the CPU by test_isa_hazards.py."""
     monkeypatch.setenv("FUSED_PROJ_KERNEL", "fast")
     wl = WORKLOADS["smallk_qkv_bf16"]
     inp = make_inputs(wl)
