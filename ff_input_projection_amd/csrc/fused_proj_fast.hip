@@ -9,12 +9,13 @@
 //   - rotate-half RoPE on q/k (NVIDIA/Fuser issue "Improve performance on RoPE
 //     (and code around it)", rope_one_entry): the partner column j +- hd/2 sits
 //     in the same lane, hd/32 MFMA row tiles (or hd/16 column groups) away;
-//   - 8-byte stores straight into ff [b,S,ff] and the head-major q/k/v buffers
-//     [b*H,S,hd] (memory-efficient-attention issue "Improve performance via
-//     batched-matmul and fused multiplies"), with consecutive tokens adjacent
-//     in q/k/v.
-// Every branch of the epilogue depends only on the column group, which is the
-// same for the whole wave, so it never diverges.
+//   - stores into ff [b,S,ff] and the head-major q/k/v buffers [b*H,S,hd]
+//     (memory-efficient-attention issue "Improve performance via batched-matmul
+//     and fused multiplies"), with consecutive tokens adjacent in q/k/v: 8 bytes
+//     per lane straight from registers, or restaged through LDS into whole
+//     256-byte token rows.
+// Every branch of the compute part of the epilogue depends only on the column
+// group, which is the same for the whole wave, so it never diverges.
 //
 // Operands. x is read straight from its channels-first [b,c,spatial] or
 // token-major [b,s,c] layout (Walrus PR "Make fused_ff_qkv contiguous": no
@@ -28,16 +29,13 @@
 // ones through ds_read_b128. Chunks outside the problem (ragged M, N or K) are
 // read from a small zero block instead, so no access leaves the operands.
 //
-// Schedule. The kernel is persistent: one workgroup of 4 waves per CU, one wave
-// per SIMD, walks a list of 256 x 256 tiles. Each wave owns 128 (f) x 128 (token)
-// outputs, 256 fp32 accumulators (the compiler keeps them in the accumulation
-// registers, which one wave per SIMD may use next to 256 ordinary ones). The large
-// wave tile reads 0.5 KB of operands from LDS per MFMA instead of 0.75 KB for a
-// 128 x 64 tile, which keeps the LDS, also written by the direct loads, well below
-// its bandwidth. The direct-load pipeline is four K steps of 32 deep and runs
-// straight on into the next tile, and the operands of the next K step are read from
-// LDS while the MFMAs of the current one run. The workgroup's tiles come from a
-// contiguous, grouped range of the XCD it runs on.
+// Schedule. Two tile shapes (see LargeTile / SmallTile below). Large: 256 x 256
+// tiles, 8 waves of 128 (f) x 64 (token) outputs, two per SIMD, one persistent
+// workgroup per CU walking a list of tiles from a contiguous, grouped range of the
+// XCD it runs on. Small (problems with fewer large tiles than CUs): 128 x 128 tiles,
+// 4 waves of 128 x 32, two workgroups per CU. The direct-load pipeline is four K
+// steps of 32 deep and runs straight on into the next tile, and the operands of
+// the next K step are read from LDS while the MFMAs of the current one run.
 #include "device_common.h"
 #include "fused_proj_kernels.h"
 
@@ -62,12 +60,11 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Four fp32 values rounded to bf16 and stored as 8 bytes.
 __device__ __forceinline__ void store4_bf16(char* dst, const float* o) {
     bf16x4 v;
-    v[0] = (__bf16)o[0];
-    v[1] = (__bf16)o[1];
-    v[2] = (__bf16)o[2];
-    v[3] = (__bf16)o[3];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = (__bf16)o[u];
     *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, v);
 }
 
@@ -310,15 +307,21 @@ __device__ __forceinline__ bool block_tile(int k, int tiles_t, int tiles_f, int 
 //  - large: 256 x 256 by 2 x 4 waves of 128 x 64, one workgroup per CU (128 KB of LDS);
 //  - small: 128 x 128 by 1 x 4 waves of 128 x 32, two workgroups per CU (64 KB each), for
 //    problems with fewer large tiles than CUs (short K, few tokens): four times the tiles.
-struct LargeTile { static constexpr int BF = 256, BT = 256, NWF = 2, NWT = 4; };
-struct SmallTile { static constexpr int BF = 128, BT = 128, NWF = 1, NWT = 4; };
+struct LargeTile {
+    static constexpr int BF = 256, BT = 256, NWF = 2, NWT = 4, PER_CU = 1;
+    static constexpr bool RESTAGE = false;
+};
+struct SmallTile {
+    static constexpr int BF = 128, BT = 128, NWF = 1, NWT = 4, PER_CU = 2;
+    static constexpr bool RESTAGE = true;
+};
 constexpr int kBK = 32, kStages = 4;
 
 // X_TL: x token-major [b,s,c] (else channels-first). W_FC: W [F,C] (else [C,F]).
 // DG: RoPE partner distance in 8-column groups (hd/16), 0 = no RoPE. TAILK: K is not a
 // multiple of STAGES * BK (some K steps are partial or padding).
 template <bool X_TL, bool W_FC, int DG, bool TAILK, class T>
-__global__ __launch_bounds__(64 * T::NWF * T::NWT, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+__global__ __launch_bounds__(64 * T::NWF * T::NWT, T::PER_CU) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 fused_proj_fast_kernel(KernelArgs p) {
     constexpr int BF = T::BF, BT = T::BT, BK = kBK, STAGES = kStages, kNWT = T::NWT;
     using C = FastCfg<X_TL, W_FC, BF, BT, T::NWF, kNWT, BK, STAGES>;
@@ -392,7 +395,6 @@ fused_proj_fast_kernel(KernelArgs p) {
 
     // epilogue constants
     const int hl = lane >> 5;
-    char* const out_ff = static_cast<char*>(p.ff);
     const float* __restrict__ const rope_cos = p.rope_cos;
     const float* __restrict__ const rope_sin = p.rope_sin;
     const int ff_dim = p.ff_dim, hd = p.head_dim, act = p.act;
@@ -486,25 +488,14 @@ fused_proj_fast_kernel(KernelArgs p) {
             kt += STAGES;
         } while (kt < KTp);
 
-        // ---- epilogue in registers.
-        // acc[a][j][e] (bias included): column f = 32a + 8(e/4) + 4(lane/32) + e%4, token
-        // 32j + lane%32 (both relative to the wave tile). Outputs never overlap the inputs
-        // (checked on the host), so loads may be hoisted above stores.
-        //
-        // Per-lane byte offsets (32-bit: the host keeps every output under 4 GiB) of this
-        // lane's token: its ff row, its q/k/v row of head 0, its cos/sin row.
-        unsigned ff_off[TJ], hv_off[TJ], rp_off[TJ];
-        bool tv[TJ];
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-            const int t = m0 + wt * WT + 32 * j + (lane & 31);
-            tv[j] = t < M;
-            const int tc = tv[j] ? t : 0;
-            const int bi = tc / S, s = tc - bi * S;
-            ff_off[j] = (unsigned)((tc * ff_dim + 4 * hl) * 2);
-            hv_off[j] = (unsigned)(((int64_t)bi * slab_elems + (int64_t)s * hd + 4 * hl) * 2);
-            rp_off[j] = (unsigned)((s * (DG * 8) + 4 * hl) * 4);
-        }
+        // ---- epilogue. acc[a][j][e] (bias included): column f = 32a + 8(e/4) + 4(lane/32)
+        // + e%4, token 32j + lane%32 (both relative to the wave tile). Outputs never overlap
+        // the inputs (checked on the host), so loads may be hoisted above stores. GELU on ff
+        // columns and RoPE on q/k columns run in registers; the bf16 results are stored
+        // either straight from registers, 8 bytes per lane as each column group is done
+        // (large tiles: the stores drain while the rest is computed), or restaged through
+        // LDS into whole 256-byte token rows once every group is done (small tiles).
+        const int tw0 = m0 + wt * WT;   // the wave's first token
         // The wave's 16 column groups: kind (0 ff, 1 q, 2 k, 3 v) in bits 30-31 and the
         // element offset of the group's first column in the low bits (ff: column; q/k/v:
         // head * S * hd + place in head), all sixteen in one scalar load.
@@ -513,71 +504,220 @@ fused_proj_fast_kernel(KernelArgs p) {
         // whether the wave's columns meet the q or k slice (then RoPE applies)
         const bool wave_rope = DG > 0 && fw < ff_dim + 2 * p.qw && fw + WF > ff_dim;
         constexpr int HD = DG > 0 ? 16 * DG : 16, HALF = HD / 2, NR = HALF / 8, NRB = NR > 4 ? 4 : NR;
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-            // cos/sin of this lane's token at its 4 columns of each first-half group of a
-            // head; every head of the wave uses the same ones. Loaded before this token
-            // block's stores, so that the wait for them does not wait for those stores --
-            // all at once for head sizes up to 64, in two halves for 128 (registers).
+
+        if constexpr (T::RESTAGE) {
+            // The stores: written straight from the accumulator layout, a store instruction
+            // touches 32 token rows with 16 bytes each; restaged, each one writes 4 token rows of
+            // 256 contiguous bytes (the wave's 128 columns). The wave owns a 4 KB region of the
+            // stage no K step uses until the next tile's first barrier: 16 tokens x 128 bf16
+            // columns, the 16-byte chunk of column group G of token row t at chunk G ^ t
+            // (conflict-free writes and reads).
+            static_assert(C::W_BYTES == C::X_BYTES && C::W_BYTES == C::NW / 2 * 4096, "restage regions");
+            const unsigned wave_lds = wave < C::NW / 2 ? pp.lds0 + (STAGES - 1) * C::W_BYTES + wave * 4096
+                                                       : pp.lds0 + C::X_REGION + (STAGES - 1) * C::X_BYTES +
+                                                             (wave - C::NW / 2) * 4096;
+            // The lane index again, recomputed per tile where the compiler cannot see it: the
+            // LDS addresses and column selects below depend only on it, and hoisted out of the
+            // tile loop they would hold some 40 registers through the K loop (spilled to
+            // scratch, whose reload waits for every load in flight).
+            int lane_e;
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+            // this lane's 16-byte chunk of a token row: column group gl, its destination buffer
+            // and element offset, and the per-token byte offset rule of that buffer
+            const int gl = lane_e & 15;
+            unsigned dl = desc[0];
+    #pragma unroll
+            for (int g = 1; g < 16; ++g) dl = gl == g ? desc[g] : dl;
+            const unsigned kind_l = dl >> 30;
+            char* const base_l = static_cast<char*>(kind_l == 0 ? p.ff : kind_l == 1 ? p.q : kind_l == 2 ? p.k : p.v) +
+                                 (size_t)(dl & 0x3fffffffu) * 2;
+            const bool col_ok = fw + 8 * gl < N;
+            // the wave's tokens usually lie in one slab: then the slab index is wave-uniform
+            const int bi_first = tw0 / S;
+            const bool one_slab = (tw0 + WT - 1 < M ? tw0 + WT - 1 : M - 1) / S == bi_first;
+            auto token_off = [&](int t) __attribute__((always_inline)) {
+                const int bi = one_slab ? bi_first : t / S;
+                const int s = t - bi * S;
+                return kind_l == 0 ? (unsigned)t * (unsigned)(2 * ff_dim)
+                                   : (unsigned)(((int64_t)bi * slab_elems + (int64_t)s * hd) * 2);
+            };
+
+            // cos/sin of this lane's token at its 4 columns of each first-half group of a head;
+            // every head of the wave uses the same ones -- all at once for head sizes up to 64,
+            // in two halves for 128 (registers). Every token block is finished and rounded
+            // before the first store: a load issued after a store would wait for it too (the
+            // vector memory counter counts in order).
             f32x4 rc[NRB], rsn[NRB];
-            auto load_rope = [&](int r0) __attribute__((always_inline)) {
-#pragma unroll
+            auto load_rope = [&](int j, int r0) __attribute__((always_inline)) {
+                const int t = tw0 + 32 * j + (lane_e & 31);
+                const int tc = t < M ? t : 0;
+                const int s = tc - (tc / S) * S;
+                const unsigned rp_off = (unsigned)((s * (DG * 8) + 4 * (lane_e >> 5)) * 4);
+    #pragma unroll
                 for (int r = 0; r < NRB; ++r) {
                     rc[r] = f32x4{};
                     rsn[r] = f32x4{};
                 }
                 if (wave_rope) {
-#pragma unroll
+    #pragma unroll
                     for (int r = 0; r < NRB; ++r) {
-                        const char* const c = reinterpret_cast<const char*>(rope_cos + 8 * (r0 + r)) + rp_off[j];
-                        const char* const sn = reinterpret_cast<const char*>(rope_sin + 8 * (r0 + r)) + rp_off[j];
+                        const char* const c = reinterpret_cast<const char*>(rope_cos + 8 * (r0 + r)) + rp_off;
+                        const char* const sn = reinterpret_cast<const char*>(rope_sin + 8 * (r0 + r)) + rp_off;
                         rc[r] = *reinterpret_cast<const f32x4*>(c);
                         rsn[r] = *reinterpret_cast<const f32x4*>(sn);
                     }
                 }
             };
-            load_rope(0);
-#pragma unroll
-            for (int G = 0; G < NG; ++G) {
-                if (fw + 8 * G >= N) continue;   // ragged last column tile
-                const unsigned d = desc[G];
-                const unsigned kind = d >> 30, off = d & 0x3fffffffu;
-                float y[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) y[u] = acc[G >> 2][j][4 * (G & 3) + u];
-                if (kind == 0) {
-                    if (act == 1) {
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) y[u] = gelu_erf_fast(y[u]);
+            u32x2 pk[TJ][NG];   // the outputs rounded to bf16: half the registers of acc
+    #pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+                // (a fence per token block: the next block's loads hoisted here would raise the
+                // register peak)
+                __builtin_amdgcn_sched_barrier(0);
+                load_rope(j, 0);
+    #pragma unroll
+                for (int G = 0; G < NG; ++G) {
+                    if (fw + 8 * G >= N) continue;   // ragged last column tile
+                    const unsigned kind = desc[G] >> 30;
+                    if (kind == 0) {
+                        if (act == 1) {
+    #pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                acc[G >> 2][j][4 * (G & 3) + u] = gelu_erf_fast(acc[G >> 2][j][4 * (G & 3) + u]);
+                        }
+                        continue;
                     }
-                    if (tv[j]) store4_bf16(out_ff + (size_t)off * 2 + ff_off[j], y);
-                    continue;
+                    if (DG > 0 && kind != 3) {
+                        // Heads start on head_dim boundaries of the wave's columns, so the
+                        // group's place in its head is a compile-time constant. A first-half
+                        // group is rotated together with its partner DG groups on.
+                        const int jh8 = (8 * G) % HD;
+                        if (jh8 >= HALF || G + DG >= NG) continue;
+                        const int G2 = (G + DG < NG) ? G + DG : G;   // constant after unrolling
+                        if (NR > NRB && jh8 == 8 * NRB) load_rope(j, NRB);   // second half (head size 128)
+                        const f32x4 c = rc[(jh8 / 8) % NRB], sn = rsn[(jh8 / 8) % NRB];
+    #pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const float y1 = acc[G >> 2][j][4 * (G & 3) + u];
+                            const float y2 = acc[G2 >> 2][j][4 * (G2 & 3) + u];
+                            acc[G >> 2][j][4 * (G & 3) + u] = y1 * c[u] - y2 * sn[u];
+                            acc[G2 >> 2][j][4 * (G2 & 3) + u] = y2 * c[u] + y1 * sn[u];
+                        }
+                    }
                 }
-                char* const base = static_cast<char*>(kind == 1 ? p.q : kind == 2 ? p.k : p.v) + (size_t)off * 2;
-                if (DG > 0 && kind != 3) {
-                    // Heads start on head_dim boundaries of the wave's columns, so the
-                    // group's place in its head is a compile-time constant. A first-half
-                    // group is rotated together with its partner DG groups on, whose own
-                    // slot does nothing.
-                    const int jh8 = (8 * G) % HD;
-                    if (jh8 >= HALF || G + DG >= NG) continue;
-                    const int G2 = (G + DG < NG) ? G + DG : G;   // constant after unrolling
-                    if (NR > NRB && jh8 == 8 * NRB) load_rope(NRB);   // second half (head size 128)
-                    const f32x4 c = rc[(jh8 / 8) % NRB], sn = rsn[(jh8 / 8) % NRB];
-                    float o1[4], o2[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const float y2 = acc[G2 >> 2][j][4 * (G2 & 3) + u];
-                        o1[u] = y[u] * c[u] - y2 * sn[u];
-                        o2[u] = y2 * c[u] + y[u] * sn[u];
-                    }
-                    if (tv[j]) {
-                        store4_bf16(base + hv_off[j], o1);
-                        store4_bf16(base + hv_off[j] + HALF * 2, o2);
-                    }
-                    continue;
+    #pragma unroll
+                for (int G = 0; G < NG; ++G) {
+                    bf16x4 v;
+    #pragma unroll
+                    for (int u = 0; u < 4; ++u) v[u] = (__bf16)acc[G >> 2][j][4 * (G & 3) + u];
+                    pk[j][G] = __builtin_bit_cast(u32x2, v);
                 }
-                if (tv[j]) store4_bf16(base + hv_off[j], y);
+            }
+    #pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+    #pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    // the lanes whose token is in this half of the token block write its rows
+                    if (((lane_e & 31) >> 4) == h) {
+                        const int t = lane_e & 15;
+    #pragma unroll
+                        for (int G = 0; G < NG; ++G) {
+                            const unsigned a = wave_lds + t * 256 + ((G ^ t) * 16) + (lane_e >> 5) * 8;
+                            *(__attribute__((address_space(3))) u32x2*)(size_t)a = pk[j][G];
+                        }
+                    }
+    #pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int r = (lane_e >> 4) + 4 * rr;   // token row of the half block
+                        const unsigned a = wave_lds + r * 256 + ((gl ^ r) * 16);
+                        const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(size_t)a;
+                        const int t = tw0 + 32 * j + 16 * h + r;
+                        if (t < M && col_ok) *reinterpret_cast<u32x4*>(base_l + token_off(t)) = v;
+                    }
+                }
+            }
+        } else {
+            // Per-lane byte offsets (32-bit: the host keeps every output under 4 GiB) of this
+            // lane's token: its ff row, its q/k/v row of head 0, its cos/sin row.
+            unsigned ff_off[TJ], hv_off[TJ], rp_off[TJ];
+            bool tv[TJ];
+    #pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+                const int t = tw0 + 32 * j + (lane & 31);
+                tv[j] = t < M;
+                const int tc = tv[j] ? t : 0;
+                const int bi = tc / S, s = tc - bi * S;
+                ff_off[j] = (unsigned)tc * (unsigned)(2 * ff_dim) + (unsigned)(8 * hl);
+                hv_off[j] = (unsigned)(((int64_t)bi * slab_elems + (int64_t)s * hd + 4 * hl) * 2);
+                rp_off[j] = (unsigned)((s * (DG * 8) + 4 * hl) * 4);
+            }
+            char* const out_ff = static_cast<char*>(p.ff);
+    #pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+                // cos/sin of this lane's token at its 4 columns of each first-half group of a
+                // head; every head of the wave uses the same ones. Loaded before this token
+                // block's stores, so that the wait for them does not wait for those stores --
+                // all at once for head sizes up to 64, in two halves for 128 (registers).
+                f32x4 rc[NRB], rsn[NRB];
+                auto load_rope = [&](int r0) __attribute__((always_inline)) {
+    #pragma unroll
+                    for (int r = 0; r < NRB; ++r) {
+                        rc[r] = f32x4{};
+                        rsn[r] = f32x4{};
+                    }
+                    if (wave_rope) {
+    #pragma unroll
+                        for (int r = 0; r < NRB; ++r) {
+                            const char* const c = reinterpret_cast<const char*>(rope_cos + 8 * (r0 + r)) + rp_off[j];
+                            const char* const sn = reinterpret_cast<const char*>(rope_sin + 8 * (r0 + r)) + rp_off[j];
+                            rc[r] = *reinterpret_cast<const f32x4*>(c);
+                            rsn[r] = *reinterpret_cast<const f32x4*>(sn);
+                        }
+                    }
+                };
+                load_rope(0);
+    #pragma unroll
+                for (int G = 0; G < NG; ++G) {
+                    if (fw + 8 * G >= N) continue;   // ragged last column tile
+                    const unsigned d = desc[G];
+                    const unsigned kind = d >> 30, off = d & 0x3fffffffu;
+                    float y[4];
+    #pragma unroll
+                    for (int u = 0; u < 4; ++u) y[u] = acc[G >> 2][j][4 * (G & 3) + u];
+                    if (kind == 0) {
+                        if (act == 1) {
+    #pragma unroll
+                            for (int u = 0; u < 4; ++u) y[u] = gelu_erf_fast(y[u]);
+                        }
+                        if (tv[j]) store4_bf16(out_ff + (size_t)off * 2 + ff_off[j], y);
+                        continue;
+                    }
+                    char* const base = static_cast<char*>(kind == 1 ? p.q : kind == 2 ? p.k : p.v) + (size_t)off * 2;
+                    if (DG > 0 && kind != 3) {
+                        // Heads start on head_dim boundaries of the wave's columns, so the
+                        // group's place in its head is a compile-time constant. A first-half
+                        // group is rotated together with its partner DG groups on, whose own
+                        // slot does nothing.
+                        const int jh8 = (8 * G) % HD;
+                        if (jh8 >= HALF || G + DG >= NG) continue;
+                        const int G2 = (G + DG < NG) ? G + DG : G;   // constant after unrolling
+                        if (NR > NRB && jh8 == 8 * NRB) load_rope(NRB);   // second half (head size 128)
+                        const f32x4 c = rc[(jh8 / 8) % NRB], sn = rsn[(jh8 / 8) % NRB];
+                        float o1[4], o2[4];
+    #pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const float y2 = acc[G2 >> 2][j][4 * (G2 & 3) + u];
+                            o1[u] = y[u] * c[u] - y2 * sn[u];
+                            o2[u] = y2 * c[u] + y[u] * sn[u];
+                        }
+                        if (tv[j]) {
+                            store4_bf16(base + hv_off[j], o1);
+                            store4_bf16(base + hv_off[j] + HALF * 2, o2);
+                        }
+                        continue;
+                    }
+                    if (tv[j]) store4_bf16(base + hv_off[j], y);
+                }
             }
         }
         if (!has_next) break;

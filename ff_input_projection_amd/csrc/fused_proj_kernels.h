@@ -56,10 +56,11 @@ hipError_t launch_fused_proj(DType dt, bool x_tokens_last, bool w_fc, const Tile
 // Whether a tile plan is compiled for this combination.
 bool plan_supported(DType dt, const TilePlan& plan);
 
-// Fast bf16 kernel (F-major MFMA orientation, register epilogue, persistent workgroups
-// of two wave groups over 256 x 128 tiles). fast_rope_groups returns the RoPE partner distance in 8-column
-// groups it needs (0 without RoPE) or -1 when the head size is not supported by it.
-// fast_plan picks its tiles and grid (one workgroup per CU, a multiple of 8).
+// Fast bf16 kernel (F-major MFMA orientation, register epilogue; persistent 256 x 256
+// tiles, or 128 x 128 tiles two per CU when the large ones cannot fill the CUs).
+// fast_rope_groups returns the RoPE partner distance in 8-column groups it needs (0
+// without RoPE) or -1 when the head size is not supported by it. fast_plan picks the
+// tile shape and grid (a multiple of 8).
 int fast_rope_groups(int head_dim, bool rope);
 TilePlan fast_plan(int64_t M, int64_t F, int num_cus);
 // Whether the fast kernel can address this problem with its 32-bit per-lane output
