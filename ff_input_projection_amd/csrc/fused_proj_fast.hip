@@ -60,12 +60,15 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Four fp32 values rounded to bf16 and stored as 8 bytes.
-__device__ __forceinline__ void store4_bf16(char* dst, const float* o) {
+// Four fp32 values rounded to bf16, as 8 bytes; and stored.
+__device__ __forceinline__ u32x2 pack4_bf16(const float* o) {
     bf16x4 v;
 #pragma unroll
     for (int u = 0; u < 4; ++u) v[u] = (__bf16)o[u];
-    *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, v);
+    return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ void store4_bf16(char* dst, const float* o) {
+    *reinterpret_cast<u32x2*>(dst) = pack4_bf16(o);
 }
 
 // Four bf16 bias values from LDS, as fp32.
@@ -125,7 +128,7 @@ __device__ __forceinline__ unsigned k_operand_base(int rb, int kk, int lane) {
 }
 
 // Tile geometry: BF output columns x BT tokens per workgroup, NWF x NWT waves.
-template <bool X_TL, bool W_FC, int BF, int BT, int NWF, int NWT, int BK, int STAGES>
+template <bool X_TL, bool W_FC, int BF, int BT, int NWF, int NWT, int BK, int STAGES, int PAD>
 struct FastCfg {
     static constexpr int NW = NWF * NWT, THREADS = 64 * NW;
     static constexpr int WF = BF / NWF, WT = BT / NWT;   // wave tile
@@ -133,8 +136,9 @@ struct FastCfg {
     static constexpr int NG = TI * 4;                    // 8-column groups per wave
     static constexpr int KK = BK / 16;                   // MFMA k steps per K step
     static constexpr int W_BYTES = BF * BK * 2, X_BYTES = BT * BK * 2;
-    static constexpr int X_REGION = STAGES * W_BYTES;
-    static constexpr int LDS_BYTES = STAGES * (W_BYTES + X_BYTES);
+    // W stages, PAD spare bytes, X stages, PAD spare bytes
+    static constexpr int X_REGION = STAGES * W_BYTES + PAD;
+    static constexpr int LDS_BYTES = STAGES * (W_BYTES + X_BYTES) + 2 * PAD;
     static constexpr int W_CPR = W_FC ? BK / 8 : BF / 8;
     static constexpr int X_CPR = X_TL ? BK / 8 : BT / 8;
     static constexpr int W_INSTR = BF * BK / 8 / 64 / NW;   // direct loads per wave per K step
@@ -303,33 +307,47 @@ __device__ __forceinline__ bool block_tile(int k, int tiles_t, int tiles_f, int 
 }
 
 // Tile shapes compiled for the fast kernel, BF output columns x BT tokens per workgroup
-// with NWF x NWT waves; K steps of BK through STAGES LDS stages for both.
-//  - large: 256 x 256 by 2 x 4 waves of 128 x 64, one workgroup per CU (128 KB of LDS);
-//  - small: 128 x 128 by 1 x 4 waves of 128 x 32, two workgroups per CU (64 KB each), for
+// with NWF x NWT waves; K steps of BK through STAGES LDS stages for both. The loads run
+// three K steps ahead, which three stages carry; a fourth one is idle at the end of a
+// tile, where RESTAGE epilogues use it.
+//  - large: 256 x 256 by 2 x 4 waves of 128 x 64, one workgroup per CU (130 KB of LDS);
+//  - mid: 256 x 128 by 2 x 2 waves of 128 x 64, two workgroups per CU (72 KB each), which
+//    run out of step: one's epilogue overlaps the other's MFMAs;
+//  - small: 128 x 128 by 1 x 4 waves of 128 x 32, two workgroups per CU (65 KB each), for
 //    problems with fewer large tiles than CUs (short K, few tokens): four times the tiles.
 struct LargeTile {
-    static constexpr int BF = 256, BT = 256, NWF = 2, NWT = 4, PER_CU = 1;
+    static constexpr int BF = 256, BT = 256, NWF = 2, NWT = 4, PER_CU = 1, STAGES = 4;
+    static constexpr bool RESTAGE = true;
+};
+struct MidTile {
+    static constexpr int BF = 256, BT = 128, NWF = 2, NWT = 2, PER_CU = 2, STAGES = 3;
     static constexpr bool RESTAGE = false;
 };
 struct SmallTile {
-    static constexpr int BF = 128, BT = 128, NWF = 1, NWT = 4, PER_CU = 2;
+    static constexpr int BF = 128, BT = 128, NWF = 1, NWT = 4, PER_CU = 2, STAGES = 4;
     static constexpr bool RESTAGE = true;
 };
-constexpr int kBK = 32, kStages = 4;
+constexpr int kBK = 32, kPrefetch = 3;
+// Restaged epilogue rows: 16 tokens x (128 bf16 columns + 16 bytes of padding).
+constexpr int kRestageRows = 16, kRestageRow = 272;
 
 // X_TL: x token-major [b,s,c] (else channels-first). W_FC: W [F,C] (else [C,F]).
 // DG: RoPE partner distance in 8-column groups (hd/16), 0 = no RoPE. TAILK: K is not a
-// multiple of STAGES * BK (some K steps are partial or padding).
+// multiple of T::STAGES * BK (some K steps are partial or padding).
 template <bool X_TL, bool W_FC, int DG, bool TAILK, class T>
 __global__ __launch_bounds__(64 * T::NWF * T::NWT, T::PER_CU) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 fused_proj_fast_kernel(KernelArgs p) {
-    constexpr int BF = T::BF, BT = T::BT, BK = kBK, STAGES = kStages, kNWT = T::NWT;
-    using C = FastCfg<X_TL, W_FC, BF, BT, T::NWF, kNWT, BK, STAGES>;
+    constexpr int BF = T::BF, BT = T::BT, BK = kBK, STAGES = T::STAGES, PF = kPrefetch, kNWT = T::NWT;
+    // restaged epilogues: each wave owns kRestageRows rows of kRestageRow bytes in the idle
+    // last stage and the spare bytes after it
+    constexpr int PAD = T::RESTAGE ? T::NWF * T::NWT / 2 * (kRestageRows * kRestageRow - 4096) : 0;
+    using C = FastCfg<X_TL, W_FC, BF, BT, T::NWF, kNWT, BK, STAGES, PAD>;
     using Pipe = FastPipe<C, X_TL, W_FC, BK, TAILK>;
     using Ops = typename Pipe::Ops;
     constexpr int WF = C::WF, WT = C::WT, TI = C::TI, TJ = C::TJ, NG = C::NG, NLOAD = C::NLOAD;
     static_assert(C::KK == 2, "two MFMA k steps per K step");
-    static_assert(STAGES == 4, "the wait counts below are written for four stages");
+    static_assert(PF == 3 && (STAGES == 3 || STAGES == 4), "the wait counts below are written for three steps ahead");
+    static_assert(!T::RESTAGE || STAGES == 4, "the restaged epilogue uses the idle fourth stage");
     static_assert(NG == 16, "one 16-entry column descriptor load per wave");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
     __shared__ __attribute__((aligned(16))) __bf16 bias_s[2][BF];   // tile bias, double-buffered
@@ -403,7 +421,7 @@ fused_proj_fast_kernel(KernelArgs p) {
     unsigned voff_cur[NLOAD], voff_nxt[NLOAD];
     tile_offsets<C, X_TL, W_FC>(voff_cur, pp.kofs, tt * BT, tf * BF, wave, lane, K, N, M, S, p.x_sb, p.x_ss,
                                 p.x_sc);
-    // Prologue: the first STAGES-1 K steps of the first tile and its bias in flight; once
+    // Prologue: the first PF K steps of the first tile and its bias in flight; once
     // step 0 has landed (steps 1 and 2 may still be in flight), read its operands.
     pp.template issue<0>(voff_cur, 0, K, zeros);
     issue_bias(0, tf * BF);
@@ -447,8 +465,8 @@ fused_proj_fast_kernel(KernelArgs p) {
 
         // One K step kt, whose operands c0/c1 (its two MFMA k steps) are already in
         // registers: wait for this wave's loads of step kt+1 (those of kt+2 may stay in
-        // flight), barrier (every wave's loads of kt+1 landed; every wave has consumed the
-        // stage of kt-1), refill that stage with step kt+3, and read step kt+1's operands
+        // flight), barrier (every wave's loads of kt+1 landed; every wave has read the
+        // stages of kt and kt-1), fill the stage of kt+3, and read step kt+1's operands
         // while the MFMAs of kt run. Once kt+3 is past the tile the loads are the next
         // tile's first steps (its bias right after its step 0), and the last step reads the
         // next tile's step 0 ahead. Every step has the same code -- no step is peeled -- so
@@ -458,11 +476,11 @@ fused_proj_fast_kernel(KernelArgs p) {
         // LDS reads and MFMAs itself (forcing all reads first measured slower).
         auto k_step = [&](auto stc, int kt) __attribute__((always_inline)) {
             constexpr int ST = decltype(stc)::value;
-            constexpr int SN = (ST + 1) % STAGES, SL = (ST + STAGES - 1) % STAGES;
+            constexpr int SN = (ST + 1) % STAGES, SL = (ST + PF) % STAGES;
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<NLOAD>();
             __syncthreads();
-            const int s_load = kt + STAGES - 1;
+            const int s_load = kt + PF;
             const bool ahead = s_load >= KTp;   // wave-uniform
             unsigned vo[NLOAD];
 #pragma unroll
@@ -484,7 +502,7 @@ fused_proj_fast_kernel(KernelArgs p) {
             k_step(std::integral_constant<int, 0>{}, kt);
             k_step(std::integral_constant<int, 1>{}, kt + 1);
             k_step(std::integral_constant<int, 2>{}, kt + 2);
-            k_step(std::integral_constant<int, 3>{}, kt + 3);
+            if constexpr (STAGES == 4) k_step(std::integral_constant<int, 3>{}, kt + 3);
             kt += STAGES;
         } while (kt < KTp);
 
@@ -508,35 +526,45 @@ fused_proj_fast_kernel(KernelArgs p) {
         if constexpr (T::RESTAGE) {
             // The stores: written straight from the accumulator layout, a store instruction
             // touches 32 token rows with 16 bytes each; restaged, each one writes 4 token rows of
-            // 256 contiguous bytes (the wave's 128 columns). The wave owns a 4 KB region of the
-            // stage no K step uses until the next tile's first barrier: 16 tokens x 128 bf16
-            // columns, the 16-byte chunk of column group G of token row t at chunk G ^ t
-            // (conflict-free writes and reads).
-            static_assert(C::W_BYTES == C::X_BYTES && C::W_BYTES == C::NW / 2 * 4096, "restage regions");
-            const unsigned wave_lds = wave < C::NW / 2 ? pp.lds0 + (STAGES - 1) * C::W_BYTES + wave * 4096
+            // 256 contiguous bytes (the wave's 128 columns). The wave owns 16 rows of 272 bytes
+            // (a token's 128 bf16 columns and 16 bytes of padding, which keep both the row
+            // writes and the 16-byte chunk reads free of bank conflicts) in the stage no K step
+            // uses until the next tile's first barrier and the spare bytes after it. Every LDS
+            // address is a per-lane base plus a constant.
+            static_assert(C::W_BYTES == C::X_BYTES &&
+                              C::W_BYTES + PAD == C::NW / 2 * kRestageRows * kRestageRow,
+                          "restage regions");
+            constexpr int RGN = kRestageRows * kRestageRow;
+            const unsigned wave_lds = wave < C::NW / 2 ? pp.lds0 + (STAGES - 1) * C::W_BYTES + wave * RGN
                                                        : pp.lds0 + C::X_REGION + (STAGES - 1) * C::X_BYTES +
-                                                             (wave - C::NW / 2) * 4096;
+                                                             (wave - C::NW / 2) * RGN;
             // The lane index again, recomputed per tile where the compiler cannot see it: the
             // LDS addresses and column selects below depend only on it, and hoisted out of the
-            // tile loop they would hold some 40 registers through the K loop (spilled to
-            // scratch, whose reload waits for every load in flight).
+            // tile loop they would hold registers through the K loop (spilled to scratch, whose
+            // reload waits for every load in flight).
             int lane_e;
             asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
-            // this lane's 16-byte chunk of a token row: column group gl, its destination buffer
-            // and element offset, and the per-token byte offset rule of that buffer
-            const int gl = lane_e & 15;
+            // writer: token row lane%16 of a 16-token half block, column half lane/32 of each
+            // group; reader: 16-byte chunk (column group) gl of token rows r0 + 4 rr
+            const int gl = lane_e & 15, r0 = lane_e >> 4;
+            const unsigned wr_lds = wave_lds + (lane_e & 15) * kRestageRow + (lane_e >> 5) * 8;
+            const unsigned rd_lds = wave_lds + r0 * kRestageRow + gl * 16;
+            // this lane's chunk: its destination buffer and element offset, and the bytes
+            // between consecutive tokens there
             unsigned dl = desc[0];
-    #pragma unroll
+#pragma unroll
             for (int g = 1; g < 16; ++g) dl = gl == g ? desc[g] : dl;
             const unsigned kind_l = dl >> 30;
             char* const base_l = static_cast<char*>(kind_l == 0 ? p.ff : kind_l == 1 ? p.q : kind_l == 2 ? p.k : p.v) +
                                  (size_t)(dl & 0x3fffffffu) * 2;
+            const unsigned stride_l = kind_l == 0 ? (unsigned)(2 * ff_dim) : (unsigned)(2 * hd);
+            char* const row0_l = base_l + r0 * stride_l;
             const bool col_ok = fw + 8 * gl < N;
-            // the wave's tokens usually lie in one slab: then the slab index is wave-uniform
+            // the wave's tokens usually lie in one slab: then a token's offset is linear in it
             const int bi_first = tw0 / S;
             const bool one_slab = (tw0 + WT - 1 < M ? tw0 + WT - 1 : M - 1) / S == bi_first;
             auto token_off = [&](int t) __attribute__((always_inline)) {
-                const int bi = one_slab ? bi_first : t / S;
+                const int bi = t / S;
                 const int s = t - bi * S;
                 return kind_l == 0 ? (unsigned)t * (unsigned)(2 * ff_dim)
                                    : (unsigned)(((int64_t)bi * slab_elems + (int64_t)s * hd) * 2);
@@ -544,22 +572,22 @@ fused_proj_fast_kernel(KernelArgs p) {
 
             // cos/sin of this lane's token at its 4 columns of each first-half group of a head;
             // every head of the wave uses the same ones -- all at once for head sizes up to 64,
-            // in two halves for 128 (registers). Every token block is finished and rounded
-            // before the first store: a load issued after a store would wait for it too (the
-            // vector memory counter counts in order).
+            // in two halves for 128 (registers). Those of the next token block are loaded
+            // before this block's stores: a load issued after a store would wait for it too
+            // (the vector memory counter counts in order).
             f32x4 rc[NRB], rsn[NRB];
             auto load_rope = [&](int j, int r0) __attribute__((always_inline)) {
                 const int t = tw0 + 32 * j + (lane_e & 31);
                 const int tc = t < M ? t : 0;
                 const int s = tc - (tc / S) * S;
                 const unsigned rp_off = (unsigned)((s * (DG * 8) + 4 * (lane_e >> 5)) * 4);
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < NRB; ++r) {
                     rc[r] = f32x4{};
                     rsn[r] = f32x4{};
                 }
                 if (wave_rope) {
-    #pragma unroll
+#pragma unroll
                     for (int r = 0; r < NRB; ++r) {
                         const char* const c = reinterpret_cast<const char*>(rope_cos + 8 * (r0 + r)) + rp_off;
                         const char* const sn = reinterpret_cast<const char*>(rope_sin + 8 * (r0 + r)) + rp_off;
@@ -568,71 +596,79 @@ fused_proj_fast_kernel(KernelArgs p) {
                     }
                 }
             };
-            u32x2 pk[TJ][NG];   // the outputs rounded to bf16: half the registers of acc
-    #pragma unroll
+            load_rope(0, 0);
+#pragma unroll
             for (int j = 0; j < TJ; ++j) {
-                // (a fence per token block: the next block's loads hoisted here would raise the
-                // register peak)
-                __builtin_amdgcn_sched_barrier(0);
-                load_rope(j, 0);
-    #pragma unroll
+                // every group's outputs rounded to bf16 (each branch packs its own results:
+                // results written back into acc under these branches would cost a register
+                // copy per value where the branches join)
+                u32x2 pk[NG];
+#pragma unroll
+                for (int G = 0; G < NG; ++G) pk[G] = u32x2{0u, 0u};
+#pragma unroll
                 for (int G = 0; G < NG; ++G) {
-                    if (fw + 8 * G >= N) continue;   // ragged last column tile
+                    if (fw + 8 * G >= N) continue;   // ragged last column tile (not stored)
                     const unsigned kind = desc[G] >> 30;
+                    float y[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) y[u] = acc[G >> 2][j][4 * (G & 3) + u];
                     if (kind == 0) {
                         if (act == 1) {
-    #pragma unroll
-                            for (int u = 0; u < 4; ++u)
-                                acc[G >> 2][j][4 * (G & 3) + u] = gelu_erf_fast(acc[G >> 2][j][4 * (G & 3) + u]);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) y[u] = gelu_erf_poly(y[u]);
                         }
+                        pk[G] = pack4_bf16(y);
                         continue;
                     }
                     if (DG > 0 && kind != 3) {
                         // Heads start on head_dim boundaries of the wave's columns, so the
                         // group's place in its head is a compile-time constant. A first-half
-                        // group is rotated together with its partner DG groups on.
+                        // group is rotated together with its partner DG groups on, which it
+                        // also packs.
                         const int jh8 = (8 * G) % HD;
                         if (jh8 >= HALF || G + DG >= NG) continue;
                         const int G2 = (G + DG < NG) ? G + DG : G;   // constant after unrolling
                         if (NR > NRB && jh8 == 8 * NRB) load_rope(j, NRB);   // second half (head size 128)
                         const f32x4 c = rc[(jh8 / 8) % NRB], sn = rsn[(jh8 / 8) % NRB];
-    #pragma unroll
+                        float o1[4], o2[4];
+#pragma unroll
                         for (int u = 0; u < 4; ++u) {
-                            const float y1 = acc[G >> 2][j][4 * (G & 3) + u];
                             const float y2 = acc[G2 >> 2][j][4 * (G2 & 3) + u];
-                            acc[G >> 2][j][4 * (G & 3) + u] = y1 * c[u] - y2 * sn[u];
-                            acc[G2 >> 2][j][4 * (G2 & 3) + u] = y2 * c[u] + y1 * sn[u];
+                            o1[u] = y[u] * c[u] - y2 * sn[u];
+                            o2[u] = y2 * c[u] + y[u] * sn[u];
                         }
+                        pk[G] = pack4_bf16(o1);
+                        pk[G2] = pack4_bf16(o2);
+                        continue;
                     }
+                    pk[G] = pack4_bf16(y);
                 }
-    #pragma unroll
-                for (int G = 0; G < NG; ++G) {
-                    bf16x4 v;
-    #pragma unroll
-                    for (int u = 0; u < 4; ++u) v[u] = (__bf16)acc[G >> 2][j][4 * (G & 3) + u];
-                    pk[j][G] = __builtin_bit_cast(u32x2, v);
-                }
-            }
-    #pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-    #pragma unroll
+                // the next block's cos/sin, ahead of this block's stores
+                if (j + 1 < TJ) load_rope(j + 1, 0);
+#pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     // the lanes whose token is in this half of the token block write its rows
                     if (((lane_e & 31) >> 4) == h) {
-                        const int t = lane_e & 15;
-    #pragma unroll
-                        for (int G = 0; G < NG; ++G) {
-                            const unsigned a = wave_lds + t * 256 + ((G ^ t) * 16) + (lane_e >> 5) * 8;
-                            *(__attribute__((address_space(3))) u32x2*)(size_t)a = pk[j][G];
-                        }
+#pragma unroll
+                        for (int G = 0; G < NG; ++G)
+                            *(__attribute__((address_space(3))) u32x2*)(size_t)(wr_lds + G * 16) = pk[G];
                     }
-    #pragma unroll
+                    const int t0 = tw0 + 32 * j + 16 * h;   // the half block's first token
+                    const int rows = M - t0;                 // its rows that exist
+                    // in one slab: row r of this lane's chunk at row0_l + u + (r - r0) * stride_l
+                    const unsigned u = kind_l == 0 ? (unsigned)t0 * (unsigned)(2 * ff_dim)
+                                                   : (unsigned)(((int64_t)bi_first * slab_elems +
+                                                                 (int64_t)(t0 - bi_first * S) * hd) * 2);
+#pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
-                        const int r = (lane_e >> 4) + 4 * rr;   // token row of the half block
-                        const unsigned a = wave_lds + r * 256 + ((gl ^ r) * 16);
-                        const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(size_t)a;
-                        const int t = tw0 + 32 * j + 16 * h + r;
-                        if (t < M && col_ok) *reinterpret_cast<u32x4*>(base_l + token_off(t)) = v;
+                        const int r = r0 + 4 * rr;   // token row of the half block
+                        const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(size_t)(
+                            rd_lds + rr * 4 * kRestageRow);
+                        if (r < rows && col_ok) {
+                            char* const dst = one_slab ? row0_l + (u + (unsigned)(4 * rr) * stride_l)
+                                                       : base_l + token_off(t0 + r);
+                            *reinterpret_cast<u32x4*>(dst) = v;
+                        }
                     }
                 }
             }
@@ -641,7 +677,7 @@ fused_proj_fast_kernel(KernelArgs p) {
             // lane's token: its ff row, its q/k/v row of head 0, its cos/sin row.
             unsigned ff_off[TJ], hv_off[TJ], rp_off[TJ];
             bool tv[TJ];
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < TJ; ++j) {
                 const int t = tw0 + 32 * j + (lane & 31);
                 tv[j] = t < M;
@@ -652,7 +688,7 @@ fused_proj_fast_kernel(KernelArgs p) {
                 rp_off[j] = (unsigned)((s * (DG * 8) + 4 * hl) * 4);
             }
             char* const out_ff = static_cast<char*>(p.ff);
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < TJ; ++j) {
                 // cos/sin of this lane's token at its 4 columns of each first-half group of a
                 // head; every head of the wave uses the same ones. Loaded before this token
@@ -660,13 +696,13 @@ fused_proj_fast_kernel(KernelArgs p) {
                 // all at once for head sizes up to 64, in two halves for 128 (registers).
                 f32x4 rc[NRB], rsn[NRB];
                 auto load_rope = [&](int r0) __attribute__((always_inline)) {
-    #pragma unroll
+#pragma unroll
                     for (int r = 0; r < NRB; ++r) {
                         rc[r] = f32x4{};
                         rsn[r] = f32x4{};
                     }
                     if (wave_rope) {
-    #pragma unroll
+#pragma unroll
                         for (int r = 0; r < NRB; ++r) {
                             const char* const c = reinterpret_cast<const char*>(rope_cos + 8 * (r0 + r)) + rp_off[j];
                             const char* const sn = reinterpret_cast<const char*>(rope_sin + 8 * (r0 + r)) + rp_off[j];
@@ -676,18 +712,18 @@ fused_proj_fast_kernel(KernelArgs p) {
                     }
                 };
                 load_rope(0);
-    #pragma unroll
+#pragma unroll
                 for (int G = 0; G < NG; ++G) {
                     if (fw + 8 * G >= N) continue;   // ragged last column tile
                     const unsigned d = desc[G];
                     const unsigned kind = d >> 30, off = d & 0x3fffffffu;
                     float y[4];
-    #pragma unroll
+#pragma unroll
                     for (int u = 0; u < 4; ++u) y[u] = acc[G >> 2][j][4 * (G & 3) + u];
                     if (kind == 0) {
                         if (act == 1) {
-    #pragma unroll
-                            for (int u = 0; u < 4; ++u) y[u] = gelu_erf_fast(y[u]);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) y[u] = gelu_erf_poly(y[u]);
                         }
                         if (tv[j]) store4_bf16(out_ff + (size_t)off * 2 + ff_off[j], y);
                         continue;
@@ -704,7 +740,7 @@ fused_proj_fast_kernel(KernelArgs p) {
                         if (NR > NRB && jh8 == 8 * NRB) load_rope(NRB);   // second half (head size 128)
                         const f32x4 c = rc[(jh8 / 8) % NRB], sn = rsn[(jh8 / 8) % NRB];
                         float o1[4], o2[4];
-    #pragma unroll
+#pragma unroll
                         for (int u = 0; u < 4; ++u) {
                             const float y2 = acc[G2 >> 2][j][4 * (G2 & 3) + u];
                             o1[u] = y[u] * c[u] - y2 * sn[u];
@@ -732,7 +768,7 @@ fused_proj_fast_kernel(KernelArgs p) {
 template <bool X_TL, bool W_FC, int DG, class T>
 hipError_t launch_fast_one(const KernelArgs& a, int grid, hipStream_t stream) {
     const dim3 block(64 * T::NWF * T::NWT);
-    if (a.K > 0 && a.K % (kBK * kStages) == 0)
+    if (a.K > 0 && a.K % (kBK * T::STAGES) == 0)
         hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, false, T>), dim3(grid), block, 0, stream, a);
     else
         hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, true, T>), dim3(grid), block, 0, stream, a);
@@ -787,7 +823,7 @@ bool fast_addressable(int64_t M, int64_t S, int64_t ff_dim, int64_t qw) {
     return M * ff_dim * 2 < lim32 && M * qw * 2 < lim32 && ff_dim < lim30 && S * qw < lim30;
 }
 
-int fast_k_multiple() { return kBK * kStages; }
+int fast_k_multiple() { return kBK * LargeTile::STAGES; }
 
 // Entries for whole large column tiles, which also covers whole small ones.
 int64_t fast_col_desc_entries(int64_t F) { return (F + LargeTile::BF - 1) / LargeTile::BF * (LargeTile::BF / 8); }
@@ -816,6 +852,8 @@ hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, const T
     if (pl.bk != kBK || pl.grid <= 0 || pl.grid % 8) return hipErrorInvalidValue;
     if (pl.bm == LargeTile::BT && pl.bn == LargeTile::BF)
         return dispatch_fast_rope<LargeTile>(dg, x_tokens_last, w_fc, a, pl.grid, stream);
+    if (pl.bm == MidTile::BT && pl.bn == MidTile::BF)
+        return dispatch_fast_rope<MidTile>(dg, x_tokens_last, w_fc, a, pl.grid, stream);
     if (pl.bm == SmallTile::BT && pl.bn == SmallTile::BF)
         return dispatch_fast_rope<SmallTile>(dg, x_tokens_last, w_fc, a, pl.grid, stream);
     return hipErrorInvalidValue;

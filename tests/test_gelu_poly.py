@@ -1,0 +1,55 @@
+"""The polynomial GELU of the fast kernel (gelu_erf_poly in device_common.h), checked on
+the CPU: its coefficients are read from the header and its instruction sequence is
+evaluated in float32 against exact-erf GELU (scipy's erf in float64). This pins the
+formula; the GPU parity tests pin its execution."""
+import os
+import re
+
+import numpy as np
+from scipy.special import erf
+
+from ff_input_projection_amd import build as fpbuild
+
+
+def _coefficients():
+    src = open(os.path.join(fpbuild.CSRC, "device_common.h")).read()
+    body = src[src.index("float gelu_erf_poly(float y)"):]
+    body = body[: body.index("\n}\n")]
+    first = re.search(r"float p = ([-+0-9.e]+)f;", body).group(1)
+    rest = re.findall(r"p = fmaf\(p, a, ([-+0-9.e]+)f\);", body)
+    clamp = float(re.search(r"fminf\(fabsf\(y\), ([0-9.]+)f\)", body).group(1))
+    return [np.float32(first)] + [np.float32(c) for c in rest], np.float32(clamp)
+
+
+def _gelu_poly_f32(y, coef, clamp):
+    y = np.asarray(y, np.float32)
+    a = np.minimum(np.abs(y), clamp)
+    p = np.full_like(a, coef[0])
+    for c in coef[1:]:
+        # fmaf: one rounding of the exact p * a + c
+        p = (p.astype(np.float64) * a.astype(np.float64) + np.float64(c)).astype(np.float32)
+    e = np.exp2(p.astype(np.float64)).astype(np.float32)
+    out = -a.astype(np.float64) * e.astype(np.float64) + np.maximum(y, np.float32(0)).astype(np.float64)
+    return out.astype(np.float32)
+
+
+def _gelu_exact(y):
+    y = np.asarray(y, np.float64)
+    return 0.5 * y * (1.0 + erf(y / np.sqrt(2.0)))
+
+
+def test_polynomial_gelu_within_1e6_of_exact_erf_gelu():
+    coef, clamp = _coefficients()
+    assert len(coef) == 8 and clamp == 6.0
+    y = np.concatenate([np.linspace(-12, 12, 1_200_001), [-1e4, -50.0, 0.0, 50.0, 1e4]]).astype(np.float32)
+    err = np.abs(_gelu_poly_f32(y, coef, clamp).astype(np.float64) - _gelu_exact(y))
+    assert err.max() < 1e-6, err.max()
+
+
+def test_polynomial_gelu_special_values():
+    coef, clamp = _coefficients()
+    y = np.array([0.0, 1.0, -1.0, 3.0, -3.0], np.float32)
+    got = _gelu_poly_f32(y, coef, clamp).astype(np.float64)
+    # gelu(0) = 0; gelu(y) - gelu(-y) = y (Phi(y) + Phi(-y) = 1)
+    assert abs(got[0]) < 1e-9
+    assert abs((got[1] - got[2]) - 1.0) < 2e-6 and abs((got[3] - got[4]) - 3.0) < 2e-6

@@ -69,6 +69,12 @@ SMALL = [
     # tile), RoPE hd 64, GELU
     with_shape(WORKLOADS["walrus_bf16"], "cf_small_tiles_rope", x_shape=(2, 72, 8, 16, 1), ff_dim=64,
                n_heads=2, head_dim=64, seed=110),
+    # small tiles whose waves straddle slabs (48 and 80 tokens per slab): the per-token
+    # store offsets take the general path
+    with_shape(WORKLOADS["walrus_bf16"], "cf_small_tiles_straddle", x_shape=(8, 64, 6, 8, 1), ff_dim=64,
+               n_heads=2, head_dim=64, seed=111),
+    with_shape(WORKLOADS["bert_qkv_bf16"], "tl_small_tiles_straddle", x_shape=(8, 80, 64), ff_dim=0, n_heads=3,
+               head_dim=64, rope=True, w_layout="fc", seed=112),
     # fp32, token-major, [F,C], RoPE hd 8, GELU
     with_shape(WORKLOADS["tiny_f32"], "f32_tl_fc", layout="tokens_last", x_shape=(3, 50, 36), ff_dim=16,
                n_heads=3, head_dim=8, w_layout="fc", seed=106),
