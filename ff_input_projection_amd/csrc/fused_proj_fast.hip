@@ -307,26 +307,21 @@ __device__ __forceinline__ bool block_tile(int k, int tiles_t, int tiles_f, int 
 }
 
 // Tile shapes compiled for the fast kernel, BF output columns x BT tokens per workgroup
-// with NWF x NWT waves; K steps of BK through STAGES LDS stages for both. The loads run
-// three K steps ahead, which three stages carry; a fourth one is idle at the end of a
-// tile, where RESTAGE epilogues use it.
+// with NWF x NWT waves (WPE per SIMD); K steps of BK through STAGES LDS stages for both.
+// The loads run three K steps ahead, which three stages carry; a fourth one is idle at
+// the end of a tile, where RESTAGE epilogues use it.
 //  - large: 256 x 256 by 2 x 4 waves of 128 x 64, one workgroup per CU (130 KB of LDS);
-//  - mid: 256 x 128 by 2 x 2 waves of 128 x 64, two workgroups per CU (72 KB each), which
-//    run out of step: one's epilogue overlaps the other's MFMAs;
 //  - small: 128 x 128 by 1 x 4 waves of 128 x 32, two workgroups per CU (65 KB each), for
 //    problems with fewer large tiles than CUs (short K, few tokens): four times the tiles.
 struct LargeTile {
-    static constexpr int BF = 256, BT = 256, NWF = 2, NWT = 4, PER_CU = 1, STAGES = 4;
+    static constexpr int BF = 256, BT = 256, NWF = 2, NWT = 4, PER_CU = 1, STAGES = 4, WPE = 2;
     static constexpr bool RESTAGE = true;
-};
-struct MidTile {
-    static constexpr int BF = 256, BT = 128, NWF = 2, NWT = 2, PER_CU = 2, STAGES = 3;
-    static constexpr bool RESTAGE = false;
 };
 struct SmallTile {
-    static constexpr int BF = 128, BT = 128, NWF = 1, NWT = 4, PER_CU = 2, STAGES = 4;
+    static constexpr int BF = 128, BT = 128, NWF = 1, NWT = 4, PER_CU = 2, STAGES = 4, WPE = 2;
     static constexpr bool RESTAGE = true;
 };
+
 constexpr int kBK = 32, kPrefetch = 3;
 // Restaged epilogue rows: 16 tokens x (128 bf16 columns + 16 bytes of padding).
 constexpr int kRestageRows = 16, kRestageRow = 272;
@@ -335,12 +330,13 @@ constexpr int kRestageRows = 16, kRestageRow = 272;
 // DG: RoPE partner distance in 8-column groups (hd/16), 0 = no RoPE. TAILK: K is not a
 // multiple of T::STAGES * BK (some K steps are partial or padding).
 template <bool X_TL, bool W_FC, int DG, bool TAILK, class T>
-__global__ __launch_bounds__(64 * T::NWF * T::NWT, T::PER_CU) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+__global__ __launch_bounds__(64 * T::NWF * T::NWT, T::PER_CU) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE))) void
 fused_proj_fast_kernel(KernelArgs p) {
     constexpr int BF = T::BF, BT = T::BT, BK = kBK, STAGES = T::STAGES, PF = kPrefetch, kNWT = T::NWT;
     // restaged epilogues: each wave owns kRestageRows rows of kRestageRow bytes in the idle
     // last stage and the spare bytes after it
-    constexpr int PAD = T::RESTAGE ? T::NWF * T::NWT / 2 * (kRestageRows * kRestageRow - 4096) : 0;
+    constexpr int RGN_ALL = T::NWF * T::NWT / 2 * kRestageRows * kRestageRow, W_STAGE = BF * kBK * 2;
+    constexpr int PAD = T::RESTAGE && RGN_ALL > W_STAGE ? RGN_ALL - W_STAGE : 0;
     using C = FastCfg<X_TL, W_FC, BF, BT, T::NWF, kNWT, BK, STAGES, PAD>;
     using Pipe = FastPipe<C, X_TL, W_FC, BK, TAILK>;
     using Ops = typename Pipe::Ops;
@@ -531,8 +527,7 @@ fused_proj_fast_kernel(KernelArgs p) {
             // writes and the 16-byte chunk reads free of bank conflicts) in the stage no K step
             // uses until the next tile's first barrier and the spare bytes after it. Every LDS
             // address is a per-lane base plus a constant.
-            static_assert(C::W_BYTES == C::X_BYTES &&
-                              C::W_BYTES + PAD == C::NW / 2 * kRestageRows * kRestageRow,
+            static_assert(C::W_BYTES == C::X_BYTES && C::W_BYTES + PAD >= C::NW / 2 * kRestageRows * kRestageRow,
                           "restage regions");
             constexpr int RGN = kRestageRows * kRestageRow;
             const unsigned wave_lds = wave < C::NW / 2 ? pp.lds0 + (STAGES - 1) * C::W_BYTES + wave * RGN
@@ -806,13 +801,13 @@ TilePlan fast_plan(int64_t M, int64_t F, int num_cus) {
     const int64_t large = ((M + LargeTile::BT - 1) / LargeTile::BT) * ((F + LargeTile::BF - 1) / LargeTile::BF);
     if (large >= cus) {
         // persistent: one workgroup per CU walks the large tiles
-        TilePlan t{LargeTile::BT, LargeTile::BF, kBK, 8, 0};
+        TilePlan t{LargeTile::BT, LargeTile::BF, kBK, 8, 0, kFastLarge};
         t.grid = cus;
         t.grid = (t.grid + 7) / 8 * 8;   // a multiple of the 8 XCDs
         return t;
     }
     // too few large tiles to fill the CUs: small tiles, one per workgroup
-    TilePlan t{SmallTile::BT, SmallTile::BF, kBK, 8, 0};
+    TilePlan t{SmallTile::BT, SmallTile::BF, kBK, 8, 0, kFastSmall};
     const int64_t small = ((M + SmallTile::BT - 1) / SmallTile::BT) * ((F + SmallTile::BF - 1) / SmallTile::BF);
     t.grid = (int)((small + 7) / 8 * 8);
     return t;
@@ -850,12 +845,16 @@ void fast_col_desc(int64_t S, int64_t ff_dim, int64_t n_heads, int64_t head_dim,
 hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, const TilePlan& pl, const KernelArgs& a,
                                   hipStream_t stream) {
     if (pl.bk != kBK || pl.grid <= 0 || pl.grid % 8) return hipErrorInvalidValue;
-    if (pl.bm == LargeTile::BT && pl.bn == LargeTile::BF)
-        return dispatch_fast_rope<LargeTile>(dg, x_tokens_last, w_fc, a, pl.grid, stream);
-    if (pl.bm == MidTile::BT && pl.bn == MidTile::BF)
-        return dispatch_fast_rope<MidTile>(dg, x_tokens_last, w_fc, a, pl.grid, stream);
-    if (pl.bm == SmallTile::BT && pl.bn == SmallTile::BF)
-        return dispatch_fast_rope<SmallTile>(dg, x_tokens_last, w_fc, a, pl.grid, stream);
+    auto is = [&](auto t) { return pl.bm == decltype(t)::BT && pl.bn == decltype(t)::BF; };
+    switch (pl.shape) {
+        case kFastLarge:
+            if (is(LargeTile{})) return dispatch_fast_rope<LargeTile>(dg, x_tokens_last, w_fc, a, pl.grid, stream);
+            break;
+        case kFastSmall:
+            if (is(SmallTile{})) return dispatch_fast_rope<SmallTile>(dg, x_tokens_last, w_fc, a, pl.grid, stream);
+            break;
+        default: break;
+    }
     return hipErrorInvalidValue;
 }
 

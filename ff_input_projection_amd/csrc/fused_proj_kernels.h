@@ -44,7 +44,11 @@ struct TilePlan {
     int bm, bn, bk;
     int group_m;         // tiles along M that share a column sweep (L2 reuse)
     int grid;            // workgroups launched (0: one per tile)
+    int shape = 0;       // fast kernel: which compiled tile shape (FastShape)
 };
+
+// Tile shapes of the fast kernel.
+enum FastShape { kFastLarge = 0, kFastSmall = 1 };
 
 // Kernel variants: storage type x activation layout x weight layout.
 enum class DType { BF16 = 0, F32 = 1 };
