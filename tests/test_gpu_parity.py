@@ -115,6 +115,29 @@ def test_fast_kernel_on_padded_or_ragged_tiling(monkeypatch):
     _check(wl, inp, outs, sample_tokens(wl, 384, seed=1), wl.name)
 
 
+LARGE_FC = [
+    # [F,C] weights (nn.Linear layout) on the large tiles, both x layouts: 8192 tokens,
+    # C = 256, F = 1024 + 3 * 512 = 2560 (320 tiles of 256 x 256), RoPE hd 64, GELU
+    with_shape(WORKLOADS["bert_qkv_bf16"], "tl_fc_large_tiles", x_shape=(16, 512, 256), ff_dim=1024,
+               ff_act="gelu", n_heads=8, head_dim=64, rope=True, w_layout="fc", pos_offset=3, seed=113),
+    with_shape(WORKLOADS["walrus_bf16"], "cf_fc_large_tiles", x_shape=(8, 256, 32, 32, 1), ff_dim=1024,
+               n_heads=8, head_dim=64, w_layout="fc", seed=114),
+]
+
+
+@pytest.mark.parametrize("wl", LARGE_FC, ids=[w.name for w in LARGE_FC])
+def test_large_tiles_with_fc_weights(wl):
+    """The fast kernel's large-tile instantiations that read W as [F,C] (K-contiguous
+    rows): none of the named workloads uses them."""
+    print(f"[case] large tiles, [F,C] weight: {wl.name} x={wl.x_shape}", flush=True)
+    inp = make_inputs(wl)
+    proj, outs = run_gpu(wl, inp, DEV)
+    desc = proj.describe()
+    print(f"[plan] {desc}", flush=True)
+    assert "fused_proj_fast_kernel" in desc and "tile=256x256" in desc, desc
+    _check(wl, inp, outs, sample_tokens(wl, 384, seed=2), wl.name)
+
+
 def test_strided_views_channel_slice_and_row_stride(kernel_choice):
     """x as a view: a channel slice of a wider channels-first tensor, and a token-major
     view whose row stride exceeds C. No copy is made; results match the oracle."""
