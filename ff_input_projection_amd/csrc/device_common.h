@@ -107,19 +107,19 @@ __device__ __forceinline__ float gelu_erf_fast(float y) {
 
 // The same GELU with one exp2 and no reciprocal. With a = |y| and q(a) = Phi(-a) =
 // erfc(a / sqrt 2) / 2, GELU(y) = max(y, 0) - |y| q(|y|); log2 q is smooth on [0, 6]
-// and is taken as one degree-7 polynomial in a (near-minimax fit from
-// gelu_poly_fit.py; absolute error of the whole GELU under 1e-6 in fp32). a is clamped
+// and is taken as one degree-6 polynomial in a (near-minimax fit from
+// gelu_poly_fit.py; absolute error of the whole GELU under 1e-5 in fp32, far below the
+// bf16 rounding of the outputs this serves). a is clamped
 // to 6 in both places it is used: past 6, |y| q(|y|) < 1e-8 and 6 q(6) stands for it.
 __device__ __forceinline__ float gelu_erf_poly(float y) {
     const float a = fminf(fabsf(y), 6.0f);
-    float p = -1.8348863e-06f;
-    p = fmaf(p, a, 6.159977e-05f);
-    p = fmaf(p, a, -0.00093053613f);
-    p = fmaf(p, a, 0.008507933f);
-    p = fmaf(p, a, -0.05396015f);
-    p = fmaf(p, a, -0.45846432f);
-    p = fmaf(p, a, -1.1512511f);
-    p = fmaf(p, a, -0.9999953f);
+    float p = 2.2990056e-05f;
+    p = fmaf(p, a, -0.00061110023f);
+    p = fmaf(p, a, 0.0071955691f);
+    p = fmaf(p, a, -0.051185358f);
+    p = fmaf(p, a, -0.46127188f);
+    p = fmaf(p, a, -1.1501743f);
+    p = fmaf(p, a, -1.0000647f);
     return fmaf(-a, __builtin_amdgcn_exp2f(p), fmaxf(y, 0.0f));
 }
 

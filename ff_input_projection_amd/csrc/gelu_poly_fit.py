@@ -7,7 +7,7 @@ q(a) = Phi(-a) = erfc(a / sqrt(2)) / 2 for a = |y| >= 0 gives
     gelu(y) = max(y, 0) - |y| * q(|y|),
 
 and log2 q(a) is smooth on [0, A] (it tends to -a^2 / (2 ln 2) minus a slowly growing
-logarithm), so it is approximated by one polynomial P of degree 7 in a. The kernel
+logarithm), so it is approximated by one polynomial P of degree 6 in a. The kernel
 clamps a to A = 6 in both places it is used (past 6, |y| * q(|y|) < 1e-8, and
 6 * q(6) stands for it).
 
@@ -19,7 +19,7 @@ import numpy as np
 from scipy.special import erf, erfc
 
 A = 6.0
-DEG = 7
+DEG = 6
 
 
 def fit(deg=DEG, a_max=A, nodes=4000, iters=40):
@@ -52,7 +52,7 @@ def gelu_exact(y):
 
 if __name__ == "__main__":
     c = fit()
-    print("coefficients (a^7 .. a^0):")
+    print(f"coefficients (a^{DEG} .. a^0):")
     for ci in c:
         print(f"    {float(np.float32(ci))!r}f")
     y = np.linspace(-12, 12, 2_000_001)

@@ -38,12 +38,12 @@ def _gelu_exact(y):
     return 0.5 * y * (1.0 + erf(y / np.sqrt(2.0)))
 
 
-def test_polynomial_gelu_within_1e6_of_exact_erf_gelu():
+def test_polynomial_gelu_within_1e5_of_exact_erf_gelu():
     coef, clamp = _coefficients()
-    assert len(coef) == 8 and clamp == 6.0
+    assert len(coef) == 7 and clamp == 6.0
     y = np.concatenate([np.linspace(-12, 12, 1_200_001), [-1e4, -50.0, 0.0, 50.0, 1e4]]).astype(np.float32)
     err = np.abs(_gelu_poly_f32(y, coef, clamp).astype(np.float64) - _gelu_exact(y))
-    assert err.max() < 1e-6, err.max()
+    assert err.max() < 1e-5, err.max()
 
 
 def test_polynomial_gelu_special_values():
@@ -52,4 +52,4 @@ def test_polynomial_gelu_special_values():
     got = _gelu_poly_f32(y, coef, clamp).astype(np.float64)
     # gelu(0) = 0; gelu(y) - gelu(-y) = y (Phi(y) + Phi(-y) = 1)
     assert abs(got[0]) < 1e-9
-    assert abs((got[1] - got[2]) - 1.0) < 2e-6 and abs((got[3] - got[4]) - 3.0) < 2e-6
+    assert abs((got[1] - got[2]) - 1.0) < 2e-5 and abs((got[3] - got[4]) - 3.0) < 2e-5
