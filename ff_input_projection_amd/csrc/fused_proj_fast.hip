@@ -315,11 +315,14 @@ __device__ __forceinline__ bool block_tile(int k, int tiles_t, int tiles_f, int 
 //    problems with fewer large tiles than CUs (short K, few tokens): four times the tiles.
 struct LargeTile {
     static constexpr int BF = 256, BT = 256, NWF = 2, NWT = 4, PER_CU = 1, STAGES = 4, WPE = 2;
-    static constexpr bool RESTAGE = true;
+    static constexpr bool RESTAGE = true, SINGLE = false;
 };
+// SINGLE: every workgroup gets at most one tile (the host launches one per tile), so the
+// K steps are not padded to a multiple of the stage count and no loads run ahead into a
+// next tile
 struct SmallTile {
     static constexpr int BF = 128, BT = 128, NWF = 1, NWT = 4, PER_CU = 2, STAGES = 4, WPE = 2;
-    static constexpr bool RESTAGE = true;
+    static constexpr bool RESTAGE = true, SINGLE = true;
 };
 
 constexpr int kBK = 32, kPrefetch = 3;
@@ -404,8 +407,9 @@ fused_proj_fast_kernel(KernelArgs p) {
 
     // K steps per tile, padded to a multiple of the stage count so that step s of every
     // tile uses stage s mod STAGES (the padding steps read zeros). At least one group.
+    // Single-tile workgroups run just the K steps there are.
     const int KT = K > 0 ? (K + BK - 1) / BK : 1;
-    const int KTp = (KT + STAGES - 1) / STAGES * STAGES;
+    const int KTp = T::SINGLE ? KT : (KT + STAGES - 1) / STAGES * STAGES;
 
     // epilogue constants
     const int hl = lane >> 5;
@@ -474,15 +478,24 @@ fused_proj_fast_kernel(KernelArgs p) {
             constexpr int ST = decltype(stc)::value;
             constexpr int SN = (ST + 1) % STAGES, SL = (ST + PF) % STAGES;
             __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<NLOAD>();
-            __syncthreads();
             const int s_load = kt + PF;
-            const bool ahead = s_load >= KTp;   // wave-uniform
-            unsigned vo[NLOAD];
+            if constexpr (T::SINGLE) {
+                // the loads of step kt+2 were issued (by the prologue or step kt-1) only
+                // while it exists; without them wait for everything
+                if (kt + 2 < KTp || kt == 0) wait_vmcnt<NLOAD>();
+                else wait_vmcnt<0>();
+                __syncthreads();
+                if (s_load < KTp) pp.template issue<SL>(voff_cur, s_load, K, zeros);
+            } else {
+                wait_vmcnt<NLOAD>();
+                __syncthreads();
+                const bool ahead = s_load >= KTp;   // wave-uniform
+                unsigned vo[NLOAD];
 #pragma unroll
-            for (int q = 0; q < NLOAD; ++q) vo[q] = ahead ? voff_nxt[q] : voff_cur[q];
-            pp.template issue<SL>(vo, ahead ? s_load - KTp : s_load, K, zeros);
-            if (s_load == KTp) issue_bias((k_tile + 1) & 1, ntf * BF);
+                for (int q = 0; q < NLOAD; ++q) vo[q] = ahead ? voff_nxt[q] : voff_cur[q];
+                pp.template issue<SL>(vo, ahead ? s_load - KTp : s_load, K, zeros);
+                if (s_load == KTp) issue_bias((k_tile + 1) & 1, ntf * BF);
+            }
             const Ops n0 = pp.template read<SN, 0>();
             Pipe::mma(acc, c0);
             const Ops n1 = pp.template read<SN, 1>();
@@ -494,13 +507,26 @@ fused_proj_fast_kernel(KernelArgs p) {
         // (a do-while: KTp >= STAGES, and a loop the compiler thinks may run zero times
         // makes it keep a spilled copy of the initial accumulators for that path)
         int kt = 0;
-        do {
-            k_step(std::integral_constant<int, 0>{}, kt);
-            k_step(std::integral_constant<int, 1>{}, kt + 1);
-            k_step(std::integral_constant<int, 2>{}, kt + 2);
-            if constexpr (STAGES == 4) k_step(std::integral_constant<int, 3>{}, kt + 3);
-            kt += STAGES;
-        } while (kt < KTp);
+        if constexpr (T::SINGLE) {
+            static_assert(STAGES == 4, "the remainder below is written for four stages");
+            for (; kt + STAGES <= KTp; kt += STAGES) {
+                k_step(std::integral_constant<int, 0>{}, kt);
+                k_step(std::integral_constant<int, 1>{}, kt + 1);
+                k_step(std::integral_constant<int, 2>{}, kt + 2);
+                k_step(std::integral_constant<int, 3>{}, kt + 3);
+            }
+            if (kt < KTp) k_step(std::integral_constant<int, 0>{}, kt);
+            if (kt + 1 < KTp) k_step(std::integral_constant<int, 1>{}, kt + 1);
+            if (kt + 2 < KTp) k_step(std::integral_constant<int, 2>{}, kt + 2);
+        } else {
+            do {
+                k_step(std::integral_constant<int, 0>{}, kt);
+                k_step(std::integral_constant<int, 1>{}, kt + 1);
+                k_step(std::integral_constant<int, 2>{}, kt + 2);
+                if constexpr (STAGES == 4) k_step(std::integral_constant<int, 3>{}, kt + 3);
+                kt += STAGES;
+            } while (kt < KTp);
+        }
 
         // ---- epilogue. acc[a][j][e] (bias included): column f = 32a + 8(e/4) + 4(lane/32)
         // + e%4, token 32j + lane%32 (both relative to the wave tile). Outputs never overlap
@@ -851,6 +877,9 @@ hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, const T
             if (is(LargeTile{})) return dispatch_fast_rope<LargeTile>(dg, x_tokens_last, w_fc, a, pl.grid, stream);
             break;
         case kFastSmall:
+            // one tile per workgroup at most: each XCD's share of the tiles fits its workgroups
+            static_assert(SmallTile::SINGLE, "small tiles are planned one per workgroup");
+            if ((int64_t)a.tiles_m * a.tiles_n > (int64_t)(pl.grid / 8) * 8) return hipErrorInvalidValue;
             if (is(SmallTile{})) return dispatch_fast_rope<SmallTile>(dg, x_tokens_last, w_fc, a, pl.grid, stream);
             break;
         default: break;
