@@ -189,16 +189,17 @@ __device__ __forceinline__ float fetch_f32(const float* tile, int rb, int kk, in
 using dev::gelu_erf;
 using dev::tile_coords;
 
+// 16-byte output stores, non-temporal: every output is written once and not read here.
 template <typename T> __device__ __forceinline__ void store16(T* dst, const float* y);
 template <> __device__ __forceinline__ void store16<__bf16>(__bf16* dst, const float* y) {
     typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
     bf16x8_t o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (__bf16)y[e];  // round to nearest even
-    *reinterpret_cast<u32x4*>(dst) = __builtin_bit_cast(u32x4, o);
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, o), reinterpret_cast<u32x4*>(dst));
 }
 template <> __device__ __forceinline__ void store16<float>(float* dst, const float* y) {
-    *reinterpret_cast<f32x4*>(dst) = f32x4{y[0], y[1], y[2], y[3]};
+    __builtin_nontemporal_store(f32x4{y[0], y[1], y[2], y[3]}, reinterpret_cast<f32x4*>(dst));
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v) { return (float)v; }

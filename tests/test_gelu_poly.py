@@ -17,7 +17,9 @@ def _coefficients():
     body = body[: body.index("\n}\n")]
     first = re.search(r"float p = ([-+0-9.e]+)f;", body).group(1)
     rest = re.findall(r"p = fmaf\(p, a, ([-+0-9.e]+)f\);", body)
-    clamp = float(re.search(r"fminf\(fabsf\(y\), ([0-9.]+)f\)", body).group(1))
+    clamp = float(re.search(r"fmed3f\(fabsf\(y\), 0\.0f, ([0-9.]+)f\)", body).group(1))
+    # the positive part max(y, 0) is a med3 against FLT_MAX
+    assert re.search(r"fmed3f\(y, 0\.0f, 3\.40282347e\+38f\)", body)
     return [np.float32(first)] + [np.float32(c) for c in rest], np.float32(clamp)
 
 
@@ -29,7 +31,8 @@ def _gelu_poly_f32(y, coef, clamp):
         # fmaf: one rounding of the exact p * a + c
         p = (p.astype(np.float64) * a.astype(np.float64) + np.float64(c)).astype(np.float32)
     e = np.exp2(p.astype(np.float64)).astype(np.float32)
-    out = -a.astype(np.float64) * e.astype(np.float64) + np.maximum(y, np.float32(0)).astype(np.float64)
+    pos = np.minimum(np.maximum(y, np.float32(0)), np.finfo(np.float32).max)   # med3(y, 0, FLT_MAX)
+    out = -a.astype(np.float64) * e.astype(np.float64) + pos.astype(np.float64)
     return out.astype(np.float32)
 
 
