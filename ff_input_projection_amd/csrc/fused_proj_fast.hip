@@ -32,10 +32,11 @@
 // Schedule. Two tile shapes (see LargeTile / SmallTile below). Large: 256 x 256
 // tiles, 8 waves of 128 (f) x 64 (token) outputs, two per SIMD, one persistent
 // workgroup per CU walking a list of tiles from a contiguous, grouped range of the
-// XCD it runs on. Small (problems with fewer large tiles than CUs): 128 x 128 tiles,
-// 4 waves of 128 x 32, two workgroups per CU. The direct-load pipeline is four K
-// steps of 32 deep and runs straight on into the next tile, and the operands of
-// the next K step are read from LDS while the MFMAs of the current one run.
+// XCD it runs on; the direct-load pipeline runs three K steps of 32 ahead through four
+// stages, straight on into the next tile. Small (problems with fewer large tiles than
+// CUs): 128 x 128 tiles, 4 waves of 128 x 32, one tile per workgroup, two workgroups per
+// CU, loads four K steps ahead through five stages. Either way the operands of the next
+// K step are read from LDS while the MFMAs of the current one run.
 #include "device_common.h"
 #include "fused_proj_kernels.h"
 
@@ -311,25 +312,30 @@ __device__ __forceinline__ bool block_tile(int k, int tiles_t, int tiles_f, int 
 }
 
 // Tile shapes compiled for the fast kernel, BF output columns x BT tokens per workgroup
-// with NWF x NWT waves (WPE per SIMD); K steps of BK through STAGES LDS stages for both.
-// The loads run three K steps ahead, which three stages carry; a fourth one is idle at
-// the end of a tile, where RESTAGE epilogues use it.
-//  - large: 256 x 256 by 2 x 4 waves of 128 x 64, one workgroup per CU (130 KB of LDS);
-//  - small: 128 x 128 by 1 x 4 waves of 128 x 32, two workgroups per CU (65 KB each), for
-//    problems with fewer large tiles than CUs (short K, few tokens): four times the tiles.
+// with NWF x NWT waves (WPE per SIMD); K steps of BK through STAGES LDS stages for both,
+// loads issued PF K steps ahead.
+//  - large: 256 x 256 by 2 x 4 waves of 128 x 64, one workgroup per CU (130 KB of LDS).
+//    The loads run three K steps ahead, which three stages carry; the fourth is idle at the
+//    end of a tile, where the epilogue restages its stores, and the tile bias is
+//    double-buffered after the stages.
+//  - small: 128 x 128 by 1 x 4 waves of 128 x 32, two workgroups per CU, for problems with
+//    fewer large tiles than CUs (short K, few tokens): four times the tiles. SINGLE: every
+//    workgroup gets at most one tile (the host launches one per tile), so the K steps are
+//    not padded to a multiple of the stage count and no loads run ahead into a next tile.
+//    Such problems are bound by load latency rather than by the MFMAs, so the loads run
+//    four K steps ahead through five stages: 80 KB, exactly half the CU's LDS. The bias and
+//    the restaged stores live inside the stage area (a stage no load has reached yet, and
+//    the idle stages after the last K step).
 struct LargeTile {
-    static constexpr int BF = 256, BT = 256, NWF = 2, NWT = 4, PER_CU = 1, STAGES = 4, WPE = 2;
+    static constexpr int BF = 256, BT = 256, NWF = 2, NWT = 4, PER_CU = 1, STAGES = 4, PF = 3, WPE = 2;
     static constexpr bool RESTAGE = true, SINGLE = false;
 };
-// SINGLE: every workgroup gets at most one tile (the host launches one per tile), so the
-// K steps are not padded to a multiple of the stage count and no loads run ahead into a
-// next tile
 struct SmallTile {
-    static constexpr int BF = 128, BT = 128, NWF = 1, NWT = 4, PER_CU = 2, STAGES = 4, WPE = 2;
+    static constexpr int BF = 128, BT = 128, NWF = 1, NWT = 4, PER_CU = 2, STAGES = 5, PF = 4, WPE = 2;
     static constexpr bool RESTAGE = true, SINGLE = true;
 };
 
-constexpr int kBK = 32, kPrefetch = 3;
+constexpr int kBK = 32;
 // Restaged epilogue rows: 16 tokens x (128 bf16 columns + 16 bytes of padding).
 constexpr int kRestageRows = 16, kRestageRow = 272;
 
@@ -339,21 +345,28 @@ constexpr int kRestageRows = 16, kRestageRow = 272;
 template <bool X_TL, bool W_FC, int DG, bool TAILK, class T>
 __global__ __launch_bounds__(64 * T::NWF * T::NWT, T::PER_CU) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE))) void
 fused_proj_fast_kernel(KernelArgs p) {
-    constexpr int BF = T::BF, BT = T::BT, BK = kBK, STAGES = T::STAGES, PF = kPrefetch, kNWT = T::NWT;
-    // restaged epilogues: each wave owns kRestageRows rows of kRestageRow bytes in the idle
-    // last stage and the spare bytes after it
+    constexpr int BF = T::BF, BT = T::BT, BK = kBK, STAGES = T::STAGES, PF = T::PF, kNWT = T::NWT;
+    // restaged epilogues: each wave owns kRestageRows rows of kRestageRow bytes -- with a next
+    // tile in flight, in the idle last stage and the spare bytes after it; single-tile
+    // workgroups anywhere in the (then idle) stage area
     constexpr int RGN_ALL = T::NWF * T::NWT / 2 * kRestageRows * kRestageRow, W_STAGE = BF * kBK * 2;
-    constexpr int PAD = T::RESTAGE && RGN_ALL > W_STAGE ? RGN_ALL - W_STAGE : 0;
+    constexpr int PAD = T::RESTAGE && !T::SINGLE && RGN_ALL > W_STAGE ? RGN_ALL - W_STAGE : 0;
     using C = FastCfg<X_TL, W_FC, BF, BT, T::NWF, kNWT, BK, STAGES, PAD>;
     using Pipe = FastPipe<C, X_TL, W_FC, BK, TAILK>;
     using Ops = typename Pipe::Ops;
     constexpr int WF = C::WF, WT = C::WT, TI = C::TI, TJ = C::TJ, NG = C::NG, NLOAD = C::NLOAD;
     static_assert(C::KK == 2, "two MFMA k steps per K step");
-    static_assert(PF == 3 && (STAGES == 3 || STAGES == 4), "the wait counts below are written for three steps ahead");
-    static_assert(!T::RESTAGE || STAGES == 4, "the restaged epilogue uses the idle fourth stage");
+    static_assert(T::SINGLE || (PF == 3 && (STAGES == 3 || STAGES == 4)),
+                  "the multi-tile wait counts below are written for three steps ahead");
+    static_assert(!T::SINGLE || (PF >= 2 && PF <= 5 && STAGES == PF + 1), "single-tile pipeline depth");
+    static_assert(!T::RESTAGE || T::SINGLE || STAGES == 4, "the restaged epilogue uses the idle fourth stage");
+    static_assert(!T::SINGLE || C::NW * kRestageRows * kRestageRow <= C::LDS_BYTES, "single-tile restage rows");
     static_assert(NG == 16, "one 16-entry column descriptor load per wave");
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
-    __shared__ __attribute__((aligned(16))) __bf16 bias_s[2][BF];   // tile bias, double-buffered
+    // LDS: the stages, then (multi-tile workgroups) the tile bias, double-buffered. A
+    // single-tile workgroup keeps its bias in stage PF, which no load reaches before the
+    // first K step's barrier, after which the bias has been read.
+    constexpr int BIAS_OFS = T::SINGLE ? PF * C::W_BYTES : C::LDS_BYTES;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES + (T::SINGLE ? 0 : 2 * BF * 2)];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -395,11 +408,11 @@ fused_proj_fast_kernel(KernelArgs p) {
     pp.wstep = (W_FC ? (int64_t)BK : (int64_t)BK * N) * 2;
     pp.xstep = (X_TL ? (int64_t)BK : (int64_t)BK * p.x_sc) * 2;
 
-    // The bias slice of a tile, copied into bias_s[buf] by the first wave's first 32 lanes
+    // The bias slice of a tile, copied into bias buffer buf by the first wave's first lanes
     // with the same direct-to-LDS loads as the operands (from the zero block where there
     // is no bias). It is issued right after the tile's step 0, so the waits and barriers
     // that make step 0 visible also cover it.
-    const unsigned bias_lds = (unsigned)(size_t)(lds_void*)&bias_s[0][0];
+    const unsigned bias_lds = (unsigned)(size_t)(lds_void*)(smem + BIAS_OFS);
     auto issue_bias = [&](int buf, int n0) __attribute__((always_inline)) {
         if (wave == 0 && lane < BF / 8) {
             const int f = n0 + 8 * lane;
@@ -425,13 +438,26 @@ fused_proj_fast_kernel(KernelArgs p) {
     unsigned voff_cur[NLOAD], voff_nxt[NLOAD];
     tile_offsets<C, X_TL, W_FC>(voff_cur, pp.kofs, tt * BT, tf * BF, wave, lane, K, N, M, S, p.x_sb, p.x_ss,
                                 p.x_sc);
-    // Prologue: the first PF K steps of the first tile and its bias in flight; once
-    // step 0 has landed (steps 1 and 2 may still be in flight), read its operands.
+    // Wait until this wave's loads of all but the `later` most recently issued K steps have
+    // landed (the vector memory counter counts in issue order).
+    auto wait_steps = [&](int later) __attribute__((always_inline)) {
+        static_assert(PF - 2 <= 3 && (T::SINGLE || PF - 1 <= 3), "wait counts cover up to three later steps");
+        if (later >= 3) wait_vmcnt<3 * NLOAD>();
+        else if (later == 2) wait_vmcnt<2 * NLOAD>();
+        else if (later == 1) wait_vmcnt<NLOAD>();
+        else wait_vmcnt<0>();
+    };
+    // Prologue: the first PF K steps of the first tile and its bias in flight; once step 0
+    // has landed (the later ones may still be in flight), read its operands. Single-tile
+    // workgroups issue only the steps that exist, so that no load is in flight after the
+    // last K step (their epilogue reuses the whole stage area).
     pp.template issue<0>(voff_cur, 0, K, zeros);
     issue_bias(0, tf * BF);
-    pp.template issue<1>(voff_cur, 1, K, zeros);
-    pp.template issue<2>(voff_cur, 2, K, zeros);
-    wait_vmcnt<2 * NLOAD>();
+    if (!T::SINGLE || 1 < KTp) pp.template issue<1>(voff_cur, 1, K, zeros);
+    if (!T::SINGLE || 2 < KTp) pp.template issue<2>(voff_cur, 2, K, zeros);
+    if constexpr (PF >= 4) if (!T::SINGLE || 3 < KTp) pp.template issue<3>(voff_cur, 3, K, zeros);
+    if constexpr (PF >= 5) if (!T::SINGLE || 4 < KTp) pp.template issue<4>(voff_cur, 4, K, zeros);
+    wait_steps(T::SINGLE ? min(PF - 1, KTp - 1) : PF - 1);
     __syncthreads();
     Ops c0 = pp.template read<0, 0>();
     Ops c1 = pp.template read<0, 1>();
@@ -453,7 +479,8 @@ fused_proj_fast_kernel(KernelArgs p) {
 
         // The accumulators start from the bias (in LDS since the last barrier): acc[a][j][e]
         // holds column 32a + 8(e/4) + 4(lane/32) + e%4 of the wave tile.
-        const __bf16* const bias_t = bias_s[k_tile & 1] + wf * WF + 4 * hl;
+        const __bf16* const bias_t =
+            reinterpret_cast<const __bf16*>(smem + BIAS_OFS) + (k_tile & 1) * BF + wf * WF + 4 * hl;
         f32x16 acc[TI][TJ];
 #pragma unroll
         for (int a = 0; a < TI; ++a) {
@@ -484,10 +511,9 @@ fused_proj_fast_kernel(KernelArgs p) {
             __builtin_amdgcn_sched_barrier(0);
             const int s_load = kt + PF;
             if constexpr (T::SINGLE) {
-                // the loads of step kt+2 were issued (by the prologue or step kt-1) only
-                // while it exists; without them wait for everything
-                if (kt + 2 < KTp || kt == 0) wait_vmcnt<NLOAD>();
-                else wait_vmcnt<0>();
+                // steps issued so far: 0 .. kt+PF-1 while they exist (by the prologue and
+                // the steps before); those after kt+1 may stay in flight
+                wait_steps(min(kt + PF - 1, KTp - 1) - kt - 1);
                 __syncthreads();
                 if (s_load < KTp) pp.template issue<SL>(voff_cur, s_load, K, zeros);
             } else {
@@ -512,16 +538,21 @@ fused_proj_fast_kernel(KernelArgs p) {
         // makes it keep a spilled copy of the initial accumulators for that path)
         int kt = 0;
         if constexpr (T::SINGLE) {
-            static_assert(STAGES == 4, "the remainder below is written for four stages");
+            static_assert(STAGES >= 3 && STAGES <= 6, "the unrolling below covers 3 to 6 stages");
             for (; kt + STAGES <= KTp; kt += STAGES) {
                 k_step(std::integral_constant<int, 0>{}, kt);
                 k_step(std::integral_constant<int, 1>{}, kt + 1);
                 k_step(std::integral_constant<int, 2>{}, kt + 2);
-                k_step(std::integral_constant<int, 3>{}, kt + 3);
+                if constexpr (STAGES >= 4) k_step(std::integral_constant<int, 3 % STAGES>{}, kt + 3);
+                if constexpr (STAGES >= 5) k_step(std::integral_constant<int, 4 % STAGES>{}, kt + 4);
+                if constexpr (STAGES >= 6) k_step(std::integral_constant<int, 5 % STAGES>{}, kt + 5);
             }
+            // the last KTp mod STAGES steps
             if (kt < KTp) k_step(std::integral_constant<int, 0>{}, kt);
             if (kt + 1 < KTp) k_step(std::integral_constant<int, 1>{}, kt + 1);
-            if (kt + 2 < KTp) k_step(std::integral_constant<int, 2>{}, kt + 2);
+            if constexpr (STAGES >= 4) if (kt + 2 < KTp) k_step(std::integral_constant<int, 2>{}, kt + 2);
+            if constexpr (STAGES >= 5) if (kt + 3 < KTp) k_step(std::integral_constant<int, 3 % STAGES>{}, kt + 3);
+            if constexpr (STAGES >= 6) if (kt + 4 < KTp) k_step(std::integral_constant<int, 4 % STAGES>{}, kt + 4);
         } else {
             do {
                 k_step(std::integral_constant<int, 0>{}, kt);
@@ -557,12 +588,16 @@ fused_proj_fast_kernel(KernelArgs p) {
             // writes and the 16-byte chunk reads free of bank conflicts) in the stage no K step
             // uses until the next tile's first barrier and the spare bytes after it. Every LDS
             // address is a per-lane base plus a constant.
-            static_assert(C::W_BYTES == C::X_BYTES && C::W_BYTES + PAD >= C::NW / 2 * kRestageRows * kRestageRow,
+            static_assert(T::SINGLE ||
+                              (C::W_BYTES == C::X_BYTES && C::W_BYTES + PAD >= C::NW / 2 * kRestageRows * kRestageRow),
                           "restage regions");
             constexpr int RGN = kRestageRows * kRestageRow;
-            const unsigned wave_lds = wave < C::NW / 2 ? pp.lds0 + (STAGES - 1) * C::W_BYTES + wave * RGN
-                                                       : pp.lds0 + C::X_REGION + (STAGES - 1) * C::X_BYTES +
-                                                             (wave - C::NW / 2) * RGN;
+            // single-tile workgroups: no load is in flight after the last K step's wait and
+            // every wave has passed its barrier, so the whole stage area is free
+            const unsigned wave_lds = T::SINGLE          ? pp.lds0 + wave * RGN
+                                      : wave < C::NW / 2 ? pp.lds0 + (STAGES - 1) * C::W_BYTES + wave * RGN
+                                                         : pp.lds0 + C::X_REGION + (STAGES - 1) * C::X_BYTES +
+                                                               (wave - C::NW / 2) * RGN;
             // The lane index again, recomputed per tile where the compiler cannot see it: the
             // LDS addresses and column selects below depend only on it, and hoisted out of the
             // tile loop they would hold registers through the K loop (spilled to scratch, whose

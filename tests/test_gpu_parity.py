@@ -75,6 +75,15 @@ SMALL = [
                n_heads=2, head_dim=64, seed=111),
     with_shape(WORKLOADS["bert_qkv_bf16"], "tl_small_tiles_straddle", x_shape=(8, 80, 64), ff_dim=0, n_heads=3,
                head_dim=64, rope=True, w_layout="fc", seed=112),
+    # small tiles with one K step (K = 24: the load pipeline is deeper than the K loop), with
+    # K = 160 (five whole steps: one pass of the five-stage loop, no partial steps) and with
+    # K = 224 (seven whole steps: a pass and a remainder of two)
+    with_shape(WORKLOADS["walrus_bf16"], "cf_small_tiles_one_kstep", x_shape=(2, 24, 8, 16, 1), ff_dim=64,
+               n_heads=2, head_dim=64, seed=113),
+    with_shape(WORKLOADS["bert_qkv_bf16"], "tl_small_tiles_k160", x_shape=(2, 128, 160), ff_dim=0, n_heads=2,
+               head_dim=64, seed=114),
+    with_shape(WORKLOADS["smallk_qkv_bf16"], "cf_small_tiles_k224", x_shape=(2, 224, 8, 16), n_heads=2,
+               seed=115),
     # fp32, token-major, [F,C], RoPE hd 8, GELU
     with_shape(WORKLOADS["tiny_f32"], "f32_tl_fc", layout="tokens_last", x_shape=(3, 50, 36), ff_dim=16,
                n_heads=3, head_dim=8, w_layout="fc", seed=106),
