@@ -211,6 +211,8 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     a.tiles_m = (int32_t)((r.M + h->tile.bm - 1) / h->tile.bm);  // token tiles
     a.tiles_n = (int32_t)((r.F + h->tile.bn - 1) / h->tile.bn);
     a.group_m = h->tile.group_m;
+    a.div_s = fp::make_fastdiv_u31((uint32_t)r.S);
+    a.div_group = fp::make_fastdiv_u31((uint32_t)((int64_t)a.group_m * a.tiles_n));
 
     if (a.rope && r.S > 0) {
         // cos/sin of (s + pos_offset) * base^(-2i/hd), computed in float64, stored fp32

@@ -245,8 +245,8 @@ struct FastPipe {
 // Rows past N and tokens past M read row / token 0 instead (in bounds, never stored).
 template <class C, bool X_TL, bool W_FC>
 __device__ __forceinline__ void tile_offsets(unsigned (&voff)[C::NLOAD], int (&kofs)[C::NLOAD], int m0, int n0,
-                                             int wave, int lane, int K, int N, int M, int S, int64_t sb,
-                                             int64_t ss, int64_t sc) {
+                                             int wave, int lane, int K, int N, int M, int S, FastDivU31 ds,
+                                             int64_t sb, int64_t ss, int64_t sc) {
 #pragma unroll
     for (int q = 0; q < C::W_INSTR; ++q) {
         const int pch = (wave * C::W_INSTR + q) * 64 + lane;
@@ -282,7 +282,7 @@ __device__ __forceinline__ void tile_offsets(unsigned (&voff)[C::NLOAD], int (&k
             krow = row;
         }
         const int mm = m < M ? m : 0;
-        const int bi = mm / S, s = mm - bi * S;
+        const int bi = (int)fastdiv_u31((uint32_t)mm, ds), s = mm - bi * S;
         const int64_t off = (int64_t)bi * sb + (int64_t)s * ss + (int64_t)krow * sc;
         voff[C::W_INSTR + q] = (unsigned)(off * 2);
         kofs[C::W_INSTR + q] = krow;
@@ -293,7 +293,11 @@ __device__ __forceinline__ void tile_offsets(unsigned (&voff)[C::NLOAD], int (&k
 // contiguous ranges, one per XCD (workgroup b runs on XCD b mod 8); inside its range a
 // workgroup takes every (workgroups per XCD)-th tile. Linear order: groups of group_m
 // token tiles sweep the column tiles together.
-__device__ __forceinline__ bool block_tile(int k, int tiles_t, int tiles_f, int group_m, int& tt, int& tf) {
+// Wave-uniform; the division by the group size is a host-computed multiply-high, and the
+// groups of group_m token tiles (a power of two except possibly the last group) are
+// walked with shifts.
+__device__ __forceinline__ bool block_tile(int k, const KernelArgs& p, int& tt, int& tf) {
+    const int tiles_t = p.tiles_m, tiles_f = p.tiles_n, group_m = p.group_m;
     const int total = tiles_t * tiles_f;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
     const int q = total >> 3, r = total & 7;
@@ -302,12 +306,18 @@ __device__ __forceinline__ bool block_tile(int k, int tiles_t, int tiles_f, int 
     if (li >= count) return false;
     const int lin = xcd * q + (xcd < r ? xcd : r) + li;
     const int per_group = group_m * tiles_f;
-    const int grp = lin / per_group;
+    const int grp = (int)fastdiv_u31((uint32_t)lin, p.div_group);
     const int first = grp * group_m;
     const int gsz = (tiles_t - first) < group_m ? (tiles_t - first) : group_m;
     const int in = lin - grp * per_group;
-    tt = first + in % gsz;
-    tf = in / gsz;
+    if ((gsz & (gsz - 1)) == 0) {
+        const int sh = __builtin_ctz((unsigned)gsz);
+        tt = first + (in & (gsz - 1));
+        tf = in >> sh;
+    } else {
+        tt = first + in % gsz;
+        tf = in / gsz;
+    }
     return true;
 }
 
@@ -376,7 +386,7 @@ fused_proj_fast_kernel(KernelArgs p) {
     const __bf16* const bias = static_cast<const __bf16*>(p.bias);
 
     int tt, tf;
-    if (!block_tile(0, p.tiles_m, p.tiles_n, p.group_m, tt, tf)) return;
+    if (!block_tile(0, p, tt, tf)) return;
 
     Pipe pp;
     pp.wave = wave;
@@ -436,8 +446,8 @@ fused_proj_fast_kernel(KernelArgs p) {
     const int64_t slab_elems = (int64_t)S * p.qw;   // q/k/v elements of one slab (all heads)
 
     unsigned voff_cur[NLOAD], voff_nxt[NLOAD];
-    tile_offsets<C, X_TL, W_FC>(voff_cur, pp.kofs, tt * BT, tf * BF, wave, lane, K, N, M, S, p.x_sb, p.x_ss,
-                                p.x_sc);
+    tile_offsets<C, X_TL, W_FC>(voff_cur, pp.kofs, tt * BT, tf * BF, wave, lane, K, N, M, S, p.div_s, p.x_sb,
+                                p.x_ss, p.x_sc);
     // Wait until this wave's loads of all but the `later` most recently issued K steps have
     // landed (the vector memory counter counts in issue order).
     auto wait_steps = [&](int later) __attribute__((always_inline)) {
@@ -465,10 +475,10 @@ fused_proj_fast_kernel(KernelArgs p) {
     for (int k_tile = 0;; ++k_tile) {
         const int m0 = tt * BT, n0 = tf * BF;
         int ntt = 0, ntf = 0;
-        const bool has_next = block_tile(k_tile + 1, p.tiles_m, p.tiles_n, p.group_m, ntt, ntf);
+        const bool has_next = block_tile(k_tile + 1, p, ntt, ntf);
         if (has_next) {
-            tile_offsets<C, X_TL, W_FC>(voff_nxt, pp.kofs, ntt * BT, ntf * BF, wave, lane, K, N, M, S, p.x_sb,
-                                        p.x_ss, p.x_sc);
+            tile_offsets<C, X_TL, W_FC>(voff_nxt, pp.kofs, ntt * BT, ntf * BF, wave, lane, K, N, M, S, p.div_s,
+                                        p.x_sb, p.x_ss, p.x_sc);
         } else {
             // past the last tile the loads repeat this tile's first steps (in bounds, never
             // read), which keeps the K loop free of branches
@@ -621,10 +631,11 @@ fused_proj_fast_kernel(KernelArgs p) {
             char* const row0_l = base_l + r0 * stride_l;
             const bool col_ok = fw + 8 * gl < N;
             // the wave's tokens usually lie in one slab: then a token's offset is linear in it
-            const int bi_first = tw0 / S;
-            const bool one_slab = (tw0 + WT - 1 < M ? tw0 + WT - 1 : M - 1) / S == bi_first;
+            const int bi_first = (int)fastdiv_u31((uint32_t)tw0, p.div_s);
+            const bool one_slab =
+                (int)fastdiv_u31((uint32_t)(tw0 + WT - 1 < M ? tw0 + WT - 1 : M - 1), p.div_s) == bi_first;
             auto token_off = [&](int t) __attribute__((always_inline)) {
-                const int bi = t / S;
+                const int bi = (int)fastdiv_u31((uint32_t)t, p.div_s);
                 const int s = t - bi * S;
                 return kind_l == 0 ? (unsigned)t * (unsigned)(2 * ff_dim)
                                    : (unsigned)(((int64_t)bi * slab_elems + (int64_t)s * hd) * 2);
@@ -639,7 +650,7 @@ fused_proj_fast_kernel(KernelArgs p) {
             auto load_rope = [&](int j, int r0) __attribute__((always_inline)) {
                 const int t = tw0 + 32 * j + (lane_e & 31);
                 const int tc = t < M ? t : 0;
-                const int s = tc - (tc / S) * S;
+                const int s = tc - (int)fastdiv_u31((uint32_t)tc, p.div_s) * S;
                 const unsigned rp_off = (unsigned)((s * (DG * 8) + 4 * (lane_e >> 5)) * 4);
 #pragma unroll
                 for (int r = 0; r < NRB; ++r) {
@@ -742,7 +753,7 @@ fused_proj_fast_kernel(KernelArgs p) {
                 const int t = tw0 + 32 * j + (lane & 31);
                 tv[j] = t < M;
                 const int tc = tv[j] ? t : 0;
-                const int bi = tc / S, s = tc - bi * S;
+                const int bi = (int)fastdiv_u31((uint32_t)tc, p.div_s), s = tc - bi * S;
                 ff_off[j] = (unsigned)tc * (unsigned)(2 * ff_dim) + (unsigned)(8 * hl);
                 hv_off[j] = (unsigned)(((int64_t)bi * slab_elems + (int64_t)s * hd + 4 * hl) * 2);
                 rp_off[j] = (unsigned)((s * (DG * 8) + 4 * hl) * 4);

@@ -5,6 +5,27 @@
 
 namespace fp {
 
+// Division by a divisor d >= 1 fixed at plan time, for dividends 0 <= n < 2^31, as one
+// multiply-high, an add and a shift (Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994): with l = ceil(log2 d) and
+// m = ceil(2^(32+l) / d), m - 2^32 fits 32 bits and n / d = (umulhi(n, m - 2^32) + n) >> l.
+// Exact: m d - 2^(32+l) < d <= 2^l, so n m / 2^(32+l) exceeds n / d by less than 1 / (2d).
+struct FastDivU31 {
+    uint32_t mul;    // m - 2^32
+    uint32_t shift;  // l
+};
+inline FastDivU31 make_fastdiv_u31(uint32_t d) {
+    if (d == 0) d = 1;
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint64_t p = uint64_t(1) << (32 + l);
+    const uint64_t m = p / d + (p % d != 0 ? 1 : 0);
+    return FastDivU31{(uint32_t)(m - (uint64_t(1) << 32)), l};
+}
+__host__ __device__ inline uint32_t fastdiv_u31(uint32_t n, FastDivU31 f) {
+    return (uint32_t)((((uint64_t)n * f.mul) >> 32) + n) >> f.shift;
+}
+
 // Everything a launch needs, passed by value as the kernel argument.
 struct KernelArgs {
     const void* x;       // activation (storage type)
@@ -37,6 +58,9 @@ struct KernelArgs {
     // full. Bits 30-31: 0 ff, 1 q, 2 k, 3 v; bits 0-29: element offset of the group's
     // first column (ff: its column; q/k/v: head * S * head_dim + place in the head).
     const unsigned* col_desc;
+    // Fast kernel only: division by S (token -> slab) and by group_m * tiles_n (tile order).
+    FastDivU31 div_s;
+    FastDivU31 div_group;
 };
 
 // Tile plan chosen on the host.
