@@ -27,6 +27,9 @@ _SRC = os.path.join(_HERE, "fused_proj_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle_fused_proj.so")
 _lib = None
 
+# ff-slice activations: identity, exact-erf GELU, tanh GELU, squared ReLU
+ACTIVATIONS = {"none": 0, "gelu": 1, "gelu_tanh": 2, "relu2": 3}
+
 GCC_FLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared", "-std=c99"]
 
 
@@ -143,7 +146,7 @@ def fused_proj(x: np.ndarray, layout: str, w: np.ndarray, w_layout: str, bias: n
     v_rows = np.empty((ntok, qw)) if qw > 0 else None
     spz = (ctypes.c_int64 * len(sp))(*sp)
     sps = (ctypes.c_int64 * len(sp))(*sp_stride)
-    act = {"none": 0, "gelu": 1}[ff_act]
+    act = ACTIVATIONS[ff_act]
     rc = lib.oracle_fused_proj(
         x.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), nb, C, S, sb, sc, len(sp), spz, sps,
         _dptr(w), F, w_fc, _dptr(bias),

@@ -8,7 +8,10 @@ scale = ||x_t|| * ||w_col|| + |b_col|, rel = 4e-3 for bf16 storage and 1e-5
 for fp32. For q/k elements after RoPE the output is itself a projection with
 the effective column w_eff = cos(phi) W[:, j] -/+ sin(phi) W[:, j'] (and the
 same mix of biases), since RoPE is linear; its norm is used. For GELU outputs
-the pre-activation scale is used (GELU is 1.13-Lipschitz).
+(either form) the pre-activation scale is used (both are under 1.13-Lipschitz).
+Squared ReLU doubles an input error by |y| at y: its outputs o use the
+pre-activation scale times (1 + 2 sqrt(o)), which bounds
+|d(y^2)| <= 2|y||dy| + dy^2 while |dy| <= 1.
 
 A second, tighter diagnostic bar is also reported for bf16: the output's own
 rounding (2^-8 relative) plus 1e-4 * scale of accumulation error.
@@ -47,8 +50,10 @@ class Scales:
 
 
 def scales(rows: np.ndarray, positions: np.ndarray, w_cf: np.ndarray, bias: np.ndarray | None, ff_dim: int,
-           n_heads: int, head_dim: int, rope: bool, rope_base: float = 10000.0, pos_offset: int = 0) -> Scales:
-    """Per-element scale for tokens with gathered rows [n, C]; w_cf is W as [C, F]."""
+           n_heads: int, head_dim: int, rope: bool, rope_base: float = 10000.0, pos_offset: int = 0,
+           ff_act: str = "none", ff_ref: np.ndarray | None = None) -> Scales:
+    """Per-element scale for tokens with gathered rows [n, C]; w_cf is W as [C, F].
+    For ff_act "relu2" the oracle's ff outputs ff_ref [n, FF] are needed."""
     n = rows.shape[0]
     F = w_cf.shape[1]
     xn = np.linalg.norm(rows, axis=1)                         # [n]
@@ -56,6 +61,10 @@ def scales(rows: np.ndarray, positions: np.ndarray, w_cf: np.ndarray, bias: np.n
     b = np.zeros(F) if bias is None else np.asarray(bias, dtype=np.float64)
     plain = xn[:, None] * wn[None, :] + np.abs(b)[None, :]    # [n, F]
     ff = plain[:, :ff_dim] if ff_dim > 0 else None
+    if ff is not None and ff_act == "relu2":
+        if ff_ref is None:
+            raise ValueError("squared ReLU scales need the oracle's ff outputs")
+        ff = ff * (1.0 + 2.0 * np.sqrt(np.maximum(np.asarray(ff_ref, dtype=np.float64).reshape(ff.shape), 0.0)))
     qw = n_heads * head_dim
     if qw == 0:
         return Scales(ff, None, None, None)

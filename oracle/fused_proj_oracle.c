@@ -27,7 +27,12 @@
  *     the q/k/v slices holding n_heads heads of head_dim columns, head-major.
  *
  *  4. Activation on the ff slice: exact-erf GELU, 0.5*y*(1+erf(y/sqrt 2)).
- *     (The pages name no GELU form; erf is the reading taken.)
+ *     (The pages name no GELU form; erf is the reading taken.) Two more
+ *     activations on the same slice: the tanh form of GELU, from the paper
+ *     that defines GELU (Hendrycks and Gimpel, "Gaussian Error Linear Units
+ *     (GELUs)", 2016): 0.5*y*(1+tanh(sqrt(2/pi)*(y+0.044715*y^3))); and
+ *     squared ReLU, max(y,0)^2, which the xformers PR discussion names among
+ *     the activations a fused linear layer handles natively.
  *
  *  5. Head-major buffers. memory-efficient-attention issue "Improve
  *     performance via batched-matmul and fused multiplies" (first comment):
@@ -83,6 +88,29 @@ static double gelu_erf(double y)
     return 0.5 * y * (1.0 + erf(y / sqrt(2.0)));
 }
 
+static double gelu_tanh(double y)
+{
+    const double k = sqrt(2.0 / 3.14159265358979323846);
+    return 0.5 * y * (1.0 + tanh(k * (y + 0.044715 * y * y * y)));
+}
+
+static double relu_squared(double y)
+{
+    const double r = y > 0.0 ? y : 0.0;
+    return r * r;
+}
+
+/* ff_act: 0 identity, 1 exact-erf GELU, 2 tanh GELU, 3 squared ReLU */
+static double activate(int ff_act, double y)
+{
+    switch (ff_act) {
+    case 1: return gelu_erf(y);
+    case 2: return gelu_tanh(y);
+    case 3: return relu_squared(y);
+    default: return y;
+    }
+}
+
 /* Rotate-half RoPE of one head vector v[0..hd) at position p, in place. */
 static void rope_rotate_half(double *v, int64_t hd, double p, double base)
 {
@@ -106,7 +134,8 @@ static void rope_rotate_half(double *v, int64_t hd, double p, double base)
  *   w        float64 weight, [C,F] (w_fc=0) or [F,C] (w_fc=1)
  *   bias     float64 [F] or NULL
  *   ff_dim   width of the ff slice; F = ff_dim + 3*n_heads*head_dim
- *   ff_gelu  1: exact-erf GELU on the ff slice, 0: identity
+ *   ff_act   activation on the ff slice: 0 identity, 1 exact-erf GELU,
+ *            2 tanh GELU, 3 squared ReLU
  *   rope     1: rotate-half RoPE on q and k (head_dim must be even)
  *   tokens   global token indices t = bi*S + s, each in [0, nb*S)
  *   outputs  token-major rows: ff_rows [ntok, ff_dim],
@@ -118,7 +147,7 @@ static void rope_rotate_half(double *v, int64_t hd, double p, double base)
 int oracle_fused_proj(const double *x, int64_t nb, int64_t C, int64_t S, int64_t sb, int64_t sc,
                       int nsp, const int64_t *sp_size, const int64_t *sp_stride,
                       const double *w, int64_t F, int w_fc, const double *bias,
-                      int64_t ff_dim, int ff_gelu, int64_t n_heads, int64_t head_dim,
+                      int64_t ff_dim, int ff_act, int64_t n_heads, int64_t head_dim,
                       int rope, double rope_base, int64_t pos_offset,
                       const int64_t *tokens, int64_t ntok,
                       double *ff_rows, double *q_rows, double *k_rows, double *v_rows,
@@ -133,6 +162,7 @@ int oracle_fused_proj(const double *x, int64_t nb, int64_t C, int64_t S, int64_t
     }
     if (prod != S) return ORACLE_EINVAL;
     if (ff_dim < 0 || n_heads < 0 || head_dim < 0) return ORACLE_EINVAL;
+    if (ff_act < 0 || ff_act > 3) return ORACLE_EINVAL;
     const int64_t qw = n_heads * head_dim;
     if (F != ff_dim + 3 * qw || F <= 0) return ORACLE_EINVAL;
     if (rope && (head_dim % 2 != 0)) return ORACLE_EINVAL;
@@ -184,7 +214,7 @@ int oracle_fused_proj(const double *x, int64_t nb, int64_t C, int64_t S, int64_t
                 for (int64_t f = 0; f < F; ++f) y[f] += bias[f];
             /* 3+4. ff slice with activation */
             for (int64_t f = 0; f < ff_dim; ++f)
-                ff_rows[i * ff_dim + f] = ff_gelu ? gelu_erf(y[f]) : y[f];
+                ff_rows[i * ff_dim + f] = activate(ff_act, y[f]);
             /* 3+6. q, k, v slices; RoPE on q and k per head */
             if (qw > 0) {
                 double *dst[3] = {q_rows + i * qw, k_rows + i * qw, v_rows + i * qw};

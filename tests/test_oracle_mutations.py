@@ -31,6 +31,10 @@ MUTATIONS = [
      "const double *src = y + ff_dim + (which == 0 ? 1 : which == 1 ? 0 : 2) * qw;"),
     ("tanh GELU", "return 0.5 * y * (1.0 + erf(y / sqrt(2.0)));",
      "return 0.5 * y * (1.0 + tanh(0.7978845608028654 * (y + 0.044715 * y * y * y)));"),
+    ("tanh GELU constant", "0.044715 * y * y * y", "0.04715 * y * y * y"),
+    ("tanh GELU without the cube", "(y + 0.044715 * y * y * y)", "(y + 0.044715 * y * y)"),
+    ("squared ReLU without the clamp", "const double r = y > 0.0 ? y : 0.0;", "const double r = y;"),
+    ("squared ReLU not squared", "    return r * r;", "    return r;"),
     ("spatial dims unflattened in reverse", "int64_t idx = rem % sp_size[d];", "int64_t idx = rem % sp_size[nsp - 1 - d];"),
     ("bias skipped on the ff slice", "for (int64_t f = 0; f < F; ++f) y[f] += bias[f];",
      "for (int64_t f = 0; f < F; ++f) y[f] += (f < ff_dim ? 0.0 : bias[f]);"),

@@ -207,6 +207,53 @@ def test_gelu_identities_and_torch_exact_gelu():
     assert np.max(np.abs(g - tanh)) > 1e-4
 
 
+def _act_via_oracle(vals, act):
+    """Run the oracle with W = I on the FF slice so that ff = act(x)."""
+    n = len(vals)
+    x = np.asarray(vals, dtype=np.float64).reshape(1, 1, n)
+    return oracle.fused_proj(x, "tokens_last", np.eye(n), "cf", None, n, act, 0, 0, rope=False).ff.reshape(-1)
+
+
+def test_tanh_gelu_against_torch_tanh_gelu():
+    """The tanh form of GELU (Hendrycks and Gimpel, 2016): torch's GELU with
+    approximate='tanh' in float64 (a library routine), the odd-part identity
+    g(y) - g(-y) = y, and a distance of 1e-4 .. 1e-3 from the exact-erf form. Catches a
+    wrong constant (0.044715, sqrt(2/pi)), a missing cube, or the erf form in its place."""
+    y = np.linspace(-8, 8, 161)
+    g = _act_via_oracle(y, "gelu_tanh")
+    gm = _act_via_oracle(-y, "gelu_tanh")
+    assert np.allclose(g - gm, y, rtol=0, atol=4e-15)
+    t = torch.nn.functional.gelu(torch.from_numpy(y), approximate="tanh").numpy()
+    assert np.allclose(g, t, rtol=0, atol=2e-15)
+    d = np.max(np.abs(g - _act_via_oracle(y, "gelu")))
+    assert 1e-4 < d < 1e-3, d
+
+
+def test_squared_relu_against_torch_relu():
+    """Squared ReLU max(y, 0)^2 (named in the xformers PR discussion): zero for y <= 0,
+    torch.relu(y) ** 2 in float64, and degree-2 homogeneity r(2y) = 4 r(y). Catches a
+    missing square, |y| in place of max(y, 0), or a missing clamp."""
+    y = np.linspace(-5, 5, 101)
+    r = _act_via_oracle(y, "relu2")
+    assert np.all(r[y <= 0] == 0.0)
+    t = (torch.relu(torch.from_numpy(y)) ** 2).numpy()
+    assert np.allclose(r, t, rtol=1e-15, atol=0)
+    assert np.allclose(_act_via_oracle(2 * y, "relu2"), 4 * r, rtol=1e-15, atol=0)
+
+
+def test_activation_applies_to_the_ff_slice_only():
+    """The activation acts on the ff columns after the bias; q/k/v are untouched.
+    Catches an activation on every column, or one applied before the bias."""
+    x, w, b = rng_inputs(21, (2, 5, 12), 12, 8 + 3 * 8)
+    for act in ("gelu_tanh", "relu2"):
+        res = oracle.fused_proj(x, "tokens_last", w, "cf", b, 8, act, 2, 4, rope=False)
+        plain = oracle.fused_proj(x, "tokens_last", w, "cf", b, 8, "none", 2, 4, rope=False)
+        for a, c in ((res.q, plain.q), (res.k, plain.k), (res.v, plain.v)):
+            assert np.array_equal(a, c)
+        assert np.allclose(res.ff, _act_via_oracle(plain.ff.reshape(-1), act).reshape(plain.ff.shape),
+                           rtol=0, atol=1e-15)
+
+
 # --------------------------------------------------------------------------- RoPE
 
 def _rope_via_oracle(vec, p, base, which="q"):
