@@ -234,7 +234,7 @@ def main() -> int:
         rows, pos = cmp.token_rows(inp.x64, wl.layout, tokens)
         w_cf = inp.w64 if wl.w_layout == "cf" else inp.w64.T
         sc = cmp.scales(rows, pos, w_cf, inp.bias64, wl.ff_dim, wl.n_heads, wl.head_dim, wl.rope, wl.rope_base,
-                        wl.pos_offset)
+                        wl.pos_offset, ff_act=wl.ff_act, ff_ref=ref.ff)
         vd = cmp.compare(got, [ref.ff, ref.q, ref.k, ref.v], [sc.ff, sc.q, sc.k, sc.v], wl.dtype)
         result["parity"] = {"ok": vd.ok, "max_err_over_tol": round(vd.max_ratio, 5),
                             "tight_ratio": round(vd.max_tight_ratio, 5), "elements": vd.n}

@@ -30,7 +30,7 @@ OK, EINVAL, EUNSUPPORTED, EALIGN, EALIAS, EHIP = 0, -1, -2, -3, -4, -5
 BF16, F32 = 0, 1
 X_CHANNELS_FIRST, X_TOKENS_LAST = 0, 1
 W_CF, W_FC = 0, 1
-ACT_NONE, ACT_GELU_ERF = 0, 1
+ACT_NONE, ACT_GELU_ERF, ACT_GELU_TANH, ACT_RELU_SQUARED = 0, 1, 2, 3
 
 
 class Desc(ctypes.Structure):
@@ -134,7 +134,7 @@ def make_desc(x_shape, x_strides, layout: str, dtype: torch.dtype, *, w_layout: 
     d.w_layout = {"cf": W_CF, "fc": W_FC}[w_layout]
     d.has_bias = int(bool(has_bias))
     d.ff_dim = ff_dim
-    d.ff_act = {"none": ACT_NONE, "gelu": ACT_GELU_ERF}[ff_act]
+    d.ff_act = {"none": ACT_NONE, "gelu": ACT_GELU_ERF, "gelu_tanh": ACT_GELU_TANH, "relu2": ACT_RELU_SQUARED}[ff_act]
     d.n_heads, d.head_dim = n_heads, head_dim
     d.rope, d.rope_base, d.pos_offset = int(bool(rope)), float(rope_base), pos_offset
     return d

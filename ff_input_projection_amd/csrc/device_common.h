@@ -126,6 +126,21 @@ __device__ __forceinline__ float gelu_erf_poly(float y) {
     return fmaf(-a, __builtin_amdgcn_exp2f(p), __builtin_amdgcn_fmed3f(y, 0.0f, 3.40282347e+38f));
 }
 
+// tanh form of GELU (Hendrycks and Gimpel, "Gaussian Error Linear Units (GELUs)",
+// 2016): 0.5 y (1 + tanh(u)), u = sqrt(2/pi) (y + 0.044715 y^3). Since
+// 0.5 (1 + tanh u) = 1 / (1 + e^(-2u)), it is y / (1 + 2^(-2u log2 e)): one exp2 and
+// one reciprocal, each within a few ulps in fp32. For large |u| the exp2 goes to 0 or
+// +inf and the result to y or -0.
+__device__ __forceinline__ float gelu_tanh(float y) {
+    const float u2 = (y + 0.044715f * (y * y * y)) * (2.0f * 0.79788456080286536f * 1.4426950408889634f);
+    return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u2));
+}
+// Squared ReLU, max(y, 0)^2.
+__device__ __forceinline__ float relu_squared(float y) {
+    const float r = y > 0.0f ? y : 0.0f;
+    return r * r;
+}
+
 __device__ __forceinline__ float bf16_to_f32(__bf16 v) { return (float)v; }
 
 // Tile of linear block id. Workgroups are dispatched round-robin over the 8 XCDs

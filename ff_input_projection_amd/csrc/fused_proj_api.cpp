@@ -45,7 +45,9 @@ int check_desc(const fused_proj_desc* d, Derived* out) {
     if (d->dtype != FUSED_PROJ_BF16 && d->dtype != FUSED_PROJ_F32) return FUSED_PROJ_EINVAL;
     if (d->x_layout != FUSED_PROJ_X_CHANNELS_FIRST && d->x_layout != FUSED_PROJ_X_TOKENS_LAST) return FUSED_PROJ_EINVAL;
     if (d->w_layout != FUSED_PROJ_W_CF && d->w_layout != FUSED_PROJ_W_FC) return FUSED_PROJ_EINVAL;
-    if (d->ff_act != FUSED_PROJ_ACT_NONE && d->ff_act != FUSED_PROJ_ACT_GELU_ERF) return FUSED_PROJ_EINVAL;
+    if (d->ff_act != FUSED_PROJ_ACT_NONE && d->ff_act != FUSED_PROJ_ACT_GELU_ERF &&
+        d->ff_act != FUSED_PROJ_ACT_GELU_TANH && d->ff_act != FUSED_PROJ_ACT_RELU_SQUARED)
+        return FUSED_PROJ_EINVAL;
     if (d->batch < 0 || d->channels < 0 || d->ff_dim < 0 || d->n_heads < 0 || d->head_dim < 0) return FUSED_PROJ_EINVAL;
     if ((d->n_heads > 0) != (d->head_dim > 0)) return FUSED_PROJ_EINVAL;
     if (d->x_layout == FUSED_PROJ_X_TOKENS_LAST ? d->n_spatial != 1 : (d->n_spatial < 1 || d->n_spatial > 3))
@@ -170,10 +172,9 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
         return FUSED_PROJ_EHIP;
     }
     // Kernel choice. The fast bf16 kernel needs a RoPE head size of 32, 64 or 128 (or no
-    // RoPE) and x and W spans under 4 GiB (it addresses them with 32-bit offsets). With
-    // its large tiles it is used only on exact tilings; with its small tiles (chosen when
-    // the large ones cannot fill the CUs) on whole token tiles. Every other shape goes to
-    // the general kernel.
+    // RoPE) and x and W spans under 4 GiB (it addresses them with 32-bit offsets). It takes
+    // whole token tiles; with its large tiles also whole groups of K steps. Every other
+    // shape goes to the general kernel.
     // FUSED_PROJ_KERNEL=general forces the general kernel (the tests use it to cover both);
     // FUSED_PROJ_KERNEL=fast takes the fast kernel on any shape it can address.
     const char* force = std::getenv("FUSED_PROJ_KERNEL");
@@ -183,13 +184,19 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     const bool fits32 = r.x_span * 2 < (int64_t(1) << 32) && desc->channels * r.F * 2 < (int64_t(1) << 32);
     const fp::TilePlan fp_plan = fp::fast_plan(r.M, r.F, num_cus);
     const bool large = fp_plan.bn == 256;
-    // large tiles: exact tilings only; small tiles (too few large tiles to fill the CUs):
-    // whole token tiles, any column count (ragged last column tile) and any K (partial and
-    // padding K steps read zeros)
+    // Both tile shapes take any column count: columns past F in the last column tile read
+    // row 0 of W and the zero block for the bias, and are neither computed into an output
+    // nor stored. Large tiles take C in whole groups of K steps; small tiles (too few large
+    // tiles to fill the CUs) any C (partial K steps read zeros).
     const bool exact = desc->channels > 0 && r.M % fp_plan.bm == 0 &&
-                       (!large || (r.F % fp_plan.bn == 0 && desc->channels % fp::fast_k_multiple() == 0));
+                       (!large || desc->channels % fp::fast_k_multiple() == 0);
     const bool addressable = fp::fast_addressable(r.M, r.S, desc->ff_dim, r.qw);
-    h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && addressable && (exact || want_fast) && !want_general;
+    // the fast kernel's epilogue applies exact-erf GELU or nothing: other activations take
+    // the general kernel, even when the fast one is forced
+    const bool fast_act = desc->ff_dim == 0 || desc->ff_act == FUSED_PROJ_ACT_NONE ||
+                          desc->ff_act == FUSED_PROJ_ACT_GELU_ERF;
+    h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && addressable && fast_act && (exact || want_fast) &&
+              !want_general;
     h->dg = dg < 0 ? 0 : dg;
     h->tile = h->fast ? fp_plan : fp::TilePlan{128, 128, h->dt == fp::DType::BF16 ? 64 : 32, 8, 0};
 
@@ -206,7 +213,10 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     a.n_heads = (int32_t)desc->n_heads;
     a.head_dim = (int32_t)desc->head_dim;
     a.qw = (int32_t)r.qw;
-    a.act = desc->ff_act == FUSED_PROJ_ACT_GELU_ERF ? 1 : 0;
+    a.act = desc->ff_act == FUSED_PROJ_ACT_GELU_ERF      ? 1
+            : desc->ff_act == FUSED_PROJ_ACT_GELU_TANH     ? 2
+            : desc->ff_act == FUSED_PROJ_ACT_RELU_SQUARED ? 3
+                                                           : 0;
     a.rope = (desc->rope && r.qw > 0) ? 1 : 0;
     a.tiles_m = (int32_t)((r.M + h->tile.bm - 1) / h->tile.bm);  // token tiles
     a.tiles_n = (int32_t)((r.F + h->tile.bn - 1) / h->tile.bn);

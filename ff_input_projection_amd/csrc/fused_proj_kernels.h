@@ -48,7 +48,7 @@ struct KernelArgs {
     int32_t n_heads;
     int32_t head_dim;
     int32_t qw;          // n_heads * head_dim
-    int32_t act;         // 0 none, 1 exact-erf GELU on the ff slice
+    int32_t act;         // ff slice: 0 none, 1 exact-erf GELU, 2 tanh GELU, 3 squared ReLU
     int32_t rope;        // 1: RoPE on q and k
     int32_t tiles_m;
     int32_t tiles_n;

@@ -187,6 +187,8 @@ __device__ __forceinline__ float fetch_f32(const float* tile, int rb, int kk, in
 
 // ---------------------------------------------------------------- epilogue helpers
 using dev::gelu_erf;
+using dev::gelu_tanh;
+using dev::relu_squared;
 using dev::tile_coords;
 
 // 16-byte output stores, non-temporal: every output is written once and not read here.
@@ -345,6 +347,12 @@ __global__ __launch_bounds__(kThreads, 2) void fused_proj_tile_kernel(KernelArgs
             if (p.act == 1) {
 #pragma unroll
                 for (int e = 0; e < OV; ++e) y[e] = gelu_erf(y[e]);
+            } else if (p.act == 2) {
+#pragma unroll
+                for (int e = 0; e < OV; ++e) y[e] = gelu_tanh(y[e]);
+            } else if (p.act == 3) {
+#pragma unroll
+                for (int e = 0; e < OV; ++e) y[e] = relu_squared(y[e]);
             }
             store16<T>(dst + (int64_t)m * p.ff_dim + f0, y);
         } else {

@@ -36,7 +36,7 @@ class Workload:
     layout: str             # "channels_first" ([b,c,spatial...]) or "tokens_last" ([b,s,c])
     x_shape: tuple
     ff_dim: int
-    ff_act: str             # "gelu" or "none"
+    ff_act: str             # "none", "gelu" (exact erf), "gelu_tanh" or "relu2" (squared ReLU)
     n_heads: int
     head_dim: int
     has_bias: bool
@@ -107,6 +107,15 @@ WORKLOADS = {
                  description="decoder QKV+RoPE bf16: x [2,4096,4096], W [4096,12288], 3 x [64,4096,128]"),
         Workload("smallk_qkv_bf16", "bf16", "channels_first", (2, 320, 64, 64), 0, "none", 5, 64, False, False, 5,
                  description="small-K bf16: x [2,320,64,64] channels-first, W [320,960], 3 x [10,4096,64]"),
+        # BERT-base FF with squared ReLU (an activation the xformers PR discussion names)
+        Workload("bert_ff_relu2_bf16", "bf16", "tokens_last", (32, 512, 768), 3072, "relu2", 0, 0, True, False, 7,
+                 description="BERT-base FF bf16 with squared ReLU: x [32,512,768], W [768,3072]"),
+        # The Walrus block at the width its profiles imply (C = 1408, F = 7C: FF 4C and
+        # Q/K/V C each): F is not a multiple of 256, so the last large column tile is ragged.
+        Workload("walrus_c1408_bf16", "bf16", "channels_first", (24, 1408, 32, 32, 1), 5632, "gelu", 22, 64, True,
+                 True, 6,
+                 description="Walrus block at width 1408 bf16: x [24,1408,32,32,1] (4 x 6 steps), W [1408,9856], "
+                             "FF 5632 GELU, Q/K/V 22x64, RoPE"),
     ]
 }
 

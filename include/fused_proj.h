@@ -13,7 +13,7 @@
  *   into an ff slice [0, ff_dim), then q, k and v slices of n_heads*head_dim
  *   columns each (head h, element j at slice column h*head_dim + j):
  *
- *     ff[bi, s, f]            = act(y[t, f])                    act: none | exact-erf GELU
+ *     ff[bi, s, f]            = act(y[t, f])                    act: see FUSED_PROJ_ACT_*
  *     q[bi*H + h, s, j]       = RoPE_p(y[t, Q0 + h*hd + .])[j]  p = s + pos_offset
  *     k[bi*H + h, s, j]       = RoPE_p(y[t, K0 + h*hd + .])[j]
  *     v[bi*H + h, s, j]       = y[t, V0 + h*hd + j]
@@ -78,6 +78,13 @@ extern "C" {
 /* Activation on the ff slice. */
 #define FUSED_PROJ_ACT_NONE 0
 #define FUSED_PROJ_ACT_GELU_ERF 1 /* 0.5 y (1 + erf(y / sqrt 2)) */
+/* 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))): the tanh form of GELU from the paper that
+ * defines GELU (Hendrycks and Gimpel, "Gaussian Error Linear Units (GELUs)", 2016). */
+#define FUSED_PROJ_ACT_GELU_TANH 2
+/* max(y, 0)^2: squared ReLU, which the xformers PR "Fused linear: small FW cleanup and much
+ * better perfs" discussion names among the activations a fused linear layer handles
+ * natively. Both run on the general kernel (128 x 128 tiles) for now. */
+#define FUSED_PROJ_ACT_RELU_SQUARED 3
 
 typedef struct fused_proj_desc {
     int32_t dtype;             /* FUSED_PROJ_BF16 | FUSED_PROJ_F32 */

@@ -73,7 +73,7 @@ def verdict(wl: Workload, inp, outs, tokens: np.ndarray) -> cmp.Verdict:
     rows, pos = cmp.token_rows(inp.x64, wl.layout, tokens)
     w_cf = inp.w64 if wl.w_layout == "cf" else inp.w64.T
     sc = cmp.scales(rows, pos, w_cf, inp.bias64, wl.ff_dim, wl.n_heads, wl.head_dim, wl.rope, wl.rope_base,
-                    wl.pos_offset)
+                    wl.pos_offset, ff_act=wl.ff_act, ff_ref=ref[0])
     return cmp.compare(got, ref, [sc.ff, sc.q, sc.k, sc.v], wl.dtype)
 
 

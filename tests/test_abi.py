@@ -72,6 +72,12 @@ def test_validate_accepts_all_benchmark_workloads():
         assert fpa.validate(d) == fpa.OK, wl.name
 
 
+def test_validate_accepts_every_activation():
+    for act in ("none", "gelu", "gelu_tanh", "relu2"):
+        d = walrus_desc(ff_act=act)
+        assert fpa.validate(d) == fpa.OK, act
+
+
 @pytest.mark.parametrize("mutate,code", [
     (lambda d: setattr(d, "dtype", 7), fpa.EINVAL),
     (lambda d: setattr(d, "x_layout", 5), fpa.EINVAL),

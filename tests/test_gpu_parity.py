@@ -84,6 +84,16 @@ SMALL = [
                head_dim=64, seed=114),
     with_shape(WORKLOADS["smallk_qkv_bf16"], "cf_small_tiles_k224", x_shape=(2, 224, 8, 16), n_heads=2,
                seed=115),
+    # the other ff activations (general kernel): tanh GELU with RoPE on a token-major x, and
+    # squared ReLU on a shape the fast kernel's small tiles would take with exact GELU
+    with_shape(WORKLOADS["bert_ff_bf16"], "tl_gelu_tanh_rope", x_shape=(2, 70, 96), ff_dim=64,
+               ff_act="gelu_tanh", n_heads=2, head_dim=32, rope=True, seed=117),
+    with_shape(WORKLOADS["walrus_bf16"], "cf_relu2", x_shape=(2, 72, 8, 16, 1), ff_dim=128, ff_act="relu2",
+               n_heads=2, head_dim=64, seed=118),
+    with_shape(WORKLOADS["tiny_f32"], "f32_tl_gelu_tanh", layout="tokens_last", x_shape=(2, 40, 48), ff_dim=32,
+               ff_act="gelu_tanh", n_heads=2, head_dim=8, seed=119),
+    with_shape(WORKLOADS["tiny_f32"], "f32_cf_relu2", x_shape=(1, 40, 8, 8, 1), ff_dim=64, ff_act="relu2",
+               n_heads=2, head_dim=8, seed=120),
     # fp32, token-major, [F,C], RoPE hd 8, GELU
     with_shape(WORKLOADS["tiny_f32"], "f32_tl_fc", layout="tokens_last", x_shape=(3, 50, 36), ff_dim=16,
                n_heads=3, head_dim=8, w_layout="fc", seed=106),
@@ -124,6 +134,19 @@ def test_fast_kernel_on_padded_or_ragged_tiling(monkeypatch):
     _check(wl, inp, outs, sample_tokens(wl, 384, seed=1), wl.name)
 
 
+def test_other_activations_never_take_the_fast_kernel(monkeypatch):
+    """The fast kernel applies exact-erf GELU or nothing; forcing it with tanh GELU or
+    squared ReLU must still plan the general kernel (and give the oracle's results)."""
+    monkeypatch.setenv("FUSED_PROJ_KERNEL", "fast")
+    for act in ("gelu_tanh", "relu2"):
+        wl = with_shape(WORKLOADS["walrus_bf16"], f"forced_{act}", x_shape=(2, 64, 8, 16, 1), ff_dim=64,
+                        ff_act=act, n_heads=2, head_dim=64, seed=121)
+        inp = make_inputs(wl)
+        proj, outs = run_gpu(wl, inp, DEV)
+        assert "fused_proj_tile_kernel" in proj.describe(), proj.describe()
+        _check(wl, inp, outs, all_tokens(wl), wl.name)
+
+
 LARGE_FC = [
     # [F,C] weights (nn.Linear layout) on the large tiles, both x layouts: 8192 tokens,
     # C = 256, F = 1024 + 3 * 512 = 2560 (320 tiles of 256 x 256), RoPE hd 64, GELU
@@ -134,10 +157,18 @@ LARGE_FC = [
 ]
 
 
+LARGE_FC += [
+    # large tiles with a ragged last column tile: F = 1152 + 3 * 256 = 1920 (7.5 column
+    # tiles of 256), 16384 tokens (64 x 8 = 512 tiles), RoPE hd 64, GELU, [C,F] weight
+    with_shape(WORKLOADS["walrus_bf16"], "cf_large_tiles_ragged_f", x_shape=(16, 256, 32, 32, 1), ff_dim=1152,
+               n_heads=4, head_dim=64, seed=116),
+]
+
+
 @pytest.mark.parametrize("wl", LARGE_FC, ids=[w.name for w in LARGE_FC])
 def test_large_tiles_with_fc_weights(wl):
     """The fast kernel's large-tile instantiations that read W as [F,C] (K-contiguous
-    rows): none of the named workloads uses them."""
+    rows), which none of the named workloads uses, and a ragged last column tile."""
     print(f"[case] large tiles, [F,C] weight: {wl.name} x={wl.x_shape}", flush=True)
     inp = make_inputs(wl)
     proj, outs = run_gpu(wl, inp, DEV)
