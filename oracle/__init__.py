@@ -56,6 +56,7 @@ def _load():
             d, i64, i64, i64, i64, i64, ctypes.c_int, p64, p64,
             d, i64, ctypes.c_int, d,
             i64, ctypes.c_int, i64, i64,
+            i64, ctypes.c_int, i64,
             ctypes.c_int, ctypes.c_double, i64,
             p64, i64, d, d, d, d, ctypes.c_int,
         ]
@@ -70,8 +71,8 @@ def max_threads() -> int:
 
 @dataclass
 class OracleResult:
-    """Outputs in float64. Full runs: ff [nb, S, FF], q/k/v [nb*H, S, hd].
-    Token-subset runs: ff [ntok, FF], q/k/v [ntok, H, hd] (token-major)."""
+    """Outputs in float64. Full runs: ff [nb, S, FF], q [nb*H, S, hd], k/v [nb*KVH, S, hd].
+    Token-subset runs: ff [ntok, FF], q [ntok, H, hd], k/v [ntok, KVH, hd] (token-major)."""
     ff: np.ndarray | None
     q: np.ndarray | None
     k: np.ndarray | None
@@ -87,7 +88,8 @@ def _dptr(a: np.ndarray | None):
 def fused_proj(x: np.ndarray, layout: str, w: np.ndarray, w_layout: str, bias: np.ndarray | None,
                ff_dim: int, ff_act: str, n_heads: int, head_dim: int, rope: bool,
                rope_base: float = 10000.0, pos_offset: int = 0, tokens: np.ndarray | None = None,
-               nthreads: int = 0) -> OracleResult:
+               nthreads: int = 0, n_kv_heads: int = 0, qkv_order: str = "contiguous",
+               rope_dims: int = 0) -> OracleResult:
     """Float64 fused projection.
 
     x: float64 array, ``layout`` "channels_first" ([b,c,h,w,d] or [b,c,s...]:
@@ -96,6 +98,9 @@ def fused_proj(x: np.ndarray, layout: str, w: np.ndarray, w_layout: str, bias: n
     w: float64 [C,F] (w_layout "cf") or [F,C] (w_layout "fc").
     tokens: None for every token (full layouts returned) or an int64 array of
        global token indices bi*S + s (token-major rows returned).
+    n_kv_heads: k/v heads (0: n_heads); qkv_order: "contiguous" ([q | k | v]) or
+       "grouped" (per k/v head: its q heads, then k, then v); rope_dims: rotated
+       width of each q/k head (0: head_dim).
     """
     lib = _load()
     x = np.asarray(x)
@@ -139,31 +144,34 @@ def fused_proj(x: np.ndarray, layout: str, w: np.ndarray, w_layout: str, bias: n
         tokens = np.arange(nb * S, dtype=np.int64)
     tokens = np.ascontiguousarray(tokens, dtype=np.int64)
     ntok = tokens.shape[0]
-    qw = n_heads * head_dim
+    kvh = n_kv_heads if n_kv_heads > 0 else n_heads
+    grouped = {"contiguous": 0, "grouped": 1}[qkv_order]
+    qw, kvw = n_heads * head_dim, kvh * head_dim
     ff_rows = np.empty((ntok, ff_dim)) if ff_dim > 0 else None
     q_rows = np.empty((ntok, qw)) if qw > 0 else None
-    k_rows = np.empty((ntok, qw)) if qw > 0 else None
-    v_rows = np.empty((ntok, qw)) if qw > 0 else None
+    k_rows = np.empty((ntok, kvw)) if qw > 0 else None
+    v_rows = np.empty((ntok, kvw)) if qw > 0 else None
     spz = (ctypes.c_int64 * len(sp))(*sp)
     sps = (ctypes.c_int64 * len(sp))(*sp_stride)
     act = ACTIVATIONS[ff_act]
     rc = lib.oracle_fused_proj(
         x.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), nb, C, S, sb, sc, len(sp), spz, sps,
         _dptr(w), F, w_fc, _dptr(bias),
-        ff_dim, act, n_heads, head_dim, int(bool(rope)), float(rope_base), int(pos_offset),
+        ff_dim, act, n_heads, head_dim, int(n_kv_heads), grouped, int(rope_dims),
+        int(bool(rope)), float(rope_base), int(pos_offset),
         tokens.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ntok,
         _dptr(ff_rows), _dptr(q_rows), _dptr(k_rows), _dptr(v_rows), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")
     if not full:
-        rs = (lambda a: None if a is None else a.reshape(ntok, n_heads, head_dim))
-        return OracleResult(ff_rows, rs(q_rows), rs(k_rows), rs(v_rows))
+        rs = (lambda a, h: None if a is None else a.reshape(ntok, h, head_dim))
+        return OracleResult(ff_rows, rs(q_rows, n_heads), rs(k_rows, kvh), rs(v_rows, kvh))
 
-    def head_major(a):
+    def head_major(a, h):
         if a is None:
             return None
         # [b, S, H, hd] -> [b, H, S, hd] -> [b*H, S, hd]
-        return a.reshape(nb, S, n_heads, head_dim).transpose(0, 2, 1, 3).reshape(nb * n_heads, S, head_dim)
+        return a.reshape(nb, S, h, head_dim).transpose(0, 2, 1, 3).reshape(nb * h, S, head_dim)
 
     ff = None if ff_rows is None else ff_rows.reshape(nb, S, ff_dim)
-    return OracleResult(ff, head_major(q_rows), head_major(k_rows), head_major(v_rows))
+    return OracleResult(ff, head_major(q_rows, n_heads), head_major(k_rows, kvh), head_major(v_rows, kvh))

@@ -11,7 +11,9 @@ same mix of biases), since RoPE is linear; its norm is used. For GELU outputs
 (either form) the pre-activation scale is used (both are under 1.13-Lipschitz).
 Squared ReLU doubles an input error by |y| at y: its outputs o use the
 pre-activation scale times (1 + 2 sqrt(o)), which bounds
-|d(y^2)| <= 2|y||dy| + dy^2 while |dy| <= 1.
+|d(y^2)| <= 2|y||dy| + dy^2 while |dy| <= 1. With fewer k/v heads, the grouped
+column order or partial rotary, the scales follow the column map of qkv_columns,
+and RoPE mixes only the rotated width.
 
 A second, tighter diagnostic bar is also reported for bf16: the output's own
 rounding (2^-8 relative) plus 1e-4 * scale of accumulation error.
@@ -49,11 +51,34 @@ class Scales:
     v: np.ndarray | None
 
 
+def qkv_columns(ff_dim: int, n_heads: int, head_dim: int, n_kv_heads: int = 0, qkv_order: str = "contiguous"):
+    """Fused column of every q/k/v output element: three int arrays [heads, head_dim]
+    (q with n_heads heads, k and v with n_kv_heads), following the contiguous
+    [q | k | v] order or the grouped order (per k/v head: its q heads, then k, then v)."""
+    kvh = n_kv_heads if n_kv_heads > 0 else n_heads
+    j = np.arange(head_dim)
+    if qkv_order == "contiguous":
+        q = ff_dim + np.arange(n_heads)[:, None] * head_dim + j
+        k = ff_dim + n_heads * head_dim + np.arange(kvh)[:, None] * head_dim + j
+        v = k + kvh * head_dim
+        return q, k, v
+    qpk = n_heads // kvh
+    gw = (qpk + 2) * head_dim
+    h = np.arange(n_heads)
+    q = ff_dim + (h // qpk)[:, None] * gw + (h % qpk)[:, None] * head_dim + j
+    g = np.arange(kvh)[:, None]
+    k = ff_dim + g * gw + qpk * head_dim + j
+    return q, k, k + head_dim
+
+
 def scales(rows: np.ndarray, positions: np.ndarray, w_cf: np.ndarray, bias: np.ndarray | None, ff_dim: int,
            n_heads: int, head_dim: int, rope: bool, rope_base: float = 10000.0, pos_offset: int = 0,
-           ff_act: str = "none", ff_ref: np.ndarray | None = None) -> Scales:
+           ff_act: str = "none", ff_ref: np.ndarray | None = None, n_kv_heads: int = 0,
+           qkv_order: str = "contiguous", rope_dims: int = 0) -> Scales:
     """Per-element scale for tokens with gathered rows [n, C]; w_cf is W as [C, F].
-    For ff_act "relu2" the oracle's ff outputs ff_ref [n, FF] are needed."""
+    For ff_act "relu2" the oracle's ff outputs ff_ref [n, FF] are needed. q is
+    [n, H, hd], k and v [n, KVH, hd]; RoPE mixes the first rope_dims (0: head_dim)
+    elements of each q/k head."""
     n = rows.shape[0]
     F = w_cf.shape[1]
     xn = np.linalg.norm(rows, axis=1)                         # [n]
@@ -65,31 +90,30 @@ def scales(rows: np.ndarray, positions: np.ndarray, w_cf: np.ndarray, bias: np.n
         if ff_ref is None:
             raise ValueError("squared ReLU scales need the oracle's ff outputs")
         ff = ff * (1.0 + 2.0 * np.sqrt(np.maximum(np.asarray(ff_ref, dtype=np.float64).reshape(ff.shape), 0.0)))
-    qw = n_heads * head_dim
-    if qw == 0:
+    if n_heads * head_dim == 0:
         return Scales(ff, None, None, None)
+    R = rope_dims if rope_dims > 0 else head_dim
+    half = R // 2
     out = []
-    for which in range(3):
-        off = ff_dim + which * qw
-        s_plain = plain[:, off:off + qw].reshape(n, n_heads, head_dim)
+    for which, cols in enumerate(qkv_columns(ff_dim, n_heads, head_dim, n_kv_heads, qkv_order)):
+        s_plain = plain[:, cols]                               # [n, heads, hd]
         if not (rope and which < 2):
             out.append(s_plain)
             continue
-        half = head_dim // 2
-        Wh = w_cf[:, off:off + qw].reshape(-1, n_heads, head_dim)
-        bh = b[off:off + qw].reshape(n_heads, head_dim)
-        w1, w2 = Wh[:, :, :half], Wh[:, :, half:]             # [C, H, half]
-        n1, n2 = (w1 ** 2).sum(0), (w2 ** 2).sum(0)            # [H, half]
+        Wh = w_cf[:, cols]                                     # [C, heads, hd]
+        bh = b[cols]                                           # [heads, hd]
+        w1, w2 = Wh[:, :, :half], Wh[:, :, half:R]             # [C, heads, half]
+        n1, n2 = (w1 ** 2).sum(0), (w2 ** 2).sum(0)            # [heads, half]
         d12 = (w1 * w2).sum(0)
-        theta = rope_base ** (-2.0 * np.arange(half) / head_dim)
+        theta = rope_base ** (-2.0 * np.arange(half) / R)
         phi = (positions.astype(np.float64) + pos_offset)[:, None] * theta[None, :]   # [n, half]
         c, s = np.cos(phi)[:, None, :], np.sin(phi)[:, None, :]                     # [n, 1, half]
         # first half: c w1 - s w2 ; second half: c w2 + s w1
         e1 = np.sqrt(np.maximum(c * c * n1 + s * s * n2 - 2 * c * s * d12, 0.0))
         e2 = np.sqrt(np.maximum(c * c * n2 + s * s * n1 + 2 * c * s * d12, 0.0))
-        b1 = np.abs(c * bh[None, :, :half] - s * bh[None, :, half:])
-        b2 = np.abs(c * bh[None, :, half:] + s * bh[None, :, :half])
-        sc = np.concatenate([xn[:, None, None] * e1 + b1, xn[:, None, None] * e2 + b2], axis=2)
+        b1 = np.abs(c * bh[None, :, :half] - s * bh[None, :, half:R])
+        b2 = np.abs(c * bh[None, :, half:R] + s * bh[None, :, :half])
+        sc = np.concatenate([xn[:, None, None] * e1 + b1, xn[:, None, None] * e2 + b2, s_plain[:, :, R:]], axis=2)
         out.append(sc)
     return Scales(ff, out[0], out[1], out[2])
 

@@ -111,17 +111,54 @@ static double activate(int ff_act, double y)
     }
 }
 
-/* Rotate-half RoPE of one head vector v[0..hd) at position p, in place. */
-static void rope_rotate_half(double *v, int64_t hd, double p, double base)
+/* Rotate-half RoPE on the first rd elements of one head vector v at position p, in
+ * place (rd even; rd equal to the head size is the full rotation). Elements from rd on
+ * are left as they are (partial rotary, rope_one_entry with rope_n_elem in the nvFuser
+ * RoPE issue: the angles belong to the rotated width rd). */
+static void rope_rotate_half(double *v, int64_t rd, double p, double base)
 {
-    int64_t half = hd / 2;
+    int64_t half = rd / 2;
     for (int64_t i = 0; i < half; ++i) {
-        double theta = pow(base, -2.0 * (double)i / (double)hd);
+        double theta = pow(base, -2.0 * (double)i / (double)rd);
         double phi = p * theta;
         double cs = cos(phi), sn = sin(phi);
         double x1 = v[i], x2 = v[i + half];
         v[i] = x1 * cs - x2 * sn;        /* x1*cos + (-x2)*sin */
         v[i + half] = x2 * cs + x1 * sn; /* x2*cos + ( x1)*sin */
+    }
+}
+
+/* Destination of column r of the q/k/v part of the fused output (column ff_dim + r):
+ * which (0 q, 1 k, 2 v), head and element j. Contiguous order: all q heads, then the k
+ * heads, then the v heads. Grouped order (split_qkv in the nvFuser RoPE issue, the
+ * lit-gpt layout): n_kv groups of q_per_kv q heads, one k head and one v head; q head i
+ * of group g is head g*q_per_kv + i. */
+static void qkv_column(int64_t r, int64_t n_heads, int64_t n_kv, int64_t hd, int grouped, int *which,
+                       int64_t *head, int64_t *j)
+{
+    *j = r % hd;
+    if (!grouped) {
+        const int64_t qw = n_heads * hd, kvw = n_kv * hd;
+        if (r < qw) {
+            *which = 0;
+            *head = r / hd;
+        } else if (r < qw + kvw) {
+            *which = 1;
+            *head = (r - qw) / hd;
+        } else {
+            *which = 2;
+            *head = (r - qw - kvw) / hd;
+        }
+    } else {
+        const int64_t qpk = n_heads / n_kv, gw = (qpk + 2) * hd;
+        const int64_t g = r / gw, slot = (r % gw) / hd;
+        if (slot < qpk) {
+            *which = 0;
+            *head = g * qpk + slot;
+        } else {
+            *which = slot == qpk ? 1 : 2;
+            *head = g;
+        }
     }
 }
 
@@ -136,10 +173,14 @@ static void rope_rotate_half(double *v, int64_t hd, double p, double base)
  *   ff_dim   width of the ff slice; F = ff_dim + 3*n_heads*head_dim
  *   ff_act   activation on the ff slice: 0 identity, 1 exact-erf GELU,
  *            2 tanh GELU, 3 squared ReLU
- *   rope     1: rotate-half RoPE on q and k (head_dim must be even)
+ *   n_kv     k and v heads (0: n_heads); must divide n_heads
+ *   grouped  0: q/k/v columns in contiguous order, 1: grouped per k/v head
+ *   rope_dims rotated width of each q and k head (0: head_dim); even
+ *   rope     1: rotate-half RoPE on q and k
  *   tokens   global token indices t = bi*S + s, each in [0, nb*S)
  *   outputs  token-major rows: ff_rows [ntok, ff_dim],
- *            q_rows/k_rows/v_rows [ntok, n_heads*head_dim]; any may be NULL
+ *            q_rows [ntok, n_heads*head_dim], k_rows/v_rows
+ *            [ntok, n_kv*head_dim]; any may be NULL
  *            when its slice is empty.
  *   nthreads OpenMP threads (<= 0: runtime default)
  * Returns 0, or -1 on an invalid argument (nothing is written then).
@@ -148,6 +189,7 @@ int oracle_fused_proj(const double *x, int64_t nb, int64_t C, int64_t S, int64_t
                       int nsp, const int64_t *sp_size, const int64_t *sp_stride,
                       const double *w, int64_t F, int w_fc, const double *bias,
                       int64_t ff_dim, int ff_act, int64_t n_heads, int64_t head_dim,
+                      int64_t n_kv, int grouped, int64_t rope_dims,
                       int rope, double rope_base, int64_t pos_offset,
                       const int64_t *tokens, int64_t ntok,
                       double *ff_rows, double *q_rows, double *k_rows, double *v_rows,
@@ -163,9 +205,13 @@ int oracle_fused_proj(const double *x, int64_t nb, int64_t C, int64_t S, int64_t
     if (prod != S) return ORACLE_EINVAL;
     if (ff_dim < 0 || n_heads < 0 || head_dim < 0) return ORACLE_EINVAL;
     if (ff_act < 0 || ff_act > 3) return ORACLE_EINVAL;
-    const int64_t qw = n_heads * head_dim;
-    if (F != ff_dim + 3 * qw || F <= 0) return ORACLE_EINVAL;
-    if (rope && (head_dim % 2 != 0)) return ORACLE_EINVAL;
+    if (n_kv == 0) n_kv = n_heads;
+    if (n_kv < 0 || (n_heads > 0 && (n_kv == 0 || n_heads % n_kv != 0)) || (grouped != 0 && grouped != 1))
+        return ORACLE_EINVAL;
+    const int64_t qw = n_heads * head_dim, kvw = n_kv * head_dim;
+    if (F != ff_dim + qw + 2 * kvw || F <= 0) return ORACLE_EINVAL;
+    const int64_t rd = rope_dims > 0 ? rope_dims : head_dim;
+    if (rope && (rd % 2 != 0 || rd > head_dim)) return ORACLE_EINVAL;
     if (ff_dim > 0 && !ff_rows) return ORACLE_EINVAL;
     if (qw > 0 && (!q_rows || !k_rows || !v_rows)) return ORACLE_EINVAL;
     for (int64_t i = 0; i < ntok; ++i)
@@ -217,15 +263,16 @@ int oracle_fused_proj(const double *x, int64_t nb, int64_t C, int64_t S, int64_t
                 ff_rows[i * ff_dim + f] = activate(ff_act, y[f]);
             /* 3+6. q, k, v slices; RoPE on q and k per head */
             if (qw > 0) {
-                double *dst[3] = {q_rows + i * qw, k_rows + i * qw, v_rows + i * qw};
-                for (int which = 0; which < 3; ++which) {
-                    const double *src = y + ff_dim + which * qw;
-                    for (int64_t e = 0; e < qw; ++e) dst[which][e] = src[e];
-                    if (rope && which < 2)
-                        for (int64_t h = 0; h < n_heads; ++h)
-                            rope_rotate_half(dst[which] + h * head_dim, head_dim,
-                                             (double)(s + pos_offset), rope_base);
+                double *dst[3] = {q_rows + i * qw, k_rows + i * kvw, v_rows + i * kvw};
+                for (int64_t r = 0; r < qw + 2 * kvw; ++r) {
+                    int which;
+                    int64_t head, j;
+                    qkv_column(r, n_heads, n_kv, head_dim, grouped, &which, &head, &j);
+                    dst[which][head * head_dim + j] = y[ff_dim + r];
                 }
+                for (int which = 0; rope && which < 2; ++which)
+                    for (int64_t h = 0; h < (which == 0 ? n_heads : n_kv); ++h)
+                        rope_rotate_half(dst[which] + h * head_dim, rd, (double)(s + pos_offset), rope_base);
             }
         }
         free(y);

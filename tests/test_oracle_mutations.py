@@ -18,17 +18,21 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 MUTATIONS = [
     ("RoPE first-half sign", "v[i] = x1 * cs - x2 * sn;", "v[i] = x1 * cs + x2 * sn;"),
     ("RoPE second-half sign", "v[i + half] = x2 * cs + x1 * sn;", "v[i + half] = x2 * cs - x1 * sn;"),
-    ("RoPE frequency exponent", "pow(base, -2.0 * (double)i / (double)hd)", "pow(base, -(double)i / (double)hd)"),
+    ("RoPE frequency exponent", "pow(base, -2.0 * (double)i / (double)rd)", "pow(base, -(double)i / (double)rd)"),
     ("RoPE interleaved pairs", "double x1 = v[i], x2 = v[i + half];", "double x1 = v[2 * i], x2 = v[2 * i + 1];"),
     ("RoPE global token position", "(double)(s + pos_offset)", "(double)(t + pos_offset)"),
     ("RoPE ignores pos_offset", "(double)(s + pos_offset)", "(double)(s)"),
-    ("RoPE applied to v", "if (rope && which < 2)", "if (rope && which < 3)"),
+    ("RoPE applied to v", "rope && which < 2;", "rope && which < 3;"),
     ("dropped last channel", "for (int64_t c = 0; c < C; ++c) {\n                    const double xc",
      "for (int64_t c = 0; c < C - 1; ++c) {\n                    const double xc"),
     ("[F,C] weight read as [C,F]", "return w_fc ? w[f * C + c] : w[c * F + f];",
      "return w_fc ? w[c * F + f] : w[c * F + f];"),
-    ("q and k slices swapped", "const double *src = y + ff_dim + which * qw;",
-     "const double *src = y + ff_dim + (which == 0 ? 1 : which == 1 ? 0 : 2) * qw;"),
+    ("q and k slices swapped", "            *which = 0;\n            *head = r / hd;",
+     "            *which = 1;\n            *head = r / hd;"),
+    ("grouped order: k and v slots swapped", "*which = slot == qpk ? 1 : 2;", "*which = slot == qpk ? 2 : 1;"),
+    ("grouped order: q heads numbered across groups", "*head = g * qpk + slot;", "*head = slot * n_kv + g;"),
+    ("partial RoPE rotates the whole head", "rope_rotate_half(dst[which] + h * head_dim, rd,",
+     "rope_rotate_half(dst[which] + h * head_dim, head_dim,"),
     ("tanh GELU", "return 0.5 * y * (1.0 + erf(y / sqrt(2.0)));",
      "return 0.5 * y * (1.0 + tanh(0.7978845608028654 * (y + 0.044715 * y * y * y)));"),
     ("tanh GELU constant", "0.044715 * y * y * y", "0.04715 * y * y * y"),

@@ -254,6 +254,98 @@ def test_activation_applies_to_the_ff_slice_only():
                            rtol=0, atol=1e-15)
 
 
+# --------------------------------------------------------------------------- grouped q/k/v (GQA)
+
+def _head_major(a, nb, S, H, hd):
+    """[nb*S, H*hd] token-major rows -> [nb*H, S, hd] (numpy reshape/transpose)."""
+    return a.reshape(nb, S, H, hd).transpose(0, 2, 1, 3).reshape(nb * H, S, hd)
+
+
+def test_grouped_order_matches_pages_split_qkv():
+    """The grouped q/k/v order against the nvFuser RoPE issue's split_qkv written with
+    numpy: view the fused output as [B, T, groups, q_per_kv + 2, hs], move groups and
+    slots ahead of T, take q_per_kv q heads, one k and one v head per group (k and v not
+    expanded). Catches swapped k/v slots and q heads numbered across groups."""
+    B, T, C, H, G, hd = 2, 5, 12, 4, 2, 4
+    F = (H + 2 * G) * hd
+    x, w, _ = rng_inputs(31, (B, T, C), C, F, bias=False)
+    res = oracle.fused_proj(x, "tokens_last", w, "cf", None, 0, "none", H, hd, rope=False, n_kv_heads=G,
+                            qkv_order="grouped")
+    y = (x.reshape(-1, C) @ w).reshape(B, T, G, H // G + 2, hd).transpose(0, 2, 3, 1, 4)  # [B, G, slot, T, hs]
+    q = y[:, :, : H // G].reshape(B * H, T, hd)
+    k = y[:, :, H // G].reshape(B * G, T, hd)
+    v = y[:, :, H // G + 1].reshape(B * G, T, hd)
+    for got, ref in ((res.q, q), (res.k, k), (res.v, v)):
+        assert got.shape == ref.shape
+        assert np.allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_contiguous_gqa_slices():
+    """Contiguous order with fewer k/v heads: q is the first H*hd columns, k and v the
+    next two blocks of G*hd, each head-major. Catches k/v blocks sized by the q width."""
+    B, T, C, H, G, hd = 2, 6, 10, 6, 3, 4
+    F = 8 + (H + 2 * G) * hd
+    x, w, b = rng_inputs(32, (B, T, C), C, F)
+    res = oracle.fused_proj(x, "tokens_last", w, "cf", b, 8, "gelu", H, hd, rope=False, n_kv_heads=G)
+    y = x.reshape(-1, C) @ w + b
+    q0, k0 = 8, 8 + H * hd
+    v0 = k0 + G * hd
+    assert np.allclose(res.q, _head_major(y[:, q0:k0], B, T, H, hd), rtol=0, atol=1e-12)
+    assert np.allclose(res.k, _head_major(y[:, k0:v0], B, T, G, hd), rtol=0, atol=1e-12)
+    assert np.allclose(res.v, _head_major(y[:, v0:], B, T, G, hd), rtol=0, atol=1e-12)
+
+
+def test_partial_rope_matches_pages_rope_one_entry():
+    """Partial rotary on q and k against the nvFuser RoPE issue's rope_one_entry written
+    with numpy: rotate-half over the first rope_n_elem elements with cos/sin tables of that
+    width (the page's cat(cos, cos) layout), the rest passed through. The angles follow
+    base^(-2i/rope_n_elem) (the convention shared with the GPU path). Catches rotating the
+    whole head, pairs taken across the head instead of across the rotated width, and the
+    sign of the rotated half."""
+    B, T, C, H, G, hd, R = 1, 9, 8, 4, 2, 16, 8
+    F = (H + 2 * G) * hd
+    x, w, _ = rng_inputs(33, (B, T, C), C, F, bias=False)
+    kw = dict(n_kv_heads=G, qkv_order="grouped")
+    plain = oracle.fused_proj(x, "tokens_last", w, "cf", None, 0, "none", H, hd, rope=False, **kw)
+    roped = oracle.fused_proj(x, "tokens_last", w, "cf", None, 0, "none", H, hd, rope=True, rope_dims=R, **kw)
+    theta = 10000.0 ** (-2.0 * np.arange(R // 2) / R)
+    ang = np.arange(T)[:, None] * theta[None, :]                      # [T, R/2]
+    cos = np.concatenate([np.cos(ang), np.cos(ang)], axis=1)          # [T, R]
+    sin = np.concatenate([np.sin(ang), np.sin(ang)], axis=1)
+    for got, pre in ((roped.q, plain.q), (roped.k, plain.k)):
+        x_rope = pre[..., :R]
+        x1, x2 = x_rope[..., : R // 2], x_rope[..., R // 2:]
+        rotated = np.concatenate([-x2, x1], axis=-1)
+        ref = np.concatenate([x_rope * cos + rotated * sin, pre[..., R:]], axis=-1)
+        assert np.allclose(got, ref, rtol=0, atol=1e-12)
+        assert np.array_equal(got[..., R:], pre[..., R:])
+    assert np.array_equal(roped.v, plain.v)
+
+
+def test_comparison_column_map_matches_oracle():
+    """The parity bar's column map (oracle/compare.qkv_columns) picks, for every q/k/v
+    element, the fused column the oracle writes there (both orders, fewer k/v heads)."""
+    from oracle import compare as cmp
+    B, T, C, H, G, hd = 2, 4, 6, 4, 2, 4
+    for order in ("contiguous", "grouped"):
+        F = 8 + (H + 2 * G) * hd
+        x, w, _ = rng_inputs(35, (B, T, C), C, F, bias=False)
+        res = oracle.fused_proj(x, "tokens_last", w, "cf", None, 8, "none", H, hd, rope=False, n_kv_heads=G,
+                                qkv_order=order, tokens=np.arange(B * T))
+        y = x.reshape(-1, C) @ w
+        for got, cols in zip((res.q, res.k, res.v), cmp.qkv_columns(8, H, hd, G, order)):
+            assert np.allclose(got, y[:, cols], rtol=0, atol=1e-12)
+
+
+def test_full_width_rope_dims_equals_default():
+    """rope_dims = head_dim is the full rotation (the default)."""
+    x, w, b = rng_inputs(34, (2, 7, 8), 8, 3 * 2 * 8)
+    a = oracle.fused_proj(x, "tokens_last", w, "cf", b, 0, "none", 2, 8, rope=True)
+    c = oracle.fused_proj(x, "tokens_last", w, "cf", b, 0, "none", 2, 8, rope=True, rope_dims=8)
+    for u, v in ((a.q, c.q), (a.k, c.k), (a.v, c.v)):
+        assert np.array_equal(u, v)
+
+
 # --------------------------------------------------------------------------- RoPE
 
 def _rope_via_oracle(vec, p, base, which="q"):
