@@ -108,7 +108,8 @@ def main() -> int:
     proj = FusedProjection.for_tensor(xs[0], wl.layout, w_layout=wl.w_layout, has_bias=wl.has_bias,
                                       ff_dim=wl.ff_dim, ff_act=wl.ff_act, n_heads=wl.n_heads,
                                       head_dim=wl.head_dim, rope=wl.rope, rope_base=wl.rope_base,
-                                      pos_offset=wl.pos_offset)
+                                      pos_offset=wl.pos_offset, n_kv_heads=wl.n_kv_heads,
+                                      qkv_order=wl.qkv_order, rope_dims=wl.rope_dims)
     outs = [proj.alloc_outputs(dev) for _ in range(ring)]
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
@@ -179,6 +180,7 @@ def main() -> int:
         "data": "synthetic: seeded x ~ N(0,1), W ~ N(0,1/C), bias ~ N(0,0.02), rounded once to the storage type",
         "config": {"workload": wl.name, "x_shape": list(wl.x_shape), "layout": wl.layout, "C": wl.C, "F": wl.F,
                    "ff_dim": wl.ff_dim, "n_heads": wl.n_heads, "head_dim": wl.head_dim, "rope": wl.rope,
+                   "n_kv_heads": wl.kvh, "qkv_order": wl.qkv_order, "rope_dims": wl.rd if wl.rope else 0,
                    "bias": wl.has_bias, "tokens": wl.M, "w_layout": wl.w_layout, "ring": ring,
                    "graph": bool(graph is not None)},
         "gb_per_s": round(gbs, 1), "hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
@@ -199,7 +201,8 @@ def main() -> int:
             t = time.perf_counter()
             r = oracle.fused_proj(inp.x64, wl.layout, inp.w64, wl.w_layout, inp.bias64, wl.ff_dim, wl.ff_act,
                                   wl.n_heads, wl.head_dim, wl.rope, wl.rope_base, wl.pos_offset, tokens=tokens,
-                                  nthreads=cores)
+                                  nthreads=cores, n_kv_heads=wl.n_kv_heads, qkv_order=wl.qkv_order,
+                                  rope_dims=wl.rope_dims)
             return r, time.perf_counter() - t
 
         # calibrate on a probe large enough to amortise thread start-up, then size the sample
@@ -228,13 +231,14 @@ def main() -> int:
         bi = torch.from_numpy(tokens // wl.S).to(dev)
         si = torch.from_numpy(tokens % wl.S).to(dev)
         got = [None if ff is None else ff.view(wl.nb, wl.S, wl.ff_dim)[bi, si].double().cpu().numpy()]
-        for t in (q, k, v):
+        for t, heads in ((q, wl.n_heads), (k, wl.kvh), (v, wl.kvh)):
             got.append(None if t is None else
-                       t.view(wl.nb, wl.n_heads, wl.S, wl.head_dim)[bi, :, si].double().cpu().numpy())
+                       t.view(wl.nb, heads, wl.S, wl.head_dim)[bi, :, si].double().cpu().numpy())
         rows, pos = cmp.token_rows(inp.x64, wl.layout, tokens)
         w_cf = inp.w64 if wl.w_layout == "cf" else inp.w64.T
         sc = cmp.scales(rows, pos, w_cf, inp.bias64, wl.ff_dim, wl.n_heads, wl.head_dim, wl.rope, wl.rope_base,
-                        wl.pos_offset, ff_act=wl.ff_act, ff_ref=ref.ff)
+                        wl.pos_offset, ff_act=wl.ff_act, ff_ref=ref.ff, n_kv_heads=wl.n_kv_heads,
+                        qkv_order=wl.qkv_order, rope_dims=wl.rope_dims)
         vd = cmp.compare(got, [ref.ff, ref.q, ref.k, ref.v], [sc.ff, sc.q, sc.k, sc.v], wl.dtype)
         result["parity"] = {"ok": vd.ok, "max_err_over_tol": round(vd.max_ratio, 5),
                             "tight_ratio": round(vd.max_tight_ratio, 5), "elements": vd.n}

@@ -31,6 +31,7 @@ BF16, F32 = 0, 1
 X_CHANNELS_FIRST, X_TOKENS_LAST = 0, 1
 W_CF, W_FC = 0, 1
 ACT_NONE, ACT_GELU_ERF, ACT_GELU_TANH, ACT_RELU_SQUARED = 0, 1, 2, 3
+QKV_CONTIGUOUS, QKV_GROUPED = 0, 1
 
 
 class Desc(ctypes.Structure):
@@ -45,6 +46,7 @@ class Desc(ctypes.Structure):
         ("ff_dim", ctypes.c_int64), ("ff_act", ctypes.c_int32),
         ("n_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
         ("rope", ctypes.c_int32), ("rope_base", ctypes.c_double), ("pos_offset", ctypes.c_int64),
+        ("n_kv_heads", ctypes.c_int64), ("qkv_order", ctypes.c_int32), ("rope_dims", ctypes.c_int64),
     ]
 
 
@@ -109,7 +111,8 @@ _DTYPES = {torch.bfloat16: BF16, torch.float32: F32}
 
 def make_desc(x_shape, x_strides, layout: str, dtype: torch.dtype, *, w_layout: str = "cf",
               has_bias: bool = False, ff_dim: int = 0, ff_act: str = "none", n_heads: int = 0,
-              head_dim: int = 0, rope: bool = False, rope_base: float = 10000.0, pos_offset: int = 0) -> Desc:
+              head_dim: int = 0, rope: bool = False, rope_base: float = 10000.0, pos_offset: int = 0,
+              n_kv_heads: int = 0, qkv_order: str = "contiguous", rope_dims: int = 0) -> Desc:
     """Descriptor from an activation's shape and element strides.
     layout "channels_first": x [b, c, spatial...] (1-3 spatial dims);
     layout "tokens_last": x [b, s, c]."""
@@ -137,6 +140,9 @@ def make_desc(x_shape, x_strides, layout: str, dtype: torch.dtype, *, w_layout: 
     d.ff_act = {"none": ACT_NONE, "gelu": ACT_GELU_ERF, "gelu_tanh": ACT_GELU_TANH, "relu2": ACT_RELU_SQUARED}[ff_act]
     d.n_heads, d.head_dim = n_heads, head_dim
     d.rope, d.rope_base, d.pos_offset = int(bool(rope)), float(rope_base), pos_offset
+    d.n_kv_heads = n_kv_heads
+    d.qkv_order = {"contiguous": QKV_CONTIGUOUS, "grouped": QKV_GROUPED}[qkv_order]
+    d.rope_dims = rope_dims
     return d
 
 
@@ -165,7 +171,8 @@ class FusedProjection:
             self.S *= d.spatial[i]
         self.B, self.C = d.batch, d.channels
         self.H, self.hd, self.ff_dim = d.n_heads, d.head_dim, d.ff_dim
-        self.F = d.ff_dim + 3 * d.n_heads * d.head_dim
+        self.KVH = d.n_kv_heads if d.n_kv_heads > 0 else d.n_heads
+        self.F = d.ff_dim + (d.n_heads + 2 * self.KVH) * d.head_dim
         self.has_bias = bool(d.has_bias)
         h = ctypes.c_void_p()
         rc = self._lib.fused_proj_create(ctypes.byref(self.desc), ctypes.byref(h))
@@ -183,14 +190,16 @@ class FusedProjection:
         return buf.value.decode()
 
     def out_shapes(self):
+        """(ff, q, kv) shapes: ff [b, S, ff_dim], q [b*H, S, hd], k and v [b*KVH, S, hd]."""
         ff = (self.B, self.S, self.ff_dim) if self.ff_dim > 0 else None
-        qkv = (self.B * self.H, self.S, self.hd) if self.H * self.hd > 0 else None
-        return ff, qkv
+        q = (self.B * self.H, self.S, self.hd) if self.H * self.hd > 0 else None
+        kv = (self.B * self.KVH, self.S, self.hd) if self.H * self.hd > 0 else None
+        return ff, q, kv
 
     def alloc_outputs(self, device):
-        ffs, qkvs = self.out_shapes()
+        ffs, qs, kvs = self.out_shapes()
         mk = lambda s: None if s is None else torch.empty(s, dtype=self.dtype, device=device)
-        return mk(ffs), mk(qkvs), mk(qkvs), mk(qkvs)
+        return mk(ffs), mk(qs), mk(kvs), mk(kvs)
 
     def __call__(self, x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
                  out=None, stream: torch.cuda.Stream | None = None):
@@ -207,8 +216,8 @@ class FusedProjection:
             if bias is None or tuple(bias.shape) != (self.F,) or not bias.is_contiguous():
                 raise ValueError(f"bias must be a contiguous [{self.F}] tensor")
         ff, q, k, v = out if out is not None else self.alloc_outputs(x.device)
-        ffs, qkvs = self.out_shapes()
-        for t, s in ((ff, ffs), (q, qkvs), (k, qkvs), (v, qkvs)):
+        ffs, qs, kvs = self.out_shapes()
+        for t, s in ((ff, ffs), (q, qs), (k, kvs), (v, kvs)):
             if s is not None and (t is None or tuple(t.shape) != s or not t.is_contiguous()
                                   or t.dtype != self.dtype):
                 raise ValueError(f"output must be a contiguous {s} {self.dtype} tensor")

@@ -35,6 +35,7 @@ int64_t add_cap(int64_t a, int64_t b) {
 
 struct Derived {
     int64_t S = 0, M = 0, F = 0, qw = 0, V = 8;
+    int64_t kvh = 0, kvw = 0, rd = 0;  // k/v heads and columns per k/v slice, rotated width
     int64_t sb = 0, ss = 0, sc = 0;  // canonical strides: slab, token, channel
     int64_t x_span = 0;              // 1 + largest element offset of x (0 when empty)
 };
@@ -50,6 +51,10 @@ int check_desc(const fused_proj_desc* d, Derived* out) {
         return FUSED_PROJ_EINVAL;
     if (d->batch < 0 || d->channels < 0 || d->ff_dim < 0 || d->n_heads < 0 || d->head_dim < 0) return FUSED_PROJ_EINVAL;
     if ((d->n_heads > 0) != (d->head_dim > 0)) return FUSED_PROJ_EINVAL;
+    if (d->n_kv_heads < 0 || (d->n_heads == 0 && d->n_kv_heads != 0)) return FUSED_PROJ_EINVAL;
+    if (d->n_kv_heads > 0 && d->n_heads % d->n_kv_heads != 0) return FUSED_PROJ_EINVAL;
+    if (d->qkv_order != FUSED_PROJ_QKV_CONTIGUOUS && d->qkv_order != FUSED_PROJ_QKV_GROUPED) return FUSED_PROJ_EINVAL;
+    if (d->rope_dims < 0) return FUSED_PROJ_EINVAL;
     if (d->x_layout == FUSED_PROJ_X_TOKENS_LAST ? d->n_spatial != 1 : (d->n_spatial < 1 || d->n_spatial > 3))
         return FUSED_PROJ_EINVAL;
     if (d->x_stride_batch < 0 || d->x_stride_channel < 0) return FUSED_PROJ_EINVAL;
@@ -58,13 +63,19 @@ int check_desc(const fused_proj_desc* d, Derived* out) {
     if (d->pos_offset < 0) return FUSED_PROJ_EINVAL;
     if (d->rope) {
         if (d->head_dim % 2 != 0) return FUSED_PROJ_EINVAL;
+        const int64_t rd = d->rope_dims > 0 ? d->rope_dims : d->head_dim;
+        if (rd % 2 != 0 || rd > d->head_dim) return FUSED_PROJ_EINVAL;
         if (!(d->rope_base > 0.0) || !std::isfinite(d->rope_base)) return FUSED_PROJ_EINVAL;
     }
     Derived r;
     r.V = d->dtype == FUSED_PROJ_BF16 ? 8 : 4;
     r.qw = mul_cap(d->n_heads, d->head_dim);
     if (r.qw < 0 || r.qw > kMaxIndex) return FUSED_PROJ_EUNSUPPORTED;
-    r.F = add_cap(d->ff_dim, mul_cap(3, r.qw));
+    r.kvh = d->n_kv_heads > 0 ? d->n_kv_heads : d->n_heads;
+    r.kvw = mul_cap(r.kvh, d->head_dim);
+    r.rd = d->rope_dims > 0 ? d->rope_dims : d->head_dim;
+    if (r.kvw < 0 || r.kvw > kMaxIndex) return FUSED_PROJ_EUNSUPPORTED;
+    r.F = add_cap(add_cap(d->ff_dim, r.qw), mul_cap(2, r.kvw));
     if (r.F == 0) return FUSED_PROJ_EINVAL;
     if (r.F < 0 || r.F > kMaxIndex || d->channels > kMaxIndex) return FUSED_PROJ_EUNSUPPORTED;
     int64_t S = 1;
@@ -81,7 +92,6 @@ int check_desc(const fused_proj_desc* d, Derived* out) {
     if (d->channels % V || d->ff_dim % V || d->head_dim % V) return FUSED_PROJ_EUNSUPPORTED;
     if (d->rope && r.qw > 0) {
         const int64_t hd = d->head_dim;
-        if ((hd / 2) % V) return FUSED_PROJ_EUNSUPPORTED;
         if (128 % hd) return FUSED_PROJ_EUNSUPPORTED;         // a 128-column tile holds whole heads
         if (d->ff_dim % hd) return FUSED_PROJ_EUNSUPPORTED;   // heads start on head boundaries
         if (add_cap(S, d->pos_offset) < 0 || S + d->pos_offset > kMaxIndex) return FUSED_PROJ_EUNSUPPORTED;
@@ -195,8 +205,12 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     // the general kernel, even when the fast one is forced
     const bool fast_act = desc->ff_dim == 0 || desc->ff_act == FUSED_PROJ_ACT_NONE ||
                           desc->ff_act == FUSED_PROJ_ACT_GELU_ERF;
-    h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && addressable && fast_act && (exact || want_fast) &&
-              !want_general;
+    // ... and the plain multi-head layout: as many k/v heads as q heads, contiguous order,
+    // the full head rotated
+    const bool fast_heads = r.kvh == desc->n_heads && desc->qkv_order == FUSED_PROJ_QKV_CONTIGUOUS &&
+                            (!desc->rope || r.rd == desc->head_dim);
+    h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && addressable && fast_act && fast_heads &&
+              (exact || want_fast) && !want_general;
     h->dg = dg < 0 ? 0 : dg;
     h->tile = h->fast ? fp_plan : fp::TilePlan{128, 128, h->dt == fp::DType::BF16 ? 64 : 32, 8, 0};
 
@@ -213,6 +227,9 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     a.n_heads = (int32_t)desc->n_heads;
     a.head_dim = (int32_t)desc->head_dim;
     a.qw = (int32_t)r.qw;
+    a.n_kv_heads = (int32_t)r.kvh;
+    a.qkv_grouped = desc->qkv_order == FUSED_PROJ_QKV_GROUPED ? 1 : 0;
+    a.rope_dims = (int32_t)r.rd;
     a.act = desc->ff_act == FUSED_PROJ_ACT_GELU_ERF      ? 1
             : desc->ff_act == FUSED_PROJ_ACT_GELU_TANH     ? 2
             : desc->ff_act == FUSED_PROJ_ACT_RELU_SQUARED ? 3
@@ -225,13 +242,14 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     a.div_group = fp::make_fastdiv_u31((uint32_t)((int64_t)a.group_m * a.tiles_n));
 
     if (a.rope && r.S > 0) {
-        // cos/sin of (s + pos_offset) * base^(-2i/hd), computed in float64, stored fp32
-        const int64_t half = desc->head_dim / 2;
+        // cos/sin of (s + pos_offset) * base^(-2i/rd) for the rotated width rd (the head
+        // size unless partial), computed in float64, stored fp32
+        const int64_t half = r.rd / 2;
         const size_t n = (size_t)r.S * (size_t)half;
         std::vector<float> hc(n), hs(n);
         std::vector<double> theta((size_t)half);
         for (int64_t i = 0; i < half; ++i)
-            theta[(size_t)i] = std::pow(desc->rope_base, -2.0 * (double)i / (double)desc->head_dim);
+            theta[(size_t)i] = std::pow(desc->rope_base, -2.0 * (double)i / (double)r.rd);
         for (int64_t s = 0; s < r.S; ++s) {
             const double p = (double)(s + desc->pos_offset);
             for (int64_t i = 0; i < half; ++i) {
@@ -304,8 +322,10 @@ int fused_proj_run(fused_proj_t h, const void* x, const void* w, const void* bia
     }
     if (h->d.has_bias) ins.push_back({(uintptr_t)bias, (uintptr_t)bias + (uintptr_t)r.F * es});
     if (h->d.ff_dim > 0) outs.push_back({(uintptr_t)ff, (uintptr_t)ff + (uintptr_t)(r.M * h->d.ff_dim) * es});
-    if (r.qw > 0)
-        for (void* p : {q, k, v}) outs.push_back({(uintptr_t)p, (uintptr_t)p + (uintptr_t)(r.M * r.qw) * es});
+    if (r.qw > 0) {
+        outs.push_back({(uintptr_t)q, (uintptr_t)q + (uintptr_t)(r.M * r.qw) * es});
+        for (void* p : {k, v}) outs.push_back({(uintptr_t)p, (uintptr_t)p + (uintptr_t)(r.M * r.kvw) * es});
+    }
     for (size_t i = 0; i < outs.size(); ++i) {
         for (size_t j = i + 1; j < outs.size(); ++j)
             if (overlap(outs[i], outs[j])) return FUSED_PROJ_EALIAS;

@@ -317,20 +317,41 @@ __global__ __launch_bounds__(kThreads, 2) void fused_proj_tile_kernel(KernelArgs
     const int g = tid % GPR, rsub = tid / GPR;
     const int f0 = n0 + g * OV;
     if (f0 >= p.N) return;
+    // The group's slice (0 ff, 1 q, 2 k, 3 v), head h and element j0 in the head. The q/k/v
+    // columns are either contiguous (all q heads, the k heads, the v heads) or grouped per
+    // k/v head (its q heads, then k, then v). A group never straddles heads (head_dim is a
+    // multiple of OV).
     int kind = 0, h = 0, j0 = 0;
+    const int hd = p.head_dim, kvh = p.n_kv_heads;
     if (f0 >= p.ff_dim) {
         const int r = f0 - p.ff_dim;
-        const int which = r / p.qw;
-        const int rem = r - which * p.qw;
-        h = rem / p.head_dim;
-        j0 = rem - h * p.head_dim;
-        kind = 1 + which;
+        if (!p.qkv_grouped) {
+            const int kvw = kvh * hd;
+            const int which = r < p.qw ? 0 : r < p.qw + kvw ? 1 : 2;
+            const int rem = which == 0 ? r : r - p.qw - (which - 1) * kvw;
+            h = rem / hd;
+            j0 = rem - h * hd;
+            kind = 1 + which;
+        } else {
+            const int qpk = p.n_heads / kvh, gw = (qpk + 2) * hd;
+            const int grp = r / gw, within = r - grp * gw, slot = within / hd;
+            j0 = within - slot * hd;
+            kind = slot < qpk ? 1 : slot == qpk ? 2 : 3;
+            h = slot < qpk ? grp * qpk + slot : grp;
+        }
     }
-    const bool do_rope = p.rope && (kind == 1 || kind == 2);
-    const int half = p.head_dim >> 1;
+    // RoPE over the first rope_dims elements of each q/k head: the partner of element j is
+    // j +- rope_dims/2 in the same head, which lies in this tile (the host keeps heads whole
+    // in 128-column tiles). When the group lies in one half of the rotated width the whole
+    // group shares one partner offset (vector path); otherwise (partial rotation narrower
+    // than two groups, or a group crossing rope_dims) each element finds its own.
+    const int rd = p.rope_dims, half = rd >> 1;
+    const bool do_rope = p.rope && (kind == 1 || kind == 2) && j0 < rd;
+    const bool vec_rope = do_rope && half % OV == 0;
     const bool first_half = j0 < half;
     const int i0 = first_half ? j0 : j0 - half;
     const int pcol = g * OV + (first_half ? half : -half);
+    const int heads = kind == 1 ? p.n_heads : kvh;
     T* const dst = static_cast<T*>(kind == 0 ? p.ff : kind == 1 ? p.q : kind == 2 ? p.k : p.v);
 
     for (int row = rsub; row < BM; row += RPP) {
@@ -357,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_proj_tile_kernel(KernelArgs
             store16<T>(dst + (int64_t)m * p.ff_dim + f0, y);
         } else {
             const int bi = m / p.S, s = m - bi * p.S;
-            if (do_rope) {
+            if (vec_rope) {
                 const float* ps = Cs + row * CST + pcol;
                 const float* cs = p.rope_cos + (int64_t)s * half + i0;
                 const float* sn = p.rope_sin + (int64_t)s * half + i0;
@@ -374,8 +395,20 @@ __global__ __launch_bounds__(kThreads, 2) void fused_proj_tile_kernel(KernelArgs
                         y[e + u] = first_half ? y[e + u] * cv[u] - ypv[u] * svv[u]
                                               : y[e + u] * cv[u] + ypv[u] * svv[u];
                 }
+            } else if (do_rope) {
+#pragma unroll
+                for (int e = 0; e < OV; ++e) {
+                    const int j = j0 + e;
+                    if (j >= rd) continue;
+                    const bool fh = j < half;
+                    const int i = fh ? j : j - half;
+                    const float yp = Cs[row * CST + g * OV + e + (fh ? half : -half)];
+                    const float c = p.rope_cos[(int64_t)s * half + i];
+                    const float sv = p.rope_sin[(int64_t)s * half + i];
+                    y[e] = fh ? y[e] * c - yp * sv : y[e] * c + yp * sv;
+                }
             }
-            const int64_t off = ((int64_t)(bi * p.n_heads + h) * p.S + s) * p.head_dim + j0;
+            const int64_t off = ((int64_t)(bi * heads + h) * p.S + s) * hd + j0;
             store16<T>(dst + off, y);
         }
     }

@@ -46,6 +46,17 @@ class Workload:
     pos_offset: int = 0
     w_layout: str = "cf"    # "cf": W [C,F]; "fc": W [F,C]
     description: str = field(default="", compare=False)
+    n_kv_heads: int = 0     # k/v heads (0: n_heads)
+    qkv_order: str = "contiguous"   # or "grouped" (per k/v head: its q heads, k, v)
+    rope_dims: int = 0      # rotated width of each q/k head (0: head_dim)
+
+    @property
+    def kvh(self) -> int:
+        return self.n_kv_heads if self.n_kv_heads > 0 else self.n_heads
+
+    @property
+    def rd(self) -> int:
+        return self.rope_dims if self.rope_dims > 0 else self.head_dim
 
     @property
     def C(self) -> int:
@@ -67,7 +78,7 @@ class Workload:
 
     @property
     def F(self) -> int:
-        return self.ff_dim + 3 * self.n_heads * self.head_dim
+        return self.ff_dim + (self.n_heads + 2 * self.kvh) * self.head_dim
 
     @property
     def flops(self) -> float:
@@ -87,7 +98,7 @@ class Workload:
         if self.has_bias:
             b += self.F * e
         if self.rope and self.n_heads > 0:
-            b += 2 * 4 * (self.S + self.pos_offset) * (self.head_dim // 2)
+            b += 2 * 4 * self.S * (self.rd // 2)
         return float(b)
 
 
@@ -110,6 +121,13 @@ WORKLOADS = {
         # BERT-base FF with squared ReLU (an activation the xformers PR discussion names)
         Workload("bert_ff_relu2_bf16", "bf16", "tokens_last", (32, 512, 768), 3072, "relu2", 0, 0, True, False, 7,
                  description="BERT-base FF bf16 with squared ReLU: x [32,512,768], W [768,3072]"),
+        # The nvFuser RoPE issue's lit-gpt block: bsz 2, T 1024, n_embd 512, 16 q heads in 4
+        # query groups (k/v once per group), head size 32, RoPE on the first 8 elements,
+        # q/k/v columns grouped per k/v head, no bias
+        Workload("gqa_rope8_bf16", "bf16", "tokens_last", (2, 1024, 512), 0, "none", 16, 32, False, True, 8,
+                 n_kv_heads=4, qkv_order="grouped", rope_dims=8,
+                 description="lit-gpt GQA bf16: x [2,1024,512], W [512,768], 16 q heads / 4 k-v groups x 32, "
+                             "grouped columns, RoPE on 8 of 32"),
         # The Walrus block at the width its profiles imply (C = 1408, F = 7C: FF 4C and
         # Q/K/V C each): F is not a multiple of 256, so the last large column tile is ragged.
         Workload("walrus_c1408_bf16", "bf16", "channels_first", (24, 1408, 32, 32, 1), 5632, "gelu", 22, 64, True,

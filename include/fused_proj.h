@@ -86,6 +86,14 @@ extern "C" {
  * natively. Both run on the general kernel (128 x 128 tiles) for now. */
 #define FUSED_PROJ_ACT_RELU_SQUARED 3
 
+/* Order of the q, k and v columns after the ff slice. */
+#define FUSED_PROJ_QKV_CONTIGUOUS 0 /* all q heads, then the k heads, then the v heads */
+/* n_kv_heads groups, each holding n_heads/n_kv_heads q heads, then one k head and one v head;
+ * q head i of group g is head g*(n_heads/n_kv_heads) + i (split_qkv in the NVIDIA/Fuser issue
+ * "Improve performance on RoPE (and code around it)", the lit-gpt layout). k and v are written
+ * once per group, not repeated for every q head. */
+#define FUSED_PROJ_QKV_GROUPED 1
+
 typedef struct fused_proj_desc {
     int32_t dtype;             /* FUSED_PROJ_BF16 | FUSED_PROJ_F32 */
     int32_t x_layout;          /* FUSED_PROJ_X_* */
@@ -100,11 +108,19 @@ typedef struct fused_proj_desc {
     int32_t has_bias;          /* 1: bias[F] (storage type) is added to every column */
     int64_t ff_dim;            /* width of the ff slice, >= 0 */
     int32_t ff_act;            /* FUSED_PROJ_ACT_* */
-    int64_t n_heads;           /* H >= 0; q, k, v each hold H*head_dim columns */
+    int64_t n_heads;           /* H >= 0; q holds H*head_dim columns, k and v KVH*head_dim */
     int64_t head_dim;          /* hd >= 0 */
     int32_t rope;              /* 1: rotate-half RoPE on q and k */
     double rope_base;          /* > 0; 10000 is customary */
     int64_t pos_offset;        /* >= 0; position of token s is s + pos_offset */
+    /* Fields below are zero in a zero-initialised descriptor, which keeps the plain
+     * multi-head layout: as many k/v heads as q heads, contiguous order, full rotation. */
+    int64_t n_kv_heads;        /* k and v heads, dividing n_heads; 0 means n_heads */
+    int32_t qkv_order;         /* FUSED_PROJ_QKV_* */
+    int64_t rope_dims;         /* rotated width of each q/k head: even, <= head_dim; 0 means
+                                  head_dim. Elements from rope_dims on pass through; the
+                                  angles are (s + pos_offset) * base^(-2i/rope_dims)
+                                  (rope_one_entry with rope_n_elem in the same issue). */
 } fused_proj_desc;
 
 typedef struct fused_proj_plan *fused_proj_t;
@@ -112,10 +128,11 @@ typedef struct fused_proj_plan *fused_proj_t;
 /*
  * Checks a descriptor on the host; touches no GPU and allocates nothing.
  * Returns FUSED_PROJ_OK, FUSED_PROJ_EINVAL (malformed: a size < 0, F = ff_dim +
- * 3*H*hd == 0, n_spatial out of range, unknown enum, odd hd with RoPE, base <= 0)
- * or FUSED_PROJ_EUNSUPPORTED. Supported, with V = 8 for bf16 and 4 for fp32:
- *   C, ff_dim and head_dim multiples of V; with RoPE, head_dim/2 a multiple of V,
- *   head_dim <= 256 and ff_dim a multiple of head_dim;
+ * (H + 2*KVH)*hd == 0, n_spatial out of range, unknown enum, KVH not dividing H,
+ * rope_dims odd or above hd with RoPE, base <= 0) or FUSED_PROJ_EUNSUPPORTED.
+ * Supported, with V = 8 for bf16 and 4 for fp32:
+ *   C, ff_dim and head_dim multiples of V; with RoPE, 128 a multiple of head_dim
+ *   and ff_dim a multiple of head_dim;
  *   channels-first: spatial strides that flatten into one unit-stride token
  *   index (stride of the last spatial dim 1, each outer stride the product of the
  *   inner sizes), S, x_stride_channel and x_stride_batch multiples of V;

@@ -14,7 +14,8 @@ from ff_input_projection_amd.workloads import Workload, make_inputs
 def plan_for(wl: Workload, x: torch.Tensor) -> FusedProjection:
     return FusedProjection.for_tensor(
         x, wl.layout, w_layout=wl.w_layout, has_bias=wl.has_bias, ff_dim=wl.ff_dim, ff_act=wl.ff_act,
-        n_heads=wl.n_heads, head_dim=wl.head_dim, rope=wl.rope, rope_base=wl.rope_base, pos_offset=wl.pos_offset)
+        n_heads=wl.n_heads, head_dim=wl.head_dim, rope=wl.rope, rope_base=wl.rope_base, pos_offset=wl.pos_offset,
+        n_kv_heads=wl.n_kv_heads, qkv_order=wl.qkv_order, rope_dims=wl.rope_dims)
 
 
 def run_gpu(wl: Workload, inp, device="cuda:0", x_dev: torch.Tensor | None = None):
@@ -52,18 +53,19 @@ def gpu_rows(wl: Workload, outs, tokens: np.ndarray):
         res.append(ff.view(wl.nb, wl.S, wl.ff_dim)[bi.to(ff.device), s.to(ff.device)].double().cpu().numpy())
     else:
         res.append(None)
-    for t in (q, k, v):
+    for t, heads in ((q, wl.n_heads), (k, wl.kvh), (v, wl.kvh)):
         if t is None:
             res.append(None)
             continue
-        t4 = t.view(wl.nb, wl.n_heads, wl.S, wl.head_dim)
+        t4 = t.view(wl.nb, heads, wl.S, wl.head_dim)
         res.append(t4[bi.to(t.device), :, s.to(t.device)].double().cpu().numpy())
     return res
 
 
 def oracle_rows(wl: Workload, inp, tokens: np.ndarray):
     r = oracle.fused_proj(inp.x64, wl.layout, inp.w64, wl.w_layout, inp.bias64, wl.ff_dim, wl.ff_act,
-                          wl.n_heads, wl.head_dim, wl.rope, wl.rope_base, wl.pos_offset, tokens=tokens)
+                          wl.n_heads, wl.head_dim, wl.rope, wl.rope_base, wl.pos_offset, tokens=tokens,
+                          n_kv_heads=wl.n_kv_heads, qkv_order=wl.qkv_order, rope_dims=wl.rope_dims)
     return [r.ff, r.q, r.k, r.v]
 
 
@@ -73,7 +75,8 @@ def verdict(wl: Workload, inp, outs, tokens: np.ndarray) -> cmp.Verdict:
     rows, pos = cmp.token_rows(inp.x64, wl.layout, tokens)
     w_cf = inp.w64 if wl.w_layout == "cf" else inp.w64.T
     sc = cmp.scales(rows, pos, w_cf, inp.bias64, wl.ff_dim, wl.n_heads, wl.head_dim, wl.rope, wl.rope_base,
-                    wl.pos_offset, ff_act=wl.ff_act, ff_ref=ref[0])
+                    wl.pos_offset, ff_act=wl.ff_act, ff_ref=ref[0], n_kv_heads=wl.n_kv_heads,
+                    qkv_order=wl.qkv_order, rope_dims=wl.rope_dims)
     return cmp.compare(got, ref, [sc.ff, sc.q, sc.k, sc.v], wl.dtype)
 
 

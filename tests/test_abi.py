@@ -83,6 +83,11 @@ def test_validate_accepts_every_activation():
     (lambda d: setattr(d, "x_layout", 5), fpa.EINVAL),
     (lambda d: setattr(d, "w_layout", 2), fpa.EINVAL),
     (lambda d: setattr(d, "ff_act", 9), fpa.EINVAL),
+    (lambda d: setattr(d, "n_kv_heads", 5), fpa.EINVAL),     # does not divide 12 q heads
+    (lambda d: setattr(d, "n_kv_heads", -1), fpa.EINVAL),
+    (lambda d: setattr(d, "qkv_order", 2), fpa.EINVAL),
+    (lambda d: setattr(d, "rope_dims", 7), fpa.EINVAL),      # odd rotated width
+    (lambda d: setattr(d, "rope_dims", 128), fpa.EINVAL),    # wider than the 64-element head
     (lambda d: setattr(d, "batch", -1), fpa.EINVAL),
     (lambda d: setattr(d, "n_spatial", 4), fpa.EINVAL),
     (lambda d: setattr(d, "head_dim", 0), fpa.EINVAL),             # heads without width

@@ -94,6 +94,14 @@ SMALL = [
                ff_act="gelu_tanh", n_heads=2, head_dim=8, seed=119),
     with_shape(WORKLOADS["tiny_f32"], "f32_cf_relu2", x_shape=(1, 40, 8, 8, 1), ff_dim=64, ff_act="relu2",
                n_heads=2, head_dim=8, seed=120),
+    # fewer k/v heads than q heads, both column orders, partial rotary (general kernel)
+    with_shape(WORKLOADS["gqa_rope8_bf16"], "tl_gqa_grouped_rope8", x_shape=(2, 77, 64), seed=122),
+    with_shape(WORKLOADS["bert_qkv_bf16"], "tl_gqa_contiguous_rope16", x_shape=(2, 90, 96), ff_dim=64,
+               ff_act="gelu", n_heads=6, head_dim=32, n_kv_heads=2, rope=True, rope_dims=16, seed=123),
+    with_shape(WORKLOADS["walrus_bf16"], "cf_mqa_grouped_fullrope", x_shape=(2, 64, 8, 8, 1), ff_dim=64,
+               n_heads=4, head_dim=64, n_kv_heads=1, qkv_order="grouped", seed=124),
+    with_shape(WORKLOADS["tiny_f32"], "f32_gqa_grouped_rope4", layout="tokens_last", x_shape=(2, 30, 32), ff_dim=0,
+               n_heads=4, head_dim=8, n_kv_heads=2, qkv_order="grouped", rope_dims=4, has_bias=True, seed=125),
     # fp32, token-major, [F,C], RoPE hd 8, GELU
     with_shape(WORKLOADS["tiny_f32"], "f32_tl_fc", layout="tokens_last", x_shape=(3, 50, 36), ff_dim=16,
                n_heads=3, head_dim=8, w_layout="fc", seed=106),
@@ -234,10 +242,10 @@ def test_canary_guard_bands_untouched():
     inp = make_inputs(wl)
     x, w, b = inp.x.to(DEV), inp.w.to(DEV), inp.bias.to(DEV)
     proj = plan_for(wl, x)
-    ffs, qkvs = proj.out_shapes()
+    ffs, qs, kvs = proj.out_shapes()
     guard = 4096
     bufs, outs = [], []
-    for s in (ffs, qkvs, qkvs, qkvs):
+    for s in (ffs, qs, kvs, kvs):
         n = int(np.prod(s))
         buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.bfloat16, device=DEV)
         bufs.append(buf)
