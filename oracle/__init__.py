@@ -60,6 +60,9 @@ def _load():
             ctypes.c_int, ctypes.c_double, i64,
             p64, i64, d, d, d, d, ctypes.c_int,
         ]
+        lib.oracle_split_rope.restype = ctypes.c_int
+        lib.oracle_split_rope.argtypes = [d, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, i64,
+                                          ctypes.c_double, i64, ctypes.c_int, d, d, d]
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -175,3 +178,26 @@ def fused_proj(x: np.ndarray, layout: str, w: np.ndarray, w_layout: str, bias: n
 
     ff = None if ff_rows is None else ff_rows.reshape(nb, S, ff_dim)
     return OracleResult(ff, head_major(q_rows, n_heads), head_major(k_rows, kvh), head_major(v_rows, kvh))
+
+
+def split_rope(qkv: np.ndarray, n_heads: int, head_dim: int, n_kv_heads: int = 0, qkv_order: str = "contiguous",
+               rope: bool = True, rope_dims: int = 0, rope_base: float = 10000.0, pos_offset: int = 0,
+               k_transposed: bool = False):
+    """Float64 split + RoPE of a projected q/k/v tensor qkv [b, T, (H + 2*KVH)*hd].
+    Returns (q [b*H, T, hd], k [b*KVH, T, hd] or [b*KVH, hd, T], v [b*KVH, T, hd])."""
+    lib = _load()
+    qkv = np.ascontiguousarray(qkv, dtype=np.float64)
+    nb, T, Fq = qkv.shape
+    kvh = n_kv_heads if n_kv_heads > 0 else n_heads
+    if Fq != (n_heads + 2 * kvh) * head_dim:
+        raise ValueError("qkv width does not match the heads")
+    q = np.empty((nb * n_heads, T, head_dim))
+    v = np.empty((nb * kvh, T, head_dim))
+    k = np.empty((nb * kvh, head_dim, T) if k_transposed else (nb * kvh, T, head_dim))
+    rc = lib.oracle_split_rope(_dptr(qkv), nb, T, n_heads, int(n_kv_heads), head_dim,
+                               {"contiguous": 0, "grouped": 1}[qkv_order], int(bool(rope)), int(rope_dims),
+                               float(rope_base), int(pos_offset), int(bool(k_transposed)), _dptr(q), _dptr(k),
+                               _dptr(v))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    return q, k, v

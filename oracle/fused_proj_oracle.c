@@ -281,6 +281,56 @@ int oracle_fused_proj(const double *x, int64_t nb, int64_t C, int64_t S, int64_t
     return status;
 }
 
+/*
+ * Split + RoPE of an already projected q/k/v tensor (the nvFuser RoPE issue's
+ * split_qkv followed by rope_one_entry on q and k): qkv [nb, T, (H + 2*KVH)*hd]
+ * token-major, columns in contiguous or grouped order (qkv_column). Outputs:
+ * q [nb*H, T, hd], v [nb*KVH, T, hd], and k [nb*KVH, T, hd], or [nb*KVH, hd, T]
+ * with k_transposed = 1 (the pre-transposed key of the memory-efficient-attention
+ * issue). RoPE on the first rope_dims elements of each q and k head at position
+ * s + pos_offset. Returns 0, or -1 on an invalid argument.
+ */
+int oracle_split_rope(const double *qkv, int64_t nb, int64_t T, int64_t n_heads, int64_t n_kv, int64_t hd,
+                      int grouped, int rope, int64_t rope_dims, double rope_base, int64_t pos_offset,
+                      int k_transposed, double *q, double *k, double *v)
+{
+    if (!qkv || !q || !k || !v || nb <= 0 || T <= 0 || n_heads <= 0 || hd <= 0) return ORACLE_EINVAL;
+    if (n_kv == 0) n_kv = n_heads;
+    if (n_kv < 0 || n_heads % n_kv != 0 || (grouped != 0 && grouped != 1)) return ORACLE_EINVAL;
+    const int64_t rd = rope_dims > 0 ? rope_dims : hd;
+    if (rope && (rd % 2 != 0 || rd > hd)) return ORACLE_EINVAL;
+    const int64_t Fq = (n_heads + 2 * n_kv) * hd;
+    double *head = (double *)malloc((size_t)hd * sizeof(double));
+    if (!head) return ORACLE_EINVAL;
+    for (int64_t bi = 0; bi < nb; ++bi) {
+        for (int64_t s = 0; s < T; ++s) {
+            const double *row = qkv + (bi * T + s) * Fq;
+            /* every head of this token: gather its hd columns, rotate, store */
+            for (int which = 0; which < 3; ++which) {
+                const int64_t heads = which == 0 ? n_heads : n_kv;
+                for (int64_t h = 0; h < heads; ++h) {
+                    for (int64_t r = 0; r < Fq; ++r) {
+                        int wh;
+                        int64_t hh, j;
+                        qkv_column(r, n_heads, n_kv, hd, grouped, &wh, &hh, &j);
+                        if (wh == which && hh == h) head[j] = row[r];
+                    }
+                    if (rope && which < 2) rope_rotate_half(head, rd, (double)(s + pos_offset), rope_base);
+                    for (int64_t j = 0; j < hd; ++j) {
+                        const int64_t slab = bi * heads + h;
+                        if (which == 0) q[(slab * T + s) * hd + j] = head[j];
+                        else if (which == 2) v[(slab * T + s) * hd + j] = head[j];
+                        else if (!k_transposed) k[(slab * T + s) * hd + j] = head[j];
+                        else k[(slab * hd + j) * T + s] = head[j];
+                    }
+                }
+            }
+        }
+    }
+    free(head);
+    return ORACLE_OK;
+}
+
 /* Threads the OpenMP runtime would use by default (for reporting). */
 int oracle_max_threads(void)
 {

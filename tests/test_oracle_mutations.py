@@ -39,6 +39,9 @@ MUTATIONS = [
     ("tanh GELU without the cube", "(y + 0.044715 * y * y * y)", "(y + 0.044715 * y * y)"),
     ("squared ReLU without the clamp", "const double r = y > 0.0 ? y : 0.0;", "const double r = y;"),
     ("squared ReLU not squared", "    return r * r;", "    return r;"),
+    ("split+RoPE transposed key indexed as untransposed", "else k[(slab * hd + j) * T + s] = head[j];",
+     "else k[(slab * T + s) * hd + j] = head[j];"),
+    ("split+RoPE RoPE skipped", "if (rope && which < 2) rope_rotate_half(head, rd,", "if (0) rope_rotate_half(head, rd,"),
     ("spatial dims unflattened in reverse", "int64_t idx = rem % sp_size[d];", "int64_t idx = rem % sp_size[nsp - 1 - d];"),
     ("bias skipped on the ff slice", "for (int64_t f = 0; f < F; ++f) y[f] += bias[f];",
      "for (int64_t f = 0; f < F; ++f) y[f] += (f < ff_dim ? 0.0 : bias[f]);"),

@@ -346,6 +346,39 @@ def test_full_width_rope_dims_equals_default():
         assert np.array_equal(u, v)
 
 
+# --------------------------------------------------------------------------- standalone split + RoPE
+
+@pytest.mark.parametrize("order,kvh,rd", [("grouped", 2, 8), ("contiguous", 4, 0), ("grouped", 1, 4)])
+def test_split_rope_equals_fused_projection_with_identity_weight(order, kvh, rd):
+    """Split + RoPE of a projected tensor is the fused projection of that tensor with
+    W = I: both layouts of the columns, fewer k/v heads, partial rotary, a position
+    offset. Pins the standalone op to the pinned fused definition."""
+    B, T, H, hd = 2, 6, 4, 16
+    Fq = (H + 2 * kvh) * hd
+    r = np.random.default_rng(41)
+    y = r.standard_normal((B, T, Fq))
+    q, k, v = oracle.split_rope(y, H, hd, n_kv_heads=kvh, qkv_order=order, rope=True, rope_dims=rd, pos_offset=3)
+    ref = oracle.fused_proj(y, "tokens_last", np.eye(Fq), "cf", None, 0, "none", H, hd, rope=True, pos_offset=3,
+                            n_kv_heads=kvh, qkv_order=order, rope_dims=rd)
+    for a, c in ((q, ref.q), (k, ref.k), (v, ref.v)):
+        assert a.shape == c.shape
+        assert np.allclose(a, c, rtol=0, atol=1e-14)
+
+
+def test_split_rope_transposed_key_and_plain_copy_of_v():
+    """The transposed key is the [hd, T] transpose of each k head; v is a plain copy of
+    its columns (no RoPE)."""
+    B, T, H, G, hd = 1, 5, 4, 2, 8
+    Fq = (H + 2 * G) * hd
+    y = np.random.default_rng(42).standard_normal((B, T, Fq))
+    args = dict(n_kv_heads=G, qkv_order="grouped", rope=True, rope_dims=4)
+    q, k, v = oracle.split_rope(y, H, hd, **args)
+    _, kt, _ = oracle.split_rope(y, H, hd, k_transposed=True, **args)
+    assert np.array_equal(kt, k.transpose(0, 2, 1))
+    vref = y.reshape(B, T, G, H // G + 2, hd)[:, :, :, H // G + 1].transpose(0, 2, 1, 3).reshape(B * G, T, hd)
+    assert np.array_equal(v, vref)
+
+
 # --------------------------------------------------------------------------- RoPE
 
 def _rope_via_oracle(vec, p, base, which="q"):
