@@ -93,8 +93,10 @@ def main() -> int:
     import torch
 
     from ff_input_projection_amd import FusedProjection
-    from ff_input_projection_amd.workloads import WORKLOADS, make_inputs
+    from ff_input_projection_amd.workloads import SPLIT_ROPE_WORKLOADS, WORKLOADS, make_inputs
 
+    if args.workload in SPLIT_ROPE_WORKLOADS:
+        return bench_split_rope(args, SPLIT_ROPE_WORKLOADS[args.workload])
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -244,6 +246,82 @@ def main() -> int:
                             "tight_ratio": round(vd.max_tight_ratio, 5), "elements": vd.n}
         print(f"[bench] parity on the oracle sample: {vd}", file=sys.stderr, flush=True)
 
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_split_rope(args, wl) -> int:
+    """The standalone split + RoPE (split_rope.h) on a seeded projected q/k/v tensor:
+    memory-bound, priced against HBM bandwidth (input once + outputs once)."""
+    import numpy as np
+    import torch
+
+    from ff_input_projection_amd import SplitRope
+    from ff_input_projection_amd.workloads import make_qkv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {wl.name}: {wl.description}", file=sys.stderr, flush=True)
+    x, x64 = make_qkv(wl.batch, wl.tokens, wl.Fq, wl.seed)
+    ring = args.ring or max(1, min(64, math.ceil(512e6 / wl.alg_bytes)))
+    xs = [x.to(dev) for _ in range(ring)]
+    op = SplitRope(wl.batch, wl.tokens, wl.n_heads, wl.head_dim, n_kv_heads=wl.n_kv_heads, qkv_order=wl.qkv_order,
+                   rope=True, rope_dims=wl.rope_dims, pos_offset=wl.pos_offset, k_transposed=wl.k_transposed)
+    outs = [op.alloc_outputs(dev) for _ in range(ring)]
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    calls = [(xs[i].data_ptr(), *[t.data_ptr() for t in outs[i]]) for i in range(ring)]
+
+    def step(i):
+        rc = op.run_ptrs(*calls[i % ring], sh)
+        if rc != 0:
+            raise RuntimeError(f"split_rope_run failed with status {rc}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    gbs = wl.alg_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded qkv ~ N(0,1), rounded once to bf16",
+        "config": {"workload": wl.name, "op": "split_rope", "batch": wl.batch, "tokens": wl.tokens,
+                   "n_heads": wl.n_heads, "n_kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
+                   "qkv_order": wl.qkv_order, "rope_dims": wl.rope_dims, "k_transposed": wl.k_transposed,
+                   "ring": ring},
+        "gb_per_s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        "kernel": "split_rope_kernel", "kernel_hash": kernel_hash(),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            ref = oracle.split_rope(x64, wl.n_heads, wl.head_dim, n_kv_heads=wl.n_kv_heads,
+                                    qkv_order=wl.qkv_order, rope=True, rope_dims=wl.rope_dims,
+                                    pos_offset=wl.pos_offset, k_transposed=wl.k_transposed)
+            reps += 1
+            secs = time.perf_counter() - t0
+            if secs >= min(args.cpu_seconds, 10.0) or reps >= 50:
+                break
+        result["cpu_baseline"] = {"value": round(wl.alg_bytes * reps / secs / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"the whole tensor x {reps} run(s), float64, one thread, {secs:.1f} s"}
+        q, k, v = (t.double().cpu().numpy() for t in outs[0])
+        err = max(float(np.max(np.abs(g - r) / (2.0 ** -8 * np.abs(r) + 1e-5 * np.abs(x64).max())))
+                  for g, r in zip((q, k, v), ref))
+        result["parity"] = {"ok": err <= 1.0, "max_err_over_tol": round(err, 5)}
     print(json.dumps(result), flush=True)
     return 0
 

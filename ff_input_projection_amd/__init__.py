@@ -18,13 +18,15 @@ import os
 
 import torch
 
-__all__ = ["FusedProjection", "FusedProjError", "load_library", "LIB_PATH", "EXPORTED_SYMBOLS", "Desc"]
+__all__ = ["FusedProjection", "FusedProjError", "SplitRope", "load_library", "LIB_PATH", "EXPORTED_SYMBOLS", "Desc",
+           "SplitRopeDesc"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfused_proj.so")
 
 EXPORTED_SYMBOLS = ["fused_proj_validate", "fused_proj_create", "fused_proj_run", "fused_proj_destroy",
-                    "fused_proj_strerror", "fused_proj_describe"]
+                    "fused_proj_strerror", "fused_proj_describe",
+                    "split_rope_validate", "split_rope_create", "split_rope_run", "split_rope_destroy"]
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, EALIAS, EHIP = 0, -1, -2, -3, -4, -5
 BF16, F32 = 0, 1
@@ -47,6 +49,16 @@ class Desc(ctypes.Structure):
         ("n_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
         ("rope", ctypes.c_int32), ("rope_base", ctypes.c_double), ("pos_offset", ctypes.c_int64),
         ("n_kv_heads", ctypes.c_int64), ("qkv_order", ctypes.c_int32), ("rope_dims", ctypes.c_int64),
+    ]
+
+
+class SplitRopeDesc(ctypes.Structure):
+    """Mirror of ``split_rope_desc``."""
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("batch", ctypes.c_int64), ("tokens", ctypes.c_int64),
+        ("n_heads", ctypes.c_int64), ("n_kv_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+        ("qkv_order", ctypes.c_int32), ("rope", ctypes.c_int32), ("rope_dims", ctypes.c_int64),
+        ("rope_base", ctypes.c_double), ("pos_offset", ctypes.c_int64), ("k_transposed", ctypes.c_int32),
     ]
 
 
@@ -82,6 +94,14 @@ def load_library():
     lib.fused_proj_strerror.restype = ctypes.c_char_p
     lib.fused_proj_describe.argtypes = [vp, ctypes.c_char_p, ctypes.c_size_t]
     lib.fused_proj_describe.restype = ctypes.c_int
+    lib.split_rope_validate.argtypes = [ctypes.POINTER(SplitRopeDesc)]
+    lib.split_rope_validate.restype = ctypes.c_int
+    lib.split_rope_create.argtypes = [ctypes.POINTER(SplitRopeDesc), ctypes.POINTER(vp)]
+    lib.split_rope_create.restype = ctypes.c_int
+    lib.split_rope_run.argtypes = [vp] * 6
+    lib.split_rope_run.restype = ctypes.c_int
+    lib.split_rope_destroy.argtypes = [vp]
+    lib.split_rope_destroy.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -238,6 +258,85 @@ class FusedProjection:
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:
             self._lib.fused_proj_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def make_split_rope_desc(batch: int, tokens: int, n_heads: int, head_dim: int, *, n_kv_heads: int = 0,
+                         qkv_order: str = "contiguous", rope: bool = True, rope_dims: int = 0,
+                         rope_base: float = 10000.0, pos_offset: int = 0, k_transposed: bool = False,
+                         dtype: torch.dtype = torch.bfloat16) -> SplitRopeDesc:
+    d = SplitRopeDesc()
+    d.dtype = _DTYPES[dtype]
+    d.batch, d.tokens, d.n_heads, d.n_kv_heads, d.head_dim = batch, tokens, n_heads, n_kv_heads, head_dim
+    d.qkv_order = {"contiguous": QKV_CONTIGUOUS, "grouped": QKV_GROUPED}[qkv_order]
+    d.rope, d.rope_dims, d.rope_base, d.pos_offset = int(bool(rope)), rope_dims, float(rope_base), pos_offset
+    d.k_transposed = int(bool(k_transposed))
+    return d
+
+
+def validate_split_rope(desc: SplitRopeDesc) -> int:
+    return load_library().split_rope_validate(ctypes.byref(desc))
+
+
+class SplitRope:
+    """One planned standalone split + RoPE (owns its cos/sin table; see split_rope.h).
+
+    Call with a contiguous bf16 GPU tensor ``qkv`` [b, T, (H + 2*KVH)*hd]; returns
+    ``(q, k, v)``: q [b*H, T, hd], k [b*KVH, T, hd] (or [b*KVH, hd, T] when
+    k_transposed), v [b*KVH, T, hd]. Outputs may be passed in; the launch goes to
+    torch's current stream (or ``stream``) and is asynchronous.
+    """
+
+    def __init__(self, batch: int, tokens: int, n_heads: int, head_dim: int, **kw):
+        self._lib = load_library()
+        self.desc = make_split_rope_desc(batch, tokens, n_heads, head_dim, **kw)
+        self.B, self.T, self.H, self.hd = batch, tokens, n_heads, head_dim
+        self.KVH = self.desc.n_kv_heads if self.desc.n_kv_heads > 0 else n_heads
+        self.k_transposed = bool(self.desc.k_transposed)
+        h = ctypes.c_void_p()
+        rc = self._lib.split_rope_create(ctypes.byref(self.desc), ctypes.byref(h))
+        if rc != OK:
+            raise FusedProjError(rc, "split_rope_create")
+        self._h = h
+
+    def shapes(self):
+        q = (self.B * self.H, self.T, self.hd)
+        kv = (self.B * self.KVH, self.T, self.hd)
+        k = (self.B * self.KVH, self.hd, self.T) if self.k_transposed else kv
+        return (self.B, self.T, (self.H + 2 * self.KVH) * self.hd), q, k, kv
+
+    def alloc_outputs(self, device):
+        _, qs, ks, vs = self.shapes()
+        return tuple(torch.empty(s, dtype=torch.bfloat16, device=device) for s in (qs, ks, vs))
+
+    def __call__(self, qkv: torch.Tensor, out=None, stream: torch.cuda.Stream | None = None):
+        ins, qs, ks, vs = self.shapes()
+        if tuple(qkv.shape) != ins or not qkv.is_contiguous() or qkv.dtype != torch.bfloat16 or not qkv.is_cuda:
+            raise ValueError(f"qkv must be a contiguous bf16 GPU tensor of shape {ins}")
+        q, k, v = out if out is not None else self.alloc_outputs(qkv.device)
+        for t, s in ((q, qs), (k, ks), (v, vs)):
+            if tuple(t.shape) != s or not t.is_contiguous() or t.dtype != torch.bfloat16:
+                raise ValueError(f"output must be a contiguous bf16 tensor of shape {s}")
+        st = stream if stream is not None else torch.cuda.current_stream(qkv.device)
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        rc = self._lib.split_rope_run(self._h, p(qkv), p(q), p(k), p(v), ctypes.c_void_p(st.cuda_stream))
+        if rc != OK:
+            raise FusedProjError(rc, "split_rope_run")
+        return q, k, v
+
+    def run_ptrs(self, qkv, q, k, v, stream_handle: int) -> int:
+        c = lambda a: None if a is None else ctypes.c_void_p(a)
+        return self._lib.split_rope_run(self._h, c(qkv), c(q), c(k), c(v), ctypes.c_void_p(stream_handle))
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.split_rope_destroy(self._h)
             self._h = ctypes.c_void_p()
 
     def __del__(self):

@@ -137,6 +137,8 @@ bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi
 
 }  // namespace
 
+void fp::set_last_hip_error(hipError_t e) { g_last_hip = e; }
+
 struct fused_proj_plan {
     fused_proj_desc d;
     Derived r;

@@ -80,6 +80,10 @@ enum FastShape { kFastLarge = 0, kFastSmall = 1 };
 // Kernel variants: storage type x activation layout x weight layout.
 enum class DType { BF16 = 0, F32 = 1 };
 
+// Records the HIP error that fused_proj_strerror reports for FUSED_PROJ_EHIP (both C-ABI
+// files report through it).
+void set_last_hip_error(hipError_t e);
+
 // Launches one fused projection. Returns hipSuccess or the launch error.
 hipError_t launch_fused_proj(DType dt, bool x_tokens_last, bool w_fc, const TilePlan& plan,
                              const KernelArgs& args, hipStream_t stream);

@@ -180,3 +180,50 @@ def with_shape(wl: Workload, name: str, **kw) -> Workload:
     d.update(kw)
     d["name"] = name
     return Workload(**d)
+
+
+@dataclass(frozen=True)
+class SplitRopeWorkload:
+    """A projected q/k/v tensor [batch, tokens, (H + 2*KVH)*hd] ~ N(0,1), split into
+    head-major q/k/v with RoPE (the standalone op of split_rope.h)."""
+    name: str
+    batch: int
+    tokens: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    qkv_order: str
+    rope_dims: int
+    k_transposed: bool
+    seed: int
+    pos_offset: int = 0
+    description: str = field(default="", compare=False)
+
+    @property
+    def Fq(self) -> int:
+        return (self.n_heads + 2 * self.n_kv_heads) * self.head_dim
+
+    @property
+    def alg_bytes(self) -> float:
+        """The input once, every output once (the same count), and the fp32 cos/sin table."""
+        return 2.0 * 2 * self.batch * self.tokens * self.Fq + 2 * 4 * self.tokens * (self.rope_dims // 2)
+
+
+SPLIT_ROPE_WORKLOADS = {
+    w.name: w
+    for w in [
+        # the nvFuser RoPE issue's workload: bf16 [2, 1024, 768], 16 q heads in 4 groups of
+        # head size 32, grouped columns, RoPE on the first 8 elements
+        SplitRopeWorkload("splitrope_gqa_bf16", 2, 1024, 16, 4, 32, "grouped", 8, False, 9,
+                          description="split+RoPE bf16 [2,1024,768]: 16 q / 4 k-v heads x 32, grouped, RoPE on 8"),
+        SplitRopeWorkload("splitrope_gqa_kt_bf16", 2, 1024, 16, 4, 32, "grouped", 8, True, 9,
+                          description="as splitrope_gqa_bf16 with the key written transposed [8, 32, 1024]"),
+    ]
+}
+
+
+def make_qkv(batch: int, tokens: int, width: int, seed: int):
+    """Seeded qkv ~ N(0,1) [batch, tokens, width]: the bf16 tensor and its exact float64 image."""
+    a = np.random.default_rng(seed).standard_normal((batch, tokens, width))
+    t = round_to(a, "bf16")
+    return t, as_f64(t)

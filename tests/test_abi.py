@@ -11,13 +11,15 @@ import ff_input_projection_amd as fpa
 from ff_input_projection_amd import Desc, make_desc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fused_proj.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("fused_proj.h", "split_rope.h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fused_proj_[a-z_]+)\s*\(", text)))
+    names = set()
+    for header in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+        names.update(re.findall(r"\b((?:fused_proj|split_rope)_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -27,12 +29,13 @@ def test_library_exports_every_declared_symbol():
     for name in decl:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", fpa.LIB_PATH], capture_output=True, text=True).stdout
-    exported = set(re.findall(r" T (fused_proj_\w+)", out))
+    exported = set(re.findall(r" T ((?:fused_proj|split_rope)_\w+)", out))
     assert set(decl) <= exported
 
 
 def test_header_compiles_as_plain_c():
-    src = '#include "fused_proj.h"\nint main(void){ fused_proj_desc d; (void)d; return 0; }\n'
+    src = ('#include "fused_proj.h"\n#include "split_rope.h"\n'
+           'int main(void){ fused_proj_desc d; split_rope_desc e; (void)d; (void)e; return 0; }\n')
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
                         "-x", "c", "-", "-fsyntax-only"], input=src, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
@@ -51,6 +54,46 @@ def test_desc_struct_layout_matches_c():
     os.remove(exe)
     assert vals == [ctypes.sizeof(Desc), Desc.rope_base.offset, Desc.x_stride_spatial.offset,
                     Desc.pos_offset.offset]
+
+
+def test_split_rope_desc_layout_matches_c():
+    src = ('#include <stdio.h>\n#include <stddef.h>\n#include "split_rope.h"\n'
+           'int main(void){printf("%zu %zu %zu %zu\\n", sizeof(split_rope_desc), '
+           'offsetof(split_rope_desc, rope_base), offsetof(split_rope_desc, rope_dims), '
+           'offsetof(split_rope_desc, k_transposed)); return 0;}\n')
+    exe = os.path.join("/tmp", f"sr_desc_layout_{os.getpid()}")
+    r = subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), "-x", "c", "-", "-o", exe],
+                       input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    vals = list(map(int, subprocess.run([exe], capture_output=True, text=True).stdout.split()))
+    os.remove(exe)
+    D = fpa.SplitRopeDesc
+    assert vals == [ctypes.sizeof(D), D.rope_base.offset, D.rope_dims.offset, D.k_transposed.offset]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), fpa.OK),
+    (dict(k_transposed=True), fpa.OK),
+    (dict(n_kv_heads=5), fpa.EINVAL),        # does not divide 16
+    (dict(rope_dims=9), fpa.EINVAL),         # odd rotated width
+    (dict(rope_dims=64), fpa.EINVAL),        # wider than the head
+    (dict(rope_base=0.0), fpa.EINVAL),
+    (dict(qkv_order="contiguous", n_kv_heads=16), fpa.OK),
+])
+def test_split_rope_validate(kw, code):
+    base = dict(n_kv_heads=4, qkv_order="grouped", rope_dims=8)
+    base.update(kw)
+    d = fpa.make_split_rope_desc(2, 1024, 16, 32, **base)
+    assert fpa.validate_split_rope(d) == code
+
+
+def test_split_rope_validate_unsupported():
+    d = fpa.make_split_rope_desc(2, 1024, 16, 12)            # head size not a multiple of 8
+    assert fpa.validate_split_rope(d) == fpa.EUNSUPPORTED
+    d = fpa.make_split_rope_desc(2, 1020, 16, 32, k_transposed=True)   # T not a multiple of 8
+    assert fpa.validate_split_rope(d) == fpa.EUNSUPPORTED
+    d = fpa.make_split_rope_desc(2, 1024, 16, 32, dtype=__import__("torch").float32)
+    assert fpa.validate_split_rope(d) == fpa.EUNSUPPORTED
 
 
 def walrus_desc(**kw):
