@@ -60,6 +60,15 @@ __device__ __forceinline__ float roped(const SplitRopeArgs& p, const __bf16* row
     return first ? y * c - yp * sn : y * c + yp * sn;
 }
 
+// Element idx (0..7, a runtime value) of an 8-element vector, by selects rather than an
+// indexed register access.
+__device__ __forceinline__ float pick8(const bf16x8& v, int idx) {
+    float r = (float)v[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) r = idx == k ? (float)v[k] : r;
+    return r;
+}
+
 __global__ __launch_bounds__(256) void split_rope_kernel(SplitRopeArgs p) {
     const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t total = p.q_chunks + 2 * p.kv_chunks;
@@ -96,8 +105,34 @@ __global__ __launch_bounds__(256) void split_rope_kernel(SplitRopeArgs p) {
         const int64_t bi = slab / heads;
         const __bf16* row = p.qkv + (bi * p.T + s) * p.Fq;
         const bf16x8 x = *reinterpret_cast<const bf16x8*>(row + qkv_col(p, which, h, j0));
+        const int half = p.rd >> 1;
+        if (!p.rope || which == 2 || j0 >= p.rd) {
+            o = x;   // v, and elements past the rotated width: copies
+        } else if (p.rd <= 8 || (half & 7) == 0) {
+            // the partners are in this chunk (rotated width up to 8, so j0 = 0) or form one
+            // aligned chunk half a rotated width away (half a multiple of 8: the chunk lies in
+            // one half)
+            const bf16x8 xp = p.rd <= 8 ? x
+                                        : *reinterpret_cast<const bf16x8*>(
+                                              row + qkv_col(p, which, h, j0 < half ? j0 + half : j0 - half));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (__bf16)roped(p, row, which, h, j0 + e, (float)x[e], s);
+            for (int e = 0; e < 8; ++e) {
+                const int j = j0 + e;
+                if (j >= p.rd) {
+                    o[e] = x[e];
+                    continue;
+                }
+                const bool first = j < half;
+                const int i = first ? j : j - half;
+                const float yp = p.rd <= 8 ? pick8(xp, first ? e + half : e - half) : (float)xp[e];
+                const float c = p.rope_cos[(int64_t)s * half + i], sn = p.rope_sin[(int64_t)s * half + i];
+                const float y = (float)x[e];
+                o[e] = (__bf16)(first ? y * c - yp * sn : y * c + yp * sn);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = (__bf16)roped(p, row, which, h, j0 + e, (float)x[e], s);
+        }
     }
     __builtin_nontemporal_store(o, reinterpret_cast<bf16x8*>(out) + cc);
 }
