@@ -111,7 +111,7 @@ def main() -> int:
                                       ff_dim=wl.ff_dim, ff_act=wl.ff_act, n_heads=wl.n_heads,
                                       head_dim=wl.head_dim, rope=wl.rope, rope_base=wl.rope_base,
                                       pos_offset=wl.pos_offset, n_kv_heads=wl.n_kv_heads,
-                                      qkv_order=wl.qkv_order, rope_dims=wl.rope_dims)
+                                      qkv_order=wl.qkv_order, rope_dims=wl.rope_dims, ff_layout=wl.ff_layout)
     outs = [proj.alloc_outputs(dev) for _ in range(ring)]
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
@@ -232,7 +232,12 @@ def main() -> int:
         ff, q, k, v = outs[0]
         bi = torch.from_numpy(tokens // wl.S).to(dev)
         si = torch.from_numpy(tokens % wl.S).to(dev)
-        got = [None if ff is None else ff.view(wl.nb, wl.S, wl.ff_dim)[bi, si].double().cpu().numpy()]
+        if ff is None:
+            got = [None]
+        elif wl.ff_layout == "channels_first":
+            got = [ff.view(wl.nb, wl.ff_dim, wl.S)[bi, :, si].double().cpu().numpy()]
+        else:
+            got = [ff.view(wl.nb, wl.S, wl.ff_dim)[bi, si].double().cpu().numpy()]
         for t, heads in ((q, wl.n_heads), (k, wl.kvh), (v, wl.kvh)):
             got.append(None if t is None else
                        t.view(wl.nb, heads, wl.S, wl.head_dim)[bi, :, si].double().cpu().numpy())

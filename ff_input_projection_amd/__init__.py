@@ -49,6 +49,7 @@ class Desc(ctypes.Structure):
         ("n_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
         ("rope", ctypes.c_int32), ("rope_base", ctypes.c_double), ("pos_offset", ctypes.c_int64),
         ("n_kv_heads", ctypes.c_int64), ("qkv_order", ctypes.c_int32), ("rope_dims", ctypes.c_int64),
+        ("ff_layout", ctypes.c_int32),
     ]
 
 
@@ -132,7 +133,8 @@ _DTYPES = {torch.bfloat16: BF16, torch.float32: F32}
 def make_desc(x_shape, x_strides, layout: str, dtype: torch.dtype, *, w_layout: str = "cf",
               has_bias: bool = False, ff_dim: int = 0, ff_act: str = "none", n_heads: int = 0,
               head_dim: int = 0, rope: bool = False, rope_base: float = 10000.0, pos_offset: int = 0,
-              n_kv_heads: int = 0, qkv_order: str = "contiguous", rope_dims: int = 0) -> Desc:
+              n_kv_heads: int = 0, qkv_order: str = "contiguous", rope_dims: int = 0,
+              ff_layout: str = "tokens_last") -> Desc:
     """Descriptor from an activation's shape and element strides.
     layout "channels_first": x [b, c, spatial...] (1-3 spatial dims);
     layout "tokens_last": x [b, s, c]."""
@@ -163,6 +165,7 @@ def make_desc(x_shape, x_strides, layout: str, dtype: torch.dtype, *, w_layout: 
     d.n_kv_heads = n_kv_heads
     d.qkv_order = {"contiguous": QKV_CONTIGUOUS, "grouped": QKV_GROUPED}[qkv_order]
     d.rope_dims = rope_dims
+    d.ff_layout = {"tokens_last": 0, "channels_first": 1}[ff_layout]
     return d
 
 
@@ -192,6 +195,7 @@ class FusedProjection:
         self.B, self.C = d.batch, d.channels
         self.H, self.hd, self.ff_dim = d.n_heads, d.head_dim, d.ff_dim
         self.KVH = d.n_kv_heads if d.n_kv_heads > 0 else d.n_heads
+        self.ff_channels_first = d.ff_layout == 1
         self.F = d.ff_dim + (d.n_heads + 2 * self.KVH) * d.head_dim
         self.has_bias = bool(d.has_bias)
         h = ctypes.c_void_p()
@@ -210,8 +214,11 @@ class FusedProjection:
         return buf.value.decode()
 
     def out_shapes(self):
-        """(ff, q, kv) shapes: ff [b, S, ff_dim], q [b*H, S, hd], k and v [b*KVH, S, hd]."""
-        ff = (self.B, self.S, self.ff_dim) if self.ff_dim > 0 else None
+        """(ff, q, kv) shapes: ff [b, S, ff_dim] (or [b, ff_dim, S]), q [b*H, S, hd], k and v
+        [b*KVH, S, hd]."""
+        ff = None
+        if self.ff_dim > 0:
+            ff = (self.B, self.ff_dim, self.S) if self.ff_channels_first else (self.B, self.S, self.ff_dim)
         q = (self.B * self.H, self.S, self.hd) if self.H * self.hd > 0 else None
         kv = (self.B * self.KVH, self.S, self.hd) if self.H * self.hd > 0 else None
         return ff, q, kv

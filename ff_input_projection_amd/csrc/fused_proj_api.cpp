@@ -55,6 +55,8 @@ int check_desc(const fused_proj_desc* d, Derived* out) {
     if (d->n_kv_heads > 0 && d->n_heads % d->n_kv_heads != 0) return FUSED_PROJ_EINVAL;
     if (d->qkv_order != FUSED_PROJ_QKV_CONTIGUOUS && d->qkv_order != FUSED_PROJ_QKV_GROUPED) return FUSED_PROJ_EINVAL;
     if (d->rope_dims < 0) return FUSED_PROJ_EINVAL;
+    if (d->ff_layout != FUSED_PROJ_FF_TOKENS_LAST && d->ff_layout != FUSED_PROJ_FF_CHANNELS_FIRST)
+        return FUSED_PROJ_EINVAL;
     if (d->x_layout == FUSED_PROJ_X_TOKENS_LAST ? d->n_spatial != 1 : (d->n_spatial < 1 || d->n_spatial > 3))
         return FUSED_PROJ_EINVAL;
     if (d->x_stride_batch < 0 || d->x_stride_channel < 0) return FUSED_PROJ_EINVAL;
@@ -96,6 +98,8 @@ int check_desc(const fused_proj_desc* d, Derived* out) {
         if (d->ff_dim % hd) return FUSED_PROJ_EUNSUPPORTED;   // heads start on head boundaries
         if (add_cap(S, d->pos_offset) < 0 || S + d->pos_offset > kMaxIndex) return FUSED_PROJ_EUNSUPPORTED;
     }
+    // a channels-first ff output is stored V tokens of one column at a time
+    if (d->ff_layout == FUSED_PROJ_FF_CHANNELS_FIRST && d->ff_dim > 0 && S % V) return FUSED_PROJ_EUNSUPPORTED;
     // Canonical strides.
     r.sb = d->x_stride_batch;
     r.sc = d->x_stride_channel;
@@ -210,7 +214,8 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     // ... and the plain multi-head layout: as many k/v heads as q heads, contiguous order,
     // the full head rotated
     const bool fast_heads = r.kvh == desc->n_heads && desc->qkv_order == FUSED_PROJ_QKV_CONTIGUOUS &&
-                            (!desc->rope || r.rd == desc->head_dim);
+                            (!desc->rope || r.rd == desc->head_dim) &&
+                            (desc->ff_dim == 0 || desc->ff_layout == FUSED_PROJ_FF_TOKENS_LAST);
     h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && addressable && fast_act && fast_heads &&
               (exact || want_fast) && !want_general;
     h->dg = dg < 0 ? 0 : dg;
@@ -232,6 +237,7 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     a.n_kv_heads = (int32_t)r.kvh;
     a.qkv_grouped = desc->qkv_order == FUSED_PROJ_QKV_GROUPED ? 1 : 0;
     a.rope_dims = (int32_t)r.rd;
+    a.ff_channels_first = desc->ff_layout == FUSED_PROJ_FF_CHANNELS_FIRST ? 1 : 0;
     a.act = desc->ff_act == FUSED_PROJ_ACT_GELU_ERF      ? 1
             : desc->ff_act == FUSED_PROJ_ACT_GELU_TANH     ? 2
             : desc->ff_act == FUSED_PROJ_ACT_RELU_SQUARED ? 3

@@ -51,6 +51,7 @@ struct KernelArgs {
     int32_t n_kv_heads;  // k and v heads (n_heads unless grouped-query)
     int32_t qkv_grouped; // 0: q, k, v columns contiguous; 1: grouped per k/v head
     int32_t rope_dims;   // rotated width of each q/k head (head_dim unless partial)
+    int32_t ff_channels_first;  // 1: ff stored [b, ff_dim, S] (general kernel only)
     int32_t act;         // ff slice: 0 none, 1 exact-erf GELU, 2 tanh GELU, 3 squared ReLU
     int32_t rope;        // 1: RoPE on q and k
     int32_t tiles_m;

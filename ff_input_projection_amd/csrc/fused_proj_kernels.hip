@@ -353,6 +353,38 @@ __global__ __launch_bounds__(kThreads, 2) void fused_proj_tile_kernel(KernelArgs
     const int pcol = g * OV + (first_half ? half : -half);
     const int heads = kind == 1 ? p.n_heads : kvh;
     T* const dst = static_cast<T*>(kind == 0 ? p.ff : kind == 1 ? p.q : kind == 2 ? p.k : p.v);
+    auto activate = [&](float (&y)[OV]) __attribute__((always_inline)) {
+        if (p.act == 1) {
+#pragma unroll
+            for (int e = 0; e < OV; ++e) y[e] = gelu_erf(y[e]);
+        } else if (p.act == 2) {
+#pragma unroll
+            for (int e = 0; e < OV; ++e) y[e] = gelu_tanh(y[e]);
+        } else if (p.act == 3) {
+#pragma unroll
+            for (int e = 0; e < OV; ++e) y[e] = relu_squared(y[e]);
+        }
+    };
+
+    if (kind == 0 && p.ff_channels_first) {
+        // ff[bi, f, s] (the 1x1x1-convolution layout): each store holds OV consecutive tokens
+        // of one column. Rows start at multiples of OV and S is a multiple of OV (checked on
+        // the host), so those tokens lie in one slab and all exist once the first does.
+        for (int rc = rsub; rc < BM / OV; rc += RPP) {
+            const int m = m0 + rc * OV;
+            if (m >= p.M) break;
+            const int bi = m / p.S, s0 = m - bi * p.S;
+#pragma unroll
+            for (int c = 0; c < OV; ++c) {
+                float y[OV];
+#pragma unroll
+                for (int e = 0; e < OV; ++e) y[e] = Cs[(rc * OV + e) * CST + g * OV + c];
+                activate(y);
+                store16<T>(dst + ((int64_t)bi * p.ff_dim + f0 + c) * p.S + s0, y);
+            }
+        }
+        return;
+    }
 
     for (int row = rsub; row < BM; row += RPP) {
         const int m = m0 + row;
@@ -365,16 +397,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_proj_tile_kernel(KernelArgs
             y[e] = t.x; y[e + 1] = t.y; y[e + 2] = t.z; y[e + 3] = t.w;
         }
         if (kind == 0) {
-            if (p.act == 1) {
-#pragma unroll
-                for (int e = 0; e < OV; ++e) y[e] = gelu_erf(y[e]);
-            } else if (p.act == 2) {
-#pragma unroll
-                for (int e = 0; e < OV; ++e) y[e] = gelu_tanh(y[e]);
-            } else if (p.act == 3) {
-#pragma unroll
-                for (int e = 0; e < OV; ++e) y[e] = relu_squared(y[e]);
-            }
+            activate(y);
             store16<T>(dst + (int64_t)m * p.ff_dim + f0, y);
         } else {
             const int bi = m / p.S, s = m - bi * p.S;

@@ -49,6 +49,7 @@ class Workload:
     n_kv_heads: int = 0     # k/v heads (0: n_heads)
     qkv_order: str = "contiguous"   # or "grouped" (per k/v head: its q heads, k, v)
     rope_dims: int = 0      # rotated width of each q/k head (0: head_dim)
+    ff_layout: str = "tokens_last"  # or "channels_first": ff [b, ff_dim, S] (1x1x1-convolution layout)
 
     @property
     def kvh(self) -> int:
@@ -128,6 +129,11 @@ WORKLOADS = {
                  n_kv_heads=4, qkv_order="grouped", rope_dims=8,
                  description="lit-gpt GQA bf16: x [2,1024,512], W [512,768], 16 q heads / 4 k-v groups x 32, "
                              "grouped columns, RoPE on 8 of 32"),
+        # The Walrus page's 1x1x1 Conv3d comparison: the temporal q/k/v projection of the
+        # latent grid as a convolution, output channels-first [24, 2304, 32, 32, 1]
+        Workload("conv1x1_walrus_bf16", "bf16", "channels_first", (24, 768, 32, 32, 1), 2304, "none", 0, 0, True,
+                 False, 10, ff_layout="channels_first",
+                 description="1x1x1 Conv3d-shaped bf16: x [24,768,32,32,1] -> [24,2304,32,32,1] channels-first"),
         # The Walrus block at the width its profiles imply (C = 1408, F = 7C: FF 4C and
         # Q/K/V C each): F is not a multiple of 256, so the last large column tile is ragged.
         Workload("walrus_c1408_bf16", "bf16", "channels_first", (24, 1408, 32, 32, 1), 5632, "gelu", 22, 64, True,

@@ -14,6 +14,7 @@
  *   columns each (head h, element j at slice column h*head_dim + j):
  *
  *     ff[bi, s, f]            = act(y[t, f])                    act: see FUSED_PROJ_ACT_*
+ *                               (or ff[bi, f, s], see FUSED_PROJ_FF_*)
  *     q[bi*H + h, s, j]       = RoPE_p(y[t, Q0 + h*hd + .])[j]  p = s + pos_offset
  *     k[bi*H + h, s, j]       = RoPE_p(y[t, K0 + h*hd + .])[j]
  *     v[bi*H + h, s, j]       = y[t, V0 + h*hd + j]
@@ -94,6 +95,12 @@ extern "C" {
  * once per group, not repeated for every q head. */
 #define FUSED_PROJ_QKV_GROUPED 1
 
+/* Layout of the ff output. */
+#define FUSED_PROJ_FF_TOKENS_LAST 0   /* ff[bi, s, f] */
+/* ff[bi, f, s]: channels-first like x, the output of the equivalent 1x1x1 convolution (the
+ * Walrus PR compares the fused linear with a 1x1x1 Conv3d). Runs on the general kernel. */
+#define FUSED_PROJ_FF_CHANNELS_FIRST 1
+
 typedef struct fused_proj_desc {
     int32_t dtype;             /* FUSED_PROJ_BF16 | FUSED_PROJ_F32 */
     int32_t x_layout;          /* FUSED_PROJ_X_* */
@@ -121,6 +128,7 @@ typedef struct fused_proj_desc {
                                   head_dim. Elements from rope_dims on pass through; the
                                   angles are (s + pos_offset) * base^(-2i/rope_dims)
                                   (rope_one_entry with rope_n_elem in the same issue). */
+    int32_t ff_layout;         /* FUSED_PROJ_FF_*; channels-first needs S a multiple of V */
 } fused_proj_desc;
 
 typedef struct fused_proj_plan *fused_proj_t;

@@ -15,7 +15,7 @@ def plan_for(wl: Workload, x: torch.Tensor) -> FusedProjection:
     return FusedProjection.for_tensor(
         x, wl.layout, w_layout=wl.w_layout, has_bias=wl.has_bias, ff_dim=wl.ff_dim, ff_act=wl.ff_act,
         n_heads=wl.n_heads, head_dim=wl.head_dim, rope=wl.rope, rope_base=wl.rope_base, pos_offset=wl.pos_offset,
-        n_kv_heads=wl.n_kv_heads, qkv_order=wl.qkv_order, rope_dims=wl.rope_dims)
+        n_kv_heads=wl.n_kv_heads, qkv_order=wl.qkv_order, rope_dims=wl.rope_dims, ff_layout=wl.ff_layout)
 
 
 def run_gpu(wl: Workload, inp, device="cuda:0", x_dev: torch.Tensor | None = None):
@@ -49,7 +49,9 @@ def gpu_rows(wl: Workload, outs, tokens: np.ndarray):
     bi = torch.from_numpy(tokens // wl.S)
     s = torch.from_numpy(tokens % wl.S)
     res = []
-    if ff is not None:
+    if ff is not None and wl.ff_layout == "channels_first":
+        res.append(ff.view(wl.nb, wl.ff_dim, wl.S)[bi.to(ff.device), :, s.to(ff.device)].double().cpu().numpy())
+    elif ff is not None:
         res.append(ff.view(wl.nb, wl.S, wl.ff_dim)[bi.to(ff.device), s.to(ff.device)].double().cpu().numpy())
     else:
         res.append(None)

@@ -131,6 +131,7 @@ def test_validate_accepts_every_activation():
     (lambda d: setattr(d, "qkv_order", 2), fpa.EINVAL),
     (lambda d: setattr(d, "rope_dims", 7), fpa.EINVAL),      # odd rotated width
     (lambda d: setattr(d, "rope_dims", 128), fpa.EINVAL),    # wider than the 64-element head
+    (lambda d: setattr(d, "ff_layout", 2), fpa.EINVAL),
     (lambda d: setattr(d, "batch", -1), fpa.EINVAL),
     (lambda d: setattr(d, "n_spatial", 4), fpa.EINVAL),
     (lambda d: setattr(d, "head_dim", 0), fpa.EINVAL),             # heads without width

@@ -102,6 +102,14 @@ SMALL = [
                n_heads=4, head_dim=64, n_kv_heads=1, qkv_order="grouped", seed=124),
     with_shape(WORKLOADS["tiny_f32"], "f32_gqa_grouped_rope4", layout="tokens_last", x_shape=(2, 30, 32), ff_dim=0,
                n_heads=4, head_dim=8, n_kv_heads=2, qkv_order="grouped", rope_dims=4, has_bias=True, seed=125),
+    # channels-first ff output (the 1x1x1-convolution layout; general kernel): with q/k/v
+    # and RoPE on a channels-first x, GELU on a token-major x, and fp32
+    with_shape(WORKLOADS["walrus_bf16"], "cf_ff_channels_first", x_shape=(2, 64, 8, 16, 1), ff_dim=128,
+               n_heads=2, head_dim=32, ff_layout="channels_first", seed=126),
+    with_shape(WORKLOADS["bert_ff_bf16"], "tl_ff_channels_first", x_shape=(3, 40, 96), ff_dim=136,
+               ff_layout="channels_first", seed=127),
+    with_shape(WORKLOADS["tiny_f32"], "f32_cf_ff_channels_first", x_shape=(1, 32, 6, 6, 1), ff_dim=64,
+               ff_layout="channels_first", seed=128),
     # fp32, token-major, [F,C], RoPE hd 8, GELU
     with_shape(WORKLOADS["tiny_f32"], "f32_tl_fc", layout="tokens_last", x_shape=(3, 50, 36), ff_dim=16,
                n_heads=3, head_dim=8, w_layout="fc", seed=106),

@@ -101,6 +101,18 @@ def test_layout_invariance_channels_first_vs_contiguous_copy():
         assert np.array_equal(a, c)
 
 
+def test_ff_slice_equals_1x1x1_conv3d():
+    """The ff slice of a channels-first input, laid out channels-first, is the 1x1x1
+    Conv3d the Walrus PR compares the linear with: torch's conv3d in float64 (a library
+    routine) with the weight W[:, :ff]^T as [ff, C, 1, 1, 1] and the bias."""
+    x, w, b = rng_inputs(51, (2, 6, 3, 4, 2), 6, 10)
+    res = oracle.fused_proj(x, "channels_first", w, "cf", b, 10, "none", 0, 0, rope=False)
+    ff_cf = res.ff.reshape(2, 3, 4, 2, 10).transpose(0, 4, 1, 2, 3)           # [b, ff, h, w, d]
+    conv = torch.nn.functional.conv3d(torch.from_numpy(x), torch.from_numpy(w.T.copy()).reshape(10, 6, 1, 1, 1),
+                                      torch.from_numpy(b)).numpy()
+    assert np.allclose(ff_cf, conv, rtol=0, atol=1e-13)
+
+
 def test_strided_view_equals_contiguous_copy():
     """x as a channel slice of a larger tensor (non-unit batch stride) and a view with
     a transposed spatial order give the same result as contiguous copies."""
