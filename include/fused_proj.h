@@ -9,21 +9,25 @@
  *
  *     y[t, f] = sum_c x[t, c] * W[c, f] + bias[f],        f in [0, F)
  *
- *   as one [tokens, C] x [C, F] product. The columns split, in this order,
- *   into an ff slice [0, ff_dim), then q, k and v slices of n_heads*head_dim
- *   columns each (head h, element j at slice column h*head_dim + j):
+ *   as one [tokens, C] x [C, F] product. The columns split into an ff slice
+ *   [0, ff_dim), then H q heads and KVH k and v heads of head_dim columns each
+ *   (F = ff_dim + (H + 2*KVH)*hd). In the default contiguous order the q slice
+ *   comes first (head h, element j at slice column h*hd + j), then the k slice,
+ *   then the v slice; FUSED_PROJ_QKV_GROUPED groups them per k/v head instead.
  *
  *     ff[bi, s, f]            = act(y[t, f])                    act: see FUSED_PROJ_ACT_*
  *                               (or ff[bi, f, s], see FUSED_PROJ_FF_*)
- *     q[bi*H + h, s, j]       = RoPE_p(y[t, Q0 + h*hd + .])[j]  p = s + pos_offset
- *     k[bi*H + h, s, j]       = RoPE_p(y[t, K0 + h*hd + .])[j]
- *     v[bi*H + h, s, j]       = y[t, V0 + h*hd + j]
+ *     q[bi*H + h, s, j]       = RoPE_p(q head h of y[t, .])[j]  p = s + pos_offset
+ *     k[bi*KVH + g, s, j]     = RoPE_p(k head g of y[t, .])[j]
+ *     v[bi*KVH + g, s, j]     = v head g of y[t, .], element j
  *
- *   RoPE is rotate-half: for i < hd/2, with phi = p * base^(-2i/hd),
- *     out[i]        = y[i] cos(phi) - y[i + hd/2] sin(phi)
- *     out[i + hd/2] = y[i + hd/2] cos(phi) + y[i] sin(phi).
- *   Accumulation, bias, GELU and RoPE run in fp32; each output is rounded once
- *   to the storage type (round to nearest even).
+ *   RoPE is rotate-half over the first rd = rope_dims (default hd) elements of a
+ *   head: for i < rd/2, with phi = p * base^(-2i/rd),
+ *     out[i]        = y[i] cos(phi) - y[i + rd/2] sin(phi)
+ *     out[i + rd/2] = y[i + rd/2] cos(phi) + y[i] sin(phi),
+ *   and elements from rd on pass through.
+ *   Accumulation, bias, the activation and RoPE run in fp32; each output is
+ *   rounded once to the storage type (round to nearest even).
  *
  * Where each part is defined:
  *   - gather + single GEMM instead of one GEMV per token: Walrus PR
