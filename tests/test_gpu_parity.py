@@ -163,6 +163,34 @@ def test_other_activations_never_take_the_fast_kernel(monkeypatch):
         _check(wl, inp, outs, all_tokens(wl), wl.name)
 
 
+RAGGED_M = [
+    # token counts that are not whole tiles, forced onto the fast kernel: large tiles
+    # (16300 tokens, 640 tiles of 256 x 256, RoPE, GELU, token-major) and small tiles
+    # (8144 tokens of the small-K shape, channels-first, slabs of 4072 tokens)
+    with_shape(WORKLOADS["bert_qkv_bf16"], "tl_large_tiles_ragged_m", x_shape=(2, 8150, 256), ff_dim=1024,
+               ff_act="gelu", n_heads=8, head_dim=64, rope=True, seed=129),
+    with_shape(WORKLOADS["smallk_qkv_bf16"], "cf_small_tiles_ragged_m", x_shape=(2, 320, 4072), seed=130),
+]
+
+
+@pytest.mark.parametrize("wl", RAGGED_M, ids=[w.name for w in RAGGED_M])
+def test_fast_kernel_ragged_token_count(wl, monkeypatch):
+    """The fast kernel on token counts that are not whole tiles: tokens past M read token
+    0 and are not stored. Sampled tokens include the last ones and the slab boundary."""
+    monkeypatch.setenv("FUSED_PROJ_KERNEL", "fast")
+    print(f"[case] fast kernel, ragged M: {wl.name} x={wl.x_shape} M={wl.M}", flush=True)
+    inp = make_inputs(wl)
+    proj, outs = run_gpu(wl, inp, DEV)
+    desc = proj.describe()
+    print(f"[plan] {desc}", flush=True)
+    assert "fused_proj_fast_kernel" in desc, desc
+    tokens = np.unique(np.concatenate([sample_tokens(wl, 384, seed=3), np.arange(wl.M - 300, wl.M)]))
+    _check(wl, inp, outs, tokens, wl.name)
+    for t in outs:
+        if t is not None:
+            assert torch.isfinite(t).all().item()
+
+
 LARGE_FC = [
     # [F,C] weights (nn.Linear layout) on the large tiles, both x layouts: 8192 tokens,
     # C = 256, F = 1024 + 3 * 512 = 2560 (320 tiles of 256 x 256), RoPE hd 64, GELU
