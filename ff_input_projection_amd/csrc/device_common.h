@@ -19,54 +19,6 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-// ---------------------------------------------------------------- LDS swizzles (16-byte chunks)
-// The LDS has 64 four-byte banks (256 bytes per sweep); measured on gfx950 these
-// layouts let every MFMA-operand read run at the full ds_read rate.
-//
-// K-major tile: rows of CPR chunks (the contiguous k axis). Chunk c of row r sits
-// at c ^ ((r * CPR / 16) mod CPR): the 16 rows read together by one 16-lane
-// phase then cover all 16 chunk slots of a bank sweep.
-template <int CPR>
-__device__ __forceinline__ int kmaj_chunk(int r, int c) {
-    static_assert(CPR == 4 || CPR == 8 || CPR == 16, "K-major rows of 4, 8 or 16 chunks");
-    return r * CPR + (c ^ ((r * CPR / 16) % CPR));
-}
-// M/N-major tile: rows are k, CPR chunks of the contiguous m (or n) axis. Chunk c of
-// row k sits at c ^ (4 * (k mod 4)), so the 4 k rows read by one transposing load
-// land in 4 different 64-byte bank groups.
-template <int CPR>
-__device__ __forceinline__ int mnmaj_chunk(int k, int c) {
-    static_assert(CPR >= 16, "M/N-major rows need at least 16 chunks");
-    return k * CPR + (c ^ ((k & 3) << 2));
-}
-
-// ---------------------------------------------------------------- MFMA operands from LDS
-// 32x32x16 bf16 operand for rows rb..rb+31 (the MFMA row for A, column for B) at
-// k step kk of the tile: lane l holds row rb + l%32, k = 16kk + 8(l/32) + [0..7].
-template <int CPR>
-__device__ __forceinline__ bf16x8 operand_kmajor(const __bf16* tile, int rb, int kk, int lane) {
-    const int r = rb + (lane & 31);
-    const int c = kk * 2 + (lane >> 5);
-    const u32x4 v = reinterpret_cast<const u32x4*>(tile)[kmaj_chunk<CPR>(r, c)];
-    return __builtin_bit_cast(bf16x8, v);
-}
-// Transposing variant for an M/N-major tile. ds_read_b64_tr_b16: in each 16-lane
-// group, lane 4r+c names row r, columns 4c..4c+3 of a 4 x 16 block and receives
-// column (lane mod 16) of the 4 rows. Two reads give the 8 k of one operand.
-template <int CPR>
-__device__ __forceinline__ bf16x8 operand_mnmajor(const __bf16* tile, int rb, int kk, int lane) {
-    const int g = lane >> 4, q = lane & 15;
-    const int m = rb + (g & 1) * 16 + (q & 3) * 4;
-    const int k = kk * 16 + (g >> 1) * 8 + (q >> 2);
-    const short* base = reinterpret_cast<const short*>(tile);
-    const int e1 = mnmaj_chunk<CPR>(k, m >> 3) * 8 + (m & 7);
-    const int e2 = mnmaj_chunk<CPR>(k + 4, m >> 3) * 8 + (m & 7);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + e1));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + e2));
-    const i16x8 v = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    return __builtin_bit_cast(bf16x8, v);
-}
-
 // ---------------------------------------------------------------- epilogue arithmetic
 // erf by Abramowitz & Stegun, Handbook of Mathematical Functions, eq. 7.1.26
 // (Hastings' rational-exponential form): erf(x) = 1 - (a1 t + ... + a5 t^5) e^{-x^2},
@@ -85,24 +37,6 @@ __device__ __forceinline__ float erf_as7126(float x) {
 // Exact-erf GELU: y * Phi(y) = 0.5 y (1 + erf(y / sqrt 2)).
 __device__ __forceinline__ float gelu_erf(float y) {
     return 0.5f * y * (1.0f + erf_as7126(y * 0.70710678118654752440f));
-}
-
-// The same GELU, rearranged for fewer instructions. With a = |y|, eq. 7.1.26 gives
-// erfc(a/sqrt2) ~= P(t) exp(-a^2/2), t = 1/(1 + (p/sqrt2) a). Phi(y) = 1 - erfc/2 for
-// y >= 0 and erfc/2 for y < 0, so with h = y P(t) exp(-y^2/2) / 2 (sign of y):
-// GELU(y) = y - h (y >= 0), h (y < 0), i.e. max(y, 0) - |h|. The 1/2 is folded into
-// the coefficients and log2(e)/2 into the exponent.
-__device__ __forceinline__ float gelu_erf_fast(float y) {
-    const float a = fabsf(y);
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, a, 1.0f));
-    float q = fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
-    q = fmaf(q, t, 0.5f * 1.421413741f);
-    q = fmaf(q, t, 0.5f * -0.284496736f);
-    q = fmaf(q, t, 0.5f * 0.254829592f);
-    q *= t;
-    const float e = __builtin_amdgcn_exp2f((y * y) * -0.72134752044448170368f);  // exp(-y^2/2)
-    const float h = (y * q) * e;
-    return fmaxf(y, 0.0f) - fabsf(h);
 }
 
 // The same GELU with one exp2 and no reciprocal. With a = |y| and q(a) = Phi(-a) =
@@ -140,8 +74,6 @@ __device__ __forceinline__ float relu_squared(float y) {
     const float r = y > 0.0f ? y : 0.0f;
     return r * r;
 }
-
-__device__ __forceinline__ float bf16_to_f32(__bf16 v) { return (float)v; }
 
 // Tile of linear block id. Workgroups are dispatched round-robin over the 8 XCDs
 // (each with its own L2): every XCD is given a contiguous range of tiles, walked in

@@ -11,9 +11,8 @@
 //     in the same lane, hd/32 MFMA row tiles (or hd/16 column groups) away;
 //   - stores into ff [b,S,ff] and the head-major q/k/v buffers [b*H,S,hd]
 //     (memory-efficient-attention issue "Improve performance via batched-matmul
-//     and fused multiplies"), with consecutive tokens adjacent in q/k/v: 8 bytes
-//     per lane straight from registers, or restaged through LDS into whole
-//     256-byte token rows.
+//     and fused multiplies"), with consecutive tokens adjacent in q/k/v,
+//     restaged through LDS into whole 256-byte token rows.
 // Every branch of the compute part of the epilogue depends only on the column
 // group, which is the same for the whole wave, so it never diverges.
 //
@@ -61,21 +60,13 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Four fp32 values rounded to bf16, as 8 bytes; and stored.
+// Four fp32 values rounded to bf16, as 8 bytes.
 __device__ __forceinline__ u32x2 pack4_bf16(const float* o) {
     bf16x4 v;
 #pragma unroll
     for (int u = 0; u < 4; ++u) v[u] = (__bf16)o[u];
     return __builtin_bit_cast(u32x2, v);
 }
-// Output stores are non-temporal (global_store ... nt): the outputs are written once and
-// not read again here, so they should not hold L2 lines that the operand panels use, nor
-// be left dirty in the XCD's L2 for the write-back at the end of the kernel. Measured on
-// the Walrus-sized block: 222.8 -> 217.3 us per launch; small-K shape: 14.5 -> 12.6 us.
-__device__ __forceinline__ void store4_bf16(char* dst, const float* o) {
-    __builtin_nontemporal_store(pack4_bf16(o), reinterpret_cast<u32x2*>(dst));
-}
-
 // Four bf16 bias values from LDS, as fp32.
 __device__ __forceinline__ f32x4 bias4(const __bf16* p) {
     const bf16x4 v = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(p));
@@ -338,11 +329,11 @@ __device__ __forceinline__ bool block_tile(int k, const KernelArgs& p, int& tt, 
 //    the idle stages after the last K step).
 struct LargeTile {
     static constexpr int BF = 256, BT = 256, NWF = 2, NWT = 4, PER_CU = 1, STAGES = 4, PF = 3, WPE = 2;
-    static constexpr bool RESTAGE = true, SINGLE = false;
+    static constexpr bool SINGLE = false;
 };
 struct SmallTile {
     static constexpr int BF = 128, BT = 128, NWF = 1, NWT = 4, PER_CU = 2, STAGES = 5, PF = 4, WPE = 2;
-    static constexpr bool RESTAGE = true, SINGLE = true;
+    static constexpr bool SINGLE = true;
 };
 
 constexpr int kBK = 32;
@@ -360,7 +351,7 @@ fused_proj_fast_kernel(KernelArgs p) {
     // tile in flight, in the idle last stage and the spare bytes after it; single-tile
     // workgroups anywhere in the (then idle) stage area
     constexpr int RGN_ALL = T::NWF * T::NWT / 2 * kRestageRows * kRestageRow, W_STAGE = BF * kBK * 2;
-    constexpr int PAD = T::RESTAGE && !T::SINGLE && RGN_ALL > W_STAGE ? RGN_ALL - W_STAGE : 0;
+    constexpr int PAD = !T::SINGLE && RGN_ALL > W_STAGE ? RGN_ALL - W_STAGE : 0;
     using C = FastCfg<X_TL, W_FC, BF, BT, T::NWF, kNWT, BK, STAGES, PAD>;
     using Pipe = FastPipe<C, X_TL, W_FC, BK, TAILK>;
     using Ops = typename Pipe::Ops;
@@ -369,7 +360,7 @@ fused_proj_fast_kernel(KernelArgs p) {
     static_assert(T::SINGLE || (PF == 3 && (STAGES == 3 || STAGES == 4)),
                   "the multi-tile wait counts below are written for three steps ahead");
     static_assert(!T::SINGLE || (PF >= 2 && PF <= 5 && STAGES == PF + 1), "single-tile pipeline depth");
-    static_assert(!T::RESTAGE || T::SINGLE || STAGES == 4, "the restaged epilogue uses the idle fourth stage");
+    static_assert(T::SINGLE || STAGES == 4, "the restaged epilogue uses the idle fourth stage");
     static_assert(!T::SINGLE || C::NW * kRestageRows * kRestageRow <= C::LDS_BYTES, "single-tile restage rows");
     static_assert(NG == 16, "one 16-entry column descriptor load per wave");
     // LDS: the stages, then (multi-tile workgroups) the tile bias, double-buffered. A
@@ -576,10 +567,11 @@ fused_proj_fast_kernel(KernelArgs p) {
         // ---- epilogue. acc[a][j][e] (bias included): column f = 32a + 8(e/4) + 4(lane/32)
         // + e%4, token 32j + lane%32 (both relative to the wave tile). Outputs never overlap
         // the inputs (checked on the host), so loads may be hoisted above stores. GELU on ff
-        // columns and RoPE on q/k columns run in registers; the bf16 results are stored
-        // either straight from registers, 8 bytes per lane as each column group is done
-        // (large tiles: the stores drain while the rest is computed), or restaged through
-        // LDS into whole 256-byte token rows once every group is done (small tiles).
+        // columns and RoPE on q/k columns run in registers; the bf16 results of each 32-token
+        // block are restaged through LDS into whole 256-byte token rows and stored with
+        // non-temporal 16-byte stores (the outputs are written once and not read back here:
+        // they should neither evict the operand panels from the XCD's L2 nor sit dirty
+        // there for the write-back at the end of the kernel).
         const int tw0 = m0 + wt * WT;   // the wave's first token
         // The wave's 16 column groups: kind (0 ff, 1 q, 2 k, 3 v) in bits 30-31 and the
         // element offset of the group's first column in the low bits (ff: column; q/k/v:
@@ -590,240 +582,155 @@ fused_proj_fast_kernel(KernelArgs p) {
         const bool wave_rope = DG > 0 && fw < ff_dim + 2 * p.qw && fw + WF > ff_dim;
         constexpr int HD = DG > 0 ? 16 * DG : 16, HALF = HD / 2, NR = HALF / 8, NRB = NR > 4 ? 4 : NR;
 
-        if constexpr (T::RESTAGE) {
-            // The stores: written straight from the accumulator layout, a store instruction
-            // touches 32 token rows with 16 bytes each; restaged, each one writes 4 token rows of
-            // 256 contiguous bytes (the wave's 128 columns). The wave owns 16 rows of 272 bytes
-            // (a token's 128 bf16 columns and 16 bytes of padding, which keep both the row
-            // writes and the 16-byte chunk reads free of bank conflicts) in the stage no K step
-            // uses until the next tile's first barrier and the spare bytes after it. Every LDS
-            // address is a per-lane base plus a constant.
-            static_assert(T::SINGLE ||
-                              (C::W_BYTES == C::X_BYTES && C::W_BYTES + PAD >= C::NW / 2 * kRestageRows * kRestageRow),
-                          "restage regions");
-            constexpr int RGN = kRestageRows * kRestageRow;
-            // single-tile workgroups: no load is in flight after the last K step's wait and
-            // every wave has passed its barrier, so the whole stage area is free
-            const unsigned wave_lds = T::SINGLE          ? pp.lds0 + wave * RGN
-                                      : wave < C::NW / 2 ? pp.lds0 + (STAGES - 1) * C::W_BYTES + wave * RGN
-                                                         : pp.lds0 + C::X_REGION + (STAGES - 1) * C::X_BYTES +
-                                                               (wave - C::NW / 2) * RGN;
-            // The lane index again, recomputed per tile where the compiler cannot see it: the
-            // LDS addresses and column selects below depend only on it, and hoisted out of the
-            // tile loop they would hold registers through the K loop (spilled to scratch, whose
-            // reload waits for every load in flight).
-            int lane_e;
-            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
-            // writer: token row lane%16 of a 16-token half block, column half lane/32 of each
-            // group; reader: 16-byte chunk (column group) gl of token rows r0 + 4 rr
-            const int gl = lane_e & 15, r0 = lane_e >> 4;
-            const unsigned wr_lds = wave_lds + (lane_e & 15) * kRestageRow + (lane_e >> 5) * 8;
-            const unsigned rd_lds = wave_lds + r0 * kRestageRow + gl * 16;
-            // this lane's chunk: its destination buffer and element offset, and the bytes
-            // between consecutive tokens there
-            unsigned dl = desc[0];
+        // The stores: written straight from the accumulator layout, a store instruction
+        // touches 32 token rows with 16 bytes each; restaged, each one writes 4 token rows of
+        // 256 contiguous bytes (the wave's 128 columns). The wave owns 16 rows of 272 bytes
+        // (a token's 128 bf16 columns and 16 bytes of padding, which keep both the row
+        // writes and the 16-byte chunk reads free of bank conflicts) in the stage no K step
+        // uses until the next tile's first barrier and the spare bytes after it. Every LDS
+        // address is a per-lane base plus a constant.
+        static_assert(T::SINGLE ||
+                          (C::W_BYTES == C::X_BYTES && C::W_BYTES + PAD >= C::NW / 2 * kRestageRows * kRestageRow),
+                      "restage regions");
+        constexpr int RGN = kRestageRows * kRestageRow;
+        // single-tile workgroups: no load is in flight after the last K step's wait and
+        // every wave has passed its barrier, so the whole stage area is free
+        const unsigned wave_lds = T::SINGLE          ? pp.lds0 + wave * RGN
+                                  : wave < C::NW / 2 ? pp.lds0 + (STAGES - 1) * C::W_BYTES + wave * RGN
+                                                     : pp.lds0 + C::X_REGION + (STAGES - 1) * C::X_BYTES +
+                                                           (wave - C::NW / 2) * RGN;
+        // The lane index again, recomputed per tile where the compiler cannot see it: the
+        // LDS addresses and column selects below depend only on it, and hoisted out of the
+        // tile loop they would hold registers through the K loop (spilled to scratch, whose
+        // reload waits for every load in flight).
+        int lane_e;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+        // writer: token row lane%16 of a 16-token half block, column half lane/32 of each
+        // group; reader: 16-byte chunk (column group) gl of token rows r0 + 4 rr
+        const int gl = lane_e & 15, r0 = lane_e >> 4;
+        const unsigned wr_lds = wave_lds + (lane_e & 15) * kRestageRow + (lane_e >> 5) * 8;
+        const unsigned rd_lds = wave_lds + r0 * kRestageRow + gl * 16;
+        // this lane's chunk: its destination buffer and element offset, and the bytes
+        // between consecutive tokens there
+        unsigned dl = desc[0];
 #pragma unroll
-            for (int g = 1; g < 16; ++g) dl = gl == g ? desc[g] : dl;
-            const unsigned kind_l = dl >> 30;
-            char* const base_l = static_cast<char*>(kind_l == 0 ? p.ff : kind_l == 1 ? p.q : kind_l == 2 ? p.k : p.v) +
-                                 (size_t)(dl & 0x3fffffffu) * 2;
-            const unsigned stride_l = kind_l == 0 ? (unsigned)(2 * ff_dim) : (unsigned)(2 * hd);
-            char* const row0_l = base_l + r0 * stride_l;
-            const bool col_ok = fw + 8 * gl < N;
-            // the wave's tokens usually lie in one slab: then a token's offset is linear in it
-            const int bi_first = (int)fastdiv_u31((uint32_t)tw0, p.div_s);
-            const bool one_slab =
-                (int)fastdiv_u31((uint32_t)(tw0 + WT - 1 < M ? tw0 + WT - 1 : M - 1), p.div_s) == bi_first;
-            auto token_off = [&](int t) __attribute__((always_inline)) {
-                const int bi = (int)fastdiv_u31((uint32_t)t, p.div_s);
-                const int s = t - bi * S;
-                return kind_l == 0 ? (unsigned)t * (unsigned)(2 * ff_dim)
-                                   : (unsigned)(((int64_t)bi * slab_elems + (int64_t)s * hd) * 2);
-            };
+        for (int g = 1; g < 16; ++g) dl = gl == g ? desc[g] : dl;
+        const unsigned kind_l = dl >> 30;
+        char* const base_l = static_cast<char*>(kind_l == 0 ? p.ff : kind_l == 1 ? p.q : kind_l == 2 ? p.k : p.v) +
+                             (size_t)(dl & 0x3fffffffu) * 2;
+        const unsigned stride_l = kind_l == 0 ? (unsigned)(2 * ff_dim) : (unsigned)(2 * hd);
+        char* const row0_l = base_l + r0 * stride_l;
+        const bool col_ok = fw + 8 * gl < N;
+        // the wave's tokens usually lie in one slab: then a token's offset is linear in it
+        const int bi_first = (int)fastdiv_u31((uint32_t)tw0, p.div_s);
+        const bool one_slab =
+            (int)fastdiv_u31((uint32_t)(tw0 + WT - 1 < M ? tw0 + WT - 1 : M - 1), p.div_s) == bi_first;
+        auto token_off = [&](int t) __attribute__((always_inline)) {
+            const int bi = (int)fastdiv_u31((uint32_t)t, p.div_s);
+            const int s = t - bi * S;
+            return kind_l == 0 ? (unsigned)t * (unsigned)(2 * ff_dim)
+                               : (unsigned)(((int64_t)bi * slab_elems + (int64_t)s * hd) * 2);
+        };
 
-            // cos/sin of this lane's token at its 4 columns of each first-half group of a head;
-            // every head of the wave uses the same ones -- all at once for head sizes up to 64,
-            // in two halves for 128 (registers). Those of the next token block are loaded
-            // before this block's stores: a load issued after a store would wait for it too
-            // (the vector memory counter counts in order).
-            f32x4 rc[NRB], rsn[NRB];
-            auto load_rope = [&](int j, int r0) __attribute__((always_inline)) {
-                const int t = tw0 + 32 * j + (lane_e & 31);
-                const int tc = t < M ? t : 0;
-                const int s = tc - (int)fastdiv_u31((uint32_t)tc, p.div_s) * S;
-                const unsigned rp_off = (unsigned)((s * (DG * 8) + 4 * (lane_e >> 5)) * 4);
+        // cos/sin of this lane's token at its 4 columns of each first-half group of a head;
+        // every head of the wave uses the same ones -- all at once for head sizes up to 64,
+        // in two halves for 128 (registers). Those of the next token block are loaded
+        // before this block's stores: a load issued after a store would wait for it too
+        // (the vector memory counter counts in order).
+        f32x4 rc[NRB], rsn[NRB];
+        auto load_rope = [&](int j, int r0) __attribute__((always_inline)) {
+            const int t = tw0 + 32 * j + (lane_e & 31);
+            const int tc = t < M ? t : 0;
+            const int s = tc - (int)fastdiv_u31((uint32_t)tc, p.div_s) * S;
+            const unsigned rp_off = (unsigned)((s * (DG * 8) + 4 * (lane_e >> 5)) * 4);
+#pragma unroll
+            for (int r = 0; r < NRB; ++r) {
+                rc[r] = f32x4{};
+                rsn[r] = f32x4{};
+            }
+            if (wave_rope) {
 #pragma unroll
                 for (int r = 0; r < NRB; ++r) {
-                    rc[r] = f32x4{};
-                    rsn[r] = f32x4{};
+                    const char* const c = reinterpret_cast<const char*>(rope_cos + 8 * (r0 + r)) + rp_off;
+                    const char* const sn = reinterpret_cast<const char*>(rope_sin + 8 * (r0 + r)) + rp_off;
+                    rc[r] = *reinterpret_cast<const f32x4*>(c);
+                    rsn[r] = *reinterpret_cast<const f32x4*>(sn);
                 }
-                if (wave_rope) {
+            }
+        };
+        load_rope(0, 0);
 #pragma unroll
-                    for (int r = 0; r < NRB; ++r) {
-                        const char* const c = reinterpret_cast<const char*>(rope_cos + 8 * (r0 + r)) + rp_off;
-                        const char* const sn = reinterpret_cast<const char*>(rope_sin + 8 * (r0 + r)) + rp_off;
-                        rc[r] = *reinterpret_cast<const f32x4*>(c);
-                        rsn[r] = *reinterpret_cast<const f32x4*>(sn);
-                    }
-                }
-            };
-            load_rope(0, 0);
+        for (int j = 0; j < TJ; ++j) {
+            // every group's outputs rounded to bf16 (each branch packs its own results:
+            // results written back into acc under these branches would cost a register
+            // copy per value where the branches join)
+            u32x2 pk[NG];
 #pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-                // every group's outputs rounded to bf16 (each branch packs its own results:
-                // results written back into acc under these branches would cost a register
-                // copy per value where the branches join)
-                u32x2 pk[NG];
+            for (int G = 0; G < NG; ++G) pk[G] = u32x2{0u, 0u};
 #pragma unroll
-                for (int G = 0; G < NG; ++G) pk[G] = u32x2{0u, 0u};
+            for (int G = 0; G < NG; ++G) {
+                if (fw + 8 * G >= N) continue;   // ragged last column tile (not stored)
+                const unsigned kind = desc[G] >> 30;
+                float y[4];
 #pragma unroll
-                for (int G = 0; G < NG; ++G) {
-                    if (fw + 8 * G >= N) continue;   // ragged last column tile (not stored)
-                    const unsigned kind = desc[G] >> 30;
-                    float y[4];
+                for (int u = 0; u < 4; ++u) y[u] = acc[G >> 2][j][4 * (G & 3) + u];
+                if (kind == 0) {
+                    if (act == 1) {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) y[u] = acc[G >> 2][j][4 * (G & 3) + u];
-                    if (kind == 0) {
-                        if (act == 1) {
-#pragma unroll
-                            for (int u = 0; u < 4; ++u) y[u] = gelu_erf_poly(y[u]);
-                        }
-                        pk[G] = pack4_bf16(y);
-                        continue;
-                    }
-                    if (DG > 0 && kind != 3) {
-                        // Heads start on head_dim boundaries of the wave's columns, so the
-                        // group's place in its head is a compile-time constant. A first-half
-                        // group is rotated together with its partner DG groups on, which it
-                        // also packs.
-                        const int jh8 = (8 * G) % HD;
-                        if (jh8 >= HALF || G + DG >= NG) continue;
-                        const int G2 = (G + DG < NG) ? G + DG : G;   // constant after unrolling
-                        if (NR > NRB && jh8 == 8 * NRB) load_rope(j, NRB);   // second half (head size 128)
-                        const f32x4 c = rc[(jh8 / 8) % NRB], sn = rsn[(jh8 / 8) % NRB];
-                        float o1[4], o2[4];
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const float y2 = acc[G2 >> 2][j][4 * (G2 & 3) + u];
-                            o1[u] = y[u] * c[u] - y2 * sn[u];
-                            o2[u] = y2 * c[u] + y[u] * sn[u];
-                        }
-                        pk[G] = pack4_bf16(o1);
-                        pk[G2] = pack4_bf16(o2);
-                        continue;
+                        for (int u = 0; u < 4; ++u) y[u] = gelu_erf_poly(y[u]);
                     }
                     pk[G] = pack4_bf16(y);
+                    continue;
                 }
-                // the next block's cos/sin, ahead of this block's stores
-                if (j + 1 < TJ) load_rope(j + 1, 0);
+                if (DG > 0 && kind != 3) {
+                    // Heads start on head_dim boundaries of the wave's columns, so the
+                    // group's place in its head is a compile-time constant. A first-half
+                    // group is rotated together with its partner DG groups on, which it
+                    // also packs.
+                    const int jh8 = (8 * G) % HD;
+                    if (jh8 >= HALF || G + DG >= NG) continue;
+                    const int G2 = (G + DG < NG) ? G + DG : G;   // constant after unrolling
+                    if (NR > NRB && jh8 == 8 * NRB) load_rope(j, NRB);   // second half (head size 128)
+                    const f32x4 c = rc[(jh8 / 8) % NRB], sn = rsn[(jh8 / 8) % NRB];
+                    float o1[4], o2[4];
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    // the lanes whose token is in this half of the token block write its rows
-                    if (((lane_e & 31) >> 4) == h) {
-#pragma unroll
-                        for (int G = 0; G < NG; ++G)
-                            *(__attribute__((address_space(3))) u32x2*)(size_t)(wr_lds + G * 16) = pk[G];
+                    for (int u = 0; u < 4; ++u) {
+                        const float y2 = acc[G2 >> 2][j][4 * (G2 & 3) + u];
+                        o1[u] = y[u] * c[u] - y2 * sn[u];
+                        o2[u] = y2 * c[u] + y[u] * sn[u];
                     }
-                    const int t0 = tw0 + 32 * j + 16 * h;   // the half block's first token
-                    const int rows = M - t0;                 // its rows that exist
-                    // in one slab: row r of this lane's chunk at row0_l + u + (r - r0) * stride_l
-                    const unsigned u = kind_l == 0 ? (unsigned)t0 * (unsigned)(2 * ff_dim)
-                                                   : (unsigned)(((int64_t)bi_first * slab_elems +
-                                                                 (int64_t)(t0 - bi_first * S) * hd) * 2);
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const int r = r0 + 4 * rr;   // token row of the half block
-                        const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(size_t)(
-                            rd_lds + rr * 4 * kRestageRow);
-                        if (r < rows && col_ok) {
-                            char* const dst = one_slab ? row0_l + (u + (unsigned)(4 * rr) * stride_l)
-                                                       : base_l + token_off(t0 + r);
-                            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
-                        }
-                    }
+                    pk[G] = pack4_bf16(o1);
+                    pk[G2] = pack4_bf16(o2);
+                    continue;
                 }
+                pk[G] = pack4_bf16(y);
             }
-        } else {
-            // Per-lane byte offsets (32-bit: the host keeps every output under 4 GiB) of this
-            // lane's token: its ff row, its q/k/v row of head 0, its cos/sin row.
-            unsigned ff_off[TJ], hv_off[TJ], rp_off[TJ];
-            bool tv[TJ];
+            // the next block's cos/sin, ahead of this block's stores
+            if (j + 1 < TJ) load_rope(j + 1, 0);
 #pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-                const int t = tw0 + 32 * j + (lane & 31);
-                tv[j] = t < M;
-                const int tc = tv[j] ? t : 0;
-                const int bi = (int)fastdiv_u31((uint32_t)tc, p.div_s), s = tc - bi * S;
-                ff_off[j] = (unsigned)tc * (unsigned)(2 * ff_dim) + (unsigned)(8 * hl);
-                hv_off[j] = (unsigned)(((int64_t)bi * slab_elems + (int64_t)s * hd + 4 * hl) * 2);
-                rp_off[j] = (unsigned)((s * (DG * 8) + 4 * hl) * 4);
-            }
-            char* const out_ff = static_cast<char*>(p.ff);
+            for (int h = 0; h < 2; ++h) {
+                // the lanes whose token is in this half of the token block write its rows
+                if (((lane_e & 31) >> 4) == h) {
 #pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-                // cos/sin of this lane's token at its 4 columns of each first-half group of a
-                // head; every head of the wave uses the same ones. Loaded before this token
-                // block's stores, so that the wait for them does not wait for those stores --
-                // all at once for head sizes up to 64, in two halves for 128 (registers).
-                f32x4 rc[NRB], rsn[NRB];
-                auto load_rope = [&](int r0) __attribute__((always_inline)) {
+                    for (int G = 0; G < NG; ++G)
+                        *(__attribute__((address_space(3))) u32x2*)(size_t)(wr_lds + G * 16) = pk[G];
+                }
+                const int t0 = tw0 + 32 * j + 16 * h;   // the half block's first token
+                const int rows = M - t0;                 // its rows that exist
+                // in one slab: row r of this lane's chunk at row0_l + u + (r - r0) * stride_l
+                const unsigned u = kind_l == 0 ? (unsigned)t0 * (unsigned)(2 * ff_dim)
+                                               : (unsigned)(((int64_t)bi_first * slab_elems +
+                                                             (int64_t)(t0 - bi_first * S) * hd) * 2);
 #pragma unroll
-                    for (int r = 0; r < NRB; ++r) {
-                        rc[r] = f32x4{};
-                        rsn[r] = f32x4{};
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int r = r0 + 4 * rr;   // token row of the half block
+                    const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(size_t)(
+                        rd_lds + rr * 4 * kRestageRow);
+                    if (r < rows && col_ok) {
+                        char* const dst = one_slab ? row0_l + (u + (unsigned)(4 * rr) * stride_l)
+                                                   : base_l + token_off(t0 + r);
+                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
                     }
-                    if (wave_rope) {
-#pragma unroll
-                        for (int r = 0; r < NRB; ++r) {
-                            const char* const c = reinterpret_cast<const char*>(rope_cos + 8 * (r0 + r)) + rp_off[j];
-                            const char* const sn = reinterpret_cast<const char*>(rope_sin + 8 * (r0 + r)) + rp_off[j];
-                            rc[r] = *reinterpret_cast<const f32x4*>(c);
-                            rsn[r] = *reinterpret_cast<const f32x4*>(sn);
-                        }
-                    }
-                };
-                load_rope(0);
-#pragma unroll
-                for (int G = 0; G < NG; ++G) {
-                    if (fw + 8 * G >= N) continue;   // ragged last column tile
-                    const unsigned d = desc[G];
-                    const unsigned kind = d >> 30, off = d & 0x3fffffffu;
-                    float y[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) y[u] = acc[G >> 2][j][4 * (G & 3) + u];
-                    if (kind == 0) {
-                        if (act == 1) {
-#pragma unroll
-                            for (int u = 0; u < 4; ++u) y[u] = gelu_erf_poly(y[u]);
-                        }
-                        if (tv[j]) store4_bf16(out_ff + (size_t)off * 2 + ff_off[j], y);
-                        continue;
-                    }
-                    char* const base = static_cast<char*>(kind == 1 ? p.q : kind == 2 ? p.k : p.v) + (size_t)off * 2;
-                    if (DG > 0 && kind != 3) {
-                        // Heads start on head_dim boundaries of the wave's columns, so the
-                        // group's place in its head is a compile-time constant. A first-half
-                        // group is rotated together with its partner DG groups on, whose own
-                        // slot does nothing.
-                        const int jh8 = (8 * G) % HD;
-                        if (jh8 >= HALF || G + DG >= NG) continue;
-                        const int G2 = (G + DG < NG) ? G + DG : G;   // constant after unrolling
-                        if (NR > NRB && jh8 == 8 * NRB) load_rope(NRB);   // second half (head size 128)
-                        const f32x4 c = rc[(jh8 / 8) % NRB], sn = rsn[(jh8 / 8) % NRB];
-                        float o1[4], o2[4];
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const float y2 = acc[G2 >> 2][j][4 * (G2 & 3) + u];
-                            o1[u] = y[u] * c[u] - y2 * sn[u];
-                            o2[u] = y2 * c[u] + y[u] * sn[u];
-                        }
-                        if (tv[j]) {
-                            store4_bf16(base + hv_off[j], o1);
-                            store4_bf16(base + hv_off[j] + HALF * 2, o2);
-                        }
-                        continue;
-                    }
-                    if (tv[j]) store4_bf16(base + hv_off[j], y);
                 }
             }
         }
