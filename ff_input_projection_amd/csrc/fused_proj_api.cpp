@@ -188,9 +188,8 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
         return FUSED_PROJ_EHIP;
     }
     // Kernel choice. The fast bf16 kernel needs a RoPE head size of 32, 64 or 128 (or no
-    // RoPE) and x and W spans under 4 GiB (it addresses them with 32-bit offsets); with its
-    // large tiles also whole groups of K steps. Every other shape goes to the general
-    // kernel.
+    // RoPE) and x and W spans under 4 GiB (it addresses them with 32-bit offsets). Every
+    // other shape goes to the general kernel.
     // FUSED_PROJ_KERNEL=general forces the general kernel (the tests use it to cover both);
     // FUSED_PROJ_KERNEL=fast takes the fast kernel on any shape it can address.
     const char* force = std::getenv("FUSED_PROJ_KERNEL");
@@ -199,13 +198,13 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     const int dg = fp::fast_rope_groups((int)desc->head_dim, desc->rope && r.qw > 0);
     const bool fits32 = r.x_span * 2 < (int64_t(1) << 32) && desc->channels * r.F * 2 < (int64_t(1) << 32);
     const fp::TilePlan fp_plan = fp::fast_plan(r.M, r.F, num_cus);
-    const bool large = fp_plan.bn == 256;
-    // Both tile shapes take any token and column count: tokens past M read token 0 and
-    // columns past F read row 0 of W and the zero block for the bias, and neither is
-    // stored (a channels-first x has S, hence M, a multiple of the 8-token load chunk).
-    // Large tiles take C in whole groups of K steps; small tiles (too few large tiles to
-    // fill the CUs) any C (partial K steps read zeros).
-    const bool exact = desc->channels > 0 && (!large || desc->channels % fp::fast_k_multiple() == 0);
+    // Both tile shapes take any token, column and channel count: tokens past M read token
+    // 0 and columns past F read row 0 of W and the zero block for the bias, and neither is
+    // stored (a channels-first x has S, hence M, a multiple of the 8-token load chunk);
+    // channels past C (a partial last K step, and on large tiles the steps that pad the K
+    // loop to a multiple of its four stages) read the zero block. Measured against the
+    // general kernel on such shapes (C 320, 72, 200 on large tiles): faster or equal.
+    const bool exact = desc->channels > 0;
     const bool addressable = fp::fast_addressable(r.M, r.S, desc->ff_dim, r.qw);
     // the fast kernel's epilogue applies exact-erf GELU or nothing: other activations take
     // the general kernel, even when the fast one is forced

@@ -801,8 +801,6 @@ bool fast_addressable(int64_t M, int64_t S, int64_t ff_dim, int64_t qw) {
     return M * ff_dim * 2 < lim32 && M * qw * 2 < lim32 && ff_dim < lim30 && S * qw < lim30;
 }
 
-int fast_k_multiple() { return kBK * LargeTile::STAGES; }
-
 // Entries for whole large column tiles, which also covers whole small ones.
 int64_t fast_col_desc_entries(int64_t F) { return (F + LargeTile::BF - 1) / LargeTile::BF * (LargeTile::BF / 8); }
 

@@ -106,8 +106,6 @@ bool fast_addressable(int64_t M, int64_t S, int64_t ff_dim, int64_t qw);
 void fast_col_desc(int64_t S, int64_t ff_dim, int64_t n_heads, int64_t head_dim, int64_t F, unsigned* out,
                    int64_t entries);
 int64_t fast_col_desc_entries(int64_t F);
-// Channel counts that are a multiple of this take no partial or padding K steps.
-int fast_k_multiple();
 hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, const TilePlan& plan,
                                   const KernelArgs& args, hipStream_t stream);
 

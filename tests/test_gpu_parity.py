@@ -173,6 +173,18 @@ RAGGED_M = [
 ]
 
 
+RAGGED_M += [
+    # large tiles with C not a multiple of 128 (partial and zero-padding K steps): the
+    # small-K shape at batch 8 (32768 tokens, C 320, 512 tiles), a token-major C 72 and a
+    # channels-first C 200 with RoPE and GELU
+    with_shape(WORKLOADS["smallk_qkv_bf16"], "cf_large_tiles_c320", x_shape=(8, 320, 64, 64), seed=131),
+    with_shape(WORKLOADS["bert_qkv_bf16"], "tl_large_tiles_c72", x_shape=(4, 4000, 72), ff_dim=1024, ff_act="gelu",
+               n_heads=4, head_dim=64, seed=132),
+    with_shape(WORKLOADS["walrus_bf16"], "cf_large_tiles_c200", x_shape=(12, 200, 32, 32, 1), ff_dim=512,
+               n_heads=8, head_dim=64, seed=133),
+]
+
+
 @pytest.mark.parametrize("wl", RAGGED_M, ids=[w.name for w in RAGGED_M])
 def test_fast_kernel_ragged_token_count(wl, monkeypatch):
     """The fast kernel on token counts that are not whole tiles: tokens past M read token
