@@ -9,11 +9,24 @@ the 256 MB Infinity Cache.
 
 Prints ONE JSON line. `value` is the contraction's algorithmic TFLOP/s
 (2*M*C*F per step) of the default workload, the Walrus-like bf16 block
-(x [24,768,32,32,1] channels-first, W [768,5376], FF 3072 + Q/K/V 12x64, RoPE).
-`roofline` prices the kernel against the dense bf16 MFMA peak (or HBM for a
-memory-bound workload); `cpu_baseline` is the float64 oracle timed on this
-host's cores over a bounded token sample, on which the GPU outputs are also
-checked for parity.
+(x [24,768,32,32,1] channels-first, W [768,5376], FF 3072 + Q/K/V 12x64, RoPE),
+timed over exactly `steps` back-to-back launches bracketed by two HIP events
+after a warm-up of at least `--min-warmup-s` seconds (whatever `--warmup` says:
+the clocks take about a second to settle). A second pass over the same number of
+launches, each between its own pair of events, gives the per-launch median, p10
+and p90.
+
+Also on the line:
+  roofline      the dominant kernel against the dense bf16 MFMA peak (or HBM for a
+                memory-bound workload), with the HBM bytes from the committed counter
+                summary when it was taken on the current kernel sources;
+  cpu_baseline  the float64 oracle timed on this host's cores;
+  configs       every workload of the workload table (tiny fp32, Walrus, BERT FF and
+                QKV, decoder, small-K), each timed the same way and checked against
+                the oracle on every output element;
+  cpu_1core     the oracle on one core for the tiny and small-K workloads;
+  sclk_mhz      the graphics clock sampled while the headline kernel runs;
+  context       the pages' own figures for the pathology this op removes.
 """
 from __future__ import annotations
 
@@ -32,6 +45,19 @@ METRIC = "fused projection TFLOP/s and GB/s on 1 MI355X, % of bf16 MFMA / HBM pe
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, MI355X published
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "ff_input_projection_amd", "csrc")
+# the workload table's configurations, in its order (3 is the BERT FF + QKV pair)
+CONFIG_WORKLOADS = ["tiny_f32", "walrus_bf16", "bert_ff_bf16", "bert_qkv_bf16", "decoder_qkv_rope_bf16",
+                    "smallk_qkv_bf16"]
+ONE_CORE_WORKLOADS = ["tiny_f32", "smallk_qkv_bf16"]
+# The Walrus PR's own measurements (L40S, before its fix), restated: the figures this
+# op exists to remove. Context only, not a target.
+CONTEXT = {
+    "source": "Walrus PR 'Make fused_ff_qkv contiguous' (profiles in its comments, NVIDIA L40S, torch 2.5.1)",
+    "forward_before_s": "about 6-7 s per bf16 forward of the batch-4 Walrus processor before the fix",
+    "bmm_share_of_device_time": 0.857,
+    "gemv_calls_per_projection": 24576,
+    "speedup_from_contiguous_input": "about 6x",
+}
 
 
 def kernel_hash() -> str:
@@ -58,16 +84,251 @@ def load_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
+def pct(vals, q):
+    s = sorted(vals)
+    if not s:
+        return None
+    i = min(len(s) - 1, max(0, int(round(q / 100.0 * (len(s) - 1)))))
+    return s[i]
+
+
+def time_launches(launch, steps: int, warmup: int, min_warmup_s: float, stream, per_launch: bool = True):
+    """Warm up for at least `warmup` launches and `min_warmup_s` seconds, then time
+    exactly `steps` launches between two HIP events on `stream` (the stream the kernel
+    runs on); then, when per_launch, the same number again with an event pair around
+    each launch. launch(i) enqueues launch i. Returns a dict of microsecond figures."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < min_warmup_s:
+        for _ in range(16):
+            launch(n)
+            n += 1
+        torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t0
+
+    # ---- timed region: exactly `steps` launches, bracketed by two events
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        launch(n + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    mean_us = ev0.elapsed_time(ev1) * 1e3 / max(steps, 1)
+    res = {"mean_us": mean_us, "wall_us_per_step": wall * 1e6 / max(steps, 1), "warmup_launches": n,
+           "warmup_s": round(warm_s, 3)}
+    if per_launch:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record(stream)
+        for i in range(steps):
+            launch(n + steps + i)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps)]
+        res.update({"median_us": pct(per, 50), "p10_us": pct(per, 10), "p90_us": pct(per, 90),
+                    "min_us": min(per), "max_us": max(per), "per_launch_n": steps})
+    return res
+
+
+def sample_sclk(launch, kernel_us: float, seconds: float = 0.4):
+    """Graphics clock (MHz) sampled through amdsmi while `launch` keeps the GPU busy
+    (about 20 ms of launches queued per 10 ms sample interval); None when the clock
+    cannot be read here."""
+    import torch
+
+    try:
+        import amdsmi
+    except Exception:
+        return None
+    try:
+        amdsmi.amdsmi_init()
+    except Exception:
+        return None
+    try:
+        props = torch.cuda.get_device_properties(torch.cuda.current_device())
+        want = (int(getattr(props, "pci_domain_id", 0)), int(getattr(props, "pci_bus_id", -1)))
+        handle = None
+        for h in amdsmi.amdsmi_get_processor_handles():
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)          # "dddd:bb:dd.f"
+            dom, bus = bdf.split(":")[0], bdf.split(":")[1]
+            if (int(dom, 16), int(bus, 16)) == want:
+                handle = h
+                break
+        if handle is None:
+            return None
+        samples = []
+        chunk = max(1, int(20e-3 / max(kernel_us * 1e-6, 1e-7)))
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(chunk):
+                launch(i)
+                i += 1
+            info = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
+            samples.append(int(info["clk"]))
+            time.sleep(0.01)
+        torch.cuda.synchronize()
+        if not samples:
+            return None
+        return {"median": pct(samples, 50), "min": min(samples), "max": max(samples), "n": len(samples),
+                "source": "amdsmi_get_clock_info(GFX) during back-to-back launches"}
+    except Exception as e:   # measurement aid only: never fail the bench on it
+        return {"error": str(e)[:200]}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+
+def make_plan(wl, x):
+    from ff_input_projection_amd import FusedProjection
+
+    return FusedProjection.for_tensor(x, wl.layout, w_layout=wl.w_layout, has_bias=wl.has_bias,
+                                      ff_dim=wl.ff_dim, ff_act=wl.ff_act, n_heads=wl.n_heads,
+                                      head_dim=wl.head_dim, rope=wl.rope, rope_base=wl.rope_base,
+                                      pos_offset=wl.pos_offset, n_kv_heads=wl.n_kv_heads,
+                                      qkv_order=wl.qkv_order, rope_dims=wl.rope_dims, ff_layout=wl.ff_layout)
+
+
+def gpu_outputs_to_host(wl, outs):
+    """The outputs of one launch, as CPU tensors in their storage type."""
+    return [None if t is None else t.cpu() for t in outs]
+
+
+def host_rows(wl, outs, tokens):
+    """Outputs (CPU tensors) as float64 token-major rows: ff [n, FF], q/k/v [n, heads, hd]."""
+    import torch
+
+    ff, q, k, v = outs
+    bi = torch.from_numpy(tokens // wl.S)
+    si = torch.from_numpy(tokens % wl.S)
+    if ff is None:
+        got = [None]
+    elif wl.ff_layout == "channels_first":
+        got = [ff.view(wl.nb, wl.ff_dim, wl.S)[bi, :, si].double().numpy()]
+    else:
+        got = [ff.view(wl.nb, wl.S, wl.ff_dim)[bi, si].double().numpy()]
+    for t, heads in ((q, wl.n_heads), (k, wl.kvh), (v, wl.kvh)):
+        got.append(None if t is None else t.view(wl.nb, heads, wl.S, wl.head_dim)[bi, :, si].double().numpy())
+    return got
+
+
+def run_oracle(wl, inp, tokens, threads):
+    import oracle
+
+    t = time.perf_counter()
+    r = oracle.fused_proj(inp.x64, wl.layout, inp.w64, wl.w_layout, inp.bias64, wl.ff_dim, wl.ff_act,
+                          wl.n_heads, wl.head_dim, wl.rope, wl.rope_base, wl.pos_offset, tokens=tokens,
+                          nthreads=threads, n_kv_heads=wl.n_kv_heads, qkv_order=wl.qkv_order,
+                          rope_dims=wl.rope_dims)
+    return r, time.perf_counter() - t
+
+
+def parity(wl, inp, host_outs, tokens, ref):
+    """Per-element comparison of the GPU outputs with the oracle's at `tokens`."""
+    from oracle import compare as cmp
+
+    got = host_rows(wl, host_outs, tokens)
+    rows, pos = cmp.token_rows(inp.x64, wl.layout, tokens)
+    w_cf = inp.w64 if wl.w_layout == "cf" else inp.w64.T
+    sc = cmp.scales(rows, pos, w_cf, inp.bias64, wl.ff_dim, wl.n_heads, wl.head_dim, wl.rope, wl.rope_base,
+                    wl.pos_offset, ff_act=wl.ff_act, ff_ref=ref.ff, n_kv_heads=wl.n_kv_heads,
+                    qkv_order=wl.qkv_order, rope_dims=wl.rope_dims)
+    vd = cmp.compare(got, [ref.ff, ref.q, ref.k, ref.v], [sc.ff, sc.q, sc.k, sc.v], wl.dtype)
+    return {"ok": vd.ok, "max_err_over_tol": round(vd.max_ratio, 5), "tight_ratio": round(vd.max_tight_ratio, 5),
+            "elements": vd.n, "all_elements": vd.n == wl.M * wl.F}
+
+
+def roofline_of(wl, us):
+    tflops = wl.flops / (us * 1e-6) / 1e12
+    gbs = wl.alg_bytes / (us * 1e-6) / 1e9
+    ridge = PEAK_TFLOPS[wl.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if wl.flops / wl.alg_bytes < ridge:
+        return tflops, gbs, {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic(wl.name)}
+    return tflops, gbs, {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS[wl.dtype],
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS[wl.dtype], 4),
+                         "traffic": load_traffic(wl.name)}
+
+
+def measure_workload(wl, dev, steps, warmup, min_warmup_s, ring_arg=0, graph=False, want_sclk=False):
+    """Time one workload on the GPU. Returns (timing dict, plan description, host copy of
+    one launch's outputs, inputs, sclk)."""
+    import torch
+
+    from ff_input_projection_amd.workloads import make_inputs
+
+    inp = make_inputs(wl)
+    ring = ring_arg or max(1, min(24, math.ceil(512e6 / wl.alg_bytes)))
+    xs = [inp.x.to(dev) for _ in range(ring)]
+    w = inp.w.to(dev)
+    b = inp.bias.to(dev) if inp.bias is not None else None
+    proj = make_plan(wl, xs[0])
+    outs = [proj.alloc_outputs(dev) for _ in range(ring)]
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    ptr = lambda t: None if t is None else t.data_ptr()
+    calls = [(ptr(xs[i]), ptr(w), ptr(b), *[ptr(t) for t in outs[i]]) for i in range(ring)]
+
+    def launch(i):
+        rc = proj.run_ptrs(*calls[i % ring], sh)
+        if rc != 0:
+            raise RuntimeError(f"fused_proj_run failed with status {rc}")
+
+    desc = proj.describe()
+    print(f"[bench] {wl.name}: {desc} ring={ring}", file=sys.stderr, flush=True)
+    if graph:
+        # the timed launches replayed from one HIP graph (launch overhead excluded): warm
+        # up eagerly, then time one replay of `steps` launches between two events
+        s2 = torch.cuda.Stream(dev)
+        s2.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s2):
+            with torch.cuda.graph(g, stream=s2):
+                cs = torch.cuda.current_stream(dev).cuda_stream
+                for i in range(steps):
+                    assert proj.run_ptrs(*calls[i % ring], cs) == 0
+        stream.wait_stream(s2)
+        torch.cuda.synchronize()
+        t = time_launches(launch, 0, warmup, min_warmup_s, stream, per_launch=False)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t["mean_us"] = ev0.elapsed_time(ev1) * 1e3 / steps
+    else:
+        t = time_launches(launch, steps, warmup, min_warmup_s, stream)
+    sclk = sample_sclk(launch, t["mean_us"]) if want_sclk else None
+    torch.cuda.synchronize()
+    host = gpu_outputs_to_host(wl, outs[0])
+    t["ring"] = ring
+    del xs, outs, w, b
+    proj.close()
+    torch.cuda.empty_cache()
+    return t, desc, host, inp, sclk
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--min-warmup-s", type=float, default=1.5,
+                    help="warm up for at least this long whatever --warmup is (clock ramp)")
     ap.add_argument("--workload", default="walrus_bf16")
     ap.add_argument("--ring", type=int, default=0, help="input/output sets cycled through (0: auto, >=512 MB)")
     ap.add_argument("--graph", action="store_true", help="replay the timed steps from one HIP graph")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle (timing and parity)")
+    ap.add_argument("--no-configs", action="store_true", help="time only --workload (no per-config array)")
+    ap.add_argument("--config-steps", type=int, default=200, help="timed launches per config (x5 for small-K)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times), to scale HBM counters")
     args = ap.parse_args()
@@ -92,8 +353,7 @@ def main() -> int:
     import numpy as np
     import torch
 
-    from ff_input_projection_amd import FusedProjection
-    from ff_input_projection_amd.workloads import SPLIT_ROPE_WORKLOADS, WORKLOADS, make_inputs
+    from ff_input_projection_amd.workloads import SPLIT_ROPE_WORKLOADS, WORKLOADS
 
     if args.workload in SPLIT_ROPE_WORKLOADS:
         return bench_split_rope(args, SPLIT_ROPE_WORKLOADS[args.workload])
@@ -102,79 +362,13 @@ def main() -> int:
     torch.cuda.set_device(dev)
     print(f"[bench] workload {wl.name}: {wl.description}", file=sys.stderr, flush=True)
 
-    inp = make_inputs(wl)
-    ring = args.ring or max(1, min(24, math.ceil(512e6 / wl.alg_bytes)))
-    xs = [inp.x.to(dev) for _ in range(ring)]
-    w = inp.w.to(dev)
-    b = inp.bias.to(dev) if inp.bias is not None else None
-    proj = FusedProjection.for_tensor(xs[0], wl.layout, w_layout=wl.w_layout, has_bias=wl.has_bias,
-                                      ff_dim=wl.ff_dim, ff_act=wl.ff_act, n_heads=wl.n_heads,
-                                      head_dim=wl.head_dim, rope=wl.rope, rope_base=wl.rope_base,
-                                      pos_offset=wl.pos_offset, n_kv_heads=wl.n_kv_heads,
-                                      qkv_order=wl.qkv_order, rope_dims=wl.rope_dims, ff_layout=wl.ff_layout)
-    outs = [proj.alloc_outputs(dev) for _ in range(ring)]
-    stream = torch.cuda.current_stream(dev)
-    sh = stream.cuda_stream
-    ptr = lambda t: None if t is None else t.data_ptr()
-    calls = [(ptr(xs[i]), ptr(w), ptr(b), *[ptr(t) for t in outs[i]]) for i in range(ring)]
-
-    def step(i):
-        rc = proj.run_ptrs(*calls[i % ring], sh)
-        if rc != 0:
-            raise RuntimeError(f"fused_proj_run failed with status {rc}")
-
-    print(f"[bench] plan: {proj.describe()} ring={ring}", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    graph = None
-    if args.graph:
-        s2 = torch.cuda.Stream(dev)
-        s2.wait_stream(stream)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(s2):
-            with torch.cuda.graph(graph, stream=s2):
-                cs = torch.cuda.current_stream(dev).cuda_stream
-                for i in range(args.steps):
-                    rc = proj.run_ptrs(*calls[i % ring], cs)
-                    assert rc == 0
-        stream.wait_stream(s2)
-        graph.replay()
-        torch.cuda.synchronize()
-
-    # ---- timed region: exactly `steps` launches on `stream`, bracketed by HIP events
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(args.steps):
-            step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms * 1e3:.2f} us/step (events), wall {wall * 1e6 / args.steps:.2f} us/step",
-          file=sys.stderr, flush=True)
-
-    tflops = wl.flops / (ms * 1e-3) / 1e12
-    gbs = wl.alg_bytes / (ms * 1e-3) / 1e9
-    mfma_frac = tflops / PEAK_TFLOPS[wl.dtype]
-    hbm_frac = gbs / PEAK_HBM_GBS
-    ridge = PEAK_TFLOPS[wl.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
-    hbm_bound = wl.flops / wl.alg_bytes < ridge
-    traffic = load_traffic(wl.name)
-    if hbm_bound:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(hbm_frac, 4), "traffic": traffic}
-    else:
-        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS[wl.dtype], "unit": "TFLOP/s",
-                "frac": round(mfma_frac, 4), "traffic": traffic}
-
+    t, desc, host, inp, sclk = measure_workload(wl, dev, args.steps, args.warmup, args.min_warmup_s, args.ring,
+                                                args.graph, want_sclk=not args.graph)
+    us = t["mean_us"]
+    ms = us * 1e-3
+    print(f"[bench] timed {args.steps} steps: {us:.2f} us/step (events), median {t.get('median_us', 0):.2f}, "
+          f"wall {t['wall_us_per_step']:.2f} us/step", file=sys.stderr, flush=True)
+    tflops, gbs, roof = roofline_of(wl, us)
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
@@ -183,73 +377,89 @@ def main() -> int:
         "config": {"workload": wl.name, "x_shape": list(wl.x_shape), "layout": wl.layout, "C": wl.C, "F": wl.F,
                    "ff_dim": wl.ff_dim, "n_heads": wl.n_heads, "head_dim": wl.head_dim, "rope": wl.rope,
                    "n_kv_heads": wl.kvh, "qkv_order": wl.qkv_order, "rope_dims": wl.rd if wl.rope else 0,
-                   "bias": wl.has_bias, "tokens": wl.M, "w_layout": wl.w_layout, "ring": ring,
-                   "graph": bool(graph is not None)},
-        "gb_per_s": round(gbs, 1), "hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
+                   "bias": wl.has_bias, "tokens": wl.M, "w_layout": wl.w_layout, "ring": t["ring"],
+                   "graph": bool(args.graph)},
+        "gb_per_s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "mfma_frac": round(tflops / PEAK_TFLOPS[wl.dtype], 4),
         "roofline": roof,
-        "kernel": proj.describe(), "kernel_hash": kernel_hash(),
+        "launch_us": {k: (round(v, 2) if isinstance(v, float) else v) for k, v in t.items()},
+        "sclk_mhz": sclk,
+        "kernel": desc, "kernel_hash": kernel_hash(),
+        "context": CONTEXT,
     }
 
-    # ---- CPU baseline (float64 oracle, bounded token sample) + parity on that sample
+    # ---- every configuration of the workload table, timed the same way (GPU first;
+    # the oracle checks follow on the CPU)
+    measured = {wl.name: (t, desc, host, inp)}
+    if not args.no_configs:
+        for name in CONFIG_WORKLOADS:
+            if name in measured:
+                continue
+            cw = WORKLOADS[name]
+            steps = args.config_steps * (5 if name == "smallk_qkv_bf16" else 1)
+            ct, cdesc, chost, cinp, _ = measure_workload(cw, dev, steps, 10, min(args.min_warmup_s, 1.0))
+            measured[name] = (ct, cdesc, chost, cinp)
+            print(f"[bench] {name}: mean {ct['mean_us']:.2f} us, median {ct['median_us']:.2f} "
+                  f"(p10 {ct['p10_us']:.2f}, p90 {ct['p90_us']:.2f})", file=sys.stderr, flush=True)
+
+    # ---- the oracle: CPU baseline on the headline workload, then every output element of
+    # every measured workload against it
+    cores = len(os.sched_getaffinity(0))
+    refs = {}
     if not args.no_cpu_baseline:
         import oracle
-        from oracle import compare as cmp
 
-        cores = len(os.sched_getaffinity(0))
-        rng = np.random.default_rng(12345)
-        per_tok_flops = 2.0 * wl.C * wl.F
-
-        def run_oracle(tokens):
-            t = time.perf_counter()
-            r = oracle.fused_proj(inp.x64, wl.layout, inp.w64, wl.w_layout, inp.bias64, wl.ff_dim, wl.ff_act,
-                                  wl.n_heads, wl.head_dim, wl.rope, wl.rope_base, wl.pos_offset, tokens=tokens,
-                                  nthreads=cores, n_kv_heads=wl.n_kv_heads, qkv_order=wl.qkv_order,
-                                  rope_dims=wl.rope_dims)
-            return r, time.perf_counter() - t
-
-        # calibrate on a probe large enough to amortise thread start-up, then size the sample
-        probe = np.sort(rng.choice(wl.M, size=min(wl.M, max(64 * cores, 1)), replace=False)).astype(np.int64)
-        _, tp = run_oracle(probe)
-        per_tok = tp / len(probe)
-        n = int(min(wl.M, max(len(probe), args.cpu_seconds / max(per_tok, 1e-9))))
-        if n >= wl.M:
-            # the whole workload fits the time budget: run all of it, repeated to fill it
-            tokens = np.arange(wl.M, dtype=np.int64)
-            reps = max(1, min(10, int(args.cpu_seconds / max(per_tok * wl.M, 1e-9))))
-        else:
-            tokens = np.sort(rng.choice(wl.M, size=n, replace=False)).astype(np.int64)
-            reps = 1
-        secs = 0.0
-        for _ in range(reps):
-            ref, s_ = run_oracle(tokens)
+        tokens = np.arange(wl.M, dtype=np.int64)
+        ref, secs = run_oracle(wl, inp, tokens, cores)
+        reps = 1
+        while secs < args.cpu_seconds and reps < 10:
+            _, s_ = run_oracle(wl, inp, tokens, cores)
             secs += s_
-        cpu_tflops = per_tok_flops * n * reps / secs / 1e12
-        what = (f"all {wl.M} tokens x {reps} run(s)" if n >= wl.M
-                else f"{n} of {wl.M} tokens (random, seed 12345)")
-        result["cpu_baseline"] = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": cores,
-                                  "kind": "oracle",
-                                  "sample": f"{what}, all F={wl.F} columns, float64, {secs:.1f} s"}
-        ff, q, k, v = outs[0]
-        bi = torch.from_numpy(tokens // wl.S).to(dev)
-        si = torch.from_numpy(tokens % wl.S).to(dev)
-        if ff is None:
-            got = [None]
-        elif wl.ff_layout == "channels_first":
-            got = [ff.view(wl.nb, wl.ff_dim, wl.S)[bi, :, si].double().cpu().numpy()]
-        else:
-            got = [ff.view(wl.nb, wl.S, wl.ff_dim)[bi, si].double().cpu().numpy()]
-        for t, heads in ((q, wl.n_heads), (k, wl.kvh), (v, wl.kvh)):
-            got.append(None if t is None else
-                       t.view(wl.nb, heads, wl.S, wl.head_dim)[bi, :, si].double().cpu().numpy())
-        rows, pos = cmp.token_rows(inp.x64, wl.layout, tokens)
-        w_cf = inp.w64 if wl.w_layout == "cf" else inp.w64.T
-        sc = cmp.scales(rows, pos, w_cf, inp.bias64, wl.ff_dim, wl.n_heads, wl.head_dim, wl.rope, wl.rope_base,
-                        wl.pos_offset, ff_act=wl.ff_act, ff_ref=ref.ff, n_kv_heads=wl.n_kv_heads,
-                        qkv_order=wl.qkv_order, rope_dims=wl.rope_dims)
-        vd = cmp.compare(got, [ref.ff, ref.q, ref.k, ref.v], [sc.ff, sc.q, sc.k, sc.v], wl.dtype)
-        result["parity"] = {"ok": vd.ok, "max_err_over_tol": round(vd.max_ratio, 5),
-                            "tight_ratio": round(vd.max_tight_ratio, 5), "elements": vd.n}
-        print(f"[bench] parity on the oracle sample: {vd}", file=sys.stderr, flush=True)
+            reps += 1
+        refs[wl.name] = ref
+        result["cpu_baseline"] = {"value": round(wl.flops * reps / secs / 1e12, 6), "unit": "TFLOP/s",
+                                  "cores": cores, "kind": "oracle",
+                                  "sample": f"all {wl.M} tokens x {reps} run(s), all F={wl.F} columns, float64, "
+                                            f"{secs:.1f} s on {cores} threads"}
+        result["parity"] = parity(wl, inp, host, tokens, ref)
+        print(f"[bench] parity {wl.name}: {result['parity']}", file=sys.stderr, flush=True)
+
+        one_core = []
+        for name in ONE_CORE_WORKLOADS:
+            cw = WORKLOADS[name]
+            cinp = measured[name][3] if name in measured else None
+            if cinp is None:
+                continue
+            _, s1 = run_oracle(cw, cinp, np.arange(cw.M, dtype=np.int64), 1)
+            one_core.append({"workload": name, "seconds": round(s1, 4), "gflop_per_s": round(cw.flops / s1 / 1e9, 3),
+                             "tokens": cw.M, "cores": 1})
+        result["cpu_1core"] = one_core
+
+    configs = []
+    for name in (CONFIG_WORKLOADS if not args.no_configs else [wl.name]):
+        if name not in measured:
+            continue
+        ct, cdesc, chost, cinp = measured[name]
+        cw = WORKLOADS[name]
+        c_tflops, c_gbs, c_roof = roofline_of(cw, ct["mean_us"])
+        entry = {"workload": name, "tokens": cw.M, "C": cw.C, "F": cw.F, "dtype": cw.dtype,
+                 "us_mean": round(ct["mean_us"], 2), "us_median": round(ct["median_us"], 2),
+                 "us_p10": round(ct["p10_us"], 2), "us_p90": round(ct["p90_us"], 2), "launches": ct["per_launch_n"],
+                 "tflop_per_s": round(c_tflops, 2), "gb_per_s": round(c_gbs, 1), "bound": c_roof["bound"],
+                 "frac": c_roof["frac"], "frac_at_median": round(roofline_of(cw, ct["median_us"])[2]["frac"], 4),
+                 "kernel": cdesc}
+        if not args.no_cpu_baseline:
+            if name == wl.name:
+                entry["parity"] = result["parity"]
+            else:
+                tokens = np.arange(cw.M, dtype=np.int64)
+                ref, s_ = run_oracle(cw, cinp, tokens, cores)
+                entry["parity"] = parity(cw, cinp, chost, tokens, ref)
+                entry["oracle_s"] = round(s_, 2)
+                del ref
+            print(f"[bench] parity {name}: {entry['parity']}", file=sys.stderr, flush=True)
+        configs.append(entry)
+    result["configs"] = configs
 
     print(json.dumps(result), flush=True)
     return 0
@@ -277,26 +487,17 @@ def bench_split_rope(args, wl) -> int:
     sh = stream.cuda_stream
     calls = [(xs[i].data_ptr(), *[t.data_ptr() for t in outs[i]]) for i in range(ring)]
 
-    def step(i):
+    def launch(i):
         rc = op.run_ptrs(*calls[i % ring], sh)
         if rc != 0:
             raise RuntimeError(f"split_rope_run failed with status {rc}")
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
-    gbs = wl.alg_bytes / (ms * 1e-3) / 1e9
+    t = time_launches(launch, args.steps, args.warmup, args.min_warmup_s, stream)
+    us = t["mean_us"]
+    gbs = wl.alg_bytes / (us * 1e-6) / 1e9
     result = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(us * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded qkv ~ N(0,1), rounded once to bf16",
         "config": {"workload": wl.name, "op": "split_rope", "batch": wl.batch, "tokens": wl.tokens,
                    "n_heads": wl.n_heads, "n_kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
@@ -305,6 +506,7 @@ def bench_split_rope(args, wl) -> int:
         "gb_per_s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        "launch_us": {k: (round(v, 2) if isinstance(v, float) else v) for k, v in t.items()},
         "kernel": "split_rope_kernel", "kernel_hash": kernel_hash(),
     }
     if not args.no_cpu_baseline:
@@ -323,7 +525,7 @@ def bench_split_rope(args, wl) -> int:
         result["cpu_baseline"] = {"value": round(wl.alg_bytes * reps / secs / 1e9, 4), "unit": "GB/s", "cores": 1,
                                   "kind": "oracle",
                                   "sample": f"the whole tensor x {reps} run(s), float64, one thread, {secs:.1f} s"}
-        q, k, v = (t.double().cpu().numpy() for t in outs[0])
+        q, k, v = (t_.double().cpu().numpy() for t_ in outs[0])
         err = max(float(np.max(np.abs(g - r) / (2.0 ** -8 * np.abs(r) + 1e-5 * np.abs(x64).max())))
                   for g, r in zip((q, k, v), ref))
         result["parity"] = {"ok": err <= 1.0, "max_err_over_tol": round(err, 5)}

@@ -320,24 +320,27 @@ int fused_proj_run(fused_proj_t h, const void* x, const void* w, const void* bia
     for (const void* p : ptrs)
         if (p && (reinterpret_cast<uintptr_t>(p) & 15u)) return FUSED_PROJ_EALIGN;
 
-    // Outputs may overlap neither each other nor an input.
+    // Outputs may overlap neither each other nor an input (at most 3 inputs and 4 outputs:
+    // fixed arrays, nothing allocated).
     const uintptr_t es = h->dt == fp::DType::BF16 ? 2 : 4;
-    std::vector<Range> ins, outs;
+    Range ins[3], outs[4];
+    int n_in = 0, n_out = 0;
     if (need_xw) {
-        ins.push_back({(uintptr_t)x, (uintptr_t)x + (uintptr_t)r.x_span * es});
-        ins.push_back({(uintptr_t)w, (uintptr_t)w + (uintptr_t)(h->d.channels * r.F) * es});
+        ins[n_in++] = {(uintptr_t)x, (uintptr_t)x + (uintptr_t)r.x_span * es};
+        ins[n_in++] = {(uintptr_t)w, (uintptr_t)w + (uintptr_t)(h->d.channels * r.F) * es};
     }
-    if (h->d.has_bias) ins.push_back({(uintptr_t)bias, (uintptr_t)bias + (uintptr_t)r.F * es});
-    if (h->d.ff_dim > 0) outs.push_back({(uintptr_t)ff, (uintptr_t)ff + (uintptr_t)(r.M * h->d.ff_dim) * es});
+    if (h->d.has_bias) ins[n_in++] = {(uintptr_t)bias, (uintptr_t)bias + (uintptr_t)r.F * es};
+    if (h->d.ff_dim > 0) outs[n_out++] = {(uintptr_t)ff, (uintptr_t)ff + (uintptr_t)(r.M * h->d.ff_dim) * es};
     if (r.qw > 0) {
-        outs.push_back({(uintptr_t)q, (uintptr_t)q + (uintptr_t)(r.M * r.qw) * es});
-        for (void* p : {k, v}) outs.push_back({(uintptr_t)p, (uintptr_t)p + (uintptr_t)(r.M * r.kvw) * es});
+        outs[n_out++] = {(uintptr_t)q, (uintptr_t)q + (uintptr_t)(r.M * r.qw) * es};
+        outs[n_out++] = {(uintptr_t)k, (uintptr_t)k + (uintptr_t)(r.M * r.kvw) * es};
+        outs[n_out++] = {(uintptr_t)v, (uintptr_t)v + (uintptr_t)(r.M * r.kvw) * es};
     }
-    for (size_t i = 0; i < outs.size(); ++i) {
-        for (size_t j = i + 1; j < outs.size(); ++j)
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = i + 1; j < n_out; ++j)
             if (overlap(outs[i], outs[j])) return FUSED_PROJ_EALIAS;
-        for (const Range& in : ins)
-            if (overlap(outs[i], in)) return FUSED_PROJ_EALIAS;
+        for (int j = 0; j < n_in; ++j)
+            if (overlap(outs[i], ins[j])) return FUSED_PROJ_EALIAS;
     }
 
     int dev = -1;

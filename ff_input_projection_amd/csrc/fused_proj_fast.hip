@@ -577,7 +577,7 @@ fused_proj_fast_kernel(KernelArgs p) {
         // element offset of the group's first column in the low bits (ff: column; q/k/v:
         // head * S * hd + place in head), all sixteen in one scalar load.
         const int fw = n0 + wf * WF;
-        const u32x16 desc = scalar_load16(p.col_desc + (fw >> 3));
+        const u32x16 desc = scalar_load16(p.col_desc + (unsigned)fw / 8u);
         // whether the wave's columns meet the q or k slice (then RoPE applies)
         const bool wave_rope = DG > 0 && fw < ff_dim + 2 * p.qw && fw + WF > ff_dim;
         constexpr int HD = DG > 0 ? 16 * DG : 16, HALF = HD / 2, NR = HALF / 8, NRB = NR > 4 ? 4 : NR;

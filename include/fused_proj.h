@@ -108,8 +108,10 @@ extern "C" {
 typedef struct fused_proj_desc {
     int32_t dtype;             /* FUSED_PROJ_BF16 | FUSED_PROJ_F32 */
     int32_t x_layout;          /* FUSED_PROJ_X_* */
-    int64_t batch;             /* b >= 1 (slabs; time steps may be folded in) */
-    int64_t channels;          /* C >= 1, the contraction length */
+    int64_t batch;             /* b >= 0 (slabs; time steps may be folded in); with b = 0
+                                  fused_proj_run does nothing */
+    int64_t channels;          /* C >= 0, the contraction length; with C = 0 every output
+                                  is computed from the bias alone (y = bias) */
     int32_t n_spatial;         /* 1..3 for channels-first, exactly 1 for tokens-last */
     int64_t spatial[3];        /* sizes of the spatial dims; S = their product */
     int64_t x_stride_batch;    /* element strides of x, all >= 0 */

@@ -18,12 +18,22 @@ def plan_for(wl: Workload, x: torch.Tensor) -> FusedProjection:
         n_kv_heads=wl.n_kv_heads, qkv_order=wl.qkv_order, rope_dims=wl.rope_dims, ff_layout=wl.ff_layout)
 
 
+def nan_outputs(proj: FusedProjection, device) -> tuple:
+    """Output buffers filled with NaN, so that a finite value proves the kernel wrote it
+    (torch.empty may hand back a block still holding an earlier run's correct results)."""
+    outs = proj.alloc_outputs(device)
+    for t in outs:
+        if t is not None:
+            t.fill_(float("nan"))
+    return outs
+
+
 def run_gpu(wl: Workload, inp, device="cuda:0", x_dev: torch.Tensor | None = None):
     x = x_dev if x_dev is not None else inp.x.to(device)
     w = inp.w.to(device)
     b = inp.bias.to(device) if inp.bias is not None else None
     proj = plan_for(wl, x)
-    outs = proj(x, w, b)
+    outs = proj(x, w, b, out=nan_outputs(proj, device))
     torch.cuda.synchronize()
     return proj, outs
 
@@ -71,14 +81,19 @@ def oracle_rows(wl: Workload, inp, tokens: np.ndarray):
     return [r.ff, r.q, r.k, r.v]
 
 
+def scales_for(wl: Workload, inp, tokens: np.ndarray, ref) -> cmp.Scales:
+    """Per-element bar scales at the given tokens (ref: the oracle's rows there)."""
+    rows, pos = cmp.token_rows(inp.x64, wl.layout, tokens)
+    w_cf = inp.w64 if wl.w_layout == "cf" else inp.w64.T
+    return cmp.scales(rows, pos, w_cf, inp.bias64, wl.ff_dim, wl.n_heads, wl.head_dim, wl.rope, wl.rope_base,
+                      wl.pos_offset, ff_act=wl.ff_act, ff_ref=ref[0], n_kv_heads=wl.n_kv_heads,
+                      qkv_order=wl.qkv_order, rope_dims=wl.rope_dims)
+
+
 def verdict(wl: Workload, inp, outs, tokens: np.ndarray) -> cmp.Verdict:
     got = gpu_rows(wl, outs, tokens)
     ref = oracle_rows(wl, inp, tokens)
-    rows, pos = cmp.token_rows(inp.x64, wl.layout, tokens)
-    w_cf = inp.w64 if wl.w_layout == "cf" else inp.w64.T
-    sc = cmp.scales(rows, pos, w_cf, inp.bias64, wl.ff_dim, wl.n_heads, wl.head_dim, wl.rope, wl.rope_base,
-                    wl.pos_offset, ff_act=wl.ff_act, ff_ref=ref[0], n_kv_heads=wl.n_kv_heads,
-                    qkv_order=wl.qkv_order, rope_dims=wl.rope_dims)
+    sc = scales_for(wl, inp, tokens, ref)
     return cmp.compare(got, ref, [sc.ff, sc.q, sc.k, sc.v], wl.dtype)
 
 
@@ -86,5 +101,5 @@ def all_tokens(wl: Workload) -> np.ndarray:
     return np.arange(wl.M, dtype=np.int64)
 
 
-__all__ = ["make_inputs", "plan_for", "run_gpu", "sample_tokens", "gpu_rows", "oracle_rows", "verdict",
+__all__ = ["make_inputs", "plan_for", "nan_outputs", "run_gpu", "sample_tokens", "gpu_rows", "oracle_rows", "scales_for", "verdict",
            "all_tokens"]

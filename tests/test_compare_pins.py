@@ -1,0 +1,168 @@
+"""Pins of the per-element parity bar (oracle/compare.py) to a brute-force bar (CPU only).
+
+The bar every GPU parity verdict rests on is |gpu - oracle| <= rel * scale with
+scale = ||x_t|| * ||w_eff|| + |b_eff|, where w_eff and b_eff are the effective
+column and bias of one output element: the plain W column and bias for ff and v
+elements, and for q/k elements after RoPE (RoPE is linear) the rotation-mixed column
+and bias at that token's position.
+
+Here w_eff and b_eff are not computed from any formula: they are read off the float64
+oracle itself, which is linear in x and in the bias when the ff activation is left
+out. Running it on unit activation rows e_c (channel c set to 1, no bias) returns
+w_eff[c] for every output element at every position; running it on a zero activation
+with the bias returns b_eff. scales() must match the bar built from those, for both
+column orders, fewer k/v heads, partial rotary, a position offset, squared ReLU (whose
+bar is the pre-activation one times 1 + 2 sqrt(output)) and no bias.
+compare() is pinned with planted errors just above and just below the bar, and with
+non-finite values.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import compare as cmp
+
+
+def _rows(res, which):
+    return {"ff": res.ff, "q": res.q, "k": res.k, "v": res.v}[which]
+
+
+def brute_force_scales(x, w, b, S, ff_dim, H, hd, rope, pos_offset, kvh, order, rope_dims, ff_act):
+    """Brute-force bar per output element for a token-major x [1, S, C] and W [C, F]."""
+    C = x.shape[2]
+    tokens = np.arange(S, dtype=np.int64)
+    kw = dict(n_kv_heads=kvh, qkv_order=order, rope_dims=rope_dims, tokens=tokens)
+    parts = ("ff", "q", "k", "v")
+    weff = {p: [] for p in parts}
+    for c in range(C):
+        e = np.zeros((1, S, C))
+        e[0, :, c] = 1.0
+        r = oracle.fused_proj(e, "tokens_last", w, "cf", None, ff_dim, "none", H, hd, rope, 10000.0, pos_offset,
+                              **kw)
+        for p in parts:
+            weff[p].append(_rows(r, p))
+    if b is not None:
+        beff = oracle.fused_proj(np.zeros((1, S, C)), "tokens_last", w, "cf", b, ff_dim, "none", H, hd, rope,
+                                 10000.0, pos_offset, **kw)
+    xn = np.linalg.norm(x[0], axis=1)                              # [S]
+    act_out = oracle.fused_proj(x, "tokens_last", w, "cf", b, ff_dim, ff_act, H, hd, rope, 10000.0, pos_offset,
+                                **kw)
+    out = {}
+    for p in parts:
+        if weff[p][0] is None:
+            out[p] = None
+            continue
+        stack = np.stack(weff[p], axis=0)                          # [C, S, ...]
+        wn = np.sqrt((stack ** 2).sum(axis=0))                     # [S, ...]
+        xs = xn.reshape((S,) + (1,) * (wn.ndim - 1))
+        bar = xs * wn + (np.abs(_rows(beff, p)) if b is not None else 0.0)
+        if p == "ff" and ff_act == "relu2":
+            bar = bar * (1.0 + 2.0 * np.sqrt(np.maximum(act_out.ff, 0.0)))
+        out[p] = bar
+    return out, act_out
+
+
+CASES = [
+    # (name, C, S, ff_dim, H, hd, kvh, order, rope, rope_dims, pos_offset, bias, ff_act)
+    ("contiguous_full_rope", 6, 5, 8, 2, 8, 0, "contiguous", True, 0, 0, True, "gelu"),
+    ("contiguous_full_rope_offset", 5, 4, 0, 3, 4, 0, "contiguous", True, 0, 11, True, "none"),
+    ("grouped_gqa_partial_rope", 7, 6, 0, 4, 8, 2, "grouped", True, 4, 3, True, "none"),
+    ("contiguous_gqa_partial_rope_relu2", 6, 5, 12, 6, 8, 3, "contiguous", True, 6, 0, True, "relu2"),
+    ("grouped_mqa_no_bias", 5, 4, 4, 2, 6, 1, "grouped", True, 0, 2, False, "gelu"),
+    ("no_rope_relu2", 4, 3, 10, 1, 4, 0, "contiguous", False, 0, 0, True, "relu2"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_scales_equal_brute_force_bar(case):
+    """scales() == the bar built from the oracle's own effective columns. Catches the
+    column norm over the wrong axis, the sign of the RoPE cross term, a bias mixed with
+    the wrong sign or partner, the partner taken over the head instead of the rotated
+    width, and a wrong squared-ReLU factor."""
+    name, C, S, ff_dim, H, hd, kvh, order, rope, rd, off, has_b, act = case
+    K = kvh if kvh > 0 else H
+    F = ff_dim + (H + 2 * K) * hd
+    r = np.random.default_rng(sum(map(ord, name)))
+    x = r.standard_normal((1, S, C))
+    w = r.standard_normal((C, F)) / math.sqrt(C)
+    b = r.standard_normal(F) * 0.5 if has_b else None
+    ref, act_out = brute_force_scales(x, w, b, S, ff_dim, H, hd, rope, off, kvh, order, rd, act)
+    rows, pos = cmp.token_rows(x, "tokens_last", np.arange(S, dtype=np.int64))
+    sc = cmp.scales(rows, pos, w, b, ff_dim, H, hd, rope, 10000.0, off, ff_act=act, ff_ref=act_out.ff,
+                    n_kv_heads=kvh, qkv_order=order, rope_dims=rd)
+    for p in ("ff", "q", "k", "v"):
+        got, exp = getattr(sc, p), ref[p]
+        if exp is None:
+            assert got is None, p
+            continue
+        assert got.shape == exp.shape, (p, got.shape, exp.shape)
+        assert np.allclose(got, exp, rtol=1e-12, atol=1e-14), (p, np.max(np.abs(got - exp)))
+
+
+def test_channels_first_token_rows():
+    """token_rows() gathers channel c of token (bi, s) from x[bi, c, s...] for a
+    channels-first x with two spatial dims, and returns the in-slab position s."""
+    r = np.random.default_rng(7)
+    x = r.standard_normal((3, 4, 2, 5))
+    tokens = np.array([0, 4, 9, 10, 23, 29], dtype=np.int64)
+    rows, pos = cmp.token_rows(x, "channels_first", tokens)
+    for i, t in enumerate(tokens):
+        bi, s = divmod(int(t), 10)
+        assert pos[i] == s
+        assert np.array_equal(rows[i], x[bi, :, s // 5, s % 5])
+
+
+def _planted(dtype, factor, where=(1, 2)):
+    r = np.random.default_rng(3)
+    ref = r.standard_normal((4, 5))
+    scl = np.abs(r.standard_normal((4, 5))) + 0.5
+    got = ref.copy()
+    got[where] += factor * cmp.REL[dtype] * scl[where]
+    return got, ref, scl
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_compare_fails_just_above_the_bar(dtype):
+    got, ref, scl = _planted(dtype, 1.01)
+    v = cmp.compare([got], [ref], [scl], dtype)
+    assert not v.ok and 1.009 < v.max_ratio < 1.011, v
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_compare_passes_just_below_the_bar(dtype):
+    got, ref, scl = _planted(dtype, 0.99)
+    v = cmp.compare([got], [ref], [scl], dtype)
+    assert v.ok and 0.989 < v.max_ratio < 0.991, v
+    # a negative error of the same size too
+    got, ref, scl = _planted(dtype, -0.99, where=(3, 0))
+    assert cmp.compare([got], [ref], [scl], dtype).ok
+
+
+def test_compare_checks_every_array_and_skips_none():
+    """An error in the last of several arrays still fails; None entries are skipped."""
+    good = np.ones((2, 3))
+    got, ref, scl = _planted("bf16", 1.5)
+    v = cmp.compare([good, None, got], [good, None, ref], [good, None, scl], "bf16")
+    assert not v.ok and v.n == good.size + got.size
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf"), -float("inf")])
+def test_compare_fails_on_non_finite(bad):
+    got, ref, scl = _planted("bf16", 0.0)
+    got[0, 0] = bad
+    v = cmp.compare([got], [ref], [scl], "bf16")
+    assert not v.ok and math.isinf(v.max_ratio)
+
+
+def test_tight_bar_is_reported_for_bf16():
+    """The diagnostic bar 2^-8 |ref| + 1e-4 scale: an error of 2^-8 |ref| alone sits at
+    about 1 of it, while the main bar (4e-3 scale) is far from reached."""
+    ref = np.array([[1.0, -2.0, 4.0]])
+    scl = np.array([[100.0, 100.0, 100.0]])
+    got = ref + 2.0 ** -8 * np.abs(ref)
+    v = cmp.compare([got], [ref], [scl], "bf16")
+    assert v.ok
+    expect = max(2.0 ** -8 * abs(r) / (2.0 ** -8 * abs(r) + 1e-4 * 100.0) for r in ref[0])
+    assert abs(v.max_tight_ratio - expect) < 1e-12

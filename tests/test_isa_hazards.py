@@ -21,14 +21,41 @@ from ff_input_projection_amd import build as fpbuild
 HIPCC = fpbuild.HIPCC
 
 
-def _asm(tmp_path):
-    src = os.path.join(fpbuild.CSRC, "fused_proj_fast.hip")
-    out = os.path.join(tmp_path, "fast.s")
+def _start_asm(src, out):
     flags = [f for f in fpbuild.FLAGS if f not in ("-fPIC", "-shared")]
-    cmd = [HIPCC, *flags, "--cuda-device-only", "-S", "-x", "hip", src, "-o", out]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-4000:]
+    cmd = [HIPCC, *flags, "-I", fpbuild.CSRC, "--cuda-device-only", "-S", "-x", "hip", src, "-o", out]
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+
+
+def _finish_asm(proc, out):
+    _, err = proc.communicate()
+    assert proc.returncode == 0, err[-4000:]
     return open(out).read()
+
+
+# The form of scalar_load16 that once sign-extended the descriptor address: readfirstlane
+# returns int, and widening the low half straight to 64 bits copies its bit 31 into the
+# high half.
+_GOOD_WIDEN = ("((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32)) << 32) |\n"
+               "                        (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((unsigned)a)")
+_BAD_WIDEN = ("((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32)) << 32) |\n"
+              "                        (uint64_t)__builtin_amdgcn_readfirstlane((unsigned)a)")
+
+
+@pytest.fixture(scope="module")
+def fast_asm(tmp_path_factory):
+    """The fast kernel's gfx950 assembly, and that of a copy with the sign-extending
+    widening planted in scalar_load16 (both compiled at once)."""
+    d = tmp_path_factory.mktemp("isa")
+    src = os.path.join(fpbuild.CSRC, "fused_proj_fast.hip")
+    text = open(src).read()
+    assert text.count(_GOOD_WIDEN) == 1, "scalar_load16's widening changed: update this test"
+    bad_src = os.path.join(d, "fast_bad.hip")
+    with open(bad_src, "w") as f:
+        f.write(text.replace(_GOOD_WIDEN, _BAD_WIDEN))
+    good_out, bad_out = os.path.join(d, "fast.s"), os.path.join(d, "fast_bad.s")
+    pg, pb = _start_asm(src, good_out), _start_asm(bad_src, bad_out)
+    return _finish_asm(pg, good_out), _finish_asm(pb, bad_out)
 
 
 def _kernels(asm):
@@ -58,8 +85,8 @@ def _valu_sgpr_defs(inst):
 
 
 @pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC), reason="hipcc not available")
-def test_inline_asm_memory_instructions_have_their_wait_states(tmp_path):
-    asm = _asm(str(tmp_path))
+def test_inline_asm_memory_instructions_have_their_wait_states(fast_asm):
+    asm = fast_asm[0]
     checked = 0
     problems = []
     for name, lines in _kernels(asm):
@@ -101,3 +128,63 @@ def test_inline_asm_memory_instructions_have_their_wait_states(tmp_path):
                 k -= 1
     assert checked > 100, "no inline-asm memory instructions found"
     assert not problems, "\n".join(problems[:20])
+
+
+_SGPR_PAIR = re.compile(r"s\[(\d+):(\d+)\]")
+
+
+def _dest_and_sources(inst):
+    """Scalar registers an instruction writes (its first operand) and reads (the rest)."""
+    if " " not in inst:
+        return set(), set()
+    ops = [o.strip() for o in inst.split(None, 1)[1].split(",")]
+    return _sgprs(ops[0]), _sgprs(",".join(ops[1:]))
+
+
+def _sign_extension(inst):
+    return (re.match(r"s_ashr_i(32|64)\s.*,\s*(31|63)$", inst) is not None or inst.startswith("s_bfe_i64")
+            or inst.startswith("s_sext_"))
+
+
+def _address_slice_problems(asm):
+    """For every inline-asm s_load_dwordx16, follow the scalar registers its address pair
+    is computed from back through its basic block; report any sign extension among them."""
+    problems, checked = [], 0
+    for name, lines in _kernels(asm):
+        insts = [l.strip() for l in lines]
+        for i, t in enumerate(insts):
+            if not t.startswith("s_load_dwordx16"):
+                continue
+            checked += 1
+            m = _SGPR_PAIR.findall(t.split(",", 1)[1])[0]
+            needed = set(range(int(m[0]), int(m[1]) + 1))
+            for p in reversed(insts[max(0, i - 200):i]):
+                if p.startswith(".LBB") or p.startswith("s_cbranch") or p.startswith("s_branch"):
+                    break
+                if not p or p.startswith((";", ".")) or not p.startswith("s_"):
+                    if p.startswith("v_readlane") or p.startswith("v_readfirstlane"):
+                        needed -= _dest_and_sources(p)[0]
+                    continue
+                dst, src = _dest_and_sources(p)
+                if not dst & needed:
+                    continue
+                if _sign_extension(p):
+                    problems.append(f"{name}: '{p}' feeds the address of '{t}'")
+                    break
+                needed = (needed - dst) | src
+    return checked, problems
+
+
+@pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC), reason="hipcc not available")
+def test_descriptor_address_is_not_sign_extended(fast_asm):
+    """The column-descriptor address reaching s_load_dwordx16 (scalar_load16) is formed
+    from the table's 64-bit address and an unsigned index: no sign extension anywhere in
+    the scalar registers it is computed from. A sign-extended low half once turned the
+    address into garbage whenever its bit 31 was set; a copy of the kernel with that
+    widening planted back must be caught by the same check."""
+    good, bad = fast_asm
+    checked, problems = _address_slice_problems(good)
+    assert checked >= 8, "no descriptor loads found"
+    assert not problems, "\n".join(problems[:10])
+    checked_bad, problems_bad = _address_slice_problems(bad)
+    assert checked_bad >= 8 and problems_bad, "the planted sign extension was not detected"

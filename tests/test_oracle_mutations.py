@@ -1,8 +1,8 @@
 """Each plausible mistake planted in a scratch copy of the oracle must fail a pin.
 
-The mistakes are planted in the oracle's C source on the CPU (never on a GPU);
-the pins in test_oracle_pins.py are then run against the mutated copy in a
-subprocess. A mutation that every pin lets through would mean the pins do not
+The mistakes are planted in the oracle's C source, or in its parity bar
+(compare.py), on the CPU (never on a GPU); the pins in test_oracle_pins.py (or
+test_compare_pins.py) are then run against the mutated copy in a subprocess. A mutation that every pin lets through would mean the pins do not
 cover that part of the definition.
 """
 import os
@@ -59,6 +59,48 @@ def test_planted_mistake_fails_a_pin(tmp_path, desc, orig, bad):
     (tmp_path / "oracle" / "fused_proj_oracle.c").write_text(src.replace(orig, bad, 1))
     env = dict(os.environ, OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle_pins.py", "-q", "-x",
+                        "-p", "no:cacheprovider"], cwd=tmp_path, env=env, capture_output=True, text=True,
+                       timeout=600)
+    assert r.returncode != 0, f"no pin caught the planted mistake: {desc}\n{r.stdout[-2000:]}"
+    assert "failed" in r.stdout, r.stdout[-2000:]
+
+
+# Mistakes planted in the parity bar (oracle/compare.py); each must fail a test of
+# test_compare_pins.py, which builds the bar by brute force from the oracle's own
+# effective columns.
+BAR_MUTATIONS = [
+    ("token norm taken as L1", "xn = np.linalg.norm(rows, axis=1)", "xn = np.abs(rows).sum(axis=1)"),
+    ("column norm over the wrong axis", "wn = np.linalg.norm(w_cf, axis=0)",
+     "wn = np.linalg.norm(w_cf, axis=0)[::-1]"),
+    ("RoPE cross term sign, first half", "c * c * n1 + s * s * n2 - 2 * c * s * d12",
+     "c * c * n1 + s * s * n2 + 2 * c * s * d12"),
+    ("RoPE cross term sign, second half", "c * c * n2 + s * s * n1 + 2 * c * s * d12",
+     "c * c * n2 + s * s * n1 - 2 * c * s * d12"),
+    ("RoPE bias mix sign", "b1 = np.abs(c * bh[None, :, :half] - s * bh[None, :, half:R])",
+     "b1 = np.abs(c * bh[None, :, :half] + s * bh[None, :, half:R])"),
+    ("RoPE angles over the head instead of the rotated width", "theta = rope_base ** (-2.0 * np.arange(half) / R)",
+     "theta = rope_base ** (-2.0 * np.arange(half) / head_dim)"),
+    ("RoPE position offset dropped", "phi = (positions.astype(np.float64) + pos_offset)",
+     "phi = (positions.astype(np.float64) + 0)"),
+    ("squared-ReLU factor halved", "ff = ff * (1.0 + 2.0 * np.sqrt(", "ff = ff * (1.0 + 1.0 * np.sqrt("),
+    ("bias left out of the bar", "plain = xn[:, None] * wn[None, :] + np.abs(b)[None, :]",
+     "plain = xn[:, None] * wn[None, :] + 0.0 * np.abs(b)[None, :]"),
+    ("bar loosened by 2", "ratio = err / (rel * s + 1e-300)", "ratio = err / (2 * rel * s + 1e-300)"),
+    ("non-finite outputs accepted", "finite &= bool(np.all(np.isfinite(g)))", "finite &= True"),
+]
+
+
+@pytest.mark.parametrize("desc,orig,bad", BAR_MUTATIONS, ids=[m[0] for m in BAR_MUTATIONS])
+def test_planted_bar_mistake_fails_a_pin(tmp_path, desc, orig, bad):
+    src = open(os.path.join(ROOT, "oracle", "compare.py")).read()
+    assert src.count(orig) == 1, f"mutation site not found: {desc}"
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
+                    ignore=shutil.ignore_patterns("*.tmp", "__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "tests"), tmp_path / "tests",
+                    ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutations.py"))
+    (tmp_path / "oracle" / "compare.py").write_text(src.replace(orig, bad, 1))
+    env = dict(os.environ, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_compare_pins.py", "-q", "-x",
                         "-p", "no:cacheprovider"], cwd=tmp_path, env=env, capture_output=True, text=True,
                        timeout=600)
     assert r.returncode != 0, f"no pin caught the planted mistake: {desc}\n{r.stdout[-2000:]}"

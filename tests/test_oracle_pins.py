@@ -273,20 +273,31 @@ def _head_major(a, nb, S, H, hd):
     return a.reshape(nb, S, H, hd).transpose(0, 2, 1, 3).reshape(nb * H, S, hd)
 
 
-def test_grouped_order_matches_pages_split_qkv():
-    """The grouped q/k/v order against the nvFuser RoPE issue's split_qkv written with
-    numpy: view the fused output as [B, T, groups, q_per_kv + 2, hs], move groups and
-    slots ahead of T, take q_per_kv q heads, one k and one v head per group (k and v not
-    expanded). Catches swapped k/v slots and q heads numbered across groups."""
+def test_grouped_order_column_formula():
+    """The grouped q/k/v order (split_qkv in the nvFuser RoPE issue, the lit-gpt layout):
+    each k/v group holds q_per_kv q heads, then one k head, then one v head, so element j of
+    slot `slot` of group g sits in fused column ff + (g*(q_per_kv + 2) + slot)*hd + j. The
+    expected buffers are filled element by element from that formula on the plain product
+    x @ W. Catches swapped k/v slots and q heads numbered across groups."""
     B, T, C, H, G, hd = 2, 5, 12, 4, 2, 4
+    qpk = H // G
     F = (H + 2 * G) * hd
     x, w, _ = rng_inputs(31, (B, T, C), C, F, bias=False)
     res = oracle.fused_proj(x, "tokens_last", w, "cf", None, 0, "none", H, hd, rope=False, n_kv_heads=G,
                             qkv_order="grouped")
-    y = (x.reshape(-1, C) @ w).reshape(B, T, G, H // G + 2, hd).transpose(0, 2, 3, 1, 4)  # [B, G, slot, T, hs]
-    q = y[:, :, : H // G].reshape(B * H, T, hd)
-    k = y[:, :, H // G].reshape(B * G, T, hd)
-    v = y[:, :, H // G + 1].reshape(B * G, T, hd)
+    y = x.reshape(B, T, C) @ w                                          # [B, T, F]
+    q = np.empty((B * H, T, hd))
+    k = np.empty((B * G, T, hd))
+    v = np.empty((B * G, T, hd))
+    for b in range(B):
+        for t in range(T):
+            for g in range(G):
+                for j in range(hd):
+                    col = lambda slot: (g * (qpk + 2) + slot) * hd + j
+                    for i in range(qpk):
+                        q[b * H + g * qpk + i, t, j] = y[b, t, col(i)]
+                    k[b * G + g, t, j] = y[b, t, col(qpk)]
+                    v[b * G + g, t, j] = y[b, t, col(qpk + 1)]
     for got, ref in ((res.q, q), (res.k, k), (res.v, v)):
         assert got.shape == ref.shape
         assert np.allclose(got, ref, rtol=0, atol=1e-12)
@@ -307,28 +318,25 @@ def test_contiguous_gqa_slices():
     assert np.allclose(res.v, _head_major(y[:, v0:], B, T, G, hd), rtol=0, atol=1e-12)
 
 
-def test_partial_rope_matches_pages_rope_one_entry():
-    """Partial rotary on q and k against the nvFuser RoPE issue's rope_one_entry written
-    with numpy: rotate-half over the first rope_n_elem elements with cos/sin tables of that
-    width (the page's cat(cos, cos) layout), the rest passed through. The angles follow
-    base^(-2i/rope_n_elem) (the convention shared with the GPU path). Catches rotating the
-    whole head, pairs taken across the head instead of across the rotated width, and the
-    sign of the rotated half."""
+def test_partial_rope_as_complex_rotation():
+    """Partial rotary on q and k (rope_one_entry with rope_n_elem in the nvFuser RoPE
+    issue): the pairs (i, i + R/2) of the first R elements of a head, read as the complex
+    number z = y_i + 1j*y_{i+R/2}, are multiplied by e^{1j*phi_i} with
+    phi_i = p * base^(-2i/R) (the angle convention shared with the GPU path); elements from
+    R on pass through. Catches rotating the whole head, pairs taken across the head
+    instead of across the rotated width, and the sign of the rotation."""
     B, T, C, H, G, hd, R = 1, 9, 8, 4, 2, 16, 8
     F = (H + 2 * G) * hd
     x, w, _ = rng_inputs(33, (B, T, C), C, F, bias=False)
     kw = dict(n_kv_heads=G, qkv_order="grouped")
     plain = oracle.fused_proj(x, "tokens_last", w, "cf", None, 0, "none", H, hd, rope=False, **kw)
     roped = oracle.fused_proj(x, "tokens_last", w, "cf", None, 0, "none", H, hd, rope=True, rope_dims=R, **kw)
-    theta = 10000.0 ** (-2.0 * np.arange(R // 2) / R)
-    ang = np.arange(T)[:, None] * theta[None, :]                      # [T, R/2]
-    cos = np.concatenate([np.cos(ang), np.cos(ang)], axis=1)          # [T, R]
-    sin = np.concatenate([np.sin(ang), np.sin(ang)], axis=1)
     for got, pre in ((roped.q, plain.q), (roped.k, plain.k)):
-        x_rope = pre[..., :R]
-        x1, x2 = x_rope[..., : R // 2], x_rope[..., R // 2:]
-        rotated = np.concatenate([-x2, x1], axis=-1)
-        ref = np.concatenate([x_rope * cos + rotated * sin, pre[..., R:]], axis=-1)
+        ref = pre.copy()
+        for i in range(R // 2):
+            phi = np.arange(T) * 10000.0 ** (-2.0 * i / R)                    # [T]
+            z = (pre[..., i] + 1j * pre[..., i + R // 2]) * np.exp(1j * phi)[None, :]
+            ref[..., i], ref[..., i + R // 2] = z.real, z.imag
         assert np.allclose(got, ref, rtol=0, atol=1e-12)
         assert np.array_equal(got[..., R:], pre[..., R:])
     assert np.array_equal(roped.v, plain.v)
