@@ -233,3 +233,42 @@ def make_qkv(batch: int, tokens: int, width: int, seed: int):
     a = np.random.default_rng(seed).standard_normal((batch, tokens, width))
     t = round_to(a, "bf16")
     return t, as_f64(t)
+
+
+@dataclass
+class Grads:
+    """Seeded upstream gradients of the four outputs, laid out like the outputs: d_ff
+    [b, S, FF] (or [b, FF, S] for a channels-first ff), dq [b*H, S, hd], dk and dv
+    [b*KVH, S, hd]; storage type on the CPU, with their exact float64 images."""
+    d_ff: torch.Tensor | None
+    dq: torch.Tensor | None
+    dk: torch.Tensor | None
+    dv: torch.Tensor | None
+    d_ff64: np.ndarray | None
+    dq64: np.ndarray | None
+    dk64: np.ndarray | None
+    dv64: np.ndarray | None
+
+
+def make_grads(wl: Workload, seed: int | None = None) -> Grads:
+    """Upstream gradients ~ N(0,1), drawn after nothing else (their own generator, seeded
+    with the workload's seed + 1000): d_ff, then dq, dk, dv; rounded once to the storage type."""
+    rng = np.random.default_rng((wl.seed if seed is None else seed) + 1000)
+    out, out64 = [], []
+    ff_shape = None
+    if wl.ff_dim > 0:
+        ff_shape = (wl.nb, wl.ff_dim, wl.S) if wl.ff_layout == "channels_first" else (wl.nb, wl.S, wl.ff_dim)
+    heads = wl.n_heads * wl.head_dim > 0
+    shapes = [ff_shape,
+              (wl.nb * wl.n_heads, wl.S, wl.head_dim) if heads else None,
+              (wl.nb * wl.kvh, wl.S, wl.head_dim) if heads else None,
+              (wl.nb * wl.kvh, wl.S, wl.head_dim) if heads else None]
+    for s in shapes:
+        if s is None:
+            out.append(None)
+            out64.append(None)
+            continue
+        t = round_to(rng.standard_normal(s), wl.dtype)
+        out.append(t)
+        out64.append(as_f64(t))
+    return Grads(*out, *out64)

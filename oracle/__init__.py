@@ -63,6 +63,16 @@ def _load():
         lib.oracle_split_rope.restype = ctypes.c_int
         lib.oracle_split_rope.argtypes = [d, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, i64,
                                           ctypes.c_double, i64, ctypes.c_int, d, d, d]
+        lib.oracle_fused_proj_backward.restype = ctypes.c_int
+        lib.oracle_fused_proj_backward.argtypes = [
+            d, i64, i64, i64, i64, i64, ctypes.c_int, p64, p64,
+            d, i64, ctypes.c_int, d,
+            i64, ctypes.c_int, i64, i64,
+            i64, ctypes.c_int, i64,
+            ctypes.c_int, ctypes.c_double, i64, ctypes.c_int,
+            d, d, d, d,
+            d, d, d, d, ctypes.c_int,
+        ]
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -178,6 +188,85 @@ def fused_proj(x: np.ndarray, layout: str, w: np.ndarray, w_layout: str, bias: n
 
     ff = None if ff_rows is None else ff_rows.reshape(nb, S, ff_dim)
     return OracleResult(ff, head_major(q_rows, n_heads), head_major(k_rows, kvh), head_major(v_rows, kvh))
+
+
+def _x_geometry(x: np.ndarray, layout: str):
+    """(nb, C, spatial sizes, spatial element strides, batch stride, channel stride)."""
+    item = x.itemsize
+    if layout == "channels_first":
+        nb, C = x.shape[0], x.shape[1]
+        sp = x.shape[2:]
+        sp_stride = [st // item for st in x.strides[2:]]
+        sb, sc = x.strides[0] // item, x.strides[1] // item
+    elif layout == "tokens_last":
+        nb, C = x.shape[0], x.shape[2]
+        sp = (x.shape[1],)
+        sp_stride = [x.strides[1] // item]
+        sb, sc = x.strides[0] // item, x.strides[2] // item
+    else:
+        raise ValueError(layout)
+    if not 1 <= len(sp) <= 3:
+        raise ValueError("1 to 3 spatial dims")
+    if any(st < 0 for st in x.strides):
+        raise ValueError("negative strides not supported by the oracle wrapper")
+    return nb, C, tuple(sp), sp_stride, sb, sc
+
+
+@dataclass
+class BackwardResult:
+    """Float64 gradients: dx in x's logical layout (dense), dw in w's layout, db [F] or
+    None, and dy [nb*S, F], the gradient of the fused pre-activation output."""
+    dx: np.ndarray
+    dw: np.ndarray
+    db: np.ndarray | None
+    dy: np.ndarray
+
+
+def fused_proj_backward(x: np.ndarray, layout: str, w: np.ndarray, w_layout: str, bias: np.ndarray | None,
+                        ff_dim: int, ff_act: str, n_heads: int, head_dim: int, rope: bool,
+                        d_ff: np.ndarray | None, dq: np.ndarray | None, dk: np.ndarray | None,
+                        dv: np.ndarray | None, rope_base: float = 10000.0, pos_offset: int = 0,
+                        n_kv_heads: int = 0, qkv_order: str = "contiguous", rope_dims: int = 0,
+                        ff_layout: str = "tokens_last", nthreads: int = 0) -> BackwardResult:
+    """Float64 backward pass of fused_proj (same arguments) for upstream gradients laid out
+    like the outputs: d_ff [b, S, FF] (or [b, FF, S] with ff_layout "channels_first"),
+    dq [b*H, S, hd], dk and dv [b*KVH, S, hd]. Every token is included."""
+    lib = _load()
+    x = np.asarray(x)
+    if x.dtype != np.float64:
+        raise TypeError("oracle takes float64 inputs")
+    nb, C, sp, sp_stride, sb, sc = _x_geometry(x, layout)
+    S = int(np.prod(sp))
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    F = w.shape[1] if w_layout == "cf" else w.shape[0]
+    w_fc = {"cf": 0, "fc": 1}[w_layout]
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float64)
+    grads = [None if g is None else np.ascontiguousarray(g, dtype=np.float64) for g in (d_ff, dq, dk, dv)]
+    M = nb * S
+    dy = np.empty((M, F))
+    dx_rows = np.empty((M, C))
+    dw = np.empty((C, F))
+    db = np.empty(F) if bias is not None else None
+    spz = (ctypes.c_int64 * len(sp))(*sp)
+    sps = (ctypes.c_int64 * len(sp))(*sp_stride)
+    rc = lib.oracle_fused_proj_backward(
+        x.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), nb, C, S, sb, sc, len(sp), spz, sps,
+        _dptr(w), F, w_fc, _dptr(bias),
+        ff_dim, ACTIVATIONS[ff_act], n_heads, head_dim, int(n_kv_heads),
+        {"contiguous": 0, "grouped": 1}[qkv_order], int(rope_dims),
+        int(bool(rope)), float(rope_base), int(pos_offset), {"tokens_last": 0, "channels_first": 1}[ff_layout],
+        *[_dptr(g) for g in grads], _dptr(dy), _dptr(dx_rows), _dptr(dw), _dptr(db), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    if layout == "channels_first":
+        # token-major rows [b, S, C] -> [b, C, spatial...]
+        dx = dx_rows.reshape(nb, S, C).transpose(0, 2, 1).reshape((nb, C) + sp)
+    else:
+        dx = dx_rows.reshape(nb, S, C)
+    if w_layout == "fc":
+        dw = np.ascontiguousarray(dw.T)
+    return BackwardResult(np.ascontiguousarray(dx), dw, db, dy)
 
 
 def split_rope(qkv: np.ndarray, n_heads: int, head_dim: int, n_kv_heads: int = 0, qkv_order: str = "contiguous",

@@ -154,3 +154,28 @@ def compare(got: list, ref: list, scl: list, dtype: str) -> Verdict:
     if not finite:
         mr = mt = math.inf
     return Verdict(finite and mr <= 1.0, mr, mt, ma, n)
+
+
+@dataclass
+class BackwardScales:
+    dx: np.ndarray   # [M, C] token-major rows
+    dw: np.ndarray   # [C, F]
+    db: np.ndarray   # [F]
+
+
+def backward_scales(x_rows: np.ndarray, w_cf: np.ndarray, dy: np.ndarray) -> BackwardScales:
+    """Per-element scales of the backward pass: each gradient element is one sum of
+    products, and its scale is the Cauchy-Schwarz bound of that sum,
+      dx[t, c] = sum_f dy[t, f] W[c, f]  ->  ||dy[t, :]|| ||W[c, :]||
+      dW[c, f] = sum_t x[t, c] dy[t, f]  ->  ||x[:, c]|| ||dy[:, f]||
+      db[f]    = sum_t dy[t, f]          ->  sqrt(M) ||dy[:, f]||,
+    with dy the oracle's float64 gradient of the fused output ([M, F]) and x_rows the
+    gathered activation [M, C]. Rounding dy once to the storage type moves each sum by at
+    most 2^-9 of its bound, and each rounded output by 2^-9 of itself."""
+    dyn_t = np.linalg.norm(dy, axis=1)          # [M]
+    dyn_f = np.linalg.norm(dy, axis=0)          # [F]
+    wn_c = np.linalg.norm(w_cf, axis=1)         # [C]
+    xn_c = np.linalg.norm(x_rows, axis=0)       # [C]
+    M = dy.shape[0]
+    return BackwardScales(dyn_t[:, None] * wn_c[None, :], xn_c[:, None] * dyn_f[None, :],
+                          math.sqrt(M) * dyn_f)

@@ -48,6 +48,9 @@
  *     phi = p * base^(-2i/head_dim) (a convention, not fixed by the pages),
  *     with p = s + pos_offset, the token's position inside its slab.
  *
+ *  7. The backward pass (oracle_fused_proj_backward below): the gradients of x,
+ *     W and the bias by the chain rule through steps 1-6, in reverse order.
+ *
  * No step is blocked, fused or reordered beyond that statement.
  */
 #include <math.h>
@@ -328,6 +331,189 @@ int oracle_split_rope(const double *qkv, int64_t nb, int64_t T, int64_t n_heads,
         }
     }
     free(head);
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- backward pass
+ *
+ * The gradient of the fused projection (the backward pass the xformers PR "Fused
+ * linear: small FW cleanup and much better perfs" discusses in its follow-up comments:
+ * the weight and input gradients of y = act(x W^T + b)), by the chain rule through the
+ * forward steps above, in their reverse order. Given the upstream gradients of the
+ * four outputs (d_ff, dq, dk, dv, laid out like the outputs):
+ *
+ *  a. dy[t, f], the gradient of the fused pre-activation output y[t, f]:
+ *     - ff column f: d_ff[t, f] * act'(y[t, f]), with y recomputed as in the forward;
+ *     - q/k head: RoPE is a rotation R_p of each pair (i, i + rd/2), so the gradient of
+ *       the head before the rotation is R_p^T (the rotation by -phi) applied to the
+ *       head's upstream gradient; elements from rd on, and v, pass through;
+ *  b. dx[t, c] = sum_f dy[t, f] * W[c, f]   (summed in increasing f);
+ *  c. dW[c, f] = sum_t x[t, c] * dy[t, f]   (summed in increasing t);
+ *  d. db[f]    = sum_t dy[t, f].
+ *
+ * act' in float64: exact GELU  Phi(y) + y phi(y);
+ *                  tanh GELU   0.5 (1 + tanh u) + 0.5 y (1 - tanh^2 u) u'(y),
+ *                              u = sqrt(2/pi) (y + 0.044715 y^3);
+ *                  squared ReLU 2 max(y, 0);  identity 1.
+ */
+static double activate_grad(int ff_act, double y)
+{
+    switch (ff_act) {
+    case 1: {
+        const double pdf = exp(-0.5 * y * y) / sqrt(2.0 * 3.14159265358979323846);
+        return 0.5 * (1.0 + erf(y / sqrt(2.0))) + y * pdf;
+    }
+    case 2: {
+        const double k = sqrt(2.0 / 3.14159265358979323846);
+        const double u = k * (y + 0.044715 * y * y * y);
+        const double th = tanh(u);
+        const double du = k * (1.0 + 3.0 * 0.044715 * y * y);
+        return 0.5 * (1.0 + th) + 0.5 * y * (1.0 - th * th) * du;
+    }
+    case 3: return y > 0.0 ? 2.0 * y : 0.0;
+    default: return 1.0;
+    }
+}
+
+/* The transpose of rope_rotate_half: rotate each pair (i, i + rd/2) of g by -phi. */
+static void rope_rotate_half_transposed(double *g, int64_t rd, double p, double base)
+{
+    int64_t half = rd / 2;
+    for (int64_t i = 0; i < half; ++i) {
+        double theta = pow(base, -2.0 * (double)i / (double)rd);
+        double phi = p * theta;
+        double cs = cos(phi), sn = sin(phi);
+        double g1 = g[i], g2 = g[i + half];
+        g[i] = g1 * cs + g2 * sn;
+        g[i + half] = g2 * cs - g1 * sn;
+    }
+}
+
+/*
+ * Backward pass for every token of the batch. Arguments as oracle_fused_proj, plus:
+ *   ff_cf    layout of d_ff: 0 [nb, S, ff_dim], 1 [nb, ff_dim, S]
+ *   d_ff     float64 upstream gradient of ff (NULL when ff_dim == 0)
+ *   dq       float64 [nb*n_heads, S, head_dim]; dk, dv [nb*n_kv, S, head_dim]
+ *            (NULL when there are no heads)
+ * Outputs (float64, all written):
+ *   dy       [nb*S, F] token-major: the gradient of the fused output y
+ *   dx_rows  [nb*S, C] token-major rows of the input gradient
+ *   dw       [C, F] (whatever the layout of w)
+ *   db       [F], or NULL
+ * Returns 0, or -1 on an invalid argument.
+ */
+int oracle_fused_proj_backward(const double *x, int64_t nb, int64_t C, int64_t S, int64_t sb, int64_t sc,
+                               int nsp, const int64_t *sp_size, const int64_t *sp_stride,
+                               const double *w, int64_t F, int w_fc, const double *bias,
+                               int64_t ff_dim, int ff_act, int64_t n_heads, int64_t head_dim,
+                               int64_t n_kv, int grouped, int64_t rope_dims,
+                               int rope, double rope_base, int64_t pos_offset, int ff_cf,
+                               const double *d_ff, const double *dq, const double *dk, const double *dv,
+                               double *dy, double *dx_rows, double *dw, double *db, int nthreads)
+{
+    if (!x || !w || !dy || !dx_rows || !dw || nb <= 0 || C <= 0 || S <= 0 || nsp < 1 || nsp > 3)
+        return ORACLE_EINVAL;
+    int64_t prod = 1;
+    for (int d = 0; d < nsp; ++d) {
+        if (sp_size[d] <= 0) return ORACLE_EINVAL;
+        prod *= sp_size[d];
+    }
+    if (prod != S) return ORACLE_EINVAL;
+    if (ff_dim < 0 || n_heads < 0 || head_dim < 0 || ff_act < 0 || ff_act > 3) return ORACLE_EINVAL;
+    if (n_kv == 0) n_kv = n_heads;
+    if (n_kv < 0 || (n_heads > 0 && (n_kv == 0 || n_heads % n_kv != 0)) || (grouped != 0 && grouped != 1))
+        return ORACLE_EINVAL;
+    const int64_t qw = n_heads * head_dim, kvw = n_kv * head_dim;
+    if (F != ff_dim + qw + 2 * kvw || F <= 0) return ORACLE_EINVAL;
+    const int64_t rd = rope_dims > 0 ? rope_dims : head_dim;
+    if (rope && (rd % 2 != 0 || rd > head_dim)) return ORACLE_EINVAL;
+    if (ff_dim > 0 && !d_ff) return ORACLE_EINVAL;
+    if (qw > 0 && (!dq || !dk || !dv)) return ORACLE_EINVAL;
+    const int64_t M = nb * S;
+
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+
+    int status = ORACLE_OK;
+    /* a + b: per token, the gradient of y, then the input gradient */
+#pragma omp parallel
+    {
+        double *y = (double *)malloc((size_t)F * sizeof(double));
+        double *xr = (double *)malloc((size_t)C * sizeof(double));
+        double *g = (double *)malloc((size_t)(head_dim > 0 ? head_dim : 1) * sizeof(double));
+        if (!y || !xr || !g) {
+#pragma omp atomic write
+            status = ORACLE_EINVAL;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < M; ++t) {
+            if (!y || !xr || !g) continue;
+            const int64_t bi = t / S, s = t % S;
+            double *dyt = dy + t * F;
+            /* the forward pre-activation output of the ff slice */
+            if (ff_dim > 0 && ff_act != 0) {
+                for (int64_t c = 0; c < C; ++c)
+                    xr[c] = x_at(x, bi, s, c, sb, sc, nsp, sp_size, sp_stride);
+                for (int64_t f = 0; f < ff_dim; ++f) {
+                    double acc = 0.0;
+                    for (int64_t c = 0; c < C; ++c) acc += xr[c] * w_at(w, c, f, C, F, w_fc);
+                    y[f] = acc + (bias ? bias[f] : 0.0);
+                }
+            }
+            for (int64_t f = 0; f < ff_dim; ++f) {
+                const double up = ff_cf ? d_ff[(bi * ff_dim + f) * S + s] : d_ff[t * ff_dim + f];
+                dyt[f] = up * activate_grad(ff_act, ff_act != 0 ? y[f] : 0.0);
+            }
+            /* q, k, v heads: each head's upstream gradient, rotated back for q and k,
+             * scattered to its fused columns */
+            for (int which = 0; qw > 0 && which < 3; ++which) {
+                const int64_t heads = which == 0 ? n_heads : n_kv;
+                const double *src = which == 0 ? dq : which == 1 ? dk : dv;
+                for (int64_t h = 0; h < heads; ++h) {
+                    for (int64_t j = 0; j < head_dim; ++j)
+                        g[j] = src[((bi * heads + h) * S + s) * head_dim + j];
+                    if (rope && which < 2)
+                        rope_rotate_half_transposed(g, rd, (double)(s + pos_offset), rope_base);
+                    for (int64_t r = 0; r < qw + 2 * kvw; ++r) {
+                        int wh;
+                        int64_t hh, j;
+                        qkv_column(r, n_heads, n_kv, head_dim, grouped, &wh, &hh, &j);
+                        if (wh == which && hh == h) dyt[ff_dim + r] = g[j];
+                    }
+                }
+            }
+            /* b. dx[t, c] = sum_f dy[t, f] W[c, f] */
+            for (int64_t c = 0; c < C; ++c) {
+                double acc = 0.0;
+                for (int64_t f = 0; f < F; ++f) acc += dyt[f] * w_at(w, c, f, C, F, w_fc);
+                dx_rows[t * C + c] = acc;
+            }
+        }
+        free(y);
+        free(xr);
+        free(g);
+    }
+    if (status != ORACLE_OK) return status;
+    /* c. dW[c, f] = sum_t x[t, c] dy[t, f] */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < C; ++c) {
+        double *row = dw + c * F;
+        for (int64_t f = 0; f < F; ++f) row[f] = 0.0;
+        for (int64_t t = 0; t < M; ++t) {
+            const double xv = x_at(x, t / S, t % S, c, sb, sc, nsp, sp_size, sp_stride);
+            const double *dyt = dy + t * F;
+            for (int64_t f = 0; f < F; ++f) row[f] += xv * dyt[f];
+        }
+    }
+    /* d. db[f] = sum_t dy[t, f] */
+    if (db) {
+        for (int64_t f = 0; f < F; ++f) db[f] = 0.0;
+        for (int64_t t = 0; t < M; ++t)
+            for (int64_t f = 0; f < F; ++f) db[f] += dy[t * F + f];
+    }
     return ORACLE_OK;
 }
 

@@ -166,3 +166,30 @@ def test_tight_bar_is_reported_for_bf16():
     assert v.ok
     expect = max(2.0 ** -8 * abs(r) / (2.0 ** -8 * abs(r) + 1e-4 * 100.0) for r in ref[0])
     assert abs(v.max_tight_ratio - expect) < 1e-12
+
+
+def test_backward_scales_are_the_cauchy_schwarz_bounds():
+    """backward_scales() against norms written out as loops: dx[t, c] scale
+    sqrt(sum_f dy[t,f]^2) * sqrt(sum_f W[c,f]^2), dW[c, f] scale
+    sqrt(sum_t x[t,c]^2) * sqrt(sum_t dy[t,f]^2), db[f] scale sqrt(M) * sqrt(sum_t dy[t,f]^2);
+    and every oracle gradient element lies within its scale (the bound holds)."""
+    r = np.random.default_rng(11)
+    M, C, F = 5, 3, 4
+    x = r.standard_normal((M, C))
+    w = r.standard_normal((C, F))
+    dy = r.standard_normal((M, F))
+    sc = cmp.backward_scales(x, w, dy)
+    for t in range(M):
+        for c in range(C):
+            e = math.sqrt(sum(dy[t, f] ** 2 for f in range(F))) * math.sqrt(sum(w[c, f] ** 2 for f in range(F)))
+            assert abs(sc.dx[t, c] - e) <= 1e-12 * e
+            assert abs(sum(dy[t, f] * w[c, f] for f in range(F))) <= sc.dx[t, c]
+    for c in range(C):
+        for f in range(F):
+            e = math.sqrt(sum(x[t, c] ** 2 for t in range(M))) * math.sqrt(sum(dy[t, f] ** 2 for t in range(M)))
+            assert abs(sc.dw[c, f] - e) <= 1e-12 * e
+            assert abs(sum(x[t, c] * dy[t, f] for t in range(M))) <= sc.dw[c, f]
+    for f in range(F):
+        e = math.sqrt(M) * math.sqrt(sum(dy[t, f] ** 2 for t in range(M)))
+        assert abs(sc.db[f] - e) <= 1e-12 * e
+        assert abs(sum(dy[t, f] for t in range(M))) <= sc.db[f]

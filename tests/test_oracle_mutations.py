@@ -105,3 +105,46 @@ def test_planted_bar_mistake_fails_a_pin(tmp_path, desc, orig, bad):
                        timeout=600)
     assert r.returncode != 0, f"no pin caught the planted mistake: {desc}\n{r.stdout[-2000:]}"
     assert "failed" in r.stdout, r.stdout[-2000:]
+
+
+# Mistakes planted in the backward oracle; each must fail a test of
+# test_oracle_backward_pins.py (finite differences of the forward oracle, numpy products).
+BACKWARD_MUTATIONS = [
+    ("inverse RoPE first-half sign", "g[i] = g1 * cs + g2 * sn;", "g[i] = g1 * cs - g2 * sn;"),
+    ("inverse RoPE second-half sign", "g[i + half] = g2 * cs - g1 * sn;", "g[i + half] = g2 * cs + g1 * sn;"),
+    ("inverse RoPE ignores pos_offset", "rope_rotate_half_transposed(g, rd, (double)(s + pos_offset), rope_base)",
+     "rope_rotate_half_transposed(g, rd, (double)(s), rope_base)"),
+    ("inverse RoPE over the whole head", "rope_rotate_half_transposed(g, rd,", "rope_rotate_half_transposed(g, head_dim,"),
+    ("GELU derivative without y phi(y)", "return 0.5 * (1.0 + erf(y / sqrt(2.0))) + y * pdf;",
+     "return 0.5 * (1.0 + erf(y / sqrt(2.0)));"),
+    ("tanh GELU derivative without the cube's factor 3", "du = k * (1.0 + 3.0 * 0.044715 * y * y);",
+     "du = k * (1.0 + 0.044715 * y * y);"),
+    ("squared ReLU derivative without the factor 2", "case 3: return y > 0.0 ? 2.0 * y : 0.0;",
+     "case 3: return y > 0.0 ? y : 0.0;"),
+    ("bias left out of the recomputed pre-activation", "y[f] = acc + (bias ? bias[f] : 0.0);", "y[f] = acc;"),
+    ("channels-first d_ff read token-major", "const double up = ff_cf ? d_ff[(bi * ff_dim + f) * S + s]",
+     "const double up = ff_cf ? d_ff[t * ff_dim + f]"),
+    ("dx drops the ff columns", "for (int64_t f = 0; f < F; ++f) acc += dyt[f] * w_at(w, c, f, C, F, w_fc);",
+     "for (int64_t f = ff_dim; f < F; ++f) acc += dyt[f] * w_at(w, c, f, C, F, w_fc);"),
+    ("dW tokens unflattened batch-minor", "const double xv = x_at(x, t / S, t % S, c,",
+     "const double xv = x_at(x, t % nb, t / nb, c,"),
+    ("db misses the last token", "for (int64_t t = 0; t < M; ++t)\n            for (int64_t f = 0; f < F; ++f) db[f]",
+     "for (int64_t t = 0; t < M - 1; ++t)\n            for (int64_t f = 0; f < F; ++f) db[f]"),
+]
+
+
+@pytest.mark.parametrize("desc,orig,bad", BACKWARD_MUTATIONS, ids=[m[0] for m in BACKWARD_MUTATIONS])
+def test_planted_backward_mistake_fails_a_pin(tmp_path, desc, orig, bad):
+    src = open(os.path.join(ROOT, "oracle", "fused_proj_oracle.c")).read()
+    assert src.count(orig) == 1, f"mutation site not found: {desc}"
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
+                    ignore=shutil.ignore_patterns("*.so", "*.tmp", "__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "tests"), tmp_path / "tests",
+                    ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutations.py"))
+    (tmp_path / "oracle" / "fused_proj_oracle.c").write_text(src.replace(orig, bad, 1))
+    env = dict(os.environ, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle_backward_pins.py", "-q", "-x",
+                        "-p", "no:cacheprovider"], cwd=tmp_path, env=env, capture_output=True, text=True,
+                       timeout=600)
+    assert r.returncode != 0, f"no pin caught the planted mistake: {desc}\n{r.stdout[-2000:]}"
+    assert "failed" in r.stdout, r.stdout[-2000:]
