@@ -25,7 +25,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfused_proj.so")
 
 EXPORTED_SYMBOLS = ["fused_proj_validate", "fused_proj_create", "fused_proj_run", "fused_proj_destroy",
-                    "fused_proj_strerror", "fused_proj_describe",
+                    "fused_proj_strerror", "fused_proj_describe", "fused_proj_backward_workspace_size",
+                    "fused_proj_backward",
                     "split_rope_validate", "split_rope_create", "split_rope_run", "split_rope_destroy"]
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, EALIAS, EHIP = 0, -1, -2, -3, -4, -5
@@ -95,6 +96,10 @@ def load_library():
     lib.fused_proj_strerror.restype = ctypes.c_char_p
     lib.fused_proj_describe.argtypes = [vp, ctypes.c_char_p, ctypes.c_size_t]
     lib.fused_proj_describe.restype = ctypes.c_int
+    lib.fused_proj_backward_workspace_size.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.fused_proj_backward_workspace_size.restype = ctypes.c_int
+    lib.fused_proj_backward.argtypes = [vp] * 12 + [ctypes.c_size_t, vp]
+    lib.fused_proj_backward.restype = ctypes.c_int
     lib.split_rope_validate.argtypes = [ctypes.POINTER(SplitRopeDesc)]
     lib.split_rope_validate.restype = ctypes.c_int
     lib.split_rope_create.argtypes = [ctypes.POINTER(SplitRopeDesc), ctypes.POINTER(vp)]
@@ -261,6 +266,66 @@ class FusedProjection:
         c = lambda a: None if a is None else ctypes.c_void_p(a)
         return self._lib.fused_proj_run(self._h, c(x), c(w), c(bias), c(ff), c(q), c(k), c(v),
                                         ctypes.c_void_p(stream_handle))
+
+    # ---------------------------------------------------------------- backward pass
+    def workspace_bytes(self) -> int:
+        """Device workspace the backward pass needs (fused_proj_backward_workspace_size)."""
+        n = ctypes.c_size_t()
+        rc = self._lib.fused_proj_backward_workspace_size(self._h, ctypes.byref(n))
+        if rc != OK:
+            raise FusedProjError(rc, "fused_proj_backward_workspace_size")
+        return int(n.value)
+
+    def grad_shapes(self):
+        """(dx, dw, db) shapes: dx dense in x's logical shape, dw in W's layout, db [F]."""
+        if self.layout == "channels_first":
+            dx = (self.B, self.C) + tuple(self.desc.spatial[i] for i in range(self.desc.n_spatial))
+        else:
+            dx = (self.B, self.S, self.C)
+        dw = (self.C, self.F) if self.w_layout == "cf" else (self.F, self.C)
+        return dx, dw, ((self.F,) if self.has_bias else None)
+
+    def alloc_grads(self, device):
+        mk = lambda s: None if s is None else torch.empty(s, dtype=self.dtype, device=device)
+        return tuple(mk(s) for s in self.grad_shapes())
+
+    def backward(self, x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None, d_ff=None, dq=None,
+                 dk=None, dv=None, out=None, workspace: torch.Tensor | None = None,
+                 stream: torch.cuda.Stream | None = None):
+        """Gradients (dx, dw, db) of x, W and the bias for upstream gradients shaped like the
+        outputs (None for empty slices). Outputs may be passed in; the workspace (uint8
+        device tensor of at least workspace_bytes()) is allocated when not given."""
+        ffs, qs, kvs = self.out_shapes()
+        for name, t, shp in (("d_ff", d_ff, ffs), ("dq", dq, qs), ("dk", dk, kvs), ("dv", dv, kvs)):
+            if shp is None:
+                continue
+            if t is None or tuple(t.shape) != shp or not t.is_contiguous() or t.dtype != self.dtype:
+                raise ValueError(f"{name} must be a contiguous {shp} {self.dtype} tensor")
+        dx, dw, db = out if out is not None else self.alloc_grads(x.device)
+        for t, shp in zip((dx, dw, db), self.grad_shapes()):
+            if shp is not None and (t is None or tuple(t.shape) != shp or not t.is_contiguous()
+                                    or t.dtype != self.dtype):
+                raise ValueError(f"gradient output must be a contiguous {shp} {self.dtype} tensor")
+        need = self.workspace_bytes()
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        st = stream if stream is not None else torch.cuda.current_stream(x.device)
+        p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+        wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        rc = self._lib.fused_proj_backward(self._h, p(x), p(w), p(bias) if self.has_bias else None, p(d_ff),
+                                           p(dq), p(dk), p(dv), p(dx), p(dw), p(db) if self.has_bias else None,
+                                           p(workspace), ctypes.c_size_t(wsb), ctypes.c_void_p(st.cuda_stream))
+        if rc != OK:
+            raise FusedProjError(rc, "fused_proj_backward")
+        return dx, dw, db
+
+    def backward_ptrs(self, x, w, bias, d_ff, dq, dk, dv, dx, dw, db, workspace, workspace_bytes: int,
+                      stream_handle: int) -> int:
+        """Raw backward call with integer device addresses (for timing loops); returns the status."""
+        c = lambda a: None if a is None else ctypes.c_void_p(a)
+        return self._lib.fused_proj_backward(self._h, c(x), c(w), c(bias), c(d_ff), c(dq), c(dk), c(dv), c(dx),
+                                             c(dw), c(db), c(workspace), ctypes.c_size_t(workspace_bytes),
+                                             ctypes.c_void_p(stream_handle))
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:

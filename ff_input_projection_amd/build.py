@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfused_proj.so")
 SOURCES = [os.path.join(CSRC, "fused_proj_api.cpp"), os.path.join(CSRC, "fused_proj_kernels.hip"),
-           os.path.join(CSRC, "fused_proj_fast.hip"), os.path.join(CSRC, "split_rope.hip")]
+           os.path.join(CSRC, "fused_proj_fast.hip"), os.path.join(CSRC, "split_rope.hip"),
+           os.path.join(CSRC, "fused_proj_bwd.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

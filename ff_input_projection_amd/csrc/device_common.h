@@ -75,6 +75,27 @@ __device__ __forceinline__ float relu_squared(float y) {
     return r * r;
 }
 
+// ---------------------------------------------------------------- activation derivatives
+// (the backward pass: dy = d_ff * act'(y))
+// Exact GELU: d/dy [y Phi(y)] = Phi(y) + y phi(y), phi(y) = e^(-y^2/2) / sqrt(2 pi).
+__device__ __forceinline__ float gelu_erf_grad(float y) {
+    const float cdf = 0.5f * (1.0f + erf_as7126(y * 0.70710678118654752440f));
+    const float pdf = 0.39894228040143267794f * __builtin_amdgcn_exp2f(-0.5f * y * y * 1.4426950408889634f);
+    return fmaf(y, pdf, cdf);
+}
+// tanh GELU: with s = 1 / (1 + e^(-2u)) = (1 + tanh u) / 2, u = sqrt(2/pi) (y + 0.044715 y^3),
+// d/dy [y s] = s + y * 2 s (1 - s) * u'(y), u'(y) = sqrt(2/pi) (1 + 3 * 0.044715 y^2). For
+// large |u| the exp2 goes to 0 or +inf and s to 1 or 0.
+__device__ __forceinline__ float gelu_tanh_grad(float y) {
+    const float k = 0.79788456080286536f;
+    const float u2 = (y + 0.044715f * (y * y * y)) * (2.0f * k * 1.4426950408889634f);
+    const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u2));
+    const float du = k * (1.0f + 3.0f * 0.044715f * (y * y));
+    return s + 2.0f * y * s * (1.0f - s) * du;
+}
+// Squared ReLU: 2 max(y, 0).
+__device__ __forceinline__ float relu_squared_grad(float y) { return y > 0.0f ? 2.0f * y : 0.0f; }
+
 // Tile of linear block id. Workgroups are dispatched round-robin over the 8 XCDs
 // (each with its own L2): every XCD is given a contiguous range of tiles, walked in
 // groups of group_m tile rows that sweep the tile columns together.

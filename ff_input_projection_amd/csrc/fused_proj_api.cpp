@@ -157,14 +157,99 @@ struct fused_proj_plan {
     void* d_zeros = nullptr;
     unsigned* d_desc = nullptr;  // fast kernel: column descriptors
     int device = 0;
+    int num_cus = 0;
     bool debug_sync = false;
+    // backward pass
+    fused_proj_plan* dx_plan = nullptr;  // dx = dy W^T as a forward projection (null when C == 0)
+    fp::BwdArgs bwd{};                   // everything but the per-call pointers
+    size_t ws_dbp = 0, ws_dwp = 0;       // workspace offsets (dy at 0)
+    size_t ws_bytes = 0;                 // workspace size
 };
+
+namespace {
+
+int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backward);
+
+constexpr size_t kWsAlign = 256;
+size_t ws_round(size_t n) { return (n + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Backward plan: the dx sub-projection, the dy and dW tilings and the workspace layout.
+int plan_backward(fused_proj_plan* h) {
+    const fused_proj_desc& d = h->d;
+    const Derived& r = h->r;
+    const int64_t es = h->dt == fp::DType::BF16 ? 2 : 4;
+    if (d.channels > 0) {
+        // dx[t, c] = sum_f dy[t, f] W[c, f]: dy [b, S, F] token-major is the activation, W is
+        // read the other way round, and the result is an ff slice of width C laid out like x
+        fused_proj_desc s{};
+        s.dtype = d.dtype;
+        s.x_layout = FUSED_PROJ_X_TOKENS_LAST;
+        s.batch = d.batch;
+        s.channels = r.F;
+        s.n_spatial = 1;
+        s.spatial[0] = r.S;
+        s.x_stride_batch = r.S * r.F;
+        s.x_stride_channel = 1;
+        s.x_stride_spatial[0] = r.F;
+        s.w_layout = d.w_layout == FUSED_PROJ_W_CF ? FUSED_PROJ_W_FC : FUSED_PROJ_W_CF;
+        s.has_bias = 0;
+        s.ff_dim = d.channels;
+        s.ff_act = FUSED_PROJ_ACT_NONE;
+        s.rope_base = 10000.0;
+        s.ff_layout = d.x_layout == FUSED_PROJ_X_CHANNELS_FIRST ? FUSED_PROJ_FF_CHANNELS_FIRST
+                                                                 : FUSED_PROJ_FF_TOKENS_LAST;
+        const int rc = create_plan(&s, &h->dx_plan, false);
+        if (rc) return rc;
+    }
+    fp::BwdArgs& b = h->bwd;
+    b.f = h->base;
+    const int bk = fp::tile_bk(h->dt);
+    b.f.tiles_m = (int32_t)((r.M + 127) / 128);
+    b.f.tiles_n = (int32_t)((r.F + 127) / 128);
+    b.f.group_m = 8;
+    b.ff_cf = d.ff_layout == FUSED_PROJ_FF_CHANNELS_FIRST ? 1 : 0;
+    b.w_fc = d.w_layout == FUSED_PROJ_W_FC ? 1 : 0;
+    b.dw_tiles_m = (int32_t)((d.channels + 127) / 128);
+    b.dw_tiles_n = b.f.tiles_n;
+    b.db_tiles = b.f.tiles_m;
+    // dW contracts over the tokens: split them into ranges when the dW tiles alone
+    // cannot fill the CUs (two workgroups each), at most 16 ranges
+    const int64_t dw_tiles = (int64_t)b.dw_tiles_m * b.dw_tiles_n;
+    const int64_t ksteps = (r.M + bk - 1) / bk;
+    int64_t splits = 1;
+    if (dw_tiles > 0 && ksteps > 0) {
+        splits = (2 * (int64_t)h->num_cus + dw_tiles - 1) / dw_tiles;
+        if (splits > 16) splits = 16;
+        if (splits > ksteps) splits = ksteps;
+        if (splits < 1) splits = 1;
+    }
+    const int64_t chunk = ksteps > 0 ? (ksteps + splits - 1) / splits * bk : bk;
+    splits = r.M > 0 ? (r.M + chunk - 1) / chunk : 1;
+    b.splits = (int32_t)splits;
+    b.chunk = (int32_t)chunk;
+    // workspace: dy, then the column sums of dy per token tile (bias), then the dW partials
+    size_t off = ws_round((size_t)(r.M * r.F * es));
+    h->ws_dbp = off;
+    if (d.has_bias) off += ws_round((size_t)b.db_tiles * (size_t)r.F * 4);
+    h->ws_dwp = off;
+    if (splits > 1) off += ws_round((size_t)splits * (size_t)d.channels * (size_t)r.F * 4);
+    h->ws_bytes = r.M > 0 ? off : 0;
+    return FUSED_PROJ_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
 int fused_proj_validate(const fused_proj_desc* desc) { return check_desc(desc, nullptr); }
 
-int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
+int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) { return create_plan(desc, out, true); }
+
+}  // extern "C"
+
+namespace {
+
+int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backward) {
     if (!out) return FUSED_PROJ_EINVAL;
     *out = nullptr;
     Derived r;
@@ -182,6 +267,7 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
     hipError_t e = hipGetDevice(&h->device);
     int num_cus = 0;
     if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, h->device);
+    h->num_cus = num_cus > 0 ? num_cus : 256;
     if (e != hipSuccess) {
         g_last_hip = e;
         delete h;
@@ -300,9 +386,20 @@ int fused_proj_create(const fused_proj_desc* desc, fused_proj_t* out) {
         }
     }
     a.col_desc = h->d_desc;
+    if (with_backward) {
+        rc = plan_backward(h);
+        if (rc) {
+            fused_proj_destroy(h);
+            return rc;
+        }
+    }
     *out = h;
     return FUSED_PROJ_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int fused_proj_run(fused_proj_t h, const void* x, const void* w, const void* bias, void* ff, void* q, void* k,
                    void* v, void* stream) {
@@ -375,6 +472,7 @@ int fused_proj_run(fused_proj_t h, const void* x, const void* w, const void* bia
 
 int fused_proj_destroy(fused_proj_t h) {
     if (!h) return FUSED_PROJ_OK;
+    const int rc_sub = fused_proj_destroy(h->dx_plan);
     hipError_t e1 = h->d_cos ? hipFree(h->d_cos) : hipSuccess;
     hipError_t e2 = h->d_sin ? hipFree(h->d_sin) : hipSuccess;
     hipError_t e3 = h->d_zeros ? hipFree(h->d_zeros) : hipSuccess;
@@ -384,6 +482,101 @@ int fused_proj_destroy(fused_proj_t h) {
     delete h;
     if (e1 != hipSuccess || e2 != hipSuccess) {
         g_last_hip = e1 != hipSuccess ? e1 : e2;
+        return FUSED_PROJ_EHIP;
+    }
+    return rc_sub;
+}
+
+int fused_proj_backward_workspace_size(fused_proj_t h, size_t* bytes) {
+    if (!h || !bytes) return FUSED_PROJ_EINVAL;
+    *bytes = h->ws_bytes;
+    return FUSED_PROJ_OK;
+}
+
+int fused_proj_backward(fused_proj_t h, const void* x, const void* w, const void* bias, const void* d_ff,
+                        const void* dq, const void* dk, const void* dv, void* dx, void* dw, void* db,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (!h) return FUSED_PROJ_EINVAL;
+    const Derived& r = h->r;
+    const fused_proj_desc& d = h->d;
+    const bool has_c = d.channels > 0, has_m = r.M > 0;
+    const bool has_ff = d.ff_dim > 0, has_h = r.qw > 0;
+    // required pointers
+    if (has_c && ((has_m && (!x || !dx)) || !w || !dw)) return FUSED_PROJ_EINVAL;
+    if (d.has_bias && (!bias || !db)) return FUSED_PROJ_EINVAL;
+    if (has_m && ((has_ff && !d_ff) || (has_h && (!dq || !dk || !dv)))) return FUSED_PROJ_EINVAL;
+    if (h->ws_bytes > 0 && (!workspace || workspace_bytes < h->ws_bytes)) return FUSED_PROJ_EINVAL;
+    const uintptr_t es = h->dt == fp::DType::BF16 ? 2 : 4;
+    const uintptr_t M = (uintptr_t)r.M, C = (uintptr_t)d.channels, F = (uintptr_t)r.F;
+    // inputs: x, w, bias, d_ff, dq, dk, dv; outputs: dx, dw, db, workspace (fixed arrays)
+    Range ins[7], outs[4];
+    int n_in = 0, n_out = 0;
+    auto add = [](Range* arr, int& n, const void* p, uintptr_t bytes) {
+        if (p && bytes > 0) arr[n++] = Range{(uintptr_t)p, (uintptr_t)p + bytes};
+    };
+    add(ins, n_in, has_c && has_m ? x : nullptr, (uintptr_t)r.x_span * es);
+    add(ins, n_in, has_c ? w : nullptr, C * F * es);
+    add(ins, n_in, d.has_bias ? bias : nullptr, F * es);
+    add(ins, n_in, has_m && has_ff ? d_ff : nullptr, M * (uintptr_t)d.ff_dim * es);
+    add(ins, n_in, has_m && has_h ? dq : nullptr, M * (uintptr_t)r.qw * es);
+    add(ins, n_in, has_m && has_h ? dk : nullptr, M * (uintptr_t)r.kvw * es);
+    add(ins, n_in, has_m && has_h ? dv : nullptr, M * (uintptr_t)r.kvw * es);
+    add(outs, n_out, has_c && has_m ? dx : nullptr, M * C * es);
+    add(outs, n_out, has_c ? dw : nullptr, C * F * es);
+    add(outs, n_out, d.has_bias ? db : nullptr, F * es);
+    add(outs, n_out, h->ws_bytes > 0 ? workspace : nullptr, h->ws_bytes);
+    for (int i = 0; i < n_in; ++i)
+        if (ins[i].lo & 15u) return FUSED_PROJ_EALIGN;
+    for (int i = 0; i < n_out; ++i)
+        if (outs[i].lo & 15u) return FUSED_PROJ_EALIGN;
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlap(outs[i], outs[j])) return FUSED_PROJ_EALIAS;
+        for (int j = 0; j < n_in; ++j)
+            if (overlap(outs[i], ins[j])) return FUSED_PROJ_EALIAS;
+    }
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip = e;
+        return FUSED_PROJ_EHIP;
+    }
+    if (dev != h->device) return FUSED_PROJ_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if (!has_m) {
+        // no tokens: the weight and bias gradients are zero
+        if (has_c) e = fp::launch_zero_fill(dw, C * F * es, s);
+        if (e == hipSuccess && d.has_bias) e = fp::launch_zero_fill(db, F * es, s);
+    } else {
+        fp::BwdArgs b = h->bwd;
+        b.f.x = x;
+        b.f.w = w;
+        b.f.bias = d.has_bias ? bias : nullptr;
+        b.d_ff = d_ff;
+        b.dq = dq;
+        b.dk = dk;
+        b.dv = dv;
+        char* ws = static_cast<char*>(workspace);
+        b.dy = ws;
+        b.dbp = d.has_bias ? reinterpret_cast<float*>(ws + h->ws_dbp) : nullptr;
+        b.dwp = b.splits > 1 ? reinterpret_cast<float*>(ws + h->ws_dwp) : nullptr;
+        b.dw = dw;
+        b.db = d.has_bias ? db : nullptr;
+        e = fp::launch_bwd_dy(h->dt, h->x_tl, h->w_fc, b, s);
+        if (e == hipSuccess && has_c) {
+            const int rc = fused_proj_run(h->dx_plan, b.dy, w, nullptr, dx, nullptr, nullptr, nullptr, stream);
+            if (rc) return rc;
+            e = fp::launch_bwd_dw(h->dt, h->x_tl, b, s);
+        }
+        if (e == hipSuccess) e = fp::launch_bwd_reduce(h->dt, b, s);
+    }
+    if (e == hipSuccess && h->debug_sync) {
+        e = hipStreamSynchronize(s);
+        if (e == hipSuccess) e = hipGetLastError();
+    }
+    if (e != hipSuccess) {
+        g_last_hip = e;
         return FUSED_PROJ_EHIP;
     }
     return FUSED_PROJ_OK;

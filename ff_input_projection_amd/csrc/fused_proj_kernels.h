@@ -109,4 +109,39 @@ int64_t fast_col_desc_entries(int64_t F);
 hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, const TilePlan& plan,
                                   const KernelArgs& args, hipStream_t stream);
 
+// ---------------------------------------------------------------- backward pass
+// Arguments of the backward kernels. f is the forward problem (operands, layouts,
+// heads, RoPE table), with its tile counts set for the 128 x 128 tiles of the dy
+// kernel over [M, F].
+struct BwdArgs {
+    KernelArgs f;
+    const void* d_ff;    // upstream gradients: [b, S, ff] (or [b, ff, S] with ff_cf)
+    const void* dq;      // [b*H, S, hd]
+    const void* dk;      // [b*KVH, S, hd]
+    const void* dv;
+    void* dy;            // workspace: gradient of the fused output, [M, F] token-major, storage type
+    float* dbp;          // workspace: [dy tiles_m, F] fp32 column sums of dy per token tile, or null
+    void* dw;            // dW in W's layout (written by the dW kernel when splits == 1)
+    float* dwp;          // workspace: [splits, C, F] fp32 partial sums of dW (splits > 1)
+    void* db;            // [F] or null
+    int32_t ff_cf;       // d_ff channels-first
+    int32_t w_fc;        // W (and dW) stored [F, C]
+    int32_t splits;      // token ranges of the dW contraction
+    int32_t chunk;       // tokens per range (a multiple of the K step)
+    int32_t dw_tiles_m;  // 128 x 128 tiles over [C, F]
+    int32_t dw_tiles_n;
+    int32_t db_tiles;    // rows of dbp
+};
+
+// K step of the 128 x 128 tile kernels for a storage type.
+int tile_bk(DType dt);
+// The dy kernel: grid b.f.tiles_m x b.f.tiles_n (128 x 128 tiles over [M, F]).
+hipError_t launch_bwd_dy(DType dt, bool x_tokens_last, bool w_fc, const BwdArgs& b, hipStream_t stream);
+// The dW kernel: grid (dw_tiles_m x dw_tiles_n, splits).
+hipError_t launch_bwd_dw(DType dt, bool x_tokens_last, const BwdArgs& b, hipStream_t stream);
+// Sums the dW partials (splits > 1) into dW and the dy column sums into db (when db).
+hipError_t launch_bwd_reduce(DType dt, const BwdArgs& b, hipStream_t stream);
+// Writes zeros to n bytes at p (n a multiple of 4; a kernel, not a memset node).
+hipError_t launch_zero_fill(void* p, size_t n, hipStream_t stream);
+
 }  // namespace fp

@@ -193,6 +193,55 @@ int fused_proj_destroy(fused_proj_t plan);
  * text of the last HIP error seen by this library on the calling thread follows. */
 const char *fused_proj_strerror(int code);
 
+/*
+ * Backward pass. Given the upstream gradients of the four outputs, computes the
+ * gradients of x, W and the bias (the backward pass of y = act(x W^T + b) that the
+ * xformers PR "Fused linear: small FW cleanup and much better perfs" discusses in its
+ * follow-up comments), by the chain rule through the forward steps in reverse:
+ *
+ *   dy[t, f]  = d_ff[t, f] * act'(y[t, f])          ff columns (y recomputed from x, W, b)
+ *   dy[t, ..] = R_p^T dq (dk) of the head             q and k: RoPE's rotation transposed
+ *                                                     (rotation by -phi) over the first
+ *                                                     rope_dims elements, the rest copied
+ *   dy[t, ..] = dv of the head                        v
+ *   dx[t, c]  = sum_f dy[t, f] W[c, f]
+ *   dW[c, f]  = sum_t x[t, c] dy[t, f]
+ *   db[f]     = sum_t dy[t, f]
+ *
+ * Accumulation in fp32; dy is rounded once to the storage type (it lives in the
+ * workspace), every gradient once more when stored.
+ *
+ * fused_proj_backward_workspace_size: bytes of device workspace fused_proj_backward
+ * needs for this plan (0 when there are no tokens). Returns FUSED_PROJ_OK or
+ * FUSED_PROJ_EINVAL (NULL argument).
+ */
+int fused_proj_backward_workspace_size(fused_proj_t plan, size_t *bytes);
+
+/*
+ * Enqueues the backward pass on `stream` (asynchronous; allocates nothing, never
+ * synchronises, so it may be captured into a HIP graph).
+ *
+ *   x, w, bias  the forward inputs (device, as for fused_proj_run); bias required when
+ *               has_bias
+ *   d_ff        device, laid out like ff ([b, S, ff_dim], or [b, ff_dim, S] with
+ *               FUSED_PROJ_FF_CHANNELS_FIRST); required when ff_dim > 0
+ *   dq          device [b*H, S, hd]; dk, dv [b*KVH, S, hd]; required when H*hd > 0
+ *   dx          device, dense in x's logical shape: [b, C, spatial...] for a
+ *               channels-first x, [b, S, C] for a token-major one (whatever x's strides)
+ *   dw          device, in W's layout ([C, F] or [F, C])
+ *   db          device [F] when has_bias, else ignored
+ *   workspace   device, at least fused_proj_backward_workspace_size bytes; its contents
+ *               on entry do not matter and are undefined afterwards. Calls that share
+ *               a workspace must not overlap in time.
+ * With no tokens (b = 0) dw and db are set to zero. Every pointer must be 16-byte
+ * aligned (FUSED_PROJ_EALIGN); outputs and the workspace may not overlap each other or
+ * any input (FUSED_PROJ_EALIAS); a missing required pointer or a short workspace is
+ * FUSED_PROJ_EINVAL; a failed launch FUSED_PROJ_EHIP.
+ */
+int fused_proj_backward(fused_proj_t plan, const void *x, const void *w, const void *bias, const void *d_ff,
+                        const void *dq, const void *dk, const void *dv, void *dx, void *dw, void *db,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
 /* Writes a one-line description of the chosen kernel and tiling into buf
  * (NUL-terminated, truncated to len). Returns FUSED_PROJ_OK or FUSED_PROJ_EINVAL. */
 int fused_proj_describe(fused_proj_t plan, char *buf, size_t len);

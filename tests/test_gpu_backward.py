@@ -1,0 +1,226 @@
+"""GPU parity of the backward pass (fused_proj_backward through the C ABI) against the
+float64 backward oracle, element by element.
+
+Bar: each gradient element is one sum of products, and its error must stay within
+4e-3 (bf16) or 1e-5 (fp32) of the Cauchy-Schwarz bound of that sum
+(oracle/compare.py backward_scales): ||dy_t|| ||W_c|| for dx, ||x_c|| ||dy_f|| for dW,
+sqrt(M) ||dy_f|| for db, with dy the oracle's float64 gradient of the fused output.
+dy is held in the storage type between the launches, which moves every sum by at
+most 2^-9 of its bound for bf16; the bar leaves room for that and the final rounding.
+Outputs start as NaN, so every element must have been written.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import compare as cmp
+from ff_input_projection_amd import EALIAS, EALIGN, EINVAL, FusedProjError
+from ff_input_projection_amd.workloads import WORKLOADS, make_grads, make_inputs, with_shape
+
+from helpers import plan_for
+from test_gpu_parity import SMALL
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _to_dev(t):
+    return None if t is None else t.to(DEV)
+
+
+def _token_rows(a, layout, nb, C, S):
+    """dx (x's logical layout) as token-major rows [M, C]."""
+    if layout == "channels_first":
+        return a.reshape(nb, C, S).transpose(0, 2, 1).reshape(nb * S, C)
+    return a.reshape(nb * S, C)
+
+
+def run_backward(wl, inp=None, gr=None):
+    inp = inp or make_inputs(wl)
+    gr = gr or make_grads(wl)
+    x, w, b = inp.x.to(DEV), inp.w.to(DEV), _to_dev(inp.bias)
+    proj = plan_for(wl, x)
+    outs = proj.alloc_grads(DEV)
+    for t in outs:
+        if t is not None:
+            t.fill_(float("nan"))
+    grads = proj.backward(x, w, b, _to_dev(gr.d_ff), _to_dev(gr.dq), _to_dev(gr.dk), _to_dev(gr.dv), out=outs)
+    torch.cuda.synchronize()
+    return proj, inp, gr, grads
+
+
+def backward_verdict(wl, inp, gr, grads):
+    ref = oracle.fused_proj_backward(inp.x64, wl.layout, inp.w64, wl.w_layout, inp.bias64, wl.ff_dim, wl.ff_act,
+                                     wl.n_heads, wl.head_dim, wl.rope, gr.d_ff64, gr.dq64, gr.dk64, gr.dv64,
+                                     rope_base=wl.rope_base, pos_offset=wl.pos_offset, n_kv_heads=wl.n_kv_heads,
+                                     qkv_order=wl.qkv_order, rope_dims=wl.rope_dims, ff_layout=wl.ff_layout)
+    rows, _ = cmp.token_rows(inp.x64, wl.layout, np.arange(wl.M, dtype=np.int64))
+    w_cf = inp.w64 if wl.w_layout == "cf" else inp.w64.T
+    sc = cmp.backward_scales(rows, w_cf, ref.dy)
+    dx, dw, db = (None if t is None else t.double().cpu().numpy() for t in grads)
+    got = [_token_rows(dx, wl.layout, wl.nb, wl.C, wl.S), dw if wl.w_layout == "cf" else dw.T]
+    exp = [_token_rows(ref.dx, wl.layout, wl.nb, wl.C, wl.S), ref.dw if wl.w_layout == "cf" else ref.dw.T]
+    scl = [sc.dx, sc.dw]
+    if wl.has_bias:
+        got.append(db)
+        exp.append(ref.db)
+        scl.append(sc.db)
+    return cmp.compare(got, exp, scl, wl.dtype)
+
+
+def _check(wl, label):
+    proj, inp, gr, grads = run_backward(wl)
+    v = backward_verdict(wl, inp, gr, grads)
+    print(f"[bwd parity] {label}: {v} ws={proj.workspace_bytes()}", flush=True)
+    n = wl.M * wl.C + wl.C * wl.F + (wl.F if wl.has_bias else 0)
+    assert v.ok and v.n == n, f"{label}: {v}"
+    return v
+
+
+@pytest.fixture(params=["auto", "general"])
+def kernel_choice(request, monkeypatch):
+    if request.param == "general":
+        monkeypatch.setenv("FUSED_PROJ_KERNEL", "general")
+    else:
+        monkeypatch.delenv("FUSED_PROJ_KERNEL", raising=False)
+    return request.param
+
+
+FULL = ["tiny_f32", "walrus_bf16", "bert_ff_bf16", "bert_qkv_bf16", "decoder_qkv_rope_bf16", "smallk_qkv_bf16",
+        "bert_ff_relu2_bf16", "gqa_rope8_bf16", "conv1x1_walrus_bf16"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_backward_full_size_every_element(name):
+    """Each workload at full size, every gradient element against the oracle."""
+    wl = WORKLOADS[name]
+    print(f"[case] backward full-size {name}", flush=True)
+    _check(wl, name)
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_backward_small_ragged(wl, kernel_choice):
+    """Small shapes with ragged token, channel and column tails, every layout, activation,
+    grouping and rotary option, through both kernel choices for dx."""
+    print(f"[case] backward small {wl.name} x={wl.x_shape} kernel={kernel_choice}", flush=True)
+    _check(wl, wl.name)
+
+
+SPLIT = [
+    # few dW tiles (C 64, F 192): the token contraction is split into ranges; channels-first
+    # with a slab length (40) that is not a multiple of the K step, [F,C] weight
+    with_shape(WORKLOADS["walrus_bf16"], "bwd_split_cf_fc", x_shape=(6, 64, 5, 8, 1), ff_dim=64, n_heads=2,
+               head_dim=32, w_layout="fc", seed=401),
+    # token-major, [C,F], GQA grouped, partial rotary, no bias, 1000 tokens
+    with_shape(WORKLOADS["gqa_rope8_bf16"], "bwd_split_tl_gqa", x_shape=(2, 500, 64), seed=402),
+    # fp32, token-major, channels-first ff
+    with_shape(WORKLOADS["tiny_f32"], "bwd_split_f32_ffcf", x_shape=(3, 48, 8, 6, 1), ff_dim=32, n_heads=2,
+               head_dim=8, ff_layout="channels_first", seed=403),
+]
+
+
+@pytest.mark.parametrize("wl", SPLIT, ids=[w.name for w in SPLIT])
+def test_backward_split_token_ranges(wl):
+    _check(wl, wl.name)
+
+
+def test_backward_strided_channel_slice_view():
+    """x as a channel slice of a wider tensor: the backward reads it in place; dx is dense."""
+    wl = with_shape(WORKLOADS["walrus_bf16"], "bwd_view", x_shape=(2, 48, 8, 16, 1), ff_dim=64, n_heads=2,
+                    head_dim=32, seed=404)
+    inp = make_inputs(wl)
+    gr = make_grads(wl)
+    big = torch.zeros((2, 64, 8, 16, 1), dtype=torch.bfloat16)
+    big[:, 8:56] = inp.x
+    xv = big.to(DEV)[:, 8:56]
+    proj = plan_for(wl, xv)
+    grads = proj.backward(xv, inp.w.to(DEV), inp.bias.to(DEV), _to_dev(gr.d_ff), _to_dev(gr.dq), _to_dev(gr.dk),
+                          _to_dev(gr.dv))
+    torch.cuda.synchronize()
+    v = backward_verdict(wl, inp, gr, grads)
+    print(f"[bwd parity] channel-slice view: {v}", flush=True)
+    assert v.ok
+
+
+def test_backward_no_tokens_gives_zero_weight_gradients():
+    wl = with_shape(WORKLOADS["walrus_bf16"], "bwd_empty", x_shape=(0, 64, 8, 8, 1), ff_dim=64, n_heads=2,
+                    head_dim=32)
+    x = torch.empty(wl.x_shape, dtype=torch.bfloat16, device=DEV)
+    w = torch.randn((64, wl.F), device=DEV).to(torch.bfloat16)
+    b = torch.randn((wl.F,), device=DEV).to(torch.bfloat16)
+    proj = plan_for(wl, x)
+    assert proj.workspace_bytes() == 0
+    dx, dw, db = proj.alloc_grads(DEV)
+    dw.fill_(float("nan"))
+    db.fill_(float("nan"))
+    ffs, qs, kvs = proj.out_shapes()
+    e = lambda s: torch.empty(s, dtype=torch.bfloat16, device=DEV)
+    proj.backward(x, w, b, e(ffs), e(qs), e(kvs), e(kvs), out=(dx, dw, db))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dw).item() == 0 and torch.count_nonzero(db).item() == 0
+
+
+def test_backward_deterministic_and_graph_replays():
+    """Two eager calls give identical bits; a captured call replays to the same bits three
+    times (the workspace and outputs are refilled with NaN between replays)."""
+    wl = SPLIT[0]
+    inp, gr = make_inputs(wl), make_grads(wl)
+    x, w, b = inp.x.to(DEV), inp.w.to(DEV), inp.bias.to(DEV)
+    ups = [_to_dev(t) for t in (gr.d_ff, gr.dq, gr.dk, gr.dv)]
+    proj = plan_for(wl, x)
+    e1 = [t.clone() for t in proj.backward(x, w, b, *ups)]
+    e2 = proj.backward(x, w, b, *ups)
+    torch.cuda.synchronize()
+    for a, c in zip(e1, e2):
+        assert torch.equal(a, c)
+    outs = proj.alloc_grads(DEV)
+    ws = torch.empty(proj.workspace_bytes(), dtype=torch.uint8, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            proj.backward(x, w, b, *ups, out=outs, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        ws.fill_(255)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, c in zip(e1, outs):
+            assert torch.equal(a, c), f"replay {rep}"
+
+
+def test_backward_error_paths():
+    wl = SPLIT[0]
+    inp, gr = make_inputs(wl), make_grads(wl)
+    x, w, b = inp.x.to(DEV), inp.w.to(DEV), inp.bias.to(DEV)
+    d_ff, dq, dk, dv = (_to_dev(t) for t in (gr.d_ff, gr.dq, gr.dk, gr.dv))
+    proj = plan_for(wl, x)
+    dx, dw, db = proj.alloc_grads(DEV)
+    nbytes = proj.workspace_bytes()
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    st = torch.cuda.current_stream().cuda_stream
+    p = lambda t: t.data_ptr()
+    args = [p(x), p(w), p(b), p(d_ff), p(dq), p(dk), p(dv), p(dx), p(dw), p(db), p(ws)]
+    assert proj.backward_ptrs(*args, nbytes, st) == 0
+    assert proj.backward_ptrs(*args, nbytes - 1, st) == EINVAL                   # short workspace
+    bad = list(args)
+    bad[6] = None
+    assert proj.backward_ptrs(*bad, nbytes, st) == EINVAL                        # dv missing
+    bad = list(args)
+    bad[7] = p(dx) + 2
+    assert proj.backward_ptrs(*bad, nbytes, st) == EALIGN
+    bad = list(args)
+    bad[8] = p(dx)
+    assert proj.backward_ptrs(*bad, nbytes, st) == EALIAS                        # dw over dx
+    bad = list(args)
+    bad[10] = p(d_ff)
+    assert proj.backward_ptrs(*bad, nbytes, st) == EALIAS                        # workspace over d_ff
+    torch.cuda.synchronize()
+    with pytest.raises(FusedProjError):
+        proj.backward(x, w, b, d_ff, dq, dk, dv, out=(dx, dw, db), workspace=ws[:nbytes - 16])
