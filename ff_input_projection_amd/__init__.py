@@ -26,10 +26,10 @@ LIB_PATH = os.path.join(_PKG, "libfused_proj.so")
 
 EXPORTED_SYMBOLS = ["fused_proj_validate", "fused_proj_create", "fused_proj_run", "fused_proj_destroy",
                     "fused_proj_strerror", "fused_proj_describe", "fused_proj_backward_workspace_size",
-                    "fused_proj_backward",
+                    "fused_proj_backward", "fused_proj_backward_noalloc", "fused_proj_noalloc_scratch_bytes",
                     "split_rope_validate", "split_rope_create", "split_rope_run", "split_rope_destroy"]
 
-OK, EINVAL, EUNSUPPORTED, EALIGN, EALIAS, EHIP = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EUNSUPPORTED, EALIGN, EALIAS, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 BF16, F32 = 0, 1
 X_CHANNELS_FIRST, X_TOKENS_LAST = 0, 1
 W_CF, W_FC = 0, 1
@@ -100,6 +100,10 @@ def load_library():
     lib.fused_proj_backward_workspace_size.restype = ctypes.c_int
     lib.fused_proj_backward.argtypes = [vp] * 12 + [ctypes.c_size_t, vp]
     lib.fused_proj_backward.restype = ctypes.c_int
+    lib.fused_proj_backward_noalloc.argtypes = [vp] * 12
+    lib.fused_proj_backward_noalloc.restype = ctypes.c_int
+    lib.fused_proj_noalloc_scratch_bytes.argtypes = []
+    lib.fused_proj_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.split_rope_validate.argtypes = [ctypes.POINTER(SplitRopeDesc)]
     lib.split_rope_validate.restype = ctypes.c_int
     lib.split_rope_create.argtypes = [ctypes.POINTER(SplitRopeDesc), ctypes.POINTER(vp)]
@@ -317,6 +321,30 @@ class FusedProjection:
                                            p(workspace), ctypes.c_size_t(wsb), ctypes.c_void_p(st.cuda_stream))
         if rc != OK:
             raise FusedProjError(rc, "fused_proj_backward")
+        return dx, dw, db
+
+    def backward_noalloc(self, x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None, d_ff=None, dq=None,
+                         dk=None, dv=None, out=None, stream: torch.cuda.Stream | None = None):
+        """The backward pass through fused_proj_backward_noalloc: the library's static scratch
+        buffer serves as the workspace (nothing is allocated when `out` is given). Calls on
+        one GPU share that buffer and must not overlap."""
+        ffs, qs, kvs = self.out_shapes()
+        for name, t, shp in (("d_ff", d_ff, ffs), ("dq", dq, qs), ("dk", dk, kvs), ("dv", dv, kvs)):
+            if shp is not None and (t is None or tuple(t.shape) != shp or not t.is_contiguous()
+                                    or t.dtype != self.dtype):
+                raise ValueError(f"{name} must be a contiguous {shp} {self.dtype} tensor")
+        dx, dw, db = out if out is not None else self.alloc_grads(x.device)
+        for t, shp in zip((dx, dw, db), self.grad_shapes()):
+            if shp is not None and (t is None or tuple(t.shape) != shp or not t.is_contiguous()
+                                    or t.dtype != self.dtype):
+                raise ValueError(f"gradient output must be a contiguous {shp} {self.dtype} tensor")
+        st = stream if stream is not None else torch.cuda.current_stream(x.device)
+        p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+        rc = self._lib.fused_proj_backward_noalloc(self._h, p(x), p(w), p(bias) if self.has_bias else None,
+                                                   p(d_ff), p(dq), p(dk), p(dv), p(dx), p(dw),
+                                                   p(db) if self.has_bias else None, ctypes.c_void_p(st.cuda_stream))
+        if rc != OK:
+            raise FusedProjError(rc, "fused_proj_backward_noalloc")
         return dx, dw, db
 
     def backward_ptrs(self, x, w, bias, d_ff, dq, dk, dv, dx, dw, db, workspace, workspace_bytes: int,

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -142,6 +143,42 @@ bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi
 }  // namespace
 
 void fp::set_last_hip_error(hipError_t e) { g_last_hip = e; }
+
+// ---------------------------------------------------------------- static scratch
+// The workspace of fused_proj_backward_noalloc: a fixed device array (each GPU the library
+// runs on holds its own copy until the process ends). In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address is looked up once per
+// device (hipGetSymbolAddress, at plan creation with that device current) and only that
+// address is ever passed to kernels.
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+// Looks up this device's scratch address once (device current); FUSED_PROJ_OK or EHIP.
+int scratch_setup(int device) {
+    if (device < 0 || device >= kMaxDevices) return FUSED_PROJ_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[device] != nullptr) return FUSED_PROJ_OK;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+        g_last_hip = e != hipSuccess ? e : hipErrorInvalidSymbol;
+        return FUSED_PROJ_EHIP;
+    }
+    g_scratch_ptr[device] = ptr;
+    return FUSED_PROJ_OK;
+}
+void* scratch_ptr(int device) {
+    if (device < 0 || device >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch_ptr[device];
+}
+}  // namespace
 
 struct fused_proj_plan {
     fused_proj_desc d;
@@ -388,6 +425,7 @@ int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backwa
     a.col_desc = h->d_desc;
     if (with_backward) {
         rc = plan_backward(h);
+        if (rc == FUSED_PROJ_OK) rc = scratch_setup(h->device);
         if (rc) {
             fused_proj_destroy(h);
             return rc;
@@ -486,6 +524,21 @@ int fused_proj_destroy(fused_proj_t h) {
     }
     return rc_sub;
 }
+
+int fused_proj_backward_noalloc(fused_proj_t h, const void* x, const void* w, const void* bias,
+                                const void* d_ff, const void* dq, const void* dk, const void* dv, void* dx,
+                                void* dw, void* db, void* stream) {
+    if (!h) return FUSED_PROJ_EINVAL;
+    if (h->ws_bytes > kScratchBytes) return FUSED_PROJ_ESCRATCH;
+    void* ws = nullptr;
+    if (h->ws_bytes > 0) {
+        ws = scratch_ptr(h->device);
+        if (ws == nullptr) return FUSED_PROJ_EHIP;
+    }
+    return fused_proj_backward(h, x, w, bias, d_ff, dq, dk, dv, dx, dw, db, ws, ws ? kScratchBytes : 0, stream);
+}
+
+size_t fused_proj_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int fused_proj_backward_workspace_size(fused_proj_t h, size_t* bytes) {
     if (!h || !bytes) return FUSED_PROJ_EINVAL;
@@ -589,6 +642,9 @@ const char* fused_proj_strerror(int code) {
         case FUSED_PROJ_EUNSUPPORTED: return "unsupported shape, layout or stride";
         case FUSED_PROJ_EALIGN: return "device pointer not 16-byte aligned";
         case FUSED_PROJ_EALIAS: return "output overlaps another output or an input";
+        case FUSED_PROJ_ESCRATCH:
+            return "the problem needs more scratch memory than the static buffer of the allocation-free entry "
+                   "point holds (see fused_proj_noalloc_scratch_bytes)";
         case FUSED_PROJ_EHIP:
             std::snprintf(g_msg, sizeof(g_msg), "HIP error: %s", hipGetErrorString(g_last_hip));
             return g_msg;

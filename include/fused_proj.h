@@ -66,6 +66,8 @@ extern "C" {
 #define FUSED_PROJ_EALIGN (-3)       /* a device pointer is not 16-byte aligned */
 #define FUSED_PROJ_EALIAS (-4)       /* an output overlaps another output or an input */
 #define FUSED_PROJ_EHIP (-5)         /* a HIP runtime call failed (allocation, copy, launch) */
+#define FUSED_PROJ_ESCRATCH (-6)     /* fused_proj_backward_noalloc: the workspace this problem needs
+                                        exceeds the static scratch buffer */
 
 /* Storage type of x, W, bias and every output. Accumulation is always fp32. */
 #define FUSED_PROJ_BF16 0
@@ -241,6 +243,26 @@ int fused_proj_backward_workspace_size(fused_proj_t plan, size_t *bytes);
 int fused_proj_backward(fused_proj_t plan, const void *x, const void *w, const void *bias, const void *d_ff,
                         const void *dq, const void *dk, const void *dv, void *dx, void *dw, void *db,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): fused_proj_backward with the
+ * library's own static device scratch buffer as the workspace, so neither the library
+ * nor the caller allocates anything. The buffer holds fused_proj_noalloc_scratch_bytes()
+ * bytes (64 MiB) on each GPU the library runs on, for the whole life of the process; a
+ * plan whose fused_proj_backward_workspace_size exceeds it is rejected with
+ * FUSED_PROJ_ESCRATCH. Arguments, results and the other errors are those of
+ * fused_proj_backward. Every call on one GPU shares that GPU's buffer and leaves its last
+ * contents there (the kernels write every scratch byte they read, so nothing needs to
+ * start at zero): calls that overlap in time on one GPU, from any thread or stream, race
+ * and must be serialised by the caller.
+ */
+int fused_proj_backward_noalloc(fused_proj_t plan, const void *x, const void *w, const void *bias,
+                                const void *d_ff, const void *dq, const void *dk, const void *dv, void *dx,
+                                void *dw, void *db, void *stream);
+
+/* Size in bytes of the static scratch buffer of fused_proj_backward_noalloc. */
+size_t fused_proj_noalloc_scratch_bytes(void);
 
 /* Writes a one-line description of the chosen kernel and tiling into buf
  * (NUL-terminated, truncated to len). Returns FUSED_PROJ_OK or FUSED_PROJ_EINVAL. */
