@@ -25,6 +25,8 @@ Also on the line:
                 QKV, decoder, small-K), each timed the same way and checked against
                 the oracle on every output element;
   cpu_1core     the oracle on one core for the tiny and small-K workloads;
+  backward      fused_proj_backward (dy, dx, dW and db launches) timed per config, the
+                headline's gradients checked against the float64 backward oracle;
   sclk_mhz      the graphics clock sampled while the headline kernel runs;
   context       the pages' own figures for the pathology this op removes.
 """
@@ -315,6 +317,83 @@ def measure_workload(wl, dev, steps, warmup, min_warmup_s, ring_arg=0, graph=Fal
     return t, desc, host, inp, sclk
 
 
+def backward_flops(wl) -> float:
+    """Algorithmic flops of the backward pass: dx = dy W^T and dW = X^T dy (2 M C F each),
+    plus the ff columns' forward product recomputed where an activation is differentiated."""
+    f = 4.0 * wl.M * wl.C * wl.F
+    if wl.ff_dim > 0 and wl.ff_act != "none":
+        f += 2.0 * wl.M * wl.C * wl.ff_dim
+    return f
+
+
+def measure_backward(wl, dev, steps, min_warmup_s, check: bool):
+    """Time fused_proj_backward (all of its launches) on one workload; optionally check
+    every gradient element against the float64 backward oracle."""
+    import numpy as np
+    import torch
+
+    from ff_input_projection_amd.workloads import make_grads, make_inputs
+
+    inp, gr = make_inputs(wl), make_grads(wl)
+    x, w = inp.x.to(dev), inp.w.to(dev)
+    b = inp.bias.to(dev) if inp.bias is not None else None
+    ups = [None if t is None else t.to(dev) for t in (gr.d_ff, gr.dq, gr.dk, gr.dv)]
+    proj = make_plan(wl, x)
+    outs = proj.alloc_grads(dev)
+    nbytes = proj.workspace_bytes()
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    ptr = lambda t: None if t is None else t.data_ptr()
+    args = [ptr(x), ptr(w), ptr(b), *[ptr(t) for t in ups], *[ptr(t) for t in outs], ptr(ws)]
+
+    def launch(i):
+        rc = proj.backward_ptrs(*args, nbytes, sh)
+        if rc != 0:
+            raise RuntimeError(f"fused_proj_backward failed with status {rc}")
+
+    t = time_launches(launch, steps, 3, min_warmup_s, stream)
+    flops = backward_flops(wl)
+    entry = {"workload": wl.name, "us_mean": round(t["mean_us"], 2), "us_median": round(t["median_us"], 2),
+             "us_p10": round(t["p10_us"], 2), "us_p90": round(t["p90_us"], 2), "launches": steps,
+             "gflop": round(flops / 1e9, 2), "tflop_per_s": round(flops / (t["mean_us"] * 1e-6) / 1e12, 2),
+             "frac": round(flops / (t["mean_us"] * 1e-6) / 1e12 / PEAK_TFLOPS[wl.dtype], 4),
+             "workspace_bytes": nbytes}
+    if check:
+        import oracle
+        from oracle import compare as cmp
+
+        torch.cuda.synchronize()
+        ref = oracle.fused_proj_backward(inp.x64, wl.layout, inp.w64, wl.w_layout, inp.bias64, wl.ff_dim,
+                                         wl.ff_act, wl.n_heads, wl.head_dim, wl.rope, gr.d_ff64, gr.dq64, gr.dk64,
+                                         gr.dv64, rope_base=wl.rope_base, pos_offset=wl.pos_offset,
+                                         n_kv_heads=wl.n_kv_heads, qkv_order=wl.qkv_order, rope_dims=wl.rope_dims,
+                                         ff_layout=wl.ff_layout)
+        rows, _ = cmp.token_rows(inp.x64, wl.layout, np.arange(wl.M, dtype=np.int64))
+        w_cf = inp.w64 if wl.w_layout == "cf" else inp.w64.T
+        sc = cmp.backward_scales(rows, w_cf, ref.dy)
+
+        def token_rows(a):
+            if wl.layout == "channels_first":
+                return a.reshape(wl.nb, wl.C, wl.S).transpose(0, 2, 1).reshape(wl.M, wl.C)
+            return a.reshape(wl.M, wl.C)
+
+        dx, dw, db = (None if t_ is None else t_.double().cpu().numpy() for t_ in outs)
+        got = [token_rows(dx), dw if wl.w_layout == "cf" else dw.T]
+        exp = [token_rows(ref.dx), ref.dw if wl.w_layout == "cf" else ref.dw.T]
+        scl = [sc.dx, sc.dw]
+        if wl.has_bias:
+            got.append(db)
+            exp.append(ref.db)
+            scl.append(sc.db)
+        vd = cmp.compare(got, exp, scl, wl.dtype)
+        entry["parity"] = {"ok": vd.ok, "max_err_over_tol": round(vd.max_ratio, 5), "elements": vd.n}
+    del x, w, b, ups, outs, ws
+    proj.close()
+    torch.cuda.empty_cache()
+    return entry
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -329,6 +408,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle (timing and parity)")
     ap.add_argument("--no-configs", action="store_true", help="time only --workload (no per-config array)")
     ap.add_argument("--config-steps", type=int, default=200, help="timed launches per config (x5 for small-K)")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times), to scale HBM counters")
     args = ap.parse_args()
@@ -401,6 +481,17 @@ def main() -> int:
             measured[name] = (ct, cdesc, chost, cinp)
             print(f"[bench] {name}: mean {ct['mean_us']:.2f} us, median {ct['median_us']:.2f} "
                   f"(p10 {ct['p10_us']:.2f}, p90 {ct['p90_us']:.2f})", file=sys.stderr, flush=True)
+
+    # ---- the backward pass of every configuration (its own launches; the headline's
+    # gradients checked against the oracle on every element)
+    if not args.no_backward:
+        bwd = []
+        for name in (CONFIG_WORKLOADS if not args.no_configs else [wl.name]):
+            e = measure_backward(WORKLOADS[name], dev, 50, min(args.min_warmup_s, 0.5),
+                                 check=(name == wl.name and not args.no_cpu_baseline))
+            print(f"[bench] backward {name}: {e}", file=sys.stderr, flush=True)
+            bwd.append(e)
+        result["backward"] = bwd
 
     # ---- the oracle: CPU baseline on the headline workload, then every output element of
     # every measured workload against it
