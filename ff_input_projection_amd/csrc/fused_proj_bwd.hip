@@ -449,14 +449,23 @@ __global__ __launch_bounds__(256) void bwd_reduce_dw_kernel(BwdArgs b) {
     }
 }
 
+// db from the per-tile column sums: 64 columns per workgroup, its 256 threads summing
+// every fourth row (coalesced 256-byte row segments), then the four partial sums in LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_reduce_db_kernel(BwdArgs b) {
-    const int f = blockIdx.x * 256 + threadIdx.x;
+    __shared__ float part[4][64];
     const int N = b.f.N;
-    if (f >= N) return;
+    const int fx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int f = blockIdx.x * 64 + fx;
     float sum = 0.0f;
-    for (int r = 0; r < b.db_tiles; ++r) sum += b.dbp[(int64_t)r * N + f];
-    static_cast<T*>(b.db)[f] = (T)sum;
+    if (f < N) {
+#pragma unroll 4
+        for (int r = ty; r < b.db_tiles; r += 4) sum += b.dbp[(int64_t)r * N + f];
+    }
+    part[ty][fx] = sum;
+    __syncthreads();
+    if (ty == 0 && f < N)
+        static_cast<T*>(b.db)[f] = (T)((part[0][fx] + part[1][fx]) + (part[2][fx] + part[3][fx]));
 }
 
 __global__ __launch_bounds__(256) void zero_fill_kernel(unsigned* p, size_t n) {
@@ -498,7 +507,7 @@ hipError_t launch_reduce_t(const BwdArgs& b, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (b.db != nullptr && b.dbp != nullptr) {
-        hipLaunchKernelGGL((bwd_reduce_db_kernel<T>), dim3((unsigned)((b.f.N + 255) / 256)), dim3(256), 0, s, b);
+        hipLaunchKernelGGL((bwd_reduce_db_kernel<T>), dim3((unsigned)((b.f.N + 63) / 64)), dim3(256), 0, s, b);
         return hipGetLastError();
     }
     return hipSuccess;
