@@ -189,6 +189,7 @@ struct fused_proj_plan {
     fp::KernelArgs base;
     bool fast = false;  // fast bf16 kernel (else the general kernel)
     int dg = 0;         // its RoPE partner distance in 8-column groups
+    int epi = 0;        // its epilogue variant
     float* d_cos = nullptr;
     float* d_sin = nullptr;
     void* d_zeros = nullptr;
@@ -329,16 +330,20 @@ int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backwa
     // general kernel on such shapes (C 320, 72, 200 on large tiles): faster or equal.
     const bool exact = desc->channels > 0;
     const bool addressable = fp::fast_addressable(r.M, r.S, desc->ff_dim, r.qw);
-    // the fast kernel's epilogue applies exact-erf GELU or nothing: other activations take
-    // the general kernel, even when the fast one is forced
-    const bool fast_act = desc->ff_dim == 0 || desc->ff_act == FUSED_PROJ_ACT_NONE ||
-                          desc->ff_act == FUSED_PROJ_ACT_GELU_ERF;
-    // ... and the plain multi-head layout: as many k/v heads as q heads, contiguous order,
-    // the full head rotated
+    // the fast kernel's epilogue applies every ff activation; it needs the plain multi-head
+    // layout (as many k/v heads as q heads, contiguous order, the full head rotated), and a
+    // channels-first ff output only when ff_dim is a multiple of a wave's 128 columns
     const bool fast_heads = r.kvh == desc->n_heads && desc->qkv_order == FUSED_PROJ_QKV_CONTIGUOUS &&
-                            (!desc->rope || r.rd == desc->head_dim) &&
-                            (desc->ff_dim == 0 || desc->ff_layout == FUSED_PROJ_FF_TOKENS_LAST);
-    h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && addressable && fast_act && fast_heads &&
+                            (!desc->rope || r.rd == desc->head_dim);
+    // its epilogue variant: tanh GELU and squared ReLU, and a channels-first ff output (when
+    // ff_dim is a multiple of the wave's 128 columns, with exact GELU or no activation), are
+    // compiled without RoPE
+    const bool ff_cf = desc->ff_dim > 0 && desc->ff_layout == FUSED_PROJ_FF_CHANNELS_FIRST;
+    const bool other_act = desc->ff_dim > 0 && (desc->ff_act == FUSED_PROJ_ACT_GELU_TANH ||
+                                                desc->ff_act == FUSED_PROJ_ACT_RELU_SQUARED);
+    h->epi = ff_cf ? 2 : other_act ? 1 : 0;
+    const bool fast_epi = h->epi == 0 || (dg == 0 && (h->epi == 1 || (!other_act && desc->ff_dim % 128 == 0)));
+    h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && addressable && fast_heads && fast_epi &&
               (exact || want_fast) && !want_general;
     h->dg = dg < 0 ? 0 : dg;
     h->tile = h->fast ? fp_plan : fp::TilePlan{128, 128, h->dt == fp::DType::BF16 ? 64 : 32, 8, 0};
@@ -495,7 +500,7 @@ int fused_proj_run(fused_proj_t h, const void* x, const void* w, const void* bia
     a.k = k;
     a.v = v;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    e = h->fast ? fp::launch_fused_proj_fast(h->x_tl, h->w_fc, h->dg, h->tile, a, s)
+    e = h->fast ? fp::launch_fused_proj_fast(h->x_tl, h->w_fc, h->dg, h->epi, h->tile, a, s)
                 : fp::launch_fused_proj(h->dt, h->x_tl, h->w_fc, h->tile, a, s);
     if (e == hipSuccess && h->debug_sync) {
         e = hipStreamSynchronize(s);

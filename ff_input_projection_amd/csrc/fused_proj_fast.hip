@@ -339,11 +339,17 @@ struct SmallTile {
 constexpr int kBK = 32;
 // Restaged epilogue rows: 16 tokens x (128 bf16 columns + 16 bytes of padding).
 constexpr int kRestageRows = 16, kRestageRow = 272;
+// Channels-first ff restage: 32 token rows of 64 columns (8 bytes of padding per row).
+constexpr int kCfRow = 136;
+static_assert(32 * kCfRow <= kRestageRows * kRestageRow, "channels-first restage fits the wave's rows");
+// Epilogue variants: exact-erf GELU or none with token-major stores; tanh GELU or squared
+// ReLU (no RoPE); a channels-first ff output (no RoPE).
+constexpr int kEpiDefault = 0, kEpiOtherAct = 1, kEpiFfChannelsFirst = 2;
 
 // X_TL: x token-major [b,s,c] (else channels-first). W_FC: W [F,C] (else [C,F]).
 // DG: RoPE partner distance in 8-column groups (hd/16), 0 = no RoPE. TAILK: K is not a
 // multiple of T::STAGES * BK (some K steps are partial or padding).
-template <bool X_TL, bool W_FC, int DG, bool TAILK, class T>
+template <bool X_TL, bool W_FC, int DG, bool TAILK, class T, int EPI>
 __global__ __launch_bounds__(64 * T::NWF * T::NWT, T::PER_CU) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE))) void
 fused_proj_fast_kernel(KernelArgs p) {
     constexpr int BF = T::BF, BT = T::BT, BK = kBK, STAGES = T::STAGES, PF = T::PF, kNWT = T::NWT;
@@ -610,6 +616,12 @@ fused_proj_fast_kernel(KernelArgs p) {
         const int gl = lane_e & 15, r0 = lane_e >> 4;
         const unsigned wr_lds = wave_lds + (lane_e & 15) * kRestageRow + (lane_e >> 5) * 8;
         const unsigned rd_lds = wave_lds + r0 * kRestageRow + gl * 16;
+        // channels-first ff stores: the writer of token row lane%32 and column half lane/32 of
+        // each 8-column group; the transposing reader, lane l of 16-lane group g naming row
+        // 8g + (l%16)/4 and columns 4(l%4).. of a 4 x 16 block and receiving column l%16 of
+        // its 4 rows
+        const unsigned cf_wr = wave_lds + (lane_e & 31) * kCfRow + (lane_e >> 5) * 8;
+        const unsigned cf_rd = wave_lds + (8 * (lane_e >> 4) + ((lane_e & 15) >> 2)) * kCfRow + (lane_e & 3) * 8;
         // this lane's chunk: its destination buffer and element offset, and the bytes
         // between consecutive tokens there
         unsigned dl = desc[0];
@@ -675,7 +687,15 @@ fused_proj_fast_kernel(KernelArgs p) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) y[u] = acc[G >> 2][j][4 * (G & 3) + u];
                 if (kind == 0) {
-                    if (act == 1) {
+                    if constexpr (EPI == kEpiOtherAct) {
+                        if (act == 2) {
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) y[u] = gelu_tanh(y[u]);
+                        } else {
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) y[u] = relu_squared(y[u]);
+                        }
+                    } else if (act == 1) {
 #pragma unroll
                         for (int u = 0; u < 4; ++u) y[u] = gelu_erf_poly(y[u]);
                     }
@@ -707,6 +727,36 @@ fused_proj_fast_kernel(KernelArgs p) {
             }
             // the next block's cos/sin, ahead of this block's stores
             if (j + 1 < TJ) load_rope(j + 1, 0);
+            if constexpr (EPI == kEpiFfChannelsFirst) {
+                if (fw < ff_dim) {
+                    // channels-first ff [b, ff, S] (ff_dim is a multiple of the wave's 128
+                    // columns, so the whole wave is ff): the block goes through LDS one column
+                    // half at a time as 32 token rows of 64 columns; two transposing reads give
+                    // each lane 8 consecutive tokens of one column, and the 16-lane groups take
+                    // the block's four 8-token runs, so every column is stored as one 64-byte run
+#pragma unroll
+                    for (int hc = 0; hc < 2; ++hc) {
+#pragma unroll
+                        for (int G = 0; G < NG / 2; ++G)
+                            *(__attribute__((address_space(3))) u32x2*)(size_t)(cf_wr + G * 16) = pk[NG / 2 * hc + G];
+                        const int t = tw0 + 32 * j + 8 * (lane_e >> 4);   // in one slab (S % 8 == 0)
+                        const unsigned bi = fastdiv_u31((uint32_t)(t < M ? t : 0), p.div_s);
+                        const unsigned sidx = (unsigned)(t < M ? t : 0) - bi * (unsigned)S;
+#pragma unroll
+                        for (int cb = 0; cb < 4; ++cb) {
+                            const unsigned a = cf_rd + (unsigned)(32 * cb);
+                            const bf16x8 v = join_tr(lds_tr16(a), lds_tr16(a + 4 * kCfRow));
+                            if (t < M) {
+                                const unsigned col = (unsigned)(fw + 64 * hc + 16 * cb + (lane_e & 15));
+                                char* const dst = static_cast<char*>(p.ff) +
+                                                  ((bi * (unsigned)ff_dim + col) * (unsigned)S + sidx) * 2u;
+                                __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(dst));
+                            }
+                        }
+                    }
+                    continue;
+                }
+            }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 // the lanes whose token is in this half of the token block write its rows
@@ -743,30 +793,39 @@ fused_proj_fast_kernel(KernelArgs p) {
     wait_vmcnt<0>();   // the trailing loads into LDS
 }
 
-template <bool X_TL, bool W_FC, int DG, class T>
+template <bool X_TL, bool W_FC, int DG, class T, int EPI>
 hipError_t launch_fast_one(const KernelArgs& a, int grid, hipStream_t stream) {
     const dim3 block(64 * T::NWF * T::NWT);
     if (a.K > 0 && a.K % (kBK * T::STAGES) == 0)
-        hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, false, T>), dim3(grid), block, 0, stream, a);
+        hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, false, T, EPI>), dim3(grid), block, 0, stream, a);
     else
-        hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, true, T>), dim3(grid), block, 0, stream, a);
+        hipLaunchKernelGGL((fused_proj_fast_kernel<X_TL, W_FC, DG, true, T, EPI>), dim3(grid), block, 0, stream, a);
     return hipGetLastError();
 }
 
-template <int DG, class T>
+template <int DG, class T, int EPI>
 hipError_t dispatch_fast_layouts(bool x_tl, bool w_fc, const KernelArgs& a, int grid, hipStream_t s) {
     if (x_tl)
-        return w_fc ? launch_fast_one<true, true, DG, T>(a, grid, s) : launch_fast_one<true, false, DG, T>(a, grid, s);
-    return w_fc ? launch_fast_one<false, true, DG, T>(a, grid, s) : launch_fast_one<false, false, DG, T>(a, grid, s);
+        return w_fc ? launch_fast_one<true, true, DG, T, EPI>(a, grid, s)
+                    : launch_fast_one<true, false, DG, T, EPI>(a, grid, s);
+    return w_fc ? launch_fast_one<false, true, DG, T, EPI>(a, grid, s)
+                : launch_fast_one<false, false, DG, T, EPI>(a, grid, s);
 }
 
 template <class T>
-hipError_t dispatch_fast_rope(int dg, bool x_tl, bool w_fc, const KernelArgs& a, int grid, hipStream_t s) {
+hipError_t dispatch_fast_rope(int dg, int epi, bool x_tl, bool w_fc, const KernelArgs& a, int grid, hipStream_t s) {
+    if (epi != kEpiDefault) {
+        // the other epilogues are compiled without RoPE only
+        if (dg != 0) return hipErrorInvalidValue;
+        if (epi == kEpiOtherAct) return dispatch_fast_layouts<0, T, kEpiOtherAct>(x_tl, w_fc, a, grid, s);
+        if (epi == kEpiFfChannelsFirst) return dispatch_fast_layouts<0, T, kEpiFfChannelsFirst>(x_tl, w_fc, a, grid, s);
+        return hipErrorInvalidValue;
+    }
     switch (dg) {
-        case 0: return dispatch_fast_layouts<0, T>(x_tl, w_fc, a, grid, s);
-        case 2: return dispatch_fast_layouts<2, T>(x_tl, w_fc, a, grid, s);
-        case 4: return dispatch_fast_layouts<4, T>(x_tl, w_fc, a, grid, s);
-        case 8: return dispatch_fast_layouts<8, T>(x_tl, w_fc, a, grid, s);
+        case 0: return dispatch_fast_layouts<0, T, kEpiDefault>(x_tl, w_fc, a, grid, s);
+        case 2: return dispatch_fast_layouts<2, T, kEpiDefault>(x_tl, w_fc, a, grid, s);
+        case 4: return dispatch_fast_layouts<4, T, kEpiDefault>(x_tl, w_fc, a, grid, s);
+        case 8: return dispatch_fast_layouts<8, T, kEpiDefault>(x_tl, w_fc, a, grid, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -823,19 +882,19 @@ void fast_col_desc(int64_t S, int64_t ff_dim, int64_t n_heads, int64_t head_dim,
     }
 }
 
-hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, const TilePlan& pl, const KernelArgs& a,
+hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, int epi, const TilePlan& pl, const KernelArgs& a,
                                   hipStream_t stream) {
     if (pl.bk != kBK || pl.grid <= 0 || pl.grid % 8) return hipErrorInvalidValue;
     auto is = [&](auto t) { return pl.bm == decltype(t)::BT && pl.bn == decltype(t)::BF; };
     switch (pl.shape) {
         case kFastLarge:
-            if (is(LargeTile{})) return dispatch_fast_rope<LargeTile>(dg, x_tokens_last, w_fc, a, pl.grid, stream);
+            if (is(LargeTile{})) return dispatch_fast_rope<LargeTile>(dg, epi, x_tokens_last, w_fc, a, pl.grid, stream);
             break;
         case kFastSmall:
             // one tile per workgroup at most: each XCD's share of the tiles fits its workgroups
             static_assert(SmallTile::SINGLE, "small tiles are planned one per workgroup");
             if ((int64_t)a.tiles_m * a.tiles_n > (int64_t)(pl.grid / 8) * 8) return hipErrorInvalidValue;
-            if (is(SmallTile{})) return dispatch_fast_rope<SmallTile>(dg, x_tokens_last, w_fc, a, pl.grid, stream);
+            if (is(SmallTile{})) return dispatch_fast_rope<SmallTile>(dg, epi, x_tokens_last, w_fc, a, pl.grid, stream);
             break;
         default: break;
     }

@@ -106,7 +106,9 @@ bool fast_addressable(int64_t M, int64_t S, int64_t ff_dim, int64_t qw);
 void fast_col_desc(int64_t S, int64_t ff_dim, int64_t n_heads, int64_t head_dim, int64_t F, unsigned* out,
                    int64_t entries);
 int64_t fast_col_desc_entries(int64_t F);
-hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, const TilePlan& plan,
+// epi: 0 exact-erf GELU or no activation, token-major ff; 1 tanh GELU or squared ReLU;
+// 2 channels-first ff (1 and 2 without RoPE, dg == 0).
+hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, int epi, const TilePlan& plan,
                                   const KernelArgs& args, hipStream_t stream);
 
 // ---------------------------------------------------------------- backward pass

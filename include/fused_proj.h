@@ -90,7 +90,7 @@ extern "C" {
 #define FUSED_PROJ_ACT_GELU_TANH 2
 /* max(y, 0)^2: squared ReLU, which the xformers PR "Fused linear: small FW cleanup and much
  * better perfs" discussion names among the activations a fused linear layer handles
- * natively. Both run on the general kernel (128 x 128 tiles) for now. */
+ * natively. */
 #define FUSED_PROJ_ACT_RELU_SQUARED 3
 
 /* Order of the q, k and v columns after the ff slice. */
@@ -104,7 +104,7 @@ extern "C" {
 /* Layout of the ff output. */
 #define FUSED_PROJ_FF_TOKENS_LAST 0   /* ff[bi, s, f] */
 /* ff[bi, f, s]: channels-first like x, the output of the equivalent 1x1x1 convolution (the
- * Walrus PR compares the fused linear with a 1x1x1 Conv3d). Runs on the general kernel. */
+ * Walrus PR compares the fused linear with a 1x1x1 Conv3d). */
 #define FUSED_PROJ_FF_CHANNELS_FIRST 1
 
 typedef struct fused_proj_desc {

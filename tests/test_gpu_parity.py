@@ -164,17 +164,39 @@ def test_fast_kernel_on_padded_or_ragged_tiling(monkeypatch):
     _check(wl, inp, outs, sample_tokens(wl, 384, seed=1), wl.name)
 
 
-def test_other_activations_never_take_the_fast_kernel(monkeypatch):
-    """The fast kernel applies exact-erf GELU or nothing; forcing it with tanh GELU or
-    squared ReLU must still plan the general kernel (and give the oracle's results)."""
-    monkeypatch.setenv("FUSED_PROJ_KERNEL", "fast")
-    for act in ("gelu_tanh", "relu2"):
-        wl = with_shape(WORKLOADS["walrus_bf16"], f"forced_{act}", x_shape=(2, 64, 8, 16, 1), ff_dim=64,
-                        ff_act=act, n_heads=2, head_dim=64, seed=121)
-        inp = make_inputs(wl)
-        proj, outs = run_gpu(wl, inp, DEV)
-        assert "fused_proj_tile_kernel" in proj.describe(), proj.describe()
-        _check(wl, inp, outs, all_tokens(wl), wl.name)
+FAST_VARIANTS = [
+    # tanh GELU and squared ReLU on the fast kernel's small and large tiles
+    # (these epilogues are compiled without RoPE: heads without it)
+    with_shape(WORKLOADS["walrus_bf16"], "fast_gelu_tanh_small", x_shape=(2, 64, 8, 16, 1), ff_dim=64,
+               ff_act="gelu_tanh", n_heads=2, head_dim=64, rope=False, seed=121),
+    with_shape(WORKLOADS["walrus_bf16"], "fast_relu2_small", x_shape=(2, 64, 8, 16, 1), ff_dim=64,
+               ff_act="relu2", n_heads=2, head_dim=64, rope=False, seed=134),
+    with_shape(WORKLOADS["bert_ff_bf16"], "fast_gelu_tanh_large", x_shape=(16, 512, 256), ff_dim=2048,
+               ff_act="gelu_tanh", seed=135),
+    with_shape(WORKLOADS["bert_ff_bf16"], "fast_relu2_large_ragged_m", x_shape=(2, 8150, 256), ff_dim=1536,
+               ff_act="relu2", n_heads=4, head_dim=64, seed=136),
+    # channels-first ff output (ff_dim a multiple of 128, no RoPE) on small tiles with a
+    # ragged token tile and slabs of 120 tokens, and on large tiles with q/k/v heads
+    with_shape(WORKLOADS["walrus_bf16"], "fast_ffcf_small_ragged", x_shape=(3, 128, 10, 12, 1), ff_dim=256,
+               n_heads=2, head_dim=64, rope=False, ff_layout="channels_first", seed=137),
+    with_shape(WORKLOADS["walrus_bf16"], "fast_ffcf_large_heads", x_shape=(16, 256, 32, 32, 1), ff_dim=1024,
+               n_heads=4, head_dim=64, rope=False, ff_layout="channels_first", seed=138),
+    with_shape(WORKLOADS["bert_ff_bf16"], "fast_ffcf_tokens_last_gelu", x_shape=(8, 1000, 128), ff_dim=512,
+               ff_layout="channels_first", seed=139),
+]
+
+
+@pytest.mark.parametrize("wl", FAST_VARIANTS, ids=[w.name for w in FAST_VARIANTS])
+def test_fast_kernel_activation_and_ff_layout_variants(wl):
+    """tanh GELU, squared ReLU and the channels-first ff output on the fast kernel (planned
+    by default), every output element against the oracle; outputs start as NaN."""
+    print(f"[case] fast variant {wl.name} x={wl.x_shape}", flush=True)
+    inp = make_inputs(wl)
+    proj, outs = run_gpu(wl, inp, DEV)
+    desc = proj.describe()
+    print(f"[plan] {desc}", flush=True)
+    assert "fused_proj_fast_kernel" in desc, desc
+    _check(wl, inp, outs, all_tokens(wl), wl.name)
 
 
 RAGGED_M = [
