@@ -200,6 +200,14 @@ struct fused_proj_plan {
     // backward pass
     fused_proj_plan* dx_plan = nullptr;  // dx = dy W^T as a forward projection (null when C == 0)
     fp::BwdArgs bwd{};                   // everything but the per-call pointers
+    bool fast_dy = false;                // dy's ff columns on the fast kernel (grad epilogue)
+    fp::KernelArgs dy_args{};            // its arguments but the per-call pointers
+    fp::TilePlan dy_tile{};
+    unsigned* d_desc_dy = nullptr;       // its column descriptors
+    bool fast_dw = false;                // dW on the fast kernel (else the dW tile kernel)
+    bool dw_x_kmajor = false;            // ... reading x as K-major rows (channels-first x)
+    fp::KernelArgs dw_args{};            // its arguments but the per-call pointers
+    fp::TilePlan dw_tile{};
     size_t ws_dbp = 0, ws_dwp = 0;       // workspace offsets (dy at 0)
     size_t ws_bytes = 0;                 // workspace size
 };
@@ -265,12 +273,123 @@ int plan_backward(fused_proj_plan* h) {
     splits = r.M > 0 ? (r.M + chunk - 1) / chunk : 1;
     b.splits = (int32_t)splits;
     b.chunk = (int32_t)chunk;
+
+    const char* force = std::getenv("FUSED_PROJ_KERNEL");
+    const bool want_general = force && std::strcmp(force, "general") == 0;
+    const bool cf = d.x_layout == FUSED_PROJ_X_CHANNELS_FIRST;
+    const int64_t lim32 = int64_t(1) << 32;
+    // dy's ff columns on the fast kernel (bf16, an activation to differentiate, token-major
+    // d_ff): the forward product over the first ff_dim columns, then dy = d_ff * act'(y)
+    // stored into dy's rows (stride F). The 128-column tiles it covers entirely are then left
+    // out of the dy tile kernel, and their column sums (db) taken from dy afterwards.
+    if (h->dt == fp::DType::BF16 && d.ff_dim > 0 && d.ff_act != FUSED_PROJ_ACT_NONE && r.M > 0 &&
+        d.channels > 0 && d.ff_layout == FUSED_PROJ_FF_TOKENS_LAST && !want_general &&
+        r.x_span * 2 < lim32 && d.channels * r.F * 2 < lim32 && r.M * r.F * 2 < lim32 &&
+        fp::fast_addressable(r.M, r.S, d.ff_dim, 0)) {
+        fp::KernelArgs a = h->base;
+        a.N = (int32_t)d.ff_dim;
+        a.ff_dim = (int32_t)d.ff_dim;
+        a.n_heads = a.head_dim = a.qw = 0;
+        a.n_kv_heads = 0;
+        a.rope = 0;
+        a.rope_cos = a.rope_sin = nullptr;
+        a.ff_channels_first = 0;
+        a.w_ld = (int32_t)r.F;
+        a.ff_ld = (int32_t)r.F;
+        const fp::TilePlan tp = fp::fast_plan(r.M, d.ff_dim, h->num_cus);
+        a.tiles_m = (int32_t)((r.M + tp.bm - 1) / tp.bm);
+        a.tiles_n = (int32_t)((d.ff_dim + tp.bn - 1) / tp.bn);
+        a.group_m = tp.group_m;
+        a.div_group = fp::make_fastdiv_u31((uint32_t)((int64_t)a.group_m * a.tiles_n));
+        const int64_t n = fp::fast_col_desc_entries(d.ff_dim);
+        std::vector<unsigned> hd((size_t)n);
+        fp::fast_col_desc(r.S, d.ff_dim, 0, 0, d.ff_dim, hd.data(), n);
+        hipError_t e = hipMalloc((void**)&h->d_desc_dy, (size_t)n * sizeof(unsigned));
+        if (e == hipSuccess)
+            e = hipMemcpy(h->d_desc_dy, hd.data(), (size_t)n * sizeof(unsigned), hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            g_last_hip = e;
+            return FUSED_PROJ_EHIP;
+        }
+        a.col_desc = h->d_desc_dy;
+        h->dy_args = a;
+        h->dy_tile = tp;
+        h->fast_dy = true;
+        b.dy_col_tile0 = (int32_t)(d.ff_dim / 128);
+    }
+
+    // dW on the fast kernel (bf16): rows are channels, the contraction runs over the tokens,
+    // and the work is split into (256-row tile, token range) units whose fp32 partial sums
+    // the reduction adds up. A channels-first x is read as K-major rows whose K steps (32
+    // tokens) each lie in one slab (S a multiple of 32); a token-major x as M-major rows
+    // with one token stride across slabs.
+    bool fast_dw = h->dt == fp::DType::BF16 && d.channels > 0 && r.M > 0 && !want_general &&
+                   (cf ? r.S % 32 == 0 : (d.batch == 1 || r.sb == r.S * r.ss)) && r.x_span * 2 < lim32 &&
+                   r.M * r.F * 2 < lim32 && d.channels * r.F < (int64_t(1) << 31);
+    if (fast_dw) {
+        const int64_t tiles_t = (d.channels + 255) / 256, tiles_f = (r.F + 255) / 256;
+        const int64_t tiles = tiles_t * tiles_f, cus = h->num_cus;
+        // token ranges: a divisor of the K-step count (equal whole ranges), at most 16, that
+        // minimises the estimated time: rounds of units over the CUs times a unit's MFMA time
+        // (at about 40% of a CU's share of the bf16 peak), plus writing and reading back
+        // each range's fp32 partial sums (at about 4 TB/s)
+        int64_t best = 1;
+        if (r.M % 32 == 0) {
+            const int64_t steps = r.M / 32;
+            const double tile_s = 2.0 * 256 * 256 * (double)r.M / (2.5e15 / (double)cus * 0.4);
+            const double partial_s = (double)d.channels * (double)r.F * 8.0 / 4e12;
+            auto cost = [&](int64_t sp) {
+                return (double)((tiles * sp + cus - 1) / cus) / (double)sp * tile_s + (double)sp * partial_s;
+            };
+            double best_cost = cost(1);
+            for (int64_t sp = 2; sp <= 16; ++sp) {
+                if (steps % sp) continue;
+                if (cost(sp) < best_cost) {
+                    best_cost = cost(sp);
+                    best = sp;
+                }
+            }
+        }
+        fp::KernelArgs& a = h->dw_args;
+        std::memset(&a, 0, sizeof(a));
+        a.M = d.channels;          // rows: channels
+        a.S = (int32_t)d.channels; // one "slab" of rows
+        a.K = (int32_t)(r.M / best);
+        a.N = (int32_t)r.F;
+        a.ff_dim = (int32_t)r.F;
+        if (cf) {                  // K-major rows: channel stride, tokens contiguous, slabs apart
+            a.x_sb = r.sb;
+            a.x_ss = r.sc;
+            a.x_sc = 1;
+            a.k_slab_steps = (int32_t)(r.S / 32);
+            a.div_kslab = fp::make_fastdiv_u31((uint32_t)(r.S / 32));
+        } else {                   // M-major rows: channels contiguous, one token stride
+            a.x_sb = 0;
+            a.x_ss = 1;
+            a.x_sc = r.ss;
+        }
+        a.tiles_m = (int32_t)(tiles_t * best);
+        a.tiles_n = (int32_t)tiles_f;
+        a.group_m = 8;
+        a.div_s = fp::make_fastdiv_u31((uint32_t)d.channels);
+        a.div_group = fp::make_fastdiv_u31((uint32_t)(8 * tiles_f));
+        a.dw_tiles_t = (int32_t)tiles_t;
+        a.div_dwt = fp::make_fastdiv_u31((uint32_t)tiles_t);
+        a.zeros = h->d_zeros;
+        h->dw_tile = fp::TilePlan{256, 256, 32, 8, (int)((cus + 7) / 8 * 8), fp::kFastLarge};
+        h->dw_x_kmajor = cf;
+        h->fast_dw = true;
+        splits = best;
+        b.splits = (int32_t)best;
+        b.chunk = (int32_t)(r.M / best);
+        b.dw_partials = 1;
+    }
     // workspace: dy, then the column sums of dy per token tile (bias), then the dW partials
     size_t off = ws_round((size_t)(r.M * r.F * es));
     h->ws_dbp = off;
     if (d.has_bias) off += ws_round((size_t)b.db_tiles * (size_t)r.F * 4);
     h->ws_dwp = off;
-    if (splits > 1) off += ws_round((size_t)splits * (size_t)d.channels * (size_t)r.F * 4);
+    if (splits > 1 || h->fast_dw) off += ws_round((size_t)splits * (size_t)d.channels * (size_t)r.F * 4);
     h->ws_bytes = r.M > 0 ? off : 0;
     return FUSED_PROJ_OK;
 }
@@ -516,6 +635,7 @@ int fused_proj_run(fused_proj_t h, const void* x, const void* w, const void* bia
 int fused_proj_destroy(fused_proj_t h) {
     if (!h) return FUSED_PROJ_OK;
     const int rc_sub = fused_proj_destroy(h->dx_plan);
+    if (h->d_desc_dy) (void)hipFree(h->d_desc_dy);
     hipError_t e1 = h->d_cos ? hipFree(h->d_cos) : hipSuccess;
     hipError_t e2 = h->d_sin ? hipFree(h->d_sin) : hipSuccess;
     hipError_t e3 = h->d_zeros ? hipFree(h->d_zeros) : hipSuccess;
@@ -618,14 +738,32 @@ int fused_proj_backward(fused_proj_t h, const void* x, const void* w, const void
         char* ws = static_cast<char*>(workspace);
         b.dy = ws;
         b.dbp = d.has_bias ? reinterpret_cast<float*>(ws + h->ws_dbp) : nullptr;
-        b.dwp = b.splits > 1 ? reinterpret_cast<float*>(ws + h->ws_dwp) : nullptr;
+        b.dwp = (b.splits > 1 || h->fast_dw) ? reinterpret_cast<float*>(ws + h->ws_dwp) : nullptr;
         b.dw = dw;
         b.db = d.has_bias ? db : nullptr;
-        e = fp::launch_bwd_dy(h->dt, h->x_tl, h->w_fc, b, s);
+        if (h->fast_dy) {
+            fp::KernelArgs a = h->dy_args;
+            a.x = x;
+            a.w = w;
+            a.bias = d.has_bias ? bias : nullptr;
+            a.ff = b.dy;
+            a.grad_in = d_ff;
+            e = fp::launch_fused_proj_fast(h->x_tl, h->w_fc, 0, 5, h->dy_tile, a, s);
+        }
+        if (e == hipSuccess) e = fp::launch_bwd_dy(h->dt, h->x_tl, h->w_fc, b, s);
+        if (e == hipSuccess && h->fast_dy) e = fp::launch_bwd_colsum(h->dt, b, b.dy_col_tile0 * 128, s);
         if (e == hipSuccess && has_c) {
             const int rc = fused_proj_run(h->dx_plan, b.dy, w, nullptr, dx, nullptr, nullptr, nullptr, stream);
             if (rc) return rc;
-            e = fp::launch_bwd_dw(h->dt, h->x_tl, b, s);
+            if (h->fast_dw) {
+                fp::KernelArgs a = h->dw_args;
+                a.x = x;
+                a.w = b.dy;
+                a.ff = b.dwp;
+                e = fp::launch_fused_proj_fast(h->dw_x_kmajor, false, 0, 4, h->dw_tile, a, s);
+            } else {
+                e = fp::launch_bwd_dw(h->dt, h->x_tl, b, s);
+            }
         }
         if (e == hipSuccess) e = fp::launch_bwd_reduce(h->dt, b, s);
     }

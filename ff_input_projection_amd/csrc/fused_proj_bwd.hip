@@ -86,7 +86,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dy_kernel(BwdArgs b) {
     const KernelArgs& p = b.f;
 
     int tm, tn;
-    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n - b.dy_col_tile0, p.group_m, tm, tn);
+    tn += b.dy_col_tile0;
     const int m0 = tm * BT, n0 = tn * BT;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -468,6 +469,27 @@ __global__ __launch_bounds__(256) void bwd_reduce_db_kernel(BwdArgs b) {
         static_cast<T*>(b.db)[f] = (T)((part[0][fx] + part[1][fx]) + (part[2][fx] + part[3][fx]));
 }
 
+// Column sums of dy (storage type, [M, N]) over 128-token blocks: dbp[block][f] for
+// f < ncols. Workgroup (64 columns, one block): four rows of 64 columns per step, then the
+// four partial sums in LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_colsum_kernel(BwdArgs b, int ncols) {
+    __shared__ float part[4][64];
+    const int N = b.f.N, M = (int)b.f.M;
+    const int fx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int f = blockIdx.x * 64 + fx, r0 = blockIdx.y * BT;
+    const T* dy = static_cast<const T*>(b.dy);
+    float sum = 0.0f;
+    if (f < ncols) {
+        const int rend = r0 + BT < M ? r0 + BT : M;
+#pragma unroll 4
+        for (int r = r0 + ty; r < rend; r += 4) sum += (float)dy[(int64_t)r * N + f];
+    }
+    part[ty][fx] = sum;
+    __syncthreads();
+    if (ty == 0 && f < ncols) b.dbp[(int64_t)blockIdx.y * N + f] = (part[0][fx] + part[1][fx]) + (part[2][fx] + part[3][fx]);
+}
+
 __global__ __launch_bounds__(256) void zero_fill_kernel(unsigned* p, size_t n) {
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
 }
@@ -475,7 +497,8 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(unsigned* p, size_t n) {
 template <typename T, bool A_KM, bool B_KM>
 hipError_t launch_dy_one(const BwdArgs& b, hipStream_t s) {
     constexpr int BK = sizeof(T) == 2 ? 64 : 32;
-    const unsigned grid = (unsigned)b.f.tiles_m * (unsigned)b.f.tiles_n;
+    const unsigned grid = (unsigned)b.f.tiles_m * (unsigned)(b.f.tiles_n - b.dy_col_tile0);
+    if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dy_kernel<T, A_KM, B_KM, BK>), dim3(grid), dim3(kThreads), 0, s, b);
     return hipGetLastError();
 }
@@ -500,7 +523,7 @@ hipError_t launch_dw_layouts(bool x_tl, const BwdArgs& b, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_reduce_t(const BwdArgs& b, hipStream_t s) {
-    if (b.splits > 1 && b.f.K > 0) {
+    if ((b.splits > 1 || b.dw_partials) && b.f.K > 0) {
         const dim3 grid((unsigned)((b.f.K + 63) / 64), (unsigned)((b.f.N + 63) / 64));
         hipLaunchKernelGGL((bwd_reduce_dw_kernel<T>), grid, dim3(256), 0, s, b);
         const hipError_t e = hipGetLastError();
@@ -527,6 +550,16 @@ hipError_t launch_bwd_dw(DType dt, bool x_tl, const BwdArgs& b, hipStream_t s) {
 
 hipError_t launch_bwd_reduce(DType dt, const BwdArgs& b, hipStream_t s) {
     return dt == DType::BF16 ? launch_reduce_t<__bf16>(b, s) : launch_reduce_t<float>(b, s);
+}
+
+hipError_t launch_bwd_colsum(DType dt, const BwdArgs& b, int ncols, hipStream_t s) {
+    if (ncols <= 0 || b.dbp == nullptr) return hipSuccess;
+    const dim3 grid((unsigned)((ncols + 63) / 64), (unsigned)b.db_tiles);
+    if (dt == DType::BF16)
+        hipLaunchKernelGGL((bwd_colsum_kernel<__bf16>), grid, dim3(256), 0, s, b, ncols);
+    else
+        hipLaunchKernelGGL((bwd_colsum_kernel<float>), grid, dim3(256), 0, s, b, ncols);
+    return hipGetLastError();
 }
 
 hipError_t launch_zero_fill(void* p, size_t n, hipStream_t s) {

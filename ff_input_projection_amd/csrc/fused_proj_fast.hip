@@ -150,7 +150,10 @@ struct FastCfg {
 };
 
 // Wave-constant operand state: LDS read bases and the direct-load chunk map.
-template <class C, bool X_TL, bool W_FC, int BK, bool TAILK>
+// KUNITS: the tile's K steps start at step kb of the operands (a range of the contraction,
+// for contractions split over workgroups); SLABK: x's K steps cross slabs (a contraction
+// over the tokens of a channels-first x), each K step lying in one slab.
+template <class C, bool X_TL, bool W_FC, int BK, bool TAILK, bool KUNITS = false, bool SLABK = false>
 struct FastPipe {
     unsigned wbase[C::TI][W_FC ? C::KK : 1];   // LDS read bases of the W^T operands
     unsigned xbase[C::TJ][X_TL ? C::KK : 1];   // and of the x operands
@@ -160,6 +163,9 @@ struct FastPipe {
     const char* wsrc;                          // W and x byte addresses of K step 0
     const char* xsrc;
     int64_t wstep, xstep;                      // bytes per K step
+    int ksps = 1;                              // SLABK: K steps per slab of x
+    FastDivU31 div_ksps{};                     // SLABK: division by ksps
+    int64_t slab_bytes = 0;                    // SLABK: bytes between slabs of x
 
     // Issue the direct loads of K step ks (of the tile whose chunk offsets are voff) into
     // stage ST. Chunks at or past K (a ragged last step, or the steps that pad the step
@@ -167,9 +173,16 @@ struct FastPipe {
     // TAILK every step is whole.
     template <int ST>
     __device__ __forceinline__ void issue(const unsigned (&voff)[C::NLOAD], int ks, int K,
-                                          const char* zeros) const {
-        const char* ws = wsrc + (int64_t)ks * wstep;
-        const char* xs = xsrc + (int64_t)ks * xstep;
+                                          const char* zeros, int kb = 0) const {
+        const int ka = KUNITS ? kb + ks : ks;   // the step in the operands
+        const char* ws = wsrc + (int64_t)ka * wstep;
+        const char* xs;
+        if constexpr (SLABK) {
+            const int sl = (int)fastdiv_u31((uint32_t)ka, div_ksps);
+            xs = xsrc + (int64_t)sl * slab_bytes + (int64_t)(ka - sl * ksps) * xstep;
+        } else {
+            xs = xsrc + (int64_t)ka * xstep;
+        }
         const bool tail = TAILK && (ks + 1) * BK > K;
 #pragma unroll
         for (int q = 0; q < C::NLOAD; ++q) {
@@ -237,7 +250,7 @@ struct FastPipe {
 template <class C, bool X_TL, bool W_FC>
 __device__ __forceinline__ void tile_offsets(unsigned (&voff)[C::NLOAD], int (&kofs)[C::NLOAD], int m0, int n0,
                                              int wave, int lane, int K, int N, int M, int S, FastDivU31 ds,
-                                             int64_t sb, int64_t ss, int64_t sc) {
+                                             int64_t sb, int64_t ss, int64_t sc, int wld) {
 #pragma unroll
     for (int q = 0; q < C::W_INSTR; ++q) {
         const int pch = (wave * C::W_INSTR + q) * 64 + lane;
@@ -253,7 +266,7 @@ __device__ __forceinline__ void tile_offsets(unsigned (&voff)[C::NLOAD], int (&k
             const int c = pc ^ ((row & 3) << 2);
             const int n = n0 + c * 8;
             krow = row;
-            off = (int64_t)krow * N + (n < N ? n : 0);
+            off = (int64_t)krow * wld + (n < N ? n : 0);
         }
         voff[q] = (unsigned)(off * 2);
         kofs[q] = krow;
@@ -345,6 +358,14 @@ static_assert(32 * kCfRow <= kRestageRows * kRestageRow, "channels-first restage
 // Epilogue variants: exact-erf GELU or none with token-major stores; tanh GELU or squared
 // ReLU (no RoPE); a channels-first ff output (no RoPE).
 constexpr int kEpiDefault = 0, kEpiOtherAct = 1, kEpiFfChannelsFirst = 2;
+// The weight gradient's contraction over tokens (dW = X^T dy, rows are channels): tiles are
+// (row tile, token range) units, each storing its fp32 partial sums [range][C][F] straight
+// from the accumulators (no activation, bias, RoPE or restage).
+constexpr int kEpiDwPartial = 4;
+// The backward pass's dy over the ff columns: the forward product y recomputed, then
+// dy = d_ff * act'(y) (d_ff token-major, read 8 bytes per lane and group) stored token-major
+// with row stride ff_ld (no RoPE).
+constexpr int kEpiGrad = 5;
 
 // X_TL: x token-major [b,s,c] (else channels-first). W_FC: W [F,C] (else [C,F]).
 // DG: RoPE partner distance in 8-column groups (hd/16), 0 = no RoPE. TAILK: K is not a
@@ -359,7 +380,8 @@ fused_proj_fast_kernel(KernelArgs p) {
     constexpr int RGN_ALL = T::NWF * T::NWT / 2 * kRestageRows * kRestageRow, W_STAGE = BF * kBK * 2;
     constexpr int PAD = !T::SINGLE && RGN_ALL > W_STAGE ? RGN_ALL - W_STAGE : 0;
     using C = FastCfg<X_TL, W_FC, BF, BT, T::NWF, kNWT, BK, STAGES, PAD>;
-    using Pipe = FastPipe<C, X_TL, W_FC, BK, TAILK>;
+    constexpr bool DW = EPI == kEpiDwPartial;
+    using Pipe = FastPipe<C, X_TL, W_FC, BK, TAILK, DW, DW && X_TL>;
     using Ops = typename Pipe::Ops;
     constexpr int WF = C::WF, WT = C::WT, TI = C::TI, TJ = C::TJ, NG = C::NG, NLOAD = C::NLOAD;
     static_assert(C::KK == 2, "two MFMA k steps per K step");
@@ -412,8 +434,26 @@ fused_proj_fast_kernel(KernelArgs p) {
     }
     pp.wsrc = static_cast<const char*>(p.w);
     pp.xsrc = static_cast<const char*>(p.x);
-    pp.wstep = (W_FC ? (int64_t)BK : (int64_t)BK * N) * 2;
+    // the grad epilogue's product reads the ff columns of a wider [C, F] weight
+    const int wld = EPI == kEpiGrad ? p.w_ld : N;
+    pp.wstep = (W_FC ? (int64_t)BK : (int64_t)BK * wld) * 2;
     pp.xstep = (X_TL ? (int64_t)BK : (int64_t)BK * p.x_sc) * 2;
+    if constexpr (DW && X_TL) {
+        pp.ksps = p.k_slab_steps;
+        pp.div_ksps = p.div_kslab;
+        pp.slab_bytes = p.x_sb * 2;
+    }
+    // a unit of the weight gradient: row tile and token range of "tile row" tt
+    auto unit_of = [&](int t, int& trow, int& kb) __attribute__((always_inline)) {
+        if constexpr (DW) {
+            const int z = (int)fastdiv_u31((uint32_t)t, p.div_dwt);
+            trow = t - z * p.dw_tiles_t;
+            kb = z * (K / BK);   // the token range is K long, a whole number of K steps
+        } else {
+            trow = t;
+            kb = 0;
+        }
+    };
 
     // The bias slice of a tile, copied into bias buffer buf by the first wave's first lanes
     // with the same direct-to-LDS loads as the operands (from the zero block where there
@@ -440,11 +480,14 @@ fused_proj_fast_kernel(KernelArgs p) {
     const float* __restrict__ const rope_cos = p.rope_cos;
     const float* __restrict__ const rope_sin = p.rope_sin;
     const int ff_dim = p.ff_dim, hd = p.head_dim, act = p.act;
+    const int ffr = EPI == kEpiGrad ? p.ff_ld : ff_dim;   // row stride of the ff output
     const int64_t slab_elems = (int64_t)S * p.qw;   // q/k/v elements of one slab (all heads)
 
     unsigned voff_cur[NLOAD], voff_nxt[NLOAD];
-    tile_offsets<C, X_TL, W_FC>(voff_cur, pp.kofs, tt * BT, tf * BF, wave, lane, K, N, M, S, p.div_s, p.x_sb,
-                                p.x_ss, p.x_sc);
+    int trow_cur, kb_cur;
+    unit_of(tt, trow_cur, kb_cur);
+    tile_offsets<C, X_TL, W_FC>(voff_cur, pp.kofs, trow_cur * BT, tf * BF, wave, lane, K, N, M, S, p.div_s, p.x_sb,
+                                p.x_ss, p.x_sc, wld);
     // Wait until this wave's loads of all but the `later` most recently issued K steps have
     // landed (the vector memory counter counts in issue order).
     auto wait_steps = [&](int later) __attribute__((always_inline)) {
@@ -458,24 +501,25 @@ fused_proj_fast_kernel(KernelArgs p) {
     // has landed (the later ones may still be in flight), read its operands. Single-tile
     // workgroups issue only the steps that exist, so that no load is in flight after the
     // last K step (their epilogue reuses the whole stage area).
-    pp.template issue<0>(voff_cur, 0, K, zeros);
+    pp.template issue<0>(voff_cur, 0, K, zeros, kb_cur);
     issue_bias(0, tf * BF);
-    if (!T::SINGLE || 1 < KTp) pp.template issue<1>(voff_cur, 1, K, zeros);
-    if (!T::SINGLE || 2 < KTp) pp.template issue<2>(voff_cur, 2, K, zeros);
-    if constexpr (PF >= 4) if (!T::SINGLE || 3 < KTp) pp.template issue<3>(voff_cur, 3, K, zeros);
-    if constexpr (PF >= 5) if (!T::SINGLE || 4 < KTp) pp.template issue<4>(voff_cur, 4, K, zeros);
+    if (!T::SINGLE || 1 < KTp) pp.template issue<1>(voff_cur, 1, K, zeros, kb_cur);
+    if (!T::SINGLE || 2 < KTp) pp.template issue<2>(voff_cur, 2, K, zeros, kb_cur);
+    if constexpr (PF >= 4) if (!T::SINGLE || 3 < KTp) pp.template issue<3>(voff_cur, 3, K, zeros, kb_cur);
+    if constexpr (PF >= 5) if (!T::SINGLE || 4 < KTp) pp.template issue<4>(voff_cur, 4, K, zeros, kb_cur);
     wait_steps(T::SINGLE ? min(PF - 1, KTp - 1) : PF - 1);
     __syncthreads();
     Ops c0 = pp.template read<0, 0>();
     Ops c1 = pp.template read<0, 1>();
 
     for (int k_tile = 0;; ++k_tile) {
-        const int m0 = tt * BT, n0 = tf * BF;
-        int ntt = 0, ntf = 0;
+        const int m0 = trow_cur * BT, n0 = tf * BF;
+        int ntt = 0, ntf = 0, trow_nxt = 0, kb_nxt = kb_cur;
         const bool has_next = block_tile(k_tile + 1, p, ntt, ntf);
         if (has_next) {
-            tile_offsets<C, X_TL, W_FC>(voff_nxt, pp.kofs, ntt * BT, ntf * BF, wave, lane, K, N, M, S, p.div_s,
-                                        p.x_sb, p.x_ss, p.x_sc);
+            unit_of(ntt, trow_nxt, kb_nxt);
+            tile_offsets<C, X_TL, W_FC>(voff_nxt, pp.kofs, trow_nxt * BT, ntf * BF, wave, lane, K, N, M, S, p.div_s,
+                                        p.x_sb, p.x_ss, p.x_sc, wld);
         } else {
             // past the last tile the loads repeat this tile's first steps (in bounds, never
             // read), which keeps the K loop free of branches
@@ -522,7 +566,7 @@ fused_proj_fast_kernel(KernelArgs p) {
                 // the steps before); those after kt+1 may stay in flight
                 wait_steps(min(kt + PF - 1, KTp - 1) - kt - 1);
                 __syncthreads();
-                if (s_load < KTp) pp.template issue<SL>(voff_cur, s_load, K, zeros);
+                if (s_load < KTp) pp.template issue<SL>(voff_cur, s_load, K, zeros, kb_cur);
             } else {
                 wait_vmcnt<NLOAD>();
                 __syncthreads();
@@ -530,7 +574,7 @@ fused_proj_fast_kernel(KernelArgs p) {
                 unsigned vo[NLOAD];
 #pragma unroll
                 for (int q = 0; q < NLOAD; ++q) vo[q] = ahead ? voff_nxt[q] : voff_cur[q];
-                pp.template issue<SL>(vo, ahead ? s_load - KTp : s_load, K, zeros);
+                pp.template issue<SL>(vo, ahead ? s_load - KTp : s_load, K, zeros, ahead ? kb_nxt : kb_cur);
                 if (s_load == KTp) issue_bias((k_tile + 1) & 1, ntf * BF);
             }
             const Ops n0 = pp.template read<SN, 0>();
@@ -579,6 +623,26 @@ fused_proj_fast_kernel(KernelArgs p) {
         // they should neither evict the operand panels from the XCD's L2 nor sit dirty
         // there for the write-back at the end of the kernel).
         const int tw0 = m0 + wt * WT;   // the wave's first token
+        if constexpr (DW) {
+            // fp32 partial sums of this unit's token range, [range][C][F]: row tw0 + 32j +
+            // lane%32, the lane's 4 columns of each 8-column group, 16 bytes per store
+            const int z = (int)fastdiv_u31((uint32_t)tt, p.div_dwt);
+            float* const out = static_cast<float*>(p.ff) + (int64_t)z * M * N;
+            const int fw = n0 + wf * WF;
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+                const int row = tw0 + 32 * j + (lane & 31);
+                if (row >= M) continue;
+#pragma unroll
+                for (int G = 0; G < NG; ++G) {
+                    const int col = fw + 8 * G + 4 * hl;
+                    if (col >= N) continue;   // N is a multiple of 8
+                    const f32x4 v = {acc[G >> 2][j][4 * (G & 3)], acc[G >> 2][j][4 * (G & 3) + 1],
+                                     acc[G >> 2][j][4 * (G & 3) + 2], acc[G >> 2][j][4 * (G & 3) + 3]};
+                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out + (int64_t)row * N + col));
+                }
+            }
+        } else {
         // The wave's 16 column groups: kind (0 ff, 1 q, 2 k, 3 v) in bits 30-31 and the
         // element offset of the group's first column in the low bits (ff: column; q/k/v:
         // head * S * hd + place in head), all sixteen in one scalar load.
@@ -630,7 +694,7 @@ fused_proj_fast_kernel(KernelArgs p) {
         const unsigned kind_l = dl >> 30;
         char* const base_l = static_cast<char*>(kind_l == 0 ? p.ff : kind_l == 1 ? p.q : kind_l == 2 ? p.k : p.v) +
                              (size_t)(dl & 0x3fffffffu) * 2;
-        const unsigned stride_l = kind_l == 0 ? (unsigned)(2 * ff_dim) : (unsigned)(2 * hd);
+        const unsigned stride_l = kind_l == 0 ? (unsigned)(2 * ffr) : (unsigned)(2 * hd);
         char* const row0_l = base_l + r0 * stride_l;
         const bool col_ok = fw + 8 * gl < N;
         // the wave's tokens usually lie in one slab: then a token's offset is linear in it
@@ -640,7 +704,7 @@ fused_proj_fast_kernel(KernelArgs p) {
         auto token_off = [&](int t) __attribute__((always_inline)) {
             const int bi = (int)fastdiv_u31((uint32_t)t, p.div_s);
             const int s = t - bi * S;
-            return kind_l == 0 ? (unsigned)t * (unsigned)(2 * ff_dim)
+            return kind_l == 0 ? (unsigned)t * (unsigned)(2 * ffr)
                                : (unsigned)(((int64_t)bi * slab_elems + (int64_t)s * hd) * 2);
         };
 
@@ -687,6 +751,23 @@ fused_proj_fast_kernel(KernelArgs p) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) y[u] = acc[G >> 2][j][4 * (G & 3) + u];
                 if (kind == 0) {
+                    if constexpr (EPI == kEpiGrad) {
+                        // dy = d_ff * act'(y) for this lane's token and 4 columns
+                        const int tg = tw0 + 32 * j + (lane_e & 31);
+                        const u32x2 gv = *reinterpret_cast<const u32x2*>(
+                            static_cast<const __bf16*>(p.grad_in) + (int64_t)(tg < M ? tg : 0) * ff_dim + fw +
+                            8 * G + 4 * hl);
+                        const bf16x4 g4 = __builtin_bit_cast(bf16x4, gv);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const float d = act == 1 ? gelu_erf_grad(y[u])
+                                            : act == 2 ? gelu_tanh_grad(y[u])
+                                            : act == 3 ? relu_squared_grad(y[u]) : 1.0f;
+                            y[u] = (float)g4[u] * d;
+                        }
+                        pk[G] = pack4_bf16(y);
+                        continue;
+                    }
                     if constexpr (EPI == kEpiOtherAct) {
                         if (act == 2) {
 #pragma unroll
@@ -768,7 +849,7 @@ fused_proj_fast_kernel(KernelArgs p) {
                 const int t0 = tw0 + 32 * j + 16 * h;   // the half block's first token
                 const int rows = M - t0;                 // its rows that exist
                 // in one slab: row r of this lane's chunk at row0_l + u + (r - r0) * stride_l
-                const unsigned u = kind_l == 0 ? (unsigned)t0 * (unsigned)(2 * ff_dim)
+                const unsigned u = kind_l == 0 ? (unsigned)t0 * (unsigned)(2 * ffr)
                                                : (unsigned)(((int64_t)bi_first * slab_elems +
                                                              (int64_t)(t0 - bi_first * S) * hd) * 2);
 #pragma unroll
@@ -784,11 +865,14 @@ fused_proj_fast_kernel(KernelArgs p) {
                 }
             }
         }
+        }
         if (!has_next) break;
 #pragma unroll
         for (int q = 0; q < NLOAD; ++q) voff_cur[q] = voff_nxt[q];
         tt = ntt;
         tf = ntf;
+        trow_cur = trow_nxt;
+        kb_cur = kb_nxt;
     }
     wait_vmcnt<0>();   // the trailing loads into LDS
 }
@@ -814,6 +898,15 @@ hipError_t dispatch_fast_layouts(bool x_tl, bool w_fc, const KernelArgs& a, int 
 
 template <class T>
 hipError_t dispatch_fast_rope(int dg, int epi, bool x_tl, bool w_fc, const KernelArgs& a, int grid, hipStream_t s) {
+    if (epi == kEpiGrad) {
+        if (dg != 0) return hipErrorInvalidValue;
+        return dispatch_fast_layouts<0, T, kEpiGrad>(x_tl, w_fc, a, grid, s);
+    }
+    if (epi == kEpiDwPartial) {
+        if (dg != 0 || w_fc) return hipErrorInvalidValue;
+        return x_tl ? launch_fast_one<true, false, 0, T, kEpiDwPartial>(a, grid, s)
+                    : launch_fast_one<false, false, 0, T, kEpiDwPartial>(a, grid, s);
+    }
     if (epi != kEpiDefault) {
         // the other epilogues are compiled without RoPE only
         if (dg != 0) return hipErrorInvalidValue;

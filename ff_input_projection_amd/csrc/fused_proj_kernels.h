@@ -65,6 +65,18 @@ struct KernelArgs {
     // Fast kernel only: division by S (token -> slab) and by group_m * tiles_n (tile order).
     FastDivU31 div_s;
     FastDivU31 div_group;
+    // Fast kernel, weight-gradient units only: row tiles per token range (tile rows count
+    // (row tile, range) units), division by it, and for a channels-first x the K steps per
+    // slab and division by them.
+    int32_t dw_tiles_t;
+    FastDivU31 div_dwt;
+    int32_t k_slab_steps;
+    FastDivU31 div_kslab;
+    // Fast kernel, backward dy only: row stride of a [C, F] weight whose first N columns are
+    // read, row stride of the ff output, and the upstream gradient of ff ([M, ff_dim]).
+    int32_t w_ld;
+    int32_t ff_ld;
+    const void* grad_in;
 };
 
 // Tile plan chosen on the host.
@@ -107,7 +119,10 @@ void fast_col_desc(int64_t S, int64_t ff_dim, int64_t n_heads, int64_t head_dim,
                    int64_t entries);
 int64_t fast_col_desc_entries(int64_t F);
 // epi: 0 exact-erf GELU or no activation, token-major ff; 1 tanh GELU or squared ReLU;
-// 2 channels-first ff (1 and 2 without RoPE, dg == 0).
+// 2 channels-first ff (1 and 2 without RoPE, dg == 0); 5 the backward pass's dy over the ff
+// columns (dg == 0); 4 the weight gradient's fp32
+// partial sums over token ranges (dg == 0, W read as [K, N]; x_tokens_last selects K-major
+// rows with K steps crossing slabs).
 hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, int epi, const TilePlan& plan,
                                   const KernelArgs& args, hipStream_t stream);
 
@@ -133,6 +148,8 @@ struct BwdArgs {
     int32_t dw_tiles_m;  // 128 x 128 tiles over [C, F]
     int32_t dw_tiles_n;
     int32_t db_tiles;    // rows of dbp
+    int32_t dw_partials; // dW always goes through dwp (the fast kernel's fp32 partial sums)
+    int32_t dy_col_tile0;// the dy kernel's first 128-column tile (the fast kernel did the ones before)
 };
 
 // K step of the 128 x 128 tile kernels for a storage type.
@@ -141,6 +158,8 @@ int tile_bk(DType dt);
 hipError_t launch_bwd_dy(DType dt, bool x_tokens_last, bool w_fc, const BwdArgs& b, hipStream_t stream);
 // The dW kernel: grid (dw_tiles_m x dw_tiles_n, splits).
 hipError_t launch_bwd_dw(DType dt, bool x_tokens_last, const BwdArgs& b, hipStream_t stream);
+// Column sums of dy's first ncols columns per 128-token block into dbp.
+hipError_t launch_bwd_colsum(DType dt, const BwdArgs& b, int ncols, hipStream_t stream);
 // Sums the dW partials (splits > 1) into dW and the dy column sums into db (when db).
 hipError_t launch_bwd_reduce(DType dt, const BwdArgs& b, hipStream_t stream);
 // Writes zeros to n bytes at p (n a multiple of 4; a kernel, not a memset node).
