@@ -60,6 +60,24 @@ __device__ __forceinline__ float gelu_erf_poly(float y) {
     return fmaf(-a, __builtin_amdgcn_exp2f(p), __builtin_amdgcn_fmed3f(y, 0.0f, 3.40282347e+38f));
 }
 
+// Its derivative with the same Phi(-a) = 2^P(a): d/dy [y Phi(y)] = Phi(y) + y phi(y), with
+// Phi(y) = 1 - Phi(-|y|) for y >= 0 and Phi(-|y|) otherwise, phi(y) = e^(-y^2/2) / sqrt(2 pi).
+// Absolute error under 3e-5 in fp32 (pinned on the CPU with the same coefficients).
+__device__ __forceinline__ float gelu_erf_grad_poly(float y) {
+    const float a = __builtin_amdgcn_fmed3f(fabsf(y), 0.0f, 6.0f);
+    float p = 2.2990056e-05f;
+    p = fmaf(p, a, -0.00061110023f);
+    p = fmaf(p, a, 0.0071955691f);
+    p = fmaf(p, a, -0.051185358f);
+    p = fmaf(p, a, -0.46127188f);
+    p = fmaf(p, a, -1.1501743f);
+    p = fmaf(p, a, -1.0000647f);
+    const float q = __builtin_amdgcn_exp2f(p);
+    const float cdf = y >= 0.0f ? 1.0f - q : q;
+    const float pdf = 0.39894228040143267794f * __builtin_amdgcn_exp2f(-0.72134752044448170368f * (y * y));
+    return fmaf(y, pdf, cdf);
+}
+
 // tanh form of GELU (Hendrycks and Gimpel, "Gaussian Error Linear Units (GELUs)",
 // 2016): 0.5 y (1 + tanh(u)), u = sqrt(2/pi) (y + 0.044715 y^3). Since
 // 0.5 (1 + tanh u) = 1 / (1 + e^(-2u)), it is y / (1 + 2^(-2u log2 e)): one exp2 and

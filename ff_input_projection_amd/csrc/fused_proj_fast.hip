@@ -760,7 +760,7 @@ fused_proj_fast_kernel(KernelArgs p) {
                         const bf16x4 g4 = __builtin_bit_cast(bf16x4, gv);
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
-                            const float d = act == 1 ? gelu_erf_grad(y[u])
+                            const float d = act == 1 ? gelu_erf_grad_poly(y[u])
                                             : act == 2 ? gelu_tanh_grad(y[u])
                                             : act == 3 ? relu_squared_grad(y[u]) : 1.0f;
                             y[u] = (float)g4[u] * d;
