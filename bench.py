@@ -51,6 +51,10 @@ CSRC = os.path.join(ROOT, "ff_input_projection_amd", "csrc")
 CONFIG_WORKLOADS = ["tiny_f32", "walrus_bf16", "bert_ff_bf16", "bert_qkv_bf16", "decoder_qkv_rope_bf16",
                     "smallk_qkv_bf16"]
 ONE_CORE_WORKLOADS = ["tiny_f32", "smallk_qkv_bf16"]
+# the variants beside the table: grouped-query heads with 8-column RoPE, the 1x1x1
+# convolution's channels-first output, squared ReLU, and the Walrus width 1408 (timed and
+# checked the same way, reported under "variants")
+VARIANT_WORKLOADS = ["gqa_rope8_bf16", "conv1x1_walrus_bf16", "bert_ff_relu2_bf16", "walrus_c1408_bf16"]
 # The Walrus PR's own measurements (L40S, before its fix), restated: the figures this
 # op exists to remove. Context only, not a target.
 CONTEXT = {
@@ -472,11 +476,11 @@ def main() -> int:
     # the oracle checks follow on the CPU)
     measured = {wl.name: (t, desc, host, inp)}
     if not args.no_configs:
-        for name in CONFIG_WORKLOADS:
+        for name in CONFIG_WORKLOADS + VARIANT_WORKLOADS:
             if name in measured:
                 continue
             cw = WORKLOADS[name]
-            steps = args.config_steps * (5 if name == "smallk_qkv_bf16" else 1)
+            steps = args.config_steps * (5 if name in ("smallk_qkv_bf16", "gqa_rope8_bf16") else 1)
             ct, cdesc, chost, cinp, _ = measure_workload(cw, dev, steps, 10, min(args.min_warmup_s, 1.0))
             measured[name] = (ct, cdesc, chost, cinp)
             print(f"[bench] {name}: mean {ct['mean_us']:.2f} us, median {ct['median_us']:.2f} "
@@ -526,8 +530,8 @@ def main() -> int:
                              "tokens": cw.M, "cores": 1})
         result["cpu_1core"] = one_core
 
-    configs = []
-    for name in (CONFIG_WORKLOADS if not args.no_configs else [wl.name]):
+    configs, variants = [], []
+    for name in (CONFIG_WORKLOADS + VARIANT_WORKLOADS if not args.no_configs else [wl.name]):
         if name not in measured:
             continue
         ct, cdesc, chost, cinp = measured[name]
@@ -549,8 +553,10 @@ def main() -> int:
                 entry["oracle_s"] = round(s_, 2)
                 del ref
             print(f"[bench] parity {name}: {entry['parity']}", file=sys.stderr, flush=True)
-        configs.append(entry)
+        (variants if name in VARIANT_WORKLOADS else configs).append(entry)
     result["configs"] = configs
+    if variants:
+        result["variants"] = variants
 
     print(json.dumps(result), flush=True)
     return 0

@@ -303,7 +303,7 @@ int plan_backward(fused_proj_plan* h) {
         a.div_group = fp::make_fastdiv_u31((uint32_t)((int64_t)a.group_m * a.tiles_n));
         const int64_t n = fp::fast_col_desc_entries(d.ff_dim);
         std::vector<unsigned> hd((size_t)n);
-        fp::fast_col_desc(r.S, d.ff_dim, 0, 0, d.ff_dim, hd.data(), n);
+        fp::fast_col_desc(r.S, d.ff_dim, 0, 0, 0, false, false, d.ff_dim, hd.data(), n);
         hipError_t e = hipMalloc((void**)&h->d_desc_dy, (size_t)n * sizeof(unsigned));
         if (e == hipSuccess)
             e = hipMemcpy(h->d_desc_dy, hd.data(), (size_t)n * sizeof(unsigned), hipMemcpyHostToDevice);
@@ -430,15 +430,19 @@ int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backwa
         delete h;
         return FUSED_PROJ_EHIP;
     }
-    // Kernel choice. The fast bf16 kernel needs a RoPE head size of 32, 64 or 128 (or no
-    // RoPE) and x and W spans under 4 GiB (it addresses them with 32-bit offsets). Every
-    // other shape goes to the general kernel.
+    // Kernel choice. The fast bf16 kernel needs RoPE over a whole head of 32, 64 or 128
+    // columns or over the first 8 columns of each head (or no RoPE), and x and W spans under
+    // 4 GiB (it addresses them with 32-bit offsets). Every other shape goes to the general
+    // kernel.
     // FUSED_PROJ_KERNEL=general forces the general kernel (the tests use it to cover both);
     // FUSED_PROJ_KERNEL=fast takes the fast kernel on any shape it can address.
     const char* force = std::getenv("FUSED_PROJ_KERNEL");
     const bool want_general = force && std::strcmp(force, "general") == 0;
     const bool want_fast = force && std::strcmp(force, "fast") == 0;
-    const int dg = fp::fast_rope_groups((int)desc->head_dim, desc->rope && r.qw > 0);
+    const bool roped = desc->rope && r.qw > 0;
+    // RoPE on 8 columns of each head: rotated within one 8-column group (a separate epilogue)
+    const bool rope8 = roped && r.rd == 8;
+    const int dg = rope8 ? 0 : r.rd == desc->head_dim ? fp::fast_rope_groups((int)desc->head_dim, roped) : -1;
     const bool fits32 = r.x_span * 2 < (int64_t(1) << 32) && desc->channels * r.F * 2 < (int64_t(1) << 32);
     const fp::TilePlan fp_plan = fp::fast_plan(r.M, r.F, num_cus);
     // Both tile shapes take any token, column and channel count: tokens past M read token
@@ -448,22 +452,22 @@ int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backwa
     // loop to a multiple of its four stages) read the zero block. Measured against the
     // general kernel on such shapes (C 320, 72, 200 on large tiles): faster or equal.
     const bool exact = desc->channels > 0;
-    const bool addressable = fp::fast_addressable(r.M, r.S, desc->ff_dim, r.qw);
-    // the fast kernel's epilogue applies every ff activation; it needs the plain multi-head
-    // layout (as many k/v heads as q heads, contiguous order, the full head rotated), and a
-    // channels-first ff output only when ff_dim is a multiple of a wave's 128 columns
-    const bool fast_heads = r.kvh == desc->n_heads && desc->qkv_order == FUSED_PROJ_QKV_CONTIGUOUS &&
-                            (!desc->rope || r.rd == desc->head_dim);
-    // its epilogue variant: tanh GELU and squared ReLU, and a channels-first ff output (when
-    // ff_dim is a multiple of the wave's 128 columns, with exact GELU or no activation), are
-    // compiled without RoPE
+    // (the 8-column RoPE's descriptors keep bit 29 for the rotated groups)
+    const bool addressable = fp::fast_addressable(r.M, r.S, desc->ff_dim, r.qw) &&
+                             (!rope8 || r.S * r.qw < (int64_t(1) << 29));
+    // The fast kernel's epilogue takes any q/k/v layout (fewer k/v heads, grouped columns:
+    // both are in its column descriptors) and applies every ff activation. Its variants:
+    // tanh GELU and squared ReLU, and a channels-first ff output (when ff_dim is a multiple
+    // of the wave's 128 columns, with exact GELU or no activation), are compiled without
+    // RoPE; the 8-column RoPE with exact GELU or no activation and a token-major ff.
     const bool ff_cf = desc->ff_dim > 0 && desc->ff_layout == FUSED_PROJ_FF_CHANNELS_FIRST;
     const bool other_act = desc->ff_dim > 0 && (desc->ff_act == FUSED_PROJ_ACT_GELU_TANH ||
                                                 desc->ff_act == FUSED_PROJ_ACT_RELU_SQUARED);
-    h->epi = ff_cf ? 2 : other_act ? 1 : 0;
-    const bool fast_epi = h->epi == 0 || (dg == 0 && (h->epi == 1 || (!other_act && desc->ff_dim % 128 == 0)));
-    h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && addressable && fast_heads && fast_epi &&
-              (exact || want_fast) && !want_general;
+    h->epi = ff_cf ? 2 : other_act ? 1 : rope8 ? 3 : 0;
+    const bool fast_epi = h->epi == 0 || h->epi == 3 ||
+                          (!roped && (h->epi == 1 || (!other_act && desc->ff_dim % 128 == 0)));
+    h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && addressable && fast_epi && (exact || want_fast) &&
+              !want_general;
     h->dg = dg < 0 ? 0 : dg;
     h->tile = h->fast ? fp_plan : fp::TilePlan{128, 128, h->dt == fp::DType::BF16 ? 64 : 32, 8, 0};
 
@@ -537,7 +541,8 @@ int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backwa
     if (h->fast) {
         const int64_t n = fp::fast_col_desc_entries(r.F);
         std::vector<unsigned> hd((size_t)n);
-        fp::fast_col_desc(r.S, desc->ff_dim, desc->n_heads, desc->head_dim, r.F, hd.data(), n);
+        fp::fast_col_desc(r.S, desc->ff_dim, desc->n_heads, r.kvh, desc->head_dim,
+                          desc->qkv_order == FUSED_PROJ_QKV_GROUPED, h->epi == 3, r.F, hd.data(), n);
         e = hipMalloc((void**)&h->d_desc, (size_t)n * sizeof(unsigned));
         if (e == hipSuccess) e = hipMemcpy(h->d_desc, hd.data(), (size_t)n * sizeof(unsigned), hipMemcpyHostToDevice);
         if (e != hipSuccess) {

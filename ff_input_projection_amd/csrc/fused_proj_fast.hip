@@ -358,6 +358,10 @@ static_assert(32 * kCfRow <= kRestageRows * kRestageRow, "channels-first restage
 // Epilogue variants: exact-erf GELU or none with token-major stores; tanh GELU or squared
 // ReLU (no RoPE); a channels-first ff output (no RoPE).
 constexpr int kEpiDefault = 0, kEpiOtherAct = 1, kEpiFfChannelsFirst = 2;
+// As the default, with RoPE on the first 8 columns of each q/k head only (partial rotary):
+// a rotated group's pairs lie 4 columns apart, in the two half-waves, and the descriptor's
+// bit 29 marks the group.
+constexpr int kEpiRope8 = 3;
 // The weight gradient's contraction over tokens (dW = X^T dy, rows are channels): tiles are
 // (row tile, token range) units, each storing its fp32 partial sums [range][C][F] straight
 // from the accumulators (no activation, bias, RoPE or restage).
@@ -481,7 +485,9 @@ fused_proj_fast_kernel(KernelArgs p) {
     const float* __restrict__ const rope_sin = p.rope_sin;
     const int ff_dim = p.ff_dim, hd = p.head_dim, act = p.act;
     const int ffr = EPI == kEpiGrad ? p.ff_ld : ff_dim;   // row stride of the ff output
-    const int64_t slab_elems = (int64_t)S * p.qw;   // q/k/v elements of one slab (all heads)
+    // q/k/v elements of one slab (all heads of the slice): q, and k or v
+    const int64_t slab_q = (int64_t)S * p.qw, slab_kv = (int64_t)S * p.n_kv_heads * hd;
+    constexpr bool R8 = EPI == kEpiRope8;
 
     unsigned voff_cur[NLOAD], voff_nxt[NLOAD];
     int trow_cur, kb_cur;
@@ -645,12 +651,18 @@ fused_proj_fast_kernel(KernelArgs p) {
         } else {
         // The wave's 16 column groups: kind (0 ff, 1 q, 2 k, 3 v) in bits 30-31 and the
         // element offset of the group's first column in the low bits (ff: column; q/k/v:
-        // head * S * hd + place in head), all sixteen in one scalar load.
+        // head * S * hd + place in head; bit 29 marks the rotated groups of the 8-column
+        // RoPE), all sixteen in one scalar load.
         const int fw = n0 + wf * WF;
         const u32x16 desc = scalar_load16(p.col_desc + (unsigned)fw / 8u);
-        // whether the wave's columns meet the q or k slice (then RoPE applies)
-        const bool wave_rope = DG > 0 && fw < ff_dim + 2 * p.qw && fw + WF > ff_dim;
-        constexpr int HD = DG > 0 ? 16 * DG : 16, HALF = HD / 2, NR = HALF / 8, NRB = NR > 4 ? 4 : NR;
+        constexpr unsigned OFS_MASK = R8 ? 0x1fffffffu : 0x3fffffffu;
+        // whether the wave's columns meet the q or k slice (then RoPE applies): contiguous
+        // q, k, v columns end the rotated ones before v; grouped ones interleave v
+        const int rope_end = p.qkv_grouped ? N : ff_dim + p.qw + p.n_kv_heads * hd;
+        const bool wave_rope = (DG > 0 || R8) && fw < rope_end && fw + WF > ff_dim;
+        // cos/sin registers: the 4 columns of each first-half group of a head this lane
+        // rotates (8-column RoPE: the 4 pairs of the rotated group)
+        constexpr int HD = DG > 0 ? 16 * DG : 16, HALF = HD / 2, NR = R8 ? 1 : HALF / 8, NRB = NR > 4 ? 4 : NR;
 
         // The stores: written straight from the accumulator layout, a store instruction
         // touches 32 token rows with 16 bytes each; restaged, each one writes 4 token rows of
@@ -693,7 +705,8 @@ fused_proj_fast_kernel(KernelArgs p) {
         for (int g = 1; g < 16; ++g) dl = gl == g ? desc[g] : dl;
         const unsigned kind_l = dl >> 30;
         char* const base_l = static_cast<char*>(kind_l == 0 ? p.ff : kind_l == 1 ? p.q : kind_l == 2 ? p.k : p.v) +
-                             (size_t)(dl & 0x3fffffffu) * 2;
+                             (size_t)(dl & OFS_MASK) * 2;
+        const int64_t slab_l = kind_l == 1 ? slab_q : slab_kv;
         const unsigned stride_l = kind_l == 0 ? (unsigned)(2 * ffr) : (unsigned)(2 * hd);
         char* const row0_l = base_l + r0 * stride_l;
         const bool col_ok = fw + 8 * gl < N;
@@ -705,7 +718,7 @@ fused_proj_fast_kernel(KernelArgs p) {
             const int bi = (int)fastdiv_u31((uint32_t)t, p.div_s);
             const int s = t - bi * S;
             return kind_l == 0 ? (unsigned)t * (unsigned)(2 * ffr)
-                               : (unsigned)(((int64_t)bi * slab_elems + (int64_t)s * hd) * 2);
+                               : (unsigned)(((int64_t)bi * slab_l + (int64_t)s * hd) * 2);
         };
 
         // cos/sin of this lane's token at its 4 columns of each first-half group of a head;
@@ -718,7 +731,9 @@ fused_proj_fast_kernel(KernelArgs p) {
             const int t = tw0 + 32 * j + (lane_e & 31);
             const int tc = t < M ? t : 0;
             const int s = tc - (int)fastdiv_u31((uint32_t)tc, p.div_s) * S;
-            const unsigned rp_off = (unsigned)((s * (DG * 8) + 4 * (lane_e >> 5)) * 4);
+            // the table holds rd/2 values per token: a lane's 4 start at 4 * (lane / 32) of
+            // each group of 8 (8-column RoPE: both half-waves read the token's 4)
+            const unsigned rp_off = R8 ? (unsigned)(s * 16) : (unsigned)((s * (DG * 8) + 4 * (lane_e >> 5)) * 4);
 #pragma unroll
             for (int r = 0; r < NRB; ++r) {
                 rc[r] = f32x4{};
@@ -731,6 +746,12 @@ fused_proj_fast_kernel(KernelArgs p) {
                     const char* const sn = reinterpret_cast<const char*>(rope_sin + 8 * (r0 + r)) + rp_off;
                     rc[r] = *reinterpret_cast<const f32x4*>(c);
                     rsn[r] = *reinterpret_cast<const f32x4*>(sn);
+                }
+                if constexpr (R8) {
+                    // the first half of a pair takes -sin times its partner, the second +sin
+                    const float sg = (lane_e >> 5) ? 1.0f : -1.0f;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) rsn[0][u] *= sg;
                 }
             }
         };
@@ -782,6 +803,20 @@ fused_proj_fast_kernel(KernelArgs p) {
                     }
                     pk[G] = pack4_bf16(y);
                     continue;
+                }
+                if constexpr (R8) {
+                    if (desc[G] & (1u << 29)) {
+                        // the first 8 columns of a q/k head: columns c and c + 4 form pair c,
+                        // held for the same token by this lane and the one 32 lanes away
+                        float o[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const float partner = __shfl_xor(y[u], 32);
+                            o[u] = y[u] * rc[0][u] + partner * rsn[0][u];
+                        }
+                        pk[G] = pack4_bf16(o);
+                        continue;
+                    }
                 }
                 if (DG > 0 && kind != 3) {
                     // Heads start on head_dim boundaries of the wave's columns, so the
@@ -850,7 +885,7 @@ fused_proj_fast_kernel(KernelArgs p) {
                 const int rows = M - t0;                 // its rows that exist
                 // in one slab: row r of this lane's chunk at row0_l + u + (r - r0) * stride_l
                 const unsigned u = kind_l == 0 ? (unsigned)t0 * (unsigned)(2 * ffr)
-                                               : (unsigned)(((int64_t)bi_first * slab_elems +
+                                               : (unsigned)(((int64_t)bi_first * slab_l +
                                                              (int64_t)(t0 - bi_first * S) * hd) * 2);
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
@@ -896,34 +931,91 @@ hipError_t dispatch_fast_layouts(bool x_tl, bool w_fc, const KernelArgs& a, int 
                 : launch_fast_one<false, false, DG, T, EPI>(a, grid, s);
 }
 
-template <class T>
-hipError_t dispatch_fast_rope(int dg, int epi, bool x_tl, bool w_fc, const KernelArgs& a, int grid, hipStream_t s) {
-    if (epi == kEpiGrad) {
-        if (dg != 0) return hipErrorInvalidValue;
-        return dispatch_fast_layouts<0, T, kEpiGrad>(x_tl, w_fc, a, grid, s);
+// The kernel's instantiations are spread over five translation units of this file: the
+// build compiles it once per FP_FAST_PART value (0-4, in parallel); without FP_FAST_PART one
+// unit holds them all. Part 0 also holds the host functions below.
+//   0: default epilogue, no RoPE or partner distance 2     1: default, distances 4 and 8
+//   2: tanh GELU / squared ReLU, channels-first ff         3: 8-column RoPE, backward dy
+//   4: weight-gradient partial sums
+#ifdef FP_FAST_PART
+#define FP_PART(k) (FP_FAST_PART == (k))
+#else
+#define FP_PART(k) 1
+#endif
+
+constexpr int fast_part_of(int epi, int dg) {
+    return epi == kEpiDefault ? (dg <= 2 ? 0 : 1)
+           : (epi == kEpiOtherAct || epi == kEpiFfChannelsFirst) ? 2
+           : epi == kEpiDwPartial ? 4 : 3;
+}
+
+// The variants one part compiles, for tile shape T: an unsupported combination is an error.
+template <int P, class T>
+hipError_t dispatch_part(int dg, int epi, bool x_tl, bool w_fc, const KernelArgs& a, int grid, hipStream_t s) {
+    if constexpr (P == 0) {
+        if (epi == kEpiDefault && dg == 0) return dispatch_fast_layouts<0, T, kEpiDefault>(x_tl, w_fc, a, grid, s);
+        if (epi == kEpiDefault && dg == 2) return dispatch_fast_layouts<2, T, kEpiDefault>(x_tl, w_fc, a, grid, s);
+    } else if constexpr (P == 1) {
+        if (epi == kEpiDefault && dg == 4) return dispatch_fast_layouts<4, T, kEpiDefault>(x_tl, w_fc, a, grid, s);
+        if (epi == kEpiDefault && dg == 8) return dispatch_fast_layouts<8, T, kEpiDefault>(x_tl, w_fc, a, grid, s);
+    } else if constexpr (P == 2) {
+        // compiled without RoPE only
+        if (dg == 0 && epi == kEpiOtherAct) return dispatch_fast_layouts<0, T, kEpiOtherAct>(x_tl, w_fc, a, grid, s);
+        if (dg == 0 && epi == kEpiFfChannelsFirst)
+            return dispatch_fast_layouts<0, T, kEpiFfChannelsFirst>(x_tl, w_fc, a, grid, s);
+    } else if constexpr (P == 3) {
+        // the 8-column RoPE is marked in the descriptors; dy has no RoPE
+        if (dg == 0 && epi == kEpiRope8) return dispatch_fast_layouts<0, T, kEpiRope8>(x_tl, w_fc, a, grid, s);
+        if (dg == 0 && epi == kEpiGrad) return dispatch_fast_layouts<0, T, kEpiGrad>(x_tl, w_fc, a, grid, s);
+    } else {
+        if (dg == 0 && epi == kEpiDwPartial && !w_fc)
+            return x_tl ? launch_fast_one<true, false, 0, T, kEpiDwPartial>(a, grid, s)
+                        : launch_fast_one<false, false, 0, T, kEpiDwPartial>(a, grid, s);
     }
-    if (epi == kEpiDwPartial) {
-        if (dg != 0 || w_fc) return hipErrorInvalidValue;
-        return x_tl ? launch_fast_one<true, false, 0, T, kEpiDwPartial>(a, grid, s)
-                    : launch_fast_one<false, false, 0, T, kEpiDwPartial>(a, grid, s);
-    }
-    if (epi != kEpiDefault) {
-        // the other epilogues are compiled without RoPE only
-        if (dg != 0) return hipErrorInvalidValue;
-        if (epi == kEpiOtherAct) return dispatch_fast_layouts<0, T, kEpiOtherAct>(x_tl, w_fc, a, grid, s);
-        if (epi == kEpiFfChannelsFirst) return dispatch_fast_layouts<0, T, kEpiFfChannelsFirst>(x_tl, w_fc, a, grid, s);
-        return hipErrorInvalidValue;
-    }
-    switch (dg) {
-        case 0: return dispatch_fast_layouts<0, T, kEpiDefault>(x_tl, w_fc, a, grid, s);
-        case 2: return dispatch_fast_layouts<2, T, kEpiDefault>(x_tl, w_fc, a, grid, s);
-        case 4: return dispatch_fast_layouts<4, T, kEpiDefault>(x_tl, w_fc, a, grid, s);
-        case 8: return dispatch_fast_layouts<8, T, kEpiDefault>(x_tl, w_fc, a, grid, s);
-        default: return hipErrorInvalidValue;
-    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
+
+// One launcher per part, each defined in its own part and declared in every one.
+template <int P>
+hipError_t fast_launch_part(bool large, int dg, int epi, bool x_tl, bool w_fc, const KernelArgs& a, int grid,
+                            hipStream_t s);
+template <>
+hipError_t fast_launch_part<0>(bool, int, int, bool, bool, const KernelArgs&, int, hipStream_t);
+template <>
+hipError_t fast_launch_part<1>(bool, int, int, bool, bool, const KernelArgs&, int, hipStream_t);
+template <>
+hipError_t fast_launch_part<2>(bool, int, int, bool, bool, const KernelArgs&, int, hipStream_t);
+template <>
+hipError_t fast_launch_part<3>(bool, int, int, bool, bool, const KernelArgs&, int, hipStream_t);
+template <>
+hipError_t fast_launch_part<4>(bool, int, int, bool, bool, const KernelArgs&, int, hipStream_t);
+#define FP_DEFINE_PART(P)                                                                                        \
+    template <>                                                                                                  \
+    hipError_t fast_launch_part<P>(bool large, int dg, int epi, bool x_tl, bool w_fc, const KernelArgs& a,       \
+                                   int grid, hipStream_t s) {                                                    \
+        return large ? dispatch_part<P, LargeTile>(dg, epi, x_tl, w_fc, a, grid, s)                              \
+                     : dispatch_part<P, SmallTile>(dg, epi, x_tl, w_fc, a, grid, s);                             \
+    }
+#if FP_PART(0)
+FP_DEFINE_PART(0)
+#endif
+#if FP_PART(1)
+FP_DEFINE_PART(1)
+#endif
+#if FP_PART(2)
+FP_DEFINE_PART(2)
+#endif
+#if FP_PART(3)
+FP_DEFINE_PART(3)
+#endif
+#if FP_PART(4)
+FP_DEFINE_PART(4)
+#endif
+#undef FP_DEFINE_PART
+
+#if FP_PART(0)
 
 int fast_rope_groups(int head_dim, bool rope) {
     if (!rope) return 0;
@@ -956,9 +1048,9 @@ bool fast_addressable(int64_t M, int64_t S, int64_t ff_dim, int64_t qw) {
 // Entries for whole large column tiles, which also covers whole small ones.
 int64_t fast_col_desc_entries(int64_t F) { return (F + LargeTile::BF - 1) / LargeTile::BF * (LargeTile::BF / 8); }
 
-void fast_col_desc(int64_t S, int64_t ff_dim, int64_t n_heads, int64_t head_dim, int64_t F, unsigned* out,
-                   int64_t entries) {
-    const int64_t qw = n_heads * head_dim;
+void fast_col_desc(int64_t S, int64_t ff_dim, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, bool grouped,
+                   bool rope8, int64_t F, unsigned* out, int64_t entries) {
+    const int64_t hd = head_dim, qw = n_heads * hd, kvw = n_kv_heads * hd;
     for (int64_t g = 0; g < entries; ++g) {
         const int64_t f = 8 * g;
         unsigned d = 0;
@@ -966,9 +1058,25 @@ void fast_col_desc(int64_t S, int64_t ff_dim, int64_t n_heads, int64_t head_dim,
             if (f < ff_dim) {
                 d = (unsigned)f;
             } else {
-                const int64_t r = f - ff_dim, which = r / qw, rem = r - which * qw;
-                const int64_t h = rem / head_dim, jh = rem - h * head_dim;
-                d = ((unsigned)(which + 1) << 30) | (unsigned)(h * S * head_dim + jh);
+                // the group's slice (1 q, 2 k, 3 v), head and place in the head
+                const int64_t r = f - ff_dim;
+                int64_t kind, h, jh;
+                if (!grouped) {
+                    const int64_t which = r < qw ? 0 : r < qw + kvw ? 1 : 2;
+                    const int64_t rem = which == 0 ? r : r - qw - (which - 1) * kvw;
+                    h = rem / hd;
+                    jh = rem - h * hd;
+                    kind = 1 + which;
+                } else {
+                    // per k/v head: its n_heads / n_kv_heads q heads, then k, then v
+                    const int64_t qpk = n_heads / n_kv_heads, gw = (qpk + 2) * hd;
+                    const int64_t grp = r / gw, within = r - grp * gw, slot = within / hd;
+                    jh = within - slot * hd;
+                    kind = slot < qpk ? 1 : slot == qpk ? 2 : 3;
+                    h = slot < qpk ? grp * qpk + slot : grp;
+                }
+                d = ((unsigned)kind << 30) | (unsigned)(h * S * hd + jh);
+                if (rope8 && kind != 3 && jh == 0) d |= 1u << 29;
             }
         }
         out[g] = d;
@@ -979,19 +1087,29 @@ hipError_t launch_fused_proj_fast(bool x_tokens_last, bool w_fc, int dg, int epi
                                   hipStream_t stream) {
     if (pl.bk != kBK || pl.grid <= 0 || pl.grid % 8) return hipErrorInvalidValue;
     auto is = [&](auto t) { return pl.bm == decltype(t)::BT && pl.bn == decltype(t)::BF; };
+    bool large;
     switch (pl.shape) {
         case kFastLarge:
-            if (is(LargeTile{})) return dispatch_fast_rope<LargeTile>(dg, epi, x_tokens_last, w_fc, a, pl.grid, stream);
+            if (!is(LargeTile{})) return hipErrorInvalidValue;
+            large = true;
             break;
         case kFastSmall:
             // one tile per workgroup at most: each XCD's share of the tiles fits its workgroups
             static_assert(SmallTile::SINGLE, "small tiles are planned one per workgroup");
             if ((int64_t)a.tiles_m * a.tiles_n > (int64_t)(pl.grid / 8) * 8) return hipErrorInvalidValue;
-            if (is(SmallTile{})) return dispatch_fast_rope<SmallTile>(dg, epi, x_tokens_last, w_fc, a, pl.grid, stream);
+            if (!is(SmallTile{})) return hipErrorInvalidValue;
+            large = false;
             break;
-        default: break;
+        default: return hipErrorInvalidValue;
     }
-    return hipErrorInvalidValue;
+    switch (fast_part_of(epi, dg)) {
+        case 0: return fast_launch_part<0>(large, dg, epi, x_tokens_last, w_fc, a, pl.grid, stream);
+        case 1: return fast_launch_part<1>(large, dg, epi, x_tokens_last, w_fc, a, pl.grid, stream);
+        case 2: return fast_launch_part<2>(large, dg, epi, x_tokens_last, w_fc, a, pl.grid, stream);
+        case 3: return fast_launch_part<3>(large, dg, epi, x_tokens_last, w_fc, a, pl.grid, stream);
+        default: return fast_launch_part<4>(large, dg, epi, x_tokens_last, w_fc, a, pl.grid, stream);
+    }
 }
+#endif  // FP_PART(0)
 
 }  // namespace fp

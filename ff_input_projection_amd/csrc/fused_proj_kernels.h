@@ -51,7 +51,7 @@ struct KernelArgs {
     int32_t n_kv_heads;  // k and v heads (n_heads unless grouped-query)
     int32_t qkv_grouped; // 0: q, k, v columns contiguous; 1: grouped per k/v head
     int32_t rope_dims;   // rotated width of each q/k head (head_dim unless partial)
-    int32_t ff_channels_first;  // 1: ff stored [b, ff_dim, S] (general kernel only)
+    int32_t ff_channels_first;  // 1: ff stored [b, ff_dim, S] (the fast kernel: its epilogue variant)
     int32_t act;         // ff slice: 0 none, 1 exact-erf GELU, 2 tanh GELU, 3 squared ReLU
     int32_t rope;        // 1: RoPE on q and k
     int32_t tiles_m;
@@ -60,7 +60,8 @@ struct KernelArgs {
     const void* zeros;   // >= 16 zero bytes: source of operand chunks outside the problem
     // Fast kernel only: one entry per 8 output columns, covering every column tile in
     // full. Bits 30-31: 0 ff, 1 q, 2 k, 3 v; bits 0-29: element offset of the group's
-    // first column (ff: its column; q/k/v: head * S * head_dim + place in the head).
+    // first column (ff: its column; q/k/v: head * S * head_dim + place in the head), whose
+    // bit 29 instead marks a rotated group when RoPE covers the first 8 columns of a head.
     const unsigned* col_desc;
     // Fast kernel only: division by S (token -> slab) and by group_m * tiles_n (tile order).
     FastDivU31 div_s;
@@ -114,12 +115,16 @@ TilePlan fast_plan(int64_t M, int64_t F, int num_cus);
 // Whether the fast kernel can address this problem with its 32-bit per-lane output
 // offsets and 30-bit column offsets.
 bool fast_addressable(int64_t M, int64_t S, int64_t ff_dim, int64_t qw);
-// Column descriptor table of the fast kernel (entries for ceil(F / 256) full column tiles).
-void fast_col_desc(int64_t S, int64_t ff_dim, int64_t n_heads, int64_t head_dim, int64_t F, unsigned* out,
-                   int64_t entries);
+// Column descriptor table of the fast kernel (entries for ceil(F / 256) full column tiles):
+// each 8-column group's slice and element offset, for q/k/v columns either contiguous or
+// grouped per k/v head; with rope8 (RoPE on the first 8 columns of each q/k head) bit 29
+// marks those groups.
+void fast_col_desc(int64_t S, int64_t ff_dim, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, bool grouped,
+                   bool rope8, int64_t F, unsigned* out, int64_t entries);
 int64_t fast_col_desc_entries(int64_t F);
 // epi: 0 exact-erf GELU or no activation, token-major ff; 1 tanh GELU or squared ReLU;
-// 2 channels-first ff (1 and 2 without RoPE, dg == 0); 5 the backward pass's dy over the ff
+// 2 channels-first ff (1 and 2 without RoPE, dg == 0); 3 as 0 with RoPE on the first 8
+// columns of each q/k head only (the groups bit 29 of the descriptor marks, dg == 0); 5 the backward pass's dy over the ff
 // columns (dg == 0); 4 the weight gradient's fp32
 // partial sums over token ranges (dg == 0, W read as [K, N]; x_tokens_last selects K-major
 // rows with K steps crossing slabs).

@@ -108,7 +108,9 @@ SMALL = [
                ff_act="gelu_tanh", n_heads=2, head_dim=8, seed=119),
     with_shape(WORKLOADS["tiny_f32"], "f32_cf_relu2", x_shape=(1, 40, 8, 8, 1), ff_dim=64, ff_act="relu2",
                n_heads=2, head_dim=8, seed=120),
-    # fewer k/v heads than q heads, both column orders, partial rotary (general kernel)
+    # fewer k/v heads than q heads, both column orders, partial rotary (by default the fast
+    # kernel takes the bf16 ones rotating 8 columns or whole heads, the general kernel
+    # rotary width 16 and fp32)
     with_shape(WORKLOADS["gqa_rope8_bf16"], "tl_gqa_grouped_rope8", x_shape=(2, 77, 64), seed=122),
     with_shape(WORKLOADS["bert_qkv_bf16"], "tl_gqa_contiguous_rope16", x_shape=(2, 90, 96), ff_dim=64,
                ff_act="gelu", n_heads=6, head_dim=32, n_kv_heads=2, rope=True, rope_dims=16, seed=123),
@@ -183,13 +185,23 @@ FAST_VARIANTS = [
                n_heads=4, head_dim=64, rope=False, ff_layout="channels_first", seed=138),
     with_shape(WORKLOADS["bert_ff_bf16"], "fast_ffcf_tokens_last_gelu", x_shape=(8, 1000, 128), ff_dim=512,
                ff_layout="channels_first", seed=139),
+    # fewer k/v heads and grouped columns: RoPE on the first 8 columns of each head on large
+    # tiles with a GELU ff slice; 8-column heads rotated whole (k/v contiguous, ragged tokens);
+    # whole-head RoPE with 4 k/v heads, contiguous, on large tiles with a [F,C] weight
+    with_shape(WORKLOADS["gqa_rope8_bf16"], "fast_rope8_large_grouped_ff", x_shape=(4, 2048, 256), ff_dim=1024,
+               ff_act="gelu", n_heads=16, head_dim=64, n_kv_heads=4, rope_dims=8, has_bias=True, seed=140),
+    with_shape(WORKLOADS["gqa_rope8_bf16"], "fast_rope8_hd8_contiguous", x_shape=(2, 150, 64), n_heads=4,
+               head_dim=8, n_kv_heads=2, qkv_order="contiguous", rope_dims=0, seed=141),
+    with_shape(WORKLOADS["bert_qkv_bf16"], "fast_gqa_fullrope_large_fc", x_shape=(16, 1024, 256), ff_dim=0,
+               n_heads=16, head_dim=64, n_kv_heads=4, rope=True, w_layout="fc", pos_offset=3, seed=142),
 ]
 
 
 @pytest.mark.parametrize("wl", FAST_VARIANTS, ids=[w.name for w in FAST_VARIANTS])
 def test_fast_kernel_activation_and_ff_layout_variants(wl):
-    """tanh GELU, squared ReLU and the channels-first ff output on the fast kernel (planned
-    by default), every output element against the oracle; outputs start as NaN."""
+    """tanh GELU, squared ReLU, the channels-first ff output and the grouped-query layouts on
+    the fast kernel (planned by default), every output element against the oracle; outputs
+    start as NaN."""
     print(f"[case] fast variant {wl.name} x={wl.x_shape}", flush=True)
     inp = make_inputs(wl)
     proj, outs = run_gpu(wl, inp, DEV)

@@ -21,9 +21,10 @@ from ff_input_projection_amd import build as fpbuild
 HIPCC = fpbuild.HIPCC
 
 
-def _start_asm(src, out):
+def _start_asm(src, out, part):
     flags = [f for f in fpbuild.FLAGS if f not in ("-fPIC", "-shared")]
-    cmd = [HIPCC, *flags, "-I", fpbuild.CSRC, "--cuda-device-only", "-S", "-x", "hip", src, "-o", out]
+    cmd = [HIPCC, *flags, f"-DFP_FAST_PART={part}", "-I", fpbuild.CSRC, "--cuda-device-only", "-S", "-x", "hip",
+           src, "-o", out]
     return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
 
 
@@ -44,8 +45,9 @@ _BAD_WIDEN = ("((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(a 
 
 @pytest.fixture(scope="module")
 def fast_asm(tmp_path_factory):
-    """The fast kernel's gfx950 assembly, and that of a copy with the sign-extending
-    widening planted in scalar_load16 (both compiled at once)."""
+    """The fast kernel's gfx950 assembly (every part of its instantiations, as the build
+    compiles them), and that of part 0 of a copy with the sign-extending widening planted
+    in scalar_load16 (all compiled at once)."""
     d = tmp_path_factory.mktemp("isa")
     src = os.path.join(fpbuild.CSRC, "fused_proj_fast.hip")
     text = open(src).read()
@@ -53,9 +55,12 @@ def fast_asm(tmp_path_factory):
     bad_src = os.path.join(d, "fast_bad.hip")
     with open(bad_src, "w") as f:
         f.write(text.replace(_GOOD_WIDEN, _BAD_WIDEN))
-    good_out, bad_out = os.path.join(d, "fast.s"), os.path.join(d, "fast_bad.s")
-    pg, pb = _start_asm(src, good_out), _start_asm(bad_src, bad_out)
-    return _finish_asm(pg, good_out), _finish_asm(pb, bad_out)
+    good = [(os.path.join(d, f"fast.part{k}.s"), k) for k in range(fpbuild.FAST_PARTS)]
+    bad_out = os.path.join(d, "fast_bad.s")
+    procs = [(_start_asm(src, out, k), out) for out, k in good]
+    pb = _start_asm(bad_src, bad_out, 0)
+    good_asm = "\n".join(_finish_asm(p, out) for p, out in procs)
+    return good_asm, _finish_asm(pb, bad_out)
 
 
 def _kernels(asm):
