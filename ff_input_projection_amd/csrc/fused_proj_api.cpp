@@ -376,6 +376,7 @@ int plan_backward(fused_proj_plan* h) {
         a.dw_tiles_t = (int32_t)tiles_t;
         a.div_dwt = fp::make_fastdiv_u31((uint32_t)tiles_t);
         a.zeros = h->d_zeros;
+        a.sink = static_cast<char*>(h->d_zeros) + 256;
         h->dw_tile = fp::TilePlan{256, 256, 32, 8, (int)((cus + 7) / 8 * 8), fp::kFastLarge};
         h->dw_x_kmajor = cf;
         h->fast_dw = true;
@@ -528,9 +529,10 @@ int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backwa
     }
     a.rope_cos = h->d_cos;
     a.rope_sin = h->d_sin;
-    // a zero block: operand chunks outside the problem are read from here
-    e = hipMalloc(&h->d_zeros, 256);
-    if (e == hipSuccess) e = hipMemset(h->d_zeros, 0, 256);
+    // a zero block: operand chunks outside the problem are read from its first 256 bytes;
+    // the fast kernel's stores outside the problem go to the other 256
+    e = hipMalloc(&h->d_zeros, 512);
+    if (e == hipSuccess) e = hipMemset(h->d_zeros, 0, 512);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         g_last_hip = e;
@@ -538,6 +540,7 @@ int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backwa
         return FUSED_PROJ_EHIP;
     }
     a.zeros = h->d_zeros;
+    a.sink = static_cast<char*>(h->d_zeros) + 256;
     if (h->fast) {
         const int64_t n = fp::fast_col_desc_entries(r.F);
         std::vector<unsigned> hd((size_t)n);

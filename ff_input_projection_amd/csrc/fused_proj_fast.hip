@@ -488,6 +488,8 @@ fused_proj_fast_kernel(KernelArgs p) {
     // q/k/v elements of one slab (all heads of the slice): q, and k or v
     const int64_t slab_q = (int64_t)S * p.qw, slab_kv = (int64_t)S * p.n_kv_heads * hd;
     constexpr bool R8 = EPI == kEpiRope8;
+    // epilogues whose every wave issues exactly TJ * 8 stores per tile (the restaged ones)
+    constexpr bool RELAX = EPI == kEpiDefault || EPI == kEpiOtherAct || EPI == kEpiRope8;
 
     unsigned voff_cur[NLOAD], voff_nxt[NLOAD];
     int trow_cur, kb_cur;
@@ -574,7 +576,10 @@ fused_proj_fast_kernel(KernelArgs p) {
                 __syncthreads();
                 if (s_load < KTp) pp.template issue<SL>(voff_cur, s_load, K, zeros, kb_cur);
             } else {
-                wait_vmcnt<NLOAD>();
+                // After an epilogue of the restaged kind, its TJ * 8 stores follow the loads
+                // of the tile's steps 1 and 2: those two steps need not wait for them.
+                if (RELAX && kt < 2 && k_tile > 0) wait_vmcnt<NLOAD + TJ * 8>();
+                else wait_vmcnt<NLOAD>();
                 __syncthreads();
                 const bool ahead = s_load >= KTp;   // wave-uniform
                 unsigned vo[NLOAD];
@@ -656,10 +661,6 @@ fused_proj_fast_kernel(KernelArgs p) {
         const int fw = n0 + wf * WF;
         const u32x16 desc = scalar_load16(p.col_desc + (unsigned)fw / 8u);
         constexpr unsigned OFS_MASK = R8 ? 0x1fffffffu : 0x3fffffffu;
-        // whether the wave's columns meet the q or k slice (then RoPE applies): contiguous
-        // q, k, v columns end the rotated ones before v; grouped ones interleave v
-        const int rope_end = p.qkv_grouped ? N : ff_dim + p.qw + p.n_kv_heads * hd;
-        const bool wave_rope = (DG > 0 || R8) && fw < rope_end && fw + WF > ff_dim;
         // cos/sin registers: the 4 columns of each first-half group of a head this lane
         // rotates (8-column RoPE: the 4 pairs of the rotated group)
         constexpr int HD = DG > 0 ? 16 * DG : 16, HALF = HD / 2, NR = R8 ? 1 : HALF / 8, NRB = NR > 4 ? 4 : NR;
@@ -710,6 +711,7 @@ fused_proj_fast_kernel(KernelArgs p) {
         const unsigned stride_l = kind_l == 0 ? (unsigned)(2 * ffr) : (unsigned)(2 * hd);
         char* const row0_l = base_l + r0 * stride_l;
         const bool col_ok = fw + 8 * gl < N;
+        char* const sink_l = static_cast<char*>(p.sink) + 16 * gl;
         // the wave's tokens usually lie in one slab: then a token's offset is linear in it
         const int bi_first = (int)fastdiv_u31((uint32_t)tw0, p.div_s);
         const bool one_slab =
@@ -725,7 +727,9 @@ fused_proj_fast_kernel(KernelArgs p) {
         // every head of the wave uses the same ones -- all at once for head sizes up to 64,
         // in two halves for 128 (registers). Those of the next token block are loaded
         // before this block's stores: a load issued after a store would wait for it too
-        // (the vector memory counter counts in order).
+        // (the vector memory counter counts in order). Every wave loads them, rotating or
+        // not: loads under a branch leave the compiler unsure which loads are still in
+        // flight, and it then waits for this block's stores before the next block's RoPE.
         f32x4 rc[NRB], rsn[NRB];
         auto load_rope = [&](int j, int r0) __attribute__((always_inline)) {
             const int t = tw0 + 32 * j + (lane_e & 31);
@@ -734,12 +738,7 @@ fused_proj_fast_kernel(KernelArgs p) {
             // the table holds rd/2 values per token: a lane's 4 start at 4 * (lane / 32) of
             // each group of 8 (8-column RoPE: both half-waves read the token's 4)
             const unsigned rp_off = R8 ? (unsigned)(s * 16) : (unsigned)((s * (DG * 8) + 4 * (lane_e >> 5)) * 4);
-#pragma unroll
-            for (int r = 0; r < NRB; ++r) {
-                rc[r] = f32x4{};
-                rsn[r] = f32x4{};
-            }
-            if (wave_rope) {
+            if constexpr (DG > 0 || R8) {
 #pragma unroll
                 for (int r = 0; r < NRB; ++r) {
                     const char* const c = reinterpret_cast<const char*>(rope_cos + 8 * (r0 + r)) + rp_off;
@@ -892,11 +891,12 @@ fused_proj_fast_kernel(KernelArgs p) {
                     const int r = r0 + 4 * rr;   // token row of the half block
                     const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(size_t)(
                         rd_lds + rr * 4 * kRestageRow);
-                    if (r < rows && col_ok) {
-                        char* const dst = one_slab ? row0_l + (u + (unsigned)(4 * rr) * stride_l)
-                                                   : base_l + token_off(t0 + r);
-                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
-                    }
+                    // every lane stores, rows or columns outside the problem into the sink: with
+                    // a fixed store count the compiler's waits (and the K loop's) can count them
+                    char* const dst = !(r < rows && col_ok) ? sink_l
+                                      : one_slab            ? row0_l + (u + (unsigned)(4 * rr) * stride_l)
+                                                            : base_l + token_off(t0 + r);
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
                 }
             }
         }

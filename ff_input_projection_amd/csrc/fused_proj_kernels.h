@@ -58,6 +58,7 @@ struct KernelArgs {
     int32_t tiles_n;
     int32_t group_m;     // tile rows per raster group
     const void* zeros;   // >= 16 zero bytes: source of operand chunks outside the problem
+    void* sink;          // 256 bytes that the fast kernel's stores outside the problem go to (never read)
     // Fast kernel only: one entry per 8 output columns, covering every column tile in
     // full. Bits 30-31: 0 ff, 1 q, 2 k, 3 v; bits 0-29: element offset of the group's
     // first column (ff: its column; q/k/v: head * S * head_dim + place in the head), whose
