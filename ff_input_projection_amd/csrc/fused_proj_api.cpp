@@ -208,7 +208,15 @@ struct fused_proj_plan {
     bool dw_x_kmajor = false;            // ... reading x as K-major rows (channels-first x)
     fp::KernelArgs dw_args{};            // its arguments but the per-call pointers
     fp::TilePlan dw_tile{};
+    // dx in two parts when its tiles would leave most CUs idle in a last round: the first
+    // dx_head_m tokens through the nested plan's kernel, the rest in ranges of the fused
+    // columns (fp32 partial sums) and a reduction
+    bool dx_split = false;
+    int64_t dx_head_m = 0;
+    fp::KernelArgs dxt_args{};           // the range units' arguments but the per-call pointers
+    fp::TilePlan dxt_tile{};
     size_t ws_dbp = 0, ws_dwp = 0;       // workspace offsets (dy at 0)
+    size_t ws_dxp = 0;
     size_t ws_bytes = 0;                 // workspace size
 };
 
@@ -218,6 +226,86 @@ int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backwa
 
 constexpr size_t kWsAlign = 256;
 size_t ws_round(size_t n) { return (n + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// dx = dy W^T on large tiles takes rounds of tiles over the CUs; when the last round is
+// mostly idle (Walrus: 288 tiles on 256 CUs), the last token tiles are instead split into
+// (tile, range of the fused columns) units that fill one round, each storing fp32 partial
+// sums that a reduction adds into dx. The head keeps a whole number of slabs (channels-first
+// x, whose dx is stored per slab). The split (tail tiles, ranges) minimises an estimated
+// time: rounds of tiles times a tile's MFMA time (at about 55% of a CU's share of the bf16
+// peak), plus writing and reading back the partial sums (about 4 TB/s) and two launches.
+void plan_dx_split(fused_proj_plan* h) {
+    const fused_proj_desc& d = h->d;
+    const Derived& r = h->r;
+    const fused_proj_plan* xp = h->dx_plan;
+    const char* force = std::getenv("FUSED_PROJ_KERNEL");
+    if (!xp || !xp->fast || xp->tile.shape != fp::kFastLarge || xp->epi > 2 || r.M <= 0 || r.F % 32 != 0 ||
+        (force && std::strcmp(force, "general") == 0))
+        return;
+    const bool cf = d.x_layout == FUSED_PROJ_X_CHANNELS_FIRST;
+    if (cf && r.S % 64 != 0) return;
+    const int64_t bt = 256, tm = xp->base.tiles_m, tn = xp->base.tiles_n, cus = h->num_cus;
+    const int64_t ksteps = r.F / 32, C = d.channels;
+    // head tile rows come in multiples of g (a whole number of slabs)
+    int64_t g = 1;
+    if (cf) {
+        int64_t a = r.S, b2 = bt;
+        while (b2) {
+            const int64_t t = a % b2;
+            a = b2;
+            b2 = t;
+        }
+        g = r.S / a;
+    }
+    const double tile_s = 2.0 * 256 * 256 * (double)r.F / (2.5e15 / (double)cus * 0.55);
+    const double base = (double)((tm * tn + cus - 1) / cus) * tile_s;
+    double best = base * 0.97;   // worth a split only when clearly faster
+    int64_t best_head = -1, best_r = 1;
+    for (int64_t head = (tm - 1) / g * g; head >= 0; head -= g) {
+        const int64_t rows = r.M - head * bt;   // tail tokens
+        const int64_t rt = tm - head;
+        for (int64_t rs = 2; rs <= 16; ++rs) {
+            if (ksteps % rs) continue;
+            const double t = (double)((head * tn + cus - 1) / cus) * tile_s +
+                             (double)((rt * tn * rs + cus - 1) / cus) * tile_s / (double)rs +
+                             (double)rs * (double)rows * (double)C * 8.0 / 4e12 + 5e-6;
+            if (t < best) {
+                best = t;
+                best_head = head;
+                best_r = rs;
+            }
+        }
+        if (head == 0) break;
+    }
+    if (best_head < 0) return;
+    const int64_t rt = tm - best_head, rows = r.M - best_head * bt;
+    fp::KernelArgs t = xp->base;
+    t.M = rows;
+    t.S = (int32_t)rows;
+    t.div_s = fp::make_fastdiv_u31((uint32_t)rows);
+    t.x_sb = rows * r.F;
+    t.K = (int32_t)(r.F / best_r);
+    t.N = (int32_t)C;
+    t.tiles_m = (int32_t)(rt * best_r);
+    t.tiles_n = (int32_t)tn;
+    t.group_m = 8;
+    t.div_group = fp::make_fastdiv_u31((uint32_t)(8 * tn));
+    t.dw_tiles_t = (int32_t)rt;
+    t.div_dwt = fp::make_fastdiv_u31((uint32_t)rt);
+    t.k_slab_steps = (int32_t)ksteps;   // dy's rows are one "slab": no K step crosses one
+    t.div_kslab = fp::make_fastdiv_u31((uint32_t)ksteps);
+    t.w_ld = (int32_t)(xp->w_fc ? r.F : C);
+    t.bias = nullptr;
+    h->dxt_args = t;
+    h->dxt_tile = fp::TilePlan{256, 256, 32, 8, (int)((cus + 7) / 8 * 8), fp::kFastLarge};
+    h->dx_split = true;
+    h->dx_head_m = best_head * bt;
+    fp::BwdArgs& b = h->bwd;
+    b.dx_row0 = (int32_t)(best_head * bt);
+    b.dx_rows = (int32_t)rows;
+    b.dx_splits = (int32_t)best_r;
+    b.dx_cf = cf ? 1 : 0;
+}
 
 // Backward plan: the dx sub-projection, the dy and dW tilings and the workspace layout.
 int plan_backward(fused_proj_plan* h) {
@@ -385,12 +473,19 @@ int plan_backward(fused_proj_plan* h) {
         b.chunk = (int32_t)(r.M / best);
         b.dw_partials = 1;
     }
-    // workspace: dy, then the column sums of dy per token tile (bias), then the dW partials
+    plan_dx_split(h);
+    // workspace: dy, then the column sums of dy per token tile (bias), then the dW partials,
+    // then dx's partials
     size_t off = ws_round((size_t)(r.M * r.F * es));
     h->ws_dbp = off;
     if (d.has_bias) off += ws_round((size_t)b.db_tiles * (size_t)r.F * 4);
+    // (the fast kernel's partial sums are whole 256 x 256 blocks)
+    auto up256 = [](int64_t v) { return (size_t)((v + 255) / 256 * 256); };
     h->ws_dwp = off;
-    if (splits > 1 || h->fast_dw) off += ws_round((size_t)splits * (size_t)d.channels * (size_t)r.F * 4);
+    if (h->fast_dw) off += ws_round((size_t)splits * up256(d.channels) * up256(r.F) * 4);
+    else if (splits > 1) off += ws_round((size_t)splits * (size_t)d.channels * (size_t)r.F * 4);
+    h->ws_dxp = off;
+    if (h->dx_split) off += ws_round((size_t)b.dx_splits * up256(b.dx_rows) * up256(d.channels) * 4);
     h->ws_bytes = r.M > 0 ? off : 0;
     return FUSED_PROJ_OK;
 }
@@ -760,9 +855,35 @@ int fused_proj_backward(fused_proj_t h, const void* x, const void* w, const void
         }
         if (e == hipSuccess) e = fp::launch_bwd_dy(h->dt, h->x_tl, h->w_fc, b, s);
         if (e == hipSuccess && h->fast_dy) e = fp::launch_bwd_colsum(h->dt, b, b.dy_col_tile0 * 128, s);
-        if (e == hipSuccess && has_c) {
+        if (e == hipSuccess && has_c && !h->dx_split) {
             const int rc = fused_proj_run(h->dx_plan, b.dy, w, nullptr, dx, nullptr, nullptr, nullptr, stream);
             if (rc) return rc;
+        } else if (e == hipSuccess && has_c) {
+            // the head's tiles through the nested plan's kernel, the tail's range units, then
+            // their reduction into dx
+            const fused_proj_plan* xp = h->dx_plan;
+            if (h->dx_head_m > 0) {
+                fp::KernelArgs a = xp->base;
+                a.M = h->dx_head_m;
+                a.tiles_m = (int32_t)(h->dx_head_m / 256);
+                a.x = b.dy;
+                a.w = w;
+                a.bias = nullptr;
+                a.ff = dx;
+                e = fp::launch_fused_proj_fast(xp->x_tl, xp->w_fc, xp->dg, xp->epi, xp->tile, a, s);
+            }
+            if (e == hipSuccess) {
+                fp::KernelArgs a = h->dxt_args;
+                a.x = static_cast<const char*>(b.dy) + (size_t)h->dx_head_m * (size_t)F * es;
+                a.w = w;
+                a.ff = ws + h->ws_dxp;
+                e = fp::launch_fused_proj_fast(true, xp->w_fc, 0, 4, h->dxt_tile, a, s);
+            }
+            b.dxp = reinterpret_cast<float*>(ws + h->ws_dxp);
+            b.dx = dx;
+            if (e == hipSuccess) e = fp::launch_bwd_reduce_dx(b, s);
+        }
+        if (e == hipSuccess && has_c) {
             if (h->fast_dw) {
                 fp::KernelArgs a = h->dw_args;
                 a.x = x;

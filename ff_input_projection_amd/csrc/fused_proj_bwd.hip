@@ -17,13 +17,17 @@
 //      16-byte chunks), stores it token-major into the workspace and writes the tile's
 //      fp32 column sums (for db).
 //   2. dx: a forward projection planned by the C-ABI layer (dy as a token-major
-//      activation, W read transposed, the result as an "ff" slice laid out like x).
+//      activation, W read transposed, the result as an "ff" slice laid out like x). When
+//      its tiles would leave most CUs idle in a last round, the last token tiles are
+//      contracted in ranges of the fused columns into fp32 partial sums, and
+//      bwd_reduce_tiles_kernel sums them into dx.
 //   3. bwd_dw_kernel: 128 x 128 tiles over [C, F] contracted over tokens, split into
 //      token ranges when the tiles alone cannot fill the CUs; x is read in place in its
 //      own layout (channels-first: 16-byte runs of tokens; token-major: runs of
 //      channels), dy as [tokens, F].
-//   4. bwd_reduce_dw_kernel / bwd_reduce_db_kernel: the split partial sums into dW in
-//      W's layout, and the column sums into db.
+//   4. bwd_reduce_tiles_kernel (the fast kernel's partial sums, in its accumulator order)
+//      or bwd_reduce_dw_kernel (the dW tile kernel's [splits, C, F]) into dW in W's layout,
+//      and bwd_reduce_db_kernel: the column sums into db.
 #include "general_tile.h"
 
 namespace fp {
@@ -450,6 +454,83 @@ __global__ __launch_bounds__(256) void bwd_reduce_dw_kernel(BwdArgs b) {
     }
 }
 
+// Partial sums in the fast kernel's accumulator order (its range units: [range][row tile]
+// [column tile] blocks of 256 x 256 floats, 1 KB chunks ((wave * 4 + a) * 2 + j) * 4 + q
+// of 64 lanes x 4 floats, lane l at row 64 wt + 32 j + l % 32 and columns 128 wf + 32 a +
+// 8 q + 4 (l / 32) .. of the block, wave = 4 wf + wt) summed over the ranges. Workgroup:
+// a 64 x 64 block of [rows, cols], i.e. 16 chunks of one wave; each thread reads 4 lanes'
+// 64 contiguous bytes per range, the sums meet in LDS and leave as rows, transposed rows
+// or a channels-first dx (64 tokens of one slab).
+struct TileReduce {
+    const float* part;
+    void* out;
+    int64_t range_floats;   // floats per range
+    int32_t rows, cols;     // the problem's extent (the blocks may overhang it)
+    int32_t tiles_c;        // column tiles per row tile
+    int32_t splits;
+    int32_t mode;           // 0: out[row][col]; 1: out[col][row]; 2: dx [b, C, S] from tokens
+    int32_t ld;             // row stride (modes 0 and 1) or S (mode 2)
+    int32_t row0;           // first token (mode 2)
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_reduce_tiles_kernel(TileReduce tr) {
+    __shared__ float tile[64][65];
+    const int tid = threadIdx.x;
+    const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+    const int wt = (r0 & 255) >> 6, wf = (c0 & 255) >> 7, a0 = (c0 & 127) >> 5;
+    const int ci = tid >> 4, l0 = (tid & 15) * 4;
+    const int a = a0 + (ci >> 3), j = (ci >> 2) & 1, q = ci & 3;
+    const int chunk = (((wf * 4 + wt) * 4 + a) * 2 + j) * 4 + q;
+    const float* src = tr.part + ((int64_t)(r0 >> 8) * tr.tiles_c + (c0 >> 8)) * 65536 + chunk * 256 + l0 * 4;
+    f32x4 sum[4] = {};
+    for (int z = 0; z < tr.splits; ++z) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sum[k] += *reinterpret_cast<const f32x4*>(src + 4 * k);
+        src += tr.range_floats;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int l = l0 + k;
+        const int row = 32 * j + (l & 31), col = 32 * (a - a0) + 8 * q + 4 * (l >> 5);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) tile[row][col + u] = sum[k][u];
+    }
+    __syncthreads();
+    T* const out = static_cast<T*>(tr.out);
+    if (tr.mode == 0) {
+        // thread (r, cq): 16 consecutive columns of row r0 + r
+        const int r = tid >> 2, cq = (tid & 3) * 16;
+        if (r0 + r >= tr.rows) return;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = c0 + cq + 4 * k;   // cols is a multiple of 4
+            if (c < tr.cols) store4<T>(out + (int64_t)(r0 + r) * tr.ld + c, &tile[r][cq + 4 * k]);
+        }
+        return;
+    }
+    // thread (cr, rq): 16 consecutive rows of column c0 + cr (rows is a multiple of 4)
+    const int cr = tid >> 2, rq = (tid & 3) * 16;
+    const int c = c0 + cr;
+    if (c >= tr.cols) return;
+    T* base;
+    if (tr.mode == 1) {
+        base = out + (int64_t)c * tr.ld + r0;
+    } else {
+        const int t0 = tr.row0 + r0, bi = t0 / tr.ld;
+        base = out + ((int64_t)bi * tr.cols + c) * tr.ld + (t0 - bi * tr.ld);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int rr = rq + 4 * k;
+        if (r0 + rr >= tr.rows) continue;
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = tile[rr + u][cr];
+        store4<T>(base + rr, v);
+    }
+}
+
 // db from the per-tile column sums: 64 columns per workgroup, its 256 threads summing
 // every fourth row (coalesced 256-byte row segments), then the four partial sums in LDS.
 template <typename T>
@@ -522,8 +603,31 @@ hipError_t launch_dw_layouts(bool x_tl, const BwdArgs& b, hipStream_t s) {
 }
 
 template <typename T>
+hipError_t launch_reduce_tiles(const TileReduce& tr, hipStream_t s) {
+    if (tr.rows <= 0 || tr.cols <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((tr.rows + 63) / 64), (unsigned)((tr.cols + 63) / 64));
+    hipLaunchKernelGGL((bwd_reduce_tiles_kernel<T>), grid, dim3(256), 0, s, tr);
+    return hipGetLastError();
+}
+
+template <typename T>
 hipError_t launch_reduce_t(const BwdArgs& b, hipStream_t s) {
-    if ((b.splits > 1 || b.dw_partials) && b.f.K > 0) {
+    if (b.dw_partials && b.f.K > 0) {
+        // the fast kernel's units: [splits][C tiles][F tiles] blocks into dW ([C, F] rows, or
+        // [F, C] as transposed rows)
+        TileReduce tr{};
+        tr.part = b.dwp;
+        tr.out = b.dw;
+        tr.rows = b.f.K;
+        tr.cols = b.f.N;
+        tr.tiles_c = (b.f.N + 255) / 256;
+        tr.range_floats = (int64_t)((b.f.K + 255) / 256) * tr.tiles_c * 65536;
+        tr.splits = b.splits;
+        tr.mode = b.w_fc ? 1 : 0;
+        tr.ld = b.w_fc ? b.f.K : b.f.N;
+        const hipError_t e = launch_reduce_tiles<T>(tr, s);
+        if (e != hipSuccess) return e;
+    } else if (b.splits > 1 && b.f.K > 0) {
         const dim3 grid((unsigned)((b.f.K + 63) / 64), (unsigned)((b.f.N + 63) / 64));
         hipLaunchKernelGGL((bwd_reduce_dw_kernel<T>), grid, dim3(256), 0, s, b);
         const hipError_t e = hipGetLastError();
@@ -550,6 +654,29 @@ hipError_t launch_bwd_dw(DType dt, bool x_tl, const BwdArgs& b, hipStream_t s) {
 
 hipError_t launch_bwd_reduce(DType dt, const BwdArgs& b, hipStream_t s) {
     return dt == DType::BF16 ? launch_reduce_t<__bf16>(b, s) : launch_reduce_t<float>(b, s);
+}
+
+hipError_t launch_bwd_reduce_dx(const BwdArgs& b, hipStream_t s) {
+    if (b.dx_splits <= 1 || b.dx_rows <= 0) return hipSuccess;
+    // the tail's units: [splits][token tiles][C tiles] blocks into dx's last tokens
+    TileReduce tr{};
+    tr.part = b.dxp;
+    tr.rows = b.dx_rows;
+    tr.cols = b.f.K;
+    tr.tiles_c = (b.f.K + 255) / 256;
+    tr.range_floats = (int64_t)((b.dx_rows + 255) / 256) * tr.tiles_c * 65536;
+    tr.splits = b.dx_splits;
+    if (b.dx_cf) {
+        tr.out = b.dx;
+        tr.mode = 2;
+        tr.ld = b.f.S;
+        tr.row0 = b.dx_row0;
+    } else {
+        tr.out = static_cast<__bf16*>(b.dx) + (int64_t)b.dx_row0 * b.f.K;
+        tr.mode = 0;
+        tr.ld = b.f.K;
+    }
+    return launch_reduce_tiles<__bf16>(tr, s);
 }
 
 hipError_t launch_bwd_colsum(DType dt, const BwdArgs& b, int ncols, hipStream_t s) {

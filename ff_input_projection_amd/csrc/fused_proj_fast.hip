@@ -261,7 +261,7 @@ __device__ __forceinline__ void tile_offsets(unsigned (&voff)[C::NLOAD], int (&k
             const int c = pc ^ ((row * C::W_CPR / 16) % C::W_CPR);
             const int n = n0 + row;
             krow = c * 8;
-            off = (int64_t)(n < N ? n : 0) * K + krow;
+            off = (int64_t)(n < N ? n : 0) * wld + krow;
         } else {
             const int c = pc ^ ((row & 3) << 2);
             const int n = n0 + c * 8;
@@ -362,9 +362,10 @@ constexpr int kEpiDefault = 0, kEpiOtherAct = 1, kEpiFfChannelsFirst = 2;
 // a rotated group's pairs lie 4 columns apart, in the two half-waves, and the descriptor's
 // bit 29 marks the group.
 constexpr int kEpiRope8 = 3;
-// The weight gradient's contraction over tokens (dW = X^T dy, rows are channels): tiles are
-// (row tile, token range) units, each storing its fp32 partial sums [range][C][F] straight
-// from the accumulators (no activation, bias, RoPE or restage).
+// Contractions split into ranges: tiles are (row tile, K range) units, each storing its fp32
+// partial sums [range][M][N] straight from the accumulators (no activation, bias, RoPE or
+// restage). The weight gradient (dW = X^T dy over token ranges, rows are channels), and the
+// input gradient's last token tiles (dx = dy W^T over ranges of the fused columns).
 constexpr int kEpiDwPartial = 4;
 // The backward pass's dy over the ff columns: the forward product y recomputed, then
 // dy = d_ff * act'(y) (d_ff token-major, read 8 bytes per lane and group) stored token-major
@@ -438,8 +439,10 @@ fused_proj_fast_kernel(KernelArgs p) {
     }
     pp.wsrc = static_cast<const char*>(p.w);
     pp.xsrc = static_cast<const char*>(p.x);
-    // the grad epilogue's product reads the ff columns of a wider [C, F] weight
-    const int wld = EPI == kEpiGrad ? p.w_ld : N;
+    // W's row stride: [K, N] rows are N long except for the grad epilogue's product, which
+    // reads the ff columns of a wider [C, F] weight; [N, K] rows are K long except for
+    // contraction ranges (the input gradient's range units), which cover part of each row
+    const int wld = W_FC ? (DW ? p.w_ld : K) : EPI == kEpiGrad ? p.w_ld : N;
     pp.wstep = (W_FC ? (int64_t)BK : (int64_t)BK * wld) * 2;
     pp.xstep = (X_TL ? (int64_t)BK : (int64_t)BK * p.x_sc) * 2;
     if constexpr (DW && X_TL) {
@@ -635,22 +638,26 @@ fused_proj_fast_kernel(KernelArgs p) {
         // there for the write-back at the end of the kernel).
         const int tw0 = m0 + wt * WT;   // the wave's first token
         if constexpr (DW) {
-            // fp32 partial sums of this unit's token range, [range][C][F]: row tw0 + 32j +
-            // lane%32, the lane's 4 columns of each 8-column group, 16 bytes per store
+            // fp32 partial sums of this unit in the accumulators' own order, so that every
+            // store writes 1 KB contiguous: the unit's BT x BF block [range][row tile]
+            // [column tile] is 256-float chunks ((wave * TI + a) * TJ + j) * 4 + q, lane l
+            // holding floats 4l..4l+3 = acc[a][j][4q..4q+3] (row 32j + l%32 of the wave tile,
+            // columns 32a + 8q + 4(l/32) ..). Rows and columns outside the problem are stored
+            // too (the block is whole); the reduction skips them.
             const int z = (int)fastdiv_u31((uint32_t)tt, p.div_dwt);
-            float* const out = static_cast<float*>(p.ff) + (int64_t)z * M * N;
-            const int fw = n0 + wf * WF;
+            float* const blk = static_cast<float*>(p.ff) +
+                               (((int64_t)z * p.dw_tiles_t + trow_cur) * p.tiles_n + tf) * (int64_t)(BT * BF);
 #pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-                const int row = tw0 + 32 * j + (lane & 31);
-                if (row >= M) continue;
+            for (int a = 0; a < TI; ++a) {
 #pragma unroll
-                for (int G = 0; G < NG; ++G) {
-                    const int col = fw + 8 * G + 4 * hl;
-                    if (col >= N) continue;   // N is a multiple of 8
-                    const f32x4 v = {acc[G >> 2][j][4 * (G & 3)], acc[G >> 2][j][4 * (G & 3) + 1],
-                                     acc[G >> 2][j][4 * (G & 3) + 2], acc[G >> 2][j][4 * (G & 3) + 3]};
-                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out + (int64_t)row * N + col));
+                for (int j = 0; j < TJ; ++j) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int chunk = ((wave * TI + a) * TJ + j) * 4 + q;
+                        const f32x4 v = {acc[a][j][4 * q], acc[a][j][4 * q + 1], acc[a][j][4 * q + 2],
+                                         acc[a][j][4 * q + 3]};
+                        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(blk + chunk * 256 + lane * 4));
+                    }
                 }
             }
         } else {
@@ -968,9 +975,12 @@ hipError_t dispatch_part(int dg, int epi, bool x_tl, bool w_fc, const KernelArgs
         if (dg == 0 && epi == kEpiRope8) return dispatch_fast_layouts<0, T, kEpiRope8>(x_tl, w_fc, a, grid, s);
         if (dg == 0 && epi == kEpiGrad) return dispatch_fast_layouts<0, T, kEpiGrad>(x_tl, w_fc, a, grid, s);
     } else {
-        if (dg == 0 && epi == kEpiDwPartial && !w_fc)
+        // [N, K] weights: the input gradient's contraction ranges (x token-major)
+        if (dg == 0 && epi == kEpiDwPartial) {
+            if (w_fc) return x_tl ? launch_fast_one<true, true, 0, T, kEpiDwPartial>(a, grid, s) : hipErrorInvalidValue;
             return x_tl ? launch_fast_one<true, false, 0, T, kEpiDwPartial>(a, grid, s)
                         : launch_fast_one<false, false, 0, T, kEpiDwPartial>(a, grid, s);
+        }
     }
     return hipErrorInvalidValue;
 }

@@ -145,7 +145,8 @@ struct BwdArgs {
     void* dy;            // workspace: gradient of the fused output, [M, F] token-major, storage type
     float* dbp;          // workspace: [dy tiles_m, F] fp32 column sums of dy per token tile, or null
     void* dw;            // dW in W's layout (written by the dW kernel when splits == 1)
-    float* dwp;          // workspace: [splits, C, F] fp32 partial sums of dW (splits > 1)
+    float* dwp;          // workspace: fp32 partial sums of dW: [splits, C, F] from the dW tile kernel
+                         // (splits > 1), whole 256 x 256 blocks in accumulator order from the fast one
     void* db;            // [F] or null
     int32_t ff_cf;       // d_ff channels-first
     int32_t w_fc;        // W (and dW) stored [F, C]
@@ -154,8 +155,15 @@ struct BwdArgs {
     int32_t dw_tiles_m;  // 128 x 128 tiles over [C, F]
     int32_t dw_tiles_n;
     int32_t db_tiles;    // rows of dbp
-    int32_t dw_partials; // dW always goes through dwp (the fast kernel's fp32 partial sums)
+    int32_t dw_partials; // dW goes through dwp in the fast kernel's block order
     int32_t dy_col_tile0;// the dy kernel's first 128-column tile (the fast kernel did the ones before)
+    // dx's last tokens when their tiles go through contraction ranges (dx_splits > 1)
+    float* dxp;          // workspace: fp32 partial sums, [dx_splits][token tiles][C tiles] blocks
+    void* dx;            // dx in x's layout
+    int32_t dx_row0;     // the first of those tokens (a whole number of slabs for a channels-first x)
+    int32_t dx_rows;     // how many (a multiple of 64 for a channels-first x)
+    int32_t dx_splits;
+    int32_t dx_cf;       // x and dx channels-first (then S is a multiple of 64)
 };
 
 // K step of the 128 x 128 tile kernels for a storage type.
@@ -166,6 +174,8 @@ hipError_t launch_bwd_dy(DType dt, bool x_tokens_last, bool w_fc, const BwdArgs&
 hipError_t launch_bwd_dw(DType dt, bool x_tokens_last, const BwdArgs& b, hipStream_t stream);
 // Column sums of dy's first ncols columns per 128-token block into dbp.
 hipError_t launch_bwd_colsum(DType dt, const BwdArgs& b, int ncols, hipStream_t stream);
+// Sums dx's partial sums into its last tokens (bf16).
+hipError_t launch_bwd_reduce_dx(const BwdArgs& b, hipStream_t stream);
 // Sums the dW partials (splits > 1) into dW and the dy column sums into db (when db).
 hipError_t launch_bwd_reduce(DType dt, const BwdArgs& b, hipStream_t stream);
 // Writes zeros to n bytes at p (n a multiple of 4; a kernel, not a memset node).

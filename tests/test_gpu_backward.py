@@ -126,6 +126,23 @@ def test_backward_split_token_ranges(wl):
     _check(wl, wl.name)
 
 
+DX_SPLIT = [
+    # dx's large tiles one or two past a whole round: the last token tiles go through ranges
+    # of the fused columns and a reduction. Token-major, 129 token tiles x 2 channel tiles
+    # (the tail is the last tile row, 16 ranges); channels-first with 320-token slabs, 258
+    # token tiles (the last one ragged) x 1 (the head keeps whole slabs: 255 tile rows; the
+    # tail, 640 tokens in 11 ranges, is stored per slab)
+    with_shape(WORKLOADS["bert_ff_bf16"], "bwd_dx_split_tl", x_shape=(3, 11008, 512), ff_dim=2048, seed=405),
+    with_shape(WORKLOADS["walrus_bf16"], "bwd_dx_split_cf", x_shape=(206, 256, 320), ff_dim=1024, n_heads=2,
+               head_dim=64, seed=406),
+]
+
+
+@pytest.mark.parametrize("wl", DX_SPLIT, ids=[w.name for w in DX_SPLIT])
+def test_backward_dx_last_tiles_in_ranges(wl):
+    _check(wl, wl.name)
+
+
 def test_backward_strided_channel_slice_view():
     """x as a channel slice of a wider tensor: the backward reads it in place; dx is dense."""
     wl = with_shape(WORKLOADS["walrus_bf16"], "bwd_view", x_shape=(2, 48, 8, 16, 1), ff_dim=64, n_heads=2,
