@@ -204,6 +204,7 @@ struct fused_proj_plan {
     fp::KernelArgs dy_args{};            // its arguments but the per-call pointers
     fp::TilePlan dy_tile{};
     unsigned* d_desc_dy = nullptr;       // its column descriptors
+    bool dy_heads = false;               // dy's q/k/v columns by the heads kernel
     bool fast_dw = false;                // dW on the fast kernel (else the dW tile kernel)
     bool dw_x_kmajor = false;            // ... reading x as K-major rows (channels-first x)
     fp::KernelArgs dw_args{};            // its arguments but the per-call pointers
@@ -405,6 +406,11 @@ int plan_backward(fused_proj_plan* h) {
         h->fast_dy = true;
         b.dy_col_tile0 = (int32_t)(d.ff_dim / 128);
     }
+    // dy's q/k/v columns (bf16) from the head gradients alone, in a streaming kernel: the
+    // tile kernel keeps the column tiles holding ff columns
+    b.dy_col_tile1 = b.f.tiles_n;
+    h->dy_heads = h->dt == fp::DType::BF16 && r.qw > 0 && !want_general;
+    if (h->dy_heads) b.dy_col_tile1 = (int32_t)((d.ff_dim + 127) / 128);
 
     // dW on the fast kernel (bf16): rows are channels, the contraction runs over the tokens,
     // and the work is split into (256-row tile, token range) units whose fp32 partial sums
@@ -854,6 +860,7 @@ int fused_proj_backward(fused_proj_t h, const void* x, const void* w, const void
             e = fp::launch_fused_proj_fast(h->x_tl, h->w_fc, 0, 5, h->dy_tile, a, s);
         }
         if (e == hipSuccess) e = fp::launch_bwd_dy(h->dt, h->x_tl, h->w_fc, b, s);
+        if (e == hipSuccess && h->dy_heads) e = fp::launch_bwd_dy_heads(b, b.dy_col_tile1 * 128, s);
         if (e == hipSuccess && h->fast_dy) e = fp::launch_bwd_colsum(h->dt, b, b.dy_col_tile0 * 128, s);
         if (e == hipSuccess && has_c && !h->dx_split) {
             const int rc = fused_proj_run(h->dx_plan, b.dy, w, nullptr, dx, nullptr, nullptr, nullptr, stream);

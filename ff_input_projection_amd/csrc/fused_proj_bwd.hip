@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dy_kernel(BwdArgs b) {
     const KernelArgs& p = b.f;
 
     int tm, tn;
-    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n - b.dy_col_tile0, p.group_m, tm, tn);
+    tile_coords(blockIdx.x, p.tiles_m, b.dy_col_tile1 - b.dy_col_tile0, p.group_m, tm, tn);
     tn += b.dy_col_tile0;
     const int m0 = tm * BT, n0 = tn * BT;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -234,6 +234,88 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dy_kernel(BwdArgs b) {
         float sum = 0.0f;
         for (int r = 0; r < rows; ++r) sum += Cs[r * CST + tid];
         b.dbp[(int64_t)tm * N + n0 + tid] = sum;
+    }
+}
+
+// dy's q/k/v columns [col0, F) alone (bf16): the upstream head gradients rotated back,
+// no product and no LDS tile. Workgroup: 128 tokens x 128 columns; thread (token lane tl,
+// group gi) takes the 8 columns col0 + 128 blockIdx.x + 8 gi of tokens tl, tl + 16, ...
+// (16 threads store a token's 256 contiguous bytes), then the workgroup's column sums over
+// its 128 tokens meet in LDS (one dbp row per 128-token block, as the tile kernel's).
+__global__ __launch_bounds__(256) void bwd_dy_heads_kernel(BwdArgs b, int col0) {
+    using T = __bf16;
+    constexpr int OV = 8;
+    __shared__ float part[16][BT + 4];
+    const KernelArgs& p = b.f;
+    const int gi = threadIdx.x & 15, tl = threadIdx.x >> 4;
+    const int M = (int)p.M, N = p.N, S = p.S;
+    const int f0 = col0 + (int)blockIdx.x * BT + gi * OV;
+    const int m0 = (int)blockIdx.y * BT;
+    const bool col_ok = f0 < N;
+    float sum[OV];
+#pragma unroll
+    for (int e = 0; e < OV; ++e) sum[e] = 0.0f;
+    if (col_ok) {
+        int kind = 0, h = 0, j0 = 0;
+        column_group(p, f0, kind, h, j0);
+        const int hd = p.head_dim, heads = kind == 1 ? p.n_heads : p.n_kv_heads;
+        const T* src = static_cast<const T*>(kind == 1 ? b.dq : kind == 2 ? b.dk : b.dv);
+        const int rd = p.rope_dims, half = rd >> 1;
+        const bool do_rope = p.rope && kind != 3 && j0 < rd;
+        const bool vec_rope = do_rope && half % OV == 0;
+        const bool first_half = j0 < half;
+        const int i0 = first_half ? j0 : j0 - half;
+        T* const dy = static_cast<T*>(b.dy);
+        for (int k = 0; k < BT / 16; ++k) {
+            const int m = m0 + tl + 16 * k;
+            if (m >= M) break;
+            const int bi = m / S, s = m - bi * S;
+            const T* const hrow = src + ((int64_t)(bi * heads + h) * S + s) * hd;
+            float gv[OV], out[OV];
+            load16<T>(hrow + j0, gv);
+            if (vec_rope) {
+                // the partner chunk half a rotated width away, one angle per pair
+                float pv[OV];
+                load16<T>(hrow + (first_half ? j0 + half : j0 - half), pv);
+                const f32x4* cs = reinterpret_cast<const f32x4*>(p.rope_cos + (int64_t)s * half + i0);
+                const f32x4* sn = reinterpret_cast<const f32x4*>(p.rope_sin + (int64_t)s * half + i0);
+                const f32x4 c0 = cs[0], c1 = cs[1], s0 = sn[0], s1 = sn[1];
+                const float cv[OV] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                const float sv[OV] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+                for (int e = 0; e < OV; ++e)
+                    out[e] = first_half ? gv[e] * cv[e] + pv[e] * sv[e] : gv[e] * cv[e] - pv[e] * sv[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < OV; ++e) {
+                    const int j = j0 + e;
+                    out[e] = gv[e];
+                    if (do_rope && j < rd) {
+                        const bool fh = j < half;
+                        const int i = fh ? j : j - half;
+                        const float pe = (float)hrow[fh ? j + half : j - half];
+                        const float c = p.rope_cos[(int64_t)s * half + i];
+                        const float sv = p.rope_sin[(int64_t)s * half + i];
+                        out[e] = fh ? gv[e] * c + pe * sv : gv[e] * c - pe * sv;
+                    }
+                }
+            }
+            store16<T>(dy + (int64_t)m * N + f0, out);
+#pragma unroll
+            for (int e = 0; e < OV; ++e) sum[e] += out[e];
+        }
+    }
+    if (b.dbp == nullptr) return;
+#pragma unroll
+    for (int e = 0; e < OV; ++e) part[tl][gi * OV + e] = sum[e];
+    __syncthreads();
+    const int c = (int)threadIdx.x;
+    const int f = col0 + (int)blockIdx.x * BT + c;
+    if (c < BT && f < N) {
+        float t = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t += part[r][c];
+        b.dbp[(int64_t)blockIdx.y * N + f] = t;
     }
 }
 
@@ -578,7 +660,7 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(unsigned* p, size_t n) {
 template <typename T, bool A_KM, bool B_KM>
 hipError_t launch_dy_one(const BwdArgs& b, hipStream_t s) {
     constexpr int BK = sizeof(T) == 2 ? 64 : 32;
-    const unsigned grid = (unsigned)b.f.tiles_m * (unsigned)(b.f.tiles_n - b.dy_col_tile0);
+    const unsigned grid = (unsigned)b.f.tiles_m * (unsigned)(b.dy_col_tile1 - b.dy_col_tile0);
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dy_kernel<T, A_KM, B_KM, BK>), dim3(grid), dim3(kThreads), 0, s, b);
     return hipGetLastError();
@@ -677,6 +759,13 @@ hipError_t launch_bwd_reduce_dx(const BwdArgs& b, hipStream_t s) {
         tr.ld = b.f.K;
     }
     return launch_reduce_tiles<__bf16>(tr, s);
+}
+
+hipError_t launch_bwd_dy_heads(const BwdArgs& b, int col0, hipStream_t s) {
+    if (col0 >= b.f.N || b.f.M <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((b.f.N - col0 + BT - 1) / BT), (unsigned)((b.f.M + BT - 1) / BT));
+    hipLaunchKernelGGL(bwd_dy_heads_kernel, grid, dim3(256), 0, s, b, col0);
+    return hipGetLastError();
 }
 
 hipError_t launch_bwd_colsum(DType dt, const BwdArgs& b, int ncols, hipStream_t s) {

@@ -156,7 +156,8 @@ struct BwdArgs {
     int32_t dw_tiles_n;
     int32_t db_tiles;    // rows of dbp
     int32_t dw_partials; // dW goes through dwp in the fast kernel's block order
-    int32_t dy_col_tile0;// the dy kernel's first 128-column tile (the fast kernel did the ones before)
+    int32_t dy_col_tile0;// the dy tile kernel's 128-column tiles [dy_col_tile0, dy_col_tile1): the fast
+    int32_t dy_col_tile1;// kernel did the ones before, the heads kernel (bf16) the q/k/v ones after
     // dx's last tokens when their tiles go through contraction ranges (dx_splits > 1)
     float* dxp;          // workspace: fp32 partial sums, [dx_splits][token tiles][C tiles] blocks
     void* dx;            // dx in x's layout
@@ -168,8 +169,10 @@ struct BwdArgs {
 
 // K step of the 128 x 128 tile kernels for a storage type.
 int tile_bk(DType dt);
-// The dy kernel: grid b.f.tiles_m x b.f.tiles_n (128 x 128 tiles over [M, F]).
+// The dy kernel: 128 x 128 tiles over [M, F], column tiles [dy_col_tile0, dy_col_tile1).
+// The heads kernel (bf16): dy's q/k/v columns [col0, F) from the head gradients alone.
 hipError_t launch_bwd_dy(DType dt, bool x_tokens_last, bool w_fc, const BwdArgs& b, hipStream_t stream);
+hipError_t launch_bwd_dy_heads(const BwdArgs& b, int col0, hipStream_t stream);
 // The dW kernel: grid (dw_tiles_m x dw_tiles_n, splits).
 hipError_t launch_bwd_dw(DType dt, bool x_tokens_last, const BwdArgs& b, hipStream_t stream);
 // Column sums of dy's first ncols columns per 128-token block into dbp.
