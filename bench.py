@@ -192,6 +192,33 @@ def sample_sclk(launch, kernel_us: float, seconds: float = 0.4):
             pass
 
 
+def measure_stream_ceiling(wl, dev, steps, min_warmup_s):
+    """A plain streaming kernel over the workload's bytes, timed like the projection: a row
+    gather (torch.index_select) writing the M output rows of F elements from a buffer as
+    large as the inputs (read once from HBM; the rows it reads again come from the caches).
+    The ceiling that an HBM-bound projection of this size can reach in this harness."""
+    import torch
+
+    es = wl.elem_bytes
+    out_bytes = wl.M * wl.F * es
+    in_rows = max(1, round((wl.alg_bytes - out_bytes) / (wl.F * es)))
+    ring = max(1, min(24, math.ceil(512e6 / wl.alg_bytes)))
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    srcs = [torch.randn(in_rows, wl.F, device=dev).to(dt) for _ in range(ring)]
+    dsts = [torch.empty(wl.M, wl.F, dtype=dt, device=dev) for _ in range(ring)]
+    idx = torch.arange(wl.M, device=dev) % in_rows
+    stream = torch.cuda.current_stream(dev)
+
+    def launch(i):
+        torch.index_select(srcs[i % ring], 0, idx, out=dsts[i % ring])
+
+    t = time_launches(launch, steps, 10, min_warmup_s, stream)
+    moved = in_rows * wl.F * es + out_bytes
+    return {"kernel": "torch.index_select row gather", "read_bytes": in_rows * wl.F * es, "write_bytes": out_bytes,
+            "us_mean": round(t["mean_us"], 2), "us_median": round(t["median_us"], 2),
+            "gb_per_s": round(moved / (t["mean_us"] * 1e-6) / 1e9, 1)}
+
+
 def make_plan(wl, x):
     from ff_input_projection_amd import FusedProjection
 
@@ -475,6 +502,7 @@ def main() -> int:
     # ---- every configuration of the workload table, timed the same way (GPU first;
     # the oracle checks follow on the CPU)
     measured = {wl.name: (t, desc, host, inp)}
+    ceiling = None
     if not args.no_configs:
         for name in CONFIG_WORKLOADS + VARIANT_WORKLOADS:
             if name in measured:
@@ -483,6 +511,9 @@ def main() -> int:
             steps = args.config_steps * (5 if name in ("smallk_qkv_bf16", "gqa_rope8_bf16") else 1)
             ct, cdesc, chost, cinp, _ = measure_workload(cw, dev, steps, 10, min(args.min_warmup_s, 1.0))
             measured[name] = (ct, cdesc, chost, cinp)
+            if name == "smallk_qkv_bf16":
+                ceiling = measure_stream_ceiling(cw, dev, steps, min(args.min_warmup_s, 1.0))
+                print(f"[bench] stream ceiling for {name}: {ceiling}", file=sys.stderr, flush=True)
             print(f"[bench] {name}: mean {ct['mean_us']:.2f} us, median {ct['median_us']:.2f} "
                   f"(p10 {ct['p10_us']:.2f}, p90 {ct['p90_us']:.2f})", file=sys.stderr, flush=True)
 
@@ -543,6 +574,10 @@ def main() -> int:
                  "tflop_per_s": round(c_tflops, 2), "gb_per_s": round(c_gbs, 1), "bound": c_roof["bound"],
                  "frac": c_roof["frac"], "frac_at_median": round(roofline_of(cw, ct["median_us"])[2]["frac"], 4),
                  "kernel": cdesc}
+        if name == "smallk_qkv_bf16" and ceiling is not None:
+            # the same bytes through a plain streaming kernel in this harness
+            entry["stream_ceiling"] = ceiling
+            entry["frac_of_stream_ceiling"] = round(ceiling["us_mean"] / ct["mean_us"], 4)
         if not args.no_cpu_baseline:
             if name == wl.name:
                 entry["parity"] = result["parity"]

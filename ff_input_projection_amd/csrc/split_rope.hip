@@ -23,6 +23,7 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct SplitRopeArgs {
     const __bf16* qkv;       // [b*T, Fq]
@@ -32,9 +33,11 @@ struct SplitRopeArgs {
     const float* rope_cos;   // [T, rd/2]
     const float* rope_sin;
     int64_t Fq;              // (H + 2*KVH) * hd
-    int64_t q_chunks;        // 16-byte chunks of q, and of k (= of v)
+    int64_t q_chunks;        // 16-byte chunks of q, and of k (= of v); all of them fit 31 bits
     int64_t kv_chunks;
     int32_t T, H, KVH, hd, grouped, rope, rd, k_transposed;
+    // the chunk index's divisions, by multiply-high: hd/8, T, H, KVH, T/8, hd
+    fp::FastDivU31 div_c8, div_t, div_h, div_kvh, div_t8, div_hd;
 };
 
 // Column of element j of head h of slice which (0 q, 1 k, 2 v) in a token's row.
@@ -70,64 +73,73 @@ __device__ __forceinline__ float pick8(const bf16x8& v, int idx) {
 }
 
 __global__ __launch_bounds__(256) void split_rope_kernel(SplitRopeArgs p) {
-    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = p.q_chunks + 2 * p.kv_chunks;
-    if (c >= total) return;
-    const int which = c < p.q_chunks ? 0 : c < p.q_chunks + p.kv_chunks ? 1 : 2;
-    const int64_t cc = which == 0 ? c : which == 1 ? c - p.q_chunks : c - p.q_chunks - p.kv_chunks;
+    const uint32_t c = blockIdx.x * 256u + threadIdx.x;
+    const uint32_t qc = (uint32_t)p.q_chunks, kc = (uint32_t)p.kv_chunks;
+    if (c >= qc + 2 * kc) return;
+    const int which = c < qc ? 0 : c < qc + kc ? 1 : 2;
+    const uint32_t cc = which == 0 ? c : which == 1 ? c - qc : c - qc - kc;
     const int heads = which == 0 ? p.H : p.KVH;
+    const fp::FastDivU31 div_heads = which == 0 ? p.div_h : p.div_kvh;
     __bf16* const out = which == 0 ? p.q : which == 1 ? p.k : p.v;
     bf16x8 o;
     if (which == 1 && p.k_transposed) {
         // chunk (slab, j, 8 tokens): k[slab, j, s0 .. s0+7]
-        const int T8 = p.T >> 3;
-        const int sc = (int)(cc % T8);
-        const int64_t sj = cc / T8;
-        const int j = (int)(sj % p.hd);
-        const int64_t slab = sj / p.hd;
-        const int g = (int)(slab % heads);
-        const int64_t bi = slab / heads;
+        const uint32_t sj = fp::fastdiv_u31(cc, p.div_t8);
+        const int sc = (int)(cc - sj * (uint32_t)(p.T >> 3));
+        const uint32_t slab = fp::fastdiv_u31(sj, p.div_hd);
+        const int j = (int)(sj - slab * (uint32_t)p.hd);
+        const uint32_t bi = fp::fastdiv_u31(slab, div_heads);
+        const int g = (int)(slab - bi * (uint32_t)heads);
         const int64_t col = qkv_col(p, 1, g, j);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int s = sc * 8 + e;
-            const __bf16* row = p.qkv + (bi * p.T + s) * p.Fq;
+            const __bf16* row = p.qkv + ((int64_t)bi * p.T + s) * p.Fq;
             o[e] = (__bf16)roped(p, row, 1, g, j, (float)row[col], s);
         }
     } else {
         // chunk (slab, token, 8 elements): out[slab, s, j0 .. j0+7]
-        const int C8 = p.hd >> 3;
-        const int j0 = (int)(cc % C8) * 8;
-        const int64_t st = cc / C8;
-        const int s = (int)(st % p.T);
-        const int64_t slab = st / p.T;
-        const int h = (int)(slab % heads);
-        const int64_t bi = slab / heads;
-        const __bf16* row = p.qkv + (bi * p.T + s) * p.Fq;
+        const uint32_t st = fp::fastdiv_u31(cc, p.div_c8);
+        const int j0 = (int)(cc - st * (uint32_t)(p.hd >> 3)) * 8;
+        const uint32_t slab = fp::fastdiv_u31(st, p.div_t);
+        const int s = (int)(st - slab * (uint32_t)p.T);
+        const uint32_t bi = fp::fastdiv_u31(slab, div_heads);
+        const int h = (int)(slab - bi * (uint32_t)heads);
+        const __bf16* row = p.qkv + ((int64_t)bi * p.T + s) * p.Fq;
         const bf16x8 x = *reinterpret_cast<const bf16x8*>(row + qkv_col(p, which, h, j0));
         const int half = p.rd >> 1;
         if (!p.rope || which == 2 || j0 >= p.rd) {
             o = x;   // v, and elements past the rotated width: copies
-        } else if (p.rd <= 8 || (half & 7) == 0) {
-            // the partners are in this chunk (rotated width up to 8, so j0 = 0) or form one
-            // aligned chunk half a rotated width away (half a multiple of 8: the chunk lies in
-            // one half)
-            const bf16x8 xp = p.rd <= 8 ? x
-                                        : *reinterpret_cast<const bf16x8*>(
-                                              row + qkv_col(p, which, h, j0 < half ? j0 + half : j0 - half));
+        } else if ((half & 7) == 0) {
+            // the chunk lies in one half (half a multiple of 8) and its partners form one
+            // aligned chunk half a rotated width away; its 8 angles are two 16-byte loads
+            const bool first = j0 < half;
+            const int i0 = first ? j0 : j0 - half;
+            const bf16x8 xp = *reinterpret_cast<const bf16x8*>(row + qkv_col(p, which, h, first ? j0 + half : j0 - half));
+            const f32x4* cp = reinterpret_cast<const f32x4*>(p.rope_cos + (int64_t)s * half + i0);
+            const f32x4* sp = reinterpret_cast<const f32x4*>(p.rope_sin + (int64_t)s * half + i0);
+            const f32x4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+            const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int j = j0 + e;
-                if (j >= p.rd) {
+                const float y = (float)x[e], yp = (float)xp[e];
+                o[e] = (__bf16)(first ? y * cv[e] - yp * sv[e] : y * cv[e] + yp * sv[e]);
+            }
+        } else if (p.rd <= 8) {
+            // rotated width up to 8 (so j0 = 0): the partners are in this chunk
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (e >= p.rd) {
                     o[e] = x[e];
                     continue;
                 }
-                const bool first = j < half;
-                const int i = first ? j : j - half;
-                const float yp = p.rd <= 8 ? pick8(xp, first ? e + half : e - half) : (float)xp[e];
-                const float c = p.rope_cos[(int64_t)s * half + i], sn = p.rope_sin[(int64_t)s * half + i];
+                const bool first = e < half;
+                const int i = first ? e : e - half;
+                const float yp = pick8(x, first ? e + half : e - half);
+                const float cs = p.rope_cos[(int64_t)s * half + i], sn = p.rope_sin[(int64_t)s * half + i];
                 const float y = (float)x[e];
-                o[e] = (__bf16)(first ? y * c - yp * sn : y * c + yp * sn);
+                o[e] = (__bf16)(first ? y * cs - yp * sn : y * cs + yp * sn);
             }
         } else {
 #pragma unroll
@@ -269,6 +281,12 @@ int split_rope_run(split_rope_t h, const void* qkv, void* q, void* k, void* v, v
     a.rope = h->d.rope ? 1 : 0;
     a.rd = (int32_t)r.rd;
     a.k_transposed = h->d.k_transposed ? 1 : 0;
+    a.div_c8 = fp::make_fastdiv_u31((uint32_t)(a.hd / 8));
+    a.div_t = fp::make_fastdiv_u31((uint32_t)a.T);
+    a.div_h = fp::make_fastdiv_u31((uint32_t)a.H);
+    a.div_kvh = fp::make_fastdiv_u31((uint32_t)a.KVH);
+    a.div_t8 = fp::make_fastdiv_u31((uint32_t)(a.T / 8));
+    a.div_hd = fp::make_fastdiv_u31((uint32_t)a.hd);
     const int64_t blocks = (total + 255) / 256;
     hipLaunchKernelGGL(split_rope_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                        a);

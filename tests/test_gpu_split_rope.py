@@ -23,6 +23,8 @@ CASES = [
     (2, 48, 6, 2, 32, "contiguous", 16, True, 0, 11),    # grouped-query, contiguous, partial, K^T
     (1, 24, 8, 1, 16, "grouped", 0, False, 2, 12),       # multi-query, full rotation
     (2, 16, 4, 2, 24, "grouped", 6, False, 0, 13),       # rotated half (3) not a multiple of anything
+    (2, 40, 4, 2, 128, "contiguous", 0, False, 3, 14),   # head size 128, full rotation
+    (1, 64, 4, 4, 64, "grouped", 32, True, 0, 15),       # half the head rotated, K^T
 ]
 
 
