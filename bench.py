@@ -192,31 +192,31 @@ def sample_sclk(launch, kernel_us: float, seconds: float = 0.4):
             pass
 
 
-def measure_stream_ceiling(wl, dev, steps, min_warmup_s):
-    """A plain streaming kernel over the workload's bytes, timed like the projection: a row
-    gather (torch.index_select) writing the M output rows of F elements from a buffer as
-    large as the inputs (read once from HBM; the rows it reads again come from the caches).
-    The ceiling that an HBM-bound projection of this size can reach in this harness."""
+def measure_stream_ceiling(dev, read_bytes, write_bytes, row_elems, dtype, steps, min_warmup_s):
+    """A plain streaming kernel over the same bytes as a memory-bound launch, timed the same
+    way: a row gather (torch.index_select) writing rows of row_elems elements from a buffer
+    of read_bytes (read once from HBM; rows it reads again come from the caches). The
+    ceiling an HBM-bound kernel of this size reaches in this harness."""
     import torch
 
-    es = wl.elem_bytes
-    out_bytes = wl.M * wl.F * es
-    in_rows = max(1, round((wl.alg_bytes - out_bytes) / (wl.F * es)))
-    ring = max(1, min(24, math.ceil(512e6 / wl.alg_bytes)))
-    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    srcs = [torch.randn(in_rows, wl.F, device=dev).to(dt) for _ in range(ring)]
-    dsts = [torch.empty(wl.M, wl.F, dtype=dt, device=dev) for _ in range(ring)]
-    idx = torch.arange(wl.M, device=dev) % in_rows
+    es = 2 if dtype == "bf16" else 4
+    out_rows = max(1, int(write_bytes) // (row_elems * es))
+    in_rows = max(1, round(read_bytes / (row_elems * es)))
+    ring = max(1, min(24, math.ceil(512e6 / (read_bytes + write_bytes))))
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    srcs = [torch.randn(in_rows, row_elems, device=dev).to(dt) for _ in range(ring)]
+    dsts = [torch.empty(out_rows, row_elems, dtype=dt, device=dev) for _ in range(ring)]
+    idx = torch.arange(out_rows, device=dev) % in_rows
     stream = torch.cuda.current_stream(dev)
 
     def launch(i):
         torch.index_select(srcs[i % ring], 0, idx, out=dsts[i % ring])
 
     t = time_launches(launch, steps, 10, min_warmup_s, stream)
-    moved = in_rows * wl.F * es + out_bytes
-    return {"kernel": "torch.index_select row gather", "read_bytes": in_rows * wl.F * es, "write_bytes": out_bytes,
-            "us_mean": round(t["mean_us"], 2), "us_median": round(t["median_us"], 2),
-            "gb_per_s": round(moved / (t["mean_us"] * 1e-6) / 1e9, 1)}
+    moved = (in_rows + out_rows) * row_elems * es
+    return {"kernel": "torch.index_select row gather", "read_bytes": in_rows * row_elems * es,
+            "write_bytes": out_rows * row_elems * es, "us_mean": round(t["mean_us"], 2),
+            "us_median": round(t["median_us"], 2), "gb_per_s": round(moved / (t["mean_us"] * 1e-6) / 1e9, 1)}
 
 
 def make_plan(wl, x):
@@ -512,7 +512,9 @@ def main() -> int:
             ct, cdesc, chost, cinp, _ = measure_workload(cw, dev, steps, 10, min(args.min_warmup_s, 1.0))
             measured[name] = (ct, cdesc, chost, cinp)
             if name == "smallk_qkv_bf16":
-                ceiling = measure_stream_ceiling(cw, dev, steps, min(args.min_warmup_s, 1.0))
+                out_b = cw.M * cw.F * cw.elem_bytes
+                ceiling = measure_stream_ceiling(dev, int(cw.alg_bytes - out_b), out_b, cw.F, cw.dtype, steps,
+                                                 min(args.min_warmup_s, 1.0))
                 print(f"[bench] stream ceiling for {name}: {ceiling}", file=sys.stderr, flush=True)
             print(f"[bench] {name}: mean {ct['mean_us']:.2f} us, median {ct['median_us']:.2f} "
                   f"(p10 {ct['p10_us']:.2f}, p90 {ct['p90_us']:.2f})", file=sys.stderr, flush=True)
@@ -641,6 +643,11 @@ def bench_split_rope(args, wl) -> int:
         "launch_us": {k: (round(v, 2) if isinstance(v, float) else v) for k, v in t.items()},
         "kernel": "split_rope_kernel", "kernel_hash": kernel_hash(),
     }
+    # the same bytes through a plain streaming kernel in this harness
+    qkv_b = 2 * wl.batch * wl.tokens * wl.Fq
+    ceiling = measure_stream_ceiling(dev, qkv_b, qkv_b, wl.Fq, "bf16", args.steps, min(args.min_warmup_s, 1.0))
+    result["stream_ceiling"] = ceiling
+    result["frac_of_stream_ceiling"] = round(ceiling["us_mean"] / us, 4)
     if not args.no_cpu_baseline:
         import oracle
 

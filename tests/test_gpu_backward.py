@@ -133,6 +133,9 @@ DX_SPLIT = [
     # token tiles (the last one ragged) x 1 (the head keeps whole slabs: 255 tile rows; the
     # tail, 640 tokens in 11 ranges, is stored per slab)
     with_shape(WORKLOADS["bert_ff_bf16"], "bwd_dx_split_tl", x_shape=(3, 11008, 512), ff_dim=2048, seed=405),
+    # ... with W stored [F, C] (the ranges then read W as [F, C] rows)
+    with_shape(WORKLOADS["bert_ff_bf16"], "bwd_dx_split_tl_fc", x_shape=(3, 11008, 512), ff_dim=2048, w_layout="fc",
+               seed=407),
     with_shape(WORKLOADS["walrus_bf16"], "bwd_dx_split_cf", x_shape=(206, 256, 320), ff_dim=1024, n_heads=2,
                head_dim=64, seed=406),
 ]
