@@ -346,7 +346,7 @@ int plan_backward(fused_proj_plan* h) {
     b.w_fc = d.w_layout == FUSED_PROJ_W_FC ? 1 : 0;
     b.dw_tiles_m = (int32_t)((d.channels + 127) / 128);
     b.dw_tiles_n = b.f.tiles_n;
-    b.db_tiles = b.f.tiles_m;
+    b.db_tiles = (int32_t)((r.M + 31) / 32);   // one row of column sums per 32 tokens
     // dW contracts over the tokens: split them into ranges when the dW tiles alone
     // cannot fill the CUs (two workgroups each), at most 16 ranges
     const int64_t dw_tiles = (int64_t)b.dw_tiles_m * b.dw_tiles_n;
@@ -405,6 +405,8 @@ int plan_backward(fused_proj_plan* h) {
         h->dy_tile = tp;
         h->fast_dy = true;
         b.dy_col_tile0 = (int32_t)(d.ff_dim / 128);
+        // it writes the column sums of the 128-column tiles it covers entirely
+        h->dy_args.colsum_cols = b.dy_col_tile0 * 128;
     }
     // dy's q/k/v columns (bf16) from the head gradients alone, in a streaming kernel: the
     // tile kernel keeps the column tiles holding ff columns
@@ -857,11 +859,11 @@ int fused_proj_backward(fused_proj_t h, const void* x, const void* w, const void
             a.bias = d.has_bias ? bias : nullptr;
             a.ff = b.dy;
             a.grad_in = d_ff;
+            a.colsum = b.dbp;
             e = fp::launch_fused_proj_fast(h->x_tl, h->w_fc, 0, 5, h->dy_tile, a, s);
         }
         if (e == hipSuccess) e = fp::launch_bwd_dy(h->dt, h->x_tl, h->w_fc, b, s);
         if (e == hipSuccess && h->dy_heads) e = fp::launch_bwd_dy_heads(b, b.dy_col_tile1 * 128, s);
-        if (e == hipSuccess && h->fast_dy) e = fp::launch_bwd_colsum(h->dt, b, b.dy_col_tile0 * 128, s);
         if (e == hipSuccess && has_c && !h->dx_split) {
             const int rc = fused_proj_run(h->dx_plan, b.dy, w, nullptr, dx, nullptr, nullptr, nullptr, stream);
             if (rc) return rc;

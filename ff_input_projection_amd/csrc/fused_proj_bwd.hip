@@ -10,22 +10,27 @@
 //   dy[t, v head columns] = upstream v gradient
 //   dx = dy W^T (in x's layout), dW = X^T dy, db = column sums of dy.
 //
-// Launches, all on the caller's stream:
-//   1. bwd_dy_kernel: 128 x 128 tiles over [M, F]. Tiles holding ff columns with an
-//      activation recompute y with the same MFMA K loop as the forward general kernel;
-//      the epilogue turns each tile into dy in LDS (loading the upstream gradients as
-//      16-byte chunks), stores it token-major into the workspace and writes the tile's
-//      fp32 column sums (for db).
-//   2. dx: a forward projection planned by the C-ABI layer (dy as a token-major
+// Launches, all on the caller's stream (the fast kernel's variants take some of them
+// for bf16; the C-ABI layer plans which):
+//   1. dy's ff columns: the fast kernel's grad epilogue (bf16, an activation, token-major
+//      d_ff; it writes their column sums too), or bwd_dy_kernel: 128 x 128
+//      tiles over [M, F]; tiles holding ff columns with an activation recompute y with
+//      the same MFMA K loop as the forward general kernel; the epilogue turns each tile
+//      into dy in LDS (loading the upstream gradients as 16-byte chunks), stores it
+//      token-major into the workspace and writes the tile's fp32 column sums (for db).
+//   2. dy's q/k/v columns: bwd_dy_heads_kernel (bf16; a streaming kernel, no product),
+//      or bwd_dy_kernel's tiles.
+//   3. dx: a forward projection planned by the C-ABI layer (dy as a token-major
 //      activation, W read transposed, the result as an "ff" slice laid out like x). When
 //      its tiles would leave most CUs idle in a last round, the last token tiles are
 //      contracted in ranges of the fused columns into fp32 partial sums, and
 //      bwd_reduce_tiles_kernel sums them into dx.
-//   3. bwd_dw_kernel: 128 x 128 tiles over [C, F] contracted over tokens, split into
-//      token ranges when the tiles alone cannot fill the CUs; x is read in place in its
-//      own layout (channels-first: 16-byte runs of tokens; token-major: runs of
-//      channels), dy as [tokens, F].
-//   4. bwd_reduce_tiles_kernel (the fast kernel's partial sums, in its accumulator order)
+//   4. dW: the fast kernel's (row tile, token range) units (bf16), or bwd_dw_kernel:
+//      128 x 128 tiles over [C, F] contracted over tokens, split into token ranges when
+//      the tiles alone cannot fill the CUs; x is read in place in its own layout
+//      (channels-first: 16-byte runs of tokens; token-major: runs of channels), dy as
+//      [tokens, F].
+//   5. bwd_reduce_tiles_kernel (the fast kernel's partial sums, in its accumulator order)
 //      or bwd_reduce_dw_kernel (the dW tile kernel's [splits, C, F]) into dW in W's layout,
 //      and bwd_reduce_db_kernel: the column sums into db.
 #include "general_tile.h"
@@ -230,18 +235,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dy_kernel(BwdArgs b) {
         }
     }
     if (b.dbp != nullptr && tid < BT && n0 + tid < N) {
+        // one dbp row per 32 tokens (the rows that exist)
         const int rows = M - m0 < BT ? M - m0 : BT;
-        float sum = 0.0f;
-        for (int r = 0; r < rows; ++r) sum += Cs[r * CST + tid];
-        b.dbp[(int64_t)tm * N + n0 + tid] = sum;
+        for (int q = 0; q * 32 < rows; ++q) {
+            float sum = 0.0f;
+            const int rend = rows < 32 * q + 32 ? rows : 32 * q + 32;
+            for (int r = 32 * q; r < rend; ++r) sum += Cs[r * CST + tid];
+            b.dbp[(int64_t)(m0 / 32 + q) * N + n0 + tid] = sum;
+        }
     }
 }
 
 // dy's q/k/v columns [col0, F) alone (bf16): the upstream head gradients rotated back,
 // no product and no LDS tile. Workgroup: 128 tokens x 128 columns; thread (token lane tl,
-// group gi) takes the 8 columns col0 + 128 blockIdx.x + 8 gi of tokens tl, tl + 16, ...
-// (16 threads store a token's 256 contiguous bytes), then the workgroup's column sums over
-// its 128 tokens meet in LDS (one dbp row per 128-token block, as the tile kernel's).
+// group gi) takes the 8 columns col0 + 128 blockIdx.x + 8 gi of the 8 tokens 8 tl .. 8 tl
+// + 7 (16 threads store a token's 256 contiguous bytes), then the column sums of each
+// 32-token block meet in LDS (one dbp row per 32 tokens, as everywhere).
 __global__ __launch_bounds__(256) void bwd_dy_heads_kernel(BwdArgs b, int col0) {
     using T = __bf16;
     constexpr int OV = 8;
@@ -267,7 +276,7 @@ __global__ __launch_bounds__(256) void bwd_dy_heads_kernel(BwdArgs b, int col0) 
         const int i0 = first_half ? j0 : j0 - half;
         T* const dy = static_cast<T*>(b.dy);
         for (int k = 0; k < BT / 16; ++k) {
-            const int m = m0 + tl + 16 * k;
+            const int m = m0 + 8 * tl + k;
             if (m >= M) break;
             const int bi = m / S, s = m - bi * S;
             const T* const hrow = src + ((int64_t)(bi * heads + h) * S + s) * hd;
@@ -309,13 +318,15 @@ __global__ __launch_bounds__(256) void bwd_dy_heads_kernel(BwdArgs b, int col0) 
 #pragma unroll
     for (int e = 0; e < OV; ++e) part[tl][gi * OV + e] = sum[e];
     __syncthreads();
-    const int c = (int)threadIdx.x;
+    // thread (q, c): column c of 32-token block q (token lanes 4q .. 4q + 3)
+    const int c = (int)threadIdx.x & (BT - 1), q = (int)threadIdx.x >> 7;
     const int f = col0 + (int)blockIdx.x * BT + c;
-    if (c < BT && f < N) {
-        float t = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) t += part[r][c];
-        b.dbp[(int64_t)blockIdx.y * N + f] = t;
+    if (f < N) {
+        for (int qq = q; qq < 4; qq += 2) {
+            if (m0 + 32 * qq >= M) break;
+            const float t = (part[4 * qq][c] + part[4 * qq + 1][c]) + (part[4 * qq + 2][c] + part[4 * qq + 3][c]);
+            b.dbp[(int64_t)(m0 / 32 + qq) * N + f] = t;
+        }
     }
 }
 
@@ -632,27 +643,6 @@ __global__ __launch_bounds__(256) void bwd_reduce_db_kernel(BwdArgs b) {
         static_cast<T*>(b.db)[f] = (T)((part[0][fx] + part[1][fx]) + (part[2][fx] + part[3][fx]));
 }
 
-// Column sums of dy (storage type, [M, N]) over 128-token blocks: dbp[block][f] for
-// f < ncols. Workgroup (64 columns, one block): four rows of 64 columns per step, then the
-// four partial sums in LDS.
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_colsum_kernel(BwdArgs b, int ncols) {
-    __shared__ float part[4][64];
-    const int N = b.f.N, M = (int)b.f.M;
-    const int fx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    const int f = blockIdx.x * 64 + fx, r0 = blockIdx.y * BT;
-    const T* dy = static_cast<const T*>(b.dy);
-    float sum = 0.0f;
-    if (f < ncols) {
-        const int rend = r0 + BT < M ? r0 + BT : M;
-#pragma unroll 4
-        for (int r = r0 + ty; r < rend; r += 4) sum += (float)dy[(int64_t)r * N + f];
-    }
-    part[ty][fx] = sum;
-    __syncthreads();
-    if (ty == 0 && f < ncols) b.dbp[(int64_t)blockIdx.y * N + f] = (part[0][fx] + part[1][fx]) + (part[2][fx] + part[3][fx]);
-}
-
 __global__ __launch_bounds__(256) void zero_fill_kernel(unsigned* p, size_t n) {
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
 }
@@ -768,15 +758,6 @@ hipError_t launch_bwd_dy_heads(const BwdArgs& b, int col0, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_colsum(DType dt, const BwdArgs& b, int ncols, hipStream_t s) {
-    if (ncols <= 0 || b.dbp == nullptr) return hipSuccess;
-    const dim3 grid((unsigned)((ncols + 63) / 64), (unsigned)b.db_tiles);
-    if (dt == DType::BF16)
-        hipLaunchKernelGGL((bwd_colsum_kernel<__bf16>), grid, dim3(256), 0, s, b, ncols);
-    else
-        hipLaunchKernelGGL((bwd_colsum_kernel<float>), grid, dim3(256), 0, s, b, ncols);
-    return hipGetLastError();
-}
 
 hipError_t launch_zero_fill(void* p, size_t n, hipStream_t s) {
     const size_t words = n / 4;

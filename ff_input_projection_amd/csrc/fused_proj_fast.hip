@@ -764,6 +764,11 @@ fused_proj_fast_kernel(KernelArgs p) {
         load_rope(0, 0);
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
+            // grad epilogue: column sums of the stored dy over this lane's rows of the block
+            // (its 8-column chunk gl of token rows r0, r0 + 4, ... of both half blocks), for db
+            float csum[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) csum[e] = 0.0f;
             // every group's outputs rounded to bf16 (each branch packs its own results:
             // results written back into acc under these branches would cost a register
             // copy per value where the branches join)
@@ -904,6 +909,30 @@ fused_proj_fast_kernel(KernelArgs p) {
                                       : one_slab            ? row0_l + (u + (unsigned)(4 * rr) * stride_l)
                                                             : base_l + token_off(t0 + r);
                     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+                    if constexpr (EPI == kEpiGrad) {
+                        if (r < rows) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                csum[2 * e] += __uint_as_float(v[e] << 16);
+                                csum[2 * e + 1] += __uint_as_float(v[e] & 0xffff0000u);
+                            }
+                        }
+                    }
+                }
+            }
+            if constexpr (EPI == kEpiGrad) {
+                // the four lanes of a chunk (lane bits 4 and 5) add up their rows: the block's
+                // 32 tokens; lanes 0-15 store the chunk's 8 sums into the block's row
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    csum[e] += __shfl_xor(csum[e], 16);
+                    csum[e] += __shfl_xor(csum[e], 32);
+                }
+                const int c0 = fw + 8 * gl, tb = tw0 + 32 * j;
+                if (p.colsum != nullptr && r0 == 0 && tb < M && c0 < p.colsum_cols) {
+                    float* const dst = p.colsum + (int64_t)(tb / 32) * ffr + c0;
+                    *reinterpret_cast<f32x4*>(dst) = f32x4{csum[0], csum[1], csum[2], csum[3]};
+                    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{csum[4], csum[5], csum[6], csum[7]};
                 }
             }
         }

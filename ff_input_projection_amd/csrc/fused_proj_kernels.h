@@ -79,6 +79,10 @@ struct KernelArgs {
     int32_t w_ld;
     int32_t ff_ld;
     const void* grad_in;
+    // ... and where dy's column sums go: [M/32 rows, ff_ld] fp32, one row per 32 tokens,
+    // for columns below colsum_cols (null: none)
+    float* colsum;
+    int32_t colsum_cols;
 };
 
 // Tile plan chosen on the host.
@@ -143,7 +147,7 @@ struct BwdArgs {
     const void* dk;      // [b*KVH, S, hd]
     const void* dv;
     void* dy;            // workspace: gradient of the fused output, [M, F] token-major, storage type
-    float* dbp;          // workspace: [dy tiles_m, F] fp32 column sums of dy per token tile, or null
+    float* dbp;          // workspace: [db_tiles, F] fp32 column sums of dy per 32 tokens, or null
     void* dw;            // dW in W's layout (written by the dW kernel when splits == 1)
     float* dwp;          // workspace: fp32 partial sums of dW: [splits, C, F] from the dW tile kernel
                          // (splits > 1), whole 256 x 256 blocks in accumulator order from the fast one
@@ -154,7 +158,7 @@ struct BwdArgs {
     int32_t chunk;       // tokens per range (a multiple of the K step)
     int32_t dw_tiles_m;  // 128 x 128 tiles over [C, F]
     int32_t dw_tiles_n;
-    int32_t db_tiles;    // rows of dbp
+    int32_t db_tiles;    // rows of dbp (32-token blocks)
     int32_t dw_partials; // dW goes through dwp in the fast kernel's block order
     int32_t dy_col_tile0;// the dy tile kernel's 128-column tiles [dy_col_tile0, dy_col_tile1): the fast
     int32_t dy_col_tile1;// kernel did the ones before, the heads kernel (bf16) the q/k/v ones after
@@ -175,8 +179,6 @@ hipError_t launch_bwd_dy(DType dt, bool x_tokens_last, bool w_fc, const BwdArgs&
 hipError_t launch_bwd_dy_heads(const BwdArgs& b, int col0, hipStream_t stream);
 // The dW kernel: grid (dw_tiles_m x dw_tiles_n, splits).
 hipError_t launch_bwd_dw(DType dt, bool x_tokens_last, const BwdArgs& b, hipStream_t stream);
-// Column sums of dy's first ncols columns per 128-token block into dbp.
-hipError_t launch_bwd_colsum(DType dt, const BwdArgs& b, int ncols, hipStream_t stream);
 // Sums dx's partial sums into its last tokens (bf16).
 hipError_t launch_bwd_reduce_dx(const BwdArgs& b, hipStream_t stream);
 // Sums the dW partials (splits > 1) into dW and the dy column sums into db (when db).
