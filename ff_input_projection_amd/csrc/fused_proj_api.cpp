@@ -204,6 +204,8 @@ struct fused_proj_plan {
     fp::KernelArgs dy_args{};            // its arguments but the per-call pointers
     fp::TilePlan dy_tile{};
     unsigned* d_desc_dy = nullptr;       // its column descriptors
+    int dw_epi = 4;                      // the fast dW's epilogue: 4 partial sums, 6 or 7 dW itself
+    unsigned* d_desc_dw = nullptr;       // column descriptors when it stores dW itself
     bool dy_heads = false;               // dy's q/k/v columns by the heads kernel
     bool fast_dw = false;                // dW on the fast kernel (else the dW tile kernel)
     bool dw_x_kmajor = false;            // ... reading x as K-major rows (channels-first x)
@@ -480,6 +482,25 @@ int plan_backward(fused_proj_plan* h) {
         b.splits = (int32_t)best;
         b.chunk = (int32_t)(r.M / best);
         b.dw_partials = 1;
+        // one token range: the units store dW itself in bf16 (no partial sums, no
+        // reduction), [C, F] as token-major rows of a "forward" with C tokens and F ff
+        // columns, [F, C] as its channels-first ff (whole 128-column waves: F % 128 == 0)
+        if (best == 1 && (d.w_layout == FUSED_PROJ_W_CF || r.F % 128 == 0)) {
+            const int64_t n = fp::fast_col_desc_entries(r.F);
+            std::vector<unsigned> hd((size_t)n);
+            fp::fast_col_desc(d.channels, r.F, 0, 0, 0, false, false, r.F, hd.data(), n);
+            hipError_t e = hipMalloc((void**)&h->d_desc_dw, (size_t)n * sizeof(unsigned));
+            if (e == hipSuccess)
+                e = hipMemcpy(h->d_desc_dw, hd.data(), (size_t)n * sizeof(unsigned), hipMemcpyHostToDevice);
+            if (e != hipSuccess) {
+                g_last_hip = e;
+                return FUSED_PROJ_EHIP;
+            }
+            a.col_desc = h->d_desc_dw;
+            a.ff_dim = (int32_t)r.F;
+            h->dw_epi = d.w_layout == FUSED_PROJ_W_CF ? 6 : 7;
+            b.dw_partials = 0;
+        }
     }
     plan_dx_split(h);
     // workspace: dy, then the column sums of dy per token tile (bias), then the dW partials,
@@ -490,7 +511,7 @@ int plan_backward(fused_proj_plan* h) {
     // (the fast kernel's partial sums are whole 256 x 256 blocks)
     auto up256 = [](int64_t v) { return (size_t)((v + 255) / 256 * 256); };
     h->ws_dwp = off;
-    if (h->fast_dw) off += ws_round((size_t)splits * up256(d.channels) * up256(r.F) * 4);
+    if (h->fast_dw && h->dw_epi == 4) off += ws_round((size_t)splits * up256(d.channels) * up256(r.F) * 4);
     else if (splits > 1) off += ws_round((size_t)splits * (size_t)d.channels * (size_t)r.F * 4);
     h->ws_dxp = off;
     if (h->dx_split) off += ws_round((size_t)b.dx_splits * up256(b.dx_rows) * up256(d.channels) * 4);
@@ -747,6 +768,7 @@ int fused_proj_destroy(fused_proj_t h) {
     if (!h) return FUSED_PROJ_OK;
     const int rc_sub = fused_proj_destroy(h->dx_plan);
     if (h->d_desc_dy) (void)hipFree(h->d_desc_dy);
+    if (h->d_desc_dw) (void)hipFree(h->d_desc_dw);
     hipError_t e1 = h->d_cos ? hipFree(h->d_cos) : hipSuccess;
     hipError_t e2 = h->d_sin ? hipFree(h->d_sin) : hipSuccess;
     hipError_t e3 = h->d_zeros ? hipFree(h->d_zeros) : hipSuccess;
@@ -849,7 +871,8 @@ int fused_proj_backward(fused_proj_t h, const void* x, const void* w, const void
         char* ws = static_cast<char*>(workspace);
         b.dy = ws;
         b.dbp = d.has_bias ? reinterpret_cast<float*>(ws + h->ws_dbp) : nullptr;
-        b.dwp = (b.splits > 1 || h->fast_dw) ? reinterpret_cast<float*>(ws + h->ws_dwp) : nullptr;
+        b.dwp = (b.splits > 1 || (h->fast_dw && h->dw_epi == 4)) ? reinterpret_cast<float*>(ws + h->ws_dwp)
+                                                                    : nullptr;
         b.dw = dw;
         b.db = d.has_bias ? db : nullptr;
         if (h->fast_dy) {
@@ -897,8 +920,8 @@ int fused_proj_backward(fused_proj_t h, const void* x, const void* w, const void
                 fp::KernelArgs a = h->dw_args;
                 a.x = x;
                 a.w = b.dy;
-                a.ff = b.dwp;
-                e = fp::launch_fused_proj_fast(h->dw_x_kmajor, false, 0, 4, h->dw_tile, a, s);
+                a.ff = h->dw_epi == 4 ? static_cast<void*>(b.dwp) : dw;
+                e = fp::launch_fused_proj_fast(h->dw_x_kmajor, false, 0, h->dw_epi, h->dw_tile, a, s);
             } else {
                 e = fp::launch_bwd_dw(h->dt, h->x_tl, b, s);
             }

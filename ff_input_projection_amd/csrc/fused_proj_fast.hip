@@ -367,6 +367,10 @@ constexpr int kEpiRope8 = 3;
 // restage). The weight gradient (dW = X^T dy over token ranges, rows are channels), and the
 // input gradient's last token tiles (dx = dy W^T over ranges of the fused columns).
 constexpr int kEpiDwPartial = 4;
+// The weight gradient in one token range: the same units' pipeline, stored straight into
+// dW in bf16 by the restaged token-major store ([C, F] rows; no activation) or by the
+// channels-first store ([F, C]: column f's channels as one run).
+constexpr int kEpiDwRows = 6, kEpiDwCols = 7;
 // The backward pass's dy over the ff columns: the forward product y recomputed, then
 // dy = d_ff * act'(y) (d_ff token-major, read 8 bytes per lane and group) stored token-major
 // with row stride ff_ld (no RoPE).
@@ -385,7 +389,12 @@ fused_proj_fast_kernel(KernelArgs p) {
     constexpr int RGN_ALL = T::NWF * T::NWT / 2 * kRestageRows * kRestageRow, W_STAGE = BF * kBK * 2;
     constexpr int PAD = !T::SINGLE && RGN_ALL > W_STAGE ? RGN_ALL - W_STAGE : 0;
     using C = FastCfg<X_TL, W_FC, BF, BT, T::NWF, kNWT, BK, STAGES, PAD>;
-    constexpr bool DW = EPI == kEpiDwPartial;
+    // range units (the weight gradient's, dx's last tiles): their pipeline, and whether the
+    // epilogue stores fp32 partial sums
+    constexpr bool DW = EPI == kEpiDwPartial || EPI == kEpiDwRows || EPI == kEpiDwCols;
+    constexpr bool DWP = EPI == kEpiDwPartial;
+    // the channels-first ff store
+    constexpr bool CF_STORE = EPI == kEpiFfChannelsFirst || EPI == kEpiDwCols;
     using Pipe = FastPipe<C, X_TL, W_FC, BK, TAILK, DW, DW && X_TL>;
     using Ops = typename Pipe::Ops;
     constexpr int WF = C::WF, WT = C::WT, TI = C::TI, TJ = C::TJ, NG = C::NG, NLOAD = C::NLOAD;
@@ -492,7 +501,7 @@ fused_proj_fast_kernel(KernelArgs p) {
     const int64_t slab_q = (int64_t)S * p.qw, slab_kv = (int64_t)S * p.n_kv_heads * hd;
     constexpr bool R8 = EPI == kEpiRope8;
     // epilogues whose every wave issues exactly TJ * 8 stores per tile (the restaged ones)
-    constexpr bool RELAX = EPI == kEpiDefault || EPI == kEpiOtherAct || EPI == kEpiRope8;
+    constexpr bool RELAX = EPI == kEpiDefault || EPI == kEpiOtherAct || EPI == kEpiRope8 || EPI == kEpiDwRows;
 
     unsigned voff_cur[NLOAD], voff_nxt[NLOAD];
     int trow_cur, kb_cur;
@@ -637,7 +646,7 @@ fused_proj_fast_kernel(KernelArgs p) {
         // they should neither evict the operand panels from the XCD's L2 nor sit dirty
         // there for the write-back at the end of the kernel).
         const int tw0 = m0 + wt * WT;   // the wave's first token
-        if constexpr (DW) {
+        if constexpr (DWP) {
             // fp32 partial sums of this unit in the accumulators' own order, so that every
             // store writes 1 KB contiguous: the unit's BT x BF block [range][row tile]
             // [column tile] is 256-float chunks ((wave * TI + a) * TJ + j) * 4 + q, lane l
@@ -854,7 +863,7 @@ fused_proj_fast_kernel(KernelArgs p) {
             }
             // the next block's cos/sin, ahead of this block's stores
             if (j + 1 < TJ) load_rope(j + 1, 0);
-            if constexpr (EPI == kEpiFfChannelsFirst) {
+            if constexpr (CF_STORE) {
                 if (fw < ff_dim) {
                     // channels-first ff [b, ff, S] (ff_dim is a multiple of the wave's 128
                     // columns, so the whole wave is ff): the block goes through LDS one column
@@ -972,7 +981,7 @@ hipError_t dispatch_fast_layouts(bool x_tl, bool w_fc, const KernelArgs& a, int 
 // unit holds them all. Part 0 also holds the host functions below.
 //   0: default epilogue, no RoPE or partner distance 2     1: default, distances 4 and 8
 //   2: tanh GELU / squared ReLU, channels-first ff         3: 8-column RoPE, backward dy
-//   4: weight-gradient partial sums
+//   4: range units (partial sums, or the weight gradient stored directly)
 #ifdef FP_FAST_PART
 #define FP_PART(k) (FP_FAST_PART == (k))
 #else
@@ -982,7 +991,7 @@ hipError_t dispatch_fast_layouts(bool x_tl, bool w_fc, const KernelArgs& a, int 
 constexpr int fast_part_of(int epi, int dg) {
     return epi == kEpiDefault ? (dg <= 2 ? 0 : 1)
            : (epi == kEpiOtherAct || epi == kEpiFfChannelsFirst) ? 2
-           : epi == kEpiDwPartial ? 4 : 3;
+           : (epi == kEpiDwPartial || epi == kEpiDwRows || epi == kEpiDwCols) ? 4 : 3;
 }
 
 // The variants one part compiles, for tile shape T: an unsupported combination is an error.
@@ -1009,6 +1018,15 @@ hipError_t dispatch_part(int dg, int epi, bool x_tl, bool w_fc, const KernelArgs
             if (w_fc) return x_tl ? launch_fast_one<true, true, 0, T, kEpiDwPartial>(a, grid, s) : hipErrorInvalidValue;
             return x_tl ? launch_fast_one<true, false, 0, T, kEpiDwPartial>(a, grid, s)
                         : launch_fast_one<false, false, 0, T, kEpiDwPartial>(a, grid, s);
+        }
+        // the weight gradient stored directly (large tiles only)
+        if constexpr (!T::SINGLE) {
+            if (dg == 0 && epi == kEpiDwRows && !w_fc)
+                return x_tl ? launch_fast_one<true, false, 0, T, kEpiDwRows>(a, grid, s)
+                            : launch_fast_one<false, false, 0, T, kEpiDwRows>(a, grid, s);
+            if (dg == 0 && epi == kEpiDwCols && !w_fc)
+                return x_tl ? launch_fast_one<true, false, 0, T, kEpiDwCols>(a, grid, s)
+                            : launch_fast_one<false, false, 0, T, kEpiDwCols>(a, grid, s);
         }
     }
     return hipErrorInvalidValue;

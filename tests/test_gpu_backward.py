@@ -146,6 +146,22 @@ def test_backward_dx_last_tiles_in_ranges(wl):
     _check(wl, wl.name)
 
 
+DW_DIRECT = [
+    # dW in one token range, stored straight into W's layout in bf16: [F, C] (a token-major
+    # x, 4096 tokens, 256 dW tiles) and [C, F] with a channels-first x (224 dW tiles, RoPE
+    # heads); the decoder's full-size case takes this path too
+    with_shape(WORKLOADS["bert_ff_bf16"], "bwd_dw_direct_fc", x_shape=(2, 2048, 4096), ff_dim=4096, w_layout="fc",
+               seed=408),
+    with_shape(WORKLOADS["walrus_bf16"], "bwd_dw_direct_cf", x_shape=(4, 4096, 32, 32, 1), ff_dim=3072, n_heads=2,
+               head_dim=64, seed=409),
+]
+
+
+@pytest.mark.parametrize("wl", DW_DIRECT, ids=[w.name for w in DW_DIRECT])
+def test_backward_dw_stored_directly(wl):
+    _check(wl, wl.name)
+
+
 def test_backward_strided_channel_slice_view():
     """x as a channel slice of a wider tensor: the backward reads it in place; dx is dense."""
     wl = with_shape(WORKLOADS["walrus_bf16"], "bwd_view", x_shape=(2, 48, 8, 16, 1), ff_dim=64, n_heads=2,
