@@ -624,23 +624,30 @@ __global__ __launch_bounds__(256) void bwd_reduce_tiles_kernel(TileReduce tr) {
     }
 }
 
-// db from the per-tile column sums: 64 columns per workgroup, its 256 threads summing
-// every fourth row (coalesced 256-byte row segments), then the four partial sums in LDS.
+// db from the column sums per 32 tokens: 16 columns per workgroup; thread (row group g,
+// quad q) adds the 16-byte column quad q of rows g, g + 64, ..., then the 64 row groups'
+// sums meet in LDS (a fixed order: the result does not depend on timing).
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_reduce_db_kernel(BwdArgs b) {
-    __shared__ float part[4][64];
+    __shared__ f32x4 part[64][4];
     const int N = b.f.N;
-    const int fx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    const int f = blockIdx.x * 64 + fx;
-    float sum = 0.0f;
+    const int q = threadIdx.x & 3, g = threadIdx.x >> 2;
+    const int f = blockIdx.x * 16 + 4 * q;   // N is a multiple of 4
+    f32x4 sum = {};
     if (f < N) {
 #pragma unroll 4
-        for (int r = ty; r < b.db_tiles; r += 4) sum += b.dbp[(int64_t)r * N + f];
+        for (int r = g; r < b.db_tiles; r += 64) sum += *reinterpret_cast<const f32x4*>(b.dbp + (int64_t)r * N + f);
     }
-    part[ty][fx] = sum;
+    part[g][q] = sum;
     __syncthreads();
-    if (ty == 0 && f < N)
-        static_cast<T*>(b.db)[f] = (T)((part[0][fx] + part[1][fx]) + (part[2][fx] + part[3][fx]));
+    // 16 threads finish the 16 columns: column 4 qq + u of the quad
+    if (threadIdx.x < 16) {
+        const int qq = threadIdx.x >> 2, u = threadIdx.x & 3;
+        const int fc = blockIdx.x * 16 + threadIdx.x;
+        float t = 0.0f;
+        for (int r = 0; r < 64; ++r) t += part[r][qq][u];
+        if (fc < N) static_cast<T*>(b.db)[fc] = (T)t;
+    }
 }
 
 __global__ __launch_bounds__(256) void zero_fill_kernel(unsigned* p, size_t n) {
@@ -706,7 +713,7 @@ hipError_t launch_reduce_t(const BwdArgs& b, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (b.db != nullptr && b.dbp != nullptr) {
-        hipLaunchKernelGGL((bwd_reduce_db_kernel<T>), dim3((unsigned)((b.f.N + 63) / 64)), dim3(256), 0, s, b);
+        hipLaunchKernelGGL((bwd_reduce_db_kernel<T>), dim3((unsigned)((b.f.N + 15) / 16)), dim3(256), 0, s, b);
         return hipGetLastError();
     }
     return hipSuccess;
