@@ -417,7 +417,7 @@ def measure_backward(wl, dev, steps, min_warmup_s, check: bool):
             got.append(db)
             exp.append(ref.db)
             scl.append(sc.db)
-        vd = cmp.compare(got, exp, scl, wl.dtype)
+        vd = cmp.compare_backward(got, exp, scl, wl.dtype)
         entry["parity"] = {"ok": vd.ok, "max_err_over_tol": round(vd.max_ratio, 5), "elements": vd.n}
     del x, w, b, ups, outs, ws
     proj.close()

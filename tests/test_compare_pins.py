@@ -193,3 +193,53 @@ def test_backward_scales_are_the_cauchy_schwarz_bounds():
         e = math.sqrt(M) * math.sqrt(sum(dy[t, f] ** 2 for t in range(M)))
         assert abs(sc.db[f] - e) <= 1e-12 * e
         assert abs(sum(dy[t, f] for t in range(M))) <= sc.db[f]
+
+
+def _bf16(a):
+    """Round float64 values to bf16 (round to nearest even) and back, through torch."""
+    import torch
+
+    return torch.from_numpy(np.asarray(a, dtype=np.float64)).float().to(torch.bfloat16).double().numpy()
+
+
+def test_backward_bar_covers_two_bf16_roundings():
+    """The backward bar is the arithmetic's: a dW element summed over 3 tokens from dy rounded
+    to bf16 (its 7 fraction bits give each rounding up to 2^-8 of the value), then rounded
+    itself, lands 0.62% of its Cauchy-Schwarz bound from the exact sum (one such element
+    came out of a seeded backward case): more than the forward's 4e-3, less than the
+    backward's 8e-3."""
+    x = np.array([-0.02160645, 0.81640625, -0.546875])          # bf16 values
+    dy = np.array([-0.18385676, 1.07453544, -2.13347303])       # exact float64 gradient
+    exact = float(x @ dy)
+    bound = float(np.linalg.norm(x) * np.linalg.norm(dy))
+    got = float(_bf16(np.float32(x @ _bf16(dy))))
+    err = abs(got - exact) / bound
+    assert cmp.REL["bf16"] < err < cmp.BACKWARD_REL["bf16"], err
+
+
+def test_backward_bar_bounds_random_double_roundings():
+    """Random short and long sums with dy rounded to bf16 and the fp32 result rounded again:
+    every error stays within 2 * 2^-8 (1 + 2^-8) of the bound, below BACKWARD_REL."""
+    rng = np.random.default_rng(17)
+    worst = 0.0
+    for n in (1, 2, 3, 4, 8, 64):
+        x = _bf16(rng.standard_normal((4000, n)))
+        dy = rng.standard_normal((4000, n)) * rng.choice([0.25, 1.0, 3.0], size=(4000, 1))
+        exact = np.einsum("ij,ij->i", x, dy)
+        got = _bf16(np.einsum("ij,ij->i", x, _bf16(dy)).astype(np.float32))
+        bound = np.linalg.norm(x, axis=1) * np.linalg.norm(dy, axis=1)
+        worst = max(worst, float(np.max(np.abs(got - exact) / bound)))
+    assert worst <= 2 * 2.0 ** -8 * (1 + 2.0 ** -8)
+    assert worst < cmp.BACKWARD_REL["bf16"]
+    # and the bar is that bound, not looser (within 5%)
+    assert cmp.BACKWARD_REL["bf16"] <= 1.05 * 2 * 2.0 ** -8 * (1 + 2.0 ** -8)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_compare_backward_uses_the_backward_bar(dtype):
+    """compare_backward() fails at 1.01x BACKWARD_REL and passes at 0.99x."""
+    ref = np.array([1.0, -2.0, 0.5])
+    scl = np.array([3.0, 4.0, 5.0])
+    rel = cmp.BACKWARD_REL[dtype]
+    assert not cmp.compare_backward([ref + 1.01 * rel * scl], [ref], [scl], dtype).ok
+    assert cmp.compare_backward([ref + 0.99 * rel * scl], [ref], [scl], dtype).ok

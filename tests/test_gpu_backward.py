@@ -2,11 +2,12 @@
 float64 backward oracle, element by element.
 
 Bar: each gradient element is one sum of products, and its error must stay within
-4e-3 (bf16) or 1e-5 (fp32) of the Cauchy-Schwarz bound of that sum
-(oracle/compare.py backward_scales): ||dy_t|| ||W_c|| for dx, ||x_c|| ||dy_f|| for dW,
-sqrt(M) ||dy_f|| for db, with dy the oracle's float64 gradient of the fused output.
-dy is held in the storage type between the launches, which moves every sum by at
-most 2^-9 of its bound for bf16; the bar leaves room for that and the final rounding.
+8e-3 (bf16) or 1e-5 (fp32) of the Cauchy-Schwarz bound of that sum
+(oracle/compare.py backward_scales, BACKWARD_REL): ||dy_t|| ||W_c|| for dx,
+||x_c|| ||dy_f|| for dW, sqrt(M) ||dy_f|| for db, with dy the oracle's float64 gradient of
+the fused output. dy is held in the storage type between the launches, which moves every
+sum by at most 2^-8 of its bound for bf16, and the final rounding moves the result by 2^-8
+of itself again; with few terms (3 tokens) both come close to their bound together.
 Outputs start as NaN, so every element must have been written.
 """
 import numpy as np
@@ -67,7 +68,7 @@ def backward_verdict(wl, inp, gr, grads):
         got.append(db)
         exp.append(ref.db)
         scl.append(sc.db)
-    return cmp.compare(got, exp, scl, wl.dtype)
+    return cmp.compare_backward(got, exp, scl, wl.dtype)
 
 
 def _check(wl, label):

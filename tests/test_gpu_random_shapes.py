@@ -128,3 +128,14 @@ def test_random_shape_parity_fast_kernel(seed):
     v = verdict(wl, inp, outs, tokens)
     print(f"[parity] random fast {seed}: {v}", flush=True)
     assert v.ok and v.max_tight_ratio <= 1.0, f"random fast {seed}: {v}"
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_shape_backward(seed):
+    """The same draws through the backward pass (default kernel choice): every element of
+    dx, dW and db against the float64 backward oracle."""
+    from test_gpu_backward import _check
+
+    wl = draw(seed)
+    print(f"[case] random backward {seed}: {wl}", flush=True)
+    _check(wl, f"random backward {seed}")

@@ -87,6 +87,10 @@ BAR_MUTATIONS = [
      "plain = xn[:, None] * wn[None, :] + 0.0 * np.abs(b)[None, :]"),
     ("bar loosened by 2", "ratio = err / (rel * s + 1e-300)", "ratio = err / (2 * rel * s + 1e-300)"),
     ("non-finite outputs accepted", "finite &= bool(np.all(np.isfinite(g)))", "finite &= True"),
+    ("backward bar without the second rounding", 'BACKWARD_REL = {"bf16": 8e-3', 'BACKWARD_REL = {"bf16": 4e-3'),
+    ("backward bar loosened", 'BACKWARD_REL = {"bf16": 8e-3', 'BACKWARD_REL = {"bf16": 2e-2'),
+    ("backward comparison with the forward bar", "return compare(got, ref, scl, dtype, rel=BACKWARD_REL[dtype])",
+     "return compare(got, ref, scl, dtype)"),
 ]
 
 
