@@ -194,6 +194,11 @@ struct fused_proj_plan {
     float* d_sin = nullptr;
     void* d_zeros = nullptr;
     unsigned* d_desc = nullptr;  // fast kernel: column descriptors
+    // Forward tail: when the large tiles' last round would leave most CUs idle, the tokens
+    // from tail_m0 on (whole slabs) run on small tiles in a second launch (0: no tail).
+    int64_t tail_m0 = 0;
+    fp::TilePlan tail_tile{};
+    fp::KernelArgs tail_args{};          // the tail's arguments but the per-call pointers
     int device = 0;
     int num_cus = 0;
     bool debug_sync = false;
@@ -229,6 +234,50 @@ int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backwa
 
 constexpr size_t kWsAlign = 256;
 size_t ws_round(size_t n) { return (n + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// The forward's tail. Large tiles are walked by one persistent workgroup per CU, so a last
+// round of a few tiles leaves most CUs idle. Then the tokens of the last slabs (enough for
+// the head to end one round earlier) go to a second launch on small tiles, at most two per
+// CU (one round of them). The tail starts on a slab boundary, so its inputs and outputs
+// are the whole problem's with every pointer advanced by its first token and the same
+// column descriptors and rotary table. The estimate charges the last large round in full
+// (a tile's MFMA time at about 55% of a CU's share of the bf16 peak), the small tiles 0.55
+// (one per CU) to 0.7 (two per CU) of it, and a launch. Measured, a part-filled last round
+// costs less than a full one (its few tiles contend less: at K = 768, 18 us against 27 us
+// for a quarter-filled round), about what the small tiles take, so the split gains a few
+// percent: 73.6 -> 71.3 us on 16384 tokens x 2304 columns, 100.7 -> 99.2 us on 24576 x 2304.
+// FUSED_PROJ_TAIL=0 never splits, =1 splits wherever a tail fits.
+void plan_fwd_tail(fused_proj_plan* h) {
+    const Derived& r = h->r;
+    if (!h->fast || h->tile.shape != fp::kFastLarge || r.M <= 0 || r.S <= 0 || h->d.channels <= 0) return;
+    const char* env = std::getenv("FUSED_PROJ_TAIL");
+    const int force = env && env[0] == '0' ? 0 : env && env[0] == '1' ? 1 : -1;
+    if (force == 0) return;
+    const int64_t cus = h->num_cus, K = h->d.channels;
+    const int64_t tn = (r.F + 255) / 256, tiles = h->base.tiles_m * tn;
+    const int64_t rounds = (tiles + cus - 1) / cus;
+    if (rounds < 2) return;
+    // the most whole slabs whose tiles fit one round fewer
+    const int64_t head_rows = (rounds - 1) * cus / tn;         // 256-token rows
+    const int64_t n1 = std::min(head_rows * 256 / r.S, r.M / r.S - 1);
+    if (n1 <= 0) return;
+    const int64_t m0 = n1 * r.S, mt = r.M - m0;
+    const int64_t small = ((mt + 127) / 128) * ((r.F + 127) / 128);
+    if (small > 2 * cus) return;
+    const double round_s = 2.0 * 256 * 256 * (double)K / (2.5e15 / (double)cus * 0.55);
+    const double t_split = (double)(((m0 + 255) / 256 * tn + cus - 1) / cus) * round_s +
+                           (small <= cus ? 0.55 : 0.7) * round_s + 3e-6;
+    if (force != 1 && t_split >= 0.97 * (double)rounds * round_s) return;
+    fp::KernelArgs t = h->base;
+    t.M = mt;
+    t.tiles_m = (int32_t)((mt + 127) / 128);
+    t.tiles_n = (int32_t)((r.F + 127) / 128);
+    t.group_m = 8;
+    t.div_group = fp::make_fastdiv_u31((uint32_t)(8 * t.tiles_n));
+    h->tail_args = t;
+    h->tail_tile = fp::TilePlan{128, 128, 32, 8, (int)((small + 7) / 8 * 8), fp::kFastSmall};
+    h->tail_m0 = m0;
+}
 
 // dx = dy W^T on large tiles takes rounds of tiles over the CUs; when the last round is
 // mostly idle (Walrus: 288 tiles on 256 CUs), the last token tiles are instead split into
@@ -550,6 +599,12 @@ int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backwa
     int num_cus = 0;
     if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, h->device);
     h->num_cus = num_cus > 0 ? num_cus : 256;
+    // FUSED_PROJ_CUS=n (8 <= n <= the device's CUs) plans for n CUs: the tests use it to
+    // reach the persistent walk and the tail split at small sizes
+    if (const char* cu_env = std::getenv("FUSED_PROJ_CUS")) {
+        const int n = std::atoi(cu_env);
+        if (n >= 8 && n <= h->num_cus) h->num_cus = n;
+    }
     if (e != hipSuccess) {
         g_last_hip = e;
         delete h;
@@ -569,7 +624,7 @@ int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backwa
     const bool rope8 = roped && r.rd == 8;
     const int dg = rope8 ? 0 : r.rd == desc->head_dim ? fp::fast_rope_groups((int)desc->head_dim, roped) : -1;
     const bool fits32 = r.x_span * 2 < (int64_t(1) << 32) && desc->channels * r.F * 2 < (int64_t(1) << 32);
-    const fp::TilePlan fp_plan = fp::fast_plan(r.M, r.F, num_cus);
+    const fp::TilePlan fp_plan = fp::fast_plan(r.M, r.F, h->num_cus);
     // Both tile shapes take any token, column and channel count: tokens past M read token
     // 0 and columns past F read row 0 of W and the zero block for the bias, and neither is
     // stored (a channels-first x has S, hence M, a multiple of the 8-token load chunk);
@@ -679,6 +734,7 @@ int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backwa
         }
     }
     a.col_desc = h->d_desc;
+    plan_fwd_tail(h);
     if (with_backward) {
         rc = plan_backward(h);
         if (rc == FUSED_PROJ_OK) rc = scratch_setup(h->device);
@@ -751,8 +807,26 @@ int fused_proj_run(fused_proj_t h, const void* x, const void* w, const void* bia
     a.k = k;
     a.v = v;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    e = h->fast ? fp::launch_fused_proj_fast(h->x_tl, h->w_fc, h->dg, h->epi, h->tile, a, s)
-                : fp::launch_fused_proj(h->dt, h->x_tl, h->w_fc, h->tile, a, s);
+    if (h->tail_m0 > 0) {
+        // the head's tokens on the large tiles, then the tail's (whole slabs from tail_m0)
+        // on small tiles: every pointer advanced by the tail's first token
+        fp::KernelArgs t = h->tail_args;
+        const int64_t m0 = h->tail_m0, n1 = m0 / r.S;
+        t.x = static_cast<const char*>(x) + (size_t)(n1 * r.sb) * es;
+        t.w = w;
+        t.bias = a.bias;
+        t.ff = ff ? static_cast<char*>(ff) + (size_t)(m0 * h->d.ff_dim) * es : nullptr;
+        t.q = q ? static_cast<char*>(q) + (size_t)(m0 * r.qw) * es : nullptr;
+        t.k = k ? static_cast<char*>(k) + (size_t)(m0 * r.kvw) * es : nullptr;
+        t.v = v ? static_cast<char*>(v) + (size_t)(m0 * r.kvw) * es : nullptr;
+        a.M = m0;
+        a.tiles_m = (int32_t)((m0 + h->tile.bm - 1) / h->tile.bm);
+        e = fp::launch_fused_proj_fast(h->x_tl, h->w_fc, h->dg, h->epi, h->tile, a, s);
+        if (e == hipSuccess) e = fp::launch_fused_proj_fast(h->x_tl, h->w_fc, h->dg, h->epi, h->tail_tile, t, s);
+    } else {
+        e = h->fast ? fp::launch_fused_proj_fast(h->x_tl, h->w_fc, h->dg, h->epi, h->tile, a, s)
+                    : fp::launch_fused_proj(h->dt, h->x_tl, h->w_fc, h->tile, a, s);
+    }
     if (e == hipSuccess && h->debug_sync) {
         e = hipStreamSynchronize(s);
         if (e == hipSuccess) e = hipGetLastError();
@@ -967,6 +1041,13 @@ int fused_proj_describe(fused_proj_t h, char* buf, size_t len) {
                   h->tile.grid > 0 ? h->tile.grid : h->base.tiles_m * h->base.tiles_n,
                   h->base.tiles_m * h->base.tiles_n, (long long)h->r.M, (long long)h->d.channels,
                   (long long)h->r.F);
+    if (h->tail_m0 > 0) {
+        const size_t n = std::strlen(buf);
+        if (n + 1 < len)
+            std::snprintf(buf + n, len - n, " tail=%lld+%lld tail_tile=%dx%d tail_grid=%d",
+                          (long long)h->tail_m0, (long long)(h->r.M - h->tail_m0), h->tail_tile.bm,
+                          h->tail_tile.bn, h->tail_tile.grid);
+    }
     return FUSED_PROJ_OK;
 }
 

@@ -282,6 +282,44 @@ def test_large_tiles_with_fc_weights(wl):
     _check(wl, inp, outs, sample_tokens(wl, 384, seed=2), wl.name)
 
 
+TAIL = [
+    # (CUs planned for, shape): with few CUs these small shapes walk the large tiles
+    # persistently with a part-filled last round, which the split moves to small tiles.
+    # token-major, RoPE hd 64, GELU ff, bias: 4 token rows x 5 column tiles on 16 CUs
+    (16, with_shape(WORKLOADS["bert_qkv_bf16"], "tail_tl_rope_gelu", x_shape=(8, 128, 192), ff_dim=512,
+                    ff_act="gelu", n_heads=4, head_dim=64, rope=True, seed=151)),
+    # channels-first x, grouped query heads with RoPE on 8 columns, no ff: 9 tiles on 8 CUs
+    (8, with_shape(WORKLOADS["gqa_rope8_bf16"], "tail_cf_gqa_rope8", layout="channels_first",
+                   x_shape=(6, 256, 16, 16, 1), ff_dim=0, n_heads=8, head_dim=64, n_kv_heads=2, rope_dims=8,
+                   seed=152)),
+    # channels-first x and ff output, [F,C] weight, slabs of 64 tokens: 9 tiles on 8 CUs
+    (8, with_shape(WORKLOADS["walrus_bf16"], "tail_cf_ffcf_fc", x_shape=(10, 128, 8, 8, 1), ff_dim=256,
+                   n_heads=2, head_dim=64, rope=False, w_layout="fc", ff_layout="channels_first", seed=153)),
+    # squared ReLU, slabs of 150 tokens (the head ends inside a large tile row): 10 tiles on 8 CUs
+    (8, with_shape(WORKLOADS["bert_ff_bf16"], "tail_tl_relu2_ragged_s", x_shape=(8, 150, 96), ff_dim=320,
+                   ff_act="relu2", n_heads=1, head_dim=64, seed=154)),
+]
+
+
+@pytest.mark.parametrize("cus,wl", TAIL, ids=[w.name for _, w in TAIL])
+def test_large_tiles_with_small_tile_tail(cus, wl, monkeypatch):
+    """The large tiles' last round moved to a second launch on small tiles (whole slabs
+    from the split token on, every pointer advanced by it): planned for a few CUs and
+    forced, every output element against the oracle; outputs start as NaN."""
+    monkeypatch.setenv("FUSED_PROJ_CUS", str(cus))
+    monkeypatch.setenv("FUSED_PROJ_TAIL", "1")
+    print(f"[case] small-tile tail {wl.name} x={wl.x_shape} cus={cus}", flush=True)
+    inp = make_inputs(wl)
+    proj, outs = run_gpu(wl, inp, DEV)
+    desc = proj.describe()
+    print(f"[plan] {desc}", flush=True)
+    assert "tile=256x256" in desc and " tail=" in desc, desc
+    _check(wl, inp, outs, all_tokens(wl), wl.name)
+    for t in outs:
+        if t is not None:
+            assert torch.isfinite(t).all().item()
+
+
 def test_strided_views_channel_slice_and_row_stride(kernel_choice):
     """x as a view: a channel slice of a wider channels-first tensor, and a token-major
     view whose row stride exceeds C. No copy is made; results match the oracle."""
