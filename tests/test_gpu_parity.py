@@ -343,6 +343,31 @@ def test_strided_views_channel_slice_and_row_stride(kernel_choice):
     _check(wl2, inp2, outs2, all_tokens(wl2), "row-stride view")
 
 
+def test_x_span_beyond_4gib_takes_the_general_kernel():
+    """A token-major x whose span reaches past 4 GiB: 65536 tokens of 256 channels with a
+    row stride of 33024 elements (4.33 GB). That is beyond the fast kernel's 32-bit
+    offsets, so the plan takes the general kernel, whose offsets are 64-bit. Every output
+    element against the oracle; outputs start as NaN."""
+    wl = with_shape(WORKLOADS["bert_qkv_bf16"], "tl_span_4gib", x_shape=(1, 65536, 256), ff_dim=128,
+                    ff_act="gelu", n_heads=2, head_dim=64, rope=True, seed=203)
+    stride = 33024
+    assert ((wl.M - 1) * stride + wl.C) * 2 >= 1 << 32
+    print(f"[case] x span past 4 GiB: {wl.name} x={wl.x_shape} row stride {stride}", flush=True)
+    inp = make_inputs(wl)
+    big = torch.empty((1, wl.M, stride), dtype=torch.bfloat16, device=DEV)
+    big[:, :, :wl.C] = inp.x.to(DEV)
+    proj, outs = run_gpu(wl, inp, DEV, x_dev=big[:, :, :wl.C])
+    desc = proj.describe()
+    print(f"[plan] {desc}", flush=True)
+    assert "fused_proj_tile_kernel" in desc, desc
+    _check(wl, inp, outs, all_tokens(wl), wl.name)
+    for t in outs:
+        if t is not None:
+            assert torch.isfinite(t).all().item()
+    del big, outs, proj
+    torch.cuda.empty_cache()
+
+
 def test_layout_invariance_on_gpu(kernel_choice):
     """Channels-first input and its channels-last copy give the same outputs."""
     wl = with_shape(WORKLOADS["walrus_bf16"], "inv", x_shape=(2, 64, 8, 16, 1), ff_dim=64, n_heads=2,
