@@ -184,21 +184,27 @@ struct FastPipe {
             xs = xsrc + (int64_t)ka * xstep;
         }
         const bool tail = TAILK && (ks + 1) * BK > K;
+        auto dst_of = [&](int q) __attribute__((always_inline)) {
+            return lds0 + (q < C::W_INSTR ? ST * C::W_BYTES + (wave * C::W_INSTR + q) * 1024
+                                          : C::X_REGION + ST * C::X_BYTES +
+                                                (wave * C::X_INSTR + (q - C::W_INSTR)) * 1024);
+        };
+        // one branch around all of the step's loads (one per load, as the compiler would
+        // otherwise lay it out, costs a K step of the small tiles about a tenth)
+        if (!tail) {
 #pragma unroll
-        for (int q = 0; q < C::NLOAD; ++q) {
-            const bool isw = q < C::W_INSTR;
-            const unsigned dst = lds0 + (isw ? ST * C::W_BYTES + (wave * C::W_INSTR + q) * 1024
-                                             : C::X_REGION + ST * C::X_BYTES +
-                                                   (wave * C::X_INSTR + (q - C::W_INSTR)) * 1024);
-            const char* base = isw ? ws : xs;
-            if (!tail) {
+            for (int q = 0; q < C::NLOAD; ++q) {
                 // SGPR base + 32-bit lane offset: no per-load VALU. Inline asm keeps the
                 // compiler from waiting on every stage in flight before each LDS read.
-                asm volatile(HAZARD_NOPS "global_load_lds_dwordx4 %0, %1" ::"v"(voff[q]), "s"(base), "{m0}"(dst)
+                asm volatile(HAZARD_NOPS "global_load_lds_dwordx4 %0, %1" ::"v"(voff[q]),
+                             "s"(q < C::W_INSTR ? ws : xs), "{m0}"(dst_of(q))
                              : "memory");
-            } else {
-                const char* a = (ks * BK + kofs[q] < K) ? base + voff[q] : zeros;
-                asm volatile(HAZARD_NOPS "global_load_lds_dwordx4 %0, off" ::"v"(a), "{m0}"(dst) : "memory");
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < C::NLOAD; ++q) {
+                const char* a = (ks * BK + kofs[q] < K) ? (q < C::W_INSTR ? ws : xs) + voff[q] : zeros;
+                asm volatile(HAZARD_NOPS "global_load_lds_dwordx4 %0, off" ::"v"(a), "{m0}"(dst_of(q)) : "memory");
             }
         }
     }
@@ -511,7 +517,7 @@ fused_proj_fast_kernel(KernelArgs p) {
     // Wait until this wave's loads of all but the `later` most recently issued K steps have
     // landed (the vector memory counter counts in issue order).
     auto wait_steps = [&](int later) __attribute__((always_inline)) {
-        static_assert(PF - 2 <= 3 && (T::SINGLE || PF - 1 <= 3), "wait counts cover up to three later steps");
+        static_assert(PF - 1 <= 3, "wait counts cover up to three later steps");
         if (later >= 3) wait_vmcnt<3 * NLOAD>();
         else if (later == 2) wait_vmcnt<2 * NLOAD>();
         else if (later == 1) wait_vmcnt<NLOAD>();
@@ -520,14 +526,22 @@ fused_proj_fast_kernel(KernelArgs p) {
     // Prologue: the first PF K steps of the first tile and its bias in flight; once step 0
     // has landed (the later ones may still be in flight), read its operands. Single-tile
     // workgroups issue only the steps that exist, so that no load is in flight after the
-    // last K step (their epilogue reuses the whole stage area).
+    // last K step (their epilogue reuses the whole stage area) -- except in the ragged-K
+    // form (UNIFORM), where a step past the last one reads the zero block like any chunk
+    // past K: every K step then has the same code and waits (no branches on the step), and
+    // the epilogue first waits for all loads. (On a whole-K shape the extra loads and that
+    // wait cost more than the branches: small-K 11.3 against 11.0 us; grouped-query 10.3
+    // against 10.65.)
+    constexpr bool UNIFORM = T::SINGLE && TAILK;
+    const bool exists1 = !T::SINGLE || UNIFORM || 1 < KTp, exists2 = !T::SINGLE || UNIFORM || 2 < KTp;
+    const bool exists3 = !T::SINGLE || UNIFORM || 3 < KTp, exists4 = !T::SINGLE || UNIFORM || 4 < KTp;
     pp.template issue<0>(voff_cur, 0, K, zeros, kb_cur);
     issue_bias(0, tf * BF);
-    if (!T::SINGLE || 1 < KTp) pp.template issue<1>(voff_cur, 1, K, zeros, kb_cur);
-    if (!T::SINGLE || 2 < KTp) pp.template issue<2>(voff_cur, 2, K, zeros, kb_cur);
-    if constexpr (PF >= 4) if (!T::SINGLE || 3 < KTp) pp.template issue<3>(voff_cur, 3, K, zeros, kb_cur);
-    if constexpr (PF >= 5) if (!T::SINGLE || 4 < KTp) pp.template issue<4>(voff_cur, 4, K, zeros, kb_cur);
-    wait_steps(T::SINGLE ? min(PF - 1, KTp - 1) : PF - 1);
+    if (exists1) pp.template issue<1>(voff_cur, 1, K, zeros, kb_cur);
+    if (exists2) pp.template issue<2>(voff_cur, 2, K, zeros, kb_cur);
+    if constexpr (PF >= 4) if (exists3) pp.template issue<3>(voff_cur, 3, K, zeros, kb_cur);
+    if constexpr (PF >= 5) if (exists4) pp.template issue<4>(voff_cur, 4, K, zeros, kb_cur);
+    wait_steps(T::SINGLE && !UNIFORM ? min(PF - 1, KTp - 1) : PF - 1);
     __syncthreads();
     Ops c0 = pp.template read<0, 0>();
     Ops c1 = pp.template read<0, 1>();
@@ -581,7 +595,12 @@ fused_proj_fast_kernel(KernelArgs p) {
             constexpr int SN = (ST + 1) % STAGES, SL = (ST + PF) % STAGES;
             __builtin_amdgcn_sched_barrier(0);
             const int s_load = kt + PF;
-            if constexpr (T::SINGLE) {
+            if constexpr (UNIFORM) {
+                // steps issued so far: 0 .. kt+PF-1; those after kt+1 may stay in flight
+                wait_steps(PF - 2);
+                __syncthreads();
+                pp.template issue<SL>(voff_cur, s_load, K, zeros, kb_cur);
+            } else if constexpr (T::SINGLE) {
                 // steps issued so far: 0 .. kt+PF-1 while they exist (by the prologue and
                 // the steps before); those after kt+1 may stay in flight
                 wait_steps(min(kt + PF - 1, KTp - 1) - kt - 1);
@@ -627,6 +646,11 @@ fused_proj_fast_kernel(KernelArgs p) {
             if constexpr (STAGES >= 4) if (kt + 2 < KTp) k_step(std::integral_constant<int, 2>{}, kt + 2);
             if constexpr (STAGES >= 5) if (kt + 3 < KTp) k_step(std::integral_constant<int, 3 % STAGES>{}, kt + 3);
             if constexpr (STAGES >= 6) if (kt + 4 < KTp) k_step(std::integral_constant<int, 4 % STAGES>{}, kt + 4);
+            if constexpr (UNIFORM) {
+                // the loads past the last step, before the epilogue takes over the stage area
+                wait_vmcnt<0>();
+                __syncthreads();
+            }
         } else {
             do {
                 k_step(std::integral_constant<int, 0>{}, kt);
@@ -692,8 +716,8 @@ fused_proj_fast_kernel(KernelArgs p) {
                           (C::W_BYTES == C::X_BYTES && C::W_BYTES + PAD >= C::NW / 2 * kRestageRows * kRestageRow),
                       "restage regions");
         constexpr int RGN = kRestageRows * kRestageRow;
-        // single-tile workgroups: no load is in flight after the last K step's wait and
-        // every wave has passed its barrier, so the whole stage area is free
+        // single-tile workgroups: no load is in flight after the last K step's wait (or the
+        // wait after it) and every wave has passed its barrier, so the whole stage area is free
         const unsigned wave_lds = T::SINGLE          ? pp.lds0 + wave * RGN
                                   : wave < C::NW / 2 ? pp.lds0 + (STAGES - 1) * C::W_BYTES + wave * RGN
                                                      : pp.lds0 + C::X_REGION + (STAGES - 1) * C::X_BYTES +
