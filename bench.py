@@ -28,6 +28,9 @@ Also on the line:
   backward      fused_proj_backward (dy, dx, dW and db launches) timed per config, the
                 headline's gradients checked against the float64 backward oracle;
   sclk_mhz      the graphics clock sampled while the headline kernel runs;
+  mfma_ceiling  the bf16 rate the matrix cores sustain alone (an MFMA-only kernel on
+                pseudo-random operands, clock sampled), and frac_of_mfma_ceiling beside
+                roofline.frac for the headline and every MFMA-bound configuration;
   context       the pages' own figures for the pathology this op removes.
 """
 from __future__ import annotations
@@ -66,11 +69,15 @@ CONTEXT = {
 }
 
 
+# the MFMA-only calibration kernel runs in none of the profiled launches
+HASH_EXCLUDED = {"mfma_ceiling.hip"}
+
+
 def kernel_hash() -> str:
     """Hash of every kernel and C-ABI source: ties committed counter summaries to the code."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".cpp", ".h")):
+        if name.endswith((".hip", ".cpp", ".h")) and name not in HASH_EXCLUDED:
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(name.encode())
                 h.update(f.read())
@@ -190,6 +197,34 @@ def sample_sclk(launch, kernel_us: float, seconds: float = 0.4):
             amdsmi.amdsmi_shut_down()
         except Exception:
             pass
+
+
+def measure_mfma_ceiling(dev, min_warmup_s: float, iterations: int = 2000, steps: int = 20):
+    """The bf16 rate the matrix cores sustain on their own on this GPU: launches of a kernel
+    that issues only v_mfma_f32_32x32x16_bf16 (one wave per SIMD on every CU, 8 independent
+    accumulators, pseudo-random operands rotated between instructions;
+    fused_proj_mfma_ceiling), timed like the projection, with the clock sampled while they
+    run. The published peak assumes the top clock; this is what the power limit leaves."""
+    import torch
+
+    import ff_input_projection_amd as fpa
+
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(cus * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    flops = fpa.mfma_ceiling_launch(iterations, sink, stream)
+
+    def launch(i):
+        fpa.mfma_ceiling_launch(iterations, sink, stream, seed=12345 + i)
+
+    t = time_launches(launch, steps, 4, min_warmup_s, stream)
+    sclk = sample_sclk(launch, t["mean_us"])
+    torch.cuda.synchronize()
+    return {"tflop_per_s": round(flops / (t["mean_us"] * 1e-6) / 1e12, 1),
+            "tflop_per_s_median": round(flops / (t["median_us"] * 1e-6) / 1e12, 1),
+            "us_per_launch": round(t["mean_us"], 1), "sclk_mhz": sclk.get("median") if sclk else None,
+            "kernel": f"fused_proj_mfma_ceiling: v_mfma_f32_32x32x16_bf16 only, {cus} CUs x 4 waves x "
+                      f"{iterations * 16} MFMAs, pseudo-random bf16 operands"}
 
 
 def measure_stream_ceiling(dev, read_bytes, write_bytes, row_elems, dtype, steps, min_warmup_s):
@@ -498,6 +533,13 @@ def main() -> int:
         "kernel": desc, "kernel_hash": kernel_hash(),
         "context": CONTEXT,
     }
+    # the matrix cores' own sustained rate, beside the published peak (bf16 workloads)
+    mfma_ceiling = None
+    if wl.dtype == "bf16" and not args.graph:
+        mfma_ceiling = measure_mfma_ceiling(dev, min(args.min_warmup_s, 1.0))
+        result["mfma_ceiling"] = mfma_ceiling
+        result["frac_of_mfma_ceiling"] = round(tflops / mfma_ceiling["tflop_per_s"], 4)
+        print(f"[bench] sustained MFMA rate: {mfma_ceiling}", file=sys.stderr, flush=True)
 
     # ---- every configuration of the workload table, timed the same way (GPU first;
     # the oracle checks follow on the CPU)
@@ -576,6 +618,8 @@ def main() -> int:
                  "tflop_per_s": round(c_tflops, 2), "gb_per_s": round(c_gbs, 1), "bound": c_roof["bound"],
                  "frac": c_roof["frac"], "frac_at_median": round(roofline_of(cw, ct["median_us"])[2]["frac"], 4),
                  "kernel": cdesc}
+        if mfma_ceiling is not None and cw.dtype == "bf16" and c_roof["bound"] == "mfma":
+            entry["frac_of_mfma_ceiling"] = round(c_tflops / mfma_ceiling["tflop_per_s"], 4)
         if name == "smallk_qkv_bf16" and ceiling is not None:
             # the same bytes through a plain streaming kernel in this harness
             entry["stream_ceiling"] = ceiling

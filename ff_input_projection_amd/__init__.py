@@ -27,7 +27,8 @@ LIB_PATH = os.path.join(_PKG, "libfused_proj.so")
 EXPORTED_SYMBOLS = ["fused_proj_validate", "fused_proj_create", "fused_proj_run", "fused_proj_destroy",
                     "fused_proj_strerror", "fused_proj_describe", "fused_proj_backward_workspace_size",
                     "fused_proj_backward", "fused_proj_backward_noalloc", "fused_proj_noalloc_scratch_bytes",
-                    "split_rope_validate", "split_rope_create", "split_rope_run", "split_rope_destroy"]
+                    "split_rope_validate", "split_rope_create", "split_rope_run", "split_rope_destroy",
+                    "fused_proj_mfma_ceiling"]
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, EALIAS, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 BF16, F32 = 0, 1
@@ -112,6 +113,9 @@ def load_library():
     lib.split_rope_run.restype = ctypes.c_int
     lib.split_rope_destroy.argtypes = [vp]
     lib.split_rope_destroy.restype = ctypes.c_int
+    lib.fused_proj_mfma_ceiling.argtypes = [ctypes.c_int, ctypes.c_uint, vp, ctypes.c_size_t, vp,
+                                            ctypes.POINTER(ctypes.c_double)]
+    lib.fused_proj_mfma_ceiling.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -134,6 +138,22 @@ def _check_single_hip_runtime():
 
 def strerror(code: int) -> str:
     return load_library().fused_proj_strerror(code).decode()
+
+
+def mfma_ceiling_launch(iterations: int, sink: torch.Tensor, stream=None, seed: int = 12345) -> float:
+    """Enqueues one launch of the MFMA-only calibration kernel (fused_proj_mfma_ceiling)
+    on `stream` (default: the current stream of sink's device); returns its flop count.
+    sink: a float32 device tensor of at least CUs * 256 elements."""
+    lib = load_library()
+    if stream is None:
+        stream = torch.cuda.current_stream(sink.device)
+    flops = ctypes.c_double(0.0)
+    rc = lib.fused_proj_mfma_ceiling(int(iterations), int(seed) & 0xFFFFFFFF, ctypes.c_void_p(sink.data_ptr()),
+                                     sink.numel() * sink.element_size(), ctypes.c_void_p(stream.cuda_stream),
+                                     ctypes.byref(flops))
+    if rc != OK:
+        raise FusedProjError(rc, "fused_proj_mfma_ceiling")
+    return flops.value
 
 
 _DTYPES = {torch.bfloat16: BF16, torch.float32: F32}

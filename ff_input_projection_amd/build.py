@@ -19,7 +19,7 @@ OBJDIR = os.path.join(PKG, "_build")
 FAST_PARTS = 5
 SOURCES = [os.path.join(CSRC, "fused_proj_api.cpp"), os.path.join(CSRC, "fused_proj_kernels.hip"),
            os.path.join(CSRC, "fused_proj_fast.hip"), os.path.join(CSRC, "split_rope.hip"),
-           os.path.join(CSRC, "fused_proj_bwd.hip")]
+           os.path.join(CSRC, "fused_proj_bwd.hip"), os.path.join(CSRC, "mfma_ceiling.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

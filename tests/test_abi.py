@@ -11,7 +11,7 @@ import ff_input_projection_amd as fpa
 from ff_input_projection_amd import Desc, make_desc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("fused_proj.h", "split_rope.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("fused_proj.h", "split_rope.h", "fused_proj_calibrate.h")]
 
 
 def declared_functions():
@@ -184,3 +184,18 @@ def test_null_handles_and_strerror():
     for code in (0, -1, -2, -3, -4):
         assert len(fpa.strerror(code)) > 3
     assert "unknown" in fpa.strerror(42)
+
+
+def test_mfma_ceiling_rejects_bad_arguments():
+    """The calibration call checks its arguments before touching a device."""
+    import ctypes
+
+    lib = fpa.load_library()
+    sink = (ctypes.c_float * 16)()
+    flops = ctypes.c_double(-1.0)
+    # no iterations, no flop counter, no sink
+    assert lib.fused_proj_mfma_ceiling(0, 1, ctypes.cast(sink, ctypes.c_void_p), 64, None, ctypes.byref(flops)) == \
+        fpa.EINVAL
+    assert lib.fused_proj_mfma_ceiling(10, 1, ctypes.cast(sink, ctypes.c_void_p), 64, None, None) == fpa.EINVAL
+    assert lib.fused_proj_mfma_ceiling(10, 1, None, 64, None, ctypes.byref(flops)) == fpa.EINVAL
+    assert flops.value == -1.0
