@@ -168,6 +168,19 @@ def test_tight_bar_is_reported_for_bf16():
     assert abs(v.max_tight_ratio - expect) < 1e-12
 
 
+def test_backward_diagnostic_is_the_backward_bar():
+    """compare_backward reports its own bar as the diagnostic: an error at 0.9 of the
+    backward bar on a near-zero gradient element reads 0.9 twice (the forward's 2^-8 |ref|
+    diagnostic would call the same element far over)."""
+    ref = np.array([[1e-6, 3.0]])
+    scl = np.array([[10.0, 10.0]])
+    got = ref + np.array([[0.9 * cmp.BACKWARD_REL["bf16"] * 10.0, 0.0]])
+    v = cmp.compare_backward([got], [ref], [scl], "bf16")
+    assert v.ok and abs(v.max_ratio - 0.9) < 1e-9 and abs(v.max_tight_ratio - 0.9) < 1e-9
+    f = cmp.compare([got], [ref], [scl], "bf16", rel=cmp.BACKWARD_REL["bf16"])
+    assert f.max_tight_ratio > 10.0
+
+
 def test_backward_scales_are_the_cauchy_schwarz_bounds():
     """backward_scales() against norms written out as loops: dx[t, c] scale
     sqrt(sum_f dy[t,f]^2) * sqrt(sum_f W[c,f]^2), dW[c, f] scale
