@@ -167,11 +167,12 @@ class Inputs:
 
 
 def make_inputs(wl: Workload, seed: int | None = None) -> Inputs:
-    """Draw x ~ N(0,1), W ~ N(0,1/C), bias ~ N(0,0.02) (second argument = variance)."""
+    """Draw x ~ N(0,1), W ~ N(0,1/C), bias ~ N(0,0.02) (second argument = variance).
+    With C = 0 (no channels) W is empty and its scale is irrelevant."""
     rng = np.random.default_rng(wl.seed if seed is None else seed)
     C, F = wl.C, wl.F
     x = rng.standard_normal(wl.x_shape)
-    w = rng.standard_normal((C, F)) * math.sqrt(1.0 / C)
+    w = rng.standard_normal((C, F)) * math.sqrt(1.0 / max(C, 1))
     if wl.w_layout == "fc":
         w = np.ascontiguousarray(w.T)
     b = rng.standard_normal(F) * math.sqrt(0.02) if wl.has_bias else None

@@ -6,8 +6,11 @@ benchmark's CPU-baseline leg).
 The bar: |gpu - oracle| <= rel * scale, element by element, with
 scale = ||x_t|| * ||w_col|| + |b_col|, rel = 4e-3 for bf16 storage and 1e-5
 for fp32. For q/k elements after RoPE the output is itself a projection with
-the effective column w_eff = cos(phi) W[:, j] -/+ sin(phi) W[:, j'] (and the
-same mix of biases), since RoPE is linear; its norm is used. For GELU outputs
+the effective column w_eff = cos(phi) W[:, j] -/+ sin(phi) W[:, j'], since RoPE is
+linear; its norm is used. The bias enters such an element as two products,
+cos(phi) b_j -/+ sin(phi) b_j', and its part of the scale is the sum of their
+magnitudes (the usual bound for the rounding of a sum of products), which stays
+apart from zero where the two cancel (with C = 0 the bias is the whole output). For GELU outputs
 (either form) the pre-activation scale is used (both are under 1.13-Lipschitz).
 Squared ReLU doubles an input error by |y| at y: its outputs o use the
 pre-activation scale times (1 + 2 sqrt(o)), which bounds
@@ -117,8 +120,9 @@ def scales(rows: np.ndarray, positions: np.ndarray, w_cf: np.ndarray, bias: np.n
         # first half: c w1 - s w2 ; second half: c w2 + s w1
         e1 = np.sqrt(np.maximum(c * c * n1 + s * s * n2 - 2 * c * s * d12, 0.0))
         e2 = np.sqrt(np.maximum(c * c * n2 + s * s * n1 + 2 * c * s * d12, 0.0))
-        b1 = np.abs(c * bh[None, :, :half] - s * bh[None, :, half:R])
-        b2 = np.abs(c * bh[None, :, half:R] + s * bh[None, :, :half])
+        a1, a2 = np.abs(bh[None, :, :half]), np.abs(bh[None, :, half:R])
+        b1 = np.abs(c) * a1 + np.abs(s) * a2
+        b2 = np.abs(c) * a2 + np.abs(s) * a1
         sc = np.concatenate([xn[:, None, None] * e1 + b1, xn[:, None, None] * e2 + b2, s_plain[:, :, R:]], axis=2)
         out.append(sc)
     return Scales(ff, out[0], out[1], out[2])

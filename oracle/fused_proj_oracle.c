@@ -170,7 +170,8 @@ static void qkv_column(int64_t r, int64_t n_heads, int64_t n_kv, int64_t hd, int
  *
  *   x        float64 activation; element (bi, c, s) at
  *            bi*sb + c*sc + sum_d idx_d(s)*sp_stride[d]
- *   nb, C, S slabs, channels, tokens per slab (S = prod sp_size)
+ *   nb, C, S slabs, channels, tokens per slab (S = prod sp_size); C may be 0,
+ *            an empty contraction: y is then the bias (or zero)
  *   w        float64 weight, [C,F] (w_fc=0) or [F,C] (w_fc=1)
  *   bias     float64 [F] or NULL
  *   ff_dim   width of the ff slice; F = ff_dim + 3*n_heads*head_dim
@@ -198,7 +199,7 @@ int oracle_fused_proj(const double *x, int64_t nb, int64_t C, int64_t S, int64_t
                       double *ff_rows, double *q_rows, double *k_rows, double *v_rows,
                       int nthreads)
 {
-    if (!x || !w || !tokens || nb <= 0 || C <= 0 || S <= 0 || nsp < 1 || nsp > 3 || ntok < 0)
+    if (!x || !w || !tokens || nb <= 0 || C < 0 || S <= 0 || nsp < 1 || nsp > 3 || ntok < 0)
         return ORACLE_EINVAL;
     int64_t prod = 1;
     for (int d = 0; d < nsp; ++d) {
@@ -230,7 +231,7 @@ int oracle_fused_proj(const double *x, int64_t nb, int64_t C, int64_t S, int64_t
 #pragma omp parallel
     {
         double *y = (double *)malloc((size_t)F * sizeof(double));
-        double *xr = (double *)malloc((size_t)C * sizeof(double));
+        double *xr = (double *)malloc((size_t)(C > 0 ? C : 1) * sizeof(double));
         if (!y || !xr) {
 #pragma omp atomic write
             status = ORACLE_EINVAL;
@@ -411,7 +412,7 @@ int oracle_fused_proj_backward(const double *x, int64_t nb, int64_t C, int64_t S
                                const double *d_ff, const double *dq, const double *dk, const double *dv,
                                double *dy, double *dx_rows, double *dw, double *db, int nthreads)
 {
-    if (!x || !w || !dy || !dx_rows || !dw || nb <= 0 || C <= 0 || S <= 0 || nsp < 1 || nsp > 3)
+    if (!x || !w || !dy || !dx_rows || !dw || nb <= 0 || C < 0 || S <= 0 || nsp < 1 || nsp > 3)
         return ORACLE_EINVAL;
     int64_t prod = 1;
     for (int d = 0; d < nsp; ++d) {
@@ -442,7 +443,7 @@ int oracle_fused_proj_backward(const double *x, int64_t nb, int64_t C, int64_t S
 #pragma omp parallel
     {
         double *y = (double *)malloc((size_t)F * sizeof(double));
-        double *xr = (double *)malloc((size_t)C * sizeof(double));
+        double *xr = (double *)malloc((size_t)(C > 0 ? C : 1) * sizeof(double));
         double *g = (double *)malloc((size_t)(head_dim > 0 ? head_dim : 1) * sizeof(double));
         if (!y || !xr || !g) {
 #pragma omp atomic write

@@ -43,9 +43,18 @@ def brute_force_scales(x, w, b, S, ff_dim, H, hd, rope, pos_offset, kvh, order, 
                               **kw)
         for p in parts:
             weff[p].append(_rows(r, p))
+    bterm = {p: 0.0 for p in parts}
     if b is not None:
-        beff = oracle.fused_proj(np.zeros((1, S, C)), "tokens_last", w, "cf", b, ff_dim, "none", H, hd, rope,
-                                 10000.0, pos_offset, **kw)
+        # the bias's part: sum over bias entries j of |d out / d b_j| * |b_j|, each
+        # derivative read from a run with a one-hot bias and x = 0
+        for j in range(w.shape[1]):
+            ej = np.zeros(w.shape[1])
+            ej[j] = 1.0
+            r = oracle.fused_proj(np.zeros((1, S, C)), "tokens_last", w, "cf", ej, ff_dim, "none", H, hd, rope,
+                                  10000.0, pos_offset, **kw)
+            for p in parts:
+                if _rows(r, p) is not None:
+                    bterm[p] = bterm[p] + np.abs(_rows(r, p)) * abs(b[j])
     xn = np.linalg.norm(x[0], axis=1)                              # [S]
     act_out = oracle.fused_proj(x, "tokens_last", w, "cf", b, ff_dim, ff_act, H, hd, rope, 10000.0, pos_offset,
                                 **kw)
@@ -57,7 +66,7 @@ def brute_force_scales(x, w, b, S, ff_dim, H, hd, rope, pos_offset, kvh, order, 
         stack = np.stack(weff[p], axis=0)                          # [C, S, ...]
         wn = np.sqrt((stack ** 2).sum(axis=0))                     # [S, ...]
         xs = xn.reshape((S,) + (1,) * (wn.ndim - 1))
-        bar = xs * wn + (np.abs(_rows(beff, p)) if b is not None else 0.0)
+        bar = xs * wn + bterm[p]
         if p == "ff" and ff_act == "relu2":
             bar = bar * (1.0 + 2.0 * np.sqrt(np.maximum(act_out.ff, 0.0)))
         out[p] = bar
@@ -77,10 +86,10 @@ CASES = [
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_scales_equal_brute_force_bar(case):
-    """scales() == the bar built from the oracle's own effective columns. Catches the
-    column norm over the wrong axis, the sign of the RoPE cross term, a bias mixed with
-    the wrong sign or partner, the partner taken over the head instead of the rotated
-    width, and a wrong squared-ReLU factor."""
+    """scales() == the bar built from the oracle's own effective columns and the
+    magnitudes of the bias's terms. Catches the column norm over the wrong axis, the sign
+    of the RoPE cross term, a bias mixed with the wrong partner, the partner taken over the
+    head instead of the rotated width, and a wrong squared-ReLU factor."""
     name, C, S, ff_dim, H, hd, kvh, order, rope, rd, off, has_b, act = case
     K = kvh if kvh > 0 else H
     F = ff_dim + (H + 2 * K) * hd

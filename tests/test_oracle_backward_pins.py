@@ -164,6 +164,34 @@ def test_dy_without_activation_or_rope_is_the_upstream_gradient():
                     np.testing.assert_array_equal(bw.dy[t, col:col + hd], g[bi * H + h, s])
 
 
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_no_channels_equals_one_zero_channel(case):
+    """C = 0: dx and dW are empty, and dy and db must equal, bit for bit, those of a run
+    with one channel whose x is zero (the pre-activation is the bias in both)."""
+    _, layout, x_shape, w_layout, bias, ff_dim, act, H, KVH, hd, order, rope, rd, pos, ff_layout = case
+    KVH = KVH or H
+    F = ff_dim + (H + 2 * KVH) * hd
+    nb = x_shape[0]
+    S = math.prod(x_shape[2:]) if layout == "channels_first" else x_shape[1]
+    ci = 1 if layout == "channels_first" else 2
+    shape0, shape1 = list(x_shape), list(x_shape)
+    shape0[ci], shape1[ci] = 0, 1
+    r = np.random.default_rng(51)
+    b = r.standard_normal(F) * 0.3 if bias else None
+    w1 = r.standard_normal((1, F)) if w_layout == "cf" else r.standard_normal((F, 1))
+    w0 = np.zeros((0, F)) if w_layout == "cf" else np.zeros((F, 0))
+    grads = _grads(r, nb, S, ff_dim, ff_layout, H, KVH, hd)
+    kw = dict(rope_base=10000.0, pos_offset=pos, n_kv_heads=KVH, qkv_order=order, rope_dims=rd, ff_layout=ff_layout)
+    b0 = oracle.fused_proj_backward(np.zeros(shape0), layout, w0, w_layout, b, ff_dim, act, H, hd, rope, *grads, **kw)
+    b1 = oracle.fused_proj_backward(np.zeros(shape1), layout, w1, w_layout, b, ff_dim, act, H, hd, rope, *grads, **kw)
+    assert b0.dx.size == 0 and b0.dw.size == 0
+    assert np.count_nonzero(b1.dw) == 0
+    np.testing.assert_array_equal(b0.dy, b1.dy)
+    if bias:
+        np.testing.assert_array_equal(b0.db, b1.db)
+        np.testing.assert_allclose(b0.db, b0.dy.sum(axis=0), rtol=1e-12, atol=1e-12)
+
+
 @pytest.mark.parametrize("act,torch_act", [("gelu", "none"), ("gelu_tanh", "tanh"), ("relu2", None)])
 def test_activation_derivatives_equal_torch_autograd(act, torch_act):
     """dy = d_ff * act'(y) with W = 0, so that y equals the bias, against torch's autograd of

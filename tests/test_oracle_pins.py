@@ -190,6 +190,32 @@ def test_zero_weight_gives_activated_bias():
     assert np.array_equal(res.q[:, 0].reshape(-1), b[FF:FF + H * hd])  # position 0
 
 
+@pytest.mark.parametrize("layout,x_shape", [("channels_first", (2, 0, 3, 4, 1)), ("tokens_last", (2, 6, 0))])
+def test_no_channels_equals_one_zero_channel(layout, x_shape):
+    """C = 0: the contraction is an empty sum, so y = b. The result must equal, bit for
+    bit, a run with one channel whose x is zero (0 * w = 0 exactly), for any weight row;
+    and v = b and an identity ff slice = b exactly."""
+    FF, H, hd = 6, 2, 4
+    F = FF + 3 * H * hd
+    b = np.linspace(-2.0, 2.0, F)
+    x0 = np.zeros(x_shape)
+    one = list(x_shape)
+    one[1 if layout == "channels_first" else 2] = 1
+    x1 = np.zeros(one)
+    w1 = np.random.default_rng(7).standard_normal((1, F))
+    for act in ("none", "gelu", "relu2"):
+        r0 = oracle.fused_proj(x0, layout, np.zeros((0, F)), "cf", b, FF, act, H, hd, rope=True, pos_offset=3)
+        r1 = oracle.fused_proj(x1, layout, w1, "cf", b, FF, act, H, hd, rope=True, pos_offset=3)
+        for a0, a1 in zip((r0.ff, r0.q, r0.k, r0.v), (r1.ff, r1.q, r1.k, r1.v)):
+            assert np.array_equal(a0, a1)
+        if act == "none":
+            assert np.array_equal(r0.ff.reshape(-1, FF), np.broadcast_to(b[:FF], (r0.ff.size // FF, FF)))
+        v = r0.v.reshape(2, H, -1, hd).transpose(0, 2, 1, 3).reshape(-1, H * hd)   # [b*S, H*hd]
+        assert np.array_equal(v, np.broadcast_to(b[FF + 2 * H * hd:], v.shape))
+    r_nb = oracle.fused_proj(x0, layout, np.zeros((F, 0)), "fc", None, FF, "gelu", H, hd, rope=True)
+    assert all(np.count_nonzero(a) == 0 for a in (r_nb.ff, r_nb.q, r_nb.k, r_nb.v))
+
+
 def _gelu_via_oracle(vals):
     """Run the oracle with W = I on the FF slice so that ff = gelu(x)."""
     n = len(vals)
