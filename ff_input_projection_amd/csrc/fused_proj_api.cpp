@@ -101,24 +101,28 @@ int check_desc(const fused_proj_desc* d, Derived* out) {
     }
     // a channels-first ff output is stored V tokens of one column at a time
     if (d->ff_layout == FUSED_PROJ_FF_CHANNELS_FIRST && d->ff_dim > 0 && S % V) return FUSED_PROJ_EUNSUPPORTED;
-    // Canonical strides.
+    // Canonical strides. x is read only when it holds elements (C > 0 and b*S > 0); an
+    // empty x may report any strides (an empty tensor's carry no layout), so they are
+    // checked only then.
+    const bool x_read = d->channels > 0 && r.M > 0;
     r.sb = d->x_stride_batch;
     r.sc = d->x_stride_channel;
     if (d->x_layout == FUSED_PROJ_X_TOKENS_LAST) {
         r.ss = d->x_stride_spatial[0];
-        if (d->channels > 1 && r.sc != 1) return FUSED_PROJ_EUNSUPPORTED;
+        if (x_read && d->channels > 1 && r.sc != 1) return FUSED_PROJ_EUNSUPPORTED;
         r.sc = 1;
-        if ((S > 1 && r.ss % V) || (d->batch > 1 && r.sb % V)) return FUSED_PROJ_EUNSUPPORTED;
+        if (x_read && ((S > 1 && r.ss % V) || (d->batch > 1 && r.sb % V))) return FUSED_PROJ_EUNSUPPORTED;
     } else {
         // spatial dims must flatten into one unit-stride token index
         int64_t expect = 1;
         for (int i = d->n_spatial - 1; i >= 0; --i) {
-            if (d->spatial[i] > 1 && d->x_stride_spatial[i] != expect) return FUSED_PROJ_EUNSUPPORTED;
+            if (x_read && d->spatial[i] > 1 && d->x_stride_spatial[i] != expect) return FUSED_PROJ_EUNSUPPORTED;
             expect = mul_cap(expect, d->spatial[i]);
             if (expect < 0) return FUSED_PROJ_EUNSUPPORTED;
         }
         r.ss = 1;
-        if (S % V || (d->channels > 1 && r.sc % V) || (d->batch > 1 && r.sb % V)) return FUSED_PROJ_EUNSUPPORTED;
+        if (S % V) return FUSED_PROJ_EUNSUPPORTED;
+        if (x_read && ((d->channels > 1 && r.sc % V) || (d->batch > 1 && r.sb % V))) return FUSED_PROJ_EUNSUPPORTED;
     }
     // Offsets must stay below 2^62.
     if (r.M > 0 && d->channels > 0) {

@@ -116,7 +116,8 @@ typedef struct fused_proj_desc {
                                   is computed from the bias alone (y = bias) */
     int32_t n_spatial;         /* 1..3 for channels-first, exactly 1 for tokens-last */
     int64_t spatial[3];        /* sizes of the spatial dims; S = their product */
-    int64_t x_stride_batch;    /* element strides of x, all >= 0 */
+    int64_t x_stride_batch;    /* element strides of x, all >= 0; their layout is checked
+                                  only when x holds elements (C > 0 and b*S > 0) */
     int64_t x_stride_channel;
     int64_t x_stride_spatial[3];
     int32_t w_layout;          /* FUSED_PROJ_W_* */
@@ -152,7 +153,9 @@ typedef struct fused_proj_plan *fused_proj_t;
  *   channels-first: spatial strides that flatten into one unit-stride token
  *   index (stride of the last spatial dim 1, each outer stride the product of the
  *   inner sizes), S, x_stride_channel and x_stride_batch multiples of V;
- *   tokens-last: x_stride_channel 1, token and batch strides multiples of V;
+ *   tokens-last: x_stride_channel 1, token and batch strides multiples of V
+ *   (the stride rules of both layouts apply only when x holds elements: C > 0
+ *   and b*S > 0; S stays a multiple of V for channels-first);
  *   every element offset of x, W and the outputs below 2^62.
  */
 int fused_proj_validate(const fused_proj_desc *desc);

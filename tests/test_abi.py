@@ -173,6 +173,26 @@ def test_validate_accepts_edge_shapes():
     assert fpa.validate(d) == fpa.OK
 
 
+@pytest.mark.parametrize("shape,strides,layout", [
+    ((2, 0, 8, 8, 1), (0, 0, 0, 0, 0), "channels_first"),    # an empty array's strides
+    ((2, 0, 8, 8, 1), (64, 64, 8, 1, 1), "channels_first"),
+    ((3, 40, 0), (0, 0, 0), "tokens_last"),
+    ((0, 64, 8, 8, 1), (0, 0, 0, 0, 0), "channels_first"),   # no tokens
+])
+def test_validate_ignores_the_strides_of_an_empty_x(shape, strides, layout):
+    """x is read only when it holds elements (C > 0 and b*S > 0); an empty x passes with
+    whatever non-negative strides it reports, while a non-empty x with all-zero strides is
+    refused and a negative stride is malformed either way."""
+    import torch
+    kw = dict(has_bias=True, ff_dim=64, ff_act="gelu", n_heads=2, head_dim=32, rope=True)
+    assert fpa.validate(make_desc(shape, strides, layout, torch.bfloat16, **kw)) == fpa.OK
+    if not any(strides):
+        full = tuple(8 if n == 0 else n for n in shape)
+        assert fpa.validate(make_desc(full, strides, layout, torch.bfloat16, **kw)) == fpa.EUNSUPPORTED
+    neg = (-1,) + tuple(strides[1:])
+    assert fpa.validate(make_desc(shape, neg, layout, torch.bfloat16, **kw)) == fpa.EINVAL
+
+
 def test_null_handles_and_strerror():
     lib = fpa.load_library()
     assert lib.fused_proj_validate(None) == fpa.EINVAL

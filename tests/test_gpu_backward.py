@@ -199,6 +199,23 @@ def test_backward_no_tokens_gives_zero_weight_gradients():
     assert torch.count_nonzero(dw).item() == 0 and torch.count_nonzero(db).item() == 0
 
 
+NO_CHANNELS = [
+    with_shape(WORKLOADS["walrus_bf16"], "bwd_c0_cf_gelu_rope", x_shape=(2, 0, 8, 8, 1), ff_dim=64, n_heads=2,
+               head_dim=32),
+    with_shape(WORKLOADS["bert_ff_relu2_bf16"], "bwd_c0_tl_relu2_fc", x_shape=(3, 40, 0), ff_dim=136,
+               w_layout="fc"),
+    with_shape(WORKLOADS["tiny_f32"], "bwd_c0_f32", x_shape=(1, 0, 8, 8, 1)),
+]
+
+
+@pytest.mark.parametrize("wl", NO_CHANNELS, ids=[w.name for w in NO_CHANNELS])
+def test_backward_no_channels_gives_the_bias_gradient(wl, kernel_choice):
+    """C = 0: dx and dW hold no elements; db is the sum over tokens of dy, whose ff part
+    takes the activation's derivative at y = b and whose q/k part is rotated back."""
+    assert wl.C == 0
+    _check(wl, f"{wl.name} {kernel_choice}")
+
+
 def test_backward_deterministic_and_graph_replays():
     """Two eager calls give identical bits; a captured call replays to the same bits three
     times (the workspace and outputs are refilled with NaN between replays)."""

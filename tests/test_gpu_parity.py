@@ -439,6 +439,40 @@ def test_empty_batch_is_a_noop():
     assert ff.numel() == 0 and q.numel() == 0
 
 
+NO_CHANNELS = [
+    # channels-first, exact GELU, RoPE over heads of 32, bias: ff = gelu(b), q/k = RoPE(b)
+    with_shape(WORKLOADS["walrus_bf16"], "c0_cf_gelu_rope", x_shape=(2, 0, 8, 8, 1), ff_dim=64, n_heads=2,
+               head_dim=32),
+    # fp32, channels-first, 224 columns (two column tiles, the last ragged)
+    with_shape(WORKLOADS["tiny_f32"], "c0_f32", x_shape=(1, 0, 8, 8, 1)),
+    # token-major, squared ReLU on a ragged ff slice of 136, three slabs of 40 tokens
+    with_shape(WORKLOADS["bert_ff_relu2_bf16"], "c0_tl_relu2", x_shape=(3, 40, 0), ff_dim=136),
+    # grouped q/k/v with RoPE on 8 of 32, no bias: every output is zero
+    with_shape(WORKLOADS["gqa_rope8_bf16"], "c0_gqa_no_bias", x_shape=(2, 40, 0)),
+    # channels-first ff output
+    with_shape(WORKLOADS["conv1x1_walrus_bf16"], "c0_ff_channels_first", x_shape=(2, 0, 4, 4, 1), ff_dim=256),
+]
+
+
+@pytest.mark.parametrize("choice", ["auto", "general", "fast"])
+@pytest.mark.parametrize("wl", NO_CHANNELS, ids=[w.name for w in NO_CHANNELS])
+def test_no_channels_outputs_the_bias(wl, choice, monkeypatch):
+    """C = 0: the contraction is empty, so every output is the bias through the activation
+    or RoPE (zero without a bias). x and W hold no elements; every output element is
+    compared with the oracle. The fast kernel runs one K step read from its zero block."""
+    if choice == "auto":
+        monkeypatch.delenv("FUSED_PROJ_KERNEL", raising=False)
+    else:
+        monkeypatch.setenv("FUSED_PROJ_KERNEL", choice)
+    inp = make_inputs(wl)
+    assert wl.C == 0 and inp.x.numel() == 0 and inp.w.numel() == 0
+    print(f"[case] no channels {wl.name} kernel={choice}", flush=True)
+    proj, outs = run_gpu(wl, inp, DEV)
+    print(f"[plan] {proj.describe()}", flush=True)
+    v = _check(wl, inp, outs, all_tokens(wl), f"{wl.name} {choice}")
+    assert v.n == wl.M * wl.F
+
+
 def test_run_error_paths():
     wl = SMALL[0]
     inp = make_inputs(wl)
