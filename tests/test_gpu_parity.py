@@ -473,6 +473,36 @@ def test_no_channels_outputs_the_bias(wl, choice, monkeypatch):
     assert v.n == wl.M * wl.F
 
 
+DECODE = [
+    # one new token per sequence (a decode step): 16 sequences at position 4095 of the
+    # decoder's 4096-token context, RoPE over heads of 128, no bias (96 column tiles)
+    with_shape(WORKLOADS["decoder_qkv_rope_bf16"], "decode_16_at_4095", x_shape=(16, 1, 4096), pos_offset=4095),
+    # a single sequence, grouped q/k/v with RoPE on 8 of 32, at position 1023
+    with_shape(WORKLOADS["gqa_rope8_bf16"], "decode_gqa_1_at_1023", x_shape=(1, 1, 512), pos_offset=1023),
+    # fp32, token-major, exact GELU and RoPE over heads of 8, 3 sequences at position 77
+    with_shape(WORKLOADS["tiny_f32"], "decode_f32_3_at_77", layout="tokens_last", x_shape=(3, 1, 32),
+               pos_offset=77),
+]
+
+
+@pytest.mark.parametrize("choice", ["auto", "general"])
+@pytest.mark.parametrize("wl", DECODE, ids=[w.name for w in DECODE])
+def test_decode_step_one_token_per_sequence(wl, choice, monkeypatch):
+    """S = 1 with a position offset: every sequence's token sits at the offset, so RoPE
+    rotates all of them by the same angles; each output element against the oracle."""
+    if choice == "general":
+        monkeypatch.setenv("FUSED_PROJ_KERNEL", "general")
+    else:
+        monkeypatch.delenv("FUSED_PROJ_KERNEL", raising=False)
+    assert wl.S == 1 and wl.pos_offset > 0
+    inp = make_inputs(wl)
+    print(f"[case] decode step {wl.name} kernel={choice}", flush=True)
+    proj, outs = run_gpu(wl, inp, DEV)
+    print(f"[plan] {proj.describe()}", flush=True)
+    v = _check(wl, inp, outs, all_tokens(wl), f"{wl.name} {choice}")
+    assert v.n == wl.M * wl.F
+
+
 def test_run_error_paths():
     wl = SMALL[0]
     inp = make_inputs(wl)
