@@ -97,9 +97,11 @@ static double gelu_tanh(double y)
     return 0.5 * y * (1.0 + tanh(k * (y + 0.044715 * y * y * y)));
 }
 
+/* max(y, 0)^2; a NaN is not clamped to 0 but passes through, as it does through
+ * torch's relu (and through both GELU forms above in IEEE arithmetic). */
 static double relu_squared(double y)
 {
-    const double r = y > 0.0 ? y : 0.0;
+    const double r = (y > 0.0 || isnan(y)) ? y : 0.0;
     return r * r;
 }
 

@@ -37,7 +37,11 @@ MUTATIONS = [
      "return 0.5 * y * (1.0 + tanh(0.7978845608028654 * (y + 0.044715 * y * y * y)));"),
     ("tanh GELU constant", "0.044715 * y * y * y", "0.04715 * y * y * y"),
     ("tanh GELU without the cube", "(y + 0.044715 * y * y * y)", "(y + 0.044715 * y * y)"),
-    ("squared ReLU without the clamp", "const double r = y > 0.0 ? y : 0.0;", "const double r = y;"),
+    ("squared ReLU without the clamp", "const double r = (y > 0.0 || isnan(y)) ? y : 0.0;", "const double r = y;"),
+    ("squared ReLU clamps NaN to 0", "const double r = (y > 0.0 || isnan(y)) ? y : 0.0;",
+     "const double r = y > 0.0 ? y : 0.0;"),
+    ("exact GELU of -inf taken as its limit 0", "return 0.5 * y * (1.0 + erf(y / sqrt(2.0)));",
+     "return isinf(y) && y < 0.0 ? 0.0 : 0.5 * y * (1.0 + erf(y / sqrt(2.0)));"),
     ("empty contraction rejected", "nb <= 0 || C < 0 || S <= 0 || nsp < 1 || nsp > 3 || ntok < 0",
      "nb <= 0 || C <= 0 || S <= 0 || nsp < 1 || nsp > 3 || ntok < 0"),
     ("squared ReLU not squared", "    return r * r;", "    return r;"),

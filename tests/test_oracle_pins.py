@@ -216,6 +216,24 @@ def test_no_channels_equals_one_zero_channel(layout, x_shape):
     assert all(np.count_nonzero(a) == 0 for a in (r_nb.ff, r_nb.q, r_nb.k, r_nb.v))
 
 
+def test_activations_at_non_finite_values_match_torch():
+    """The oracle's activations at NaN, +-inf and large values equal torch's float64 ones
+    (exact GELU, tanh GELU, squared ReLU through torch.relu): NaN passes through every
+    activation, GELU(+inf) = +inf, GELU(-inf) = NaN (y Phi(y) in IEEE arithmetic) and
+    relu^2(-inf) = 0. One channel with weight 1, so each token's y is its own value."""
+    import torch.nn.functional as F
+    vals = np.array([np.nan, np.inf, -np.inf, -1e3, -1.5, 0.0, 2.5, 1e3])
+    x = vals.reshape(1, -1, 1)
+    tv = torch.from_numpy(vals)
+    for act, ref in (("gelu", F.gelu(tv)), ("gelu_tanh", F.gelu(tv, approximate="tanh")),
+                     ("relu2", torch.relu(tv) ** 2)):
+        got = oracle.fused_proj(x, "tokens_last", np.ones((1, 1)), "cf", None, 1, act, 0, 0, rope=False).ff
+        got, ref = got.reshape(-1), ref.numpy()
+        assert np.array_equal(np.isnan(got), np.isnan(ref)), (act, got, ref)
+        fin = ~np.isnan(ref)
+        np.testing.assert_allclose(got[fin], ref[fin], rtol=1e-12, atol=0)
+
+
 def _gelu_via_oracle(vals):
     """Run the oracle with W = I on the FF slice so that ff = gelu(x)."""
     n = len(vals)
