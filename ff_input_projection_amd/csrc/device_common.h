@@ -45,9 +45,11 @@ __device__ __forceinline__ float gelu_erf(float y) {
 // gelu_poly_fit.py; absolute error of the whole GELU under 1e-5 in fp32, far below the
 // bf16 rounding of the outputs this serves). a is clamped
 // to 6 in both places it is used: past 6, |y| q(|y|) < 1e-8 and 6 q(6) stands for it.
-// Both clamps go through v_med3_f32: fminf / fmaxf would each put a canonicalizing
-// v_max_f32 in front (IEEE mode), 12 VALU instructions per value instead of 10. For
-// finite y, med3(|y|, 0, 6) = min(|y|, 6) and med3(y, 0, FLT_MAX) = max(y, 0) exactly.
+// The clamp is one v_med3_f32 (fminf would put a canonicalizing v_max_f32 in front in
+// IEEE mode). The positive part is (y + |y|) / 2, which is max(y, 0) exactly for finite y
+// and, unlike any min / max / med3 (all of which drop a quiet NaN), keeps what the
+// defining y Phi(y) gives in IEEE arithmetic: NaN for NaN, +inf for +inf, NaN for -inf.
+// 11 VALU instructions per value.
 __device__ __forceinline__ float gelu_erf_poly(float y) {
     const float a = __builtin_amdgcn_fmed3f(fabsf(y), 0.0f, 6.0f);
     float p = 2.2990056e-05f;
@@ -57,7 +59,7 @@ __device__ __forceinline__ float gelu_erf_poly(float y) {
     p = fmaf(p, a, -0.46127188f);
     p = fmaf(p, a, -1.1501743f);
     p = fmaf(p, a, -1.0000647f);
-    return fmaf(-a, __builtin_amdgcn_exp2f(p), __builtin_amdgcn_fmed3f(y, 0.0f, 3.40282347e+38f));
+    return fmaf(-a, __builtin_amdgcn_exp2f(p), 0.5f * (y + fabsf(y)));
 }
 
 // Its derivative with the same Phi(-a) = 2^P(a): d/dy [y Phi(y)] = Phi(y) + y phi(y), with
@@ -87,9 +89,9 @@ __device__ __forceinline__ float gelu_tanh(float y) {
     const float u2 = (y + 0.044715f * (y * y * y)) * (2.0f * 0.79788456080286536f * 1.4426950408889634f);
     return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u2));
 }
-// Squared ReLU, max(y, 0)^2.
+// Squared ReLU, max(y, 0)^2, with a max that keeps NaN (v_maximum3_f32), as torch's relu does.
 __device__ __forceinline__ float relu_squared(float y) {
-    const float r = y > 0.0f ? y : 0.0f;
+    const float r = __builtin_elementwise_maximum(y, 0.0f);
     return r * r;
 }
 

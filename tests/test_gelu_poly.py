@@ -18,8 +18,8 @@ def _coefficients():
     first = re.search(r"float p = ([-+0-9.e]+)f;", body).group(1)
     rest = re.findall(r"p = fmaf\(p, a, ([-+0-9.e]+)f\);", body)
     clamp = float(re.search(r"fmed3f\(fabsf\(y\), 0\.0f, ([0-9.]+)f\)", body).group(1))
-    # the positive part max(y, 0) is a med3 against FLT_MAX
-    assert re.search(r"fmed3f\(y, 0\.0f, 3\.40282347e\+38f\)", body)
+    # the positive part max(y, 0) is (y + |y|) / 2
+    assert "0.5f * (y + fabsf(y))" in body
     return [np.float32(first)] + [np.float32(c) for c in rest], np.float32(clamp)
 
 
@@ -31,8 +31,10 @@ def _gelu_poly_f32(y, coef, clamp):
         # fmaf: one rounding of the exact p * a + c
         p = (p.astype(np.float64) * a.astype(np.float64) + np.float64(c)).astype(np.float32)
     e = np.exp2(p.astype(np.float64)).astype(np.float32)
-    pos = np.minimum(np.maximum(y, np.float32(0)), np.finfo(np.float32).max)   # med3(y, 0, FLT_MAX)
-    out = -a.astype(np.float64) * e.astype(np.float64) + pos.astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        pos = np.float32(0.5) * (y + np.abs(y))                                 # (y + |y|) / 2, exact
+    with np.errstate(invalid="ignore"):
+        out = -a.astype(np.float64) * e.astype(np.float64) + pos.astype(np.float64)
     return out.astype(np.float32)
 
 
@@ -56,6 +58,20 @@ def test_polynomial_gelu_special_values():
     # gelu(0) = 0; gelu(y) - gelu(-y) = y (Phi(y) + Phi(-y) = 1)
     assert abs(got[0]) < 1e-9
     assert abs((got[1] - got[2]) - 1.0) < 2e-5 and abs((got[3] - got[4]) - 3.0) < 2e-5
+
+
+def test_polynomial_gelu_non_finite_values_follow_the_definition():
+    """y Phi(y) in IEEE arithmetic (the oracle's and torch's float64 GELU): NaN stays NaN,
+    +inf stays +inf, and -inf gives -inf * 0 = NaN. A min / max / med3 positive part would
+    turn NaN into a finite value."""
+    import torch
+    coef, clamp = _coefficients()
+    y = np.array([np.nan, np.inf, -np.inf], np.float32)
+    got = _gelu_poly_f32(y, coef, clamp)
+    ref = torch.nn.functional.gelu(torch.from_numpy(y.astype(np.float64))).numpy()
+    assert np.isnan(got[0]) and np.isnan(ref[0])
+    assert got[1] == np.inf and ref[1] == np.inf
+    assert np.isnan(got[2]) and np.isnan(ref[2])
 
 
 def _grad_coefficients():

@@ -503,6 +503,97 @@ def test_decode_step_one_token_per_sequence(wl, choice, monkeypatch):
     assert v.n == wl.M * wl.F
 
 
+NON_FINITE = [
+    # channels-first, exact GELU, RoPE over heads of 64, bias, 4 column tiles
+    with_shape(WORKLOADS["walrus_bf16"], "nonfinite_cf_gelu_rope", x_shape=(2, 64, 8, 8, 1), ff_dim=128,
+               n_heads=2, head_dim=64),
+    # token-major, squared ReLU, [F, C] weight, ragged tokens
+    with_shape(WORKLOADS["bert_ff_relu2_bf16"], "nonfinite_tl_relu2_fc", x_shape=(2, 70, 64), ff_dim=256,
+               w_layout="fc"),
+    # token-major, tanh GELU
+    with_shape(WORKLOADS["bert_ff_bf16"], "nonfinite_tl_tanh", x_shape=(2, 70, 64), ff_dim=256, ff_act="gelu_tanh"),
+    # grouped q/k/v with RoPE on 8 of 32, no bias
+    with_shape(WORKLOADS["gqa_rope8_bf16"], "nonfinite_gqa_rope8", x_shape=(1, 100, 64)),
+    # fp32, channels-first, exact GELU and RoPE over heads of 8
+    with_shape(WORKLOADS["tiny_f32"], "nonfinite_f32"),
+    # large tiles (planned for 8 CUs: 8 tiles of 256 x 256), exact GELU and RoPE
+    with_shape(WORKLOADS["walrus_bf16"], "nonfinite_large_cf_gelu_rope", x_shape=(4, 64, 16, 16, 1), ff_dim=128,
+               n_heads=2, head_dim=64),
+    # large tiles, squared ReLU, token-major
+    with_shape(WORKLOADS["bert_ff_relu2_bf16"], "nonfinite_large_tl_relu2", x_shape=(2, 512, 64), ff_dim=512),
+]
+
+
+def _plant_non_finite(wl, inp):
+    """NaN, +inf and -inf in x (token 0 among them: rows past the last token read it), a NaN
+    in one weight entry, and (with a bias) +inf and -inf on two ff columns and NaN on a q
+    column, whose RoPE partner then turns NaN as well."""
+    from ff_input_projection_amd.workloads import as_f64
+    x, w = inp.x.clone(), inp.w.clone()
+    xv = x.view(wl.nb, wl.C, wl.S) if wl.layout == "channels_first" else x.view(wl.nb, wl.S, wl.C)
+    for t, val in ((0, float("nan")), (5, float("nan")), (9, float("inf")), (wl.M - 3, float("-inf"))):
+        bi, sp = divmod(t, wl.S)
+        if wl.layout == "channels_first":
+            xv[bi, 3, sp] = val
+        else:
+            xv[bi, sp, 3] = val
+    col_w = wl.ff_dim + 3 if wl.n_heads else 7
+    if wl.w_layout == "cf":
+        w[5, col_w] = float("nan")
+    else:
+        w[col_w, 5] = float("nan")
+    inp.x, inp.w, inp.x64, inp.w64 = x, w, as_f64(x), as_f64(w)
+    if wl.has_bias:
+        b = inp.bias.clone()
+        if wl.ff_dim >= 3:
+            b[1], b[2] = float("inf"), float("-inf")
+        if wl.n_heads:
+            b[wl.ff_dim + 1] = float("nan")
+        inp.bias, inp.bias64 = b, as_f64(b)
+    return inp
+
+
+@pytest.mark.parametrize("choice", ["auto", "general"])
+@pytest.mark.parametrize("wl", NON_FINITE, ids=[w.name for w in NON_FINITE])
+def test_non_finite_inputs_give_the_oracles_non_finite_outputs(wl, choice, monkeypatch):
+    """NaN and infinities in x, W and the bias: every output element is NaN, +inf or -inf
+    exactly where the oracle's is (NaN through every activation, GELU(+inf) = +inf,
+    GELU(-inf) = NaN, relu^2(-inf) = 0), and within the bar wherever the oracle and its
+    bar are finite. Nothing is hidden, and nothing leaks into other tokens or columns."""
+    if choice == "general":
+        monkeypatch.setenv("FUSED_PROJ_KERNEL", "general")
+    else:
+        monkeypatch.delenv("FUSED_PROJ_KERNEL", raising=False)
+    if "_large_" in wl.name:
+        monkeypatch.setenv("FUSED_PROJ_CUS", "8")
+    inp = _plant_non_finite(wl, make_inputs(wl))
+    print(f"[case] non-finite inputs {wl.name} kernel={choice}", flush=True)
+    proj, outs = run_gpu(wl, inp, DEV)
+    print(f"[plan] {proj.describe()}", flush=True)
+    if "_large_" in wl.name and choice == "auto":
+        assert "tile=256x256" in proj.describe(), proj.describe()
+    tokens = all_tokens(wl)
+    got = gpu_rows(wl, outs, tokens)
+    ref = oracle_rows(wl, inp, tokens)
+    with np.errstate(invalid="ignore", over="ignore"):
+        sc = scales_for(wl, inp, tokens, ref)
+    n_nonfinite = 0
+    for name, g, r, scl in zip(("ff", "q", "k", "v"), got, ref, (sc.ff, sc.q, sc.k, sc.v)):
+        if r is None:
+            continue
+        g, r = np.asarray(g, np.float64).reshape(r.shape), np.asarray(r)
+        for cls in (np.isnan, np.isposinf, np.isneginf):
+            assert np.array_equal(cls(g), cls(r)), f"{wl.name} {choice} {name}: {cls.__name__} differs"
+        n_nonfinite += int((~np.isfinite(r)).sum())
+        scl = np.asarray(scl).reshape(r.shape)
+        ok = np.isfinite(r) & np.isfinite(scl)
+        with np.errstate(invalid="ignore"):
+            ratio = np.abs(g[ok] - r[ok]) / (cmp.REL[wl.dtype] * scl[ok] + 1e-300)
+        assert ratio.size and ratio.max() <= 1.0, f"{wl.name} {choice} {name}: {ratio.max()}"
+    print(f"[non-finite] {wl.name} {choice}: {n_nonfinite} non-finite outputs, classes equal", flush=True)
+    assert n_nonfinite > 0
+
+
 def test_run_error_paths():
     wl = SMALL[0]
     inp = make_inputs(wl)
