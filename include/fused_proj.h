@@ -82,7 +82,12 @@ extern "C" {
 #define FUSED_PROJ_W_CF 0 /* W[C, F]: W[c*F + f] */
 #define FUSED_PROJ_W_FC 1 /* W[F, C] (torch nn.Linear weight, y = x W^T): W[f*C + c] */
 
-/* Activation on the ff slice. */
+/* Activation on the ff slice. Non-finite values come out as the formulas below give them
+ * in IEEE arithmetic: a NaN anywhere in a token's row of x, in a column of W or in the
+ * bias stays NaN through the contraction, every activation and RoPE (squared ReLU keeps
+ * NaN too); GELU(+inf) = +inf and GELU(-inf) = NaN in both forms; max(-inf, 0)^2 = 0.
+ * No NaN becomes a finite value. A non-finite x element reaches only its own token's
+ * outputs; one in W or the bias only its own column's (and, with RoPE, its partner's). */
 #define FUSED_PROJ_ACT_NONE 0
 #define FUSED_PROJ_ACT_GELU_ERF 1 /* 0.5 y (1 + erf(y / sqrt 2)) */
 /* 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))): the tanh form of GELU from the paper that
