@@ -216,6 +216,74 @@ def test_backward_no_channels_gives_the_bias_gradient(wl, kernel_choice):
     _check(wl, f"{wl.name} {kernel_choice}")
 
 
+NON_FINITE = [
+    with_shape(WORKLOADS["walrus_bf16"], "bwd_nonfinite_cf_gelu_rope", x_shape=(2, 64, 8, 8, 1), ff_dim=128,
+               n_heads=2, head_dim=64),
+    with_shape(WORKLOADS["bert_ff_relu2_bf16"], "bwd_nonfinite_tl_relu2_fc", x_shape=(2, 70, 64), ff_dim=256,
+               w_layout="fc"),
+    with_shape(WORKLOADS["tiny_f32"], "bwd_nonfinite_f32"),
+]
+
+
+@pytest.mark.parametrize("wl", NON_FINITE, ids=[w.name for w in NON_FINITE])
+def test_backward_non_finite_inputs_give_the_oracles_non_finite_gradients(wl, kernel_choice):
+    """NaN and infinities in x, in one W entry and in the upstream gradients: every element
+    of dx, dW and db is NaN, +inf or -inf exactly where the backward oracle's is, and within
+    the backward bar wherever the oracle and its bar are finite."""
+    from ff_input_projection_amd.workloads import as_f64
+    inp, gr = make_inputs(wl), make_grads(wl)
+    x, w = inp.x.clone(), inp.w.clone()
+    xv = x.view(wl.nb, wl.C, wl.S) if wl.layout == "channels_first" else x.view(wl.nb, wl.S, wl.C)
+    for t, val in ((5, float("nan")), (9, float("inf")), (wl.M - 3, float("-inf"))):
+        bi, sp = divmod(t, wl.S)
+        if wl.layout == "channels_first":
+            xv[bi, 3, sp] = val
+        else:
+            xv[bi, sp, 3] = val
+    if wl.w_layout == "cf":
+        w[5, 7] = float("nan")
+    else:
+        w[7, 5] = float("nan")
+    inp.x, inp.w, inp.x64, inp.w64 = x, w, as_f64(x), as_f64(w)
+    d_ff = gr.d_ff.clone()
+    d_ff.view(-1)[40] = float("nan")
+    d_ff.view(-1)[d_ff.numel() - 7] = float("inf")
+    gr.d_ff, gr.d_ff64 = d_ff, as_f64(d_ff)
+    if gr.dq is not None:
+        dq = gr.dq.clone()
+        dq.view(-1)[11] = float("-inf")
+        gr.dq, gr.dq64 = dq, as_f64(dq)
+    print(f"[case] backward non-finite {wl.name} kernel={kernel_choice}", flush=True)
+    proj, inp, gr, grads = run_backward(wl, inp, gr)
+    ref = oracle.fused_proj_backward(inp.x64, wl.layout, inp.w64, wl.w_layout, inp.bias64, wl.ff_dim, wl.ff_act,
+                                     wl.n_heads, wl.head_dim, wl.rope, gr.d_ff64, gr.dq64, gr.dk64, gr.dv64,
+                                     rope_base=wl.rope_base, pos_offset=wl.pos_offset, n_kv_heads=wl.n_kv_heads,
+                                     qkv_order=wl.qkv_order, rope_dims=wl.rope_dims, ff_layout=wl.ff_layout)
+    rows, _ = cmp.token_rows(inp.x64, wl.layout, np.arange(wl.M, dtype=np.int64))
+    w_cf = inp.w64 if wl.w_layout == "cf" else inp.w64.T
+    with np.errstate(invalid="ignore", over="ignore"):
+        sc = cmp.backward_scales(rows, w_cf, ref.dy)
+    dx, dw, db = (None if t is None else t.double().cpu().numpy() for t in grads)
+    pairs = [("dx", _token_rows(dx, wl.layout, wl.nb, wl.C, wl.S), _token_rows(ref.dx, wl.layout, wl.nb, wl.C, wl.S),
+              sc.dx),
+             ("dW", dw if wl.w_layout == "cf" else dw.T, ref.dw if wl.w_layout == "cf" else ref.dw.T, sc.dw)]
+    if wl.has_bias:
+        pairs.append(("db", db, ref.db, sc.db))
+    n_nonfinite = 0
+    for name, g, r, scl in pairs:
+        assert g.shape == r.shape == scl.shape, (name, g.shape, r.shape, scl.shape)
+        for cls in (np.isnan, np.isposinf, np.isneginf):
+            assert np.array_equal(cls(g), cls(r)), f"{wl.name} {kernel_choice} {name}: {cls.__name__} differs"
+        n_nonfinite += int((~np.isfinite(r)).sum())
+        ok = np.isfinite(r) & np.isfinite(scl)
+        if ok.any():
+            ratio = np.abs(g[ok] - r[ok]) / (cmp.BACKWARD_REL[wl.dtype] * scl[ok] + 1e-300)
+            assert ratio.max() <= 1.0, f"{wl.name} {kernel_choice} {name}: {ratio.max()}"
+    print(f"[bwd non-finite] {wl.name} {kernel_choice}: {n_nonfinite} non-finite gradients, classes equal",
+          flush=True)
+    assert n_nonfinite > 0
+
+
 def test_backward_deterministic_and_graph_replays():
     """Two eager calls give identical bits; a captured call replays to the same bits three
     times (the workspace and outputs are refilled with NaN between replays)."""
