@@ -67,6 +67,39 @@ def test_split_rope_parity(case):
     assert worst <= 1.0
 
 
+@pytest.mark.parametrize("kt", [False, True])
+def test_split_rope_non_finite_values(kt):
+    """NaN and infinities in the projected tensor: v and the unrotated elements copy them;
+    a rotated element is NaN, +inf or -inf exactly where the oracle's is (its partner's
+    NaN or infinity reaches it through the rotation), and finite elsewhere within the bar."""
+    from ff_input_projection_amd.workloads import as_f64
+    batch, tokens, H, KVH, hd, order, rd, off = 2, 40, 4, 2, 32, "grouped", 8, 3
+    Fq = (H + 2 * KVH) * hd
+    x, _ = make_qkv(batch, tokens, Fq, 21)
+    xv = x.view(batch, tokens, Fq)
+    for t, col, val in ((0, 0, float("nan")), (3, 5, float("inf")), (7, 2, float("-inf")), (11, 20, float("nan")),
+                        (12, 40, float("inf")), (39, Fq - 1, float("nan"))):
+        xv[t // tokens, t % tokens, col] = val
+    x64 = as_f64(x)
+    print(f"[case] split_rope non-finite kt={kt}", flush=True)
+    op = SplitRope(batch, tokens, H, hd, n_kv_heads=KVH, qkv_order=order, rope=True, rope_dims=rd,
+                   pos_offset=off, k_transposed=kt)
+    got = op(x.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.split_rope(x64, H, hd, n_kv_heads=KVH, qkv_order=order, rope=True, rope_dims=rd, pos_offset=off,
+                            k_transposed=kt)
+    n_nonfinite = 0
+    for name, g, r in zip("qkv", got, ref):
+        g = g.double().cpu().numpy()
+        for cls in (np.isnan, np.isposinf, np.isneginf):
+            assert np.array_equal(cls(g), cls(r)), f"{name}: {cls.__name__} differs"
+        n_nonfinite += int((~np.isfinite(r)).sum())
+        fin = np.isfinite(r)
+        tol = 2.0 ** -8 * np.abs(r[fin]) + 1e-5 * np.abs(x64[np.isfinite(x64)]).max()
+        assert (np.abs(g[fin] - r[fin]) <= tol).all(), name
+    assert n_nonfinite == 9   # 8 in q (NaN or an infinity and its rotation partner), 1 in v
+
+
 def test_split_rope_named_workloads_match_cases():
     for wl in SPLIT_ROPE_WORKLOADS.values():
         assert (wl.batch, wl.tokens, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.qkv_order, wl.rope_dims,
