@@ -284,6 +284,34 @@ def test_backward_non_finite_inputs_give_the_oracles_non_finite_gradients(wl, ke
     assert n_nonfinite > 0
 
 
+def test_backward_one_plan_on_two_streams_at_once():
+    """The backward pass keeps its intermediates in the caller's workspace, so one plan may
+    run it on two streams at once with two workspaces: 10 rounds on each stream without
+    waiting, and each stream's gradients equal the eager ones of its own inputs, bit for bit."""
+    wl = SPLIT[0]
+    sets = [(make_inputs(wl), make_grads(wl)), (make_inputs(wl, seed=wl.seed + 55), make_grads(wl, seed=wl.seed + 55))]
+    args = []
+    for inp, gr in sets:
+        args.append((inp.x.to(DEV), inp.w.to(DEV), inp.bias.to(DEV), *[_to_dev(t) for t in (gr.d_ff, gr.dq, gr.dk, gr.dv)]))
+    proj = plan_for(wl, args[0][0])
+    eager = [[t.clone() for t in proj.backward(*a)] for a in args]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [proj.alloc_grads(DEV) for _ in range(2)]
+    wss = [torch.empty(proj.workspace_bytes(), dtype=torch.uint8, device=DEV) for _ in range(2)]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for _ in range(10):
+        for i in range(2):
+            proj.backward(*args[i], out=outs[i], workspace=wss[i], stream=streams[i])
+    for st in streams:
+        torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    for i in range(2):
+        for e, g in zip(eager[i], outs[i]):
+            assert torch.equal(e, g), f"stream {i}"
+
+
 def test_backward_deterministic_and_graph_replays():
     """Two eager calls give identical bits; a captured call replays to the same bits three
     times (the workspace and outputs are refilled with NaN between replays)."""

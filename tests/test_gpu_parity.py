@@ -613,6 +613,35 @@ def test_run_error_paths():
         proj(x, w, b, out=(ff, q, q, v))
 
 
+@pytest.mark.parametrize("wl", [SMALL[0], SMALL[1]], ids=[SMALL[0].name, SMALL[1].name])
+def test_one_plan_on_two_streams_at_once(wl):
+    """A plan holds only read-only tables (RoPE cos/sin, column descriptors), so launches of
+    one plan on two streams may run at the same time: 20 rounds, each launching on both
+    streams without waiting, and each stream's outputs equal the eager result of its own
+    inputs, bit for bit."""
+    inp_a, inp_b = make_inputs(wl), make_inputs(wl, seed=wl.seed + 77)
+    dev = lambda inp: (inp.x.to(DEV), inp.w.to(DEV), None if inp.bias is None else inp.bias.to(DEV))
+    a, b = dev(inp_a), dev(inp_b)
+    proj = plan_for(wl, a[0])
+    eager = [[t.clone() for t in proj(*args) if t is not None] for args in (a, b)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[proj.alloc_outputs(DEV) for _ in range(2)] for _ in range(2)]   # [stream][buffer set]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for rnd in range(20):
+        for i, (st, args) in enumerate(zip(streams, (a, b))):
+            proj(*args, out=outs[i][rnd % 2], stream=st)
+    for st in streams:
+        torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    for i in range(2):
+        for j in range(2):
+            got = [t for t in outs[i][j] if t is not None]
+            for e, g in zip(eager[i], got):
+                assert torch.equal(e, g), f"stream {i} buffer set {j}"
+
+
 def test_hip_graph_capture_replays_match_eager():
     """fused_proj_run allocates and synchronises nothing, so it can be captured;
     every replay must equal the eager result."""
