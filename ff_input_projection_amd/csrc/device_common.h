@@ -47,9 +47,9 @@ __device__ __forceinline__ float gelu_erf(float y) {
 // to 6 in both places it is used: past 6, |y| q(|y|) < 1e-8 and 6 q(6) stands for it.
 // The clamp is one v_med3_f32 (fminf would put a canonicalizing v_max_f32 in front in
 // IEEE mode). The positive part is (y + |y|) / 2, which is max(y, 0) exactly for finite y
-// and, unlike any min / max / med3 (all of which drop a quiet NaN), keeps what the
-// defining y Phi(y) gives in IEEE arithmetic: NaN for NaN, +inf for +inf, NaN for -inf.
-// 11 VALU instructions per value.
+// and, unlike v_max_f32 / v_med3_f32 (which drop a quiet NaN), keeps what the defining
+// y Phi(y) gives in IEEE arithmetic: NaN for NaN, +inf for +inf, NaN for -inf (a
+// NaN-keeping v_maximum3_f32 would give about 0 for -inf). 11 VALU instructions per value.
 __device__ __forceinline__ float gelu_erf_poly(float y) {
     const float a = __builtin_amdgcn_fmed3f(fabsf(y), 0.0f, 6.0f);
     float p = 2.2990056e-05f;

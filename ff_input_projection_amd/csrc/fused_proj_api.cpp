@@ -635,7 +635,10 @@ int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backwa
     // channels past C (a partial last K step, and on large tiles the steps that pad the K
     // loop to a multiple of its four stages) read the zero block. Measured against the
     // general kernel on such shapes (C 320, 72, 200 on large tiles): faster or equal.
-    const bool exact = desc->channels > 0;
+    // Without channels (C = 0, bias only) there is no contraction to pipeline: the general
+    // kernel's empty K loop is the plain choice, and the fast kernel (one K step read from
+    // its zero block) runs only when forced.
+    const bool has_channels = desc->channels > 0;
     // (the 8-column RoPE's descriptors keep bit 29 for the rotated groups)
     const bool addressable = fp::fast_addressable(r.M, r.S, desc->ff_dim, r.qw) &&
                              (!rope8 || r.S * r.qw < (int64_t(1) << 29));
@@ -650,7 +653,7 @@ int create_plan(const fused_proj_desc* desc, fused_proj_t* out, bool with_backwa
     h->epi = ff_cf ? 2 : other_act ? 1 : rope8 ? 3 : 0;
     const bool fast_epi = h->epi == 0 || h->epi == 3 ||
                           (!roped && (h->epi == 1 || (!other_act && desc->ff_dim % 128 == 0)));
-    h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && addressable && fast_epi && (exact || want_fast) &&
+    h->fast = h->dt == fp::DType::BF16 && dg >= 0 && fits32 && addressable && fast_epi && (has_channels || want_fast) &&
               !want_general;
     h->dg = dg < 0 ? 0 : dg;
     h->tile = h->fast ? fp_plan : fp::TilePlan{128, 128, h->dt == fp::DType::BF16 ? 64 : 32, 8, 0};
