@@ -219,3 +219,34 @@ def test_mfma_ceiling_rejects_bad_arguments():
     assert lib.fused_proj_mfma_ceiling(10, 1, ctypes.cast(sink, ctypes.c_void_p), 64, None, None) == fpa.EINVAL
     assert lib.fused_proj_mfma_ceiling(10, 1, None, 64, None, ctypes.byref(flops)) == fpa.EINVAL
     assert flops.value == -1.0
+
+
+def test_product_path_fails_loudly_without_the_library_and_never_imports_the_oracle():
+    """With the HIP library absent, planning raises (there is no CPU fallback); importing
+    the package and planning bring in nothing from oracle/. Run in a fresh interpreter."""
+    import subprocess
+    import sys
+    code = r"""
+import sys
+import ff_input_projection_amd as fpa
+fpa.LIB_PATH = "/nonexistent/libfused_proj.so"
+fpa._lib = None
+import torch
+try:
+    fpa.FusedProjection((1, 8, 8), (64, 8, 1), "tokens_last", torch.bfloat16, ff_dim=8)
+except RuntimeError as e:
+    assert "no CPU fallback" in str(e), e
+else:
+    raise SystemExit("planning without the library did not raise")
+try:
+    fpa.SplitRope(1, 8, 1, 8)
+except RuntimeError as e:
+    assert "no CPU fallback" in str(e), e
+else:
+    raise SystemExit("split+RoPE without the library did not raise")
+assert not any(m == "oracle" or m.startswith("oracle.") for m in sys.modules), "the package imported the oracle"
+print("ok")
+"""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
