@@ -20,7 +20,8 @@
  *     cleanup and much better perfs" (description and follow-up comments):
  *     the op is y = act(x W^T + b); for the attention projection it is the
  *     same op with no activation, written into three buffers.
- *     y[t,f] = sum_c x[t,c] * W[c,f] + b[f], summed in increasing c.
+ *     y[t,f] = sum_c x[t,c] * W[c,f] + b[f], summed in increasing c. With no
+ *     channels (C = 0, which the pages never meet) the sum is empty: y = b.
  *
  *  3. Split. Walrus PR (second comment): the fused output is split into
  *     ff, q, k, v. Reading: contiguous column slices in that order, each of
@@ -32,7 +33,9 @@
  *     that defines GELU (Hendrycks and Gimpel, "Gaussian Error Linear Units
  *     (GELUs)", 2016): 0.5*y*(1+tanh(sqrt(2/pi)*(y+0.044715*y^3))); and
  *     squared ReLU, max(y,0)^2, which the xformers PR discussion names among
- *     the activations a fused linear layer handles natively.
+ *     the activations a fused linear layer handles natively. Non-finite values
+ *     (which the pages never meet) go through the formulas in IEEE arithmetic,
+ *     and squared ReLU leaves a NaN in place as torch's relu does.
  *
  *  5. Head-major buffers. memory-efficient-attention issue "Improve
  *     performance via batched-matmul and fused multiplies" (first comment):
@@ -45,8 +48,10 @@
  *     into halves x1, x2; the rotated vector is (-x2, x1); the output is
  *     x*cos + rotated*sin. Pairs are (i, i + head_dim/2). The page fills the
  *     cos/sin tables with random numbers, so the angle is the textbook
- *     phi = p * base^(-2i/head_dim) (a convention, not fixed by the pages),
- *     with p = s + pos_offset, the token's position inside its slab.
+ *     phi = p * base^(-2i/head_dim) (a convention, not fixed by the pages:
+ *     parity unpinned against the pages for the angles; the tests pin the
+ *     rotation itself), with p = s + pos_offset, the token's position inside
+ *     its slab.
  *
  *  7. The backward pass (oracle_fused_proj_backward below): the gradients of x,
  *     W and the bias by the chain rule through steps 1-6, in reverse order.
