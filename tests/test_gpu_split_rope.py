@@ -25,6 +25,8 @@ CASES = [
     (2, 16, 4, 2, 24, "grouped", 6, False, 0, 13),       # rotated half (3) not a multiple of anything
     (2, 40, 4, 2, 128, "contiguous", 0, False, 3, 14),   # head size 128, full rotation
     (1, 64, 4, 4, 64, "grouped", 32, True, 0, 15),       # half the head rotated, K^T
+    (16, 1, 32, 8, 128, "contiguous", 0, False, 4095, 16),   # decode step: one token per sequence at 4095
+    (4, 1, 16, 4, 32, "grouped", 8, False, 1023, 17),        # decode step, grouped, partial rotation
 ]
 
 
