@@ -312,6 +312,23 @@ def test_backward_one_plan_on_two_streams_at_once():
             assert torch.equal(e, g), f"stream {i}"
 
 
+ONE_TOKEN = [
+    # one token per sequence at a position offset: 16 sequences, GELU ff and RoPE heads
+    with_shape(WORKLOADS["bert_qkv_bf16"], "bwd_one_token_gelu_rope", x_shape=(16, 1, 256), ff_dim=128,
+               ff_act="gelu", n_heads=2, head_dim=64, rope=True, pos_offset=100, seed=431),
+    # fp32, a single sequence of one token, grouped q/k/v with RoPE on 8 of 32
+    with_shape(WORKLOADS["tiny_f32"], "bwd_one_token_f32_gqa", layout="tokens_last", x_shape=(1, 1, 64), ff_dim=32,
+               n_heads=4, head_dim=32, n_kv_heads=2, qkv_order="grouped", rope_dims=8, pos_offset=7, seed=432),
+]
+
+
+@pytest.mark.parametrize("wl", ONE_TOKEN, ids=[w.name for w in ONE_TOKEN])
+def test_backward_one_token_per_sequence(wl, kernel_choice):
+    """S = 1 with a position offset: every gradient element against the oracle."""
+    assert wl.S == 1
+    _check(wl, f"{wl.name} {kernel_choice}")
+
+
 def test_backward_deterministic_and_graph_replays():
     """Two eager calls give identical bits; a captured call replays to the same bits three
     times (the workspace and outputs are refilled with NaN between replays)."""
